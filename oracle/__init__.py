@@ -1,0 +1,146 @@
+"""CSA2 CPU oracle — TEST INFRASTRUCTURE ONLY.
+
+Plain fp64 C implementation of the CSA2 hot path (csa2_oracle.c) behind a thin
+ctypes wrapper over numpy arrays.  Only the tests, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import this package; the product
+library never does.  It shares no code with the HIP library.
+
+Functions follow the DeepSeek-V4.1-Flash report (sec. 2.3, 2.3.1, 2.4.4,
+3.2.2, 4.2.1) and the gzher.com reading of DeepSeek-V4 (sec. 4.1, 4.3); the
+C source cites the passage for each step.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "csa2_oracle.c")
+LIB = os.path.join(HERE, "libcsa2_oracle.so")
+
+IDX_HEADS, IDX_DIM, HEADS, DIM = 32, 128, 64, 512
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (fp64, no fast-math, no contraction)."""
+    if force or not os.path.exists(LIB):
+        cmd = ["gcc", "-O2", "-mfma", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+               "-shared", "-fPIC", "-std=c11", "-Wall", "-Wextra", "-Werror",
+               SRC, "-o", LIB + ".tmp", "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        L = ctypes.CDLL(LIB)
+        vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.csa2o_e2m1.argtypes, L.csa2o_e2m1.restype = [ctypes.c_uint32], dbl
+        L.csa2o_e8m0.argtypes, L.csa2o_e8m0.restype = [ctypes.c_uint32], dbl
+        L.csa2o_dequant_row.argtypes, L.csa2o_dequant_row.restype = [vp, vp, i32, vp], None
+        L.csa2o_n_visible.argtypes, L.csa2o_n_visible.restype = [i64, i32, i64], i64
+        L.csa2o_index_score.argtypes, L.csa2o_index_score.restype = [vp, vp, vp], dbl
+        L.csa2o_index.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, vp]
+        L.csa2o_index.restype = None
+        L.csa2o_topk_row.argtypes, L.csa2o_topk_row.restype = [vp, i64, i32, vp], i32
+        L.csa2o_topk.argtypes, L.csa2o_topk.restype = [vp, vp, i32, i32, i64, i32, vp], None
+        L.csa2o_attend.argtypes = [vp, vp, vp, vp, vp, vp, vp, dbl, i32, i32, i64, i32, i32, i32, vp, vp]
+        L.csa2o_attend.restype = None
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == dtype, (a.dtype, dtype)
+    return a
+
+
+def e2m1(code: int) -> float:
+    return lib().csa2o_e2m1(code)
+
+
+def e8m0(e: int) -> float:
+    return lib().csa2o_e8m0(e)
+
+
+def dequant_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """codes uint8 [R][dim/2], scales uint8 [R][dim/32] -> float64 [R][dim]."""
+    codes, scales = _c(codes, np.uint8), _c(scales, np.uint8)
+    R, half = codes.shape
+    dim = half * 2
+    out = np.empty((R, dim), np.float64)
+    L = lib()
+    for r in range(R):
+        L.csa2o_dequant_row(_ptr(codes[r]), _ptr(scales[r]), dim, _ptr(out[r]))
+    return out
+
+
+def n_visible(pos: int, ratio: int, N: int) -> int:
+    return lib().csa2o_n_visible(pos, ratio, N)
+
+
+def index_score(q: np.ndarray, w: np.ndarray, key: np.ndarray) -> float:
+    """q uint16(bf16 bits) [32][128], w float32 [32], key uint16 [128]."""
+    q, w, key = _c(q, np.uint16), _c(w, np.float32), _c(key, np.uint16)
+    return lib().csa2o_index_score(_ptr(q), _ptr(w), _ptr(key))
+
+
+def index(q_idx, w_idx, k_idx, q_pos, ratio, q_per_seq):
+    """q_idx uint16 [T][32][128], w float32 [T][32], k_idx uint16 [B][N][128],
+    q_pos int32 [T] or None -> float64 scores [T][N] (-inf beyond visibility)."""
+    q_idx, w_idx, k_idx = _c(q_idx, np.uint16), _c(w_idx, np.float32), _c(k_idx, np.uint16)
+    T = q_idx.shape[0]
+    N = k_idx.shape[1]
+    qp = None if q_pos is None else _c(q_pos, np.int32)
+    out = np.empty((T, N), np.float64)
+    lib().csa2o_index(_ptr(q_idx), _ptr(w_idx), _ptr(k_idx), _ptr(qp), ratio, T, q_per_seq, N, _ptr(out))
+    return out
+
+
+def topk_row(scores: np.ndarray, n_vis: int, k: int) -> np.ndarray:
+    scores = _c(scores, np.float64)
+    out = np.empty(k, np.int32)
+    lib().csa2o_topk_row(_ptr(scores), n_vis, k, _ptr(out))
+    return out
+
+
+def topk(scores, q_pos, ratio, k):
+    scores = _c(scores, np.float64)
+    T, N = scores.shape
+    qp = None if q_pos is None else _c(q_pos, np.int32)
+    out = np.empty((T, k), np.int32)
+    lib().csa2o_topk(_ptr(scores), _ptr(qp), ratio, T, N, k, _ptr(out))
+    return out
+
+
+def attend(q, kv_codes, kv_scales, indices, swa, swa_end, sink, softmax_scale, q_per_seq, window):
+    """q uint16 [T][64][512]; kv_codes uint8 [B][N][256]; kv_scales uint8 [B][N][16];
+    indices int32 [T][k]; swa uint16 [B][S][512]; swa_end int32 [T]; sink float64 [64] or None.
+    Returns (out float64 [T][64][512], lse float64 [T][64])."""
+    q = _c(q, np.uint16)
+    kv_codes, kv_scales = _c(kv_codes, np.uint8), _c(kv_scales, np.uint8)
+    indices, swa, swa_end = _c(indices, np.int32), _c(swa, np.uint16), _c(swa_end, np.int32)
+    sk = None if sink is None else _c(np.asarray(sink, np.float64), np.float64)
+    T = q.shape[0]
+    N = kv_codes.shape[1]
+    S = swa.shape[1]
+    k = indices.shape[1]
+    out = np.empty((T, HEADS, DIM), np.float64)
+    lse = np.empty((T, HEADS), np.float64)
+    lib().csa2o_attend(_ptr(q), _ptr(kv_codes), _ptr(kv_scales), _ptr(indices), _ptr(swa), _ptr(swa_end),
+                       _ptr(sk), float(softmax_scale), T, q_per_seq, N, S, window, k, _ptr(out), _ptr(lse))
+    return out, lse

@@ -1,0 +1,227 @@
+/*
+ * CSA2 CPU oracle (fp64).  TEST INFRASTRUCTURE ONLY: used by the tests, the
+ * smoke check and the benchmark's CPU-baseline leg, never by the product path.
+ * It shares no code with the HIP library.  See csa2_oracle.h for layouts.
+ *
+ * Every function follows the definition on the pages as plainly as possible:
+ * no blocking, no fusion, no reordering beyond the loops written here.
+ * Threads (OpenMP) only split independent queries / entry ranges; they do not
+ * change any arithmetic.
+ */
+#include "csa2_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define IDX_HEADS 32
+#define IDX_DIM 128
+#define HEADS 64
+#define DIM 512
+#define MX_BLOCK 32
+
+/* ---- formats ------------------------------------------------------------ */
+
+/* bf16 bit pattern -> double (exact). */
+static double bf16_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* OCP MX E2M1: 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit.
+ * exponent field 0 is subnormal (0 or 0.5); otherwise 2^(E-1) * (1 + M/2).
+ * The V4.1 report (sec. 2.4.4) uses E2M1 elements with largest magnitude 6. */
+double csa2o_e2m1(uint32_t code) {
+    uint32_t s = (code >> 3) & 1u, e = (code >> 1) & 3u, m = code & 1u;
+    double mag = (e == 0) ? 0.5 * (double)m : ldexp(1.0 + 0.5 * (double)m, (int)e - 1);
+    return s ? -mag : mag;
+}
+
+/* OCP MX E8M0 shared scale: 2^(e-127); 0xFF encodes NaN. */
+double csa2o_e8m0(uint32_t e) {
+    if ((e & 0xFFu) == 0xFFu) return NAN;
+    return ldexp(1.0, (int)(e & 0xFFu) - 127);
+}
+
+/* V4.1 report sec. 2.4.4: the main KV cache is stored in FP4 after RoPE and
+ * dequantised before attention.  x[c] = E2M1(code[c]) * scale[c / 32]. */
+void csa2o_dequant_row(const uint8_t* codes, const uint8_t* scales, int32_t dim, double* out) {
+    for (int32_t c = 0; c < dim; ++c) {
+        uint8_t byte = codes[c / 2];
+        uint32_t code = (c % 2 == 0) ? (byte & 0x0Fu) : (byte >> 4);
+        out[c] = csa2o_e2m1(code) * csa2o_e8m0(scales[c / MX_BLOCK]);
+    }
+}
+
+/* ---- visibility ---------------------------------------------------------- */
+
+/* V4 reading sec. 4.3: the compressed branch sees a compressed block only once
+ * every token in it has been seen; V4.1 report sec. 2.3.2 scores exactly the
+ * entries the query may see causally.  With ratio m, entry j holds tokens
+ * [m*j, m*j + m). */
+int64_t csa2o_n_visible(int64_t pos, int32_t ratio, int64_t N) {
+    if (pos < 0) return N;
+    int64_t n = 0;
+    while (n < N && (int64_t)ratio * (n + 1) <= pos + 1) ++n; /* plain count */
+    return n;
+}
+
+/* ---- indexer ------------------------------------------------------------- */
+
+/* V4 reading sec. 4.1 (lightning indexer): I_{t,s} = sum_h w_{t,h} ReLU(q_{t,h} . K_s);
+ * V4.1 report sec. 2.3 keeps CSA's indexer form, with 32 heads x 128
+ * (sec. 4.2.1).  fp64, channels in order, heads in order, each step one fma. */
+double csa2o_index_score(const uint16_t* q, const float* w, const uint16_t* key) {
+    double score = 0.0;
+    for (int h = 0; h < IDX_HEADS; ++h) {
+        double dot = 0.0;
+        for (int c = 0; c < IDX_DIM; ++c)
+            dot = fma(bf16_to_double(q[h * IDX_DIM + c]), bf16_to_double(key[c]), dot);
+        double relu = dot > 0.0 ? dot : 0.0;
+        score = fma((double)w[h], relu, score);
+    }
+    return score;
+}
+
+void csa2o_index(const uint16_t* q_idx, const float* w_idx, const uint16_t* k_idx,
+                 const int32_t* q_pos, int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N,
+                 double* scores) {
+    const int64_t chunk = 4096;
+    const int64_t nchunks = (N + chunk - 1) / chunk;
+    int64_t* n_vis = (int64_t*)malloc((size_t)(T > 0 ? T : 1) * sizeof(int64_t));
+    for (int32_t t = 0; t < T; ++t) n_vis[t] = csa2o_n_visible(q_pos ? q_pos[t] : -1, ratio, N);
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int32_t t = 0; t < T; ++t) {
+        for (int64_t ch = 0; ch < nchunks; ++ch) {
+            int64_t b = t / q_per_seq;
+            const uint16_t* q = q_idx + (int64_t)t * IDX_HEADS * IDX_DIM;
+            const float* w = w_idx + (int64_t)t * IDX_HEADS;
+            int64_t s_end = (ch + 1) * chunk < N ? (ch + 1) * chunk : N;
+            for (int64_t s = ch * chunk; s < s_end; ++s) {
+                double v = -INFINITY;
+                if (s < n_vis[t]) v = csa2o_index_score(q, w, k_idx + (b * N + s) * IDX_DIM);
+                scores[(int64_t)t * N + s] = v;
+            }
+        }
+    }
+    free(n_vis);
+}
+
+/* ---- top-k --------------------------------------------------------------- */
+
+typedef struct {
+    double score;
+    int64_t idx;
+} scored_t;
+
+/* Order used for selection: higher score first, lower index on equal scores. */
+static int cmp_score_desc_idx_asc(const void* a, const void* b) {
+    const scored_t* x = (const scored_t*)a;
+    const scored_t* y = (const scored_t*)b;
+    if (x->score > y->score) return -1;
+    if (x->score < y->score) return 1;
+    return (x->idx < y->idx) ? -1 : (x->idx > y->idx);
+}
+
+static int cmp_i32(const void* a, const void* b) {
+    int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+    return (x > y) - (x < y);
+}
+
+/* V4.1 report sec. 2.3: per query the indexer keeps the K best-scoring
+ * entries; K = 512 (sec. 4.2.1).  Full sort, keep the first min(k, n). */
+int32_t csa2o_topk_row(const double* scores, int64_t n_vis, int32_t k, int32_t* out) {
+    scored_t* all = (scored_t*)malloc((size_t)(n_vis > 0 ? n_vis : 1) * sizeof(scored_t));
+    for (int64_t s = 0; s < n_vis; ++s) {
+        all[s].score = scores[s];
+        all[s].idx = s;
+    }
+    qsort(all, (size_t)n_vis, sizeof(scored_t), cmp_score_desc_idx_asc);
+    int32_t n_sel = (int64_t)k < n_vis ? k : (int32_t)n_vis;
+    for (int32_t j = 0; j < n_sel; ++j) out[j] = (int32_t)all[j].idx;
+    qsort(out, (size_t)n_sel, sizeof(int32_t), cmp_i32);
+    for (int32_t j = n_sel; j < k; ++j) out[j] = -1;
+    free(all);
+    return n_sel;
+}
+
+void csa2o_topk(const double* scores, const int32_t* q_pos, int32_t ratio, int32_t T,
+                int64_t N, int32_t k, int32_t* indices) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t t = 0; t < T; ++t) {
+        int64_t n_vis = csa2o_n_visible(q_pos ? q_pos[t] : -1, ratio, N);
+        csa2o_topk_row(scores + (int64_t)t * N, n_vis, k, indices + (int64_t)t * k);
+    }
+}
+
+/* ---- attention ----------------------------------------------------------- */
+
+/* V4 reading sec. 4.1: shared-KV MQA, the selected compressed entry is both
+ * key and value; sec. 4.3: an SWA branch of the 128 most recent tokens and an
+ * optional per-head sink exp(z'_h) in the softmax denominator.  V4.1 report
+ * sec. 2.3: each query attends to the selected entries together with the
+ * layer-local SWA KV; sec. 3.2.2: window [max(s, i-W+1), i].
+ * One softmax over the union (the neshdevtech reading, sec. 3.3.1/3.3.2,
+ * concatenates SWA and selected main KV into a single readout). */
+void csa2o_attend(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                  const int32_t* indices, const uint16_t* swa, const int32_t* swa_end,
+                  const double* sink, double softmax_scale, int32_t T, int32_t q_per_seq,
+                  int64_t N, int32_t S, int32_t window, int32_t k, double* out, double* lse) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t t = 0; t < T; ++t) {
+        int64_t b = t / q_per_seq;
+        /* gather the rows of this query's attention set: selected entries in
+         * the order of the index list, then the window rows in order */
+        int32_t n_main = 0;
+        for (int32_t j = 0; j < k; ++j)
+            if (indices[(int64_t)t * k + j] >= 0) ++n_main;
+        int32_t end = swa_end[t];
+        int32_t start = end - window > 0 ? end - window : 0;
+        int32_t n_swa = end - start;
+        int32_t n_rows = n_main + n_swa;
+        double* rows = (double*)malloc((size_t)(n_rows > 0 ? n_rows : 1) * DIM * sizeof(double));
+        int32_t r = 0;
+        for (int32_t j = 0; j < k; ++j) {
+            int64_t s = indices[(int64_t)t * k + j];
+            if (s < 0) continue;
+            csa2o_dequant_row(kv_codes + (b * N + s) * (DIM / 2), kv_scales + (b * N + s) * (DIM / MX_BLOCK),
+                              DIM, rows + (int64_t)r * DIM);
+            ++r;
+        }
+        for (int32_t i = start; i < end; ++i, ++r)
+            for (int c = 0; c < DIM; ++c)
+                rows[(int64_t)r * DIM + c] = bf16_to_double(swa[(b * S + i) * DIM + c]);
+
+        double* z = (double*)malloc((size_t)(n_rows > 0 ? n_rows : 1) * sizeof(double));
+        for (int h = 0; h < HEADS; ++h) {
+            const uint16_t* qh = q + ((int64_t)t * HEADS + h) * DIM;
+            double m = -INFINITY;
+            for (int32_t j = 0; j < n_rows; ++j) {
+                double dot = 0.0;
+                for (int c = 0; c < DIM; ++c) dot += bf16_to_double(qh[c]) * rows[(int64_t)j * DIM + c];
+                z[j] = softmax_scale * dot;
+                if (z[j] > m) m = z[j];
+            }
+            if (sink && sink[h] > m) m = sink[h];
+            double* o = out + ((int64_t)t * HEADS + h) * DIM;
+            for (int c = 0; c < DIM; ++c) o[c] = 0.0;
+            double den = 0.0;
+            if (m == -INFINITY) { /* nothing to attend to */
+                if (lse) lse[(int64_t)t * HEADS + h] = -INFINITY;
+                continue;
+            }
+            for (int32_t j = 0; j < n_rows; ++j) {
+                double p = exp(z[j] - m);
+                den += p;
+                for (int c = 0; c < DIM; ++c) o[c] += p * rows[(int64_t)j * DIM + c];
+            }
+            if (sink) den += exp(sink[h] - m);
+            for (int c = 0; c < DIM; ++c) o[c] /= den;
+            if (lse) lse[(int64_t)t * HEADS + h] = m + log(den);
+        }
+        free(z);
+        free(rows);
+    }
+}

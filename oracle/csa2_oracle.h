@@ -1,0 +1,87 @@
+/*
+ * CSA2 CPU oracle: plain, slow, fp64 reference of the CSA2 global-attention
+ * hot path (indexer scoring, top-k selection, MXFP4 main-KV dequantisation,
+ * joint sparse + sliding-window attention, cross-layer Reuse).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link or
+ * call this code; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg do.  It shares no code, header, table or constant with the HIP
+ * library.
+ *
+ * Sources (the pages this follows):
+ *  - DeepSeek-V4.1-Flash report, sec. 2.3 "Compressed Sparse Attention 2" and
+ *    2.3.1 (Full / Reindex / Reuse modes), sec. 2.4.4 "FP4 Main KV Cache",
+ *    sec. 3.2.2 "SWA Bounded Replay" (window [max(s, i-W+1), i]), sec. 4.2.1
+ *    configuration (32 indexer heads x 128, top-k 512, 64 heads x 512, n_win 128).
+ *  - gzher.com reading of DeepSeek-V4, sec. 4.1 "CSA" (lightning-indexer score
+ *    I_{t,s} = sum_h w_{t,h} ReLU(q_{t,h} . K_s), shared key = value core
+ *    attention) and sec. 4.3 (sliding window branch, attention sink formula).
+ *  - OCP Microscaling (MX) format: E2M1 element, E8M0 shared scale per 32.
+ *
+ * Conventions shared with the library's ABI (data layout only):
+ *  - bf16 tensors are passed as uint16 bit patterns, row-major.
+ *  - MXFP4 rows: 256 bytes of codes per 512-channel entry, element 2i in the
+ *    low nibble of byte i, element 2i+1 in the high nibble; 16 E8M0 scale
+ *    bytes per entry, scale j covering channels [32j, 32j+32).
+ *  - Query t belongs to sequence t / q_per_seq.
+ */
+#ifndef CSA2_ORACLE_H
+#define CSA2_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Value of one E2M1 code (OCP MX): sign bit 3, magnitudes {0,.5,1,1.5,2,3,4,6}. */
+double csa2o_e2m1(uint32_t code);
+/* E8M0 scale 2^(e-127); e == 255 (NaN in the spec) returns NaN. */
+double csa2o_e8m0(uint32_t e);
+/* Dequantise one MXFP4 row of `dim` channels (dim % 32 == 0) into out[dim]. */
+void csa2o_dequant_row(const uint8_t* codes, const uint8_t* scales, int32_t dim, double* out);
+
+/* Number of compressed entries causally visible to the token at absolute
+ * position `pos` with compression ratio m: entry j (covering tokens
+ * [m*j, m*j+m)) is visible iff it is complete, m*(j+1) <= pos+1.
+ * Capped at N.  pos < 0 means "all N visible" (decode without positions). */
+int64_t csa2o_n_visible(int64_t pos, int32_t ratio, int64_t N);
+
+/* Indexer score of one entry: sum_h w[h] * ReLU(q[h] . key) in fp64, dot
+ * products accumulated in channel order with fma, heads in order. */
+double csa2o_index_score(const uint16_t* q /*[32][128]*/, const float* w /*[32]*/,
+                         const uint16_t* key /*[128]*/);
+
+/* Scores of all entries for T queries: scores[t][s] for s < n_vis(t), -inf
+ * beyond.  q_pos may be NULL (all visible). Threads over (t, entry chunk). */
+void csa2o_index(const uint16_t* q_idx /*[T][32][128]*/, const float* w_idx /*[T][32]*/,
+                 const uint16_t* k_idx /*[B][N][128]*/, const int32_t* q_pos /*[T] or NULL*/,
+                 int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N,
+                 double* scores /*[T][N]*/);
+
+/* Top-k of one score row: the first min(k, n_vis) entries in the order
+ * (score descending, index ascending), written ascending by index into
+ * out[k], the rest -1.  Returns the number selected. */
+int32_t csa2o_topk_row(const double* scores, int64_t n_vis, int32_t k, int32_t* out);
+
+/* Top-k for T rows of scores[T][N] with per-query visibility. */
+void csa2o_topk(const double* scores, const int32_t* q_pos, int32_t ratio, int32_t T,
+                int64_t N, int32_t k, int32_t* indices /*[T][k]*/);
+
+/* Joint sparse + sliding-window attention for T queries.
+ *  q      bf16 [T][64][512]
+ *  kv     MXFP4 codes [B][N][256], scales [B][N][16]
+ *  indices [T][k], -1 = empty slot
+ *  swa    bf16 [B][S][512]; query t attends SWA rows [max(0, end-W), end),
+ *         end = swa_end[t]
+ *  sink   [64] or NULL: extra exp(sink_h) term in each head's denominator
+ *  out    [T][64][512] fp64; lse [T][64] fp64 or NULL
+ * Key = value = the dequantised entry.  One softmax over both sets. */
+void csa2o_attend(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                  const int32_t* indices, const uint16_t* swa, const int32_t* swa_end,
+                  const double* sink, double softmax_scale, int32_t T, int32_t q_per_seq,
+                  int64_t N, int32_t S, int32_t window, int32_t k, double* out, double* lse);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

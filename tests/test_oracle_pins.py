@@ -1,0 +1,373 @@
+"""Pins of the CPU oracle against facts fixed outside it (no GPU).
+
+Each test checks the oracle against something it does not compute itself:
+values printed in a format specification or fixed by the pages (golden files),
+closed forms, exact rational arithmetic, an independent textbook
+implementation, or invariants that any correct implementation satisfies.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import csa2_gen as G
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _bf16(x):
+    """float -> bf16 bits (exact for the values used here)."""
+    u = np.array([x], np.float32).view(np.uint32)[0]
+    assert u & 0xFFFF == 0, x
+    return np.uint16(u >> 16)
+
+
+def _bf16_val(b):
+    return float(np.array([np.uint32(b) << 16], np.uint32).view(np.float32)[0])
+
+
+# ------------------------------------------------------------------ formats
+
+def test_e2m1_table_matches_spec(oracle_lib):
+    for code, val in _golden("e2m1_values.txt"):
+        got = oracle_lib.e2m1(int(code))
+        assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), code
+
+
+def test_e8m0_scales(oracle_lib):
+    for e in range(255):
+        assert oracle_lib.e8m0(e) == 2.0 ** (e - 127)
+    assert math.isnan(oracle_lib.e8m0(255))
+
+
+def test_dequant_worked_example(oracle_lib):
+    # 64-channel row: byte i packs channel 2i (low nibble) and 2i+1 (high nibble).
+    codes = np.zeros((1, 32), np.uint8)
+    codes[0, 0] = 0x21     # ch0 = code 1 (0.5), ch1 = code 2 (1.0)
+    codes[0, 1] = 0xF7     # ch2 = code 7 (6.0), ch3 = code 15 (-6.0)
+    codes[0, 16] = 0x9B    # ch32 = code 11 (-1.5), ch33 = code 9 (-0.5)
+    scales = np.array([[127 + 3, 127 - 5]], np.uint8)   # 2^3 for ch 0..31, 2^-5 for ch 32..63
+    x = oracle_lib.dequant_rows(codes, scales)[0]
+    assert list(x[:4]) == [4.0, 8.0, 48.0, -48.0]
+    assert x[32] == -1.5 / 32 and x[33] == -0.5 / 32
+    assert np.all(x[4:32] == 0) and np.all(x[34:] == 0)
+
+
+def _to_bf16_rne(x):
+    u = int(np.array([x], np.float32).view(np.uint32)[0])
+    return np.uint16((u + 0x7FFF + ((u >> 16) & 1)) >> 16)
+
+
+def test_quantize_rounding_ties(oracle_lib):
+    # generator quantiser (OCP rule) read back through the oracle's dequantiser;
+    # a 4.0 element pins the block's shared scale to 2^0, the probe is element 1
+    for inp, exp in _golden("e2m1_rounding.txt"):
+        blk = np.zeros(512, np.uint16)
+        blk[0::32] = _bf16(4.0)
+        blk[1] = _to_bf16_rne(float(inp))
+        bits = torch.from_numpy(blk.astype(np.int32)).to(torch.int16).view(1, 512)
+        codes, scales = G.mxfp4_quantize(bits)
+        assert int(scales[0, 0]) == 127
+        x = oracle_lib.dequant_rows(codes.numpy(), scales.numpy())[0]
+        assert x[1] == float(exp), (inp, x[1])
+
+
+def test_quantize_dequantize_roundtrip(oracle_lib):
+    # values already on the MXFP4 grid come back unchanged; others land on the
+    # nearest grid value (error <= half the local grid step, or clipped at 6*scale)
+    rng = np.random.default_rng(0)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    rows = 64
+    mags = grid[rng.integers(1, 8, size=(rows, 512))] * rng.choice([-1, 1], size=(rows, 512))
+    mags[:, ::32] = 6.0        # each block's amax = 6 -> scale 2^(2-2) * 2^e
+    exps = rng.integers(-8, 8, size=(rows, 16))
+    vals = mags * np.repeat(2.0 ** exps, 32, axis=1)
+    bits = torch.from_numpy(np.array([[_bf16(v) for v in r] for r in vals], np.uint16).astype(np.int32)).to(torch.int16)
+    codes, scales = G.mxfp4_quantize(bits)
+    back = oracle_lib.dequant_rows(codes.numpy(), scales.numpy())
+    assert np.array_equal(back, vals)
+    # generic N(0,1) data: error bound of round-to-nearest on the E2M1 grid
+    x = G.normal_bf16(0, 99, 0, rows * 512).view(rows, 512)
+    codes, scales = G.mxfp4_quantize(x)
+    back = oracle_lib.dequant_rows(codes.numpy(), scales.numpy())
+    xf = G.bf16_bits_to_float(x).double().numpy()
+    sc = np.repeat(np.array([[2.0 ** (int(e) - 127) for e in r] for r in scales.numpy()]), 32, axis=1)
+    r = np.abs(xf) / sc                       # in [0, 8): amax / scale lies in [4, 8)
+    step = np.where(r < 2, 0.5, np.where(r < 4, 1.0, 2.0)) * sc
+    inside = r <= 6
+    assert np.all(np.abs(back - xf)[inside] <= step[inside] / 2)
+    assert np.all(back[~inside] == np.sign(xf[~inside]) * 6 * sc[~inside])   # saturation
+    assert np.all(np.abs(back) <= 6 * sc)
+
+
+def test_kv_bytes_closed_form():
+    g = dict((k, int(v)) for k, v in _golden("kv_bytes.txt"))
+    per_entry = lambda d, grp: d // 2 + d // grp
+    assert per_entry(512, 16) == g["main_kv_e4m3_g16"]
+    assert per_entry(128, 32) == g["indexer_k_mxfp4"]
+    # three encoder Full sources at m = 2 and one decoder Full source at m = 1
+    main, idx = per_entry(512, 16), per_entry(128, 32)
+    assert Fraction(3 * (main + idx), 2) + (main + idx) == g["global_per_token"]
+    main4 = per_entry(512, 32)
+    assert main4 == g["main_kv_mxfp4"]
+    assert Fraction(3 * (main4 + idx), 2) + (main4 + idx) == g["global_per_token_mxfp4_main"]
+    # the layout the hot path reads: 256 code bytes + 16 scale bytes per entry
+    c = G.make_case("t", B=1, N=4)
+    assert c.kv_codes.shape[-1] + c.kv_scales.shape[-1] == main4
+
+
+# --------------------------------------------------------------- visibility
+
+def test_visibility_prefill_closed_form(oracle_lib):
+    g = dict((k, int(v)) for k, v in _golden("prefill_visibility.txt"))
+    nv = [oracle_lib.n_visible(p, 2, 34816) for p in range(65536, 65536 + 4096)]
+    assert nv[0] == g["first"] and nv[-1] == g["last"] and sum(nv) == g["sum"]
+
+
+def test_visibility_small_cases(oracle_lib):
+    # ratio 2: tokens {0,1} form entry 0, {2,3} entry 1 ...
+    assert [oracle_lib.n_visible(p, 2, 100) for p in range(6)] == [0, 1, 1, 2, 2, 3]
+    # ratio 1: the current token's own entry is complete
+    assert [oracle_lib.n_visible(p, 1, 100) for p in range(3)] == [1, 2, 3]
+    assert oracle_lib.n_visible(10 ** 9, 1, 100) == 100     # capped at N
+    assert oracle_lib.n_visible(-1, 4, 77) == 77            # no position: all visible
+
+
+# ------------------------------------------------------------------ indexer
+
+def _exact_score(q_bits, w, key_bits):
+    tot = Fraction(0)
+    for h in range(32):
+        d = sum(Fraction(_bf16_val(q_bits[h, c])) * Fraction(_bf16_val(key_bits[c])) for c in range(128))
+        tot += Fraction(float(w[h])) * max(d, Fraction(0))
+    return tot
+
+
+def test_index_score_integer_inputs_exact(oracle_lib):
+    # small integers: every fp64 step is exact, so the oracle must equal the
+    # integer formula sum_h w_h * max(0, sum_c q[h][c] * k[c]) exactly
+    rng = np.random.default_rng(1)
+    for trial in range(20):
+        qi = rng.integers(-3, 4, size=(32, 128))
+        ki = rng.integers(-3, 4, size=128)
+        wi = rng.integers(0, 5, size=32)
+        q = np.array([[_bf16(float(v)) for v in r] for r in qi], np.uint16)
+        k = np.array([_bf16(float(v)) for v in ki], np.uint16)
+        w = wi.astype(np.float32)
+        exp = sum(int(wi[h]) * max(0, int(np.dot(qi[h], ki))) for h in range(32))
+        assert oracle_lib.index_score(q, w, k) == exp
+
+
+def test_index_score_one_hot_weight(oracle_lib):
+    rng = np.random.default_rng(2)
+    qi = rng.integers(-3, 4, size=(32, 128))
+    ki = rng.integers(-3, 4, size=128)
+    q = np.array([[_bf16(float(v)) for v in r] for r in qi], np.uint16)
+    k = np.array([_bf16(float(v)) for v in ki], np.uint16)
+    for h in range(32):
+        w = np.zeros(32, np.float32)
+        w[h] = 1.0
+        assert oracle_lib.index_score(q, w, k) == max(0, int(np.dot(qi[h], ki)))
+    # q = -K on every head: all dot products <= 0 -> score 0
+    qn = np.array([[_bf16(-float(v)) for v in ki]] * 32, np.uint16)
+    assert oracle_lib.index_score(qn, np.ones(32, np.float32), k) == 0.0
+
+
+def test_index_score_real_inputs_vs_exact_rational(oracle_lib):
+    # N(0,1) bf16 inputs: within fp64 rounding of the exact rational value
+    for trial in range(4):
+        q = G.normal_bf16(7, 1000 + trial, 0, 32 * 128).view(32, 128).numpy().view(np.uint16)
+        k = G.normal_bf16(7, 2000 + trial, 0, 128).numpy().view(np.uint16)
+        w = G.uniform_f32(7, 3000 + trial, 0, 32).numpy()
+        exact = _exact_score(q, w, k)
+        scale = sum(abs(float(w[h])) * sum(abs(_bf16_val(q[h, c]) * _bf16_val(k[c])) for c in range(128))
+                    for h in range(32))
+        got = oracle_lib.index_score(q, w, k)
+        assert abs(Fraction(got) - exact) <= Fraction(scale) * Fraction(1, 2 ** 44)
+
+
+def test_index_power_of_two_weight_scaling(oracle_lib):
+    c = G.make_case("t", B=1, N=300, with_kv=False)
+    s1 = oracle_lib.index(c.q_idx.numpy().view(np.uint16), c.w_idx.numpy(), c.k_idx.numpy().view(np.uint16),
+                          c.q_pos.numpy(), 1, 1)
+    s2 = oracle_lib.index(c.q_idx.numpy().view(np.uint16), c.w_idx.numpy() * 8.0,
+                          c.k_idx.numpy().view(np.uint16), c.q_pos.numpy(), 1, 1)
+    assert np.array_equal(s1 * 8.0, s2)
+    assert np.array_equal(oracle_lib.topk(s1, c.q_pos.numpy(), 1, 64), oracle_lib.topk(s2, c.q_pos.numpy(), 1, 64))
+
+
+def test_index_batch_layout_and_visibility(oracle_lib):
+    # 2 sequences x 3 queries at ratio 2; each query uses its own sequence's keys
+    B, qps, N, ratio = 2, 3, 40, 2
+    T = B * qps
+    q = G.normal_bf16(3, 1, 0, T * 32 * 128).view(T, 32, 128).numpy().view(np.uint16)
+    w = G.uniform_f32(3, 2, 0, T * 32).view(T, 32).numpy()
+    k = G.normal_bf16(3, 3, 0, B * N * 128).view(B, N, 128).numpy().view(np.uint16)
+    pos = np.array([10, 41, 79, 0, 5, 200], np.int32)
+    s = oracle_lib.index(q, w, k, pos, ratio, qps)
+    for t in range(T):
+        nv = min(N, (int(pos[t]) + 1) // ratio)
+        for j in range(N):
+            if j < nv:
+                assert s[t, j] == oracle_lib.index_score(q[t], w[t], k[t // qps, j])
+            else:
+                assert s[t, j] == -np.inf
+
+
+# -------------------------------------------------------------------- top-k
+
+def _topk_reference(scores, n_vis, k):
+    order = sorted(range(n_vis), key=lambda s: (-scores[s], s))
+    sel = sorted(order[:k])
+    return sel + [-1] * (k - len(sel))
+
+
+def test_topk_equals_full_sort(oracle_lib):
+    rng = np.random.default_rng(3)
+    for n in [1, 7, 511, 512, 513, 2000]:
+        sc = rng.normal(size=n)
+        assert list(oracle_lib.topk_row(sc, n, 512)) == _topk_reference(list(sc), n, 512)
+
+
+def test_topk_ties_lower_index_wins(oracle_lib):
+    sc = np.zeros(1000)
+    sc[::3] = 1.0                  # 334 entries tie at 1.0
+    sc[500:] += 0.0                # equal values beyond
+    got = list(oracle_lib.topk_row(sc, 1000, 512))
+    exp = sorted([i for i in range(0, 1000, 3)] + [i for i in range(1000) if i % 3 != 0][:178])
+    assert got == exp
+    # all equal: the lowest 512 indices
+    assert list(oracle_lib.topk_row(np.full(2048, 3.5), 2048, 512)) == list(range(512))
+
+
+def test_topk_visibility_and_padding(oracle_lib):
+    rng = np.random.default_rng(4)
+    sc = rng.normal(size=(3, 700))
+    pos = np.array([99, 699, 2000], np.int32)
+    out = oracle_lib.topk(sc, pos, 1, 512)
+    assert list(out[0]) == list(range(100)) + [-1] * 412
+    assert list(out[1]) == _topk_reference(list(sc[1]), 700, 512)
+    assert list(out[2]) == _topk_reference(list(sc[2]), 700, 512)
+
+
+# ---------------------------------------------------------------- attention
+
+def _dense_attention(q, rows, scale, sink=None):
+    """Textbook softmax attention with key = value = rows (numpy, fp64)."""
+    z = scale * (q @ rows.T)                       # [H][n]
+    if sink is not None:
+        z = np.concatenate([z, np.asarray(sink)[:, None]], axis=1)
+        vals = np.concatenate([rows, np.zeros((1, rows.shape[1]))], axis=0)
+    else:
+        vals = rows
+    m = z.max(axis=1, keepdims=True)
+    p = np.exp(z - m)
+    out = (p / p.sum(axis=1, keepdims=True)) @ vals
+    lse = (m[:, 0] + np.log(p.sum(axis=1)))
+    return out, lse
+
+
+def _bits_to_f64(b):
+    return G.bf16_bits_to_float(torch.from_numpy(np.ascontiguousarray(b).view(np.int16))).double().numpy()
+
+
+def test_attend_dense_case_matches_textbook(oracle_lib):
+    # every entry selected (k >= N): sparse attention reduces to dense attention
+    c = G.make_case("t", B=2, N=40, q_per_seq=2, window=16, seed=5)
+    T = c.T
+    idx = np.tile(np.arange(40, dtype=np.int32), (T, 1))
+    idx = np.concatenate([idx, -np.ones((T, 8), np.int32)], axis=1)    # some empty slots
+    q = c.q[0].numpy().view(np.uint16)
+    swa = c.swa[0].numpy().view(np.uint16)
+    swa_end = np.array([16, 9, 16, 1], np.int32)
+    sink = np.linspace(-1, 2, 64)
+    for sk in (None, sink):
+        out, lse = oracle_lib.attend(q, c.kv_codes.numpy(), c.kv_scales.numpy(), idx, swa, swa_end, sk,
+                                     0.07, 2, 16)
+        for t in range(T):
+            b = t // 2
+            kv = oracle_lib.dequant_rows(c.kv_codes[b].numpy(), c.kv_scales[b].numpy())
+            e = int(swa_end[t])
+            win = _bits_to_f64(swa[b, max(0, e - 16):e])
+            rows = np.concatenate([kv, win], axis=0)
+            ref, rlse = _dense_attention(_bits_to_f64(q[t]), rows, 0.07, sk)
+            np.testing.assert_allclose(out[t], ref, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(lse[t], rlse, rtol=1e-12, atol=1e-12)
+
+
+def test_attend_degenerate_cases(oracle_lib):
+    c = G.make_case("t", B=1, N=16, window=4, seed=6)
+    q = c.q[0].numpy().view(np.uint16)
+    swa = c.swa[0].numpy().view(np.uint16)
+    kv = oracle_lib.dequant_rows(c.kv_codes[0].numpy(), c.kv_scales[0].numpy())
+    # one selected entry, no window: output = that entry, lse = its logit
+    idx = np.array([[-1, 5, -1, -1]], np.int32)
+    out, lse = oracle_lib.attend(q, c.kv_codes.numpy(), c.kv_scales.numpy(), idx, swa, np.array([0], np.int32),
+                                 None, 0.1, 1, 4)
+    assert np.allclose(out[0], np.broadcast_to(kv[5], (64, 512)), rtol=0, atol=0)
+    np.testing.assert_allclose(lse[0], 0.1 * (_bits_to_f64(q[0]) @ kv[5]), rtol=1e-13)
+    # the same entry selected several times: still that entry
+    idx = np.array([[5, 5, 5, 5]], np.int32)
+    out, _ = oracle_lib.attend(q, c.kv_codes.numpy(), c.kv_scales.numpy(), idx, swa, np.array([0], np.int32),
+                               None, 0.1, 1, 4)
+    np.testing.assert_allclose(out[0], np.broadcast_to(kv[5], (64, 512)), rtol=1e-14)
+    # a sink of -inf is the same as no sink
+    idx = np.array([[0, 3, 9, 15]], np.int32)
+    a, la = oracle_lib.attend(q, c.kv_codes.numpy(), c.kv_scales.numpy(), idx, swa, np.array([4], np.int32),
+                              None, 0.1, 1, 4)
+    b, lb = oracle_lib.attend(q, c.kv_codes.numpy(), c.kv_scales.numpy(), idx, swa, np.array([4], np.int32),
+                              np.full(64, -np.inf), 0.1, 1, 4)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    # output lies in the convex hull of the attended rows (per channel)
+    rows = np.concatenate([kv[[0, 3, 9, 15]], _bits_to_f64(swa[0, 0:4])], axis=0)
+    assert np.all(a >= rows.min(axis=0) - 1e-12) and np.all(a <= rows.max(axis=0) + 1e-12)
+
+
+def test_attend_window_bounds(oracle_lib):
+    # rows outside [end - W, end) must not matter: plant huge values there
+    c = G.make_case("t", B=1, N=8, window=4, seed=8)
+    c.S = 12
+    swa = G.normal_bf16(8, 77, 0, 12 * 512).view(1, 12, 512).numpy().view(np.uint16).copy()
+    q = c.q[0].numpy().view(np.uint16)
+    idx = np.array([[1, 2]], np.int32)
+    end = np.array([9], np.int32)
+    base, _ = oracle_lib.attend(q, c.kv_codes.numpy(), c.kv_scales.numpy(), idx, swa, end, None, 0.05, 1, 4)
+    planted = swa.copy()
+    planted[0, :5] = _bf16(100.0)
+    planted[0, 9:] = _bf16(-100.0)
+    got, _ = oracle_lib.attend(q, c.kv_codes.numpy(), c.kv_scales.numpy(), idx, planted, end, None, 0.05, 1, 4)
+    assert np.array_equal(base, got)
+    # and a row inside the window does matter
+    planted = swa.copy()
+    planted[0, 5] = _bf16(3.0)
+    got, _ = oracle_lib.attend(q, c.kv_codes.numpy(), c.kv_scales.numpy(), idx, planted, end, None, 0.05, 1, 4)
+    assert not np.array_equal(base, got)
+
+
+def test_reuse_is_attention_with_new_query(oracle_lib):
+    # Reuse (V4.1 report sec. 2.3.1) attends the Full layer's selection with
+    # its own query and window; with the Full layer's query it reproduces the
+    # Full layer's output, with another query the output changes.
+    c = G.make_case("t", B=1, N=64, window=8, n_layers=2, seed=9)
+    idx = np.arange(0, 64, 2, dtype=np.int32)[None, :]
+    args = (c.kv_codes.numpy(), c.kv_scales.numpy(), idx)
+    full, _ = oracle_lib.attend(c.q[0].numpy().view(np.uint16), *args, c.swa[0].numpy().view(np.uint16),
+                                c.swa_end.numpy(), None, 0.04, 1, 8)
+    again, _ = oracle_lib.attend(c.q[0].numpy().view(np.uint16), *args, c.swa[0].numpy().view(np.uint16),
+                                 c.swa_end.numpy(), None, 0.04, 1, 8)
+    other, _ = oracle_lib.attend(c.q[1].numpy().view(np.uint16), *args, c.swa[1].numpy().view(np.uint16),
+                                 c.swa_end.numpy(), None, 0.04, 1, 8)
+    assert np.array_equal(full, again) and not np.allclose(full, other)
