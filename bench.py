@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA2 hot path on one MI355X.
+
+One step = the whole Full-layer hot path over one decode batch of the
+long-context workload (4 sequences x 1,048,576 compressed entries, one query
+each): indexer scan -> exact top-512 -> FP4 gather/dequant + joint sparse and
+sliding-window attention.  Inputs are seeded synthetic tensors resident in HBM
+before timing starts.  Prints one JSON line.
+
+Also reported, outside the headline: per-stage times (HIP events on the
+launch stream), the Reuse-mode attention of three later layers over the same
+selection, the roofline of the dominant kernel (the indexer scan), and the CPU
+oracle timed on this host's cores on the same batch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+WORKLOADS = {
+    "long_decode": dict(B=4, N=1 << 20),
+    "batched_decode": dict(B=64, N=131072),
+    "tiny_decode": dict(B=1, N=2048),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the data-parallel path shards sequences across GPUs with no exchange, see DESIGN.md", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import compressed_sparse_attention_02_amd as csa
+    import csa2_gen as G
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = WORKLOADS[args.workload]
+    B, N = wl["B"], wl["N"]
+    print(f"[bench] generating {args.workload}: B={B} N={N}", file=sys.stderr, flush=True)
+    c = G.make_case(args.workload, B=B, N=N, n_layers=4, seed=0, device=dev)
+    T = c.T
+    q_idx = c.q_idx.view(torch.bfloat16)
+    k_idx = c.k_idx.view(torch.bfloat16)
+    q0 = c.q[0].view(torch.bfloat16)
+    swa0 = c.swa[0].view(torch.bfloat16)
+    q_re = c.q[1:].view(torch.bfloat16).contiguous()
+    swa_re = c.swa[1:].view(torch.bfloat16).contiguous()
+
+    scores = torch.empty((T, N), dtype=torch.float32, device=dev)
+    eps = torch.empty((T,), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, 512), dtype=torch.int32, device=dev)
+    out = torch.empty((T, 64, 512), dtype=torch.bfloat16, device=dev)
+    out_re = torch.empty((3, T, 64, 512), dtype=torch.bfloat16, device=dev)
+    ws_i = torch.empty(max(1, csa.index_workspace_bytes(T, 1, N)), dtype=torch.uint8, device=dev)
+    ws_t = torch.empty(max(1, csa.topk_workspace_bytes(T, N)), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(1, csa.attend_workspace_bytes(T)), dtype=torch.uint8, device=dev)
+    ws_r = torch.empty(max(1, csa.attend_workspace_bytes(T, n_layers=3)), dtype=torch.uint8, device=dev)
+    ws_a = ws_a if csa.attend_workspace_bytes(T) else None
+
+    def do_index():
+        csa.csa2_index(q_idx, c.w_idx, k_idx, c.q_pos, 1, 1, scores=scores, err_bound=eps, workspace=ws_i)
+
+    def do_topk():
+        csa.csa2_topk(scores, eps, q_idx, c.w_idx, k_idx, c.q_pos, 1, 1, indices=idx, workspace=ws_t)
+
+    def do_attend():
+        csa.csa2_attend_fp4(q0, c.kv_codes, c.kv_scales, idx, swa0, c.swa_end, None, c.softmax_scale, 1, 128,
+                            out=out, workspace=ws_a)
+
+    def do_reuse():
+        csa.csa2_reuse_attend(q_re, c.kv_codes, c.kv_scales, idx, swa_re, c.swa_end, None, c.softmax_scale, 1,
+                              128, out=out_re, workspace=ws_r)
+
+    def step():
+        do_index()
+        do_topk()
+        do_attend()
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- headline: K whole steps, wall clock between synchronisations
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    # ---- per-stage timing with events on the launch stream
+    def timed(fn, reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        return ts[len(ts) // 2], sum(ts) / len(ts)
+
+    reps = max(10, args.steps)
+    idx_med, idx_avg = timed(do_index, reps)
+    topk_med, _ = timed(do_topk, reps)
+    att_med, _ = timed(do_attend, reps)
+    do_reuse()
+    reuse_med, _ = timed(do_reuse, reps)
+
+    # dominant kernel: the indexer scan.  Algorithmic bytes per launch: each
+    # sequence's keys once (256 B/entry), q_idx (8 KiB) and w (128 B) per
+    # query, the fp32 score of every entry (4 B) and the bound (4 B).
+    idx_bytes = B * N * 256 + T * (8192 + 128 + 4) + T * N * 4
+    achieved = idx_bytes / (idx_avg * 1e-6) / 1e9
+    step_bytes = T * G.algorithmic_bytes_decode_query(N)
+
+    # plain copy bandwidth of this machine (context for the roofline fraction)
+    x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    y.copy_(x)
+    cp_med, _ = timed(lambda: y.copy_(x), 10)
+    copy_gbps = 2 * (1 << 30) / (cp_med * 1e-6) / 1e9
+    if args.copy_calibration:
+        y.copy_(x)
+    del x, y
+
+    line = {
+        "metric": "decode queries/s + achieved HBM GB/s (% peak), CSA2 top-512 FP4 attn at 1 GPU",
+        "value": T / (ms_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "entries_per_seq": N, "queries_per_seq": 1,
+                   "indexer": "32x128 bf16", "topk": 512, "heads": 64, "head_dim": 512, "window": 128,
+                   "main_kv": "MXFP4 E2M1+E8M0/32", "parallelism": "none (1 GPU)"},
+        "step_hbm_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "step_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "roofline": {"kernel": "idx_scan_kernel (csa2_index)", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": idx_bytes, "avg_launch_us": idx_avg},
+        "stages_us": {"index": idx_med, "topk": topk_med, "attend": att_med, "reuse_3_layers": reuse_med},
+        "copy_GBps": copy_gbps,
+    }
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(c, G)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(c, G):
+    """The oracle (as is) on this host's cores, on the same 4-query batch."""
+    import numpy as np
+
+    import oracle
+
+    def u16(t):
+        return np.ascontiguousarray(t.cpu().view(__import__("torch").int16).numpy().view(np.uint16))
+
+    q_idx, w, k = u16(c.q_idx), c.w_idx.cpu().numpy(), u16(c.k_idx)
+    q_pos = c.q_pos.cpu().numpy()
+    q, swa = u16(c.q[0]), u16(c.swa[0])
+    codes, scales, swa_end = c.kv_codes.cpu().numpy(), c.kv_scales.cpu().numpy(), c.swa_end.cpu().numpy()
+    oracle.lib()
+    t0 = time.perf_counter()
+    sc = oracle.index(q_idx, w, k, q_pos, c.ratio, c.q_per_seq)
+    sel = oracle.topk(sc, q_pos, c.ratio, c.k)
+    oracle.attend(q, codes, scales, sel, swa, swa_end, None, c.softmax_scale, c.q_per_seq, c.window)
+    dt = time.perf_counter() - t0
+    return {"value": c.T / dt, "unit": "queries/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"the full {c.T}-query step of the same workload (index + top-512 + attention), "
+                      f"{dt:.1f} s wall on the host"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

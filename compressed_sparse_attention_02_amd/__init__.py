@@ -1,0 +1,243 @@
+"""CSA2 hot path on MI355X (gfx950): Python binding of libcsa2.so.
+
+Thin ctypes layer over the C ABI declared in include/csa2.h: it checks tensor
+devices, dtypes and shapes, allocates outputs and workspaces with torch (device
+memory only) and passes raw pointers plus the current HIP stream.  Every step
+of the computation runs in the library's HIP kernels; there is no fallback.
+The function names match the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "Csa2Error", "lib", "library_path", "csa2_index", "csa2_topk", "csa2_attend_fp4", "csa2_reuse_attend",
+    "index_workspace_bytes", "topk_workspace_bytes", "topk_min_workspace_bytes", "attend_workspace_bytes",
+    "IDX_HEADS", "IDX_DIM", "HEADS", "DIM", "TOPK", "MAX_WINDOW", "MAX_LAYERS",
+]
+
+IDX_HEADS, IDX_DIM, HEADS, DIM, TOPK, MAX_WINDOW, MAX_LAYERS = 32, 128, 64, 512, 512, 128, 8
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libcsa2.so")
+_lib = None
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+_SIGNATURES = {
+    "csa2_status_string": ([_i32], ctypes.c_char_p),
+    "csa2_version": ([], ctypes.c_char_p),
+    "csa2_index_workspace_bytes": ([_i32, _i32, _i64], _sz),
+    "csa2_index": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _sz, _vp], _i32),
+    "csa2_topk_workspace_bytes": ([_i32, _i64, _i32], _sz),
+    "csa2_topk_min_workspace_bytes": ([_i32, _i64, _i32], _sz),
+    "csa2_topk": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp, _vp, _sz, _vp], _i32),
+    "csa2_attend_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
+    "csa2_attend_fp4": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp,
+                         _vp, _sz, _vp], _i32),
+    "csa2_reuse_attend": ([_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i64, _i32, _i32, _i32, _vp,
+                           _vp, _vp, _sz, _vp], _i32),
+}
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib().csa2_status_string(status).decode()} ({status})")
+
+
+def lib():
+    """Load libcsa2.so (built in place); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is not built; run `python -m compressed_sparse_attention_02_amd.build`"
+                               " or __graft_entry__.build()")
+        L = ctypes.CDLL(library_path)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes, fn.restype = args, res
+        _lib = L
+    return _lib
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check(t, name, shape, elem_size=None, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if elem_size is not None and t.element_size() != elem_size:
+        raise TypeError(f"{name} must have {elem_size}-byte elements (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _ws(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return workspace
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace too small: {workspace.numel() * workspace.element_size()} < {nbytes}")
+    return workspace
+
+
+def _nbytes(ws) -> int:
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
+def _raise(status, where):
+    if status != 0:
+        raise Csa2Error(status, where)
+
+
+def index_workspace_bytes(T: int, q_per_seq: int, N: int) -> int:
+    return lib().csa2_index_workspace_bytes(T, q_per_seq, N)
+
+
+def topk_workspace_bytes(T: int, N: int, k: int = TOPK) -> int:
+    return lib().csa2_topk_workspace_bytes(T, N, k)
+
+
+def topk_min_workspace_bytes(T: int, N: int, k: int = TOPK) -> int:
+    return lib().csa2_topk_min_workspace_bytes(T, N, k)
+
+
+def attend_workspace_bytes(T: int, k: int = TOPK, window: int = MAX_WINDOW, n_layers: int = 1) -> int:
+    return lib().csa2_attend_workspace_bytes(T, k, window, n_layers)
+
+
+def csa2_index(q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, scores=None, err_bound=None,
+               workspace=None):
+    """Indexer scores.  q_idx bf16 [T][32][128], w_idx fp32 [T][32], k_idx bf16 [B][N][128],
+    q_pos int32 [T] or None.  Returns (scores fp32 [T][N], err_bound fp32 [T])."""
+    T = q_idx.shape[0]
+    B, N = k_idx.shape[0], k_idx.shape[1]
+    dev = q_idx.device
+    _check(q_idx, "q_idx", (T, IDX_HEADS, IDX_DIM), elem_size=2)
+    _check(w_idx, "w_idx", (T, IDX_HEADS), dtype=torch.float32, device=dev)
+    _check(k_idx, "k_idx", (B, N, IDX_DIM), elem_size=2, device=dev)
+    if q_pos is not None:
+        _check(q_pos, "q_pos", (T,), dtype=torch.int32, device=dev)
+    if B * q_per_seq != T:
+        raise ValueError(f"T={T} must equal B*q_per_seq={B}*{q_per_seq}")
+    if scores is None:
+        scores = torch.empty((T, N), dtype=torch.float32, device=dev)
+    if err_bound is None:
+        err_bound = torch.empty((T,), dtype=torch.float32, device=dev)
+    _check(scores, "scores", (T, N), dtype=torch.float32, device=dev)
+    _check(err_bound, "err_bound", (T,), dtype=torch.float32, device=dev)
+    nbytes = index_workspace_bytes(T, q_per_seq, N)
+    workspace = _ws(nbytes, dev, workspace)
+    st = lib().csa2_index(_p(q_idx), _p(w_idx), _p(k_idx), _p(q_pos), ratio, T, q_per_seq, N, _p(scores),
+                          _p(err_bound), _p(workspace), _nbytes(workspace), _stream(q_idx))
+    _raise(st, "csa2_index")
+    return scores, err_bound
+
+
+def csa2_topk(scores, err_bound, q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, k=TOPK, indices=None,
+              workspace=None):
+    """Exact top-k (ascending indices, -1 padded) -> int32 [T][k]."""
+    T, N = scores.shape
+    B = k_idx.shape[0]
+    dev = scores.device
+    _check(scores, "scores", (T, N), dtype=torch.float32)
+    _check(err_bound, "err_bound", (T,), dtype=torch.float32, device=dev)
+    _check(q_idx, "q_idx", (T, IDX_HEADS, IDX_DIM), elem_size=2, device=dev)
+    _check(w_idx, "w_idx", (T, IDX_HEADS), dtype=torch.float32, device=dev)
+    _check(k_idx, "k_idx", (B, N, IDX_DIM), elem_size=2, device=dev)
+    if q_pos is not None:
+        _check(q_pos, "q_pos", (T,), dtype=torch.int32, device=dev)
+    if indices is None:
+        indices = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _check(indices, "indices", (T, k), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = _ws(topk_workspace_bytes(T, N, k), dev, None)
+    elif _nbytes(workspace) < topk_min_workspace_bytes(T, N, k):
+        raise ValueError("workspace below csa2_topk_min_workspace_bytes")
+    st = lib().csa2_topk(_p(scores), _p(err_bound), _p(q_idx), _p(w_idx), _p(k_idx), _p(q_pos), ratio, T,
+                         q_per_seq, N, k, _p(indices), _p(workspace), _nbytes(workspace), _stream(scores))
+    _raise(st, "csa2_topk")
+    return indices
+
+
+def _attend_common(q_shape_tail, q, kv_fp4, kv_scale, indices, swa, swa_end, sink):
+    T = indices.shape[0]
+    k = indices.shape[1]
+    B, N = kv_fp4.shape[0], kv_fp4.shape[1]
+    dev = q.device
+    _check(q, "q", (*q_shape_tail, T, HEADS, DIM), elem_size=2)
+    _check(kv_fp4, "kv_fp4", (B, N, DIM // 2), dtype=torch.uint8, device=dev)
+    _check(kv_scale, "kv_scale", (B, N, DIM // 32), dtype=torch.uint8, device=dev)
+    _check(indices, "indices", (T, k), dtype=torch.int32, device=dev)
+    S = swa.shape[-2]
+    _check(swa, "swa", (*q_shape_tail, B, S, DIM), elem_size=2, device=dev)
+    _check(swa_end, "swa_end", (T,), dtype=torch.int32, device=dev)
+    if sink is not None:
+        _check(sink, "sink", (*q_shape_tail, HEADS), dtype=torch.float32, device=dev)
+    return T, k, B, N, S, dev
+
+
+def csa2_attend_fp4(q, kv_fp4, kv_scale, indices, swa, swa_end, sink=None, softmax_scale=DIM ** -0.5,
+                    q_per_seq=1, window=MAX_WINDOW, out=None, lse=None, want_lse=False, workspace=None):
+    """Joint sparse + window attention.  q bf16 [T][64][512]; kv_fp4 uint8 [B][N][256];
+    kv_scale uint8 [B][N][16]; indices int32 [T][k]; swa bf16 [B][S][512]; swa_end int32 [T];
+    sink fp32 [64] or None.  Returns out bf16 [T][64][512] (and lse fp32 [T][64] if requested)."""
+    T, k, B, N, S, dev = _attend_common((), q, kv_fp4, kv_scale, indices, swa, swa_end, sink)
+    if B * q_per_seq != T:
+        raise ValueError(f"T={T} must equal B*q_per_seq={B}*{q_per_seq}")
+    if out is None:
+        out = torch.empty((T, HEADS, DIM), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", (T, HEADS, DIM), elem_size=2, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((T, HEADS), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", (T, HEADS), dtype=torch.float32, device=dev)
+    nbytes = attend_workspace_bytes(T, k, window, 1)
+    workspace = _ws(nbytes, dev, workspace)
+    st = lib().csa2_attend_fp4(_p(q), _p(kv_fp4), _p(kv_scale), _p(indices), _p(swa), _p(swa_end), _p(sink),
+                               float(softmax_scale), T, q_per_seq, N, S, window, k, _p(out), _p(lse),
+                               _p(workspace), _nbytes(workspace), _stream(q))
+    _raise(st, "csa2_attend_fp4")
+    return (out, lse) if (want_lse or lse is not None) else out
+
+
+def csa2_reuse_attend(q, kv_fp4, kv_scale, indices, swa, swa_end, sink=None, softmax_scale=DIM ** -0.5,
+                      q_per_seq=1, window=MAX_WINDOW, out=None, lse=None, want_lse=False, workspace=None):
+    """Reuse-mode attention of L layers over one index list / KV.  q bf16 [L][T][64][512];
+    swa bf16 [L][B][S][512]; sink fp32 [L][64] or None.  Returns out bf16 [L][T][64][512]."""
+    L = q.shape[0]
+    T, k, B, N, S, dev = _attend_common((L,), q, kv_fp4, kv_scale, indices, swa, swa_end, sink)
+    if B * q_per_seq != T:
+        raise ValueError(f"T={T} must equal B*q_per_seq={B}*{q_per_seq}")
+    if out is None:
+        out = torch.empty((L, T, HEADS, DIM), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", (L, T, HEADS, DIM), elem_size=2, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((L, T, HEADS), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", (L, T, HEADS), dtype=torch.float32, device=dev)
+    nbytes = attend_workspace_bytes(T, k, window, L)
+    workspace = _ws(nbytes, dev, workspace)
+    st = lib().csa2_reuse_attend(L, _p(q), _p(kv_fp4), _p(kv_scale), _p(indices), _p(swa), _p(swa_end), _p(sink),
+                                 float(softmax_scale), T, q_per_seq, N, S, window, k, _p(out), _p(lse),
+                                 _p(workspace), _nbytes(workspace), _stream(q))
+    _raise(st, "csa2_reuse_attend")
+    return (out, lse) if (want_lse or lse is not None) else out

@@ -1,0 +1,461 @@
+// Joint sparse + sliding-window attention over the FP4 main-KV cache
+// (csa2_attend_fp4) and its cross-layer Reuse form (csa2_reuse_attend).
+//
+// What is computed (see csa2.h): for query t and head h, one softmax over the
+// union of the selected main-KV rows (dequantised MXFP4, report sec. 2.4.4)
+// and the window rows (report sec. 3.2.2), with key = value = the row
+// (shared-KV MQA, gzher.com reading sec. 4.1) and an optional sink in the
+// denominator (gzher.com reading sec. 4.3).  Reuse layers (report sec. 2.3.1)
+// attend over the same rows with their own query and window.
+//
+// Layout of the work.  The rows of one query are processed in chunks of 32
+// (16 chunks of selected rows + up to 4 window chunks).  A chunk is gathered
+// and dequantised once into LDS in two bf16 copies:
+//   X  [32][512]  (row-major, 16-byte row pad)   -> A operand of S^T = X Q^T
+//   XT [512][32]  (transposed, 16-byte row pad)  -> A operand of O^T += X^T P^T
+// Each of the 4 waves owns 16 heads.  With heads on the N axis of both
+// products (v_mfma_f32_16x16x32_bf16), the accumulator of S^T already holds
+// P^T in the B-operand layout of the second product (the 32 rows of a chunk
+// are stored in XT in the matching permuted order), and the per-head softmax
+// statistics live in the same lanes as that head's O^T accumulators, so no
+// cross-lane shuffles are needed except the 4-lane row reductions.
+// Chunks of one query are split over work items (split-K); partial (max,
+// sum, O) are merged by a combine kernel.  For Reuse with several layers,
+// each selected-row chunk is staged once and used by every layer.
+#include "csa2_common.h"
+
+namespace csa2 {
+
+constexpr int kAttnThreads = 256;
+constexpr int kChunk = 32;
+constexpr int kXStride = kDim + 8;      // bf16 elements per X row (1040 B)
+constexpr int kXTStride = kChunk + 8;   // bf16 elements per XT row (80 B)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct AttnArgs {
+  const uint16_t* q;        // [L][T][64][512]
+  const uint8_t* kv_fp4;    // [B][N][256]
+  const uint8_t* kv_scale;  // [B][N][16]
+  const int32_t* indices;   // [T][k]
+  const uint16_t* swa;      // [L][B][S][512]
+  const int32_t* swa_end;   // [T]
+  const float* sink;        // [L][64] or null
+  float scale_log2;         // softmax_scale * log2(e)
+  int T, q_per_seq, B, S, window, k, L;
+  int64_t N;
+  int n_main, n_swa;        // chunks of selected rows / of window rows
+  int cpw;                  // chunks per work item (single layer)
+  int n_items;              // work items per query
+  int n_slots;              // partial slots per (layer, query)
+  uint16_t* out;            // [L][T][64][512]
+  float* lse;               // [L][T][64] or null
+  float* part_o;            // [L][T][n_slots][64][512]
+  float* part_ml;           // [L][T][n_slots][64][2]  (max in log2 units, sum)
+};
+
+struct AttnShared {
+  uint16_t X[kChunk * kXStride];
+  uint16_t XT[kDim * kXTStride];
+  int valid[kChunk];
+};
+
+// E2M1 magnitude (OCP MX) of a 3-bit code as an fp32 bit pattern.
+__device__ __forceinline__ uint32_t e2m1_bits(uint32_t c) {
+  const uint32_t e = c >> 1, m = c & 1u;
+  return e == 0 ? (m ? 0x3F000000u : 0u) : (((126u + e) << 23) | (m << 22));
+}
+
+// 8 FP4 codes (one 32-bit word, element 2i in the low nibble of byte i) times
+// the block scale 2^(s-127) -> 8 bf16 bit patterns (exact: every such value
+// has at most two significant bits).
+__device__ __forceinline__ void dequant8(uint32_t codes, uint32_t sbyte, uint32_t* o) {
+  const float sc = __uint_as_float(sbyte == 0 ? 0x00400000u : (sbyte << 23));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c = (codes >> (4 * i)) & 15u;
+    const float v = __uint_as_float(e2m1_bits(c & 7u)) * sc;
+    o[i] = (__float_as_uint(v) >> 16) | ((c & 8u) << 12);
+  }
+}
+
+// Stage chunk `c` of query t (layer `layer` for window chunks) into LDS.
+// Thread (g = wave, d = lane) loads 8 rows x 8 channels: rows {4g..4g+3,
+// 16+4g..16+4g+3} (the 8 rows that form XT column group g), channels 8d..8d+7.
+__device__ void stage_chunk(const AttnArgs& a, AttnShared& sh, int t, int b, int c, int layer) {
+  const int g = threadIdx.x >> 6, d = threadIdx.x & 63;
+  uint32_t v[8][4];
+  int okr[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int e = r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4);
+    bool ok = false;
+    if (c < a.n_main) {
+      const int j = c * kChunk + e;
+      const int32_t idx = j < a.k ? a.indices[(size_t)t * a.k + j] : -1;
+      if (idx >= 0) {
+        ok = true;
+        const size_t rowid = (size_t)b * a.N + idx;
+        const uint32_t codes = *reinterpret_cast<const uint32_t*>(a.kv_fp4 + rowid * 256 + 4 * d);
+        const uint32_t sbyte = a.kv_scale[rowid * 16 + (d >> 2)];
+        uint32_t o[8];
+        dequant8(codes, sbyte, o);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[r][i] = o[2 * i] | (o[2 * i + 1] << 16);
+      }
+    } else {
+      const int we = a.swa_end[t];
+      const int ws = we - a.window > 0 ? we - a.window : 0;
+      const int row = ws + (c - a.n_main) * kChunk + e;
+      if (row < we) {
+        ok = true;
+        const uint4 x = *reinterpret_cast<const uint4*>(
+            a.swa + (((size_t)layer * a.B + b) * a.S + row) * kDim + 8 * d);
+        v[r][0] = x.x; v[r][1] = x.y; v[r][2] = x.z; v[r][3] = x.w;
+      }
+    }
+    if (!ok) { v[r][0] = v[r][1] = v[r][2] = v[r][3] = 0u; }
+    okr[r] = ok;
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int e = r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4);
+    *reinterpret_cast<uint4*>(&sh.X[e * kXStride + 8 * d]) = make_uint4(v[r][0], v[r][1], v[r][2], v[r][3]);
+    if (d == 0) sh.valid[e] = okr[r];
+  }
+  // transposed copy: XT[8d + i][8g + r] = v[r][i] (channel 8d+i of row r of this group)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t lo = (v[2 * p][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      const uint32_t hi = (v[2 * p + 1][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      w[p] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint4*>(&sh.XT[(8 * d + i) * kXTStride + 8 * g]) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+struct HeadState {
+  floatx4 o[32];   // O^T: o[mb][i] = O[head][16*mb + 4*g + i]
+  float m;         // running max (log2 units)
+  float l;         // running sum (this lane's rows only)
+};
+
+__device__ __forceinline__ void load_q(const AttnArgs& a, int layer, int t, bf16x8* qb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int head = 16 * wave + (lane & 15), g = lane >> 4;
+  const uint4* qp = reinterpret_cast<const uint4*>(a.q + (((size_t)layer * a.T + t) * kHeads + head) * kDim + 8 * g);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) qb[j] = as_bf16x8(qp[4 * j]);  // channels 32j + 8g .. +8
+}
+
+__device__ __forceinline__ void state_init(HeadState& st) {
+#pragma unroll
+  for (int mb = 0; mb < 32; ++mb) st.o[mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+}
+
+// Attend the staged chunk with one query (qb) and fold it into st.
+__device__ __forceinline__ void attend_chunk(const AttnArgs& a, const AttnShared& sh, const bf16x8* qb,
+                                             HeadState& st) {
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const bf16x8 x0 = *reinterpret_cast<const bf16x8*>(&sh.X[r16 * kXStride + 32 * j + 8 * g]);
+    const bf16x8 x1 = *reinterpret_cast<const bf16x8*>(&sh.X[(16 + r16) * kXStride + 32 * j + 8 * g]);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, qb[j], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, qb[j], s1, 0, 0, 0);
+  }
+  // s0[i]: row 4g+i, s1[i]: row 16+4g+i, both for head (lane & 15)
+  float z[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    z[i] = sh.valid[4 * g + i] ? s0[i] * a.scale_log2 : -INFINITY;
+    z[4 + i] = sh.valid[16 + 4 * g + i] ? s1[i] * a.scale_log2 : -INFINITY;
+  }
+  float cm = z[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) cm = fmaxf(cm, z[i]);
+  cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+  cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+  const float mn = fmaxf(st.m, cm);
+  if (mn == -INFINITY) return;  // nothing valid so far for this head (uniform per head)
+  const float alpha = exp2f(st.m - mn);  // st.m == -inf -> 0
+  uint32_t pb[4];
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p0 = exp2f(z[2 * i] - mn), p1 = exp2f(z[2 * i + 1] - mn);
+    psum += p0 + p1;
+    pb[i] = f32_to_bf16_rne(p0) | (f32_to_bf16_rne(p1) << 16);
+  }
+  st.l = st.l * alpha + psum;
+  st.m = mn;
+  bf16x8 pv;
+  __builtin_memcpy(&pv, pb, 16);
+#pragma unroll
+  for (int mb = 0; mb < 32; ++mb) {
+    st.o[mb] *= alpha;
+    const bf16x8 xa = *reinterpret_cast<const bf16x8*>(&sh.XT[(16 * mb + r16) * kXTStride + 8 * g]);
+    st.o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, pv, st.o[mb], 0, 0, 0);
+  }
+}
+
+// Write the final output of one (layer, query) from a complete state.
+__device__ void write_final(const AttnArgs& a, const HeadState& st, int layer, int t) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int head = 16 * wave + (lane & 15), g = lane >> 4;
+  float l = st.l;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  float m = st.m;
+  float den = l, f = 1.f;
+  if (a.sink) {
+    const float sk = a.sink[(size_t)layer * kHeads + head] * kLog2e;
+    const float M = fmaxf(m, sk);
+    if (M != -INFINITY) {
+      f = (m == -INFINITY) ? 0.f : exp2f(m - M);
+      den = l * f + exp2f(sk - M);
+      m = M;
+    }
+  }
+  const float inv = (m == -INFINITY || den == 0.f) ? 0.f : f / den;
+  uint16_t* op = a.out + (((size_t)layer * a.T + t) * kHeads + head) * kDim + 4 * g;
+#pragma unroll
+  for (int mb = 0; mb < 32; ++mb) {
+    const uint32_t w0 = f32_to_bf16_rne(st.o[mb][0] * inv) | (f32_to_bf16_rne(st.o[mb][1] * inv) << 16);
+    const uint32_t w1 = f32_to_bf16_rne(st.o[mb][2] * inv) | (f32_to_bf16_rne(st.o[mb][3] * inv) << 16);
+    *reinterpret_cast<uint2*>(op + 16 * mb) = make_uint2(w0, w1);
+  }
+  if (a.lse && g == 0)
+    a.lse[((size_t)layer * a.T + t) * kHeads + head] = (m == -INFINITY) ? -INFINITY : (m + log2f(den)) * kLn2;
+}
+
+__device__ void write_partial(const AttnArgs& a, const HeadState& st, int layer, int t, int slot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int head = 16 * wave + (lane & 15), g = lane >> 4;
+  float l = st.l;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  const size_t base = (((size_t)layer * a.T + t) * a.n_slots + slot) * kHeads + head;
+  float* op = a.part_o + base * kDim + 4 * g;
+#pragma unroll
+  for (int mb = 0; mb < 32; ++mb) *reinterpret_cast<floatx4*>(op + 16 * mb) = st.o[mb];
+  if (g == 0) {
+    a.part_ml[base * 2 + 0] = st.m;
+    a.part_ml[base * 2 + 1] = l;
+  }
+}
+
+// grid (n_items, T).  Work item i of query t:
+//   L == 1: chunks [i*cpw, min((i+1)*cpw, n_main+n_swa)); if n_items == 1 the
+//           result is final, otherwise it is partial slot i.
+//   L  > 1: i < n_main: selected-row chunk i for every layer (slot i);
+//           otherwise window chunk j of layer l, i = n_main + l*n_swa + j
+//           (slot n_main + j of layer l).
+__global__ __launch_bounds__(kAttnThreads) void attend_kernel(AttnArgs a) {
+  __shared__ AttnShared sh;
+  const int item = blockIdx.x, t = blockIdx.y;
+  const int b = t / a.q_per_seq;
+  bf16x8 qb[16];
+  HeadState st;
+  if (a.L == 1) {
+    const int n_chunks = a.n_main + a.n_swa;
+    const int c0 = item * a.cpw;
+    const int c1 = c0 + a.cpw < n_chunks ? c0 + a.cpw : n_chunks;
+    load_q(a, 0, t, qb);
+    state_init(st);
+    for (int c = c0; c < c1; ++c) {
+      stage_chunk(a, sh, t, b, c, 0);
+      __syncthreads();
+      attend_chunk(a, sh, qb, st);
+      __syncthreads();
+    }
+    if (a.n_items == 1) write_final(a, st, 0, t);
+    else write_partial(a, st, 0, t, item);
+  } else if (item < a.n_main) {
+    stage_chunk(a, sh, t, b, item, 0);
+    __syncthreads();
+    for (int l = 0; l < a.L; ++l) {
+      load_q(a, l, t, qb);
+      state_init(st);
+      attend_chunk(a, sh, qb, st);
+      write_partial(a, st, l, t, item);
+    }
+  } else {
+    const int rest = item - a.n_main;
+    const int l = rest / a.n_swa, j = rest % a.n_swa;
+    load_q(a, l, t, qb);
+    state_init(st);
+    stage_chunk(a, sh, t, b, a.n_main + j, l);
+    __syncthreads();
+    attend_chunk(a, sh, qb, st);
+    write_partial(a, st, l, t, a.n_main + j);
+  }
+}
+
+// Merge the partial slots of each (layer, query): grid (T, L), 256 threads.
+__global__ __launch_bounds__(256) void attend_combine_kernel(AttnArgs a) {
+  const int t = blockIdx.x, layer = blockIdx.y;
+  __shared__ float inv_den[64], mstar[64];
+  const size_t base = ((size_t)layer * a.T + t) * a.n_slots;
+  const int tid = threadIdx.x;
+  if (tid < kHeads) {
+    const int h = tid;
+    float M = -INFINITY;
+    for (int s = 0; s < a.n_slots; ++s) M = fmaxf(M, a.part_ml[((base + s) * kHeads + h) * 2]);
+    float sk = -INFINITY;
+    if (a.sink) { sk = a.sink[(size_t)layer * kHeads + h] * kLog2e; M = fmaxf(M, sk); }
+    float den = 0.f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < a.n_slots; ++s) {
+        const float ms = a.part_ml[((base + s) * kHeads + h) * 2];
+        if (ms != -INFINITY) den += a.part_ml[((base + s) * kHeads + h) * 2 + 1] * exp2f(ms - M);
+      }
+      if (a.sink) den += exp2f(sk - M);
+    }
+    mstar[h] = M;
+    inv_den[h] = (M == -INFINITY || den == 0.f) ? 0.f : 1.f / den;
+    if (a.lse) a.lse[((size_t)layer * a.T + t) * kHeads + h] = (M == -INFINITY) ? -INFINITY : (M + log2f(den)) * kLn2;
+  }
+  __syncthreads();
+  // each thread: 4 consecutive channels of one head per step; 64 heads x 128 quads
+  for (int qd = tid; qd < kHeads * (kDim / 4); qd += 256) {
+    const int h = qd / (kDim / 4), c4 = qd % (kDim / 4);
+    const float M = mstar[h];
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+      for (int s = 0; s < a.n_slots; ++s) {
+        const float ms = a.part_ml[((base + s) * kHeads + h) * 2];
+        if (ms == -INFINITY) continue;
+        const float f = exp2f(ms - M);
+        const floatx4 o = *reinterpret_cast<const floatx4*>(a.part_o + ((base + s) * kHeads + h) * kDim + 4 * c4);
+        acc += o * f;
+      }
+    }
+    const float iv = inv_den[h];
+    uint16_t* op = a.out + (((size_t)layer * a.T + t) * kHeads + h) * kDim + 4 * c4;
+    const uint32_t w0 = f32_to_bf16_rne(acc[0] * iv) | (f32_to_bf16_rne(acc[1] * iv) << 16);
+    const uint32_t w1 = f32_to_bf16_rne(acc[2] * iv) | (f32_to_bf16_rne(acc[3] * iv) << 16);
+    *reinterpret_cast<uint2*>(op) = make_uint2(w0, w1);
+  }
+}
+
+struct AttendPlan {
+  int n_main, n_swa, cpw, n_items, n_slots;
+};
+
+static AttendPlan attend_plan(int32_t T, int32_t k, int32_t window, int32_t L) {
+  AttendPlan p;
+  p.n_main = (k + kChunk - 1) / kChunk;
+  p.n_swa = (window + kChunk - 1) / kChunk;
+  const int n_chunks = p.n_main + p.n_swa;
+  if (L == 1) {
+    // enough work items to cover the GPU (~1024 blocks), merged back by the combine
+    int64_t want = (1024 + T - 1) / T;
+    if (want > n_chunks) want = n_chunks;
+    if (want < 1) want = 1;
+    p.cpw = (int)((n_chunks + want - 1) / want);
+    p.n_items = (n_chunks + p.cpw - 1) / p.cpw;
+    p.n_slots = p.n_items;
+  } else {
+    p.cpw = 1;
+    p.n_items = p.n_main + L * p.n_swa;
+    p.n_slots = n_chunks;
+  }
+  return p;
+}
+
+static size_t attend_ws_bytes(int32_t T, const AttendPlan& p, int32_t L) {
+  if (p.n_items == 1 && L == 1) return 0;
+  const size_t slots = (size_t)L * T * p.n_slots;
+  return align_up(slots * kHeads * kDim * sizeof(float), 256) + align_up(slots * kHeads * 2 * sizeof(float), 256);
+}
+
+static csa2_status attend_launch(int32_t L, const void* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
+                                 const int32_t* indices, const void* swa, const int32_t* swa_end,
+                                 const float* sink, float softmax_scale, int32_t T, int32_t q_per_seq,
+                                 int64_t N, int32_t S, int32_t window, int32_t k, void* out, float* lse,
+                                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!q || !kv_fp4 || !kv_scale || !indices || !swa || !swa_end || !out) return CSA2_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kv_fp4) || !aligned16(kv_scale) || !aligned16(indices) || !aligned16(swa) ||
+      !aligned16(swa_end) || !aligned16(out) || (sink && !aligned16(sink)) || (lse && !aligned16(lse)))
+    return CSA2_ERR_INVALID_ARG;
+  if (T < 1 || q_per_seq < 1 || T % q_per_seq != 0 || N < 1 || S < 1) return CSA2_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.f) || !(softmax_scale < INFINITY)) return CSA2_ERR_INVALID_ARG;
+  if (k != kTopK || window < 1 || window > CSA2_MAX_WINDOW || L < 1 || L > CSA2_MAX_LAYERS || T > 65535 ||
+      N >= ((int64_t)1 << 31))
+    return CSA2_ERR_UNSUPPORTED;
+  const AttendPlan p = attend_plan(T, k, window, L);
+  const size_t need = attend_ws_bytes(T, p, L);
+  if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
+  AttnArgs a;
+  a.q = (const uint16_t*)q;
+  a.kv_fp4 = kv_fp4;
+  a.kv_scale = kv_scale;
+  a.indices = indices;
+  a.swa = (const uint16_t*)swa;
+  a.swa_end = swa_end;
+  a.sink = sink;
+  a.scale_log2 = softmax_scale * kLog2e;
+  a.T = T;
+  a.q_per_seq = q_per_seq;
+  a.B = T / q_per_seq;
+  a.S = S;
+  a.window = window;
+  a.k = k;
+  a.L = L;
+  a.N = N;
+  a.n_main = p.n_main;
+  a.n_swa = p.n_swa;
+  a.cpw = p.cpw;
+  a.n_items = p.n_items;
+  a.n_slots = p.n_slots;
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  const size_t slots = (size_t)L * T * p.n_slots;
+  a.part_o = need ? (float*)workspace : nullptr;
+  a.part_ml = need ? (float*)((char*)workspace + align_up(slots * kHeads * kDim * sizeof(float), 256)) : nullptr;
+  hipStream_t st = (hipStream_t)hip_stream;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(attend_kernel, dim3(p.n_items, T), dim3(kAttnThreads), 0, st, a);
+  if (need) hipLaunchKernelGGL(attend_combine_kernel, dim3(T, L), dim3(256), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
+  return CSA2_OK;
+}
+
+}  // namespace csa2
+
+using namespace csa2;
+
+extern "C" size_t csa2_attend_workspace_bytes(int32_t T, int32_t k, int32_t window, int32_t n_layers) {
+  if (T < 1 || k != kTopK || window < 1 || window > CSA2_MAX_WINDOW || n_layers < 1 || n_layers > CSA2_MAX_LAYERS)
+    return 0;
+  const AttendPlan p = attend_plan(T, k, window, n_layers);
+  return attend_ws_bytes(T, p, n_layers);
+}
+
+extern "C" csa2_status csa2_attend_fp4(const void* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
+                                       const int32_t* indices, const void* swa, const int32_t* swa_end,
+                                       const float* sink, float softmax_scale, int32_t T, int32_t q_per_seq,
+                                       int64_t N, int32_t S, int32_t window, int32_t k, void* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return attend_launch(1, q, kv_fp4, kv_scale, indices, swa, swa_end, sink, softmax_scale, T, q_per_seq, N, S,
+                       window, k, out, lse, workspace, workspace_bytes, hip_stream);
+}
+
+extern "C" csa2_status csa2_reuse_attend(int32_t n_layers, const void* q, const uint8_t* kv_fp4,
+                                         const uint8_t* kv_scale, const int32_t* indices, const void* swa,
+                                         const int32_t* swa_end, const float* sink, float softmax_scale,
+                                         int32_t T, int32_t q_per_seq, int64_t N, int32_t S, int32_t window,
+                                         int32_t k, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                         void* hip_stream) {
+  if (n_layers < 1 || n_layers > CSA2_MAX_LAYERS) return CSA2_ERR_UNSUPPORTED;
+  return attend_launch(n_layers, q, kv_fp4, kv_scale, indices, swa, swa_end, sink, softmax_scale, T, q_per_seq, N,
+                       S, window, k, out, lse, workspace, workspace_bytes, hip_stream);
+}

@@ -1,0 +1,235 @@
+// Indexer scan (csa2_index): I(t,s) = sum_h w[t][h] * ReLU(q[t][h] . K[b][s]).
+//
+// Lightning-indexer score of DeepSeek-V4 (gzher.com reading, sec. 4.1), kept by
+// CSA2 (DeepSeek-V4.1-Flash report, sec. 2.3) with 32 heads x 128 (sec. 4.2.1).
+//
+// Per sequence the scan is a [32 heads x 128] x [128 x N] product, far below
+// the MFMA ridge (32 flop per key byte), so the kernel is built around the key
+// stream: each wave pulls 32 keys (8 KiB) per step straight from HBM into the
+// B operand of v_mfma_f32_32x32x16_bf16 (lane l holds half a key row, 128
+// contiguous bytes; the reduction order over channels is permuted identically
+// for q and K, which leaves the dot product unchanged), keeps the query in
+// registers as the A operand, and reduces ReLU(dot) * w over the 32 heads in
+// the accumulator's register layout (16 heads per lane + one cross-lane add).
+// The same pass accumulates ||K_s||^2 so that a rigorous per-query bound on
+// |fp32 score - fp64 score| can be formed without a second read of the keys.
+#include "csa2_common.h"
+
+namespace csa2 {
+
+constexpr int kScanThreads = 256;  // 4 waves
+constexpr int kScanWaves = kScanThreads / 64;
+
+// One block: sequence b = blockIdx.y, query group blockIdx.z (QG queries of
+// that sequence held in registers), tiles [x*tpb, (x+1)*tpb) of 32 keys.
+template <int QG>
+__global__ __launch_bounds__(kScanThreads) void idx_scan_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos, int ratio,
+    int q_per_seq, int64_t N, int tiles_per_block, float* __restrict__ scores,
+    float* __restrict__ norm_partial) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 31;  // key within the tile (MFMA column)
+  const int g = lane >> 5;    // which half of the 128 channels this lane holds
+  const int b = blockIdx.y;
+
+  bf16x8 A[QG][8];
+  float wr[QG][16];
+  int64_t nvis[QG];
+  int64_t trow[QG];
+  bool valid[QG];
+  int64_t nvis_max = 0;
+#pragma unroll
+  for (int qq = 0; qq < QG; ++qq) {
+    const int ql = blockIdx.z * QG + qq;
+    valid[qq] = ql < q_per_seq;
+    const int t = b * q_per_seq + (valid[qq] ? ql : q_per_seq - 1);
+    trow[qq] = (int64_t)t * N;
+    // A operand: row = head (lane & 31), channels g*64 + j*8 .. +8 at step j
+    const uint4* qp = reinterpret_cast<const uint4*>(q_idx + ((size_t)t * kIdxHeads + col) * kIdxDim + g * 64);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) A[qq][j] = as_bf16x8(qp[j]);
+    // accumulator register r holds head 8*(r/4) + 4*g + r%4 of key `col`
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wr[qq][r] = w_idx[(size_t)t * kIdxHeads + 8 * (r >> 2) + 4 * g + (r & 3)];
+    nvis[qq] = valid[qq] ? n_visible(q_pos, t, ratio, N) : 0;
+    nvis_max = nvis[qq] > nvis_max ? nvis[qq] : nvis_max;
+  }
+
+  const int64_t tiles = (N + 31) >> 5;
+  const int64_t tile0 = (int64_t)blockIdx.x * tiles_per_block;
+  const int64_t tile1 = tile0 + tiles_per_block < tiles ? tile0 + tiles_per_block : tiles;
+  float maxn2 = 0.f;
+
+  for (int64_t tile = tile0 + wave; tile < tile1; tile += kScanWaves) {
+    const int64_t s = tile * 32 + col;
+    if (tile * 32 >= nvis_max) {  // no query of the group sees any key of this tile
+      if (g == 0 && s < N) {
+#pragma unroll
+        for (int qq = 0; qq < QG; ++qq)
+          if (valid[qq]) scores[trow[qq] + s] = -INFINITY;
+      }
+      continue;
+    }
+    const int64_t sl = s < N ? s : N - 1;
+    const uint4* kp = reinterpret_cast<const uint4*>(k_idx + ((size_t)b * N + sl) * kIdxDim + g * 64);
+    uint4 kv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kv[j] = load_stream16(kp + j);
+
+    float n2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w4[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16lo(w4[e]), hi = bf16hi(w4[e]);
+        n2 = fmaf(lo, lo, n2);
+        n2 = fmaf(hi, hi, n2);
+      }
+    }
+    n2 += __shfl_xor(n2, 32, 64);
+    if (s < N) maxn2 = fmaxf(maxn2, n2);
+
+#pragma unroll
+    for (int qq = 0; qq < QG; ++qq) {
+      if (!valid[qq]) continue;
+      floatx16 acc = {};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[qq][j], as_bf16x8(kv[j]), acc, 0, 0, 0);
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part = fmaf(wr[qq][r], fmaxf(acc[r], 0.f), part);
+      part += __shfl_xor(part, 32, 64);
+      if (g == 0 && s < N) scores[trow[qq] + s] = (s < nvis[qq]) ? part : -INFINITY;
+    }
+  }
+
+  __shared__ float red[kScanWaves];
+  maxn2 = wave_max(maxn2);
+  if (lane == 0) red[wave] = maxn2;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = red[0];
+#pragma unroll
+    for (int i = 1; i < kScanWaves; ++i) m = fmaxf(m, red[i]);
+    norm_partial[((size_t)b * gridDim.z + blockIdx.z) * gridDim.x + blockIdx.x] = m;
+  }
+}
+
+// eps_t = 2^-14 * sum_h |w_h| ||q_h||_2 * max_s ||K_s||_2 + 2^-100 (1 + sum_h |w_h|), rounded up.
+//
+// Derivation: the bf16 products are exact in fp32; eight chained MFMA steps
+// of 16 products each, even with every addition rounded or truncated, stay
+// within 136 * 2^-23 * sum_c |q_c K_c| <= 2^-15.9 ||q_h|| ||K_s|| (Cauchy-
+// Schwarz); ReLU is 1-Lipschitz; the fp32 head reduction (17 roundings) adds at
+// most 2^-19.9 sum_h |w_h| |dot_h|; the fp64 reference itself is within
+// 2^-44 of the exact value.  The sum is below 1.1 * 2^-15; 2^-14 leaves a
+// factor 1.8 of margin.  The absolute term covers products that flush to zero.
+// ||K||^2 is an fp32 sum of 128 squares (relative error < 2^-16), so it is
+// inflated by (1 + 2^-16) before the square root.
+__global__ __launch_bounds__(64) void idx_finalize_kernel(const uint16_t* __restrict__ q_idx,
+                                                          const float* __restrict__ w_idx,
+                                                          const float* __restrict__ norm_partial,
+                                                          int q_per_seq, int parts_per_seq,
+                                                          float* __restrict__ err_bound) {
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int b = t / q_per_seq;
+  float m = 0.f;
+  for (int i = lane; i < parts_per_seq; i += 64) m = fmaxf(m, norm_partial[(size_t)b * parts_per_seq + i]);
+  m = wave_max(m);
+  double qf = 0.0, sw = 0.0;
+  if (lane < kIdxHeads) {
+    const uint16_t* qh = q_idx + ((size_t)t * kIdxHeads + lane) * kIdxDim;
+    double ss = 0.0;
+    for (int c = 0; c < kIdxDim; ++c) {
+      const double v = bf16_to_f64(qh[c]);
+      ss = fma(v, v, ss);
+    }
+    const double aw = fabs((double)w_idx[(size_t)t * kIdxHeads + lane]);
+    qf = aw * sqrt(ss) * (1.0 + 0x1p-40);
+    sw = aw;
+  }
+  qf = wave_sum_f64(qf);
+  sw = wave_sum_f64(sw);
+  if (lane == 0) {
+    const double kmax = sqrt((double)m * (1.0 + 0x1p-16)) * (1.0 + 0x1p-40);
+    double eps = (0x1p-14 * qf * kmax + 0x1p-100 * (1.0 + sw)) * (1.0 + 0x1p-20);
+    float e = (float)eps;
+    if ((double)e < eps) e = __int_as_float(__float_as_int(e) + 1);  // round up (positive, finite)
+    err_bound[t] = e;
+  }
+}
+
+struct IndexPlan {
+  int qg = 1;             // queries per group (template)
+  int groups = 1;         // gridDim.z
+  int B = 1;              // gridDim.y
+  int blocks_x = 1;       // gridDim.x
+  int tiles_per_block = 4;
+};
+
+static bool index_plan(int32_t T, int32_t q_per_seq, int64_t N, IndexPlan* p) {
+  if (T < 1 || q_per_seq < 1 || T % q_per_seq != 0 || N < 1 || N >= ((int64_t)1 << 31)) return false;
+  p->qg = q_per_seq == 1 ? 1 : q_per_seq == 2 ? 2 : 4;
+  p->groups = (q_per_seq + p->qg - 1) / p->qg;
+  p->B = T / q_per_seq;
+  const int64_t tiles = (N + 31) / 32;
+  // aim for ~2048 blocks in flight over 256 CUs; at least 4 tiles (one per wave) per block
+  int64_t want = (2048 + (int64_t)p->B * p->groups - 1) / ((int64_t)p->B * p->groups);
+  int64_t max_blocks = (tiles + kScanWaves - 1) / kScanWaves;
+  if (want > max_blocks) want = max_blocks;
+  if (want < 1) want = 1;
+  int64_t tpb = (tiles + want - 1) / want;
+  tpb = (tpb + kScanWaves - 1) / kScanWaves * kScanWaves;
+  p->tiles_per_block = (int)tpb;
+  p->blocks_x = (int)((tiles + tpb - 1) / tpb);
+  return p->B <= 65535 && p->groups <= 65535;
+}
+
+}  // namespace csa2
+
+using namespace csa2;
+
+extern "C" size_t csa2_index_workspace_bytes(int32_t T, int32_t q_per_seq, int64_t N) {
+  IndexPlan p;
+  if (!index_plan(T, q_per_seq, N, &p)) return 0;
+  return align_up((size_t)p.B * p.groups * p.blocks_x * sizeof(float), 256);
+}
+
+extern "C" csa2_status csa2_index(const void* q_idx, const float* w_idx, const void* k_idx,
+                                  const int32_t* q_pos, int32_t ratio, int32_t T, int32_t q_per_seq,
+                                  int64_t N, float* scores, float* err_bound, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream) {
+  if (!q_idx || !w_idx || !k_idx || !scores || !err_bound) return CSA2_ERR_INVALID_ARG;
+  if (!aligned16(q_idx) || !aligned16(w_idx) || !aligned16(k_idx) || !aligned16(scores) ||
+      !aligned16(err_bound) || (q_pos && !aligned16(q_pos)))
+    return CSA2_ERR_INVALID_ARG;
+  if (T < 1 || q_per_seq < 1 || N < 1 || ratio < 1 || T % q_per_seq != 0) return CSA2_ERR_INVALID_ARG;
+  IndexPlan p;
+  if (!index_plan(T, q_per_seq, N, &p)) return CSA2_ERR_UNSUPPORTED;
+  const size_t need = csa2_index_workspace_bytes(T, q_per_seq, N);
+  if (!workspace || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)hip_stream;
+  (void)hipGetLastError();
+  float* partial = (float*)workspace;
+  dim3 grid(p.blocks_x, p.B, p.groups);
+  const uint16_t* q = (const uint16_t*)q_idx;
+  const uint16_t* k = (const uint16_t*)k_idx;
+  if (p.qg == 1)
+    hipLaunchKernelGGL(idx_scan_kernel<1>, grid, dim3(kScanThreads), 0, st, q, w_idx, k, q_pos, ratio, q_per_seq,
+                       N, p.tiles_per_block, scores, partial);
+  else if (p.qg == 2)
+    hipLaunchKernelGGL(idx_scan_kernel<2>, grid, dim3(kScanThreads), 0, st, q, w_idx, k, q_pos, ratio, q_per_seq,
+                       N, p.tiles_per_block, scores, partial);
+  else
+    hipLaunchKernelGGL(idx_scan_kernel<4>, grid, dim3(kScanThreads), 0, st, q, w_idx, k, q_pos, ratio, q_per_seq,
+                       N, p.tiles_per_block, scores, partial);
+  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
+  hipLaunchKernelGGL(idx_finalize_kernel, dim3(T), dim3(64), 0, st, q, w_idx, (const float*)partial, q_per_seq,
+                     p.groups * p.blocks_x, err_bound);
+  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
+  return CSA2_OK;
+}

@@ -1,0 +1,187 @@
+/*
+ * csa2.h — C ABI of the MI355X (gfx950) CSA2 hot-path library (libcsa2.so).
+ *
+ * CSA2 (Compressed Sparse Attention 2) is the global-attention step of
+ * DeepSeek-V4.1-Flash ("DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache
+ * Compression", sec. 2.3).  Per query it (1) scores every causally visible
+ * compressed entry with a lightweight indexer, (2) keeps the top-k entries,
+ * (3) gathers those entries from an FP4 main-KV cache and dequantises them,
+ * and (4) runs shared-key/value multi-head attention over them together with
+ * the layer's sliding-window (SWA) KV in one softmax.  A Reuse-mode layer
+ * (sec. 2.3.1) repeats (3)-(4) with its own query and window over the index
+ * list and KV published by an earlier layer.
+ *
+ * Fixed shapes (sec. 4.2.1 of the report): 32 indexer heads of dim 128,
+ * top-k 512, 64 query heads of dim 512, window n_win <= 128.
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers, owned by the caller, row-major,
+ *    16-byte aligned.  The library never allocates, frees or retains them;
+ *    scratch memory comes only from the caller's workspace.
+ *  - bf16 tensors are passed as void* holding IEEE bfloat16 bit patterns.
+ *  - Queries are grouped by sequence: query t belongs to sequence
+ *    b = t / q_per_seq, and T = B * q_per_seq.  Decode uses q_per_seq = 1;
+ *    a prefill chunk of one sequence uses B = 1, q_per_seq = T.
+ *  - Causal visibility: with compression ratio m, compressed entry j covers
+ *    tokens [m*j, m*j+m) and is visible to the token at absolute position p
+ *    iff m*(j+1) <= p+1, so n_vis(t) = min(N, floor((q_pos[t]+1)/m)); a
+ *    negative position sees no entry.  q_pos == NULL means every one of the
+ *    N entries is visible.
+ *  - hip_stream is a hipStream_t (e.g. torch.cuda.current_stream().cuda_stream);
+ *    NULL means the default stream.  Calls only enqueue work and return.
+ *  - Errors: arguments are checked on the host before anything is launched;
+ *    on any error nothing is enqueued and the status says why.  Device data
+ *    (positions, indices, window ends) is never read on the host: values out
+ *    of the documented ranges give undefined results.  Device faults surface
+ *    at the caller's next synchronisation.
+ *  - Thread safety: no global mutable state; calls on different streams with
+ *    disjoint outputs and workspaces may run concurrently.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_IDX_HEADS 32
+#define CSA2_IDX_DIM 128
+#define CSA2_HEADS 64
+#define CSA2_DIM 512
+#define CSA2_TOPK 512
+#define CSA2_MAX_WINDOW 128
+#define CSA2_MAX_LAYERS 8
+#define CSA2_FP4_ROW_BYTES 256   /* 512 E2M1 codes, element 2i in the low nibble of byte i */
+#define CSA2_FP4_SCALES 16       /* E8M0 scale bytes per entry, one per 32 channels */
+
+typedef enum {
+    CSA2_OK = 0,
+    CSA2_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, non-positive size, bad scale */
+    CSA2_ERR_UNSUPPORTED = 2,  /* k != 512, window or layer count out of range, size limits */
+    CSA2_ERR_WORKSPACE = 3,    /* workspace pointer NULL or smaller than required */
+    CSA2_ERR_LAUNCH = 4        /* the HIP runtime rejected a kernel launch */
+} csa2_status;
+
+/* Human-readable name of a status code (static string). */
+const char* csa2_status_string(int32_t status);
+/* Library version string, e.g. "csa2-mi355x 0.1 gfx950". */
+const char* csa2_version(void);
+
+/* ------------------------------------------------------------------ index
+ * Indexer scan: for each query t and each visible entry s < n_vis(t),
+ *   I(t,s) = sum_{h<32} w[t][h] * ReLU( sum_{c<128} q_idx[t][h][c] * k_idx[b][s][c] )
+ * (lightning-indexer score of DeepSeek-V4, gzher.com reading sec. 4.1, which
+ * CSA2 keeps, report sec. 2.3).  The scores are computed with bf16 MFMA and
+ * fp32 accumulation.
+ *
+ *  q_idx     bf16  [T][32][128]   indexer queries
+ *  w_idx     fp32  [T][32]        per-head indexer weights
+ *  k_idx     bf16  [B][N][128]    indexer keys (B = T / q_per_seq)
+ *  q_pos     int32 [T] or NULL    absolute token positions (see visibility)
+ *  ratio     compression ratio m >= 1
+ *  scores    fp32  [T][N] out     I(t,s) for s < n_vis(t), -inf for s >= n_vis(t)
+ *  err_bound fp32  [T]    out     eps_t >= |scores[t][s] - I_fp64(t,s)| for every
+ *                                 visible s, where I_fp64 is the score evaluated in
+ *                                 fp64 with one fma per term, channels then heads
+ *                                 in order; csa2_topk uses it to make the
+ *                                 selection exact.
+ *  workspace >= csa2_index_workspace_bytes(T, q_per_seq, N) bytes (any contents).
+ * Requires T >= 1, q_per_seq >= 1, T % q_per_seq == 0, 1 <= N < 2^31.
+ */
+size_t csa2_index_workspace_bytes(int32_t T, int32_t q_per_seq, int64_t N);
+csa2_status csa2_index(const void* q_idx, const float* w_idx, const void* k_idx,
+                       const int32_t* q_pos, int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N,
+                       float* scores, float* err_bound, void* workspace, size_t workspace_bytes,
+                       void* hip_stream);
+
+/* ------------------------------------------------------------------- topk
+ * Exact top-k: for each query, the first min(k, n_vis) entries of the order
+ * (I_fp64 descending, index ascending) — I_fp64 as defined under csa2_index —
+ * written ASCENDING by entry index into indices[t][0..], the remaining slots
+ * set to -1 (report sec. 2.3: each query keeps its top-k entries; k = 512 per
+ * sec. 4.2.1).  The approximate scores pick the candidates; every entry whose
+ * rank could depend on rounding (|score - k-th score| <= 2*err_bound) is
+ * rescored in fp64 on the device, so the result does not depend on MFMA
+ * rounding.
+ *
+ *  scores, err_bound   outputs of csa2_index for the same arguments
+ *  q_idx, w_idx, k_idx, q_pos, ratio   as passed to csa2_index (used for the
+ *                      fp64 rescoring and for visibility)
+ *  k                   must be CSA2_TOPK (512)
+ *  indices int32 [T][k] out
+ *  workspace >= csa2_topk_workspace_bytes(T, N, k).  A larger workspace only
+ *  raises the number of boundary candidates handled on the fast path; a
+ *  smaller one (down to csa2_topk_min_workspace_bytes) is accepted and falls
+ *  back to a slower streaming path when the candidates do not fit.
+ */
+size_t csa2_topk_workspace_bytes(int32_t T, int64_t N, int32_t k);
+size_t csa2_topk_min_workspace_bytes(int32_t T, int64_t N, int32_t k);
+csa2_status csa2_topk(const float* scores, const float* err_bound, const void* q_idx,
+                      const float* w_idx, const void* k_idx, const int32_t* q_pos, int32_t ratio,
+                      int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices,
+                      void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ----------------------------------------------------------------- attend
+ * Joint sparse + sliding-window attention over an FP4 main-KV cache.  For
+ * query t (sequence b) and head h, over the set E_t of
+ *   - main rows x_j = dequant(kv[b][indices[t][j]]) for every j with
+ *     indices[t][j] >= 0 (FP4 dequantised before attention, report sec. 2.4.4:
+ *     x[c] = E2M1(code[c]) * 2^(scale[c/32] - 127), OCP MX format), and
+ *   - window rows swa[b][r] for r in [max(0, swa_end[t] - window), swa_end[t])
+ *     (report sec. 3.2.2: a query at position i attends SWA keys
+ *     [max(s, i-W+1), i]; the caller's SWA tensor starts at row s),
+ * it computes z_j = softmax_scale * (q[t][h] . x_j) and
+ *   out[t][h] = sum_j e^{z_j - M} x_j / (sum_j e^{z_j - M} + [sink] e^{sink[h] - M}),
+ *   lse[t][h] = M + log(denominator),
+ * with key = value = x_j (shared-KV MQA, gzher.com reading sec. 4.1) and one
+ * softmax over both sets; the optional sink adds exp(sink[h]) to the
+ * denominator only (gzher.com reading sec. 4.3).  Logits and sums are fp32;
+ * probabilities enter the value product as bf16.  An empty set gives out = 0,
+ * lse = -inf.
+ *
+ *  q        bf16  [T][64][512]
+ *  kv_fp4   uint8 [B][N][256]      E2M1 codes, element 2i in the low nibble of byte i
+ *  kv_scale uint8 [B][N][16]       E8M0 scales (255 is invalid)
+ *  indices  int32 [T][k]           entry ids in [0, N) or -1; duplicates allowed
+ *  swa      bf16  [B][S][512]
+ *  swa_end  int32 [T]              in [0, S]
+ *  sink     fp32  [64] or NULL
+ *  window   1..128;  k == 512;  softmax_scale finite and > 0
+ *  out      bf16  [T][64][512] out;  lse fp32 [T][64] out or NULL
+ *  workspace >= csa2_attend_workspace_bytes(T, k, window, 1)
+ */
+size_t csa2_attend_workspace_bytes(int32_t T, int32_t k, int32_t window, int32_t n_layers);
+csa2_status csa2_attend_fp4(const void* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
+                            const int32_t* indices, const void* swa, const int32_t* swa_end,
+                            const float* sink, float softmax_scale, int32_t T, int32_t q_per_seq,
+                            int64_t N, int32_t S, int32_t window, int32_t k, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------ reuse attend
+ * Cross-layer Reuse (report sec. 2.3.1): n_layers Reuse layers attend over
+ * the index list and main KV published by the latest Full (or Reindex) layer,
+ * each with its own query, window KV and sink; nothing is scored or selected.
+ * Layer l's output equals csa2_attend_fp4 called with q[l], swa[l], sink[l]
+ * and the shared indices/KV.  With n_layers > 1 every selected main-KV row is
+ * gathered and dequantised once for all layers.
+ *
+ *  n_layers 1..8
+ *  q     bf16 [L][T][64][512];  swa bf16 [L][B][S][512];  sink fp32 [L][64] or NULL
+ *  out   bf16 [L][T][64][512];  lse fp32 [L][T][64] or NULL
+ *  other arguments as csa2_attend_fp4 (swa_end shared by all layers)
+ *  workspace >= csa2_attend_workspace_bytes(T, k, window, n_layers)
+ */
+csa2_status csa2_reuse_attend(int32_t n_layers, const void* q, const uint8_t* kv_fp4,
+                              const uint8_t* kv_scale, const int32_t* indices, const void* swa,
+                              const int32_t* swa_end, const float* sink, float softmax_scale,
+                              int32_t T, int32_t q_per_seq, int64_t N, int32_t S, int32_t window,
+                              int32_t k, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

@@ -44,6 +44,7 @@ def lib():
             build()
         L = ctypes.CDLL(LIB)
         vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.csa2o_max_threads.argtypes, L.csa2o_max_threads.restype = [], i32
         L.csa2o_e2m1.argtypes, L.csa2o_e2m1.restype = [ctypes.c_uint32], dbl
         L.csa2o_e8m0.argtypes, L.csa2o_e8m0.restype = [ctypes.c_uint32], dbl
         L.csa2o_dequant_row.argtypes, L.csa2o_dequant_row.restype = [vp, vp, i32, vp], None
@@ -67,6 +68,10 @@ def _c(a, dtype):
     a = np.ascontiguousarray(a)
     assert a.dtype == dtype, (a.dtype, dtype)
     return a
+
+
+def max_threads() -> int:
+    return lib().csa2o_max_threads()
 
 
 def e2m1(code: int) -> float:

@@ -13,12 +13,24 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define IDX_HEADS 32
 #define IDX_DIM 128
 #define HEADS 64
 #define DIM 512
 #define MX_BLOCK 32
+
+/* Threads the OpenMP loops below will use (1 without OpenMP). */
+int32_t csa2o_max_threads(void) {
+#ifdef _OPENMP
+    return (int32_t)omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ---- formats ------------------------------------------------------------ */
 
@@ -62,7 +74,6 @@ void csa2o_dequant_row(const uint8_t* codes, const uint8_t* scales, int32_t dim,
  * entries the query may see causally.  With ratio m, entry j holds tokens
  * [m*j, m*j + m). */
 int64_t csa2o_n_visible(int64_t pos, int32_t ratio, int64_t N) {
-    if (pos < 0) return N;
     int64_t n = 0;
     while (n < N && (int64_t)ratio * (n + 1) <= pos + 1) ++n; /* plain count */
     return n;
@@ -91,7 +102,7 @@ void csa2o_index(const uint16_t* q_idx, const float* w_idx, const uint16_t* k_id
     const int64_t chunk = 4096;
     const int64_t nchunks = (N + chunk - 1) / chunk;
     int64_t* n_vis = (int64_t*)malloc((size_t)(T > 0 ? T : 1) * sizeof(int64_t));
-    for (int32_t t = 0; t < T; ++t) n_vis[t] = csa2o_n_visible(q_pos ? q_pos[t] : -1, ratio, N);
+    for (int32_t t = 0; t < T; ++t) n_vis[t] = q_pos ? csa2o_n_visible(q_pos[t], ratio, N) : N;
 #pragma omp parallel for schedule(dynamic, 1) collapse(2)
     for (int32_t t = 0; t < T; ++t) {
         for (int64_t ch = 0; ch < nchunks; ++ch) {
@@ -151,7 +162,7 @@ void csa2o_topk(const double* scores, const int32_t* q_pos, int32_t ratio, int32
                 int64_t N, int32_t k, int32_t* indices) {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int32_t t = 0; t < T; ++t) {
-        int64_t n_vis = csa2o_n_visible(q_pos ? q_pos[t] : -1, ratio, N);
+        int64_t n_vis = q_pos ? csa2o_n_visible(q_pos[t], ratio, N) : N;
         csa2o_topk_row(scores + (int64_t)t * N, n_vis, k, indices + (int64_t)t * k);
     }
 }

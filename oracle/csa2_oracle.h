@@ -33,6 +33,9 @@
 extern "C" {
 #endif
 
+/* Threads the oracle's parallel loops use. */
+int32_t csa2o_max_threads(void);
+
 /* Value of one E2M1 code (OCP MX): sign bit 3, magnitudes {0,.5,1,1.5,2,3,4,6}. */
 double csa2o_e2m1(uint32_t code);
 /* E8M0 scale 2^(e-127); e == 255 (NaN in the spec) returns NaN. */
@@ -43,7 +46,8 @@ void csa2o_dequant_row(const uint8_t* codes, const uint8_t* scales, int32_t dim,
 /* Number of compressed entries causally visible to the token at absolute
  * position `pos` with compression ratio m: entry j (covering tokens
  * [m*j, m*j+m)) is visible iff it is complete, m*(j+1) <= pos+1.
- * Capped at N.  pos < 0 means "all N visible" (decode without positions). */
+ * Capped at N; a negative position sees nothing.  Functions taking a q_pos
+ * array treat NULL as "all N entries visible". */
 int64_t csa2o_n_visible(int64_t pos, int32_t ratio, int64_t N);
 
 /* Indexer score of one entry: sum_h w[h] * ReLU(q[h] . key) in fp64, dot

@@ -1,0 +1,127 @@
+"""C-ABI library checks that need no GPU: it loads, exports every declared
+entry point, and rejects bad arguments on the host before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import compressed_sparse_attention_02_amd as csa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return csa.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert {"csa2_index", "csa2_topk", "csa2_attend_fp4", "csa2_reuse_attend"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version(L):
+    assert L.csa2_status_string(0) == b"CSA2_OK"
+    assert L.csa2_status_string(3) == b"CSA2_ERR_WORKSPACE"
+    assert L.csa2_status_string(99) == b"CSA2_ERR_UNKNOWN"
+    assert b"gfx950" in L.csa2_version()
+
+
+def test_workspace_queries(L):
+    assert csa.index_workspace_bytes(4, 1, 1 << 20) > 0
+    assert csa.index_workspace_bytes(4, 3, 100) == 0          # T not a multiple of q_per_seq
+    assert csa.topk_workspace_bytes(4, 1 << 20) >= csa.topk_min_workspace_bytes(4, 1 << 20) > 0
+    assert csa.topk_workspace_bytes(4, 1 << 20, 256) == 0      # only k = 512
+    assert csa.attend_workspace_bytes(4096) == 0               # one work item per query: no partials
+    assert csa.attend_workspace_bytes(4) > 0
+    assert csa.attend_workspace_bytes(4, window=129) == 0
+    assert csa.attend_workspace_bytes(4, n_layers=9) == 0
+
+
+# Fake, never-dereferenced, 16-byte-aligned addresses: every call below must be
+# rejected by host validation, so nothing is launched and nothing is read.
+P = ctypes.c_void_p(0x10000)
+Q = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10004)   # misaligned
+
+
+def _index(L, q=P, w=P, k=P, pos=None, ratio=1, T=4, qps=1, N=1024, s=P, e=P, ws=P, wsb=1 << 20):
+    return L.csa2_index(q, w, k, pos, ratio, T, qps, N, s, e, ws, wsb, None)
+
+
+def test_index_host_validation(L):
+    assert _index(L, q=None) == INVALID
+    assert _index(L, s=None) == INVALID
+    assert _index(L, k=MIS) == INVALID
+    assert _index(L, T=0) == INVALID
+    assert _index(L, T=4, qps=3) == INVALID
+    assert _index(L, N=0) == INVALID
+    assert _index(L, ratio=0) == INVALID
+    assert _index(L, N=1 << 31) == UNSUPPORTED
+    assert _index(L, ws=None) == WORKSPACE
+    assert _index(L, wsb=csa.index_workspace_bytes(4, 1, 1024) - 1) == WORKSPACE
+
+
+def _topk(L, s=P, e=P, q=P, w=P, k_idx=P, pos=None, ratio=1, T=4, qps=1, N=4096, k=512, out=P, ws=P, wsb=None):
+    if wsb is None:
+        wsb = csa.topk_workspace_bytes(T, N, 512) or 1
+    return L.csa2_topk(s, e, q, w, k_idx, pos, ratio, T, qps, N, k, out, ws, wsb, None)
+
+
+def test_topk_host_validation(L):
+    assert _topk(L, s=None) == INVALID
+    assert _topk(L, out=MIS) == INVALID
+    assert _topk(L, T=5, qps=2) == INVALID
+    assert _topk(L, k=256) == UNSUPPORTED
+    assert _topk(L, ws=None) == WORKSPACE
+    assert _topk(L, wsb=csa.topk_min_workspace_bytes(4, 4096) - 1) == WORKSPACE
+
+
+def _attend(L, q=P, kv=P, sc=P, idx=P, swa=P, end=P, sink=None, scale=0.044, T=4, qps=1, N=4096, S=128, W=128,
+            k=512, out=P, lse=None, ws=P, wsb=1 << 30):
+    return L.csa2_attend_fp4(q, kv, sc, idx, swa, end, sink, scale, T, qps, N, S, W, k, out, lse, ws, wsb, None)
+
+
+def test_attend_host_validation(L):
+    assert _attend(L, q=None) == INVALID
+    assert _attend(L, swa=MIS) == INVALID
+    assert _attend(L, scale=0.0) == INVALID
+    assert _attend(L, scale=float("nan")) == INVALID
+    assert _attend(L, scale=float("inf")) == INVALID
+    assert _attend(L, S=0) == INVALID
+    assert _attend(L, k=256) == UNSUPPORTED
+    assert _attend(L, W=0) == UNSUPPORTED
+    assert _attend(L, W=129) == UNSUPPORTED
+    assert _attend(L, ws=None) == WORKSPACE
+    assert _attend(L, wsb=csa.attend_workspace_bytes(4) - 1) == WORKSPACE
+
+
+def test_reuse_host_validation(L):
+    args = [P, P, P, P, P, P, None, 0.044, 4, 1, 4096, 128, 128, 512, P, None, P, 1 << 30, None]
+    assert L.csa2_reuse_attend(0, *args) == UNSUPPORTED
+    assert L.csa2_reuse_attend(9, *args) == UNSUPPORTED
+    bad = list(args)
+    bad[0] = None
+    assert L.csa2_reuse_attend(2, *bad) == INVALID
+    small = list(args)
+    small[17] = csa.attend_workspace_bytes(4, n_layers=3) - 1
+    assert L.csa2_reuse_attend(3, *small) == WORKSPACE
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        csa.csa2_index(torch.zeros(1, 32, 128, dtype=torch.bfloat16), torch.zeros(1, 32),
+                       torch.zeros(1, 64, 128, dtype=torch.bfloat16))

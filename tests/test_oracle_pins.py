@@ -143,7 +143,7 @@ def test_visibility_small_cases(oracle_lib):
     # ratio 1: the current token's own entry is complete
     assert [oracle_lib.n_visible(p, 1, 100) for p in range(3)] == [1, 2, 3]
     assert oracle_lib.n_visible(10 ** 9, 1, 100) == 100     # capped at N
-    assert oracle_lib.n_visible(-1, 4, 77) == 77            # no position: all visible
+    assert oracle_lib.n_visible(-1, 4, 77) == 0             # before the first token: nothing
 
 
 # ------------------------------------------------------------------ indexer
