@@ -299,51 +299,48 @@ __global__ __launch_bounds__(kAttnThreads) void attend_kernel(AttnArgs a) {
   }
 }
 
-// Merge the partial slots of each (layer, query): grid (T, L), 256 threads.
-__global__ __launch_bounds__(256) void attend_combine_kernel(AttnArgs a) {
-  const int t = blockIdx.x, layer = blockIdx.y;
-  __shared__ float inv_den[64], mstar[64];
-  const size_t base = ((size_t)layer * a.T + t) * a.n_slots;
+// Merge the partial slots of each (layer, query, head): grid (64, T, L),
+// 128 threads x 4 channels.  out = sum_s O_s 2^(m_s - M) / den,
+// den = sum_s l_s 2^(m_s - M) (+ 2^(sink - M)), M = max_s m_s (and the sink).
+__global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a) {
+  const int h = blockIdx.x, t = blockIdx.y, layer = blockIdx.z;
   const int tid = threadIdx.x;
-  if (tid < kHeads) {
-    const int h = tid;
-    float M = -INFINITY;
-    for (int s = 0; s < a.n_slots; ++s) M = fmaxf(M, a.part_ml[((base + s) * kHeads + h) * 2]);
+  const size_t base = ((size_t)layer * a.T + t) * a.n_slots;
+  __shared__ float fac[64];
+  __shared__ float s_inv;
+  if (tid < 64) {
+    // one lane per slot (n_slots <= 64): max, then weighted sum, by wave reductions
+    const bool has = tid < a.n_slots;
+    const float ms = has ? a.part_ml[((base + tid) * kHeads + h) * 2] : -INFINITY;
+    const float ls = has ? a.part_ml[((base + tid) * kHeads + h) * 2 + 1] : 0.f;
+    float M = wave_max(ms);
     float sk = -INFINITY;
-    if (a.sink) { sk = a.sink[(size_t)layer * kHeads + h] * kLog2e; M = fmaxf(M, sk); }
-    float den = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < a.n_slots; ++s) {
-        const float ms = a.part_ml[((base + s) * kHeads + h) * 2];
-        if (ms != -INFINITY) den += a.part_ml[((base + s) * kHeads + h) * 2 + 1] * exp2f(ms - M);
-      }
-      if (a.sink) den += exp2f(sk - M);
+    if (a.sink) {
+      sk = a.sink[(size_t)layer * kHeads + h] * kLog2e;
+      M = fmaxf(M, sk);
     }
-    mstar[h] = M;
-    inv_den[h] = (M == -INFINITY || den == 0.f) ? 0.f : 1.f / den;
-    if (a.lse) a.lse[((size_t)layer * a.T + t) * kHeads + h] = (M == -INFINITY) ? -INFINITY : (M + log2f(den)) * kLn2;
+    const float f = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
+    float den = wave_sum(ls * f);
+    if (a.sink && M != -INFINITY) den += exp2f(sk - M);
+    if (has) fac[tid] = f;
+    if (tid == 0) {
+      s_inv = (M == -INFINITY || den == 0.f) ? 0.f : 1.f / den;
+      if (a.lse) a.lse[((size_t)layer * a.T + t) * kHeads + h] = (M == -INFINITY) ? -INFINITY : (M + log2f(den)) * kLn2;
+    }
   }
   __syncthreads();
-  // each thread: 4 consecutive channels of one head per step; 64 heads x 128 quads
-  for (int qd = tid; qd < kHeads * (kDim / 4); qd += 256) {
-    const int h = qd / (kDim / 4), c4 = qd % (kDim / 4);
-    const float M = mstar[h];
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-      for (int s = 0; s < a.n_slots; ++s) {
-        const float ms = a.part_ml[((base + s) * kHeads + h) * 2];
-        if (ms == -INFINITY) continue;
-        const float f = exp2f(ms - M);
-        const floatx4 o = *reinterpret_cast<const floatx4*>(a.part_o + ((base + s) * kHeads + h) * kDim + 4 * c4);
-        acc += o * f;
-      }
-    }
-    const float iv = inv_den[h];
-    uint16_t* op = a.out + (((size_t)layer * a.T + t) * kHeads + h) * kDim + 4 * c4;
-    const uint32_t w0 = f32_to_bf16_rne(acc[0] * iv) | (f32_to_bf16_rne(acc[1] * iv) << 16);
-    const uint32_t w1 = f32_to_bf16_rne(acc[2] * iv) | (f32_to_bf16_rne(acc[3] * iv) << 16);
-    *reinterpret_cast<uint2*>(op) = make_uint2(w0, w1);
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.n_slots; ++s) {
+    const float f = fac[s];
+    if (f == 0.f) continue;
+    const floatx4 o = *reinterpret_cast<const floatx4*>(a.part_o + ((base + s) * kHeads + h) * kDim + 4 * tid);
+    acc += o * f;
   }
+  const float iv = s_inv;
+  uint16_t* op = a.out + (((size_t)layer * a.T + t) * kHeads + h) * kDim + 4 * tid;
+  const uint32_t w0 = f32_to_bf16_rne(acc[0] * iv) | (f32_to_bf16_rne(acc[1] * iv) << 16);
+  const uint32_t w1 = f32_to_bf16_rne(acc[2] * iv) | (f32_to_bf16_rne(acc[3] * iv) << 16);
+  *reinterpret_cast<uint2*>(op) = make_uint2(w0, w1);
 }
 
 struct AttendPlan {
@@ -424,7 +421,7 @@ static csa2_status attend_launch(int32_t L, const void* q, const uint8_t* kv_fp4
   hipStream_t st = (hipStream_t)hip_stream;
   (void)hipGetLastError();
   hipLaunchKernelGGL(attend_kernel, dim3(p.n_items, T), dim3(kAttnThreads), 0, st, a);
-  if (need) hipLaunchKernelGGL(attend_combine_kernel, dim3(T, L), dim3(256), 0, st, a);
+  if (need) hipLaunchKernelGGL(attend_combine_kernel, dim3(kHeads, T, L), dim3(128), 0, st, a);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   return CSA2_OK;
 }

@@ -20,25 +20,32 @@ namespace csa2 {
 constexpr int kScanThreads = 256;  // 4 waves
 constexpr int kScanWaves = kScanThreads / 64;
 
+constexpr int kQRowPad = kIdxDim + 8;  // bf16 per q row in LDS (272 B: spreads rows over banks)
+constexpr int kTilesPerIter = 2;       // 32-key tiles loaded per wave per iteration (16 KiB)
+
 // One block: sequence b = blockIdx.y, query group blockIdx.z (QG queries of
-// that sequence held in registers), tiles [x*tpb, (x+1)*tpb) of 32 keys.
+// that sequence), tiles [x*tpb, (x+1)*tpb) of 32 keys.  The group's queries
+// sit in LDS (MFMA A operands are read with ds_read_b128); registers hold
+// only the keys in flight, so many waves fit per SIMD and each keeps 16 KiB
+// of keys outstanding.
 template <int QG>
 __global__ __launch_bounds__(kScanThreads) void idx_scan_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos, int ratio,
     int q_per_seq, int64_t N, int tiles_per_block, float* __restrict__ scores,
     float* __restrict__ norm_partial) {
+  __shared__ __attribute__((aligned(16))) uint16_t sq[QG * kIdxHeads * kQRowPad];
+  __shared__ float red[kScanWaves];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 31;  // key within the tile (MFMA column)
   const int g = lane >> 5;    // which half of the 128 channels this lane holds
   const int b = blockIdx.y;
 
-  bf16x8 A[QG][8];
-  float wr[QG][16];
   int64_t nvis[QG];
   int64_t trow[QG];
   bool valid[QG];
+  float wr[QG][16];
   int64_t nvis_max = 0;
 #pragma unroll
   for (int qq = 0; qq < QG; ++qq) {
@@ -46,67 +53,85 @@ __global__ __launch_bounds__(kScanThreads) void idx_scan_kernel(
     valid[qq] = ql < q_per_seq;
     const int t = b * q_per_seq + (valid[qq] ? ql : q_per_seq - 1);
     trow[qq] = (int64_t)t * N;
-    // A operand: row = head (lane & 31), channels g*64 + j*8 .. +8 at step j
-    const uint4* qp = reinterpret_cast<const uint4*>(q_idx + ((size_t)t * kIdxHeads + col) * kIdxDim + g * 64);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) A[qq][j] = as_bf16x8(qp[j]);
+    // stage q[t] (32 x 128 bf16) into LDS: 512 chunks of 16 B over 256 threads
+    for (int i = threadIdx.x; i < kIdxHeads * kIdxDim / 8; i += kScanThreads) {
+      const int h = i >> 4, c8 = i & 15;
+      *reinterpret_cast<uint4*>(&sq[(qq * kIdxHeads + h) * kQRowPad + c8 * 8]) =
+          *reinterpret_cast<const uint4*>(q_idx + ((size_t)t * kIdxHeads + h) * kIdxDim + c8 * 8);
+    }
     // accumulator register r holds head 8*(r/4) + 4*g + r%4 of key `col`
 #pragma unroll
     for (int r = 0; r < 16; ++r) wr[qq][r] = w_idx[(size_t)t * kIdxHeads + 8 * (r >> 2) + 4 * g + (r & 3)];
     nvis[qq] = valid[qq] ? n_visible(q_pos, t, ratio, N) : 0;
     nvis_max = nvis[qq] > nvis_max ? nvis[qq] : nvis_max;
   }
+  __syncthreads();
 
   const int64_t tiles = (N + 31) >> 5;
   const int64_t tile0 = (int64_t)blockIdx.x * tiles_per_block;
   const int64_t tile1 = tile0 + tiles_per_block < tiles ? tile0 + tiles_per_block : tiles;
+  const uint16_t* kseq = k_idx + (size_t)b * N * kIdxDim + g * 64;
+  const int64_t last = (nvis_max < N ? (nvis_max > 0 ? nvis_max : 1) : N) - 1;  // last row worth reading
   float maxn2 = 0.f;
 
-  for (int64_t tile = tile0 + wave; tile < tile1; tile += kScanWaves) {
-    const int64_t s = tile * 32 + col;
-    if (tile * 32 >= nvis_max) {  // no query of the group sees any key of this tile
-      if (g == 0 && s < N) {
+  // The wave's tiles: tile0 + wave*2 + {0,1} + 8*i (adjacent pairs, blocks of 8 per iteration).
+  for (int64_t base = tile0 + kTilesPerIter * wave; base < tile1; base += kTilesPerIter * kScanWaves) {
+    // Unconditional loads keep the code branch-free: keys past the end or past
+    // every query's visibility re-read row `last`, which is already cached.
+    uint4 kv[kTilesPerIter][8];
 #pragma unroll
-        for (int qq = 0; qq < QG; ++qq)
-          if (valid[qq]) scores[trow[qq] + s] = -INFINITY;
-      }
-      continue;
+    for (int u = 0; u < kTilesPerIter; ++u) {
+      const int64_t s = (base + u) * 32 + col;
+      const uint4* kp = reinterpret_cast<const uint4*>(kseq + (size_t)(s < last ? s : last) * kIdxDim);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kv[u][j] = kp[j];
     }
-    const int64_t sl = s < N ? s : N - 1;
-    const uint4* kp = reinterpret_cast<const uint4*>(k_idx + ((size_t)b * N + sl) * kIdxDim + g * 64);
-    uint4 kv[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kv[j] = load_stream16(kp + j);
-
-    float n2 = 0.f;
+    for (int u = 0; u < kTilesPerIter; ++u) {
+      const int64_t tile = base + u;
+      if (tile >= tile1) break;
+      const int64_t s = tile * 32 + col;
+      if (tile * 32 >= nvis_max) {  // no query of the group sees any key of this tile
+        if (g == 0 && s < N) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t w4[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = bf16lo(w4[e]), hi = bf16hi(w4[e]);
-        n2 = fmaf(lo, lo, n2);
-        n2 = fmaf(hi, hi, n2);
+          for (int qq = 0; qq < QG; ++qq)
+            if (valid[qq]) scores[trow[qq] + s] = -INFINITY;
+        }
+        continue;
       }
-    }
-    n2 += __shfl_xor(n2, 32, 64);
-    if (s < N) maxn2 = fmaxf(maxn2, n2);
-
+      // ||K_s||^2: 64 channels per lane with bf16 dot2, plus the other half of the row
+      float n2 = 0.f;
 #pragma unroll
-    for (int qq = 0; qq < QG; ++qq) {
-      if (!valid[qq]) continue;
-      floatx16 acc = {};
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t w4[4] = {kv[u][j].x, kv[u][j].y, kv[u][j].z, kv[u][j].w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[qq][j], as_bf16x8(kv[j]), acc, 0, 0, 0);
-      float part = 0.f;
+        for (int e = 0; e < 4; ++e) {
+          bf16x2 p;
+          __builtin_memcpy(&p, &w4[e], 4);
+          n2 = __builtin_amdgcn_fdot2_f32_bf16(p, p, n2, false);
+        }
+      }
+      n2 += __shfl_xor(n2, 32, 64);
+      if (s < N) maxn2 = fmaxf(maxn2, n2);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) part = fmaf(wr[qq][r], fmaxf(acc[r], 0.f), part);
-      part += __shfl_xor(part, 32, 64);
-      if (g == 0 && s < N) scores[trow[qq] + s] = (s < nvis[qq]) ? part : -INFINITY;
+      for (int qq = 0; qq < QG; ++qq) {
+        if (!valid[qq]) continue;
+        const uint16_t* qrow = &sq[(qq * kIdxHeads + col) * kQRowPad + g * 64];
+        floatx16 acc = {};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(qrow + j * 8);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(kv[u][j]), acc, 0, 0, 0);
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part = fmaf(wr[qq][r], fmaxf(acc[r], 0.f), part);
+        part += __shfl_xor(part, 32, 64);
+        if (g == 0 && s < N) scores[trow[qq] + s] = (s < nvis[qq]) ? part : -INFINITY;
+      }
     }
   }
 
-  __shared__ float red[kScanWaves];
   maxn2 = wave_max(maxn2);
   if (lane == 0) red[wave] = maxn2;
   __syncthreads();
@@ -127,8 +152,9 @@ __global__ __launch_bounds__(kScanThreads) void idx_scan_kernel(
 // most 2^-19.9 sum_h |w_h| |dot_h|; the fp64 reference itself is within
 // 2^-44 of the exact value.  The sum is below 1.1 * 2^-15; 2^-14 leaves a
 // factor 1.8 of margin.  The absolute term covers products that flush to zero.
-// ||K||^2 is an fp32 sum of 128 squares (relative error < 2^-16), so it is
-// inflated by (1 + 2^-16) before the square root.
+// ||K||^2 is accumulated with bf16 dot2 steps in fp32 over nonnegative terms
+// (relative error below 2^-16 even with two roundings per step), so it is
+// inflated by (1 + 2^-10) before the square root.
 __global__ __launch_bounds__(64) void idx_finalize_kernel(const uint16_t* __restrict__ q_idx,
                                                           const float* __restrict__ w_idx,
                                                           const float* __restrict__ norm_partial,
@@ -155,7 +181,7 @@ __global__ __launch_bounds__(64) void idx_finalize_kernel(const uint16_t* __rest
   qf = wave_sum_f64(qf);
   sw = wave_sum_f64(sw);
   if (lane == 0) {
-    const double kmax = sqrt((double)m * (1.0 + 0x1p-16)) * (1.0 + 0x1p-40);
+    const double kmax = sqrt((double)m * (1.0 + 0x1p-10) + 0x1p-100) * (1.0 + 0x1p-40);
     double eps = (0x1p-14 * qf * kmax + 0x1p-100 * (1.0 + sw)) * (1.0 + 0x1p-20);
     float e = (float)eps;
     if ((double)e < eps) e = __int_as_float(__float_as_int(e) + 1);  // round up (positive, finite)
@@ -179,11 +205,12 @@ static bool index_plan(int32_t T, int32_t q_per_seq, int64_t N, IndexPlan* p) {
   const int64_t tiles = (N + 31) / 32;
   // aim for ~2048 blocks in flight over 256 CUs; at least 4 tiles (one per wave) per block
   int64_t want = (2048 + (int64_t)p->B * p->groups - 1) / ((int64_t)p->B * p->groups);
-  int64_t max_blocks = (tiles + kScanWaves - 1) / kScanWaves;
+  const int64_t per_iter = (int64_t)kTilesPerIter * kScanWaves;
+  int64_t max_blocks = (tiles + per_iter - 1) / per_iter;
   if (want > max_blocks) want = max_blocks;
   if (want < 1) want = 1;
   int64_t tpb = (tiles + want - 1) / want;
-  tpb = (tpb + kScanWaves - 1) / kScanWaves * kScanWaves;
+  tpb = (tpb + per_iter - 1) / per_iter * per_iter;
   p->tiles_per_block = (int)tpb;
   p->blocks_x = (int)((tiles + tpb - 1) / tpb);
   return p->B <= 65535 && p->groups <= 65535;

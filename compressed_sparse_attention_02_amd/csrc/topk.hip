@@ -208,20 +208,27 @@ __device__ double exact_score(const uint16_t* __restrict__ q, const float* __res
   return sc;
 }
 
+constexpr int kBinLds = 1024;   // candidates of the threshold's 22-bit bin handled in LDS
+
 struct FinShared {
   uint32_t hist[256];
+  uint32_t s_sum[kFinThreads];
+  uint32_t s_bin[2];
   uint32_t out[kTopK];
+  uint32_t out_sorted[kTopK];
   uint32_t band_idx[kBandLds];
   uint64_t band_key[kBandLds];
+  float binv[kBinLds];
+  uint16_t krows[32][kIdxDim];
+  uint16_t qrows[kIdxHeads][kIdxDim + 8];
   double dots[32][kIdxHeads + 1];
-  uint32_t n_out, n_band, sel_digit, sel_rank;
-  uint64_t prefix_hi;
-  uint32_t prefix_lo;
+  uint32_t n_out, n_band, n_bin, sel_digit, sel_rank;
+  float that;
 };
 
 // Radix step over 8-bit digits, descending: given hist[256] of the elements
 // matching the current prefix and the 1-based rank among them, pick the digit
-// (thread 0) and the rank within that digit.
+// (thread 0) and the rank within that digit.  Used by the streaming path only.
 __device__ __forceinline__ void radix_pick(FinShared& sh) {
   if (threadIdx.x == 0) {
     uint32_t rank = sh.sel_rank, cum = 0;
@@ -234,43 +241,6 @@ __device__ __forceinline__ void radix_pick(FinShared& sh) {
     sh.sel_rank = rank - cum;
   }
   __syncthreads();
-}
-
-// In-LDS bitonic sort of n (power of two) composite keys, descending by
-// (key, ~idx) (i.e. larger key first, then smaller index first).
-__device__ void bitonic_desc(uint64_t* key, uint32_t* idx, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < n / 2; i += blockDim.x) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool desc = ((lo & size) == 0);
-        const uint64_t ka = key[lo], kb = key[hi];
-        const uint32_t ia = idx[lo], ib = idx[hi];
-        const bool a_first = ka > kb || (ka == kb && ia < ib);
-        if (a_first != desc) {
-          key[lo] = kb; key[hi] = ka;
-          idx[lo] = ib; idx[hi] = ia;
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
-__device__ void bitonic_asc_u32(uint32_t* v, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < n / 2; i += blockDim.x) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool asc = ((lo & size) == 0);
-        const uint32_t a = v[lo], b = v[hi];
-        if ((a > b) == asc) { v[lo] = b; v[hi] = a; }
-      }
-      __syncthreads();
-    }
-  }
 }
 
 // Find the kk-th largest fp32 key among values produced by `get(i)` for i < n
@@ -295,6 +265,55 @@ __device__ uint32_t select_f32_key(FinShared& sh, int64_t n, uint32_t kk, Get ge
   return prefix;
 }
 
+// fp64 scores of 32 band entries per round (reference operation order): thread
+// (e = tid/32, h = tid%32) forms dot(q[h], K[e]) with 128 sequential fmas from
+// LDS, then 32 threads fold the heads in order.
+__device__ void rescore_band(FinShared& sh, uint32_t nb, const uint16_t* __restrict__ qt,
+                             const float* __restrict__ wt, const uint16_t* __restrict__ kb) {
+  const int tid = threadIdx.x;
+  const int e = tid >> 5, h = tid & 31;
+  for (int i = tid; i < kIdxHeads * 16; i += kFinThreads) {
+    const int r = i >> 4, c = i & 15;
+    *reinterpret_cast<uint4*>(&sh.qrows[r][8 * c]) = *reinterpret_cast<const uint4*>(qt + r * kIdxDim + 8 * c);
+  }
+  for (uint32_t base = 0; base < nb; base += 32) {
+    // stage up to 32 key rows (32 x 256 B): 512 chunks of 16 B
+    for (int i = tid; i < 32 * 16; i += kFinThreads) {
+      const int r = i >> 4, c = i & 15;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (base + r < nb) v = *reinterpret_cast<const uint4*>(kb + (size_t)sh.band_idx[base + r] * kIdxDim + 8 * c);
+      *reinterpret_cast<uint4*>(&sh.krows[r][8 * c]) = v;
+    }
+    __syncthreads();
+    if (base + e < nb) {
+      double d = 0.0;
+#pragma unroll 2
+      for (int i = 0; i < 16; ++i) {
+        const uint4 kq = *reinterpret_cast<const uint4*>(&sh.krows[e][8 * i]);
+        const uint4 qq = *reinterpret_cast<const uint4*>(&sh.qrows[h][8 * i]);
+        const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
+        const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          d = fma((double)bf16lo(qw[p]), (double)bf16lo(kw[p]), d);
+          d = fma((double)bf16hi(qw[p]), (double)bf16hi(kw[p]), d);
+        }
+      }
+      sh.dots[e][h] = d;
+    }
+    __syncthreads();
+    if (tid < 32 && base + tid < nb) {
+      double sc = 0.0;
+      for (int hh = 0; hh < kIdxHeads; ++hh) {
+        const double d = sh.dots[tid][hh];
+        sc = fma((double)wt[hh], d > 0.0 ? d : 0.0, sc);
+      }
+      sh.band_key[base + tid] = f64_key(sc);
+    }
+    __syncthreads();
+  }
+}
+
 __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
     const float* __restrict__ scores, const float* __restrict__ err_bound, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w_idx, const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
@@ -315,24 +334,63 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
   const uint16_t* kb = k_idx + (size_t)b * N * kIdxDim;
   const float* row = scores + (size_t)t * N;
   TopkWs w = topk_ws(ws, T, cap);
-  const uint32_t cnt = w.hdr[(size_t)t * kHdrWords + 2 * kBins];
+  const uint32_t* hdr = w.hdr + (size_t)t * kHdrWords;
+  const uint32_t cnt = hdr[2 * kBins];
   const uint32_t* cidx = w.cidx + (size_t)t * cap;
   const float* cval = w.cval + (size_t)t * cap;
   const float eps = err_bound[t];
-  if (tid == 0) { sh.n_out = 0; sh.n_band = 0; }
+  if (tid == 0) { sh.n_out = 0; sh.n_band = 0; sh.n_bin = 0; }
   __syncthreads();
 
   bool fast = (int64_t)cnt <= cap;
-  uint32_t tkey = 0;
-  if (fast) tkey = select_f32_key(sh, (int64_t)cnt, kk, [&](int64_t i) { return cval[i]; });
-  else tkey = select_f32_key(sh, nv, kk, [&](int64_t i) { return row[i]; });
-  const double that = (double)key_f32(tkey);
+  if (fast) {
+    // T^ lies in the 22-bit bin (b1, b2) found by the histogram passes; its rank
+    // inside that bin is what the two passes leave over.
+    find_bin(hdr, kk, sh.s_sum, sh.s_bin);
+    const uint32_t b1 = sh.s_bin[0], above1 = sh.s_bin[1];
+    __syncthreads();
+    find_bin(hdr + kBins, kk - above1, sh.s_sum, sh.s_bin);
+    const uint32_t b2 = sh.s_bin[0], above2 = sh.s_bin[1];
+    const uint32_t r3 = kk - above1 - above2;   // 1-based rank inside the bin
+    const uint32_t prefix = (b1 << 11) | b2;
+    for (uint32_t i = tid; i < cnt; i += kFinThreads) {
+      const float v = cval[i];
+      if ((f32_key(v) >> 10) == prefix) {
+        const uint32_t p = atomicAdd(&sh.n_bin, 1u);
+        if (p < kBinLds) sh.binv[p] = v;
+      }
+    }
+    __syncthreads();
+    const uint32_t nbin = sh.n_bin;
+    if (nbin <= kBinLds) {
+      for (uint32_t i = tid; i < nbin; i += kFinThreads) {
+        const float v = sh.binv[i];
+        uint32_t above = 0, tie_before = 0;
+        for (uint32_t j = 0; j < nbin; ++j) {
+          const float u = sh.binv[j];
+          above += u > v;
+          tie_before += (u == v) & (j < i);
+        }
+        if (above + tie_before == r3 - 1) sh.that = v;
+      }
+      __syncthreads();
+    } else {
+      const uint32_t key = select_f32_key(sh, (int64_t)cnt, kk, [&](int64_t i) { return cval[i]; });
+      if (tid == 0) sh.that = key_f32(key);
+      __syncthreads();
+    }
+  } else {
+    const uint32_t key = select_f32_key(sh, nv, kk, [&](int64_t i) { return row[i]; });
+    if (tid == 0) sh.that = key_f32(key);
+    __syncthreads();
+  }
+  const double that = (double)sh.that;
   double lo = next_down(that - 2.0 * (double)eps), hi = next_up(that + 2.0 * (double)eps);
   if (!(lo <= that)) lo = -INFINITY;   // eps not finite: everything is in the band
   if (!(hi >= that)) hi = INFINITY;
 
   if (fast) {
-    for (int64_t i = tid; i < cnt; i += kFinThreads) {
+    for (uint32_t i = tid; i < cnt; i += kFinThreads) {
       const double v = (double)cval[i];
       if (v > hi) sh.out[atomicAdd(&sh.n_out, 1u)] = cidx[i];
       else if (v >= lo) {
@@ -351,30 +409,20 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
 
   if (fast) {
     const uint32_t nb = sh.n_band;
-    // fp64 rescoring of the band: 32 entries x 32 heads per round
-    for (uint32_t base = 0; base < nb; base += 32) {
-      const uint32_t e = base + (tid >> 5);
-      const int h = tid & 31;
-      if (e < nb) sh.dots[tid >> 5][h] = exact_dot(qt + h * kIdxDim, kb + (size_t)sh.band_idx[e] * kIdxDim);
-      __syncthreads();
-      if (tid < 32 && base + tid < nb) {
-        double sc = 0.0;
-        for (int hh = 0; hh < kIdxHeads; ++hh) {
-          const double d = sh.dots[tid][hh];
-          sc = fma((double)wt[hh], d > 0.0 ? d : 0.0, sc);
-        }
-        sh.band_key[base + tid] = f64_key(sc);
-      }
-      __syncthreads();
-    }
-    int n2 = 1;
-    while (n2 < (int)nb) n2 <<= 1;
-    for (int i = (int)nb + tid; i < n2; i += kFinThreads) { sh.band_key[i] = 0; sh.band_idx[i] = 0xFFFFFFFFu; }
-    __syncthreads();
-    bitonic_desc(sh.band_key, sh.band_idx, n2);
+    rescore_band(sh, nb, qt, wt, kb);
+    // the r best band entries by (fp64 score desc, index asc): rank-based, all keys distinct
     const uint32_t r = kk - sh.n_out;
     const uint32_t base_out = sh.n_out;
-    for (uint32_t i = tid; i < r; i += kFinThreads) sh.out[base_out + i] = sh.band_idx[i];
+    for (uint32_t i = tid; i < nb; i += kFinThreads) {
+      const uint64_t ki = sh.band_key[i];
+      const uint32_t ii = sh.band_idx[i];
+      uint32_t rank = 0;
+      for (uint32_t j = 0; j < nb; ++j) {
+        const uint64_t kj = sh.band_key[j];
+        rank += (kj > ki) | ((kj == ki) & (sh.band_idx[j] < ii));
+      }
+      if (rank < r) sh.out[base_out + rank] = ii;
+    }
     __syncthreads();
   } else {
     // Streaming path: candidates or band exceed capacity.  Sure entries are
@@ -422,11 +470,15 @@ __global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
     __syncthreads();
   }
 
-  // ascending output, -1 padded
-  for (int i = kk + tid; i < kTopK; i += kFinThreads) sh.out[i] = 0xFFFFFFFFu;
+  // ascending output by rank (indices are distinct)
+  for (uint32_t i = tid; i < kk; i += kFinThreads) {
+    const uint32_t v = sh.out[i];
+    uint32_t pos = 0;
+    for (uint32_t j = 0; j < kk; ++j) pos += sh.out[j] < v;
+    sh.out_sorted[pos] = v;
+  }
   __syncthreads();
-  bitonic_asc_u32(sh.out, kTopK);
-  for (int i = tid; i < k; i += kFinThreads) out[i] = i < (int)kk ? (int32_t)sh.out[i] : -1;
+  for (int i = tid; i < k; i += kFinThreads) out[i] = i < (int)kk ? (int32_t)sh.out_sorted[i] : -1;
 }
 
 }  // namespace csa2
