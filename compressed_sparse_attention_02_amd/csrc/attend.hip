@@ -30,6 +30,7 @@ constexpr int kAttnThreads = 256;
 constexpr int kChunk = 32;
 constexpr int kXStride = kDim + 8;      // bf16 elements per X row (1040 B)
 constexpr int kXTStride = kChunk + 8;   // bf16 elements per XT row (80 B)
+constexpr int kMaxSlots = (CSA2_TOPK + kChunk - 1) / kChunk + (CSA2_MAX_WINDOW + kChunk - 1) / kChunk;  // 20
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -55,10 +56,15 @@ struct AttnArgs {
 };
 
 struct AttnShared {
-  uint16_t X[kChunk * kXStride];
-  uint16_t XT[kDim * kXTStride];
+  alignas(16) uint16_t X[kChunk * kXStride];
+  alignas(16) uint16_t XT[kDim * kXTStride];
   int valid[kChunk];
 };
+
+// 16-byte LDS operand read (the offsets used are multiples of 16 bytes).
+__device__ __forceinline__ bf16x8 lds_read16(const uint16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(__builtin_assume_aligned(p, 16));
+}
 
 // E2M1 magnitude (OCP MX) of a 3-bit code as an fp32 bit pattern.
 __device__ __forceinline__ uint32_t e2m1_bits(uint32_t c) {
@@ -86,36 +92,43 @@ __device__ void stage_chunk(const AttnArgs& a, AttnShared& sh, int t, int b, int
   const int g = threadIdx.x >> 6, d = threadIdx.x & 63;
   uint32_t v[8][4];
   int okr[8];
+  if (c < a.n_main) {
+    // all index loads, then all code / scale loads (rows of -1 slots read row 0
+    // and are zeroed), so that every load of the chunk is in flight together
+    int32_t idx[8];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int e = r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4);
-    bool ok = false;
-    if (c < a.n_main) {
-      const int j = c * kChunk + e;
-      const int32_t idx = j < a.k ? a.indices[(size_t)t * a.k + j] : -1;
-      if (idx >= 0) {
-        ok = true;
-        const size_t rowid = (size_t)b * a.N + idx;
-        const uint32_t codes = *reinterpret_cast<const uint32_t*>(a.kv_fp4 + rowid * 256 + 4 * d);
-        const uint32_t sbyte = a.kv_scale[rowid * 16 + (d >> 2)];
-        uint32_t o[8];
-        dequant8(codes, sbyte, o);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[r][i] = o[2 * i] | (o[2 * i + 1] << 16);
-      }
-    } else {
-      const int we = a.swa_end[t];
-      const int ws = we - a.window > 0 ? we - a.window : 0;
-      const int row = ws + (c - a.n_main) * kChunk + e;
-      if (row < we) {
-        ok = true;
-        const uint4 x = *reinterpret_cast<const uint4*>(
-            a.swa + (((size_t)layer * a.B + b) * a.S + row) * kDim + 8 * d);
-        v[r][0] = x.x; v[r][1] = x.y; v[r][2] = x.z; v[r][3] = x.w;
-      }
+    for (int r = 0; r < 8; ++r) {
+      const int e = r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4);
+      idx[r] = a.indices[(size_t)t * a.k + c * kChunk + e];
     }
-    if (!ok) { v[r][0] = v[r][1] = v[r][2] = v[r][3] = 0u; }
-    okr[r] = ok;
+    uint32_t codes[8], sbyte[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const size_t rowid = (size_t)b * a.N + (idx[r] >= 0 ? idx[r] : 0);
+      codes[r] = *reinterpret_cast<const uint32_t*>(a.kv_fp4 + rowid * 256 + 4 * d);
+      sbyte[r] = a.kv_scale[rowid * 16 + (d >> 2)];
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      okr[r] = idx[r] >= 0;
+      uint32_t o[8];
+      dequant8(codes[r], sbyte[r], o);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[r][i] = okr[r] ? (o[2 * i] | (o[2 * i + 1] << 16)) : 0u;
+    }
+  } else {
+    const int we = a.swa_end[t];
+    const int ws = we - a.window > 0 ? we - a.window : 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int e = r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4);
+      const int row = ws + (c - a.n_main) * kChunk + e;
+      okr[r] = row < we;
+      const int rr = okr[r] ? row : (we > 0 ? we - 1 : 0);
+      const uint4 x = *reinterpret_cast<const uint4*>(a.swa + (((size_t)layer * a.B + b) * a.S + rr) * kDim + 8 * d);
+      v[r][0] = okr[r] ? x.x : 0u; v[r][1] = okr[r] ? x.y : 0u;
+      v[r][2] = okr[r] ? x.z : 0u; v[r][3] = okr[r] ? x.w : 0u;
+    }
   }
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
@@ -166,8 +179,8 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const AttnShared
   floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const bf16x8 x0 = *reinterpret_cast<const bf16x8*>(&sh.X[r16 * kXStride + 32 * j + 8 * g]);
-    const bf16x8 x1 = *reinterpret_cast<const bf16x8*>(&sh.X[(16 + r16) * kXStride + 32 * j + 8 * g]);
+    const bf16x8 x0 = lds_read16(&sh.X[r16 * kXStride + 32 * j + 8 * g]);
+    const bf16x8 x1 = lds_read16(&sh.X[(16 + r16) * kXStride + 32 * j + 8 * g]);
     s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, qb[j], s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, qb[j], s1, 0, 0, 0);
   }
@@ -201,7 +214,7 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const AttnShared
 #pragma unroll
   for (int mb = 0; mb < 32; ++mb) {
     st.o[mb] *= alpha;
-    const bf16x8 xa = *reinterpret_cast<const bf16x8*>(&sh.XT[(16 * mb + r16) * kXTStride + 8 * g]);
+    const bf16x8 xa = lds_read16(&sh.XT[(16 * mb + r16) * kXTStride + 8 * g]);
     st.o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, pv, st.o[mb], 0, 0, 0);
   }
 }
@@ -329,13 +342,15 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a) {
     }
   }
   __syncthreads();
+  // all slot loads in flight at once (at most kMaxSlots slots)
+  floatx4 o[kMaxSlots];
+#pragma unroll
+  for (int s = 0; s < kMaxSlots; ++s)
+    if (s < a.n_slots) o[s] = *reinterpret_cast<const floatx4*>(a.part_o + ((base + s) * kHeads + h) * kDim + 4 * tid);
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.n_slots; ++s) {
-    const float f = fac[s];
-    if (f == 0.f) continue;
-    const floatx4 o = *reinterpret_cast<const floatx4*>(a.part_o + ((base + s) * kHeads + h) * kDim + 4 * tid);
-    acc += o * f;
-  }
+#pragma unroll
+  for (int s = 0; s < kMaxSlots; ++s)
+    if (s < a.n_slots && fac[s] != 0.f) acc += o[s] * fac[s];
   const float iv = s_inv;
   uint16_t* op = a.out + (((size_t)layer * a.T + t) * kHeads + h) * kDim + 4 * tid;
   const uint32_t w0 = f32_to_bf16_rne(acc[0] * iv) | (f32_to_bf16_rne(acc[1] * iv) << 16);

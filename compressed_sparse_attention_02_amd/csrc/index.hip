@@ -29,7 +29,7 @@ constexpr int kTilesPerIter = 2;       // 32-key tiles loaded per wave per itera
 // only the keys in flight, so many waves fit per SIMD and each keeps 16 KiB
 // of keys outstanding.
 template <int QG>
-__global__ __launch_bounds__(kScanThreads) void idx_scan_kernel(
+__global__ __launch_bounds__(kScanThreads, QG == 1 ? 4 : 2) void idx_scan_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos, int ratio,
     int q_per_seq, int64_t N, int tiles_per_block, float* __restrict__ scores,

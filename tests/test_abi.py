@@ -44,6 +44,7 @@ def test_workspace_queries(L):
     assert csa.index_workspace_bytes(4, 3, 100) == 0          # T not a multiple of q_per_seq
     assert csa.topk_workspace_bytes(4, 1 << 20) >= csa.topk_min_workspace_bytes(4, 1 << 20) > 0
     assert csa.topk_workspace_bytes(4, 1 << 20, 256) == 0      # only k = 512
+    assert csa.topk_workspace_bytes(4, 30000) == 0             # small rows: scores stay in LDS
     assert csa.attend_workspace_bytes(4096) == 0               # one work item per query: no partials
     assert csa.attend_workspace_bytes(4) > 0
     assert csa.attend_workspace_bytes(4, window=129) == 0
@@ -74,7 +75,9 @@ def test_index_host_validation(L):
     assert _index(L, wsb=csa.index_workspace_bytes(4, 1, 1024) - 1) == WORKSPACE
 
 
-def _topk(L, s=P, e=P, q=P, w=P, k_idx=P, pos=None, ratio=1, T=4, qps=1, N=4096, k=512, out=P, ws=P, wsb=None):
+# N large enough for the multi-pass regime, where a workspace is required, so
+# that every call below is rejected by validation.
+def _topk(L, s=P, e=P, q=P, w=P, k_idx=P, pos=None, ratio=1, T=4, qps=1, N=1 << 20, k=512, out=P, ws=P, wsb=None):
     if wsb is None:
         wsb = csa.topk_workspace_bytes(T, N, 512) or 1
     return L.csa2_topk(s, e, q, w, k_idx, pos, ratio, T, qps, N, k, out, ws, wsb, None)
@@ -86,7 +89,7 @@ def test_topk_host_validation(L):
     assert _topk(L, T=5, qps=2) == INVALID
     assert _topk(L, k=256) == UNSUPPORTED
     assert _topk(L, ws=None) == WORKSPACE
-    assert _topk(L, wsb=csa.topk_min_workspace_bytes(4, 4096) - 1) == WORKSPACE
+    assert _topk(L, wsb=csa.topk_min_workspace_bytes(4, 1 << 20) - 1) == WORKSPACE
 
 
 def _attend(L, q=P, kv=P, sc=P, idx=P, swa=P, end=P, sink=None, scale=0.044, T=4, qps=1, N=4096, S=128, W=128,

@@ -24,6 +24,8 @@ SMALL = {
     "qps3": dict(B=2, N=777, q_per_seq=3),
     "qps5_ratio2": dict(B=1, N=2501, q_per_seq=5, ratio=2),
     "prefill_small": dict(B=1, N=998, q_per_seq=96, ratio=2, prefix=1900),
+    "large_rows": dict(B=2, N=40000),
+    "large_rows_ragged": dict(B=2, N=40001),
 }
 
 
@@ -91,9 +93,10 @@ def test_topk_bit_exact(name):
 
 
 def test_topk_streaming_fallback_matches():
-    # a workspace with no candidate capacity forces the streaming path
+    # a workspace with no candidate capacity forces the streaming path of the
+    # multi-pass regime
     log("[topk] streaming fallback")
-    c = case("ragged_decode")
+    c = case("large_rows_ragged")
     scores, eps = run_index(c)
     ws = torch.empty(csa.topk_min_workspace_bytes(c.T, c.N), dtype=torch.uint8, device=DEV)
     idx = run_topk(c, scores, eps, workspace=ws)
@@ -103,10 +106,10 @@ def test_topk_streaming_fallback_matches():
         assert np.array_equal(npy(idx)[t], ref[t])
 
 
-@pytest.mark.parametrize("mode", ["all_equal", "all_equal_overflow", "tie_block"])
+@pytest.mark.parametrize("mode", ["all_equal", "all_equal_overflow", "tie_block", "tie_block_large"])
 def test_topk_planted_ties(mode):
     log(f"[topk] ties {mode}")
-    N = 3000 if mode == "all_equal_overflow" else 2048
+    N = {"all_equal_overflow": 3000, "tie_block_large": 40000}.get(mode, 2048)
     c = G.make_case("ties", B=1, N=N, seed=5, device=DEV, with_kv=False)
     if mode.startswith("all_equal"):
         c.k_idx[:] = c.k_idx[0, 7]                       # every key identical: lowest 512 indices win
