@@ -5,47 +5,49 @@
 //
 // Per sequence the scan is a [32 heads x 128] x [128 x N] product, far below
 // the MFMA ridge (32 flop per key byte), so the kernel is built around the key
-// stream: each wave pulls 32 keys (8 KiB) per step straight from HBM into the
-// B operand of v_mfma_f32_32x32x16_bf16 (lane l holds half a key row, 128
-// contiguous bytes; the reduction order over channels is permuted identically
-// for q and K, which leaves the dot product unchanged), keeps the query in
-// registers as the A operand, and reduces ReLU(dot) * w over the 32 heads in
-// the accumulator's register layout (16 heads per lane + one cross-lane add).
-// The same pass accumulates ||K_s||^2 so that a rigorous per-query bound on
-// |fp32 score - fp64 score| can be formed without a second read of the keys.
+// stream.  Keys are the B operand of v_mfma_f32_16x16x32_bf16: a 16-key tile
+// per MFMA, lane l holding key l%16 and channels 32j + 8(l/16) .. +8 at step
+// j, i.e. 64 contiguous bytes of one row per lane and load instruction.  The
+// query (two 16-head halves, the A operands) sits in LDS.  ReLU(dot) * w is
+// reduced over the heads in the accumulator's layout (8 heads per lane plus
+// two cross-lane adds), and the scores of a wave's four tiles leave as one
+// fully coalesced 256-byte store.  The same pass accumulates ||K_s||^2 so that
+// a rigorous per-query bound on |fp32 score - fp64 score| can be formed
+// without a second read of the keys.
 #include "csa2_common.h"
 
 namespace csa2 {
 
 constexpr int kScanThreads = 256;  // 4 waves
 constexpr int kScanWaves = kScanThreads / 64;
-
+constexpr int kScanTileKeys = 16;  // keys per MFMA tile
+constexpr int kScanTiles = 4;      // tiles per wave per iteration: 64 keys, 16 KiB
+constexpr int kScanWaveKeys = kScanTileKeys * kScanTiles;
 constexpr int kQRowPad = kIdxDim + 8;  // bf16 per q row in LDS (272 B: spreads rows over banks)
-constexpr int kTilesPerIter = 2;       // 32-key tiles loaded per wave per iteration (16 KiB)
+constexpr int kScanBlocks = 2048;      // blocks per launch the grid aims for (8 per CU)
 
 // One block: sequence b = blockIdx.y, query group blockIdx.z (QG queries of
-// that sequence), tiles [x*tpb, (x+1)*tpb) of 32 keys.  The group's queries
-// sit in LDS (MFMA A operands are read with ds_read_b128); registers hold
-// only the keys in flight, so many waves fit per SIMD and each keeps 16 KiB
-// of keys outstanding.
+// that sequence), keys [x*kpb, (x+1)*kpb).  Each wave takes 64 consecutive
+// keys per iteration; the block's waves cover 256 consecutive keys.
+// Accumulator register i of half m holds head 16m + 4(l/16) + i of key l%16.
 template <int QG>
 __global__ __launch_bounds__(kScanThreads, QG == 1 ? 4 : 2) void idx_scan_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos, int ratio,
-    int q_per_seq, int64_t N, int tiles_per_block, float* __restrict__ scores,
+    int q_per_seq, int64_t N, int keys_per_block, float* __restrict__ scores,
     float* __restrict__ norm_partial) {
   __shared__ __attribute__((aligned(16))) uint16_t sq[QG * kIdxHeads * kQRowPad];
   __shared__ float red[kScanWaves];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int col = lane & 31;  // key within the tile (MFMA column)
-  const int g = lane >> 5;    // which half of the 128 channels this lane holds
+  const int col = lane & 15;  // key within a tile
+  const int g = lane >> 4;    // channel group: 32j + 8g .. +8
   const int b = blockIdx.y;
 
   int64_t nvis[QG];
   int64_t trow[QG];
   bool valid[QG];
-  float wr[QG][16];
+  float wr[QG][8];
   int64_t nvis_max = 0;
 #pragma unroll
   for (int qq = 0; qq < QG; ++qq) {
@@ -59,50 +61,41 @@ __global__ __launch_bounds__(kScanThreads, QG == 1 ? 4 : 2) void idx_scan_kernel
       *reinterpret_cast<uint4*>(&sq[(qq * kIdxHeads + h) * kQRowPad + c8 * 8]) =
           *reinterpret_cast<const uint4*>(q_idx + ((size_t)t * kIdxHeads + h) * kIdxDim + c8 * 8);
     }
-    // accumulator register r holds head 8*(r/4) + 4*g + r%4 of key `col`
 #pragma unroll
-    for (int r = 0; r < 16; ++r) wr[qq][r] = w_idx[(size_t)t * kIdxHeads + 8 * (r >> 2) + 4 * g + (r & 3)];
+    for (int r = 0; r < 8; ++r) wr[qq][r] = w_idx[(size_t)t * kIdxHeads + 16 * (r >> 2) + 4 * g + (r & 3)];
     nvis[qq] = valid[qq] ? n_visible(q_pos, t, ratio, N) : 0;
     nvis_max = nvis[qq] > nvis_max ? nvis[qq] : nvis_max;
   }
   __syncthreads();
 
-  const int64_t tiles = (N + 31) >> 5;
-  const int64_t tile0 = (int64_t)blockIdx.x * tiles_per_block;
-  const int64_t tile1 = tile0 + tiles_per_block < tiles ? tile0 + tiles_per_block : tiles;
-  const uint16_t* kseq = k_idx + (size_t)b * N * kIdxDim + g * 64;
+  const int64_t key0 = (int64_t)blockIdx.x * keys_per_block;
+  const int64_t key1 = key0 + keys_per_block < N ? key0 + keys_per_block : N;
+  const uint16_t* kseq = k_idx + (size_t)b * N * kIdxDim + g * 8;
   const int64_t last = (nvis_max < N ? (nvis_max > 0 ? nvis_max : 1) : N) - 1;  // last row worth reading
   float maxn2 = 0.f;
 
-  // The wave's tiles: tile0 + wave*2 + {0,1} + 8*i (adjacent pairs, blocks of 8 per iteration).
-  for (int64_t base = tile0 + kTilesPerIter * wave; base < tile1; base += kTilesPerIter * kScanWaves) {
+  for (int64_t base = key0 + kScanWaveKeys * wave; base < key1; base += kScanWaveKeys * kScanWaves) {
     // Unconditional loads keep the code branch-free: keys past the end or past
     // every query's visibility re-read row `last`, which is already cached.
-    uint4 kv[kTilesPerIter][8];
+    uint4 kv[kScanTiles][4];
 #pragma unroll
-    for (int u = 0; u < kTilesPerIter; ++u) {
-      const int64_t s = (base + u) * 32 + col;
-      const uint4* kp = reinterpret_cast<const uint4*>(kseq + (size_t)(s < last ? s : last) * kIdxDim);
+    for (int u = 0; u < kScanTiles; ++u) {
+      const int64_t s = base + u * kScanTileKeys + col;
+      const uint16_t* kp = kseq + (size_t)(s < last ? s : last) * kIdxDim;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) kv[u][j] = kp[j];
+      for (int j = 0; j < 4; ++j) kv[u][j] = *reinterpret_cast<const uint4*>(kp + 32 * j);
     }
+    float sc[QG][kScanTiles];
 #pragma unroll
-    for (int u = 0; u < kTilesPerIter; ++u) {
-      const int64_t tile = base + u;
-      if (tile >= tile1) break;
-      const int64_t s = tile * 32 + col;
-      if (tile * 32 >= nvis_max) {  // no query of the group sees any key of this tile
-        if (g == 0 && s < N) {
+    for (int u = 0; u < kScanTiles; ++u) {
 #pragma unroll
-          for (int qq = 0; qq < QG; ++qq)
-            if (valid[qq]) scores[trow[qq] + s] = -INFINITY;
-        }
-        continue;
-      }
-      // ||K_s||^2: 64 channels per lane with bf16 dot2, plus the other half of the row
+      for (int qq = 0; qq < QG; ++qq) sc[qq][u] = -INFINITY;
+      const int64_t s = base + u * kScanTileKeys + col;
+      if (base + u * kScanTileKeys >= nvis_max) continue;  // no query of the group sees this tile
+      // ||K_s||^2: 32 channels per lane with bf16 dot2, then the other three groups
       float n2 = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4; ++j) {
         const uint32_t w4[4] = {kv[u][j].x, kv[u][j].y, kv[u][j].z, kv[u][j].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -111,24 +104,40 @@ __global__ __launch_bounds__(kScanThreads, QG == 1 ? 4 : 2) void idx_scan_kernel
           n2 = __builtin_amdgcn_fdot2_f32_bf16(p, p, n2, false);
         }
       }
+      n2 += __shfl_xor(n2, 16, 64);
       n2 += __shfl_xor(n2, 32, 64);
-      if (s < N) maxn2 = fmaxf(maxn2, n2);
+      if (s < key1) maxn2 = fmaxf(maxn2, n2);
 #pragma unroll
       for (int qq = 0; qq < QG; ++qq) {
         if (!valid[qq]) continue;
-        const uint16_t* qrow = &sq[(qq * kIdxHeads + col) * kQRowPad + g * 64];
-        floatx16 acc = {};
+        floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+        const uint16_t* q0 = &sq[(qq * kIdxHeads + col) * kQRowPad + 8 * g];
+        const uint16_t* q1 = q0 + 16 * kQRowPad;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(qrow + j * 8);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16x8(kv[u][j]), acc, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8 bk = as_bf16x8(kv[u][j]);
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(q0 + 32 * j), bk, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(q1 + 32 * j), bk, acc1, 0, 0, 0);
         }
         float part = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) part = fmaf(wr[qq][r], fmaxf(acc[r], 0.f), part);
+        for (int r = 0; r < 4; ++r) {
+          part = fmaf(wr[qq][r], fmaxf(acc0[r], 0.f), part);
+          part = fmaf(wr[qq][4 + r], fmaxf(acc1[r], 0.f), part);
+        }
+        part += __shfl_xor(part, 16, 64);
         part += __shfl_xor(part, 32, 64);
-        if (g == 0 && s < N) scores[trow[qq] + s] = (s < nvis[qq]) ? part : -INFINITY;
+        sc[qq][u] = (s < nvis[qq]) ? part : -INFINITY;
       }
+    }
+    // every lane holds the score of key `col` of each tile; lane l stores key l of the 64
+    const int64_t so = base + lane;
+#pragma unroll
+    for (int qq = 0; qq < QG; ++qq) {
+      float v = sc[qq][0];
+#pragma unroll
+      for (int u = 1; u < kScanTiles; ++u) v = g == u ? sc[qq][u] : v;
+      if (valid[qq] && so < key1) scores[trow[qq] + so] = v;
     }
   }
 
@@ -145,10 +154,10 @@ __global__ __launch_bounds__(kScanThreads, QG == 1 ? 4 : 2) void idx_scan_kernel
 
 // eps_t = 2^-14 * sum_h |w_h| ||q_h||_2 * max_s ||K_s||_2 + 2^-100 (1 + sum_h |w_h|), rounded up.
 //
-// Derivation: the bf16 products are exact in fp32; eight chained MFMA steps
-// of 16 products each, even with every addition rounded or truncated, stay
-// within 136 * 2^-23 * sum_c |q_c K_c| <= 2^-15.9 ||q_h|| ||K_s|| (Cauchy-
-// Schwarz); ReLU is 1-Lipschitz; the fp32 head reduction (17 roundings) adds at
+// Derivation: the bf16 products are exact in fp32; four chained MFMA steps
+// of 32 products each (at most 132 additions on any path), even with every
+// addition rounded or truncated, stay within 136 * 2^-23 * sum_c |q_c K_c|
+// <= 2^-15.9 ||q_h|| ||K_s|| (Cauchy-Schwarz); ReLU is 1-Lipschitz; the fp32 head reduction (17 roundings) adds at
 // most 2^-19.9 sum_h |w_h| |dot_h|; the fp64 reference itself is within
 // 2^-44 of the exact value.  The sum is below 1.1 * 2^-15; 2^-14 leaves a
 // factor 1.8 of margin.  The absolute term covers products that flush to zero.
@@ -194,7 +203,7 @@ struct IndexPlan {
   int groups = 1;         // gridDim.z
   int B = 1;              // gridDim.y
   int blocks_x = 1;       // gridDim.x
-  int tiles_per_block = 4;
+  int keys_per_block = kScanWaveKeys * kScanWaves;
 };
 
 static bool index_plan(int32_t T, int32_t q_per_seq, int64_t N, IndexPlan* p) {
@@ -202,17 +211,16 @@ static bool index_plan(int32_t T, int32_t q_per_seq, int64_t N, IndexPlan* p) {
   p->qg = q_per_seq == 1 ? 1 : q_per_seq == 2 ? 2 : 4;
   p->groups = (q_per_seq + p->qg - 1) / p->qg;
   p->B = T / q_per_seq;
-  const int64_t tiles = (N + 31) / 32;
-  // aim for ~2048 blocks in flight over 256 CUs; at least 4 tiles (one per wave) per block
-  int64_t want = (2048 + (int64_t)p->B * p->groups - 1) / ((int64_t)p->B * p->groups);
-  const int64_t per_iter = (int64_t)kTilesPerIter * kScanWaves;
-  int64_t max_blocks = (tiles + per_iter - 1) / per_iter;
+  // aim for ~2048 blocks over 256 CUs; each block a multiple of one iteration of its waves
+  const int64_t per_iter = (int64_t)kScanWaveKeys * kScanWaves;
+  int64_t want = (kScanBlocks + (int64_t)p->B * p->groups - 1) / ((int64_t)p->B * p->groups);
+  const int64_t max_blocks = (N + per_iter - 1) / per_iter;
   if (want > max_blocks) want = max_blocks;
   if (want < 1) want = 1;
-  int64_t tpb = (tiles + want - 1) / want;
-  tpb = (tpb + per_iter - 1) / per_iter * per_iter;
-  p->tiles_per_block = (int)tpb;
-  p->blocks_x = (int)((tiles + tpb - 1) / tpb);
+  int64_t kpb = (N + want - 1) / want;
+  kpb = (kpb + per_iter - 1) / per_iter * per_iter;
+  p->keys_per_block = (int)kpb;
+  p->blocks_x = (int)((N + kpb - 1) / kpb);
   return p->B <= 65535 && p->groups <= 65535;
 }
 
@@ -246,14 +254,14 @@ extern "C" csa2_status csa2_index(const void* q_idx, const float* w_idx, const v
   const uint16_t* q = (const uint16_t*)q_idx;
   const uint16_t* k = (const uint16_t*)k_idx;
   if (p.qg == 1)
-    hipLaunchKernelGGL(idx_scan_kernel<1>, grid, dim3(kScanThreads), 0, st, q, w_idx, k, q_pos, ratio, q_per_seq,
-                       N, p.tiles_per_block, scores, partial);
+    hipLaunchKernelGGL(idx_scan_kernel<1>, grid, dim3(kScanThreads), 0, st, q, w_idx, k, q_pos, ratio, q_per_seq, N,
+                       p.keys_per_block, scores, partial);
   else if (p.qg == 2)
-    hipLaunchKernelGGL(idx_scan_kernel<2>, grid, dim3(kScanThreads), 0, st, q, w_idx, k, q_pos, ratio, q_per_seq,
-                       N, p.tiles_per_block, scores, partial);
+    hipLaunchKernelGGL(idx_scan_kernel<2>, grid, dim3(kScanThreads), 0, st, q, w_idx, k, q_pos, ratio, q_per_seq, N,
+                       p.keys_per_block, scores, partial);
   else
-    hipLaunchKernelGGL(idx_scan_kernel<4>, grid, dim3(kScanThreads), 0, st, q, w_idx, k, q_pos, ratio, q_per_seq,
-                       N, p.tiles_per_block, scores, partial);
+    hipLaunchKernelGGL(idx_scan_kernel<4>, grid, dim3(kScanThreads), 0, st, q, w_idx, k, q_pos, ratio, q_per_seq, N,
+                       p.keys_per_block, scores, partial);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   hipLaunchKernelGGL(idx_finalize_kernel, dim3(T), dim3(64), 0, st, q, w_idx, (const float*)partial, q_per_seq,
                      p.groups * p.blocks_x, err_bound);
