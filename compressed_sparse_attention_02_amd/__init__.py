@@ -10,16 +10,19 @@ from __future__ import annotations
 
 import ctypes
 import os
+from typing import NamedTuple, Optional
 
 import torch
 
 __all__ = [
-    "Csa2Error", "lib", "library_path", "csa2_index", "csa2_topk", "csa2_attend_fp4", "csa2_reuse_attend",
-    "index_workspace_bytes", "topk_workspace_bytes", "topk_min_workspace_bytes", "attend_workspace_bytes",
-    "IDX_HEADS", "IDX_DIM", "HEADS", "DIM", "TOPK", "MAX_WINDOW", "MAX_LAYERS",
+    "Csa2Error", "IndexResult", "lib", "library_path", "csa2_index", "csa2_topk", "csa2_attend_fp4",
+    "csa2_reuse_attend", "tile_max_ld", "index_workspace_bytes", "topk_workspace_bytes", "topk_min_workspace_bytes",
+    "attend_workspace_bytes", "IDX_HEADS", "IDX_DIM", "HEADS", "DIM", "TOPK", "MAX_WINDOW", "MAX_LAYERS", "TILE",
+    "TOPK_ROW_MAX",
 ]
 
 IDX_HEADS, IDX_DIM, HEADS, DIM, TOPK, MAX_WINDOW, MAX_LAYERS = 32, 128, 64, 512, 512, 128, 8
+TILE, TOPK_ROW_MAX = 16, 36864
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libcsa2.so")
@@ -30,17 +33,26 @@ _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ct
 _SIGNATURES = {
     "csa2_status_string": ([_i32], ctypes.c_char_p),
     "csa2_version": ([], ctypes.c_char_p),
+    "csa2_tile_max_ld": ([_i64], _i64),
     "csa2_index_workspace_bytes": ([_i32, _i32, _i64], _sz),
-    "csa2_index": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _sz, _vp], _i32),
+    "csa2_index": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "csa2_topk_workspace_bytes": ([_i32, _i64, _i32], _sz),
     "csa2_topk_min_workspace_bytes": ([_i32, _i64, _i32], _sz),
-    "csa2_topk": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp, _vp, _sz, _vp], _i32),
+    "csa2_topk": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp, _vp, _sz, _vp], _i32),
     "csa2_attend_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
     "csa2_attend_fp4": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp,
                          _vp, _sz, _vp], _i32),
     "csa2_reuse_attend": ([_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i64, _i32, _i32, _i32, _vp,
                            _vp, _vp, _sz, _vp], _i32),
 }
+
+
+class IndexResult(NamedTuple):
+    """Outputs of csa2_index: scores fp32 [T][N] (None unless requested), tile maxima fp32
+    [T][tile_max_ld(N)], error bound fp32 [T]."""
+    scores: Optional[torch.Tensor]
+    tile_max: torch.Tensor
+    err_bound: torch.Tensor
 
 
 class Csa2Error(RuntimeError):
@@ -108,6 +120,11 @@ def _raise(status, where):
         raise Csa2Error(status, where)
 
 
+def tile_max_ld(N: int) -> int:
+    """Row stride (floats) of the tile-maximum array: 4 * ceil(N / 64)."""
+    return lib().csa2_tile_max_ld(N)
+
+
 def index_workspace_bytes(T: int, q_per_seq: int, N: int) -> int:
     return lib().csa2_index_workspace_bytes(T, q_per_seq, N)
 
@@ -124,10 +141,10 @@ def attend_workspace_bytes(T: int, k: int = TOPK, window: int = MAX_WINDOW, n_la
     return lib().csa2_attend_workspace_bytes(T, k, window, n_layers)
 
 
-def csa2_index(q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, scores=None, err_bound=None,
-               workspace=None):
-    """Indexer scores.  q_idx bf16 [T][32][128], w_idx fp32 [T][32], k_idx bf16 [B][N][128],
-    q_pos int32 [T] or None.  Returns (scores fp32 [T][N], err_bound fp32 [T])."""
+def csa2_index(q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, want_scores=True, scores=None,
+               tile_max=None, err_bound=None, workspace=None) -> IndexResult:
+    """Indexer scan.  q_idx bf16 [T][32][128], w_idx fp32 [T][32], k_idx bf16 [B][N][128],
+    q_pos int32 [T] or None.  Writes the full score matrix only if want_scores (or `scores` is given)."""
     T = q_idx.shape[0]
     B, N = k_idx.shape[0], k_idx.shape[1]
     dev = q_idx.device
@@ -138,28 +155,35 @@ def csa2_index(q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, scores=Non
         _check(q_pos, "q_pos", (T,), dtype=torch.int32, device=dev)
     if B * q_per_seq != T:
         raise ValueError(f"T={T} must equal B*q_per_seq={B}*{q_per_seq}")
-    if scores is None:
+    if scores is None and want_scores:
         scores = torch.empty((T, N), dtype=torch.float32, device=dev)
+    if tile_max is None:
+        tile_max = torch.empty((T, tile_max_ld(N)), dtype=torch.float32, device=dev)
     if err_bound is None:
         err_bound = torch.empty((T,), dtype=torch.float32, device=dev)
-    _check(scores, "scores", (T, N), dtype=torch.float32, device=dev)
+    if scores is not None:
+        _check(scores, "scores", (T, N), dtype=torch.float32, device=dev)
+    _check(tile_max, "tile_max", (T, tile_max_ld(N)), dtype=torch.float32, device=dev)
     _check(err_bound, "err_bound", (T,), dtype=torch.float32, device=dev)
     nbytes = index_workspace_bytes(T, q_per_seq, N)
     workspace = _ws(nbytes, dev, workspace)
     st = lib().csa2_index(_p(q_idx), _p(w_idx), _p(k_idx), _p(q_pos), ratio, T, q_per_seq, N, _p(scores),
-                          _p(err_bound), _p(workspace), _nbytes(workspace), _stream(q_idx))
+                          _p(tile_max), _p(err_bound), _p(workspace), _nbytes(workspace), _stream(q_idx))
     _raise(st, "csa2_index")
-    return scores, err_bound
+    return IndexResult(scores, tile_max, err_bound)
 
 
-def csa2_topk(scores, err_bound, q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, k=TOPK, indices=None,
-              workspace=None):
-    """Exact top-k (ascending indices, -1 padded) -> int32 [T][k]."""
-    T, N = scores.shape
-    B = k_idx.shape[0]
-    dev = scores.device
-    _check(scores, "scores", (T, N), dtype=torch.float32)
-    _check(err_bound, "err_bound", (T,), dtype=torch.float32, device=dev)
+def csa2_topk(scores, tile_max, err_bound, q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, k=TOPK,
+              indices=None, workspace=None):
+    """Exact top-k (ascending indices, -1 padded) -> int32 [T][k].  scores may be None (the
+    selection then works from tile_max and the keys)."""
+    T = err_bound.shape[0]
+    B, N = k_idx.shape[0], k_idx.shape[1]
+    dev = err_bound.device
+    if scores is not None:
+        _check(scores, "scores", (T, N), dtype=torch.float32, device=dev)
+    _check(tile_max, "tile_max", (T, tile_max_ld(N)), dtype=torch.float32, device=dev)
+    _check(err_bound, "err_bound", (T,), dtype=torch.float32)
     _check(q_idx, "q_idx", (T, IDX_HEADS, IDX_DIM), elem_size=2, device=dev)
     _check(w_idx, "w_idx", (T, IDX_HEADS), dtype=torch.float32, device=dev)
     _check(k_idx, "k_idx", (B, N, IDX_DIM), elem_size=2, device=dev)
@@ -172,8 +196,9 @@ def csa2_topk(scores, err_bound, q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per
         workspace = _ws(topk_workspace_bytes(T, N, k), dev, None)
     elif _nbytes(workspace) < topk_min_workspace_bytes(T, N, k):
         raise ValueError("workspace below csa2_topk_min_workspace_bytes")
-    st = lib().csa2_topk(_p(scores), _p(err_bound), _p(q_idx), _p(w_idx), _p(k_idx), _p(q_pos), ratio, T,
-                         q_per_seq, N, k, _p(indices), _p(workspace), _nbytes(workspace), _stream(scores))
+    st = lib().csa2_topk(_p(scores), _p(tile_max), _p(err_bound), _p(q_idx), _p(w_idx), _p(k_idx), _p(q_pos),
+                         ratio, T, q_per_seq, N, k, _p(indices), _p(workspace), _nbytes(workspace),
+                         _stream(err_bound))
     _raise(st, "csa2_topk")
     return indices
 

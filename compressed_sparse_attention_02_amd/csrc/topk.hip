@@ -5,50 +5,49 @@
 // sec. 2.3: each query keeps its top-k entries, k = 512 per sec. 4.2.1).
 //
 // The fp32 scores of csa2_index differ from the fp64 reference by at most
-// eps (err_bound).  Let T^ be the k-th largest fp32 score.  Then
-//   * every true top-k member has fp32 score >= T^ - 2 eps  (k entries have
-//     fp32 >= T^, hence fp64 >= T^ - eps; a member's fp64 is at least the
-//     k-th fp64 value);
-//   * every entry with fp32 score > T^ + 2 eps is a member (fewer than k
-//     entries have fp32 > T^).
-// Any tau <= T^ therefore gives a candidate set {fp32 >= tau - 2 eps} that
-// contains the whole answer.  Two regimes:
+// eps (err_bound).  If k distinct entries have fp32 score >= tau, then the
+// k-th largest fp64 score T^ satisfies T^ >= tau - eps, so every true top-k
+// member has fp32 score >= tau - 2 eps: {fp32 >= tau - 2 eps} is a candidate
+// set that contains the whole answer.  Two regimes:
 //
-//  * Large rows (N > kSmallMax): the row is cut into M = 4096 groups, group j
-//    holding the float4 runs j, j+M, j+2M, ... (so every group samples the
-//    whole row); tau = a lower bound of the k-th largest group maximum, which
-//    is <= T^ because those k maxima are k distinct entries.  One pass
-//    computes the maxima (topk_gmax_kernel), one block per query brackets
-//    tau (topk_tau_kernel), one pass compacts the candidates
-//    (topk_compact_kernel), and one block per query finishes
-//    (topk_finish_kernel).  For i.i.d. scores about 1.1 k entries pass.
-//  * Small rows (N <= kSmallMax, e.g. a prefill chunk): one block per query
-//    loads the visible scores into LDS and does everything there
-//    (topk_small_kernel).
-//
-// The finish, in both regimes: bracket T^ among the candidates (lo <= T^ <= hi,
-// two levels of 256 value bins; the arguments above hold with T^ replaced by
-// hi for the sure side and by lo for the candidate side), accept entries
-// above hi + 2 eps, rescore the band [lo - 2 eps, hi + 2 eps] in fp64 with the
-// reference's exact operation sequence (fma per channel in order, then fma per
-// head in order; IEEE fma is correctly rounded on both sides) and take the
-// rest by (fp64 score desc, index asc).  If the candidates or the band exceed
-// capacity, the same block falls back to exact streaming passes over the
-// whole row (slow, exact).
-#include "csa2_common.h"
+//  * Tile regime (any N; the only one without a score matrix).  tau is a
+//    lower bound of the k-th largest of a set of tile maxima (those are k
+//    distinct entries): all maxima of the visible tiles when there are at
+//    most 16384 tiles, else the maxima of 4096 groups, group j holding the
+//    4-tile runs j, j+4096, j+8192, ... (every group samples the whole row).
+//    topk_tau_kernel finds tau (one block per query); topk_cand_kernel
+//    (16384 entries per block) re-derives the fp32 scores of the tiles whose
+//    maximum reaches tau - 2 eps with the scan's own MFMA code, keeps the
+//    entries that reach it, computes their fp64 scores with the reference's
+//    exact operation sequence, and appends them in index order to a block
+//    segment; topk_select_kernel (one block per query) selects the k largest
+//    fp64 keys among the candidates and writes them in index order.  For
+//    i.i.d. scores about 1.1 k entries are candidates.  If they exceed the
+//    workspace or LDS capacity, the same block falls back to exact radix
+//    passes over the candidate tiles (slow, exact).
+//  * Row regime (scores given, N <= kSmallMax, e.g. a prefill chunk): one
+//    block per query loads the visible scores into LDS, brackets the k-th
+//    largest fp32 value (lo <= T^ <= hi, two levels of 256 value bins), accepts
+//    entries above hi + 2 eps, rescores the band [lo - 2 eps, hi + 2 eps] in
+//    fp64 and takes the rest by (fp64 score desc, index asc).
+#include "idx_tile.h"
 
 namespace csa2 {
 
-constexpr int kFinThreads = 1024;
-constexpr int kGroups = 4096;            // large regime: group maxima per query
-constexpr int kGroupThreads = 256;       // gmax block: 64 groups x 4 sub-ranges
-constexpr int kCompactThreads = 256;
-constexpr int kCompactChunk = 8192;      // entries per compact block
-constexpr int kBandLds = 2048;           // band entries resolved in LDS
-constexpr int kCandLds = 4096;           // candidates handled in LDS by the finish
-constexpr int kDefaultCap = 2048;        // default candidate capacity per query
-constexpr int kSmallMax = 36864;         // small regime: visible scores kept in LDS
-constexpr int kHdrWords = 64;            // per query: [0] candidate count, [1] tau (fp32 bits)
+constexpr int kFinThreads = 1024;        // row-regime block
+constexpr int kBandLds = 2048;           // band entries resolved in LDS (row regime)
+constexpr int kSmallMax = CSA2_TOPK_ROW_MAX;  // row regime: visible scores kept in LDS
+
+constexpr int kTauThreads = 1024;
+constexpr int kTauDirect = 16384;        // up to this many tiles, tau comes from the tile maxima themselves
+constexpr int kTauGroups = 4096;         // otherwise from 4096 strided group maxima
+constexpr int kCandThreads = 256;
+constexpr int kCandTiles = 1024;         // tiles (16384 entries) per candidate block
+constexpr int kSelThreads = 256;
+constexpr int kSelLds = 4096;            // candidates a select block holds in LDS
+constexpr int kSelBlocks = 4096;         // candidate blocks per query the select block can index
+constexpr int kDefaultCap = 4096;        // default candidate capacity per query
+constexpr int kHdrWords = 16;            // per query: [0] candidate count, [1] tau (fp32 bits), [2] overflow
 
 // ---------------------------------------------------------------- helpers
 
@@ -360,224 +359,7 @@ __device__ __forceinline__ void band_bounds(float t_lo, float t_hi, float eps, d
   if (!(*hi >= (double)t_hi)) *hi = INFINITY;
 }
 
-// ----------------------------------------------------------- large regime
-
-struct LargeWs {
-  uint32_t* hdr;   // [T][kHdrWords]
-  float* gmax;     // [T][kGroups]
-  uint32_t* cidx;  // [T][cap]
-  float* cval;     // [T][cap]
-};
-
-__host__ __device__ __forceinline__ size_t large_ws_fixed(int T) {
-  return (size_t)T * (kHdrWords * 4 + kGroups * 4);
-}
-__device__ __forceinline__ LargeWs large_ws(void* base, int T, int64_t cap) {
-  LargeWs w;
-  w.hdr = (uint32_t*)base;
-  w.gmax = (float*)(w.hdr + (size_t)T * kHdrWords);
-  w.cidx = (uint32_t*)(w.gmax + (size_t)T * kGroups);
-  w.cval = (float*)(w.cidx + (size_t)T * cap);
-  return w;
-}
-
-// Group maxima: group j = float4 runs j, j+M, j+2M, ... of the visible row.
-// grid (kGroups/64, T), 256 threads = 64 groups x 4 interleaved sub-ranges.
-template <bool VEC>
-__global__ __launch_bounds__(kGroupThreads) void topk_gmax_kernel(const float* __restrict__ scores,
-                                                                  const int32_t* __restrict__ q_pos, int ratio,
-                                                                  int64_t N, int k, void* ws, int T, int64_t cap) {
-  const int t = blockIdx.y;
-  const int64_t nv = n_visible(q_pos, t, ratio, N);
-  if (nv <= k) return;
-  LargeWs w = large_ws(ws, T, cap);
-  if (blockIdx.x == 0 && threadIdx.x == 0) w.hdr[(size_t)t * kHdrWords] = 0u;  // candidate count
-  const int j = blockIdx.x * 64 + (threadIdx.x & 63);
-  const int r = threadIdx.x >> 6;
-  const float* row = scores + (size_t)t * N;
-  const int64_t n4 = (nv + 3) / 4;
-  float m = -INFINITY;
-  for (int64_t tile = j + (int64_t)kGroups * r; tile < n4; tile += (int64_t)kGroups * 4 * 4) {
-    float4 x[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t tl = tile + (int64_t)kGroups * 4 * u;
-      const int64_t s = 4 * tl;
-      if (VEC && s + 3 < nv) {
-        x[u] = *reinterpret_cast<const float4*>(row + s);
-      } else {
-        x[u].x = (tl < n4 && s < nv) ? row[s] : -INFINITY;
-        x[u].y = (tl < n4 && s + 1 < nv) ? row[s + 1] : -INFINITY;
-        x[u].z = (tl < n4 && s + 2 < nv) ? row[s + 2] : -INFINITY;
-        x[u].w = (tl < n4 && s + 3 < nv) ? row[s + 3] : -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) m = fmaxf(m, fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w)));
-  }
-  __shared__ float part[4][64];
-  part[r][threadIdx.x & 63] = m;
-  __syncthreads();
-  if (r == 0) {
-    const int l = threadIdx.x;
-    w.gmax[(size_t)t * kGroups + j] = fmaxf(fmaxf(part[0][l], part[1][l]), fmaxf(part[2][l], part[3][l]));
-  }
-}
-
-// tau <= T^: a lower bound of the k-th largest group maximum, with at least
-// k maxima (k distinct entries) >= tau; -inf when fewer than k groups are
-// non-empty.  grid T, 1024 threads; the maxima are staged in LDS.
-__global__ __launch_bounds__(kFinThreads) void topk_tau_kernel(const int32_t* __restrict__ q_pos, int ratio,
-                                                               int64_t N, int k, void* ws, int T, int64_t cap) {
-  __shared__ SelLds sel;
-  __shared__ float g[kGroups];
-  const int t = blockIdx.x;
-  const int64_t nv = n_visible(q_pos, t, ratio, N);
-  if (nv <= k) return;
-  LargeWs w = large_ws(ws, T, cap);
-  const int64_t ng = (nv + 3) / 4 < kGroups ? (nv + 3) / 4 : kGroups;
-  float tau = -INFINITY;
-  if (ng >= k) {
-    for (int i = threadIdx.x; i < ng; i += kFinThreads) g[i] = w.gmax[(size_t)t * kGroups + i];
-    __syncthreads();
-    float lo, hi;
-    bracket_kth(sel, ng, (uint32_t)k, [&](int64_t i) { return g[i]; }, true, &lo, &hi);
-    tau = lo;
-  }
-  if (threadIdx.x == 0) w.hdr[(size_t)t * kHdrWords + 1] = __float_as_uint(tau);
-}
-
-// Candidates: every visible entry with score >= tau - 2 eps (block-aggregated
-// append).  grid (chunks, T), 256 threads x 32 entries.
-template <bool VEC>
-__global__ __launch_bounds__(kCompactThreads) void topk_compact_kernel(const float* __restrict__ scores,
-                                                                       const float* __restrict__ err_bound,
-                                                                       const int32_t* __restrict__ q_pos, int ratio,
-                                                                       int64_t N, int k, void* ws, int T,
-                                                                       int64_t cap) {
-  const int t = blockIdx.y;
-  const int64_t nv = n_visible(q_pos, t, ratio, N);
-  const int64_t s0 = (int64_t)blockIdx.x * kCompactChunk;
-  if (nv <= k || s0 >= nv) return;
-  LargeWs w = large_ws(ws, T, cap);
-  uint32_t* hdr = w.hdr + (size_t)t * kHdrWords;
-  const float* row = scores + (size_t)t * N;
-  constexpr int kVec = kCompactChunk / kCompactThreads / 4;  // 8 float4 per thread
-  float v[4 * kVec];
-  // this block's scores: all loads in flight while tau is being found
-#pragma unroll
-  for (int i = 0; i < kVec; ++i) {
-    const int64_t s = s0 + 4 * ((int64_t)i * kCompactThreads + threadIdx.x);
-    if (VEC && s + 3 < nv) {
-      const float4 x = *reinterpret_cast<const float4*>(row + s);
-      v[4 * i] = x.x; v[4 * i + 1] = x.y; v[4 * i + 2] = x.z; v[4 * i + 3] = x.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * i + e] = (s + e < nv) ? row[s + e] : -INFINITY;
-    }
-  }
-  const float tau = __uint_as_float(hdr[1]);
-  const double thr = next_down((double)tau - 2.0 * (double)err_bound[t]);
-  __shared__ uint32_t s_cnt, s_base;
-  __shared__ uint32_t s_idx[1024];
-  __shared__ float s_val[1024];
-  if (threadIdx.x == 0) s_cnt = 0;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4 * kVec; ++i) {
-    const int64_t s = s0 + 4 * ((int64_t)(i >> 2) * kCompactThreads + threadIdx.x) + (i & 3);
-    if (s < nv && (double)v[i] >= thr) {
-      const uint32_t p = atomicAdd(&s_cnt, 1u);
-      if (p < 1024) {
-        s_idx[p] = (uint32_t)s;
-        s_val[p] = v[i];
-      } else {  // rare: a block with more than 1024 candidates appends directly
-        const uint32_t pos = atomicAdd(&hdr[0], 1u);
-        if (pos < (uint64_t)cap) {
-          w.cidx[(size_t)t * cap + pos] = (uint32_t)s;
-          w.cval[(size_t)t * cap + pos] = v[i];
-        }
-      }
-    }
-  }
-  __syncthreads();
-  const uint32_t n = s_cnt < 1024 ? s_cnt : 1024;
-  if (threadIdx.x == 0 && n) s_base = atomicAdd(&hdr[0], n);
-  __syncthreads();
-  for (uint32_t i = threadIdx.x; i < n; i += kCompactThreads) {
-    const uint32_t pos = s_base + i;
-    if (pos < (uint64_t)cap) {
-      w.cidx[(size_t)t * cap + pos] = s_idx[i];
-      w.cval[(size_t)t * cap + pos] = s_val[i];
-    }
-  }
-}
-
-struct LargeFinLds {
-  FinLds f;
-  FinTail tail;
-  alignas(16) float cval[kCandLds];
-  uint32_t cidx[kCandLds];
-};
-
-__global__ __launch_bounds__(kFinThreads) void topk_finish_kernel(
-    const float* __restrict__ scores, const float* __restrict__ err_bound, const uint16_t* __restrict__ q_idx,
-    const float* __restrict__ w_idx, const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
-    int ratio, int q_per_seq, int64_t N, int k, int32_t* __restrict__ indices, void* ws, int T, int64_t cap) {
-  __shared__ LargeFinLds L;
-  FinLds& sh = L.f;
-  FinTail& tl = L.tail;
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int64_t nv = n_visible(q_pos, t, ratio, N);
-  int32_t* out = indices + (size_t)t * k;
-  if (nv <= k) {
-    for (int i = tid; i < k; i += kFinThreads) out[i] = i < nv ? i : -1;
-    return;
-  }
-  const uint32_t kk = (uint32_t)k;
-  const int b = t / q_per_seq;
-  const uint16_t* qt = q_idx + (size_t)t * kIdxHeads * kIdxDim;
-  const float* wt = w_idx + (size_t)t * kIdxHeads;
-  const uint16_t* kb = k_idx + (size_t)b * N * kIdxDim;
-  const float* row = scores + (size_t)t * N;
-  LargeWs w = large_ws(ws, T, cap);
-  const uint32_t cnt = w.hdr[(size_t)t * kHdrWords];
-  const float eps = err_bound[t];
-  const bool fits = (int64_t)cnt <= cap && cnt <= kCandLds;
-  if (tid == 0) { sh.n_out = 0; sh.n_band = 0; }
-  if (fits) {
-    for (uint32_t i = tid; i < ((cnt + 3) & ~3u); i += kFinThreads) {
-      L.cval[i] = i < cnt ? w.cval[(size_t)t * cap + i] : -INFINITY;
-      L.cidx[i] = i < cnt ? w.cidx[(size_t)t * cap + i] : 0u;
-    }
-  }
-  __syncthreads();
-  float t_lo, t_hi;
-  if (fits) bracket_kth(sh.sel, cnt, kk, [&](int64_t i) { return L.cval[i]; }, false, &t_lo, &t_hi);
-  else bracket_kth(sh.sel, nv, kk, [&](int64_t i) { return row[i]; }, false, &t_lo, &t_hi);
-  double lo, hi;
-  band_bounds(t_lo, t_hi, eps, &lo, &hi);
-  bool fast = fits;
-  if (fast) {
-    for (uint32_t i = tid; i < cnt; i += kFinThreads) {
-      const double v = (double)L.cval[i];
-      if (v > hi) sh.out[atomicAdd(&sh.n_out, 1u)] = L.cidx[i];
-      else if (v >= lo) {
-        const uint32_t p = atomicAdd(&sh.n_band, 1u);
-        if (p < kBandLds) sh.band_idx[p] = L.cidx[i];
-      }
-    }
-    __syncthreads();
-    fast = sh.n_band <= kBandLds;
-    __syncthreads();
-  }
-  if (fast) finish_band(sh, tl, kk, qt, wt, kb);
-  else finish_streaming(sh, kk, row, nv, lo, hi, qt, wt, kb);
-  write_sorted(sh, tl, kk, k, out);
-}
-
-// ----------------------------------------------------------- small regime
+// ------------------------------------------------------------- row regime
 
 // One block per query; the visible scores live in LDS (the finishing tail
 // overlays them once they have been classified).
@@ -634,41 +416,595 @@ __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
   write_sorted(sh, tl, kk, k, out);
 }
 
+// ------------------------------------------------------------ tile regime
+
+// Workspace of the tile regime, per query: a header, one {offset, count}
+// record per candidate block, and `cap` candidates (fp64 score, index).
+struct TileWs {
+  uint32_t* hdr;    // [T][kHdrWords]
+  uint2* table;     // [T][nblk]
+  double* cscore;   // [T][cap]
+  uint32_t* cidx;   // [T][cap]
+};
+__host__ __device__ __forceinline__ int64_t cand_blocks(int64_t N) {
+  return ((N + kTileKeys - 1) / kTileKeys + kCandTiles - 1) / kCandTiles;
+}
+__host__ __device__ __forceinline__ size_t tile_ws_fixed(int T, int64_t N) {
+  return (size_t)T * (kHdrWords * 4 + (size_t)cand_blocks(N) * 8);
+}
+__device__ __forceinline__ TileWs tile_ws(void* base, int T, int64_t N, int64_t cap) {
+  TileWs w;
+  w.hdr = (uint32_t*)base;
+  w.table = (uint2*)(w.hdr + (size_t)T * kHdrWords);
+  w.cscore = (double*)(w.table + (size_t)T * cand_blocks(N));
+  w.cidx = (uint32_t*)(w.cscore + (size_t)T * cap);
+  return w;
+}
+
+// Block-wide exclusive prefix sum (all threads, blockDim.x a multiple of 64).
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    const uint32_t c = wsum[i];
+    off += i < wave ? c : 0u;
+    tot += c;
+  }
+  *total = tot;
+  return off + x - v;
+}
+
+// tau for each query (grid T, 1024 threads): a lower bound of the k-th
+// largest tile or group maximum such that at least k of those maxima are >=
+// tau; -inf when the visible row has fewer than k tiles.  Also resets the
+// query's candidate count and overflow flag.
+__global__ __launch_bounds__(kTauThreads) void topk_tau_kernel(const float* __restrict__ tile_max,
+                                                               const int32_t* __restrict__ q_pos, int ratio,
+                                                               int64_t N, int k, void* ws, int T, int64_t cap) {
+  __shared__ SelLds sel;
+  __shared__ float g[kTauDirect];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  TileWs w = tile_ws(ws, T, N, cap);
+  uint32_t* hdr = w.hdr + (size_t)t * kHdrWords;
+  const int64_t nv = n_visible(q_pos, t, ratio, N);
+  const int64_t ntv = (nv + kTileKeys - 1) / kTileKeys;
+  float tau = -INFINITY;
+  if (nv > k && ntv >= k) {
+    const float* row = tile_max + (size_t)t * tile_ld(N);
+    int64_t ng;
+    if (ntv <= kTauDirect) {
+      ng = ntv;
+      for (int64_t i = tid; i < ntv; i += kTauThreads) g[i] = row[i];
+    } else {
+      // group j = 4-tile runs j, j + G, j + 2G, ... (runs are 16-byte aligned)
+      ng = kTauGroups;
+      const int64_t nruns = (ntv + 3) / 4;
+      for (int j = tid; j < kTauGroups; j += kTauThreads) {
+        float m = -INFINITY;
+        for (int64_t r0 = j; r0 < nruns; r0 += 4 * (int64_t)kTauGroups) {
+          float4 x[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int64_t r = r0 + (int64_t)u * kTauGroups;
+            x[u] = r < nruns ? *reinterpret_cast<const float4*>(row + 4 * r)
+                             : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int64_t tl = 4 * (r0 + (int64_t)u * kTauGroups);
+            m = fmaxf(m, tl < ntv ? x[u].x : -INFINITY);
+            m = fmaxf(m, tl + 1 < ntv ? x[u].y : -INFINITY);
+            m = fmaxf(m, tl + 2 < ntv ? x[u].z : -INFINITY);
+            m = fmaxf(m, tl + 3 < ntv ? x[u].w : -INFINITY);
+          }
+        }
+        g[j] = m;
+      }
+    }
+    __syncthreads();
+    float lo, hi;
+    bracket_kth(sel, ng, (uint32_t)k, [&](int64_t i) { return g[i]; }, true, &lo, &hi);
+    tau = lo;
+  }
+  if (tid == 0) {
+    hdr[0] = 0u;
+    hdr[1] = __float_as_uint(tau);
+    hdr[2] = 0u;
+  }
+}
+
+// LDS of a candidate block.
+struct alignas(16) CandLds {
+  uint16_t sq[kIdxHeads * kQRowPad];
+  float w[kIdxHeads];
+  uint32_t wsum[kCandThreads / 64];
+  uint32_t base;
+  uint16_t ctile[kCandTiles];   // candidate tiles (offset in the block's range), ascending
+  uint16_t cmask[kCandTiles];   // entries of each candidate tile that reach the threshold
+  uint32_t eidx[kSelLds];       // passing entries, ascending
+  double escore[kSelLds];       // their fp64 scores
+};
+
+// Candidates of tiles [x*kCandTiles, (x+1)*kCandTiles) of query t
+// (grid (nblk, T), 256 threads).  Every block writes its table record.
+__global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
+    const float* __restrict__ tile_max, const float* __restrict__ err_bound, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ w_idx, const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
+    int ratio, int q_per_seq, int64_t N, int k, void* ws, int T, int64_t cap) {
+  __shared__ CandLds L;
+  const int t = blockIdx.y;
+  const int x = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  TileWs w = tile_ws(ws, T, N, cap);
+  uint32_t* hdr = w.hdr + (size_t)t * kHdrWords;
+  uint2* rec = w.table + (size_t)t * cand_blocks(N) + x;
+  const int64_t nv = n_visible(q_pos, t, ratio, N);
+  const int64_t ntv = (nv + kTileKeys - 1) / kTileKeys;
+  const int64_t tile0 = (int64_t)x * kCandTiles;
+  if (nv <= k || tile0 >= ntv) {
+    if (tid == 0) *rec = make_uint2(0u, 0u);
+    return;
+  }
+  const uint16_t* qt = q_idx + (size_t)t * kIdxHeads * kIdxDim;
+  stage_query(L.sq, qt, tid, kCandThreads);
+  if (tid < kIdxHeads) L.w[tid] = w_idx[(size_t)t * kIdxHeads + tid];
+  const float tau = __uint_as_float(hdr[1]);
+  const double thr = next_down((double)tau - 2.0 * (double)err_bound[t]);
+
+  // 1. candidate tiles, in order: thread tid owns tiles tile0 + 4 tid .. +3
+  const float* row = tile_max + (size_t)t * tile_ld(N);
+  uint32_t flags = 0;
+  {
+    const int64_t j = tile0 + 4 * tid;
+    if (j < ntv) {
+      const float4 m = *reinterpret_cast<const float4*>(row + j);
+      const float mv[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) flags |= (j + u < ntv && (double)mv[u] >= thr) ? (1u << u) : 0u;
+    }
+  }
+  uint32_t n_tiles;
+  uint32_t p = block_excl_scan(__popc(flags), L.wsum, &n_tiles);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (flags & (1u << u)) L.ctile[p++] = (uint16_t)(4 * tid + u);
+  __syncthreads();
+
+  // 2. fp32 scores of the candidate tiles (the scan's arithmetic), one tile per wave step
+  {
+    float wr[8];
+    load_head_weights(L.w, g, wr);
+    const uint16_t* kseq = k_idx + (size_t)(t / q_per_seq) * N * kIdxDim;
+    for (uint32_t ci = wave; ci < n_tiles; ci += kCandThreads / 64) {
+      const int64_t s = (tile0 + L.ctile[ci]) * kTileKeys + col;
+      uint4 kv[4];
+      load_key_slices(kseq, s < nv ? s : nv - 1, g, kv);
+      const float sc = tile_score(L.sq, kv, wr, col, g);
+      const bool pass = s < nv && (double)sc >= thr;
+      const uint64_t bal = __ballot(pass);
+      if (lane == 0) L.cmask[ci] = (uint16_t)(bal & 0xFFFFu);
+    }
+  }
+  __syncthreads();
+
+  // 3. output slots in (tile, entry) order
+  uint32_t cnt = 0;
+  for (uint32_t ci = 4 * tid; ci < 4 * tid + 4 && ci < n_tiles; ++ci) cnt += __popc((uint32_t)L.cmask[ci]);
+  uint32_t n_pass;
+  uint32_t q0 = block_excl_scan(cnt, L.wsum, &n_pass);
+  if (n_pass > kSelLds) {  // more than the select block can hold: exact fallback for this query
+    if (tid == 0) {
+      hdr[2] = 1u;
+      *rec = make_uint2(0u, 0u);
+    }
+    return;
+  }
+  for (uint32_t ci = 4 * tid; ci < 4 * tid + 4 && ci < n_tiles; ++ci) {
+    uint32_t m = L.cmask[ci];
+    const int64_t e0 = (tile0 + L.ctile[ci]) * kTileKeys;
+    while (m) {
+      const int c = __ffs(m) - 1;
+      m &= m - 1;
+      L.eidx[q0++] = (uint32_t)(e0 + c);
+    }
+  }
+  __syncthreads();
+
+  // 4. fp64 scores of the passing entries, reference operation order:
+  //    lane (e = lane / 32, h = lane % 32) forms dot(q_h, K_e) with 128
+  //    sequential fmas, then the wave folds the 32 heads in order.
+  {
+    const uint16_t* kseq = k_idx + (size_t)(t / q_per_seq) * N * kIdxDim;
+    const int h = lane & 31;
+    for (uint32_t e0 = 2 * wave; e0 < n_pass; e0 += 2 * (kCandThreads / 64)) {
+      const uint32_t e = e0 + (lane >> 5);
+      const uint32_t ee = e < n_pass ? e : e0;
+      const uint16_t* kr = kseq + (size_t)L.eidx[ee] * kIdxDim;
+      const uint16_t* qr = &L.sq[h * kQRowPad];
+      double d = 0.0;
+#pragma unroll 4
+      for (int i = 0; i < 16; ++i) {
+        const uint4 kq = *reinterpret_cast<const uint4*>(kr + 8 * i);
+        const uint4 qq = *reinterpret_cast<const uint4*>(qr + 8 * i);
+        const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
+        const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          d = fma((double)bf16lo(qw[c]), (double)bf16lo(kw[c]), d);
+          d = fma((double)bf16hi(qw[c]), (double)bf16hi(kw[c]), d);
+        }
+      }
+      const double rl = d > 0.0 ? d : 0.0;
+      double sc = 0.0;
+#pragma unroll 8
+      for (int hh = 0; hh < kIdxHeads; ++hh) sc = fma((double)L.w[hh], __shfl(rl, (lane & 32) + hh, 64), sc);
+      if (h == 0 && e < n_pass) L.escore[e] = sc;
+    }
+  }
+  __syncthreads();
+
+  // 5. reserve a segment of the query's candidate array and copy out
+  if (tid == 0) {
+    const uint32_t off = n_pass ? atomicAdd(&hdr[0], n_pass) : 0u;
+    L.base = off;
+    *rec = make_uint2(off, n_pass);
+  }
+  __syncthreads();
+  const uint32_t base = L.base;
+  for (uint32_t e = tid; e < n_pass; e += kCandThreads) {
+    const uint64_t pos = (uint64_t)base + e;
+    if (pos < (uint64_t)cap) {
+      w.cscore[(size_t)t * cap + pos] = L.escore[e];
+      w.cidx[(size_t)t * cap + pos] = L.eidx[e];
+    }
+  }
+}
+
+// LDS of a select block.
+struct alignas(16) SelectLds {
+  double v[kSelLds];
+  uint32_t idx[kSelLds];
+  uint32_t bpos[kSelBlocks];   // first candidate of each block record
+  uint32_t hist[256];
+  uint32_t wsum[kSelThreads / 64];
+  uint32_t pick[2];
+  uint32_t n_bin;
+  double red[2][kSelThreads / 64];
+  double bin_vals[64];
+  double result;
+  uint16_t sq[kIdxHeads * kQRowPad];   // query rows for the fallback's fp64 scores
+  float w[kIdxHeads];
+};
+
+// Block min / max in fp64 (all threads).
+__device__ __forceinline__ void block_minmax_f64(SelectLds& L, double& mn, double& mx) {
+  for (int o = 32; o >= 1; o >>= 1) {
+    mn = fmin(mn, __shfl_xor(mn, o, 64));
+    mx = fmax(mx, __shfl_xor(mx, o, 64));
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) { L.red[0][w] = mn; L.red[1][w] = mx; }
+  __syncthreads();
+  mn = L.red[0][0];
+  mx = L.red[1][0];
+  for (int i = 1; i < kSelThreads / 64; ++i) { mn = fmin(mn, L.red[0][i]); mx = fmax(mx, L.red[1][i]); }
+}
+
+__device__ __forceinline__ uint32_t bin_f64(double v, double a, double scale) {
+  const double f = (v - a) * scale;
+  return f >= 255.0 ? 255u : (f > 0.0 ? (uint32_t)f : 0u);
+}
+
+// The kk-th largest of L.v[0..n) (1 <= kk <= n): up to four value-binned
+// levels narrow [lo, hi] to the bin holding it; a bin of at most 64 members
+// is ranked directly by one wave, a larger one resolved exactly by radix
+// passes over the order-preserving 64-bit keys.
+__device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk) {
+  const int tid = threadIdx.x;
+  double lo = INFINITY, hi = -INFINITY;
+  for (uint32_t i = tid; i < n; i += kSelThreads) { lo = fmin(lo, L.v[i]); hi = fmax(hi, L.v[i]); }
+  block_minmax_f64(L, lo, hi);
+  uint32_t r = kk;  // rank (1-based, from the top) among the values in [lo, hi]
+  uint32_t count = n;
+  for (int level = 0; level < 4 && lo < hi && count > 64; ++level) {
+    const double scale = 256.0 / (hi - lo);
+    for (int i = tid; i < 256; i += kSelThreads) L.hist[i] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < n; i += kSelThreads) {
+      const double v = L.v[i];
+      if (v >= lo && v <= hi) atomicAdd(&L.hist[bin_f64(v, lo, scale)], 1u);
+    }
+    pick_digit(L.hist, r, L.pick);  // bin binning is monotone in v, so bins are value ranges
+    const uint32_t b = L.pick[0];
+    r = L.pick[1];
+    count = L.hist[b];
+    double nlo = INFINITY, nhi = -INFINITY;
+    for (uint32_t i = tid; i < n; i += kSelThreads) {
+      const double v = L.v[i];
+      if (v >= lo && v <= hi && bin_f64(v, lo, scale) == b) { nlo = fmin(nlo, v); nhi = fmax(nhi, v); }
+    }
+    block_minmax_f64(L, nlo, nhi);
+    lo = nlo;
+    hi = nhi;
+  }
+  if (!(lo < hi)) return lo;
+  if (count <= 64) {
+    if (tid == 0) L.n_bin = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < n; i += kSelThreads) {
+      const double v = L.v[i];
+      if (v >= lo && v <= hi) {
+        const uint32_t p = atomicAdd(&L.n_bin, 1u);
+        if (p < 64) L.bin_vals[p] = v;
+      }
+    }
+    __syncthreads();
+    if (tid < (int)count) {
+      const double va = L.bin_vals[tid];
+      uint32_t gt = 0, ge = 0;
+      for (uint32_t b = 0; b < count; ++b) {
+        const double vb = L.bin_vals[b];
+        gt += vb > va;
+        ge += vb >= va;
+      }
+      if (gt < r && r <= ge) L.result = va;  // every writer writes the same value
+    }
+    __syncthreads();
+    return L.result;
+  }
+  uint64_t pre = 0, mask = 0;
+  for (int pass = 0; pass < 8; ++pass) {
+    for (int i = tid; i < 256; i += kSelThreads) L.hist[i] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < n; i += kSelThreads) {
+      const double v = L.v[i];
+      const uint64_t key = f64_key(v);
+      if (v >= lo && v <= hi && (key & mask) == pre) atomicAdd(&L.hist[(uint32_t)(key >> (56 - 8 * pass)) & 255u], 1u);
+    }
+    pick_digit(L.hist, r, L.pick);
+    pre |= (uint64_t)L.pick[0] << (56 - 8 * pass);
+    mask |= (uint64_t)255 << (56 - 8 * pass);
+    r = L.pick[1];
+  }
+  const uint64_t u = (pre & 0x8000000000000000ull) ? (pre & 0x7FFFFFFFFFFFFFFFull) : ~pre;
+  return __longlong_as_double((long long)u);
+}
+
+// fp64 score of one key row with the reference's operation sequence, query
+// and weights in LDS (fallback path).
+__device__ double exact_score_lds(const uint16_t* __restrict__ sq, const float* __restrict__ w,
+                                  const uint16_t* __restrict__ key) {
+  uint4 kr[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) kr[i] = *reinterpret_cast<const uint4*>(key + 8 * i);
+  double sc = 0.0;
+  for (int h = 0; h < kIdxHeads; ++h) {
+    const uint16_t* qr = sq + h * kQRowPad;
+    double d = 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint4 qq = *reinterpret_cast<const uint4*>(qr + 8 * i);
+      const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
+      const uint32_t kw[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        d = fma((double)bf16lo(qw[c]), (double)bf16lo(kw[c]), d);
+        d = fma((double)bf16hi(qw[c]), (double)bf16hi(kw[c]), d);
+      }
+    }
+    sc = fma((double)w[h], d > 0.0 ? d : 0.0, sc);
+  }
+  return sc;
+}
+
+// Exact fallback of the tile regime: radix passes over the 96-bit composite
+// (fp64 key, ~index) of every visible entry of the candidate tiles, fp64
+// scores recomputed in each pass, then an ordered gather.
+__device__ void select_streaming(SelectLds& L, uint32_t kk, const float* tm_row, int64_t nv, double thr,
+                                 const uint16_t* qt, const float* wt, const uint16_t* kb, int32_t* out) {
+  const int tid = threadIdx.x;
+  stage_query(L.sq, qt, tid, kSelThreads);
+  if (tid < kIdxHeads) L.w[tid] = wt[tid];
+  const int64_t ntv = (nv + kTileKeys - 1) / kTileKeys;
+  uint32_t rank = kk;
+  uint64_t phi = 0, mhi = 0;
+  uint32_t plo = 0, mlo = 0;
+  for (int pass = 0; pass < 12; ++pass) {
+    for (int i = tid; i < 256; i += kSelThreads) L.hist[i] = 0;
+    __syncthreads();
+    for (int64_t s = tid; s < nv; s += kSelThreads) {
+      if (!((double)tm_row[s / kTileKeys] >= thr)) continue;
+      const uint64_t key = f64_key(exact_score_lds(L.sq, L.w, kb + (size_t)s * kIdxDim));
+      const uint32_t low = ~(uint32_t)s;
+      if ((key & mhi) != phi || (low & mlo) != plo) continue;
+      const uint32_t digit = pass < 8 ? (uint32_t)(key >> (56 - 8 * pass)) & 255u
+                                      : (low >> (24 - 8 * (pass - 8))) & 255u;
+      atomicAdd(&L.hist[digit], 1u);
+    }
+    pick_digit(L.hist, rank, L.pick);
+    const uint32_t digit = L.pick[0];
+    rank = L.pick[1];
+    if (pass < 8) {
+      phi |= (uint64_t)digit << (56 - 8 * pass);
+      mhi |= (uint64_t)255 << (56 - 8 * pass);
+    } else {
+      plo |= digit << (24 - 8 * (pass - 8));
+      mlo |= 255u << (24 - 8 * (pass - 8));
+    }
+  }
+  // (phi, plo) is the kk-th largest composite: keep everything >= it, in index order
+  uint32_t written = 0;
+  for (int64_t s0 = 0; s0 < ntv * kTileKeys; s0 += kSelThreads) {
+    const int64_t s = s0 + tid;
+    bool keep = false;
+    if (s < nv && (double)tm_row[s / kTileKeys] >= thr) {
+      const uint64_t key = f64_key(exact_score_lds(L.sq, L.w, kb + (size_t)s * kIdxDim));
+      const uint32_t low = ~(uint32_t)s;
+      keep = key > phi || (key == phi && low >= plo);
+    }
+    uint32_t tot;
+    const uint32_t pos = written + block_excl_scan(keep ? 1u : 0u, L.wsum, &tot);
+    if (keep && pos < kk) out[pos] = (int32_t)s;
+    written += tot;
+  }
+}
+
+// Final selection of query t (grid T, 256 threads): the k largest fp64 keys
+// among the candidates, written ascending by index.
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
+    const float* __restrict__ tile_max, const float* __restrict__ err_bound, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ w_idx, const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
+    int ratio, int q_per_seq, int64_t N, int k, int32_t* __restrict__ indices, void* ws, int T, int64_t cap) {
+  __shared__ SelectLds L;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t nv = n_visible(q_pos, t, ratio, N);
+  int32_t* out = indices + (size_t)t * k;
+  if (nv <= k) {
+    for (int i = tid; i < k; i += kSelThreads) out[i] = i < nv ? i : -1;
+    return;
+  }
+  const uint32_t kk = (uint32_t)k;
+  TileWs w = tile_ws(ws, T, N, cap);
+  const uint32_t* hdr = w.hdr + (size_t)t * kHdrWords;
+  const uint32_t cnt = hdr[0];
+  const int64_t nblk = cand_blocks(N);
+  const bool fits = hdr[2] == 0u && (int64_t)cnt <= cap && cnt <= kSelLds && cnt >= kk && nblk <= kSelBlocks;
+  if (!fits) {
+    const float tau = __uint_as_float(hdr[1]);
+    const double thr = next_down((double)tau - 2.0 * (double)err_bound[t]);
+    select_streaming(L, kk, tile_max + (size_t)t * tile_ld(N), nv, thr, q_idx + (size_t)t * kIdxHeads * kIdxDim,
+                     w_idx + (size_t)t * kIdxHeads, k_idx + (size_t)(t / q_per_seq) * N * kIdxDim, out);
+    return;
+  }
+  // candidates in index order: block records in block order, each in index order
+  const uint2* rec = w.table + (size_t)t * nblk;
+  {
+    constexpr int kPer = kSelBlocks / kSelThreads;  // 16 records per thread
+    uint32_t c[kPer], sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int64_t xb = (int64_t)tid * kPer + i;
+      c[i] = xb < nblk ? rec[xb].y : 0u;
+      sum += c[i];
+    }
+    uint32_t tot;
+    uint32_t p = block_excl_scan(sum, L.wsum, &tot);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      L.bpos[tid * kPer + i] = p;
+      p += c[i];
+    }
+  }
+  __syncthreads();
+  for (uint32_t i = tid; i < cnt; i += kSelThreads) {
+    // record holding candidate i: the last record whose first slot is <= i
+    // (records sharing a first slot are empty except possibly the last one)
+    int lo = 0, hi = (int)nblk - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (L.bpos[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const uint2 r = rec[lo];
+    const uint64_t o = (uint64_t)r.x + (i - L.bpos[lo]);
+    const bool ok = o < (uint64_t)cap;  // always true for a consistent table
+    L.v[i] = ok ? w.cscore[(size_t)t * cap + o] : -INFINITY;
+    L.idx[i] = ok ? w.cidx[(size_t)t * cap + o] : 0u;
+  }
+  __syncthreads();
+  const double V = kth_largest_f64(L, cnt, kk);
+  // entries above V are in; of those equal to V, the lowest indices (first in order)
+  constexpr int kPerC = kSelLds / kSelThreads;  // 16 consecutive candidates per thread
+  const uint32_t c0 = tid * kPerC;
+  uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int i = 0; i < kPerC; ++i) {
+    const uint32_t j = c0 + i;
+    if (j < cnt) {
+      n_gt += L.v[j] > V;
+      n_eq += L.v[j] == V;
+    }
+  }
+  uint32_t tot_gt, tot_eq;
+  block_excl_scan(n_gt, L.wsum, &tot_gt);
+  uint32_t eq_before = block_excl_scan(n_eq, L.wsum, &tot_eq);
+  const uint32_t need_eq = kk - tot_gt;
+  uint32_t n_sel = 0;
+#pragma unroll
+  for (int i = 0; i < kPerC; ++i) {
+    const uint32_t j = c0 + i;
+    if (j < cnt) {
+      const bool eq = L.v[j] == V;
+      n_sel += (L.v[j] > V) || (eq && eq_before < need_eq);
+      eq_before += eq;
+    }
+  }
+  uint32_t tot_sel;
+  uint32_t pos = block_excl_scan(n_sel, L.wsum, &tot_sel);
+  eq_before -= n_eq;  // back to this thread's first candidate
+#pragma unroll
+  for (int i = 0; i < kPerC; ++i) {
+    const uint32_t j = c0 + i;
+    if (j < cnt) {
+      const bool eq = L.v[j] == V;
+      const bool sel = (L.v[j] > V) || (eq && eq_before < need_eq);
+      eq_before += eq;
+      if (sel) {
+        if (pos < kk) out[pos] = (int32_t)L.idx[j];
+        ++pos;
+      }
+    }
+  }
+}
+
 }  // namespace csa2
 
 using namespace csa2;
 
+// Candidate capacity per query that a workspace of ws_bytes provides (-1: too small).
 static int64_t topk_cap_for(size_t ws_bytes, int32_t T, int64_t N) {
-  const size_t fixed = large_ws_fixed(T);
+  const size_t fixed = tile_ws_fixed(T, N);
   if (ws_bytes < fixed) return -1;
-  int64_t cap = (int64_t)((ws_bytes - fixed) / ((size_t)T * 8));
-  cap = cap / 4 * 4;  // keep the float array 16-byte aligned
-  if (cap > N) cap = (N + 3) / 4 * 4;
-  return cap;
+  int64_t cap = (int64_t)((ws_bytes - fixed) / ((size_t)T * 12));
+  cap = cap / 4 * 4;  // keeps the index array 16-byte aligned
+  const int64_t nmax = (N + 3) / 4 * 4;
+  return cap < nmax ? cap : nmax;
 }
 
-static bool topk_small_regime(int64_t N) { return N <= kSmallMax; }
+static bool topk_row_regime(const float* scores, int64_t N) { return scores != nullptr && N <= kSmallMax; }
 
 extern "C" size_t csa2_topk_workspace_bytes(int32_t T, int64_t N, int32_t k) {
   if (T < 1 || N < 1 || k != kTopK) return 0;
-  if (topk_small_regime(N)) return 0;
-  int64_t cap = N < kDefaultCap ? (N + 3) / 4 * 4 : kDefaultCap;
-  return large_ws_fixed(T) + (size_t)T * (size_t)cap * 8;
+  int64_t cap = (N + 3) / 4 * 4;
+  if (cap > kDefaultCap) cap = kDefaultCap;
+  return tile_ws_fixed(T, N) + (size_t)T * (size_t)cap * 12;
 }
 
 extern "C" size_t csa2_topk_min_workspace_bytes(int32_t T, int64_t N, int32_t k) {
   if (T < 1 || N < 1 || k != kTopK) return 0;
-  if (topk_small_regime(N)) return 0;
-  return large_ws_fixed(T);
+  return tile_ws_fixed(T, N);
 }
 
-extern "C" csa2_status csa2_topk(const float* scores, const float* err_bound, const void* q_idx,
-                                 const float* w_idx, const void* k_idx, const int32_t* q_pos, int32_t ratio,
-                                 int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices,
-                                 void* workspace, size_t workspace_bytes, void* hip_stream) {
-  if (!scores || !err_bound || !q_idx || !w_idx || !k_idx || !indices) return CSA2_ERR_INVALID_ARG;
-  if (!aligned16(scores) || !aligned16(err_bound) || !aligned16(q_idx) || !aligned16(w_idx) ||
-      !aligned16(k_idx) || !aligned16(indices) || (q_pos && !aligned16(q_pos)))
+extern "C" csa2_status csa2_topk(const float* scores, const float* tile_max, const float* err_bound,
+                                 const void* q_idx, const float* w_idx, const void* k_idx, const int32_t* q_pos,
+                                 int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N, int32_t k,
+                                 int32_t* indices, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!err_bound || !q_idx || !w_idx || !k_idx || !indices) return CSA2_ERR_INVALID_ARG;
+  if ((scores && !aligned16(scores)) || (tile_max && !aligned16(tile_max)) || !aligned16(err_bound) ||
+      !aligned16(q_idx) || !aligned16(w_idx) || !aligned16(k_idx) || !aligned16(indices) ||
+      (q_pos && !aligned16(q_pos)))
     return CSA2_ERR_INVALID_ARG;
   if (T < 1 || q_per_seq < 1 || T % q_per_seq != 0 || N < 1 || ratio < 1) return CSA2_ERR_INVALID_ARG;
   if (k != kTopK || N >= ((int64_t)1 << 31) || T > 65535) return CSA2_ERR_UNSUPPORTED;
@@ -676,33 +1012,23 @@ extern "C" csa2_status csa2_topk(const float* scores, const float* err_bound, co
   (void)hipGetLastError();
   const uint16_t* q = (const uint16_t*)q_idx;
   const uint16_t* kx = (const uint16_t*)k_idx;
-  if (topk_small_regime(N)) {
+  if (topk_row_regime(scores, N)) {
     hipLaunchKernelGGL(topk_small_kernel, dim3(T), dim3(kFinThreads), 0, st, scores, err_bound, q,
                        w_idx, kx, q_pos, ratio, q_per_seq, N, k, indices);
     if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
     return CSA2_OK;
   }
+  if (!tile_max) return CSA2_ERR_INVALID_ARG;
   if (!workspace || !aligned16(workspace) || workspace_bytes < csa2_topk_min_workspace_bytes(T, N, k))
     return CSA2_ERR_WORKSPACE;
   const int64_t cap = topk_cap_for(workspace_bytes, T, N);
   if (cap < 0) return CSA2_ERR_WORKSPACE;
-  const bool vec = (N & 3) == 0;
-  const dim3 ggrid(kGroups / 64, T);
-  if (vec)
-    hipLaunchKernelGGL(topk_gmax_kernel<true>, ggrid, dim3(kGroupThreads), 0, st, scores, q_pos, ratio, N, k,
-                       workspace, T, cap);
-  else
-    hipLaunchKernelGGL(topk_gmax_kernel<false>, ggrid, dim3(kGroupThreads), 0, st, scores, q_pos, ratio, N, k,
-                       workspace, T, cap);
-  hipLaunchKernelGGL(topk_tau_kernel, dim3(T), dim3(kFinThreads), 0, st, q_pos, ratio, N, k, workspace, T, cap);
-  const dim3 cgrid((unsigned)((N + kCompactChunk - 1) / kCompactChunk), T);
-  if (vec)
-    hipLaunchKernelGGL(topk_compact_kernel<true>, cgrid, dim3(kCompactThreads), 0, st, scores, err_bound, q_pos,
-                       ratio, N, k, workspace, T, cap);
-  else
-    hipLaunchKernelGGL(topk_compact_kernel<false>, cgrid, dim3(kCompactThreads), 0, st, scores, err_bound, q_pos,
-                       ratio, N, k, workspace, T, cap);
-  hipLaunchKernelGGL(topk_finish_kernel, dim3(T), dim3(kFinThreads), 0, st, scores, err_bound, q, w_idx, kx, q_pos,
+  const int64_t nblk = cand_blocks(N);
+  hipLaunchKernelGGL(topk_tau_kernel, dim3(T), dim3(kTauThreads), 0, st, tile_max, q_pos, ratio, N, k, workspace, T,
+                     cap);
+  hipLaunchKernelGGL(topk_cand_kernel, dim3((unsigned)nblk, T), dim3(kCandThreads), 0, st, tile_max, err_bound, q,
+                     w_idx, kx, q_pos, ratio, q_per_seq, N, k, workspace, T, cap);
+  hipLaunchKernelGGL(topk_select_kernel, dim3(T), dim3(kSelThreads), 0, st, tile_max, err_bound, q, w_idx, kx, q_pos,
                      ratio, q_per_seq, N, k, indices, workspace, T, cap);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   return CSA2_OK;

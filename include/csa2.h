@@ -75,15 +75,22 @@ const char* csa2_version(void);
  *   I(t,s) = sum_{h<32} w[t][h] * ReLU( sum_{c<128} q_idx[t][h][c] * k_idx[b][s][c] )
  * (lightning-indexer score of DeepSeek-V4, gzher.com reading sec. 4.1, which
  * CSA2 keeps, report sec. 2.3).  The scores are computed with bf16 MFMA and
- * fp32 accumulation.
+ * fp32 accumulation.  Entries are grouped in tiles of CSA2_TILE consecutive
+ * indices; the selection (csa2_topk) needs only each tile's maximum score and
+ * re-derives the scores of the few tiles that can hold a top-k entry, so the
+ * full score matrix is an optional output.
  *
  *  q_idx     bf16  [T][32][128]   indexer queries
  *  w_idx     fp32  [T][32]        per-head indexer weights
  *  k_idx     bf16  [B][N][128]    indexer keys (B = T / q_per_seq)
  *  q_pos     int32 [T] or NULL    absolute token positions (see visibility)
  *  ratio     compression ratio m >= 1
- *  scores    fp32  [T][N] out     I(t,s) for s < n_vis(t), -inf for s >= n_vis(t)
- *  err_bound fp32  [T]    out     eps_t >= |scores[t][s] - I_fp64(t,s)| for every
+ *  scores    fp32  [T][N] out, or NULL:  I(t,s) for s < n_vis(t), -inf beyond
+ *  tile_max  fp32  [T][ld] out, ld = csa2_tile_max_ld(N) = 4 * ceil(N / 64):
+ *            tile_max[t][j] = max of the scores of entries 16j .. 16j+15 (those
+ *            < N), -inf if none of them is visible; the ld - ceil(N/16)
+ *            padding slots of each row are left unspecified
+ *  err_bound fp32  [T]    out     eps_t >= |score(t,s) - I_fp64(t,s)| for every
  *                                 visible s, where I_fp64 is the score evaluated in
  *                                 fp64 with one fma per term, channels then heads
  *                                 in order; csa2_topk uses it to make the
@@ -91,37 +98,41 @@ const char* csa2_version(void);
  *  workspace >= csa2_index_workspace_bytes(T, q_per_seq, N) bytes (any contents).
  * Requires T >= 1, q_per_seq >= 1, T % q_per_seq == 0, 1 <= N < 2^31.
  */
+#define CSA2_TILE 16
+int64_t csa2_tile_max_ld(int64_t N);
 size_t csa2_index_workspace_bytes(int32_t T, int32_t q_per_seq, int64_t N);
 csa2_status csa2_index(const void* q_idx, const float* w_idx, const void* k_idx,
                        const int32_t* q_pos, int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N,
-                       float* scores, float* err_bound, void* workspace, size_t workspace_bytes,
-                       void* hip_stream);
+                       float* scores, float* tile_max, float* err_bound, void* workspace,
+                       size_t workspace_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------- topk
  * Exact top-k: for each query, the first min(k, n_vis) entries of the order
  * (I_fp64 descending, index ascending) — I_fp64 as defined under csa2_index —
  * written ASCENDING by entry index into indices[t][0..], the remaining slots
  * set to -1 (report sec. 2.3: each query keeps its top-k entries; k = 512 per
- * sec. 4.2.1).  The approximate scores pick the candidates; every entry whose
- * rank could depend on rounding (|score - k-th score| <= 2*err_bound) is
- * rescored in fp64 on the device, so the result does not depend on MFMA
- * rounding.
+ * sec. 4.2.1).  The fp32 scores only pick the candidates; the final order is
+ * decided on fp64 scores computed on the device, so the result does not
+ * depend on MFMA rounding.
  *
- *  scores, err_bound   outputs of csa2_index for the same arguments
- *  q_idx, w_idx, k_idx, q_pos, ratio   as passed to csa2_index (used for the
- *                      fp64 rescoring and for visibility)
- *  k                   must be CSA2_TOPK (512)
- *  indices int32 [T][k] out
+ *  scores     the scores output of csa2_index, or NULL.  When given and
+ *             N <= CSA2_TOPK_ROW_MAX, each query's row is selected in LDS in one
+ *             pass; otherwise the selection works from tile_max and the keys.
+ *  tile_max, err_bound   outputs of csa2_index for the same arguments
+ *  q_idx, w_idx, k_idx, q_pos, ratio   as passed to csa2_index
+ *  k          must be CSA2_TOPK (512)
+ *  indices    int32 [T][k] out
  *  workspace >= csa2_topk_workspace_bytes(T, N, k).  A larger workspace only
- *  raises the number of boundary candidates handled on the fast path; a
- *  smaller one (down to csa2_topk_min_workspace_bytes) is accepted and falls
- *  back to a slower streaming path when the candidates do not fit.
+ *  raises the number of candidates handled on the fast path; a smaller one
+ *  (down to csa2_topk_min_workspace_bytes) is accepted and falls back to a
+ *  slower exact streaming path when the candidates do not fit.
  */
+#define CSA2_TOPK_ROW_MAX 36864
 size_t csa2_topk_workspace_bytes(int32_t T, int64_t N, int32_t k);
 size_t csa2_topk_min_workspace_bytes(int32_t T, int64_t N, int32_t k);
-csa2_status csa2_topk(const float* scores, const float* err_bound, const void* q_idx,
-                      const float* w_idx, const void* k_idx, const int32_t* q_pos, int32_t ratio,
-                      int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices,
+csa2_status csa2_topk(const float* scores, const float* tile_max, const float* err_bound,
+                      const void* q_idx, const float* w_idx, const void* k_idx, const int32_t* q_pos,
+                      int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices,
                       void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* ----------------------------------------------------------------- attend

@@ -44,7 +44,7 @@ def test_workspace_queries(L):
     assert csa.index_workspace_bytes(4, 3, 100) == 0          # T not a multiple of q_per_seq
     assert csa.topk_workspace_bytes(4, 1 << 20) >= csa.topk_min_workspace_bytes(4, 1 << 20) > 0
     assert csa.topk_workspace_bytes(4, 1 << 20, 256) == 0      # only k = 512
-    assert csa.topk_workspace_bytes(4, 30000) == 0             # small rows: scores stay in LDS
+    assert csa.topk_workspace_bytes(4, 30000) > 0              # tile regime needs one even for short rows
     assert csa.attend_workspace_bytes(4096) == 0               # one work item per query: no partials
     assert csa.attend_workspace_bytes(4) > 0
     assert csa.attend_workspace_bytes(4, window=129) == 0
@@ -58,13 +58,23 @@ Q = ctypes.c_void_p(0x20000)
 MIS = ctypes.c_void_p(0x10004)   # misaligned
 
 
-def _index(L, q=P, w=P, k=P, pos=None, ratio=1, T=4, qps=1, N=1024, s=P, e=P, ws=P, wsb=1 << 20):
-    return L.csa2_index(q, w, k, pos, ratio, T, qps, N, s, e, ws, wsb, None)
+def test_tile_max_stride(L):
+    # ceil(N/16) tiles per row, padded to a multiple of 4 floats (16-byte rows)
+    for N, ld in [(1, 4), (16, 4), (64, 4), (65, 8), (1000, 64), (1 << 20, 65536), (40001, 2504)]:
+        assert L.csa2_tile_max_ld(N) == ld
+        assert ld >= -(-N // 16) and ld % 4 == 0
+    assert L.csa2_tile_max_ld(0) == 0
+
+
+def _index(L, q=P, w=P, k=P, pos=None, ratio=1, T=4, qps=1, N=1024, s=P, tm=P, e=P, ws=P, wsb=1 << 20):
+    return L.csa2_index(q, w, k, pos, ratio, T, qps, N, s, tm, e, ws, wsb, None)
 
 
 def test_index_host_validation(L):
     assert _index(L, q=None) == INVALID
-    assert _index(L, s=None) == INVALID
+    assert _index(L, tm=None) == INVALID
+    assert _index(L, s=MIS) == INVALID
+    assert _index(L, e=None) == INVALID
     assert _index(L, k=MIS) == INVALID
     assert _index(L, T=0) == INVALID
     assert _index(L, T=4, qps=3) == INVALID
@@ -77,14 +87,18 @@ def test_index_host_validation(L):
 
 # N large enough for the multi-pass regime, where a workspace is required, so
 # that every call below is rejected by validation.
-def _topk(L, s=P, e=P, q=P, w=P, k_idx=P, pos=None, ratio=1, T=4, qps=1, N=1 << 20, k=512, out=P, ws=P, wsb=None):
+def _topk(L, s=None, tm=P, e=P, q=P, w=P, k_idx=P, pos=None, ratio=1, T=4, qps=1, N=1 << 20, k=512, out=P, ws=P,
+          wsb=None):
     if wsb is None:
         wsb = csa.topk_workspace_bytes(T, N, 512) or 1
-    return L.csa2_topk(s, e, q, w, k_idx, pos, ratio, T, qps, N, k, out, ws, wsb, None)
+    return L.csa2_topk(s, tm, e, q, w, k_idx, pos, ratio, T, qps, N, k, out, ws, wsb, None)
 
 
 def test_topk_host_validation(L):
-    assert _topk(L, s=None) == INVALID
+    assert _topk(L, tm=None) == INVALID              # no scores and no tile maxima
+    assert _topk(L, s=P, tm=None) == INVALID         # long rows always use the tile regime
+    assert _topk(L, e=None) == INVALID
+    assert _topk(L, tm=MIS) == INVALID
     assert _topk(L, out=MIS) == INVALID
     assert _topk(L, T=5, qps=2) == INVALID
     assert _topk(L, k=256) == UNSUPPORTED

@@ -27,9 +27,13 @@ def log(msg):
     sys.stdout.flush()
 
 
-def run_full(c, layers=1):
-    scores, eps = csa.csa2_index(c.q_idx.view(BF), c.w_idx, c.k_idx.view(BF), c.q_pos, c.ratio, c.q_per_seq)
-    idx = csa.csa2_topk(scores, eps, c.q_idx.view(BF), c.w_idx, c.k_idx.view(BF), c.q_pos, c.ratio, c.q_per_seq)
+def run_full(c, layers=1, path="tiles"):
+    """The benchmarked pipeline: with path "tiles" the scan writes no score matrix and the
+    selection works from tile maxima and keys; with "rows" the scores are materialised and
+    selected in LDS.  A second scan with scores provides them for the bound check."""
+    bf = (c.q_idx.view(BF), c.w_idx, c.k_idx.view(BF), c.q_pos, c.ratio, c.q_per_seq)
+    ix = csa.csa2_index(*bf, want_scores=(path == "rows"))
+    idx = csa.csa2_topk(ix.scores, ix.tile_max, ix.err_bound, *bf)
     out = csa.csa2_attend_fp4(c.q[0].view(BF), c.kv_codes, c.kv_scales, idx, c.swa[0].view(BF), c.swa_end, None,
                               c.softmax_scale, c.q_per_seq, c.window)
     re = None
@@ -37,12 +41,15 @@ def run_full(c, layers=1):
         re = csa.csa2_reuse_attend(c.q[1:].view(BF).contiguous(), c.kv_codes, c.kv_scales, idx,
                                    c.swa[1:].view(BF).contiguous(), c.swa_end, None, c.softmax_scale, c.q_per_seq,
                                    c.window)
+    full = ix if path == "rows" else csa.csa2_index(*bf)
     torch.cuda.synchronize()
-    return scores, eps, idx, out, re
+    nt = -(-c.N // 16)
+    assert torch.equal(full.tile_max[:, :nt], ix.tile_max[:, :nt]) and torch.equal(full.err_bound, ix.err_bound)
+    return full.scores, full.err_bound, idx, out, re
 
 
-def check_sampled(c, ts, layers=1):
-    scores, eps, idx, out, re = run_full(c, layers)
+def check_sampled(c, ts, layers=1, path="tiles"):
+    scores, eps, idx, out, re = run_full(c, layers, path)
     log(f"  GPU path done; oracle on queries {ts}")
     ref_s = oracle_scores(c, ts)
     ref_i = oracle_topk(c, ref_s)
@@ -90,7 +97,8 @@ def test_reuse_group_sampled():
     check_sampled(c, [0, 31], layers=4)
 
 
-def test_causal_prefill_sampled():
-    log("[full] causal_prefill 4096 queries, 34816 entries, ratio 2")
+@pytest.mark.parametrize("path", ["rows", "tiles"])
+def test_causal_prefill_sampled(path):
+    log(f"[full] causal_prefill 4096 queries, 34816 entries, ratio 2 ({path})")
     c = G.make_case("causal_prefill", **G.CONFIGS["causal_prefill"], seed=0, device=DEV)
-    check_sampled(c, [0, 1, 2047, 4094, 4095])
+    check_sampled(c, [0, 1, 2047, 4094, 4095], path=path)

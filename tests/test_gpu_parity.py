@@ -43,35 +43,17 @@ def case(name):
     return _cases[name]
 
 
-def run_index(c):
+def run_index(c, want_scores=True):
     return csa.csa2_index(c.q_idx.view(torch.bfloat16), c.w_idx, c.k_idx.view(torch.bfloat16), c.q_pos, c.ratio,
-                          c.q_per_seq)
+                          c.q_per_seq, want_scores=want_scores)
 
 
-def run_topk(c, scores, eps, workspace=None):
-    return csa.csa2_topk(scores, eps, c.q_idx.view(torch.bfloat16), c.w_idx, c.k_idx.view(torch.bfloat16), c.q_pos,
-                         c.ratio, c.q_per_seq, workspace=workspace)
-
-
-@pytest.mark.parametrize("name", list(SMALL))
-def test_index_scores_within_bound(name):
-    log(f"[index] {name}")
-    c = case(name)
-    scores, eps = run_index(c)
-    torch.cuda.synchronize()
-    ref = oracle_scores(c, range(c.T))
-    s, e = npy(scores), npy(eps)
-    worst = 0.0
-    for t in range(c.T):
-        nv = G_nvis(c, t)
-        assert np.all(np.isneginf(s[t, nv:])), "entries beyond visibility must be -inf"
-        err = np.abs(s[t, :nv].astype(np.float64) - ref[t][:nv])
-        assert np.all(err <= e[t]), f"t={t}: max err {err.max()} > eps {e[t]}"
-        if nv:
-            worst = max(worst, float(err.max() / e[t]))
-            # the bound must stay small next to the scores, or the band explodes
-            assert e[t] < 2e-3 * np.abs(ref[t][:nv]).max()
-    log(f"  max |fp32 - fp64| / eps = {worst:.2e}")
+def run_topk(c, ix, path="tiles", workspace=None):
+    """path "rows": scores given (one-pass LDS selection when N <= 36864); "tiles": no score
+    matrix, selection from tile maxima and the keys."""
+    return csa.csa2_topk(ix.scores if path == "rows" else None, ix.tile_max, ix.err_bound,
+                         c.q_idx.view(torch.bfloat16), c.w_idx, c.k_idx.view(torch.bfloat16), c.q_pos, c.ratio,
+                         c.q_per_seq, workspace=workspace)
 
 
 def G_nvis(c, t):
@@ -80,11 +62,39 @@ def G_nvis(c, t):
 
 
 @pytest.mark.parametrize("name", list(SMALL))
-def test_topk_bit_exact(name):
-    log(f"[topk] {name}")
+def test_index_scores_within_bound(name):
+    log(f"[index] {name}")
     c = case(name)
-    scores, eps = run_index(c)
-    idx = run_topk(c, scores, eps)
+    ix = run_index(c)
+    ix2 = run_index(c, want_scores=False)
+    torch.cuda.synchronize()
+    ref = oracle_scores(c, range(c.T))
+    s, e, tm = npy(ix.scores), npy(ix.err_bound), npy(ix.tile_max)
+    # the tile maxima (padding slots excluded) and the bound do not depend on whether scores are written
+    nt = -(-c.N // 16)
+    assert np.array_equal(tm[:, :nt], npy(ix2.tile_max)[:, :nt]) and np.array_equal(e, npy(ix2.err_bound))
+    pad = np.full((c.T, nt * 16 - c.N), -np.inf, np.float32)
+    assert np.array_equal(tm[:, :nt], np.concatenate([s, pad], axis=1).reshape(c.T, nt, 16).max(axis=2))
+    worst = 0.0
+    for t in range(c.T):
+        nv = G_nvis(c, t)
+        assert np.all(np.isneginf(s[t, nv:])), "entries beyond visibility must be -inf"
+        err = np.abs(s[t, :nv].astype(np.float64) - ref[t][:nv])
+        assert np.all(err <= e[t]), f"t={t}: max err {err.max()} > eps {e[t]}"
+        if nv:
+            worst = max(worst, float(err.max() / e[t]))
+            # the bound must stay small next to the scores, or the candidate set explodes
+            assert e[t] < 2e-3 * np.abs(ref[t][:nv]).max()
+    log(f"  max |fp32 - fp64| / eps = {worst:.2e}")
+
+
+@pytest.mark.parametrize("path", ["rows", "tiles"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_topk_bit_exact(name, path):
+    log(f"[topk] {name} ({path})")
+    c = case(name)
+    ix = run_index(c, want_scores=(path == "rows"))
+    idx = run_topk(c, ix, path)
     torch.cuda.synchronize()
     ref = oracle_topk(c, oracle_scores(c, range(c.T)))
     got = npy(idx)
@@ -93,23 +103,23 @@ def test_topk_bit_exact(name):
 
 
 def test_topk_streaming_fallback_matches():
-    # a workspace with no candidate capacity forces the streaming path of the
-    # multi-pass regime
+    # a workspace with no candidate capacity forces the exact streaming path of the tile regime
     log("[topk] streaming fallback")
     c = case("large_rows_ragged")
-    scores, eps = run_index(c)
+    ix = run_index(c, want_scores=False)
     ws = torch.empty(csa.topk_min_workspace_bytes(c.T, c.N), dtype=torch.uint8, device=DEV)
-    idx = run_topk(c, scores, eps, workspace=ws)
+    idx = run_topk(c, ix, "tiles", workspace=ws)
     torch.cuda.synchronize()
     ref = oracle_topk(c, oracle_scores(c, range(c.T)))
     for t in range(c.T):
         assert np.array_equal(npy(idx)[t], ref[t])
 
 
-@pytest.mark.parametrize("mode", ["all_equal", "all_equal_overflow", "tie_block", "tie_block_large"])
-def test_topk_planted_ties(mode):
-    log(f"[topk] ties {mode}")
-    N = {"all_equal_overflow": 3000, "tie_block_large": 40000}.get(mode, 2048)
+@pytest.mark.parametrize("path", ["rows", "tiles"])
+@pytest.mark.parametrize("mode", ["all_equal", "all_equal_overflow", "all_equal_large", "tie_block", "tie_block_large"])
+def test_topk_planted_ties(mode, path):
+    log(f"[topk] ties {mode} ({path})")
+    N = {"all_equal_overflow": 3000, "all_equal_large": 40000, "tie_block_large": 40000}.get(mode, 2048)
     c = G.make_case("ties", B=1, N=N, seed=5, device=DEV, with_kv=False)
     if mode.startswith("all_equal"):
         c.k_idx[:] = c.k_idx[0, 7]                       # every key identical: lowest 512 indices win
@@ -119,8 +129,8 @@ def test_topk_planted_ties(mode):
         order = np.argsort(-sc, kind="stable")
         src = int(order[500])
         c.k_idx[0, 1000:1100] = c.k_idx[0, src]
-    scores, eps = run_index(c)
-    idx = run_topk(c, scores, eps)
+    ix = run_index(c, want_scores=(path == "rows"))
+    idx = run_topk(c, ix, path)
     torch.cuda.synchronize()
     ref = oracle_topk(c, oracle_scores(c, [0]))
     assert np.array_equal(npy(idx)[0], ref[0])
@@ -140,8 +150,7 @@ def _attend(c, idx, layer=0, sink=None, window=None, swa_end=None, lse=True):
 def test_attend_matches_oracle(name):
     log(f"[attend] {name}")
     c = case(name)
-    scores, eps = run_index(c)
-    idx = run_topk(c, scores, eps)
+    idx = run_topk(c, run_index(c, want_scores=False))
     out, lse = _attend(c, idx)
     torch.cuda.synchronize()
     ref = oracle_attend(c, {t: npy(idx)[t] for t in range(c.T)})
@@ -194,8 +203,7 @@ def test_attend_split_plans(T_q):
     # different T choose different split-K plans (many partials + combine, or one item per query)
     log(f"[attend] split plan T={T_q}")
     c = G.make_case("split", B=T_q, N=600, seed=9, device=DEV)
-    scores, eps = run_index(c)
-    idx = run_topk(c, scores, eps)
+    idx = run_topk(c, run_index(c, want_scores=False))
     out, lse = _attend(c, idx)
     torch.cuda.synchronize()
     ts = sorted(set([0, T_q // 2, T_q - 1]))
@@ -207,8 +215,7 @@ def test_attend_split_plans(T_q):
 def test_reuse_layers_match_oracle_and_attend():
     log("[reuse] 3 layers")
     c = G.make_case("reuse", B=3, N=1200, n_layers=4, seed=21, device=DEV)
-    scores, eps = run_index(c)
-    idx = run_topk(c, scores, eps)
+    idx = run_topk(c, run_index(c, want_scores=False))
     full = _attend(c, idx, layer=0, lse=False)
     q = c.q[1:].view(torch.bfloat16).contiguous()
     swa = c.swa[1:].view(torch.bfloat16).contiguous()
@@ -231,15 +238,17 @@ def test_reuse_layers_match_oracle_and_attend():
 
 def test_pipeline_is_deterministic():
     log("[determinism]")
-    c = case("ragged_decode")
-    a_s, a_e = run_index(c)
-    a_i = run_topk(c, a_s, a_e)
+    c = case("large_rows_ragged")
+    a = run_index(c)
+    a_i = run_topk(c, a, "tiles")
     a_o = _attend(c, a_i, lse=False)
-    b_s, b_e = run_index(c)
-    b_i = run_topk(c, b_s, b_e)
+    b = run_index(c)
+    b_i = run_topk(c, b, "tiles")
     b_o = _attend(c, b_i, lse=False)
     torch.cuda.synchronize()
-    assert torch.equal(a_s, b_s) and torch.equal(a_e, b_e) and torch.equal(a_i, b_i) and torch.equal(a_o, b_o)
+    assert torch.equal(a.scores, b.scores) and torch.equal(a.err_bound, b.err_bound)
+    assert torch.equal(a.tile_max[:, :-(-c.N // 16)], b.tile_max[:, :-(-c.N // 16)])
+    assert torch.equal(a_i, b_i) and torch.equal(a_o, b_o)
 
 
 def test_generator_is_device_independent():
