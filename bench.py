@@ -76,7 +76,7 @@ def main():
     rows = N <= csa.TOPK_ROW_MAX
     scores = torch.empty((T, N), dtype=torch.float32, device=dev) if rows else None
     tile_max = torch.empty((T, csa.tile_max_ld(N)), dtype=torch.float32, device=dev)
-    eps = torch.empty((T,), dtype=torch.float32, device=dev)
+    stats = torch.empty((T, csa.STATS_WORDS), dtype=torch.int32, device=dev)
     idx = torch.empty((T, 512), dtype=torch.int32, device=dev)
     out = torch.empty((T, 64, 512), dtype=torch.bfloat16, device=dev)
     out_re = torch.empty((3, T, 64, 512), dtype=torch.bfloat16, device=dev)
@@ -88,10 +88,10 @@ def main():
 
     def do_index():
         csa.csa2_index(q_idx, c.w_idx, k_idx, c.q_pos, 1, 1, want_scores=rows, scores=scores, tile_max=tile_max,
-                       err_bound=eps, workspace=ws_i)
+                       stats=stats, workspace=ws_i)
 
     def do_topk():
-        csa.csa2_topk(scores, tile_max, eps, q_idx, c.w_idx, k_idx, c.q_pos, 1, 1, indices=idx, workspace=ws_t)
+        csa.csa2_topk(scores, tile_max, stats, q_idx, c.w_idx, k_idx, c.q_pos, 1, 1, indices=idx, workspace=ws_t)
 
     def do_attend():
         csa.csa2_attend_fp4(q0, c.kv_codes, c.kv_scales, idx, swa0, c.swa_end, None, c.softmax_scale, 1, 128,
@@ -140,8 +140,8 @@ def main():
     # dominant kernel: the indexer scan.  Algorithmic bytes per launch: each
     # sequence's keys once (256 B/entry), q_idx (8 KiB) and w (128 B) per
     # query, its outputs (tile maxima, 4 B per 16 entries; the score matrix,
-    # 4 B per entry, only for short rows) and the bound (4 B).
-    idx_bytes = B * N * 256 + T * (8192 + 128 + 4) + T * csa.tile_max_ld(N) * 4 + (T * N * 4 if rows else 0)
+    # 4 B per entry, only for short rows) and the 16-byte stats.
+    idx_bytes = B * N * 256 + T * (8192 + 128 + 16) + T * csa.tile_max_ld(N) * 4 + (T * N * 4 if rows else 0)
     achieved = idx_bytes / (idx_avg * 1e-6) / 1e9
     step_bytes = T * G.algorithmic_bytes_decode_query(N)
 

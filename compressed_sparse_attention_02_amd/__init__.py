@@ -18,11 +18,11 @@ __all__ = [
     "Csa2Error", "IndexResult", "lib", "library_path", "csa2_index", "csa2_topk", "csa2_attend_fp4",
     "csa2_reuse_attend", "tile_max_ld", "index_workspace_bytes", "topk_workspace_bytes", "topk_min_workspace_bytes",
     "attend_workspace_bytes", "IDX_HEADS", "IDX_DIM", "HEADS", "DIM", "TOPK", "MAX_WINDOW", "MAX_LAYERS", "TILE",
-    "TOPK_ROW_MAX",
+    "TOPK_ROW_MAX", "STATS_WORDS",
 ]
 
 IDX_HEADS, IDX_DIM, HEADS, DIM, TOPK, MAX_WINDOW, MAX_LAYERS = 32, 128, 64, 512, 512, 128, 8
-TILE, TOPK_ROW_MAX = 16, 36864
+TILE, TOPK_ROW_MAX, STATS_WORDS = 16, 36864, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libcsa2.so")
@@ -49,10 +49,18 @@ _SIGNATURES = {
 
 class IndexResult(NamedTuple):
     """Outputs of csa2_index: scores fp32 [T][N] (None unless requested), tile maxima fp32
-    [T][tile_max_ld(N)], error bound fp32 [T]."""
+    [T][tile_max_ld(N)], per-query stats int32 [T][4] (eps and floor as fp32 bits, two counters)."""
     scores: Optional[torch.Tensor]
     tile_max: torch.Tensor
-    err_bound: torch.Tensor
+    stats: torch.Tensor
+
+    @property
+    def err_bound(self) -> torch.Tensor:
+        return self.stats.view(torch.float32)[:, 0]
+
+    @property
+    def floor(self) -> torch.Tensor:
+        return self.stats.view(torch.float32)[:, 1]
 
 
 class Csa2Error(RuntimeError):
@@ -142,7 +150,7 @@ def attend_workspace_bytes(T: int, k: int = TOPK, window: int = MAX_WINDOW, n_la
 
 
 def csa2_index(q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, want_scores=True, scores=None,
-               tile_max=None, err_bound=None, workspace=None) -> IndexResult:
+               tile_max=None, stats=None, workspace=None) -> IndexResult:
     """Indexer scan.  q_idx bf16 [T][32][128], w_idx fp32 [T][32], k_idx bf16 [B][N][128],
     q_pos int32 [T] or None.  Writes the full score matrix only if want_scores (or `scores` is given)."""
     T = q_idx.shape[0]
@@ -159,31 +167,32 @@ def csa2_index(q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, want_score
         scores = torch.empty((T, N), dtype=torch.float32, device=dev)
     if tile_max is None:
         tile_max = torch.empty((T, tile_max_ld(N)), dtype=torch.float32, device=dev)
-    if err_bound is None:
-        err_bound = torch.empty((T,), dtype=torch.float32, device=dev)
+    if stats is None:
+        stats = torch.empty((T, STATS_WORDS), dtype=torch.int32, device=dev)
     if scores is not None:
         _check(scores, "scores", (T, N), dtype=torch.float32, device=dev)
     _check(tile_max, "tile_max", (T, tile_max_ld(N)), dtype=torch.float32, device=dev)
-    _check(err_bound, "err_bound", (T,), dtype=torch.float32, device=dev)
+    _check(stats, "stats", (T, STATS_WORDS), dtype=torch.int32, device=dev)
     nbytes = index_workspace_bytes(T, q_per_seq, N)
     workspace = _ws(nbytes, dev, workspace)
     st = lib().csa2_index(_p(q_idx), _p(w_idx), _p(k_idx), _p(q_pos), ratio, T, q_per_seq, N, _p(scores),
-                          _p(tile_max), _p(err_bound), _p(workspace), _nbytes(workspace), _stream(q_idx))
+                          _p(tile_max), _p(stats), _p(workspace), _nbytes(workspace), _stream(q_idx))
     _raise(st, "csa2_index")
-    return IndexResult(scores, tile_max, err_bound)
+    return IndexResult(scores, tile_max, stats)
 
 
-def csa2_topk(scores, tile_max, err_bound, q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, k=TOPK,
+def csa2_topk(scores, tile_max, stats, q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, k=TOPK,
               indices=None, workspace=None):
     """Exact top-k (ascending indices, -1 padded) -> int32 [T][k].  scores may be None (the
-    selection then works from tile_max and the keys)."""
-    T = err_bound.shape[0]
+    selection then works from tile_max and the keys); stats is csa2_index's (its counter words
+    are used and left zero)."""
+    T = stats.shape[0]
     B, N = k_idx.shape[0], k_idx.shape[1]
-    dev = err_bound.device
+    dev = stats.device
     if scores is not None:
         _check(scores, "scores", (T, N), dtype=torch.float32, device=dev)
     _check(tile_max, "tile_max", (T, tile_max_ld(N)), dtype=torch.float32, device=dev)
-    _check(err_bound, "err_bound", (T,), dtype=torch.float32)
+    _check(stats, "stats", (T, STATS_WORDS), dtype=torch.int32)
     _check(q_idx, "q_idx", (T, IDX_HEADS, IDX_DIM), elem_size=2, device=dev)
     _check(w_idx, "w_idx", (T, IDX_HEADS), dtype=torch.float32, device=dev)
     _check(k_idx, "k_idx", (B, N, IDX_DIM), elem_size=2, device=dev)
@@ -196,9 +205,9 @@ def csa2_topk(scores, tile_max, err_bound, q_idx, w_idx, k_idx, q_pos=None, rati
         workspace = _ws(topk_workspace_bytes(T, N, k), dev, None)
     elif _nbytes(workspace) < topk_min_workspace_bytes(T, N, k):
         raise ValueError("workspace below csa2_topk_min_workspace_bytes")
-    st = lib().csa2_topk(_p(scores), _p(tile_max), _p(err_bound), _p(q_idx), _p(w_idx), _p(k_idx), _p(q_pos),
+    st = lib().csa2_topk(_p(scores), _p(tile_max), _p(stats), _p(q_idx), _p(w_idx), _p(k_idx), _p(q_pos),
                          ratio, T, q_per_seq, N, k, _p(indices), _p(workspace), _nbytes(workspace),
-                         _stream(err_bound))
+                         _stream(stats))
     _raise(st, "csa2_topk")
     return indices
 

@@ -14,12 +14,6 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// 16-byte streaming load (non-temporal hint: the data is read once).
-__device__ __forceinline__ uint4 load_stream16(const void* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 constexpr int kIdxHeads = CSA2_IDX_HEADS;  // 32
 constexpr int kIdxDim = CSA2_IDX_DIM;      // 128
 constexpr int kHeads = CSA2_HEADS;         // 64
@@ -57,6 +51,13 @@ __device__ __forceinline__ uint64_t f64_key(double d) {
   return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
 }
 
+// Bin of x among 256 equal-width bins starting at a (scale = 255.99 / width);
+// monotone non-decreasing in x.
+__device__ __forceinline__ uint32_t value_bin(float x, float a, float scale) {
+  const float f = (x - a) * scale;
+  return f >= 255.f ? 255u : (f > 0.f ? (uint32_t)f : 0u);
+}
+
 // Number of compressed entries visible to query t (see csa2.h).
 __device__ __forceinline__ int64_t n_visible(const int32_t* q_pos, int t, int ratio, int64_t N) {
   if (q_pos == nullptr) return N;
@@ -82,7 +83,7 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace csa2

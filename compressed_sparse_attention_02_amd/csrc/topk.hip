@@ -5,7 +5,7 @@
 // sec. 2.3: each query keeps its top-k entries, k = 512 per sec. 4.2.1).
 //
 // The fp32 scores of csa2_index differ from the fp64 reference by at most
-// eps (err_bound).  If k distinct entries have fp32 score >= tau, then the
+// eps (stats word 0).  If k distinct entries have fp32 score >= tau, then the
 // k-th largest fp64 score T^ satisfies T^ >= tau - eps, so every true top-k
 // member has fp32 score >= tau - 2 eps: {fp32 >= tau - 2 eps} is a candidate
 // set that contains the whole answer.  Two regimes:
@@ -38,16 +38,16 @@ constexpr int kFinThreads = 1024;        // row-regime block
 constexpr int kBandLds = 2048;           // band entries resolved in LDS (row regime)
 constexpr int kSmallMax = CSA2_TOPK_ROW_MAX;  // row regime: visible scores kept in LDS
 
-constexpr int kTauThreads = 1024;
-constexpr int kTauDirect = 16384;        // up to this many tiles, tau comes from the tile maxima themselves
-constexpr int kTauGroups = 4096;         // otherwise from 4096 strided group maxima
 constexpr int kCandThreads = 256;
-constexpr int kCandTiles = 1024;         // tiles (16384 entries) per candidate block
+constexpr int kCandTiles = 256;          // tiles (4096 entries) per candidate block
+constexpr int kCandMax = 1024;           // passing entries a candidate block holds (beyond: exact fallback)
 constexpr int kSelThreads = 256;
 constexpr int kSelLds = 4096;            // candidates a select block holds in LDS
-constexpr int kSelBlocks = 4096;         // candidate blocks per query the select block can index
-constexpr int kDefaultCap = 4096;        // default candidate capacity per query
-constexpr int kHdrWords = 16;            // per query: [0] candidate count, [1] tau (fp32 bits), [2] overflow
+constexpr int kSelBlocks = 4096;         // candidate blocks per query the select block can index (N <= 2^24)
+constexpr int kSlots = 32;               // fixed candidate slots per candidate block
+constexpr int kDefaultSpill = 2048;      // shared slots per query for blocks with more
+constexpr int kMaxSpill = 16384;
+constexpr uint32_t kOverflow = 0x80000000u;  // stats[2]: shared slots used, this bit set on overflow
 
 // ---------------------------------------------------------------- helpers
 
@@ -127,10 +127,6 @@ __device__ __forceinline__ float2 block_minmax(SelLds& s, float mn, float mx) {
   return make_float2(mn, mx);
 }
 
-__device__ __forceinline__ uint32_t value_bin(float x, float a, float scale) {
-  const float f = (x - a) * scale;
-  return f >= 255.f ? 255u : (f > 0.f ? (uint32_t)f : 0u);
-}
 
 // Visit get(i) for i < n, four at a time per thread so that four loads are in flight.
 template <typename Get, typename F>
@@ -372,7 +368,7 @@ struct SmallLds {
 };
 
 __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
-    const float* __restrict__ scores, const float* __restrict__ err_bound, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ scores, const uint32_t* __restrict__ stats, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w_idx, const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
     int ratio, int q_per_seq, int64_t N, int k, int32_t* __restrict__ indices) {
   __shared__ SmallLds L;
@@ -392,7 +388,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
   const float* wt = w_idx + (size_t)t * kIdxHeads;
   const uint16_t* kb = k_idx + (size_t)b * N * kIdxDim;
   const float* row = scores + (size_t)t * N;
-  const float eps = err_bound[t];
+  const float eps = __uint_as_float(stats[(size_t)t * CSA2_STATS_WORDS]);
   if (tid == 0) { sh.n_out = 0; sh.n_band = 0; }
   for (int64_t i = tid; i < nv; i += kFinThreads) L.u.v[i] = row[i];
   __syncthreads();
@@ -418,10 +414,11 @@ __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
 
 // ------------------------------------------------------------ tile regime
 
-// Workspace of the tile regime, per query: a header, one {offset, count}
-// record per candidate block, and `cap` candidates (fp64 score, index).
+// Workspace of the tile regime, per query: one {offset, count} record per
+// candidate block and `cap` candidates (fp64 score, index): `slots` fixed
+// ones per block, then shared ones that blocks with more candidates reserve
+// with an atomic add on stats word 2.
 struct TileWs {
-  uint32_t* hdr;    // [T][kHdrWords]
   uint2* table;     // [T][nblk]
   double* cscore;   // [T][cap]
   uint32_t* cidx;   // [T][cap]
@@ -430,13 +427,12 @@ __host__ __device__ __forceinline__ int64_t cand_blocks(int64_t N) {
   return ((N + kTileKeys - 1) / kTileKeys + kCandTiles - 1) / kCandTiles;
 }
 __host__ __device__ __forceinline__ size_t tile_ws_fixed(int T, int64_t N) {
-  return (size_t)T * (kHdrWords * 4 + (size_t)cand_blocks(N) * 8);
+  return align_up((size_t)T * (size_t)cand_blocks(N) * 8, 16);
 }
 __device__ __forceinline__ TileWs tile_ws(void* base, int T, int64_t N, int64_t cap) {
   TileWs w;
-  w.hdr = (uint32_t*)base;
-  w.table = (uint2*)(w.hdr + (size_t)T * kHdrWords);
-  w.cscore = (double*)(w.table + (size_t)T * cand_blocks(N));
+  w.table = (uint2*)base;
+  w.cscore = (double*)((char*)base + tile_ws_fixed(T, N));
   w.cidx = (uint32_t*)(w.cscore + (size_t)T * cap);
   return w;
 }
@@ -463,91 +459,50 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
   return off + x - v;
 }
 
-// tau for each query (grid T, 1024 threads): a lower bound of the k-th
-// largest tile or group maximum such that at least k of those maxima are >=
-// tau; -inf when the visible row has fewer than k tiles.  Also resets the
-// query's candidate count and overflow flag.
-__global__ __launch_bounds__(kTauThreads) void topk_tau_kernel(const float* __restrict__ tile_max,
-                                                               const int32_t* __restrict__ q_pos, int ratio,
-                                                               int64_t N, int k, void* ws, int T, int64_t cap) {
-  __shared__ SelLds sel;
-  __shared__ float g[kTauDirect];
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x;
-  TileWs w = tile_ws(ws, T, N, cap);
-  uint32_t* hdr = w.hdr + (size_t)t * kHdrWords;
-  const int64_t nv = n_visible(q_pos, t, ratio, N);
-  const int64_t ntv = (nv + kTileKeys - 1) / kTileKeys;
-  float tau = -INFINITY;
-  if (nv > k && ntv >= k) {
-    const float* row = tile_max + (size_t)t * tile_ld(N);
-    int64_t ng;
-    if (ntv <= kTauDirect) {
-      ng = ntv;
-      for (int64_t i = tid; i < ntv; i += kTauThreads) g[i] = row[i];
-    } else {
-      // group j = 4-tile runs j, j + G, j + 2G, ... (runs are 16-byte aligned)
-      ng = kTauGroups;
-      const int64_t nruns = (ntv + 3) / 4;
-      for (int j = tid; j < kTauGroups; j += kTauThreads) {
-        float m = -INFINITY;
-        for (int64_t r0 = j; r0 < nruns; r0 += 4 * (int64_t)kTauGroups) {
-          float4 x[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int64_t r = r0 + (int64_t)u * kTauGroups;
-            x[u] = r < nruns ? *reinterpret_cast<const float4*>(row + 4 * r)
-                             : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int64_t tl = 4 * (r0 + (int64_t)u * kTauGroups);
-            m = fmaxf(m, tl < ntv ? x[u].x : -INFINITY);
-            m = fmaxf(m, tl + 1 < ntv ? x[u].y : -INFINITY);
-            m = fmaxf(m, tl + 2 < ntv ? x[u].z : -INFINITY);
-            m = fmaxf(m, tl + 3 < ntv ? x[u].w : -INFINITY);
-          }
-        }
-        g[j] = m;
-      }
-    }
-    __syncthreads();
-    float lo, hi;
-    bracket_kth(sel, ng, (uint32_t)k, [&](int64_t i) { return g[i]; }, true, &lo, &hi);
-    tau = lo;
+// Position of this thread's flag among the block's set flags (ascending
+// thread order) and their total: one ballot per wave and one barrier.
+// `wsum` (one word per wave) must not be read by a previous call any more.
+__device__ __forceinline__ uint32_t block_flag_scan(bool flag, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const uint64_t b = __ballot(flag);
+  const uint32_t below = (uint32_t)__popcll(b & ((1ull << lane) - 1ull));
+  if (lane == 0) wsum[wave] = (uint32_t)__popcll(b);
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    const uint32_t c = wsum[i];
+    off += i < wave ? c : 0u;
+    tot += c;
   }
-  if (tid == 0) {
-    hdr[0] = 0u;
-    hdr[1] = __float_as_uint(tau);
-    hdr[2] = 0u;
-  }
+  *total = tot;
+  return off + below;
 }
 
 // LDS of a candidate block.
 struct alignas(16) CandLds {
   uint16_t sq[kIdxHeads * kQRowPad];
   float w[kIdxHeads];
-  uint32_t wsum[kCandThreads / 64];
+  uint32_t wsum[2][kCandThreads / 64];
   uint32_t base;
   uint16_t ctile[kCandTiles];   // candidate tiles (offset in the block's range), ascending
   uint16_t cmask[kCandTiles];   // entries of each candidate tile that reach the threshold
-  uint32_t eidx[kSelLds];       // passing entries, ascending
-  double escore[kSelLds];       // their fp64 scores
+  uint32_t eidx[kCandMax];      // passing entries, ascending
+  double escore[kCandMax];      // their fp64 scores
 };
 
 // Candidates of tiles [x*kCandTiles, (x+1)*kCandTiles) of query t
-// (grid (nblk, T), 256 threads).  Every block writes its table record.
-__global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
-    const float* __restrict__ tile_max, const float* __restrict__ err_bound, const uint16_t* __restrict__ q_idx,
+// (grid (nblk, T), one thread per tile).  Every block writes its table record.
+__global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
+    const float* __restrict__ tile_max, uint32_t* __restrict__ stats, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w_idx, const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
-    int ratio, int q_per_seq, int64_t N, int k, void* ws, int T, int64_t cap) {
+    int ratio, int q_per_seq, int64_t N, int k, void* ws, int T, int64_t cap, int slots) {
   __shared__ CandLds L;
   const int t = blockIdx.y;
   const int x = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, g = lane >> 4;
   TileWs w = tile_ws(ws, T, N, cap);
-  uint32_t* hdr = w.hdr + (size_t)t * kHdrWords;
+  uint32_t* st = stats + (size_t)t * CSA2_STATS_WORDS;
   uint2* rec = w.table + (size_t)t * cand_blocks(N) + x;
   const int64_t nv = n_visible(q_pos, t, ratio, N);
   const int64_t ntv = (nv + kTileKeys - 1) / kTileKeys;
@@ -556,63 +511,52 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
     if (tid == 0) *rec = make_uint2(0u, 0u);
     return;
   }
-  const uint16_t* qt = q_idx + (size_t)t * kIdxHeads * kIdxDim;
-  stage_query(L.sq, qt, tid, kCandThreads);
+  // all of this block's inputs at once: its tile maxima, tau, eps, the query
+  const int64_t my_tile = tile0 + tid;
+  const float tm = my_tile < ntv ? tile_max[(size_t)t * tile_ld(N) + my_tile] : -INFINITY;
+  const float eps = __uint_as_float(st[0]);
+  const float tau = __uint_as_float(st[1]);
+  stage_query(L.sq, q_idx + (size_t)t * kIdxHeads * kIdxDim, tid, kCandThreads);
   if (tid < kIdxHeads) L.w[tid] = w_idx[(size_t)t * kIdxHeads + tid];
-  const float tau = __uint_as_float(hdr[1]);
-  const double thr = next_down((double)tau - 2.0 * (double)err_bound[t]);
+  const double thr = next_down((double)tau - 2.0 * (double)eps);
 
-  // 1. candidate tiles, in order: thread tid owns tiles tile0 + 4 tid .. +3
-  const float* row = tile_max + (size_t)t * tile_ld(N);
-  uint32_t flags = 0;
-  {
-    const int64_t j = tile0 + 4 * tid;
-    if (j < ntv) {
-      const float4 m = *reinterpret_cast<const float4*>(row + j);
-      const float mv[4] = {m.x, m.y, m.z, m.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) flags |= (j + u < ntv && (double)mv[u] >= thr) ? (1u << u) : 0u;
-    }
-  }
+  // 1. candidate tiles in order
+  const bool cand = my_tile < ntv && (double)tm >= thr;
   uint32_t n_tiles;
-  uint32_t p = block_excl_scan(__popc(flags), L.wsum, &n_tiles);
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-    if (flags & (1u << u)) L.ctile[p++] = (uint16_t)(4 * tid + u);
+  const uint32_t p = block_flag_scan(cand, L.wsum[0], &n_tiles);
+  if (cand) L.ctile[p] = (uint16_t)tid;
   __syncthreads();
 
   // 2. fp32 scores of the candidate tiles (the scan's arithmetic), one tile per wave step
+  const uint16_t* kseq = k_idx + (size_t)(t / q_per_seq) * N * kIdxDim;
   {
     float wr[8];
     load_head_weights(L.w, g, wr);
-    const uint16_t* kseq = k_idx + (size_t)(t / q_per_seq) * N * kIdxDim;
     for (uint32_t ci = wave; ci < n_tiles; ci += kCandThreads / 64) {
       const int64_t s = (tile0 + L.ctile[ci]) * kTileKeys + col;
       uint4 kv[4];
       load_key_slices(kseq, s < nv ? s : nv - 1, g, kv);
       const float sc = tile_score(L.sq, kv, wr, col, g);
-      const bool pass = s < nv && (double)sc >= thr;
-      const uint64_t bal = __ballot(pass);
+      const uint64_t bal = __ballot(s < nv && (double)sc >= thr);
       if (lane == 0) L.cmask[ci] = (uint16_t)(bal & 0xFFFFu);
     }
   }
   __syncthreads();
 
-  // 3. output slots in (tile, entry) order
-  uint32_t cnt = 0;
-  for (uint32_t ci = 4 * tid; ci < 4 * tid + 4 && ci < n_tiles; ++ci) cnt += __popc((uint32_t)L.cmask[ci]);
+  // 3. output slots in (tile, entry) order: thread ci expands candidate tile ci
+  const uint32_t mine = (uint32_t)tid < n_tiles ? (uint32_t)__popc((uint32_t)L.cmask[tid]) : 0u;
   uint32_t n_pass;
-  uint32_t q0 = block_excl_scan(cnt, L.wsum, &n_pass);
-  if (n_pass > kSelLds) {  // more than the select block can hold: exact fallback for this query
+  uint32_t q0 = block_excl_scan(mine, L.wsum[1], &n_pass);
+  if (n_pass > kCandMax) {  // more than this block can hold: exact fallback for this query
     if (tid == 0) {
-      hdr[2] = 1u;
+      atomicOr(&st[2], kOverflow);
       *rec = make_uint2(0u, 0u);
     }
     return;
   }
-  for (uint32_t ci = 4 * tid; ci < 4 * tid + 4 && ci < n_tiles; ++ci) {
-    uint32_t m = L.cmask[ci];
-    const int64_t e0 = (tile0 + L.ctile[ci]) * kTileKeys;
+  if ((uint32_t)tid < n_tiles) {
+    uint32_t m = L.cmask[tid];
+    const int64_t e0 = (tile0 + L.ctile[tid]) * kTileKeys;
     while (m) {
       const int c = __ffs(m) - 1;
       m &= m - 1;
@@ -625,7 +569,6 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
   //    lane (e = lane / 32, h = lane % 32) forms dot(q_h, K_e) with 128
   //    sequential fmas, then the wave folds the 32 heads in order.
   {
-    const uint16_t* kseq = k_idx + (size_t)(t / q_per_seq) * N * kIdxDim;
     const int h = lane & 31;
     for (uint32_t e0 = 2 * wave; e0 < n_pass; e0 += 2 * (kCandThreads / 64)) {
       const uint32_t e = e0 + (lane >> 5);
@@ -654,9 +597,14 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
   }
   __syncthreads();
 
-  // 5. reserve a segment of the query's candidate array and copy out
+  // 5. the block's fixed slots, or a reserved run of shared ones, and copy out
   if (tid == 0) {
-    const uint32_t off = n_pass ? atomicAdd(&hdr[0], n_pass) : 0u;
+    uint32_t off = (uint32_t)x * (uint32_t)slots;
+    if (n_pass > (uint32_t)slots) {
+      const uint64_t first = (uint64_t)cand_blocks(N) * slots + (atomicAdd(&st[2], n_pass) & ~kOverflow);
+      if (first + n_pass > (uint64_t)cap) atomicOr(&st[2], kOverflow);
+      off = (uint32_t)(first < (uint64_t)cap ? first : cap);
+    }
     L.base = off;
     *rec = make_uint2(off, n_pass);
   }
@@ -673,33 +621,27 @@ __global__ __launch_bounds__(kCandThreads) void topk_cand_kernel(
 
 // LDS of a select block.
 struct alignas(16) SelectLds {
-  double v[kSelLds];
+  double v[kSelLds];                 // candidates' fp64 scores, index order
   uint32_t idx[kSelLds];
-  uint32_t bpos[kSelBlocks];   // first candidate of each block record
+  uint32_t bpos[kSelBlocks];         // first candidate of each block record
+  unsigned long long bmin[256], bmax[256];
   uint32_t hist[256];
-  uint32_t wsum[kSelThreads / 64];
+  uint32_t wsum[2][kSelThreads / 64];
   uint32_t pick[2];
   uint32_t n_bin;
   double red[2][kSelThreads / 64];
+  double range[2];
   double bin_vals[64];
   double result;
+  alignas(16) uint8_t flag[kSelLds];
   uint16_t sq[kIdxHeads * kQRowPad];   // query rows for the fallback's fp64 scores
   float w[kIdxHeads];
+  uint32_t hist_pad;
 };
 
-// Block min / max in fp64 (all threads).
-__device__ __forceinline__ void block_minmax_f64(SelectLds& L, double& mn, double& mx) {
-  for (int o = 32; o >= 1; o >>= 1) {
-    mn = fmin(mn, __shfl_xor(mn, o, 64));
-    mx = fmax(mx, __shfl_xor(mx, o, 64));
-  }
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) { L.red[0][w] = mn; L.red[1][w] = mx; }
-  __syncthreads();
-  mn = L.red[0][0];
-  mx = L.red[1][0];
-  for (int i = 1; i < kSelThreads / 64; ++i) { mn = fmin(mn, L.red[0][i]); mx = fmax(mx, L.red[1][i]); }
+__device__ __forceinline__ double key_f64(unsigned long long k) {
+  const unsigned long long u = (k & 0x8000000000000000ull) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+  return __longlong_as_double((long long)u);
 }
 
 __device__ __forceinline__ uint32_t bin_f64(double v, double a, double scale) {
@@ -707,37 +649,73 @@ __device__ __forceinline__ uint32_t bin_f64(double v, double a, double scale) {
   return f >= 255.0 ? 255u : (f > 0.0 ? (uint32_t)f : 0u);
 }
 
-// The kk-th largest of L.v[0..n) (1 <= kk <= n): up to four value-binned
-// levels narrow [lo, hi] to the bin holding it; a bin of at most 64 members
-// is ranked directly by one wave, a larger one resolved exactly by radix
-// passes over the order-preserving 64-bit keys.
-__device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk) {
+// Wave 0: the bin holding the rank-th largest of hist (descending from 255)
+// and the rank left inside it.
+__device__ __forceinline__ void wave_pick(const uint32_t* hist, uint32_t rank, uint32_t* bin, uint32_t* left) {
+  const int lane = threadIdx.x & 63;
+  uint32_t c[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { c[i] = hist[255 - 4 * lane - i]; sum += c[i]; }
+  uint32_t incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  uint32_t cum = incl - sum, b = 0, l = 0;
+  bool found = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (!found && cum < rank && rank <= cum + c[i]) { b = 255u - 4u * lane - i; l = rank - cum; found = true; }
+    cum += c[i];
+  }
+  const uint64_t who = __ballot(found);
+  const int src = who ? __ffsll((long long)who) - 1 : 0;
+  *bin = (uint32_t)__shfl((int)b, src, 64);
+  *left = (uint32_t)__shfl((int)l, src, 64);
+}
+
+// The kk-th largest of L.v[0..n) (1 <= kk <= n), given their range [lo, hi]:
+// value-binned levels (each keeps the chosen bin's min and max) narrow it to
+// at most 64 members, which one wave ranks directly; a bin that stays larger
+// is resolved exactly by radix passes over the 64-bit order keys.
+// L.hist / L.bmin / L.bmax must be cleared on entry.
+__device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk, double lo, double hi) {
   const int tid = threadIdx.x;
-  double lo = INFINITY, hi = -INFINITY;
-  for (uint32_t i = tid; i < n; i += kSelThreads) { lo = fmin(lo, L.v[i]); hi = fmax(hi, L.v[i]); }
-  block_minmax_f64(L, lo, hi);
-  uint32_t r = kk;  // rank (1-based, from the top) among the values in [lo, hi]
+  uint32_t r = kk;
   uint32_t count = n;
-  for (int level = 0; level < 4 && lo < hi && count > 64; ++level) {
+  for (int level = 0; level < 6 && lo < hi && count > 64; ++level) {
     const double scale = 256.0 / (hi - lo);
-    for (int i = tid; i < 256; i += kSelThreads) L.hist[i] = 0;
+    for (uint32_t i = tid; i < n; i += kSelThreads) {
+      const double v = L.v[i];
+      if (v >= lo && v <= hi) {
+        const uint32_t b = bin_f64(v, lo, scale);
+        const unsigned long long key = f64_key(v);
+        atomicAdd(&L.hist[b], 1u);
+        atomicMin(&L.bmin[b], key);
+        atomicMax(&L.bmax[b], key);
+      }
+    }
     __syncthreads();
-    for (uint32_t i = tid; i < n; i += kSelThreads) {
-      const double v = L.v[i];
-      if (v >= lo && v <= hi) atomicAdd(&L.hist[bin_f64(v, lo, scale)], 1u);
+    if (tid < 64) {
+      uint32_t b, left;
+      wave_pick(L.hist, r, &b, &left);
+      const uint32_t cb = L.hist[b];
+      const unsigned long long kmin = L.bmin[b], kmax = L.bmax[b];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { L.hist[4 * tid + i] = 0u; L.bmin[4 * tid + i] = ~0ull; L.bmax[4 * tid + i] = 0ull; }
+      if (tid == 0) {
+        L.pick[0] = cb;
+        L.pick[1] = left;
+        L.range[0] = key_f64(kmin);
+        L.range[1] = key_f64(kmax);
+      }
     }
-    pick_digit(L.hist, r, L.pick);  // bin binning is monotone in v, so bins are value ranges
-    const uint32_t b = L.pick[0];
+    __syncthreads();
+    count = L.pick[0];
     r = L.pick[1];
-    count = L.hist[b];
-    double nlo = INFINITY, nhi = -INFINITY;
-    for (uint32_t i = tid; i < n; i += kSelThreads) {
-      const double v = L.v[i];
-      if (v >= lo && v <= hi && bin_f64(v, lo, scale) == b) { nlo = fmin(nlo, v); nhi = fmax(nhi, v); }
-    }
-    block_minmax_f64(L, nlo, nhi);
-    lo = nlo;
-    hi = nhi;
+    lo = L.range[0];
+    hi = L.range[1];
   }
   if (!(lo < hi)) return lo;
   if (count <= 64) {
@@ -764,22 +742,28 @@ __device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk) {
     __syncthreads();
     return L.result;
   }
-  uint64_t pre = 0, mask = 0;
+  unsigned long long pre = 0, mask = 0;
   for (int pass = 0; pass < 8; ++pass) {
-    for (int i = tid; i < 256; i += kSelThreads) L.hist[i] = 0;
-    __syncthreads();
     for (uint32_t i = tid; i < n; i += kSelThreads) {
       const double v = L.v[i];
-      const uint64_t key = f64_key(v);
-      if (v >= lo && v <= hi && (key & mask) == pre) atomicAdd(&L.hist[(uint32_t)(key >> (56 - 8 * pass)) & 255u], 1u);
+      const unsigned long long key = f64_key(v);
+      if (v >= lo && v <= hi && (key & mask) == pre)
+        atomicAdd(&L.hist[(uint32_t)(key >> (56 - 8 * pass)) & 255u], 1u);
     }
-    pick_digit(L.hist, r, L.pick);
-    pre |= (uint64_t)L.pick[0] << (56 - 8 * pass);
-    mask |= (uint64_t)255 << (56 - 8 * pass);
+    __syncthreads();
+    if (tid < 64) {
+      uint32_t b, left;
+      wave_pick(L.hist, r, &b, &left);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) L.hist[4 * tid + i] = 0u;
+      if (tid == 0) { L.pick[0] = b; L.pick[1] = left; }
+    }
+    __syncthreads();
+    pre |= (unsigned long long)L.pick[0] << (56 - 8 * pass);
+    mask |= 255ull << (56 - 8 * pass);
     r = L.pick[1];
   }
-  const uint64_t u = (pre & 0x8000000000000000ull) ? (pre & 0x7FFFFFFFFFFFFFFFull) : ~pre;
-  return __longlong_as_double((long long)u);
+  return key_f64(pre);
 }
 
 // fp64 score of one key row with the reference's operation sequence, query
@@ -855,7 +839,7 @@ __device__ void select_streaming(SelectLds& L, uint32_t kk, const float* tm_row,
       keep = key > phi || (key == phi && low >= plo);
     }
     uint32_t tot;
-    const uint32_t pos = written + block_excl_scan(keep ? 1u : 0u, L.wsum, &tot);
+    const uint32_t pos = written + block_excl_scan(keep ? 1u : 0u, L.wsum[0], &tot);
     if (keep && pos < kk) out[pos] = (int32_t)s;
     written += tot;
   }
@@ -864,7 +848,7 @@ __device__ void select_streaming(SelectLds& L, uint32_t kk, const float* tm_row,
 // Final selection of query t (grid T, 256 threads): the k largest fp64 keys
 // among the candidates, written ascending by index.
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
-    const float* __restrict__ tile_max, const float* __restrict__ err_bound, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ tile_max, uint32_t* __restrict__ stats, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w_idx, const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
     int ratio, int q_per_seq, int64_t N, int k, int32_t* __restrict__ indices, void* ws, int T, int64_t cap) {
   __shared__ SelectLds L;
@@ -878,94 +862,128 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   }
   const uint32_t kk = (uint32_t)k;
   TileWs w = tile_ws(ws, T, N, cap);
-  const uint32_t* hdr = w.hdr + (size_t)t * kHdrWords;
-  const uint32_t cnt = hdr[0];
+  uint32_t* st = stats + (size_t)t * CSA2_STATS_WORDS;
   const int64_t nblk = cand_blocks(N);
-  const bool fits = hdr[2] == 0u && (int64_t)cnt <= cap && cnt <= kSelLds && cnt >= kk && nblk <= kSelBlocks;
-  if (!fits) {
-    const float tau = __uint_as_float(hdr[1]);
-    const double thr = next_down((double)tau - 2.0 * (double)err_bound[t]);
-    select_streaming(L, kk, tile_max + (size_t)t * tile_ld(N), nv, thr, q_idx + (size_t)t * kIdxHeads * kIdxDim,
-                     w_idx + (size_t)t * kIdxHeads, k_idx + (size_t)(t / q_per_seq) * N * kIdxDim, out);
-    return;
-  }
-  // candidates in index order: block records in block order, each in index order
   const uint2* rec = w.table + (size_t)t * nblk;
-  {
-    constexpr int kPer = kSelBlocks / kSelThreads;  // 16 records per thread
-    uint32_t c[kPer], sum = 0;
+  // header and block records in one round: thread tid owns records 16 tid .. 16 tid + 15
+  constexpr int kPer = kSelBlocks / kSelThreads;
+  uint32_t c[kPer], sum = 0;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int64_t xb = (int64_t)tid * kPer + i;
-      c[i] = xb < nblk ? rec[xb].y : 0u;
-      sum += c[i];
-    }
-    uint32_t tot;
-    uint32_t p = block_excl_scan(sum, L.wsum, &tot);
+  for (int i = 0; i < kPer; ++i) {
+    const int64_t xb = (int64_t)tid * kPer + i;
+    c[i] = xb < nblk && nblk <= kSelBlocks ? rec[xb].y : 0u;
+  }
+  const uint32_t ovf = st[2] & kOverflow;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { L.hist[4 * (tid & 63) + i] = 0u; L.bmin[4 * (tid & 63) + i] = ~0ull; L.bmax[4 * (tid & 63) + i] = 0ull; }
+  // candidates in index order: block records in block order, each in index order
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) sum += c[i];
+  uint32_t cnt;
+  {
+    uint32_t p = block_excl_scan(sum, L.wsum[0], &cnt);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       L.bpos[tid * kPer + i] = p;
       p += c[i];
     }
   }
-  __syncthreads();
-  for (uint32_t i = tid; i < cnt; i += kSelThreads) {
-    // record holding candidate i: the last record whose first slot is <= i
-    // (records sharing a first slot are empty except possibly the last one)
-    int lo = 0, hi = (int)nblk - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (L.bpos[mid] <= i) lo = mid; else hi = mid - 1;
-    }
-    const uint2 r = rec[lo];
-    const uint64_t o = (uint64_t)r.x + (i - L.bpos[lo]);
-    const bool ok = o < (uint64_t)cap;  // always true for a consistent table
-    L.v[i] = ok ? w.cscore[(size_t)t * cap + o] : -INFINITY;
-    L.idx[i] = ok ? w.cidx[(size_t)t * cap + o] : 0u;
+  if (tid == 0) st[2] = 0u;  // every thread has read it (barrier in the scan): reset for the next call
+  const bool fits = ovf == 0u && cnt <= kSelLds && cnt >= kk && nblk <= kSelBlocks;
+  if (!fits) {
+    const float tau = __uint_as_float(st[1]);
+    const double thr = next_down((double)tau - 2.0 * (double)__uint_as_float(st[0]));
+    select_streaming(L, kk, tile_max + (size_t)t * tile_ld(N), nv, thr, q_idx + (size_t)t * kIdxHeads * kIdxDim,
+                     w_idx + (size_t)t * kIdxHeads, k_idx + (size_t)(t / q_per_seq) * N * kIdxDim, out);
+    return;
   }
   __syncthreads();
-  const double V = kth_largest_f64(L, cnt, kk);
-  // entries above V are in; of those equal to V, the lowest indices (first in order)
-  constexpr int kPerC = kSelLds / kSelThreads;  // 16 consecutive candidates per thread
-  const uint32_t c0 = tid * kPerC;
-  uint32_t n_gt = 0, n_eq = 0;
+  double lo = INFINITY, hi = -INFINITY;
+  for (uint32_t i0 = 0; i0 < cnt; i0 += 4 * kSelThreads) {
+    double v[4];
+    uint32_t ix[4];
 #pragma unroll
-  for (int i = 0; i < kPerC; ++i) {
-    const uint32_t j = c0 + i;
-    if (j < cnt) {
-      n_gt += L.v[j] > V;
-      n_eq += L.v[j] == V;
-    }
-  }
-  uint32_t tot_gt, tot_eq;
-  block_excl_scan(n_gt, L.wsum, &tot_gt);
-  uint32_t eq_before = block_excl_scan(n_eq, L.wsum, &tot_eq);
-  const uint32_t need_eq = kk - tot_gt;
-  uint32_t n_sel = 0;
-#pragma unroll
-  for (int i = 0; i < kPerC; ++i) {
-    const uint32_t j = c0 + i;
-    if (j < cnt) {
-      const bool eq = L.v[j] == V;
-      n_sel += (L.v[j] > V) || (eq && eq_before < need_eq);
-      eq_before += eq;
-    }
-  }
-  uint32_t tot_sel;
-  uint32_t pos = block_excl_scan(n_sel, L.wsum, &tot_sel);
-  eq_before -= n_eq;  // back to this thread's first candidate
-#pragma unroll
-  for (int i = 0; i < kPerC; ++i) {
-    const uint32_t j = c0 + i;
-    if (j < cnt) {
-      const bool eq = L.v[j] == V;
-      const bool sel = (L.v[j] > V) || (eq && eq_before < need_eq);
-      eq_before += eq;
-      if (sel) {
-        if (pos < kk) out[pos] = (int32_t)L.idx[j];
-        ++pos;
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t i = i0 + u * kSelThreads + tid;
+      v[u] = -INFINITY;
+      ix[u] = 0u;
+      if (i < cnt) {
+        // the record holding candidate i: the last one whose first slot is <= i
+        // (records sharing a first slot are empty except possibly the last)
+        int a = 0, b = (int)nblk - 1;
+        while (a < b) {
+          const int mid = (a + b + 1) >> 1;
+          if (L.bpos[mid] <= i) a = mid; else b = mid - 1;
+        }
+        const uint64_t o = (uint64_t)rec[a].x + (i - L.bpos[a]);
+        if (o < (uint64_t)cap) {  // always true for a consistent table
+          v[u] = w.cscore[(size_t)t * cap + o];
+          ix[u] = w.cidx[(size_t)t * cap + o];
+        }
       }
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t i = i0 + u * kSelThreads + tid;
+      if (i < cnt) {
+        L.v[i] = v[u];
+        L.idx[i] = ix[u];
+        lo = fmin(lo, v[u]);
+        hi = fmax(hi, v[u]);
+      }
+    }
+  }
+  {
+    const int lane = tid & 63, wv = tid >> 6;
+    for (int o = 32; o >= 1; o >>= 1) {
+      lo = fmin(lo, __shfl_xor(lo, o, 64));
+      hi = fmax(hi, __shfl_xor(hi, o, 64));
+    }
+    if (lane == 0) { L.red[0][wv] = lo; L.red[1][wv] = hi; }
+    __syncthreads();
+    lo = L.red[0][0];
+    hi = L.red[1][0];
+    for (int i = 1; i < kSelThreads / 64; ++i) { lo = fmin(lo, L.red[0][i]); hi = fmax(hi, L.red[1][i]); }
+  }
+  const double V = kth_largest_f64(L, cnt, kk, lo, hi);
+
+  // entries above V are in; of those equal to V, the lowest indices (first in order)
+  uint32_t n_gt = 0;
+  for (uint32_t i = tid; i < kSelLds; i += kSelThreads) {
+    uint8_t f = 0;
+    if (i < cnt) {
+      const double v = L.v[i];
+      f = v > V ? 2 : (v == V ? 1 : 0);
+    }
+    L.flag[i] = f;
+    n_gt += f == 2;
+  }
+  uint32_t tot_gt;
+  block_excl_scan(n_gt, L.wsum[1], &tot_gt);  // (barrier: the flags are complete)
+  const uint32_t need_eq = kk - tot_gt;
+  constexpr int kPerC = kSelLds / kSelThreads;  // thread tid owns candidates 16 tid .. 16 tid + 15
+  const uint4 fw = *reinterpret_cast<const uint4*>(&L.flag[tid * kPerC]);
+  const uint32_t fwords[4] = {fw.x, fw.y, fw.z, fw.w};
+  uint32_t n_eq = 0;
+#pragma unroll
+  for (int i = 0; i < kPerC; ++i) n_eq += ((fwords[i >> 2] >> (8 * (i & 3))) & 255u) == 1u;
+  uint32_t tot_eq;
+  const uint32_t eq0 = block_excl_scan(n_eq, L.wsum[0], &tot_eq);
+  uint32_t selmask = 0, eqb = eq0;
+#pragma unroll
+  for (int i = 0; i < kPerC; ++i) {
+    const uint32_t f = (fwords[i >> 2] >> (8 * (i & 3))) & 255u;
+    const bool sel = f == 2u || (f == 1u && eqb < need_eq);
+    eqb += f == 1u;
+    selmask |= sel ? (1u << i) : 0u;
+  }
+  uint32_t tot_sel;
+  uint32_t pos = block_excl_scan((uint32_t)__popc(selmask), L.wsum[1], &tot_sel);
+  while (selmask) {
+    const int i = __ffs(selmask) - 1;
+    selmask &= selmask - 1;
+    if (pos < kk) out[pos] = (int32_t)L.idx[tid * kPerC + i];
+    ++pos;
   }
 }
 
@@ -973,22 +991,30 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
 
 using namespace csa2;
 
-// Candidate capacity per query that a workspace of ws_bytes provides (-1: too small).
-static int64_t topk_cap_for(size_t ws_bytes, int32_t T, int64_t N) {
+// Candidate layout a workspace of ws_bytes provides: per-block fixed slots
+// (kSlots, or 0 when it is small) and the per-query capacity; false if too small.
+static bool topk_layout(size_t ws_bytes, int32_t T, int64_t N, int* slots, int64_t* cap) {
   const size_t fixed = tile_ws_fixed(T, N);
-  if (ws_bytes < fixed) return -1;
-  int64_t cap = (int64_t)((ws_bytes - fixed) / ((size_t)T * 12));
-  cap = cap / 4 * 4;  // keeps the index array 16-byte aligned
-  const int64_t nmax = (N + 3) / 4 * 4;
-  return cap < nmax ? cap : nmax;
+  if (ws_bytes < fixed) return false;
+  const int64_t per = (int64_t)((ws_bytes - fixed) / ((size_t)T * 12));
+  const int64_t fixed_slots = cand_blocks(N) * kSlots;
+  int64_t c;
+  if (per >= fixed_slots + kDefaultSpill) {
+    *slots = kSlots;
+    c = per < fixed_slots + kMaxSpill ? per : fixed_slots + kMaxSpill;
+  } else {
+    *slots = 0;
+    c = per < kMaxSpill ? per : kMaxSpill;
+  }
+  *cap = c / 4 * 4;  // keeps the index array 16-byte aligned
+  return true;
 }
 
 static bool topk_row_regime(const float* scores, int64_t N) { return scores != nullptr && N <= kSmallMax; }
 
 extern "C" size_t csa2_topk_workspace_bytes(int32_t T, int64_t N, int32_t k) {
   if (T < 1 || N < 1 || k != kTopK) return 0;
-  int64_t cap = (N + 3) / 4 * 4;
-  if (cap > kDefaultCap) cap = kDefaultCap;
+  const int64_t cap = cand_blocks(N) * kSlots + kDefaultSpill;
   return tile_ws_fixed(T, N) + (size_t)T * (size_t)cap * 12;
 }
 
@@ -997,12 +1023,12 @@ extern "C" size_t csa2_topk_min_workspace_bytes(int32_t T, int64_t N, int32_t k)
   return tile_ws_fixed(T, N);
 }
 
-extern "C" csa2_status csa2_topk(const float* scores, const float* tile_max, const float* err_bound,
-                                 const void* q_idx, const float* w_idx, const void* k_idx, const int32_t* q_pos,
-                                 int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N, int32_t k,
-                                 int32_t* indices, void* workspace, size_t workspace_bytes, void* hip_stream) {
-  if (!err_bound || !q_idx || !w_idx || !k_idx || !indices) return CSA2_ERR_INVALID_ARG;
-  if ((scores && !aligned16(scores)) || (tile_max && !aligned16(tile_max)) || !aligned16(err_bound) ||
+extern "C" csa2_status csa2_topk(const float* scores, const float* tile_max, uint32_t* stats, const void* q_idx,
+                                 const float* w_idx, const void* k_idx, const int32_t* q_pos, int32_t ratio,
+                                 int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices,
+                                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!stats || !q_idx || !w_idx || !k_idx || !indices) return CSA2_ERR_INVALID_ARG;
+  if ((scores && !aligned16(scores)) || (tile_max && !aligned16(tile_max)) || !aligned16(stats) ||
       !aligned16(q_idx) || !aligned16(w_idx) || !aligned16(k_idx) || !aligned16(indices) ||
       (q_pos && !aligned16(q_pos)))
     return CSA2_ERR_INVALID_ARG;
@@ -1013,7 +1039,7 @@ extern "C" csa2_status csa2_topk(const float* scores, const float* tile_max, con
   const uint16_t* q = (const uint16_t*)q_idx;
   const uint16_t* kx = (const uint16_t*)k_idx;
   if (topk_row_regime(scores, N)) {
-    hipLaunchKernelGGL(topk_small_kernel, dim3(T), dim3(kFinThreads), 0, st, scores, err_bound, q,
+    hipLaunchKernelGGL(topk_small_kernel, dim3(T), dim3(kFinThreads), 0, st, scores, (const uint32_t*)stats, q,
                        w_idx, kx, q_pos, ratio, q_per_seq, N, k, indices);
     if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
     return CSA2_OK;
@@ -1021,14 +1047,13 @@ extern "C" csa2_status csa2_topk(const float* scores, const float* tile_max, con
   if (!tile_max) return CSA2_ERR_INVALID_ARG;
   if (!workspace || !aligned16(workspace) || workspace_bytes < csa2_topk_min_workspace_bytes(T, N, k))
     return CSA2_ERR_WORKSPACE;
-  const int64_t cap = topk_cap_for(workspace_bytes, T, N);
-  if (cap < 0) return CSA2_ERR_WORKSPACE;
+  int slots;
+  int64_t cap;
+  if (!topk_layout(workspace_bytes, T, N, &slots, &cap)) return CSA2_ERR_WORKSPACE;
   const int64_t nblk = cand_blocks(N);
-  hipLaunchKernelGGL(topk_tau_kernel, dim3(T), dim3(kTauThreads), 0, st, tile_max, q_pos, ratio, N, k, workspace, T,
-                     cap);
-  hipLaunchKernelGGL(topk_cand_kernel, dim3((unsigned)nblk, T), dim3(kCandThreads), 0, st, tile_max, err_bound, q,
-                     w_idx, kx, q_pos, ratio, q_per_seq, N, k, workspace, T, cap);
-  hipLaunchKernelGGL(topk_select_kernel, dim3(T), dim3(kSelThreads), 0, st, tile_max, err_bound, q, w_idx, kx, q_pos,
+  hipLaunchKernelGGL(topk_cand_kernel, dim3((unsigned)nblk, T), dim3(kCandThreads), 0, st, tile_max, stats, q,
+                     w_idx, kx, q_pos, ratio, q_per_seq, N, k, workspace, T, cap, slots);
+  hipLaunchKernelGGL(topk_select_kernel, dim3(T), dim3(kSelThreads), 0, st, tile_max, stats, q, w_idx, kx, q_pos,
                      ratio, q_per_seq, N, k, indices, workspace, T, cap);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   return CSA2_OK;

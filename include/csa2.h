@@ -90,20 +90,25 @@ const char* csa2_version(void);
  *            tile_max[t][j] = max of the scores of entries 16j .. 16j+15 (those
  *            < N), -inf if none of them is visible; the ld - ceil(N/16)
  *            padding slots of each row are left unspecified
- *  err_bound fp32  [T]    out     eps_t >= |score(t,s) - I_fp64(t,s)| for every
- *                                 visible s, where I_fp64 is the score evaluated in
- *                                 fp64 with one fma per term, channels then heads
- *                                 in order; csa2_topk uses it to make the
- *                                 selection exact.
+ *  stats     uint32 [T][CSA2_STATS_WORDS] out, per query:
+ *            [0] eps_t (fp32 bits) >= |score(t,s) - I_fp64(t,s)| for every
+ *                visible s, where I_fp64 is the score evaluated in fp64 with one
+ *                fma per term, channels then heads in order;
+ *            [1] floor_t (fp32 bits): at least CSA2_TOPK visible entries have
+ *                fp32 score >= floor_t (-inf when the row has fewer than
+ *                CSA2_TOPK non-empty tiles of 16 entries);
+ *            [2], [3] zero: counters that csa2_topk uses and leaves zero.
+ *            csa2_topk consumes eps and floor to make the selection exact.
  *  workspace >= csa2_index_workspace_bytes(T, q_per_seq, N) bytes (any contents).
  * Requires T >= 1, q_per_seq >= 1, T % q_per_seq == 0, 1 <= N < 2^31.
  */
 #define CSA2_TILE 16
+#define CSA2_STATS_WORDS 4
 int64_t csa2_tile_max_ld(int64_t N);
 size_t csa2_index_workspace_bytes(int32_t T, int32_t q_per_seq, int64_t N);
 csa2_status csa2_index(const void* q_idx, const float* w_idx, const void* k_idx,
                        const int32_t* q_pos, int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N,
-                       float* scores, float* tile_max, float* err_bound, void* workspace,
+                       float* scores, float* tile_max, uint32_t* stats, void* workspace,
                        size_t workspace_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------- topk
@@ -118,7 +123,9 @@ csa2_status csa2_index(const void* q_idx, const float* w_idx, const void* k_idx,
  *  scores     the scores output of csa2_index, or NULL.  When given and
  *             N <= CSA2_TOPK_ROW_MAX, each query's row is selected in LDS in one
  *             pass; otherwise the selection works from tile_max and the keys.
- *  tile_max, err_bound   outputs of csa2_index for the same arguments
+ *  tile_max, stats   outputs of csa2_index for the same arguments; stats words
+ *             [2] and [3] are used as counters and left zero (concurrent
+ *             csa2_topk calls must not share a stats array)
  *  q_idx, w_idx, k_idx, q_pos, ratio   as passed to csa2_index
  *  k          must be CSA2_TOPK (512)
  *  indices    int32 [T][k] out
@@ -130,7 +137,7 @@ csa2_status csa2_index(const void* q_idx, const float* w_idx, const void* k_idx,
 #define CSA2_TOPK_ROW_MAX 36864
 size_t csa2_topk_workspace_bytes(int32_t T, int64_t N, int32_t k);
 size_t csa2_topk_min_workspace_bytes(int32_t T, int64_t N, int32_t k);
-csa2_status csa2_topk(const float* scores, const float* tile_max, const float* err_bound,
+csa2_status csa2_topk(const float* scores, const float* tile_max, uint32_t* stats,
                       const void* q_idx, const float* w_idx, const void* k_idx, const int32_t* q_pos,
                       int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices,
                       void* workspace, size_t workspace_bytes, void* hip_stream);

@@ -74,7 +74,8 @@ def test_index_host_validation(L):
     assert _index(L, q=None) == INVALID
     assert _index(L, tm=None) == INVALID
     assert _index(L, s=MIS) == INVALID
-    assert _index(L, e=None) == INVALID
+    assert _index(L, e=None) == INVALID             # stats
+    assert _index(L, ws=MIS) == WORKSPACE
     assert _index(L, k=MIS) == INVALID
     assert _index(L, T=0) == INVALID
     assert _index(L, T=4, qps=3) == INVALID
@@ -97,7 +98,7 @@ def _topk(L, s=None, tm=P, e=P, q=P, w=P, k_idx=P, pos=None, ratio=1, T=4, qps=1
 def test_topk_host_validation(L):
     assert _topk(L, tm=None) == INVALID              # no scores and no tile maxima
     assert _topk(L, s=P, tm=None) == INVALID         # long rows always use the tile regime
-    assert _topk(L, e=None) == INVALID
+    assert _topk(L, e=None) == INVALID              # stats
     assert _topk(L, tm=MIS) == INVALID
     assert _topk(L, out=MIS) == INVALID
     assert _topk(L, T=5, qps=2) == INVALID

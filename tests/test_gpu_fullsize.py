@@ -33,7 +33,7 @@ def run_full(c, layers=1, path="tiles"):
     selected in LDS.  A second scan with scores provides them for the bound check."""
     bf = (c.q_idx.view(BF), c.w_idx, c.k_idx.view(BF), c.q_pos, c.ratio, c.q_per_seq)
     ix = csa.csa2_index(*bf, want_scores=(path == "rows"))
-    idx = csa.csa2_topk(ix.scores, ix.tile_max, ix.err_bound, *bf)
+    idx = csa.csa2_topk(ix.scores, ix.tile_max, ix.stats, *bf)
     out = csa.csa2_attend_fp4(c.q[0].view(BF), c.kv_codes, c.kv_scales, idx, c.swa[0].view(BF), c.swa_end, None,
                               c.softmax_scale, c.q_per_seq, c.window)
     re = None
@@ -44,7 +44,7 @@ def run_full(c, layers=1, path="tiles"):
     full = ix if path == "rows" else csa.csa2_index(*bf)
     torch.cuda.synchronize()
     nt = -(-c.N // 16)
-    assert torch.equal(full.tile_max[:, :nt], ix.tile_max[:, :nt]) and torch.equal(full.err_bound, ix.err_bound)
+    assert torch.equal(full.tile_max[:, :nt], ix.tile_max[:, :nt]) and torch.equal(full.stats[:, :2], ix.stats[:, :2])
     return full.scores, full.err_bound, idx, out, re
 
 

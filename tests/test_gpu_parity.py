@@ -51,7 +51,7 @@ def run_index(c, want_scores=True):
 def run_topk(c, ix, path="tiles", workspace=None):
     """path "rows": scores given (one-pass LDS selection when N <= 36864); "tiles": no score
     matrix, selection from tile maxima and the keys."""
-    return csa.csa2_topk(ix.scores if path == "rows" else None, ix.tile_max, ix.err_bound,
+    return csa.csa2_topk(ix.scores if path == "rows" else None, ix.tile_max, ix.stats,
                          c.q_idx.view(torch.bfloat16), c.w_idx, c.k_idx.view(torch.bfloat16), c.q_pos, c.ratio,
                          c.q_per_seq, workspace=workspace)
 
@@ -69,10 +69,11 @@ def test_index_scores_within_bound(name):
     ix2 = run_index(c, want_scores=False)
     torch.cuda.synchronize()
     ref = oracle_scores(c, range(c.T))
-    s, e, tm = npy(ix.scores), npy(ix.err_bound), npy(ix.tile_max)
-    # the tile maxima (padding slots excluded) and the bound do not depend on whether scores are written
+    s, e, tm, fl = npy(ix.scores), npy(ix.err_bound), npy(ix.tile_max), npy(ix.floor)
+    # the tile maxima (padding slots excluded) and the stats do not depend on whether scores are written
     nt = -(-c.N // 16)
-    assert np.array_equal(tm[:, :nt], npy(ix2.tile_max)[:, :nt]) and np.array_equal(e, npy(ix2.err_bound))
+    assert np.array_equal(tm[:, :nt], npy(ix2.tile_max)[:, :nt]) and np.array_equal(npy(ix.stats), npy(ix2.stats))
+    assert np.all(npy(ix.stats)[:, 2:] == 0)
     pad = np.full((c.T, nt * 16 - c.N), -np.inf, np.float32)
     assert np.array_equal(tm[:, :nt], np.concatenate([s, pad], axis=1).reshape(c.T, nt, 16).max(axis=2))
     worst = 0.0
@@ -81,6 +82,13 @@ def test_index_scores_within_bound(name):
         assert np.all(np.isneginf(s[t, nv:])), "entries beyond visibility must be -inf"
         err = np.abs(s[t, :nv].astype(np.float64) - ref[t][:nv])
         assert np.all(err <= e[t]), f"t={t}: max err {err.max()} > eps {e[t]}"
+        # the floor: at least 512 visible fp32 scores reach it (-inf if fewer than 512 non-empty tiles)
+        if -(-nv // 16) >= 512:
+            assert np.isfinite(fl[t]) and np.count_nonzero(s[t, :nv] >= fl[t]) >= 512
+            # and it is useful: no more than 4 x 512 entries reach it at these sizes
+            assert np.count_nonzero(s[t, :nv] >= fl[t]) <= 2048, np.count_nonzero(s[t, :nv] >= fl[t])
+        else:
+            assert np.isneginf(fl[t])
         if nv:
             worst = max(worst, float(err.max() / e[t]))
             # the bound must stay small next to the scores, or the candidate set explodes
@@ -96,6 +104,7 @@ def test_topk_bit_exact(name, path):
     ix = run_index(c, want_scores=(path == "rows"))
     idx = run_topk(c, ix, path)
     torch.cuda.synchronize()
+    assert np.all(npy(ix.stats)[:, 2:] == 0), "csa2_topk must leave its counters zero"
     ref = oracle_topk(c, oracle_scores(c, range(c.T)))
     got = npy(idx)
     for t in range(c.T):
@@ -246,7 +255,7 @@ def test_pipeline_is_deterministic():
     b_i = run_topk(c, b, "tiles")
     b_o = _attend(c, b_i, lse=False)
     torch.cuda.synchronize()
-    assert torch.equal(a.scores, b.scores) and torch.equal(a.err_bound, b.err_bound)
+    assert torch.equal(a.scores, b.scores) and torch.equal(a.stats, b.stats)
     assert torch.equal(a.tile_max[:, :-(-c.N // 16)], b.tile_max[:, :-(-c.N // 16)])
     assert torch.equal(a_i, b_i) and torch.equal(a_o, b_o)
 
