@@ -180,9 +180,9 @@ __global__ __launch_bounds__(kScanThreads, QG == 1 ? 4 : 2) void idx_scan_kernel
 // (relative error below 2^-16 even with two roundings per step), so it is
 // inflated by (1 + 2^-10) before the square root.  ||q_h||^2 is summed in
 // fp64 (relative error below 2^-45 in any order), covered by (1 + 2^-40).
-constexpr int kFinThreads = 1024;
+constexpr int kFinThreads = 512;
 constexpr int kFloorVals = 16384;            // maxima a finalize block ranks
-constexpr int kFloorPer = kFloorVals / kFinThreads;  // 16 per thread, in registers
+constexpr int kFloorPer = kFloorVals / kFinThreads;  // 32 per thread, in registers
 
 // LDS of the finalize block.
 struct alignas(16) FinalLds {
@@ -194,7 +194,7 @@ struct alignas(16) FinalLds {
   uint32_t res;
 };
 
-// Per query (grid T, 1024 threads): the error bound eps and the selection
+// Per query (grid T, 512 threads): the error bound eps and the selection
 // floor tau, written to stats[t] = {eps, tau, 0, 0} (the last two words are
 // csa2_topk's counters).  tau: at least CSA2_TOPK visible fp32 scores are >=
 // tau, because it bounds from below the CSA2_TOPK-th largest of a set of
@@ -205,7 +205,7 @@ struct alignas(16) FinalLds {
 // tile maxima folded to 16384 groups of tiles j, j + 16384, ...; folding
 // unions groups, which keeps them disjoint.
 //
-// Ranking: thread i holds maxima i, i + 1024, ...; the smallest per-thread
+// Ranking: each thread holds 32 of the maxima; the smallest per-thread
 // maximum L0 is already a valid lower bound when at least CSA2_TOPK threads
 // hold one (that many distinct maxima reach it), so only values >= L0 enter a
 // histogram of 256 bins over [L0, max] that also keeps each bin's minimum.
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kFinThreads) void idx_finalize_kernel(
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = t / q_per_seq;
-  if (tid < 256) { L.hist[tid] = 0u; L.bmin[tid] = 0xFFFFFFFFu; }
+  for (int i = tid; i < 256; i += kFinThreads) { L.hist[i] = 0u; L.bmin[i] = 0xFFFFFFFFu; }
 
   // ---- floor: gather the maxima into registers (folded into at most 16384 values)
   const int64_t nv = n_visible(q_pos, t, ratio, N);
@@ -227,16 +227,25 @@ __global__ __launch_bounds__(kFinThreads) void idx_finalize_kernel(
   const bool use_groups = ntv > kFloorVals && n_groups >= kGroupsWanted;
   const float* src = use_groups ? group_max + (size_t)t * n_groups : tile_max + (size_t)t * tile_ld(N);
   const int64_t nsrc = nv > kTopK ? (use_groups ? n_groups : ntv) : 0;
+  // value j = src[j] (rows are 16-byte aligned: four per load); past 16384,
+  // fold: value j is the maximum over j, j + 16384, ...
   float v[kFloorPer];
 #pragma unroll
-  for (int m = 0; m < kFloorPer; ++m) {
-    const int64_t j = (int64_t)m * kFinThreads + tid;
-    v[m] = j < nsrc ? src[j] : -INFINITY;
+  for (int m = 0; m < kFloorPer / 4; ++m) {
+    const int64_t j = 4 * ((int64_t)m * kFinThreads + tid);
+    const float4 x = j < nsrc ? *reinterpret_cast<const float4*>(src + j)
+                              : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    v[4 * m] = x.x;
+    v[4 * m + 1] = j + 1 < nsrc ? x.y : -INFINITY;
+    v[4 * m + 2] = j + 2 < nsrc ? x.z : -INFINITY;
+    v[4 * m + 3] = j + 3 < nsrc ? x.w : -INFINITY;
   }
-  if (nsrc > kFloorVals) {  // fold: value j is the maximum over j, j + 16384, ...
+  if (nsrc > kFloorVals) {
 #pragma unroll
-    for (int m = 0; m < kFloorPer; ++m)
-      for (int64_t i = (int64_t)m * kFinThreads + tid + kFloorVals; i < nsrc; i += kFloorVals) v[m] = fmaxf(v[m], src[i]);
+    for (int m = 0; m < kFloorPer; ++m) {
+      const int64_t j = 4 * ((int64_t)(m / 4) * kFinThreads + tid) + (m % 4);
+      for (int64_t i = j + kFloorVals; i < nsrc; i += kFloorVals) v[m] = fmaxf(v[m], src[i]);
+    }
   }
   float lmax = -INFINITY, lmin = INFINITY;
   uint32_t finite = 0;

@@ -623,7 +623,7 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
 struct alignas(16) SelectLds {
   double v[kSelLds];                 // candidates' fp64 scores, index order
   uint32_t idx[kSelLds];
-  uint32_t bpos[kSelBlocks];         // first candidate of each block record
+  uint32_t src[kSelLds];             // slot of each candidate, index order
   unsigned long long bmin[256], bmax[256];
   uint32_t hist[256];
   uint32_t wsum[2][kSelThreads / 64];
@@ -865,36 +865,32 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   uint32_t* st = stats + (size_t)t * CSA2_STATS_WORDS;
   const int64_t nblk = cand_blocks(N);
   const uint2* rec = w.table + (size_t)t * nblk;
-  // header and block records in one round: thread tid owns records 16 tid .. 16 tid + 15
-  constexpr int kPer = kSelBlocks / kSelThreads;
-  uint32_t c[kPer], sum = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int64_t xb = (int64_t)tid * kPer + i;
-    c[i] = xb < nblk && nblk <= kSelBlocks ? rec[xb].y : 0u;
-  }
   const uint32_t ovf = st[2] & kOverflow;
 #pragma unroll
   for (int i = 0; i < 4; ++i) { L.hist[4 * (tid & 63) + i] = 0u; L.bmin[4 * (tid & 63) + i] = ~0ull; L.bmax[4 * (tid & 63) + i] = 0ull; }
-  // candidates in index order: block records in block order, each in index order
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) sum += c[i];
-  uint32_t cnt;
-  {
-    uint32_t p = block_excl_scan(sum, L.wsum[0], &cnt);
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      L.bpos[tid * kPer + i] = p;
-      p += c[i];
-    }
+  // candidates in index order: block records in block order, each in index
+  // order.  Records are taken 256 at a time, one per thread; each thread
+  // expands its record into source offsets (LDS), then every candidate is
+  // fetched in one round of loads.  (The counter word has been read by every
+  // thread once the first scan's barrier has passed; it is reset at the end.)
+  uint32_t cnt = 0;
+  const bool small_table = nblk <= kSelBlocks;
+  for (int64_t x0 = 0; small_table && x0 < nblk; x0 += kSelThreads) {
+    const int64_t xb = x0 + tid;
+    const uint2 r = xb < nblk ? rec[xb] : make_uint2(0u, 0u);
+    uint32_t tot;
+    const uint32_t p = cnt + block_excl_scan(r.y, L.wsum[0], &tot);
+    if (cnt + tot <= kSelLds)
+      for (uint32_t j = 0; j < r.y; ++j) L.src[p + j] = r.x + j;
+    cnt += tot;
   }
-  if (tid == 0) st[2] = 0u;  // every thread has read it (barrier in the scan): reset for the next call
-  const bool fits = ovf == 0u && cnt <= kSelLds && cnt >= kk && nblk <= kSelBlocks;
+  const bool fits = ovf == 0u && small_table && cnt <= kSelLds && cnt >= kk;
   if (!fits) {
     const float tau = __uint_as_float(st[1]);
     const double thr = next_down((double)tau - 2.0 * (double)__uint_as_float(st[0]));
     select_streaming(L, kk, tile_max + (size_t)t * tile_ld(N), nv, thr, q_idx + (size_t)t * kIdxHeads * kIdxDim,
                      w_idx + (size_t)t * kIdxHeads, k_idx + (size_t)(t / q_per_seq) * N * kIdxDim, out);
+    if (tid == 0) st[2] = 0u;
     return;
   }
   __syncthreads();
@@ -908,14 +904,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
       v[u] = -INFINITY;
       ix[u] = 0u;
       if (i < cnt) {
-        // the record holding candidate i: the last one whose first slot is <= i
-        // (records sharing a first slot are empty except possibly the last)
-        int a = 0, b = (int)nblk - 1;
-        while (a < b) {
-          const int mid = (a + b + 1) >> 1;
-          if (L.bpos[mid] <= i) a = mid; else b = mid - 1;
-        }
-        const uint64_t o = (uint64_t)rec[a].x + (i - L.bpos[a]);
+        const uint32_t o = L.src[i];
         if (o < (uint64_t)cap) {  // always true for a consistent table
           v[u] = w.cscore[(size_t)t * cap + o];
           ix[u] = w.cidx[(size_t)t * cap + o];
@@ -985,6 +974,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     if (pos < kk) out[pos] = (int32_t)L.idx[tid * kPerC + i];
     ++pos;
   }
+  if (tid == 0) st[2] = 0u;
 }
 
 }  // namespace csa2
