@@ -66,24 +66,26 @@ __device__ __forceinline__ bf16x8 lds_read16(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(__builtin_assume_aligned(p, 16));
 }
 
-// E2M1 magnitude (OCP MX) of a 3-bit code as an fp32 bit pattern.
-__device__ __forceinline__ uint32_t e2m1_bits(uint32_t c) {
-  const uint32_t e = c >> 1, m = c & 1u;
-  return e == 0 ? (m ? 0x3F000000u : 0u) : (((126u + e) << 23) | (m << 22));
+// 8 FP4 codes (one 32-bit word, element 2i in the low nibble of byte i) times
+// the block scale 2^(s-127) -> 8 bf16 (4 words, element 2i in the low half).
+// v_cvt_scalef32_pk_bf16_fp4 converts the two codes of one byte with an fp32
+// scale; every E2M1 value times a power of two is exact in bf16 (at most two
+// significant bits), and the scale byte s maps to the fp32 2^(s-127) (s = 0:
+// the subnormal 2^-127; s = 255 is not a valid E8M0 scale).
+__device__ __forceinline__ uint4 dequant8(uint32_t codes, uint32_t sbyte) {
+  const float sc = __uint_as_float(sbyte == 0 ? 0x00400000u : (sbyte << 23));
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
+  return r;
 }
 
-// 8 FP4 codes (one 32-bit word, element 2i in the low nibble of byte i) times
-// the block scale 2^(s-127) -> 8 bf16 bit patterns (exact: every such value
-// has at most two significant bits).
-__device__ __forceinline__ void dequant8(uint32_t codes, uint32_t sbyte, uint32_t* o) {
-  const float sc = __uint_as_float(sbyte == 0 ? 0x00400000u : (sbyte << 23));
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t c = (codes >> (4 * i)) & 15u;
-    const float v = __uint_as_float(e2m1_bits(c & 7u)) * sc;
-    o[i] = (__float_as_uint(v) >> 16) | ((c & 8u) << 12);
-  }
-}
+// XT rows hold 32 bf16 in four 16-byte blocks; block b of row r is stored at
+// position (b + r / 8) % 4 so that the transposing writes of one staging step
+// (rows 8d + i for the 64 lanes d) spread over the LDS banks.
+__device__ __forceinline__ int xt_off(int row, int blk) { return row * kXTStride + 8 * ((blk + (row >> 3)) & 3); }
 
 // Stage chunk `c` of query t (layer `layer` for window chunks) into LDS.
 // Thread (g = wave, d = lane) loads 8 rows x 8 channels: rows {4g..4g+3,
@@ -111,10 +113,9 @@ __device__ void stage_chunk(const AttnArgs& a, AttnShared& sh, int t, int b, int
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       okr[r] = idx[r] >= 0;
-      uint32_t o[8];
-      dequant8(codes[r], sbyte[r], o);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[r][i] = okr[r] ? (o[2 * i] | (o[2 * i + 1] << 16)) : 0u;
+      const uint4 o = dequant8(codes[r], sbyte[r]);
+      v[r][0] = okr[r] ? o.x : 0u; v[r][1] = okr[r] ? o.y : 0u;
+      v[r][2] = okr[r] ? o.z : 0u; v[r][3] = okr[r] ? o.w : 0u;
     }
   } else {
     const int we = a.swa_end[t];
@@ -146,7 +147,7 @@ __device__ void stage_chunk(const AttnArgs& a, AttnShared& sh, int t, int b, int
       const uint32_t hi = (v[2 * p + 1][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
       w[p] = lo | (hi << 16);
     }
-    *reinterpret_cast<uint4*>(&sh.XT[(8 * d + i) * kXTStride + 8 * g]) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(&sh.XT[xt_off(8 * d + i, g)]) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -214,7 +215,7 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const AttnShared
 #pragma unroll
   for (int mb = 0; mb < 32; ++mb) {
     st.o[mb] *= alpha;
-    const bf16x8 xa = lds_read16(&sh.XT[(16 * mb + r16) * kXTStride + 8 * g]);
+    const bf16x8 xa = lds_read16(&sh.XT[xt_off(16 * mb + r16, g)]);
     st.o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, pv, st.o[mb], 0, 0, 0);
   }
 }
