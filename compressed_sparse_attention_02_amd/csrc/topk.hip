@@ -527,18 +527,33 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   if (cand) L.ctile[p] = (uint16_t)tid;
   __syncthreads();
 
-  // 2. fp32 scores of the candidate tiles (the scan's arithmetic), one tile per wave step
+  // 2. fp32 scores of the candidate tiles (the scan's arithmetic): wave w takes
+  //    tiles w, w + 4, ...; the rows of up to four of its tiles are requested
+  //    before any is scored
   const uint16_t* kseq = k_idx + (size_t)(t / q_per_seq) * N * kIdxDim;
   {
     float wr[8];
     load_head_weights(L.w, g, wr);
-    for (uint32_t ci = wave; ci < n_tiles; ci += kCandThreads / 64) {
-      const int64_t s = (tile0 + L.ctile[ci]) * kTileKeys + col;
-      uint4 kv[4];
-      load_key_slices(kseq, s < nv ? s : nv - 1, g, kv);
-      const float sc = tile_score(L.sq, kv, wr, col, g);
-      const uint64_t bal = __ballot(s < nv && (double)sc >= thr);
-      if (lane == 0) L.cmask[ci] = (uint16_t)(bal & 0xFFFFu);
+    constexpr int kWaves = kCandThreads / 64;
+    for (uint32_t c0 = wave; c0 < n_tiles; c0 += 4 * kWaves) {
+      uint4 kv[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t ci = c0 + u * kWaves;
+        if (ci < n_tiles) {
+          const int64_t s = (tile0 + L.ctile[ci]) * kTileKeys + col;
+          load_key_slices(kseq, s < nv ? s : nv - 1, g, kv[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t ci = c0 + u * kWaves;
+        if (ci >= n_tiles) break;
+        const int64_t s = (tile0 + L.ctile[ci]) * kTileKeys + col;
+        const float sc = tile_score(L.sq, kv[u], wr, col, g);
+        const uint64_t bal = __ballot(s < nv && (double)sc >= thr);
+        if (lane == 0) L.cmask[ci] = (uint16_t)(bal & 0xFFFFu);
+      }
     }
   }
   __syncthreads();
@@ -633,7 +648,8 @@ struct alignas(16) SelectLds {
   double range[2];
   double bin_vals[64];
   double result;
-  alignas(16) uint8_t flag[kSelLds];
+  uint64_t selm[kSelLds / 64], eqm[kSelLds / 64];
+  uint32_t wbase[kSelLds / 64];
   uint16_t sq[kIdxHeads * kQRowPad];   // query rows for the fallback's fp64 scores
   float w[kIdxHeads];
   uint32_t hist_pad;
@@ -680,7 +696,8 @@ __device__ __forceinline__ void wave_pick(const uint32_t* hist, uint32_t rank, u
 // at most 64 members, which one wave ranks directly; a bin that stays larger
 // is resolved exactly by radix passes over the 64-bit order keys.
 // L.hist / L.bmin / L.bmax must be cleared on entry.
-__device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk, double lo, double hi) {
+__device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk, double lo, double hi, uint32_t* n_gt,
+                                 uint32_t* n_eq) {
   const int tid = threadIdx.x;
   uint32_t r = kk;
   uint32_t count = n;
@@ -717,7 +734,11 @@ __device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk, double 
     lo = L.range[0];
     hi = L.range[1];
   }
-  if (!(lo < hi)) return lo;
+  if (!(lo < hi)) {  // every value in [lo, hi] is the answer; kk - r values lie above
+    *n_gt = kk - r;
+    *n_eq = count;
+    return lo;
+  }
   if (count <= 64) {
     if (tid == 0) L.n_bin = 0;
     __syncthreads();
@@ -737,9 +758,15 @@ __device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk, double 
         gt += vb > va;
         ge += vb >= va;
       }
-      if (gt < r && r <= ge) L.result = va;  // every writer writes the same value
+      if (gt < r && r <= ge) {  // every writer writes the same values
+        L.result = va;
+        L.pick[0] = kk - r + gt;
+        L.pick[1] = ge - gt;
+      }
     }
     __syncthreads();
+    *n_gt = L.pick[0];
+    *n_eq = L.pick[1];
     return L.result;
   }
   unsigned long long pre = 0, mask = 0;
@@ -763,7 +790,18 @@ __device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk, double 
     mask |= 255ull << (56 - 8 * pass);
     r = L.pick[1];
   }
-  return key_f64(pre);
+  const double V = key_f64(pre);
+  uint32_t gt = 0, eq = 0;
+  for (uint32_t i = tid; i < n; i += kSelThreads) {
+    gt += L.v[i] > V;
+    eq += L.v[i] == V;
+  }
+  uint32_t tgt, teq;
+  block_excl_scan(gt, L.wsum[0], &tgt);
+  block_excl_scan(eq, L.wsum[1], &teq);
+  *n_gt = tgt;
+  *n_eq = teq;
+  return V;
 }
 
 // fp64 score of one key row with the reference's operation sequence, query
@@ -934,45 +972,61 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     hi = L.red[1][0];
     for (int i = 1; i < kSelThreads / 64; ++i) { lo = fmin(lo, L.red[0][i]); hi = fmax(hi, L.red[1][i]); }
   }
-  const double V = kth_largest_f64(L, cnt, kk, lo, hi);
+  uint32_t n_gt, n_eq;
+  const double V = kth_largest_f64(L, cnt, kk, lo, hi, &n_gt, &n_eq);
 
-  // entries above V are in; of those equal to V, the lowest indices (first in order)
-  uint32_t n_gt = 0;
-  for (uint32_t i = tid; i < kSelLds; i += kSelThreads) {
-    uint8_t f = 0;
-    if (i < cnt) {
-      const double v = L.v[i];
-      f = v > V ? 2 : (v == V ? 1 : 0);
+  // Entries above V are in; of those equal to V, the lowest indices (first in
+  // order).  Selection masks per 64 consecutive candidates (word j covers
+  // candidates 64 j .. 64 j + 63), then one wave turns their popcounts into
+  // output positions.
+  const int lane = tid & 63, wv = tid >> 6;
+  const uint32_t need_eq = kk - n_gt;
+  const int nwords = (int)((cnt + 63) / 64);
+  for (int j0 = 0; j0 < nwords; j0 += kSelThreads / 64) {
+    const int j = j0 + wv;
+    const uint32_t i = 64u * j + lane;
+    const double v = (j < nwords && i < cnt) ? L.v[i] : -INFINITY;
+    const uint64_t gt = __ballot(v > V), eq = __ballot(v == V);
+    if (lane == 0 && j < nwords) { L.selm[j] = gt; L.eqm[j] = eq; }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int j = tid;
+    uint64_t sel = j < nwords ? L.selm[j] : 0ull, eq = j < nwords ? L.eqm[j] : 0ull;
+    if (need_eq >= n_eq) {
+      sel |= eq;  // every tie is in
+    } else {       // ties straddle the boundary: the first need_eq of them in index order
+      const uint32_t c = (uint32_t)__popcll(eq);
+      uint32_t incl = c;
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t x = __shfl_up(incl, o, 64);
+        if (j >= o) incl += x;
+      }
+      uint32_t take = incl - c < need_eq ? need_eq - (incl - c) : 0u;
+      while (eq && take) {
+        const uint64_t low = eq & (~eq + 1ull);
+        sel |= low;
+        eq ^= low;
+        --take;
+      }
     }
-    L.flag[i] = f;
-    n_gt += f == 2;
+    const uint32_t c = (uint32_t)__popcll(sel);
+    uint32_t incl = c;
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t x = __shfl_up(incl, o, 64);
+      if (j >= o) incl += x;
+    }
+    if (j < nwords) { L.selm[j] = sel; L.wbase[j] = incl - c; }
   }
-  uint32_t tot_gt;
-  block_excl_scan(n_gt, L.wsum[1], &tot_gt);  // (barrier: the flags are complete)
-  const uint32_t need_eq = kk - tot_gt;
-  constexpr int kPerC = kSelLds / kSelThreads;  // thread tid owns candidates 16 tid .. 16 tid + 15
-  const uint4 fw = *reinterpret_cast<const uint4*>(&L.flag[tid * kPerC]);
-  const uint32_t fwords[4] = {fw.x, fw.y, fw.z, fw.w};
-  uint32_t n_eq = 0;
-#pragma unroll
-  for (int i = 0; i < kPerC; ++i) n_eq += ((fwords[i >> 2] >> (8 * (i & 3))) & 255u) == 1u;
-  uint32_t tot_eq;
-  const uint32_t eq0 = block_excl_scan(n_eq, L.wsum[0], &tot_eq);
-  uint32_t selmask = 0, eqb = eq0;
-#pragma unroll
-  for (int i = 0; i < kPerC; ++i) {
-    const uint32_t f = (fwords[i >> 2] >> (8 * (i & 3))) & 255u;
-    const bool sel = f == 2u || (f == 1u && eqb < need_eq);
-    eqb += f == 1u;
-    selmask |= sel ? (1u << i) : 0u;
-  }
-  uint32_t tot_sel;
-  uint32_t pos = block_excl_scan((uint32_t)__popc(selmask), L.wsum[1], &tot_sel);
-  while (selmask) {
-    const int i = __ffs(selmask) - 1;
-    selmask &= selmask - 1;
-    if (pos < kk) out[pos] = (int32_t)L.idx[tid * kPerC + i];
-    ++pos;
+  __syncthreads();
+  for (int j0 = 0; j0 < nwords; j0 += kSelThreads / 64) {
+    const int j = j0 + wv;
+    if (j >= nwords) break;
+    const uint64_t sel = L.selm[j];
+    if ((sel >> lane) & 1ull) {
+      const uint32_t pos = L.wbase[j] + (uint32_t)__popcll(sel & ((1ull << lane) - 1ull));
+      if (pos < kk) out[pos] = (int32_t)L.idx[64u * j + lane];
+    }
   }
   if (tid == 0) st[2] = 0u;
 }
