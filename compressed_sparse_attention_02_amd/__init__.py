@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "Csa2Error", "IndexResult", "lib", "library_path", "csa2_index", "csa2_topk", "csa2_attend_fp4",
-    "csa2_reuse_attend", "tile_max_ld", "index_workspace_bytes", "topk_workspace_bytes", "topk_min_workspace_bytes",
+    "csa2_reuse_attend", "tile_max_ld", "index_stats_bytes", "topk_workspace_bytes", "topk_min_workspace_bytes",
     "attend_workspace_bytes", "IDX_HEADS", "IDX_DIM", "HEADS", "DIM", "TOPK", "MAX_WINDOW", "MAX_LAYERS", "TILE",
     "TOPK_ROW_MAX", "STATS_WORDS",
 ]
@@ -34,11 +34,12 @@ _SIGNATURES = {
     "csa2_status_string": ([_i32], ctypes.c_char_p),
     "csa2_version": ([], ctypes.c_char_p),
     "csa2_tile_max_ld": ([_i64], _i64),
-    "csa2_index_workspace_bytes": ([_i32, _i32, _i64], _sz),
-    "csa2_index": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "csa2_index_stats_bytes": ([_i32, _i32, _i64], _sz),
+    "csa2_index": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _sz, _vp], _i32),
     "csa2_topk_workspace_bytes": ([_i32, _i64, _i32], _sz),
     "csa2_topk_min_workspace_bytes": ([_i32, _i64, _i32], _sz),
-    "csa2_topk": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp, _vp, _sz, _vp], _i32),
+    "csa2_topk": ([_vp, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp, _vp, _sz, _vp],
+                  _i32),
     "csa2_attend_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
     "csa2_attend_fp4": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp,
                          _vp, _sz, _vp], _i32),
@@ -49,18 +50,27 @@ _SIGNATURES = {
 
 class IndexResult(NamedTuple):
     """Outputs of csa2_index: scores fp32 [T][N] (None unless requested), tile maxima fp32
-    [T][tile_max_ld(N)], per-query stats int32 [T][4] (eps and floor as fp32 bits, two counters)."""
+    [T][tile_max_ld(N)] and the summary the selection consumes (int32, index_stats_bytes / 4
+    words).  The summary starts with a header of STATS_WORDS words per query, zero after the
+    scan; csa2_topk writes eps and the floor (fp32 bits) into it."""
     scores: Optional[torch.Tensor]
     tile_max: torch.Tensor
     stats: torch.Tensor
 
     @property
+    def header(self) -> torch.Tensor:
+        T = self.tile_max.shape[0]
+        return self.stats[: T * STATS_WORDS].view(T, STATS_WORDS)
+
+    @property
     def err_bound(self) -> torch.Tensor:
-        return self.stats.view(torch.float32)[:, 0]
+        """eps per query (valid once csa2_topk has run on this result)."""
+        return self.header.view(torch.float32)[:, 0]
 
     @property
     def floor(self) -> torch.Tensor:
-        return self.stats.view(torch.float32)[:, 1]
+        """Selection floor per query (tile regime, valid once csa2_topk has run)."""
+        return self.header.view(torch.float32)[:, 1]
 
 
 class Csa2Error(RuntimeError):
@@ -133,8 +143,17 @@ def tile_max_ld(N: int) -> int:
     return lib().csa2_tile_max_ld(N)
 
 
-def index_workspace_bytes(T: int, q_per_seq: int, N: int) -> int:
-    return lib().csa2_index_workspace_bytes(T, q_per_seq, N)
+def index_stats_bytes(T: int, q_per_seq: int, N: int) -> int:
+    return lib().csa2_index_stats_bytes(T, q_per_seq, N)
+
+
+def _check_stats(stats, T, q_per_seq, N, device):
+    need = index_stats_bytes(T, q_per_seq, N)
+    if not isinstance(stats, torch.Tensor) or stats.dtype != torch.int32 or stats.dim() != 1:
+        raise ValueError("stats must be a 1-D int32 tensor")
+    if stats.device != device or not stats.is_contiguous() or stats.numel() * 4 < need:
+        raise ValueError(f"stats must be a contiguous int32 tensor of at least {need} bytes on {device}")
+    return need
 
 
 def topk_workspace_bytes(T: int, N: int, k: int = TOPK) -> int:
@@ -150,7 +169,7 @@ def attend_workspace_bytes(T: int, k: int = TOPK, window: int = MAX_WINDOW, n_la
 
 
 def csa2_index(q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, want_scores=True, scores=None,
-               tile_max=None, stats=None, workspace=None) -> IndexResult:
+               tile_max=None, stats=None) -> IndexResult:
     """Indexer scan.  q_idx bf16 [T][32][128], w_idx fp32 [T][32], k_idx bf16 [B][N][128],
     q_pos int32 [T] or None.  Writes the full score matrix only if want_scores (or `scores` is given)."""
     T = q_idx.shape[0]
@@ -168,15 +187,13 @@ def csa2_index(q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, want_score
     if tile_max is None:
         tile_max = torch.empty((T, tile_max_ld(N)), dtype=torch.float32, device=dev)
     if stats is None:
-        stats = torch.empty((T, STATS_WORDS), dtype=torch.int32, device=dev)
+        stats = torch.empty((index_stats_bytes(T, q_per_seq, N) + 3) // 4, dtype=torch.int32, device=dev)
     if scores is not None:
         _check(scores, "scores", (T, N), dtype=torch.float32, device=dev)
     _check(tile_max, "tile_max", (T, tile_max_ld(N)), dtype=torch.float32, device=dev)
-    _check(stats, "stats", (T, STATS_WORDS), dtype=torch.int32, device=dev)
-    nbytes = index_workspace_bytes(T, q_per_seq, N)
-    workspace = _ws(nbytes, dev, workspace)
+    _check_stats(stats, T, q_per_seq, N, dev)
     st = lib().csa2_index(_p(q_idx), _p(w_idx), _p(k_idx), _p(q_pos), ratio, T, q_per_seq, N, _p(scores),
-                          _p(tile_max), _p(stats), _p(workspace), _nbytes(workspace), _stream(q_idx))
+                          _p(tile_max), _p(stats), stats.numel() * 4, _stream(q_idx))
     _raise(st, "csa2_index")
     return IndexResult(scores, tile_max, stats)
 
@@ -184,15 +201,15 @@ def csa2_index(q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, want_score
 def csa2_topk(scores, tile_max, stats, q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, k=TOPK,
               indices=None, workspace=None):
     """Exact top-k (ascending indices, -1 padded) -> int32 [T][k].  scores may be None (the
-    selection then works from tile_max and the keys); stats is csa2_index's (its counter words
-    are used and left zero)."""
-    T = stats.shape[0]
+    selection then works from tile_max and the keys); stats is csa2_index's summary (eps and the
+    floor are written into its header, its counter words are used and left zero)."""
+    T = q_idx.shape[0]
     B, N = k_idx.shape[0], k_idx.shape[1]
-    dev = stats.device
+    dev = q_idx.device
     if scores is not None:
         _check(scores, "scores", (T, N), dtype=torch.float32, device=dev)
     _check(tile_max, "tile_max", (T, tile_max_ld(N)), dtype=torch.float32, device=dev)
-    _check(stats, "stats", (T, STATS_WORDS), dtype=torch.int32)
+    _check_stats(stats, T, q_per_seq, N, dev)
     _check(q_idx, "q_idx", (T, IDX_HEADS, IDX_DIM), elem_size=2, device=dev)
     _check(w_idx, "w_idx", (T, IDX_HEADS), dtype=torch.float32, device=dev)
     _check(k_idx, "k_idx", (B, N, IDX_DIM), elem_size=2, device=dev)
@@ -205,9 +222,9 @@ def csa2_topk(scores, tile_max, stats, q_idx, w_idx, k_idx, q_pos=None, ratio=1,
         workspace = _ws(topk_workspace_bytes(T, N, k), dev, None)
     elif _nbytes(workspace) < topk_min_workspace_bytes(T, N, k):
         raise ValueError("workspace below csa2_topk_min_workspace_bytes")
-    st = lib().csa2_topk(_p(scores), _p(tile_max), _p(stats), _p(q_idx), _p(w_idx), _p(k_idx), _p(q_pos),
-                         ratio, T, q_per_seq, N, k, _p(indices), _p(workspace), _nbytes(workspace),
-                         _stream(stats))
+    st = lib().csa2_topk(_p(scores), _p(tile_max), _p(stats), stats.numel() * 4, _p(q_idx), _p(w_idx), _p(k_idx),
+                         _p(q_pos), ratio, T, q_per_seq, N, k, _p(indices), _p(workspace), _nbytes(workspace),
+                         _stream(q_idx))
     _raise(st, "csa2_topk")
     return indices
 

@@ -5,31 +5,33 @@
 // sec. 2.3: each query keeps its top-k entries, k = 512 per sec. 4.2.1).
 //
 // The fp32 scores of csa2_index differ from the fp64 reference by at most
-// eps (stats word 0).  If k distinct entries have fp32 score >= tau, then the
-// k-th largest fp64 score T^ satisfies T^ >= tau - eps, so every true top-k
-// member has fp32 score >= tau - 2 eps: {fp32 >= tau - 2 eps} is a candidate
-// set that contains the whole answer.  Two regimes:
+// eps, formed here from the scan's summary (partial maxima of ||K||^2) and
+// the query.  If k distinct entries have fp32 score >= tau, then the k-th
+// largest fp64 score T^ satisfies T^ >= tau - eps, so every true top-k member
+// has fp32 score >= tau - 2 eps: {fp32 >= tau - 2 eps} is a candidate set
+// that contains the whole answer.  Two regimes:
 //
 //  * Tile regime (any N; the only one without a score matrix).  tau is a
-//    lower bound of the k-th largest of a set of tile maxima (those are k
-//    distinct entries): all maxima of the visible tiles when there are at
-//    most 16384 tiles, else the maxima of 4096 groups, group j holding the
-//    4-tile runs j, j+4096, j+8192, ... (every group samples the whole row).
-//    topk_tau_kernel finds tau (one block per query); topk_cand_kernel
-//    (16384 entries per block) re-derives the fp32 scores of the tiles whose
-//    maximum reaches tau - 2 eps with the scan's own MFMA code, keeps the
-//    entries that reach it, computes their fp64 scores with the reference's
-//    exact operation sequence, and appends them in index order to a block
-//    segment; topk_select_kernel (one block per query) selects the k largest
-//    fp64 keys among the candidates and writes them in index order.  For
-//    i.i.d. scores about 1.1 k entries are candidates.  If they exceed the
-//    workspace or LDS capacity, the same block falls back to exact radix
-//    passes over the candidate tiles (slow, exact).
+//    lower bound of the k-th largest of a set of maxima of disjoint groups of
+//    entries (those are k distinct entries): the visible tiles' maxima when
+//    there are at most 8192 tiles, else the scan's group maxima.  Every
+//    block of topk_cand_kernel (4096 entries each) first forms eps and tau
+//    from the summary (the same values in every block: fixed reduction
+//    order), then re-derives the fp32 scores of its tiles whose maximum
+//    reaches tau - 2 eps with the scan's own MFMA code, keeps the entries
+//    that reach it, computes their fp64 scores with the reference's exact
+//    operation sequence and writes them in index order to its slots;
+//    topk_select_kernel (one block per query) selects the k largest fp64 keys
+//    among the candidates and writes them in index order.  For i.i.d. scores
+//    about 1.1 k entries are candidates.  If they exceed the workspace or LDS
+//    capacity, the same block falls back to exact radix passes over the
+//    candidate tiles (slow, exact).
 //  * Row regime (scores given, N <= kSmallMax, e.g. a prefill chunk): one
 //    block per query loads the visible scores into LDS, brackets the k-th
 //    largest fp32 value (lo <= T^ <= hi, two levels of 256 value bins), accepts
 //    entries above hi + 2 eps, rescores the band [lo - 2 eps, hi + 2 eps] in
 //    fp64 and takes the rest by (fp64 score desc, index asc).
+#include "idx_plan.h"
 #include "idx_tile.h"
 
 namespace csa2 {
@@ -59,6 +61,65 @@ __device__ __forceinline__ double next_down(double x) {
   return __longlong_as_double(x > 0.0 ? u - 1 : u + 1);
 }
 __device__ __forceinline__ double next_up(double x) { return -next_down(-x); }
+
+// eps_t = 2^-14 * sum_h |w_h| ||q_h||_2 * max_s ||K_s||_2 + 2^-100 (1 + sum_h |w_h|), rounded up.
+//
+// Derivation: the bf16 products are exact in fp32; four chained MFMA steps
+// of 32 products each (at most 132 additions on any path), even with every
+// addition rounded or truncated, stay within 136 * 2^-23 * sum_c |q_c K_c|
+// <= 2^-15.9 ||q_h|| ||K_s|| (Cauchy-Schwarz); ReLU is 1-Lipschitz; the fp32
+// head reduction (10 roundings on any path, fewer than 17) adds at most
+// 2^-19.9 sum_h |w_h| |dot_h|; the fp64 reference itself is within 2^-44 of
+// the exact value.  The sum is below 1.1 * 2^-15; 2^-14 leaves a factor 1.8
+// of margin.  The absolute term covers products that flush to zero.
+// ||K||^2 is accumulated by the scan with bf16 dot2 steps in fp32 over
+// nonnegative terms (relative error below 2^-16 even with two roundings per
+// step), so it is inflated by (1 + 2^-10) before the square root.  ||q_h||^2
+// is summed in fp64 (relative error below 2^-45 in any order), covered by
+// (1 + 2^-40).
+//
+// This thread's share of the three terms: the maximum of its partials of
+// max ||K||^2 (the sequence's n_parts scan partials), and for threads below
+// 256, |w_h| ||q_h|| and |w_h| of head tid / 8 in the thread with tid % 8 == 0
+// (whole waves take part: the sum of squares is folded with shuffles).
+__device__ __forceinline__ void bound_terms(const uint16_t* __restrict__ q_t, const float* __restrict__ w_t,
+                                            const float* __restrict__ parts_b, int64_t n_parts, int tid,
+                                            int nthreads, float* m2, double* qf, double* sw) {
+  float m = 0.f;
+  for (int64_t i = tid; i < n_parts; i += nthreads) m = fmaxf(m, parts_b[i]);
+  double a = 0.0, s = 0.0;
+  if (tid < 256) {
+    const int h = tid >> 3;
+    const uint4* qv = reinterpret_cast<const uint4*>(q_t + h * kIdxDim + 16 * (tid & 7));
+    const uint4 x = qv[0], y = qv[1];
+    const uint32_t wd[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double lo = (double)bf16lo(wd[i]), hi = (double)bf16hi(wd[i]);
+      ss = fma(lo, lo, ss);
+      ss = fma(hi, hi, ss);
+    }
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    ss += __shfl_xor(ss, 4, 64);
+    const double aw = fabs((double)w_t[h]);
+    a = (tid & 7) == 0 ? aw * sqrt(ss) * (1.0 + 0x1p-40) : 0.0;
+    s = (tid & 7) == 0 ? aw : 0.0;
+  }
+  *m2 = m;
+  *qf = a;
+  *sw = s;
+}
+
+// eps from the block-reduced terms, rounded up to fp32.
+__device__ __forceinline__ float bound_eps(float m2, double qf, double sw) {
+  const double kmax = sqrt((double)m2 * (1.0 + 0x1p-10) + 0x1p-100) * (1.0 + 0x1p-40);
+  const double eps = (0x1p-14 * qf * kmax + 0x1p-100 * (1.0 + sw)) * (1.0 + 0x1p-20);
+  float e = (float)eps;
+  if ((double)e < eps) e = __int_as_float(__float_as_int(e) + 1);  // positive and finite
+  return e;
+}
 
 // fp64 score with the reference's exact operation sequence (global operands;
 // used by the streaming fallback only).
@@ -365,12 +426,15 @@ struct SmallLds {
     float v[kSmallMax];
     FinTail tail;
   } u;
+  float bm[kFinThreads / 64];
+  double bq[kFinThreads / 64], bs[kFinThreads / 64];
 };
 
 __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
-    const float* __restrict__ scores, const uint32_t* __restrict__ stats, const uint16_t* __restrict__ q_idx,
-    const float* __restrict__ w_idx, const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
-    int ratio, int q_per_seq, int64_t N, int k, int32_t* __restrict__ indices) {
+    const float* __restrict__ scores, uint32_t* __restrict__ stats, const float* __restrict__ parts,
+    int64_t n_parts, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos, int ratio, int q_per_seq, int64_t N,
+    int k, int32_t* __restrict__ indices) {
   __shared__ SmallLds L;
   FinLds& sh = L.f;
   FinTail& tl = L.u.tail;
@@ -378,20 +442,37 @@ __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
   const int tid = threadIdx.x;
   const int64_t nv = n_visible(q_pos, t, ratio, N);
   int32_t* out = indices + (size_t)t * k;
-  if (nv <= k) {
-    for (int i = tid; i < k; i += kFinThreads) out[i] = i < nv ? i : -1;
-    return;
-  }
   const uint32_t kk = (uint32_t)k;
   const int b = t / q_per_seq;
   const uint16_t* qt = q_idx + (size_t)t * kIdxHeads * kIdxDim;
   const float* wt = w_idx + (size_t)t * kIdxHeads;
   const uint16_t* kb = k_idx + (size_t)b * N * kIdxDim;
   const float* row = scores + (size_t)t * N;
-  const float eps = __uint_as_float(stats[(size_t)t * CSA2_STATS_WORDS]);
   if (tid == 0) { sh.n_out = 0; sh.n_band = 0; }
-  for (int64_t i = tid; i < nv; i += kFinThreads) L.u.v[i] = row[i];
+  if (nv > k)
+    for (int64_t i = tid; i < nv; i += kFinThreads) L.u.v[i] = row[i];
+  {
+    float m2;
+    double qf, sw;
+    bound_terms(qt, wt, parts + (size_t)b * n_parts, n_parts, tid, kFinThreads, &m2, &qf, &sw);
+    m2 = wave_max(m2);
+    qf = wave_sum_f64(qf);
+    sw = wave_sum_f64(sw);
+    if ((tid & 63) == 0) { L.bm[tid >> 6] = m2; L.bq[tid >> 6] = qf; L.bs[tid >> 6] = sw; }
+  }
   __syncthreads();
+  float eps;
+  {
+    float m2 = L.bm[0];
+    double qf = L.bq[0], sw = L.bs[0];
+    for (int i = 1; i < kFinThreads / 64; ++i) { m2 = fmaxf(m2, L.bm[i]); qf += L.bq[i]; sw += L.bs[i]; }
+    eps = bound_eps(m2, qf, sw);
+    if (tid == 0) stats[(size_t)t * CSA2_STATS_WORDS] = __float_as_uint(eps);
+  }
+  if (nv <= k) {
+    for (int i = tid; i < k; i += kFinThreads) out[i] = i < nv ? i : -1;
+    return;
+  }
   float t_lo, t_hi;
   bracket_kth(sh.sel, nv, kk, [&](int64_t i) { return L.u.v[i]; }, false, &t_lo, &t_hi);
   double lo, hi;
@@ -478,8 +559,155 @@ __device__ __forceinline__ uint32_t block_flag_scan(bool flag, uint32_t* wsum, u
   return off + below;
 }
 
+// ---- eps and the floor tau, formed by every candidate block
+
+constexpr int kFloorPer = 32;                          // maxima per thread, in registers
+constexpr int kFloorVals = kCandThreads * kFloorPer;  // 8192 maxima ranked per query
+
+struct alignas(16) FloorLds {
+  uint32_t hist[256];
+  uint32_t bmin[256];  // order-preserving keys
+  float fred[4][kCandThreads / 64];
+  double dred[2][kCandThreads / 64];
+  uint32_t ured[2][kCandThreads / 64];
+  uint32_t res;
+};
+
+// eps and tau of query t (all kCandThreads threads; three barriers).  tau: at
+// least CSA2_TOPK visible fp32 scores are >= tau, because it bounds from below
+// the CSA2_TOPK-th largest of a set of maxima of disjoint groups of entries
+// (each maximum is a distinct visible entry); -inf when fewer than CSA2_TOPK of
+// those maxima are finite.  The maxima ranked are the tile maxima when the row
+// has at most kFloorVals tiles, else the scan's group maxima (when there are at
+// least 4096 of them) or the tile maxima; past kFloorVals values they are
+// folded (value j is the maximum over j, j + kFloorVals, ...), and folding
+// unions groups, which keeps them disjoint.
+//
+// Ranking: each thread holds 32 of the maxima; when every thread holds two,
+// the smallest per-thread second largest L0 is already a valid lower bound
+// (two distinct maxima per thread reach it), so only values >= L0 enter a
+// histogram of 256 bins over [L0, max] that also keeps each bin's minimum.
+// The bins at and above the one holding the CSA2_TOPK-th largest hold at least
+// CSA2_TOPK values, and tau is the smallest of them.  Every reduction has a
+// fixed order, so every block of the query obtains the same eps and tau.
+__device__ __forceinline__ void floor_and_bound(FloorLds& F, int64_t nv, int64_t ntv, const float* __restrict__ tm_t,
+                                                const float* __restrict__ gmax_t, int64_t n_groups,
+                                                const float* __restrict__ parts_b, int64_t n_parts,
+                                                const uint16_t* __restrict__ q_t, const float* __restrict__ w_t,
+                                                float* eps_out, float* tau_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 256; i += kCandThreads) { F.hist[i] = 0u; F.bmin[i] = 0xFFFFFFFFu; }
+  const bool use_groups = ntv > kFloorVals && n_groups >= kGroupsWanted;
+  const float* src = use_groups ? gmax_t : tm_t;
+  const int64_t nsrc = nv > kTopK ? (use_groups ? n_groups : ntv) : 0;
+  // value j = src[j] (rows are 16-byte aligned: four per load)
+  float v[kFloorPer];
+#pragma unroll
+  for (int m = 0; m < kFloorPer / 4; ++m) {
+    const int64_t j = 4 * ((int64_t)m * kCandThreads + tid);
+    const float4 x = j < nsrc ? *reinterpret_cast<const float4*>(src + j)
+                              : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    v[4 * m] = x.x;
+    v[4 * m + 1] = j + 1 < nsrc ? x.y : -INFINITY;
+    v[4 * m + 2] = j + 2 < nsrc ? x.z : -INFINITY;
+    v[4 * m + 3] = j + 3 < nsrc ? x.w : -INFINITY;
+  }
+  float m2;
+  double qf, sw;
+  bound_terms(q_t, w_t, parts_b, n_parts, tid, kCandThreads, &m2, &qf, &sw);
+  if (nsrc > kFloorVals) {
+#pragma unroll
+    for (int m = 0; m < kFloorPer; ++m) {
+      const int64_t j = 4 * ((int64_t)(m / 4) * kCandThreads + tid) + (m % 4);
+      for (int64_t i = j + kFloorVals; i < nsrc; i += kFloorVals) v[m] = fmaxf(v[m], src[i]);
+    }
+  }
+  float first = -INFINITY, second = -INFINITY, lmin = INFINITY;
+  uint32_t finite = 0;
+#pragma unroll
+  for (int m = 0; m < kFloorPer; ++m) {
+    const float x = v[m];
+    if (x > -INFINITY) {
+      second = fmaxf(second, fminf(first, x));
+      first = fmaxf(first, x);
+      lmin = fminf(lmin, x);
+      ++finite;
+    }
+  }
+  const bool two = finite >= 2;
+
+  // one block reduction for all: max ||K||^2, sums, value range, L0, counts
+  m2 = wave_max(m2);
+  qf = wave_sum_f64(qf);
+  sw = wave_sum_f64(sw);
+  const float wmax = wave_max(first);
+  const float wmin = -wave_max(-lmin);
+  const float wl0 = -wave_max(two ? -second : -INFINITY);  // smallest second largest of the threads with two
+  uint32_t nfin = finite, ntwo = two ? 1u : 0u;
+  for (int o = 32; o >= 1; o >>= 1) {
+    nfin += __shfl_xor((int)nfin, o, 64);
+    ntwo += __shfl_xor((int)ntwo, o, 64);
+  }
+  if (lane == 0) {
+    F.fred[0][wave] = m2; F.fred[1][wave] = wmax; F.fred[2][wave] = wmin; F.fred[3][wave] = wl0;
+    F.dred[0][wave] = qf; F.dred[1][wave] = sw;
+    F.ured[0][wave] = nfin; F.ured[1][wave] = ntwo;
+  }
+  __syncthreads();
+  m2 = F.fred[0][0]; float mx = F.fred[1][0], gmin = F.fred[2][0], l0 = F.fred[3][0];
+  qf = F.dred[0][0]; sw = F.dred[1][0]; nfin = F.ured[0][0]; ntwo = F.ured[1][0];
+  for (int i = 1; i < kCandThreads / 64; ++i) {
+    m2 = fmaxf(m2, F.fred[0][i]); mx = fmaxf(mx, F.fred[1][i]); gmin = fminf(gmin, F.fred[2][i]);
+    l0 = fminf(l0, F.fred[3][i]);
+    qf += F.dred[0][i]; sw += F.dred[1][i]; nfin += F.ured[0][i]; ntwo += F.ured[1][i];
+  }
+  *eps_out = bound_eps(m2, qf, sw);
+  float tau = -INFINITY;
+  if (nfin >= (uint32_t)kTopK) {
+    const float lo = 2u * ntwo >= (uint32_t)kTopK ? l0 : gmin;
+    const float scale = mx > lo ? 255.99f / (mx - lo) : 0.f;
+#pragma unroll
+    for (int m = 0; m < kFloorPer; ++m) {
+      if (v[m] >= lo) {
+        const uint32_t bin = value_bin(v[m], lo, scale);
+        atomicAdd(&F.hist[bin], 1u);
+        atomicMin(&F.bmin[bin], f32_key(v[m]));
+      }
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane owns bins 255-4*lane .. 252-4*lane (descending); the bins at or
+      // above the one holding the rank-th largest are those whose exclusive
+      // count from the top is below rank
+      const uint32_t rank = (uint32_t)kTopK;
+      uint32_t c[4], sum = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { c[i] = F.hist[255 - 4 * lane - i]; sum += c[i]; }
+      uint32_t incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t x = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += x;
+      }
+      uint32_t cum = incl - sum, kmin = 0xFFFFFFFFu;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (cum < rank) kmin = min(kmin, F.bmin[255 - 4 * lane - i]);
+        cum += c[i];
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+      if (lane == 0) F.res = kmin;
+    }
+    __syncthreads();
+    tau = key_f32(F.res);
+  }
+  *tau_out = tau;
+}
+
 // LDS of a candidate block.
 struct alignas(16) CandLds {
+  FloorLds f;
   uint16_t sq[kIdxHeads * kQRowPad];
   float w[kIdxHeads];
   uint32_t wsum[2][kCandThreads / 64];
@@ -491,9 +719,11 @@ struct alignas(16) CandLds {
 };
 
 // Candidates of tiles [x*kCandTiles, (x+1)*kCandTiles) of query t
-// (grid (nblk, T), one thread per tile).  Every block writes its table record.
+// (grid (nblk, T), one thread per tile).  Every block writes its table record;
+// block 0 also publishes eps and tau in the summary header.
 __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
-    const float* __restrict__ tile_max, uint32_t* __restrict__ stats, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ tile_max, uint32_t* __restrict__ stats, const float* __restrict__ gmax,
+    int64_t n_groups, const float* __restrict__ parts, int64_t n_parts, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w_idx, const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
     int ratio, int q_per_seq, int64_t N, int k, void* ws, int T, int64_t cap, int slots) {
   __shared__ CandLds L;
@@ -507,17 +737,30 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   const int64_t nv = n_visible(q_pos, t, ratio, N);
   const int64_t ntv = (nv + kTileKeys - 1) / kTileKeys;
   const int64_t tile0 = (int64_t)x * kCandTiles;
-  if (nv <= k || tile0 >= ntv) {
+  if ((nv <= k || tile0 >= ntv) && x != 0) {  // block 0 publishes eps and tau in any case
     if (tid == 0) *rec = make_uint2(0u, 0u);
     return;
   }
-  // all of this block's inputs at once: its tile maxima, tau, eps, the query
+  // all of this block's inputs at once: its tile maxima, the query, then the
+  // summary for eps and tau
   const int64_t my_tile = tile0 + tid;
-  const float tm = my_tile < ntv ? tile_max[(size_t)t * tile_ld(N) + my_tile] : -INFINITY;
-  const float eps = __uint_as_float(st[0]);
-  const float tau = __uint_as_float(st[1]);
-  stage_query(L.sq, q_idx + (size_t)t * kIdxHeads * kIdxDim, tid, kCandThreads);
-  if (tid < kIdxHeads) L.w[tid] = w_idx[(size_t)t * kIdxHeads + tid];
+  const float* tm_t = tile_max + (size_t)t * tile_ld(N);
+  const float tm = my_tile < ntv ? tm_t[my_tile] : -INFINITY;
+  const uint16_t* q_t = q_idx + (size_t)t * kIdxHeads * kIdxDim;
+  const float* w_t = w_idx + (size_t)t * kIdxHeads;
+  stage_query(L.sq, q_t, tid, kCandThreads);
+  if (tid < kIdxHeads) L.w[tid] = w_t[tid];
+  float eps, tau;
+  floor_and_bound(L.f, nv, ntv, tm_t, gmax + (size_t)t * n_groups, n_groups,
+                  parts + (size_t)(t / q_per_seq) * n_parts, n_parts, q_t, w_t, &eps, &tau);
+  if (x == 0 && tid == 0) {
+    st[0] = __float_as_uint(eps);
+    st[1] = __float_as_uint(tau);
+  }
+  if (nv <= k) {  // every visible entry is selected: no candidates
+    if (tid == 0) *rec = make_uint2(0u, 0u);
+    return;
+  }
   const double thr = next_down((double)tau - 2.0 * (double)eps);
 
   // 1. candidate tiles in order
@@ -1067,10 +1310,10 @@ extern "C" size_t csa2_topk_min_workspace_bytes(int32_t T, int64_t N, int32_t k)
   return tile_ws_fixed(T, N);
 }
 
-extern "C" csa2_status csa2_topk(const float* scores, const float* tile_max, uint32_t* stats, const void* q_idx,
-                                 const float* w_idx, const void* k_idx, const int32_t* q_pos, int32_t ratio,
-                                 int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices,
-                                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+extern "C" csa2_status csa2_topk(const float* scores, const float* tile_max, uint32_t* stats, size_t stats_bytes,
+                                 const void* q_idx, const float* w_idx, const void* k_idx, const int32_t* q_pos,
+                                 int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N, int32_t k,
+                                 int32_t* indices, void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (!stats || !q_idx || !w_idx || !k_idx || !indices) return CSA2_ERR_INVALID_ARG;
   if ((scores && !aligned16(scores)) || (tile_max && !aligned16(tile_max)) || !aligned16(stats) ||
       !aligned16(q_idx) || !aligned16(w_idx) || !aligned16(k_idx) || !aligned16(indices) ||
@@ -1078,12 +1321,17 @@ extern "C" csa2_status csa2_topk(const float* scores, const float* tile_max, uin
     return CSA2_ERR_INVALID_ARG;
   if (T < 1 || q_per_seq < 1 || T % q_per_seq != 0 || N < 1 || ratio < 1) return CSA2_ERR_INVALID_ARG;
   if (k != kTopK || N >= ((int64_t)1 << 31) || T > 65535) return CSA2_ERR_UNSUPPORTED;
+  IndexPlan p;
+  if (!index_plan(T, q_per_seq, N, &p)) return CSA2_ERR_UNSUPPORTED;
+  if (stats_bytes < stats_words(T, p) * sizeof(uint32_t)) return CSA2_ERR_INVALID_ARG;
+  const float* gmax = (const float*)(stats + stats_groups_off(T));
+  const float* parts = (const float*)(stats + stats_parts_off(T, p.n_groups));
   hipStream_t st = (hipStream_t)hip_stream;
   (void)hipGetLastError();
   const uint16_t* q = (const uint16_t*)q_idx;
   const uint16_t* kx = (const uint16_t*)k_idx;
   if (topk_row_regime(scores, N)) {
-    hipLaunchKernelGGL(topk_small_kernel, dim3(T), dim3(kFinThreads), 0, st, scores, (const uint32_t*)stats, q,
+    hipLaunchKernelGGL(topk_small_kernel, dim3(T), dim3(kFinThreads), 0, st, scores, stats, parts, p.parts(), q,
                        w_idx, kx, q_pos, ratio, q_per_seq, N, k, indices);
     if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
     return CSA2_OK;
@@ -1095,8 +1343,9 @@ extern "C" csa2_status csa2_topk(const float* scores, const float* tile_max, uin
   int64_t cap;
   if (!topk_layout(workspace_bytes, T, N, &slots, &cap)) return CSA2_ERR_WORKSPACE;
   const int64_t nblk = cand_blocks(N);
-  hipLaunchKernelGGL(topk_cand_kernel, dim3((unsigned)nblk, T), dim3(kCandThreads), 0, st, tile_max, stats, q,
-                     w_idx, kx, q_pos, ratio, q_per_seq, N, k, workspace, T, cap, slots);
+  hipLaunchKernelGGL(topk_cand_kernel, dim3((unsigned)nblk, T), dim3(kCandThreads), 0, st, tile_max, stats, gmax,
+                     p.n_groups, parts, p.parts(), q, w_idx, kx, q_pos, ratio, q_per_seq, N, k, workspace, T, cap,
+                     slots);
   hipLaunchKernelGGL(topk_select_kernel, dim3(T), dim3(kSelThreads), 0, st, tile_max, stats, q, w_idx, kx, q_pos,
                      ratio, q_per_seq, N, k, indices, workspace, T, cap);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;

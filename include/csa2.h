@@ -90,26 +90,25 @@ const char* csa2_version(void);
  *            tile_max[t][j] = max of the scores of entries 16j .. 16j+15 (those
  *            < N), -inf if none of them is visible; the ld - ceil(N/16)
  *            padding slots of each row are left unspecified
- *  stats     uint32 [T][CSA2_STATS_WORDS] out, per query:
- *            [0] eps_t (fp32 bits) >= |score(t,s) - I_fp64(t,s)| for every
- *                visible s, where I_fp64 is the score evaluated in fp64 with one
- *                fma per term, channels then heads in order;
- *            [1] floor_t (fp32 bits): at least CSA2_TOPK visible entries have
- *                fp32 score >= floor_t (-inf when the row has fewer than
- *                CSA2_TOPK non-empty tiles of 16 entries);
- *            [2], [3] zero: counters that csa2_topk uses and leaves zero.
- *            csa2_topk consumes eps and floor to make the selection exact.
- *  workspace >= csa2_index_workspace_bytes(T, q_per_seq, N) bytes (any contents).
- * Requires T >= 1, q_per_seq >= 1, T % q_per_seq == 0, 1 <= N < 2^31.
+ *  stats     uint32 out, csa2_index_stats_bytes(T, q_per_seq, N) bytes: the
+ *            summary the selection consumes.  Its first T * CSA2_STATS_WORDS
+ *            words are a header per query that the scan sets to zero and
+ *            csa2_topk fills (see there); the rest (maxima of disjoint groups
+ *            of each query's entries, partial maxima of ||K_s||^2 per
+ *            sequence) has no documented layout.
+ *  stats_bytes  size of stats; smaller than csa2_index_stats_bytes -> INVALID_ARG
+ * The call is one kernel and uses no workspace.
+ * Requires T >= 1, q_per_seq >= 1, T % q_per_seq == 0, 1 <= N < 2^31
+ * (csa2_index_stats_bytes returns 0 otherwise).
  */
 #define CSA2_TILE 16
 #define CSA2_STATS_WORDS 4
 int64_t csa2_tile_max_ld(int64_t N);
-size_t csa2_index_workspace_bytes(int32_t T, int32_t q_per_seq, int64_t N);
+size_t csa2_index_stats_bytes(int32_t T, int32_t q_per_seq, int64_t N);
 csa2_status csa2_index(const void* q_idx, const float* w_idx, const void* k_idx,
                        const int32_t* q_pos, int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N,
-                       float* scores, float* tile_max, uint32_t* stats, void* workspace,
-                       size_t workspace_bytes, void* hip_stream);
+                       float* scores, float* tile_max, uint32_t* stats, size_t stats_bytes,
+                       void* hip_stream);
 
 /* ------------------------------------------------------------------- topk
  * Exact top-k: for each query, the first min(k, n_vis) entries of the order
@@ -123,9 +122,20 @@ csa2_status csa2_index(const void* q_idx, const float* w_idx, const void* k_idx,
  *  scores     the scores output of csa2_index, or NULL.  When given and
  *             N <= CSA2_TOPK_ROW_MAX, each query's row is selected in LDS in one
  *             pass; otherwise the selection works from tile_max and the keys.
- *  tile_max, stats   outputs of csa2_index for the same arguments; stats words
- *             [2] and [3] are used as counters and left zero (concurrent
- *             csa2_topk calls must not share a stats array)
+ *  tile_max, stats, stats_bytes   outputs of csa2_index for the same
+ *             arguments (T, q_per_seq, N as passed to it).  For every query
+ *             csa2_topk writes into the stats header:
+ *             [0] eps_t (fp32 bits) >= |score(t,s) - I_fp64(t,s)| for every
+ *                 visible s, where score is csa2_index's fp32 score and I_fp64
+ *                 the score evaluated in fp64 with one fma per term, channels
+ *                 then heads in order;
+ *             [1] floor_t (fp32 bits; tile regime only, the row regime leaves
+ *                 the word as csa2_index wrote it): at least CSA2_TOPK visible
+ *                 entries have fp32 score >= floor_t (-inf when fewer than
+ *                 CSA2_TOPK of the maxima it ranks are finite);
+ *             [2], [3] counters, used and left zero (concurrent csa2_topk
+ *                 calls must not share a stats array).
+ *             Every candidate of the selection has fp32 score >= floor - 2 eps.
  *  q_idx, w_idx, k_idx, q_pos, ratio   as passed to csa2_index
  *  k          must be CSA2_TOPK (512)
  *  indices    int32 [T][k] out
@@ -137,7 +147,7 @@ csa2_status csa2_index(const void* q_idx, const float* w_idx, const void* k_idx,
 #define CSA2_TOPK_ROW_MAX 36864
 size_t csa2_topk_workspace_bytes(int32_t T, int64_t N, int32_t k);
 size_t csa2_topk_min_workspace_bytes(int32_t T, int64_t N, int32_t k);
-csa2_status csa2_topk(const float* scores, const float* tile_max, uint32_t* stats,
+csa2_status csa2_topk(const float* scores, const float* tile_max, uint32_t* stats, size_t stats_bytes,
                       const void* q_idx, const float* w_idx, const void* k_idx, const int32_t* q_pos,
                       int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices,
                       void* workspace, size_t workspace_bytes, void* hip_stream);

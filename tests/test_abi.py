@@ -40,8 +40,10 @@ def test_status_strings_and_version(L):
 
 
 def test_workspace_queries(L):
-    assert csa.index_workspace_bytes(4, 1, 1 << 20) > 0
-    assert csa.index_workspace_bytes(4, 3, 100) == 0          # T not a multiple of q_per_seq
+    # the summary: a 4-word header per query, group maxima and norm partials
+    assert csa.index_stats_bytes(4, 1, 1 << 20) >= 4 * 4 * 4 + 4 * 4096 * 4
+    assert csa.index_stats_bytes(4, 3, 100) == 0              # T not a multiple of q_per_seq
+    assert csa.index_stats_bytes(1, 1, 1 << 31) == 0          # N beyond 2^31 - 1
     assert csa.topk_workspace_bytes(4, 1 << 20) >= csa.topk_min_workspace_bytes(4, 1 << 20) > 0
     assert csa.topk_workspace_bytes(4, 1 << 20, 256) == 0      # only k = 512
     assert csa.topk_workspace_bytes(4, 30000) > 0              # tile regime needs one even for short rows
@@ -66,8 +68,8 @@ def test_tile_max_stride(L):
     assert L.csa2_tile_max_ld(0) == 0
 
 
-def _index(L, q=P, w=P, k=P, pos=None, ratio=1, T=4, qps=1, N=1024, s=P, tm=P, e=P, ws=P, wsb=1 << 20):
-    return L.csa2_index(q, w, k, pos, ratio, T, qps, N, s, tm, e, ws, wsb, None)
+def _index(L, q=P, w=P, k=P, pos=None, ratio=1, T=4, qps=1, N=1024, s=P, tm=P, e=P, eb=1 << 20):
+    return L.csa2_index(q, w, k, pos, ratio, T, qps, N, s, tm, e, eb, None)
 
 
 def test_index_host_validation(L):
@@ -75,30 +77,30 @@ def test_index_host_validation(L):
     assert _index(L, tm=None) == INVALID
     assert _index(L, s=MIS) == INVALID
     assert _index(L, e=None) == INVALID             # stats
-    assert _index(L, ws=MIS) == WORKSPACE
+    assert _index(L, e=MIS) == INVALID
     assert _index(L, k=MIS) == INVALID
     assert _index(L, T=0) == INVALID
     assert _index(L, T=4, qps=3) == INVALID
     assert _index(L, N=0) == INVALID
     assert _index(L, ratio=0) == INVALID
     assert _index(L, N=1 << 31) == UNSUPPORTED
-    assert _index(L, ws=None) == WORKSPACE
-    assert _index(L, wsb=csa.index_workspace_bytes(4, 1, 1024) - 1) == WORKSPACE
+    assert _index(L, eb=csa.index_stats_bytes(4, 1, 1024) - 1) == INVALID
 
 
 # N large enough for the multi-pass regime, where a workspace is required, so
 # that every call below is rejected by validation.
-def _topk(L, s=None, tm=P, e=P, q=P, w=P, k_idx=P, pos=None, ratio=1, T=4, qps=1, N=1 << 20, k=512, out=P, ws=P,
-          wsb=None):
+def _topk(L, s=None, tm=P, e=P, eb=1 << 30, q=P, w=P, k_idx=P, pos=None, ratio=1, T=4, qps=1, N=1 << 20, k=512,
+          out=P, ws=P, wsb=None):
     if wsb is None:
         wsb = csa.topk_workspace_bytes(T, N, 512) or 1
-    return L.csa2_topk(s, tm, e, q, w, k_idx, pos, ratio, T, qps, N, k, out, ws, wsb, None)
+    return L.csa2_topk(s, tm, e, eb, q, w, k_idx, pos, ratio, T, qps, N, k, out, ws, wsb, None)
 
 
 def test_topk_host_validation(L):
     assert _topk(L, tm=None) == INVALID              # no scores and no tile maxima
     assert _topk(L, s=P, tm=None) == INVALID         # long rows always use the tile regime
     assert _topk(L, e=None) == INVALID              # stats
+    assert _topk(L, eb=csa.index_stats_bytes(4, 1, 1 << 20) - 1) == INVALID
     assert _topk(L, tm=MIS) == INVALID
     assert _topk(L, out=MIS) == INVALID
     assert _topk(L, T=5, qps=2) == INVALID

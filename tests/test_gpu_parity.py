@@ -68,12 +68,21 @@ def test_index_scores_within_bound(name):
     ix = run_index(c)
     ix2 = run_index(c, want_scores=False)
     torch.cuda.synchronize()
-    ref = oracle_scores(c, range(c.T))
-    s, e, tm, fl = npy(ix.scores), npy(ix.err_bound), npy(ix.tile_max), npy(ix.floor)
-    # the tile maxima (padding slots excluded) and the stats do not depend on whether scores are written
+    # the tile maxima (padding slots excluded) and the summary do not depend on whether scores
+    # are written; the scan leaves the summary header zero
     nt = -(-c.N // 16)
+    tm = npy(ix.tile_max)
     assert np.array_equal(tm[:, :nt], npy(ix2.tile_max)[:, :nt]) and np.array_equal(npy(ix.stats), npy(ix2.stats))
-    assert np.all(npy(ix.stats)[:, 2:] == 0)
+    assert np.all(npy(ix.header) == 0)
+    # eps and the floor come from the selection: the tile regime's (on ix2) and the row
+    # regime's eps (on ix, N <= 36864) must both bound the error
+    run_topk(c, ix2, "tiles")
+    run_topk(c, ix, "rows")
+    torch.cuda.synchronize()
+    assert np.all(npy(ix2.header)[:, 2:] == 0) and np.all(npy(ix.header)[:, 2:] == 0)
+    ref = oracle_scores(c, range(c.T))
+    s, e, fl = npy(ix.scores), npy(ix2.err_bound), npy(ix2.floor)
+    e_rows = npy(ix.err_bound) if c.N <= csa.TOPK_ROW_MAX else e
     pad = np.full((c.T, nt * 16 - c.N), -np.inf, np.float32)
     assert np.array_equal(tm[:, :nt], np.concatenate([s, pad], axis=1).reshape(c.T, nt, 16).max(axis=2))
     worst = 0.0
@@ -82,6 +91,7 @@ def test_index_scores_within_bound(name):
         assert np.all(np.isneginf(s[t, nv:])), "entries beyond visibility must be -inf"
         err = np.abs(s[t, :nv].astype(np.float64) - ref[t][:nv])
         assert np.all(err <= e[t]), f"t={t}: max err {err.max()} > eps {e[t]}"
+        assert np.all(err <= e_rows[t]), f"t={t}: max err {err.max()} > row-regime eps {e_rows[t]}"
         # the floor: at least 512 visible fp32 scores reach it (-inf if fewer than 512 non-empty tiles)
         if -(-nv // 16) >= 512:
             assert np.isfinite(fl[t]) and np.count_nonzero(s[t, :nv] >= fl[t]) >= 512
@@ -104,7 +114,7 @@ def test_topk_bit_exact(name, path):
     ix = run_index(c, want_scores=(path == "rows"))
     idx = run_topk(c, ix, path)
     torch.cuda.synchronize()
-    assert np.all(npy(ix.stats)[:, 2:] == 0), "csa2_topk must leave its counters zero"
+    assert np.all(npy(ix.header)[:, 2:] == 0), "csa2_topk must leave its counters zero"
     ref = oracle_topk(c, oracle_scores(c, range(c.T)))
     got = npy(idx)
     for t in range(c.T):
