@@ -14,10 +14,10 @@
 //  * Tile regime (any N; the only one without a score matrix).  tau is a
 //    lower bound of the k-th largest of a set of maxima of disjoint groups of
 //    entries (those are k distinct entries): the visible tiles' maxima when
-//    there are at most 8192 tiles, else the scan's group maxima.  Every
-//    block of topk_cand_kernel (4096 entries each) first forms eps and tau
-//    from the summary (the same values in every block: fixed reduction
-//    order), then re-derives the fp32 scores of its tiles whose maximum
+//    there are at most 8192 tiles, else the scan's group maxima.
+//    topk_floor_kernel (one block per query) forms eps and tau from the
+//    summary and writes them to its header; each block of topk_cand_kernel
+//    (4096 entries) re-derives the fp32 scores of its tiles whose maximum
 //    reaches tau - 2 eps with the scan's own MFMA code, keeps the entries
 //    that reach it, computes their fp64 scores with the reference's exact
 //    operation sequence and writes them in index order to its slots;
@@ -79,19 +79,34 @@ __device__ __forceinline__ double next_up(double x) { return -next_down(-x); }
 // (1 + 2^-40).
 //
 // This thread's share of the three terms: the maximum of its partials of
-// max ||K||^2 (the sequence's n_parts scan partials), and for threads below
-// 256, |w_h| ||q_h|| and |w_h| of head tid / 8 in the thread with tid % 8 == 0
-// (whole waves take part: the sum of squares is folded with shuffles).
+// max ||K||^2 (the sequence's n_parts scan partials, the first 8 per thread
+// requested at once), and for threads below 256 (whole waves), |w_h| ||q_h||
+// and |w_h| of head tid / 8, the same in the 8 lanes of each group of eight
+// (the sum of squares is folded with DPP moves); 0 in the other threads.
+// Reduce m2 with wave_max_dpp and the two sums with wave_sum_groups8_f64.
 __device__ __forceinline__ void bound_terms(const uint16_t* __restrict__ q_t, const float* __restrict__ w_t,
                                             const float* __restrict__ parts_b, int64_t n_parts, int tid,
                                             int nthreads, float* m2, double* qf, double* sw) {
+  float pm[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int64_t i = tid + (int64_t)u * nthreads;
+    pm[u] = i < n_parts ? parts_b[i] : 0.f;
+  }
+  uint4 x = make_uint4(0u, 0u, 0u, 0u), y = x;
+  float wh = 0.f;
+  if (tid < 256) {
+    const uint4* qv = reinterpret_cast<const uint4*>(q_t + (tid >> 3) * kIdxDim + 16 * (tid & 7));
+    x = qv[0];
+    y = qv[1];
+    wh = w_t[tid >> 3];
+  }
   float m = 0.f;
-  for (int64_t i = tid; i < n_parts; i += nthreads) m = fmaxf(m, parts_b[i]);
+  for (int64_t i = tid + 8 * (int64_t)nthreads; i < n_parts; i += nthreads) m = fmaxf(m, parts_b[i]);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) m = fmaxf(m, pm[u]);
   double a = 0.0, s = 0.0;
   if (tid < 256) {
-    const int h = tid >> 3;
-    const uint4* qv = reinterpret_cast<const uint4*>(q_t + h * kIdxDim + 16 * (tid & 7));
-    const uint4 x = qv[0], y = qv[1];
     const uint32_t wd[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
     double ss = 0.0;
 #pragma unroll
@@ -100,12 +115,12 @@ __device__ __forceinline__ void bound_terms(const uint16_t* __restrict__ q_t, co
       ss = fma(lo, lo, ss);
       ss = fma(hi, hi, ss);
     }
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
-    ss += __shfl_xor(ss, 4, 64);
-    const double aw = fabs((double)w_t[h]);
-    a = (tid & 7) == 0 ? aw * sqrt(ss) * (1.0 + 0x1p-40) : 0.0;
-    s = (tid & 7) == 0 ? aw : 0.0;
+    ss += dpp_f64<kDppXor1>(ss);
+    ss += dpp_f64<kDppXor2>(ss);
+    ss += dpp_f64<kDppHalfMirror>(ss);
+    const double aw = fabs((double)wh);
+    a = aw * sqrt(ss) * (1.0 + 0x1p-40);
+    s = aw;
   }
   *m2 = m;
   *qf = a;
@@ -455,9 +470,9 @@ __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
     float m2;
     double qf, sw;
     bound_terms(qt, wt, parts + (size_t)b * n_parts, n_parts, tid, kFinThreads, &m2, &qf, &sw);
-    m2 = wave_max(m2);
-    qf = wave_sum_f64(qf);
-    sw = wave_sum_f64(sw);
+    m2 = wave_max_dpp(m2);
+    qf = wave_sum_groups8_f64(qf);
+    sw = wave_sum_groups8_f64(sw);
     if ((tid & 63) == 0) { L.bm[tid >> 6] = m2; L.bq[tid >> 6] = qf; L.bs[tid >> 6] = sw; }
   }
   __syncthreads();
@@ -559,52 +574,55 @@ __device__ __forceinline__ uint32_t block_flag_scan(bool flag, uint32_t* wsum, u
   return off + below;
 }
 
-// ---- eps and the floor tau, formed by every candidate block
+// ---- eps and the floor tau: one block per query
 
-constexpr int kFloorPer = 32;                          // maxima per thread, in registers
-constexpr int kFloorVals = kCandThreads * kFloorPer;  // 8192 maxima ranked per query
+constexpr int kFloorThreads = 512;
+constexpr int kFloorPer = 16;                           // maxima per thread, in registers
+constexpr int kFloorVals = kFloorThreads * kFloorPer;  // 8192 maxima ranked per query
 
 struct alignas(16) FloorLds {
   uint32_t hist[256];
   uint32_t bmin[256];  // order-preserving keys
-  float fred[4][kCandThreads / 64];
-  double dred[2][kCandThreads / 64];
-  uint32_t ured[2][kCandThreads / 64];
+  float fred[4][kFloorThreads / 64];
+  double dred[2][kFloorThreads / 64];
+  uint32_t ured[kFloorThreads / 64];
   uint32_t res;
 };
 
-// eps and tau of query t (all kCandThreads threads; three barriers).  tau: at
-// least CSA2_TOPK visible fp32 scores are >= tau, because it bounds from below
-// the CSA2_TOPK-th largest of a set of maxima of disjoint groups of entries
-// (each maximum is a distinct visible entry); -inf when fewer than CSA2_TOPK of
-// those maxima are finite.  The maxima ranked are the tile maxima when the row
-// has at most kFloorVals tiles, else the scan's group maxima (when there are at
-// least 4096 of them) or the tile maxima; past kFloorVals values they are
-// folded (value j is the maximum over j, j + kFloorVals, ...), and folding
-// unions groups, which keeps them disjoint.
+// Query t (grid T, kFloorThreads threads): stats[t] = {eps, tau, 0, 0}.
+// tau: at least CSA2_TOPK visible fp32 scores are >= tau, because it bounds
+// from below the CSA2_TOPK-th largest of a set of maxima of disjoint groups of
+// entries (each maximum is a distinct visible entry); -inf when fewer than
+// CSA2_TOPK of those maxima are finite.  The maxima ranked are the tile maxima
+// when the row has at most kFloorVals tiles, else the scan's group maxima (when
+// there are at least 4096 of them) or the tile maxima; past kFloorVals values
+// they are folded (value j is the maximum over j, j + kFloorVals, ...), and
+// folding unions groups, which keeps them disjoint.
 //
-// Ranking: each thread holds 32 of the maxima; when every thread holds two,
-// the smallest per-thread second largest L0 is already a valid lower bound
-// (two distinct maxima per thread reach it), so only values >= L0 enter a
+// Ranking: each thread holds 16 of the maxima; the smallest per-thread
+// maximum L0 is already a valid lower bound when at least CSA2_TOPK threads
+// hold one (that many distinct maxima reach it), so only values >= L0 enter a
 // histogram of 256 bins over [L0, max] that also keeps each bin's minimum.
 // The bins at and above the one holding the CSA2_TOPK-th largest hold at least
-// CSA2_TOPK values, and tau is the smallest of them.  Every reduction has a
-// fixed order, so every block of the query obtains the same eps and tau.
-__device__ __forceinline__ void floor_and_bound(FloorLds& F, int64_t nv, int64_t ntv, const float* __restrict__ tm_t,
-                                                const float* __restrict__ gmax_t, int64_t n_groups,
-                                                const float* __restrict__ parts_b, int64_t n_parts,
-                                                const uint16_t* __restrict__ q_t, const float* __restrict__ w_t,
-                                                float* eps_out, float* tau_out) {
+// CSA2_TOPK values, and tau is the smallest of them.
+__global__ __launch_bounds__(kFloorThreads) void topk_floor_kernel(
+    const float* __restrict__ tile_max, uint32_t* __restrict__ stats, const float* __restrict__ gmax,
+    int64_t n_groups, const float* __restrict__ parts, int64_t n_parts, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ w_idx, const int32_t* __restrict__ q_pos, int ratio, int q_per_seq, int64_t N) {
+  __shared__ FloorLds F;
+  const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < 256; i += kCandThreads) { F.hist[i] = 0u; F.bmin[i] = 0xFFFFFFFFu; }
+  for (int i = tid; i < 256; i += kFloorThreads) { F.hist[i] = 0u; F.bmin[i] = 0xFFFFFFFFu; }
+  const int64_t nv = n_visible(q_pos, t, ratio, N);
+  const int64_t ntv = (nv + kTileKeys - 1) / kTileKeys;
   const bool use_groups = ntv > kFloorVals && n_groups >= kGroupsWanted;
-  const float* src = use_groups ? gmax_t : tm_t;
+  const float* src = use_groups ? gmax + (size_t)t * n_groups : tile_max + (size_t)t * tile_ld(N);
   const int64_t nsrc = nv > kTopK ? (use_groups ? n_groups : ntv) : 0;
   // value j = src[j] (rows are 16-byte aligned: four per load)
   float v[kFloorPer];
 #pragma unroll
   for (int m = 0; m < kFloorPer / 4; ++m) {
-    const int64_t j = 4 * ((int64_t)m * kCandThreads + tid);
+    const int64_t j = 4 * ((int64_t)m * kFloorThreads + tid);
     const float4 x = j < nsrc ? *reinterpret_cast<const float4*>(src + j)
                               : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
     v[4 * m] = x.x;
@@ -614,57 +632,51 @@ __device__ __forceinline__ void floor_and_bound(FloorLds& F, int64_t nv, int64_t
   }
   float m2;
   double qf, sw;
-  bound_terms(q_t, w_t, parts_b, n_parts, tid, kCandThreads, &m2, &qf, &sw);
+  bound_terms(q_idx + (size_t)t * kIdxHeads * kIdxDim, w_idx + (size_t)t * kIdxHeads,
+              parts + (size_t)(t / q_per_seq) * n_parts, n_parts, tid, kFloorThreads, &m2, &qf, &sw);
   if (nsrc > kFloorVals) {
 #pragma unroll
     for (int m = 0; m < kFloorPer; ++m) {
-      const int64_t j = 4 * ((int64_t)(m / 4) * kCandThreads + tid) + (m % 4);
+      const int64_t j = 4 * ((int64_t)(m / 4) * kFloorThreads + tid) + (m % 4);
       for (int64_t i = j + kFloorVals; i < nsrc; i += kFloorVals) v[m] = fmaxf(v[m], src[i]);
     }
   }
-  float first = -INFINITY, second = -INFINITY, lmin = INFINITY;
+  float lmax = -INFINITY, lmin = INFINITY;
   uint32_t finite = 0;
 #pragma unroll
   for (int m = 0; m < kFloorPer; ++m) {
-    const float x = v[m];
-    if (x > -INFINITY) {
-      second = fmaxf(second, fminf(first, x));
-      first = fmaxf(first, x);
-      lmin = fminf(lmin, x);
-      ++finite;
-    }
+    const bool f = v[m] > -INFINITY;
+    lmax = fmaxf(lmax, v[m]);
+    lmin = fminf(lmin, f ? v[m] : INFINITY);
+    finite += f ? 1u : 0u;
   }
-  const bool two = finite >= 2;
 
   // one block reduction for all: max ||K||^2, sums, value range, L0, counts
-  m2 = wave_max(m2);
-  qf = wave_sum_f64(qf);
-  sw = wave_sum_f64(sw);
-  const float wmax = wave_max(first);
-  const float wmin = -wave_max(-lmin);
-  const float wl0 = -wave_max(two ? -second : -INFINITY);  // smallest second largest of the threads with two
-  uint32_t nfin = finite, ntwo = two ? 1u : 0u;
-  for (int o = 32; o >= 1; o >>= 1) {
-    nfin += __shfl_xor((int)nfin, o, 64);
-    ntwo += __shfl_xor((int)ntwo, o, 64);
-  }
+  m2 = wave_max_dpp(m2);
+  qf = wave_sum_groups8_f64(qf);
+  sw = wave_sum_groups8_f64(sw);
+  const float wmax = wave_max_dpp(lmax);
+  const float wmin = wave_min_dpp(lmin);
+  const float wl0 = wave_min_dpp(lmax > -INFINITY ? lmax : INFINITY);  // smallest per-thread maximum
+  const uint32_t nfin = wave_sum_u32_dpp(finite);
+  const uint32_t nthr = (uint32_t)__popcll(__ballot(finite > 0));
   if (lane == 0) {
     F.fred[0][wave] = m2; F.fred[1][wave] = wmax; F.fred[2][wave] = wmin; F.fred[3][wave] = wl0;
     F.dred[0][wave] = qf; F.dred[1][wave] = sw;
-    F.ured[0][wave] = nfin; F.ured[1][wave] = ntwo;
+    F.ured[wave] = nfin | (nthr << 16);
   }
   __syncthreads();
   m2 = F.fred[0][0]; float mx = F.fred[1][0], gmin = F.fred[2][0], l0 = F.fred[3][0];
-  qf = F.dred[0][0]; sw = F.dred[1][0]; nfin = F.ured[0][0]; ntwo = F.ured[1][0];
-  for (int i = 1; i < kCandThreads / 64; ++i) {
+  qf = F.dred[0][0]; sw = F.dred[1][0];
+  uint32_t tfin = F.ured[0] & 0xFFFFu, tthr = F.ured[0] >> 16;
+  for (int i = 1; i < kFloorThreads / 64; ++i) {
     m2 = fmaxf(m2, F.fred[0][i]); mx = fmaxf(mx, F.fred[1][i]); gmin = fminf(gmin, F.fred[2][i]);
     l0 = fminf(l0, F.fred[3][i]);
-    qf += F.dred[0][i]; sw += F.dred[1][i]; nfin += F.ured[0][i]; ntwo += F.ured[1][i];
+    qf += F.dred[0][i]; sw += F.dred[1][i]; tfin += F.ured[i] & 0xFFFFu; tthr += F.ured[i] >> 16;
   }
-  *eps_out = bound_eps(m2, qf, sw);
   float tau = -INFINITY;
-  if (nfin >= (uint32_t)kTopK) {
-    const float lo = 2u * ntwo >= (uint32_t)kTopK ? l0 : gmin;
+  if (tfin >= (uint32_t)kTopK) {
+    const float lo = tthr >= (uint32_t)kTopK ? l0 : gmin;
     const float scale = mx > lo ? 255.99f / (mx - lo) : 0.f;
 #pragma unroll
     for (int m = 0; m < kFloorPer; ++m) {
@@ -695,19 +707,21 @@ __device__ __forceinline__ void floor_and_bound(FloorLds& F, int64_t nv, int64_t
         if (cum < rank) kmin = min(kmin, F.bmin[255 - 4 * lane - i]);
         cum += c[i];
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+      kmin = wave_min_u32_dpp(kmin);
       if (lane == 0) F.res = kmin;
     }
     __syncthreads();
     tau = key_f32(F.res);
   }
-  *tau_out = tau;
+  if (tid == 0) {
+    uint32_t* st = stats + (size_t)t * CSA2_STATS_WORDS;
+    st[0] = __float_as_uint(bound_eps(m2, qf, sw));
+    st[1] = __float_as_uint(tau);
+  }
 }
 
 // LDS of a candidate block.
 struct alignas(16) CandLds {
-  FloorLds f;
   uint16_t sq[kIdxHeads * kQRowPad];
   float w[kIdxHeads];
   uint32_t wsum[2][kCandThreads / 64];
@@ -719,11 +733,9 @@ struct alignas(16) CandLds {
 };
 
 // Candidates of tiles [x*kCandTiles, (x+1)*kCandTiles) of query t
-// (grid (nblk, T), one thread per tile).  Every block writes its table record;
-// block 0 also publishes eps and tau in the summary header.
+// (grid (nblk, T), one thread per tile).  Every block writes its table record.
 __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
-    const float* __restrict__ tile_max, uint32_t* __restrict__ stats, const float* __restrict__ gmax,
-    int64_t n_groups, const float* __restrict__ parts, int64_t n_parts, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ tile_max, uint32_t* __restrict__ stats, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w_idx, const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
     int ratio, int q_per_seq, int64_t N, int k, void* ws, int T, int64_t cap, int slots) {
   __shared__ CandLds L;
@@ -737,30 +749,17 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   const int64_t nv = n_visible(q_pos, t, ratio, N);
   const int64_t ntv = (nv + kTileKeys - 1) / kTileKeys;
   const int64_t tile0 = (int64_t)x * kCandTiles;
-  if ((nv <= k || tile0 >= ntv) && x != 0) {  // block 0 publishes eps and tau in any case
+  if (nv <= k || tile0 >= ntv) {
     if (tid == 0) *rec = make_uint2(0u, 0u);
     return;
   }
-  // all of this block's inputs at once: its tile maxima, the query, then the
-  // summary for eps and tau
+  // all of this block's inputs at once: its tile maxima, tau, eps, the query
   const int64_t my_tile = tile0 + tid;
-  const float* tm_t = tile_max + (size_t)t * tile_ld(N);
-  const float tm = my_tile < ntv ? tm_t[my_tile] : -INFINITY;
-  const uint16_t* q_t = q_idx + (size_t)t * kIdxHeads * kIdxDim;
-  const float* w_t = w_idx + (size_t)t * kIdxHeads;
-  stage_query(L.sq, q_t, tid, kCandThreads);
-  if (tid < kIdxHeads) L.w[tid] = w_t[tid];
-  float eps, tau;
-  floor_and_bound(L.f, nv, ntv, tm_t, gmax + (size_t)t * n_groups, n_groups,
-                  parts + (size_t)(t / q_per_seq) * n_parts, n_parts, q_t, w_t, &eps, &tau);
-  if (x == 0 && tid == 0) {
-    st[0] = __float_as_uint(eps);
-    st[1] = __float_as_uint(tau);
-  }
-  if (nv <= k) {  // every visible entry is selected: no candidates
-    if (tid == 0) *rec = make_uint2(0u, 0u);
-    return;
-  }
+  const float tm = my_tile < ntv ? tile_max[(size_t)t * tile_ld(N) + my_tile] : -INFINITY;
+  const float eps = __uint_as_float(st[0]);
+  const float tau = __uint_as_float(st[1]);
+  stage_query(L.sq, q_idx + (size_t)t * kIdxHeads * kIdxDim, tid, kCandThreads);
+  if (tid < kIdxHeads) L.w[tid] = w_idx[(size_t)t * kIdxHeads + tid];
   const double thr = next_down((double)tau - 2.0 * (double)eps);
 
   // 1. candidate tiles in order
@@ -1343,9 +1342,10 @@ extern "C" csa2_status csa2_topk(const float* scores, const float* tile_max, uin
   int64_t cap;
   if (!topk_layout(workspace_bytes, T, N, &slots, &cap)) return CSA2_ERR_WORKSPACE;
   const int64_t nblk = cand_blocks(N);
-  hipLaunchKernelGGL(topk_cand_kernel, dim3((unsigned)nblk, T), dim3(kCandThreads), 0, st, tile_max, stats, gmax,
-                     p.n_groups, parts, p.parts(), q, w_idx, kx, q_pos, ratio, q_per_seq, N, k, workspace, T, cap,
-                     slots);
+  hipLaunchKernelGGL(topk_floor_kernel, dim3(T), dim3(kFloorThreads), 0, st, tile_max, stats, gmax, p.n_groups,
+                     parts, p.parts(), q, w_idx, q_pos, ratio, q_per_seq, N);
+  hipLaunchKernelGGL(topk_cand_kernel, dim3((unsigned)nblk, T), dim3(kCandThreads), 0, st, tile_max, stats, q,
+                     w_idx, kx, q_pos, ratio, q_per_seq, N, k, workspace, T, cap, slots);
   hipLaunchKernelGGL(topk_select_kernel, dim3(T), dim3(kSelThreads), 0, st, tile_max, stats, q, w_idx, kx, q_pos,
                      ratio, q_per_seq, N, k, indices, workspace, T, cap);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
