@@ -40,12 +40,99 @@ def parse():
     ap.add_argument("--workload", default="long_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+                    help="also run torch.neg over 1 GiB of fp32 (reads and writes 1 GiB: the reference dispatch "
+                         "that scales rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to bytes)")
+    ap.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="print the profile summary of rocprofv3 CSV output (kernel stats, then the FETCH_SIZE and "
+                         "WRITE_SIZE runs) instead of benchmarking")
     return ap.parse_args()
+
+
+# Sources of the scan kernel: the recorded traffic holds only while they are unchanged.
+SCAN_SOURCES = ["compressed_sparse_attention_02_amd/csrc/index.hip", "compressed_sparse_attention_02_amd/csrc/idx_tile.h",
+                "compressed_sparse_attention_02_amd/csrc/idx_plan.h",
+                "compressed_sparse_attention_02_amd/csrc/csa2_common.h", "include/csa2.h"]
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "idx_scan_kernel_long_decode_hbm_traffic.md")
+CAL_BYTES = 1 << 30          # bytes the calibration dispatch reads, and writes
+
+
+def scan_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in SCAN_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per scan launch from the committed counter summary, or None when it is missing
+    or was taken on other kernel sources."""
+    try:
+        text = open(PMC_SUMMARY).read()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in text.splitlines() if line.startswith("- ") and ":" in line)
+    fields = {k[2:].strip(): v.strip().strip("`") for k, v in fields.items()}
+    if fields.get("scan sources sha256") != scan_sources_sha256():
+        return None
+    try:
+        return float(fields["HBM bytes per launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize(stats_dir, fetch_dir, write_dir):
+    """Markdown summary of rocprofv3 CSV output: per-kernel durations of the bench run and the
+    per-dispatch FETCH_SIZE / WRITE_SIZE of the scan, scaled by the calibration dispatch."""
+    import csv
+    import glob
+
+    def rows(d, suffix):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True):
+            out += list(csv.DictReader(open(f)))
+        return out
+
+    print("### Kernel durations (rocprofv3 --kernel-trace --stats)\n")
+    print("| kernel | calls | average us | min us | max us |\n|---|---|---|---|---|")
+    for r in sorted(rows(stats_dir, "kernel_stats.csv"), key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"].split("(")[0]
+        if "csa2" in name:
+            print(f"| {name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                  f"{float(r['MaxNs']) / 1e3:.1f} |")
+
+    def per_dispatch(d, counter):
+        acc = {}
+        for r in rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            key = "scan" if "idx_scan_kernel" in r["Kernel_Name"] else ("cal" if "neg_kernel" in r["Kernel_Name"] else None)
+            if key:
+                acc.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
+                acc[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return {k: sum(v.values()) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+    f, fn = per_dispatch(fetch_dir, "FETCH_SIZE")
+    w, wn = per_dispatch(write_dir, "WRITE_SIZE")
+    f_scale = CAL_BYTES / (f["cal"] * 1024)
+    w_scale = CAL_BYTES / (w["cal"] * 1024)
+    traffic = f["scan"] * 1024 * f_scale + w["scan"] * 1024 * w_scale
+    print("\n### HBM traffic of idx_scan_kernel (rocprofv3 --pmc)\n")
+    print(f"- FETCH_SIZE KiB per scan dispatch: {f['scan']:.0f} (mean of {fn['scan']})")
+    print(f"- WRITE_SIZE KiB per scan dispatch: {w['scan']:.0f} (mean of {wn['scan']})")
+    print(f"- calibration dispatch (torch.neg, reads and writes {CAL_BYTES} B): FETCH_SIZE {f['cal']:.0f} KiB, "
+          f"WRITE_SIZE {w['cal']:.0f} KiB")
+    print(f"- FETCH scale: {f_scale:.4f}")
+    print(f"- WRITE scale: {w_scale:.4f}")
+    print(f"- HBM bytes per launch: {traffic:.0f}")
+    print(f"- scan sources sha256: `{scan_sources_sha256()}`")
+    return 0
 
 
 def main():
     args = parse()
+    if args.summarize:
+        return summarize(*args.summarize)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the data-parallel path shards sequences across GPUs with no exchange, see DESIGN.md", file=sys.stderr)
@@ -151,9 +238,13 @@ def main():
     y.copy_(x)
     cp_med, _ = timed(lambda: y.copy_(x), 10)
     copy_gbps = 2 * (1 << 30) / (cp_med * 1e-6) / 1e9
-    if args.copy_calibration:
-        y.copy_(x)
     del x, y
+    if args.copy_calibration:
+        xf = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device=dev)
+        yf = torch.empty_like(xf)
+        torch.neg(xf, out=yf)
+        torch.cuda.synchronize()
+        del xf, yf
 
     line = {
         "metric": "decode queries/s + achieved HBM GB/s (% peak), CSA2 top-512 FP4 attn at 1 GPU",
@@ -174,7 +265,8 @@ def main():
         "step_hbm_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "roofline": {"kernel": "idx_scan_kernel (all of csa2_index)", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic() if args.workload == "long_decode" else None,
                      "algorithmic_bytes_per_launch": idx_bytes, "avg_launch_us": idx_avg},
         "stages_us": {"index": idx_med, "topk": topk_med, "attend": att_med, "reuse_3_layers": reuse_med},
         "copy_GBps": copy_gbps,
@@ -186,8 +278,9 @@ def main():
     return 0
 
 
-def cpu_baseline(c, G):
-    """The oracle (as is) on this host's cores, on the same 4-query batch."""
+def cpu_baseline(c, G, min_seconds=10.0, max_seconds=30.0):
+    """The oracle (as is) on this host's cores: the same 4-query step (index over every visible
+    entry, top-512, attention), repeated until about min_seconds of wall time have passed."""
     import numpy as np
 
     import oracle
@@ -200,14 +293,20 @@ def cpu_baseline(c, G):
     q, swa = u16(c.q[0]), u16(c.swa[0])
     codes, scales, swa_end = c.kv_codes.cpu().numpy(), c.kv_scales.cpu().numpy(), c.swa_end.cpu().numpy()
     oracle.lib()
-    t0 = time.perf_counter()
-    sc = oracle.index(q_idx, w, k, q_pos, c.ratio, c.q_per_seq)
-    sel = oracle.topk(sc, q_pos, c.ratio, c.k)
-    oracle.attend(q, codes, scales, sel, swa, swa_end, None, c.softmax_scale, c.q_per_seq, c.window)
-    dt = time.perf_counter() - t0
-    return {"value": c.T / dt, "unit": "queries/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"the full {c.T}-query step of the same workload (index + top-512 + attention), "
-                      f"{dt:.1f} s wall on the host"}
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        sc = oracle.index(q_idx, w, k, q_pos, c.ratio, c.q_per_seq)
+        sel = oracle.topk(sc, q_pos, c.ratio, c.k)
+        oracle.attend(q, codes, scales, sel, swa, swa_end, None, c.softmax_scale, c.q_per_seq, c.window)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or dt * (reps + 1) / reps > max_seconds:
+            break
+    # the oracle's threads run over independent queries: at most T of them are busy
+    cores = min(c.T, oracle.max_threads())
+    return {"value": reps * c.T / dt, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} repetitions of the full {c.T}-query step of the same workload (index over all "
+                      f"{c.N} entries per sequence, top-512, attention), {dt:.1f} s wall on {cores} threads"}
 
 
 if __name__ == "__main__":
