@@ -208,13 +208,18 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const AttnShared
     psum += p0 + p1;
     pb[i] = f32_to_bf16_rne(p0) | (f32_to_bf16_rne(p1) << 16);
   }
+  // a state with nothing folded in yet (every head of the wave) holds zeros: no rescale
+  const bool fresh = __ballot(st.m != -INFINITY) == 0ull;
   st.l = st.l * alpha + psum;
   st.m = mn;
   bf16x8 pv;
   __builtin_memcpy(&pv, pb, 16);
+  if (!fresh) {
+#pragma unroll
+    for (int mb = 0; mb < 32; ++mb) st.o[mb] *= alpha;
+  }
 #pragma unroll
   for (int mb = 0; mb < 32; ++mb) {
-    st.o[mb] *= alpha;
     const bf16x8 xa = lds_read16(&sh.XT[xt_off(16 * mb + r16, g)]);
     st.o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, pv, st.o[mb], 0, 0, 0);
   }
@@ -258,8 +263,9 @@ __device__ void write_partial(const AttnArgs& a, const HeadState& st, int layer,
   l += __shfl_xor(l, 32, 64);
   const size_t base = (((size_t)layer * a.T + t) * a.n_slots + slot) * kHeads + head;
   float* op = a.part_o + base * kDim + 4 * g;
+  // streaming stores: the partials are read once, by the combine kernel
 #pragma unroll
-  for (int mb = 0; mb < 32; ++mb) *reinterpret_cast<floatx4*>(op + 16 * mb) = st.o[mb];
+  for (int mb = 0; mb < 32; ++mb) __builtin_nontemporal_store(st.o[mb], reinterpret_cast<floatx4*>(op + 16 * mb));
   if (g == 0) {
     a.part_ml[base * 2 + 0] = st.m;
     a.part_ml[base * 2 + 1] = l;
@@ -322,19 +328,24 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a) {
   const size_t base = ((size_t)layer * a.T + t) * a.n_slots;
   __shared__ float fac[64];
   __shared__ float s_inv;
+  // all slot loads in flight at once (at most kMaxSlots slots), before the weights are known
+  floatx4 o[kMaxSlots];
+#pragma unroll
+  for (int s = 0; s < kMaxSlots; ++s)
+    if (s < a.n_slots) o[s] = *reinterpret_cast<const floatx4*>(a.part_o + ((base + s) * kHeads + h) * kDim + 4 * tid);
   if (tid < 64) {
     // one lane per slot (n_slots <= 64): max, then weighted sum, by wave reductions
     const bool has = tid < a.n_slots;
     const float ms = has ? a.part_ml[((base + tid) * kHeads + h) * 2] : -INFINITY;
     const float ls = has ? a.part_ml[((base + tid) * kHeads + h) * 2 + 1] : 0.f;
-    float M = wave_max(ms);
+    float M = wave_max_dpp(ms);
     float sk = -INFINITY;
     if (a.sink) {
       sk = a.sink[(size_t)layer * kHeads + h] * kLog2e;
       M = fmaxf(M, sk);
     }
     const float f = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
-    float den = wave_sum(ls * f);
+    float den = wave_sum_dpp(ls * f);
     if (a.sink && M != -INFINITY) den += exp2f(sk - M);
     if (has) fac[tid] = f;
     if (tid == 0) {
@@ -343,11 +354,6 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a) {
     }
   }
   __syncthreads();
-  // all slot loads in flight at once (at most kMaxSlots slots)
-  floatx4 o[kMaxSlots];
-#pragma unroll
-  for (int s = 0; s < kMaxSlots; ++s)
-    if (s < a.n_slots) o[s] = *reinterpret_cast<const floatx4*>(a.part_o + ((base + s) * kHeads + h) * kDim + 4 * tid);
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s)

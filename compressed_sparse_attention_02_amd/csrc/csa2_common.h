@@ -143,6 +143,21 @@ __device__ __forceinline__ uint32_t wave_min_u32_dpp(uint32_t v) {
   const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
   return min(min(a, b), min(c, d));
 }
+__device__ __forceinline__ double wave_max_f64_dpp(double v) {
+  v = fmax(v, dpp_f64<kDppXor1>(v));
+  v = fmax(v, dpp_f64<kDppXor2>(v));
+  v = fmax(v, dpp_f64<kDppHalfMirror>(v));
+  v = fmax(v, dpp_f64<kDppMirror>(v));
+  return fmax(fmax(lane_f64(v, 0), lane_f64(v, 16)), fmax(lane_f64(v, 32), lane_f64(v, 48)));
+}
+__device__ __forceinline__ double wave_min_f64_dpp(double v) { return -wave_max_f64_dpp(-v); }
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
+  return ((lane_f32(v, 0) + lane_f32(v, 16)) + lane_f32(v, 32)) + lane_f32(v, 48);
+}
 // Sum over the 8-lane groups of a wave of a value that is the same in the 8
 // lanes of each group (one term per group, in group order within each row,
 // rows in order).

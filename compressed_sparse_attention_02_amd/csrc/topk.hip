@@ -730,6 +730,7 @@ struct alignas(16) CandLds {
   uint16_t cmask[kCandTiles];   // entries of each candidate tile that reach the threshold
   uint32_t eidx[kCandMax];      // passing entries, ascending
   double escore[kCandMax];      // their fp64 scores
+  double hrel[kCandThreads / 64][64];  // per wave: ReLU(dot) of (entry, head) for the in-order head fold
 };
 
 // Candidates of tiles [x*kCandTiles, (x+1)*kCandTiles) of query t
@@ -845,11 +846,21 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
           d = fma((double)bf16hi(qw[c]), (double)bf16hi(kw[c]), d);
         }
       }
-      const double rl = d > 0.0 ? d : 0.0;
-      double sc = 0.0;
-#pragma unroll 8
-      for (int hh = 0; hh < kIdxHeads; ++hh) sc = fma((double)L.w[hh], __shfl(rl, (lane & 32) + hh, 64), sc);
-      if (h == 0 && e < n_pass) L.escore[e] = sc;
+      // the heads are folded in order by lane h == 0 of each entry, from LDS
+      L.hrel[wave][lane] = d > 0.0 ? d : 0.0;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (h == 0 && e < n_pass) {
+        const double* hr = &L.hrel[wave][lane & 32];
+        double sc = 0.0;
+#pragma unroll
+        for (int hh = 0; hh < kIdxHeads; ++hh) sc = fma((double)L.w[hh], hr[hh], sc);
+        L.escore[e] = sc;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
   __syncthreads();
@@ -885,6 +896,7 @@ struct alignas(16) SelectLds {
   uint32_t hist[256];
   uint32_t wsum[2][kSelThreads / 64];
   uint32_t pick[2];
+  uint32_t pick2;
   uint32_t n_bin;
   double red[2][kSelThreads / 64];
   double range[2];
@@ -943,6 +955,56 @@ __device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk, double 
   const int tid = threadIdx.x;
   uint32_t r = kk;
   uint32_t count = n;
+  // Fast path: counts of 256 value bins over [lo, hi]; when the bin holding
+  // the kk-th largest has at most 64 values, those are ranked directly (bin
+  // membership recomputed with the same arithmetic).  Otherwise the levels
+  // below narrow the range with per-bin minima and maxima.
+  if (lo < hi && n > 64) {
+    const double scale = 256.0 / (hi - lo);
+    for (uint32_t i = tid; i < n; i += kSelThreads) atomicAdd(&L.hist[bin_f64(L.v[i], lo, scale)], 1u);
+    __syncthreads();
+    if (tid < 64) {
+      uint32_t b, left;
+      wave_pick(L.hist, r, &b, &left);
+      const uint32_t cb = L.hist[b];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) L.hist[4 * tid + i] = 0u;
+      if (tid == 0) {
+        L.pick[0] = cb;
+        L.pick[1] = left;
+        L.pick2 = b;
+        L.n_bin = 0;
+      }
+    }
+    __syncthreads();
+    if (L.pick[0] <= 64) {
+      const uint32_t bsel = L.pick2, cnt_b = L.pick[0], rr = L.pick[1];
+      for (uint32_t i = tid; i < n; i += kSelThreads) {
+        const double v = L.v[i];
+        if (bin_f64(v, lo, scale) == bsel) L.bin_vals[atomicAdd(&L.n_bin, 1u)] = v;
+      }
+      __syncthreads();
+      if (tid < (int)cnt_b) {
+        const double va = L.bin_vals[tid];
+        uint32_t gt = 0, ge = 0;
+        for (uint32_t b = 0; b < cnt_b; ++b) {
+          const double vb = L.bin_vals[b];
+          gt += vb > va;
+          ge += vb >= va;
+        }
+        if (gt < rr && rr <= ge) {  // every writer writes the same values
+          L.result = va;
+          L.pick[0] = kk - rr + gt;
+          L.pick[1] = ge - gt;
+        }
+      }
+      __syncthreads();
+      *n_gt = L.pick[0];
+      *n_eq = L.pick[1];
+      return L.result;
+    }
+    // the histogram is clear again; bmin / bmax are untouched
+  }
   for (int level = 0; level < 6 && lo < hi && count > 64; ++level) {
     const double scale = 256.0 / (hi - lo);
     for (uint32_t i = tid; i < n; i += kSelThreads) {
@@ -1204,10 +1266,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   }
   {
     const int lane = tid & 63, wv = tid >> 6;
-    for (int o = 32; o >= 1; o >>= 1) {
-      lo = fmin(lo, __shfl_xor(lo, o, 64));
-      hi = fmax(hi, __shfl_xor(hi, o, 64));
-    }
+    lo = wave_min_f64_dpp(lo);
+    hi = wave_max_f64_dpp(hi);
     if (lane == 0) { L.red[0][wv] = lo; L.red[1][wv] = hi; }
     __syncthreads();
     lo = L.red[0][0];
