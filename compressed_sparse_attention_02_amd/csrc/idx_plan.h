@@ -15,11 +15,13 @@ namespace csa2 {
 
 constexpr int kScanThreads = 256;  // 4 waves
 constexpr int kScanWaves = kScanThreads / 64;
-constexpr int kScanTiles = 4;      // 16-key tiles per wave per iteration: 64 keys, 16 KiB
+constexpr int kScanTiles = 2;      // 16-key tiles per wave per iteration: 32 keys, 8 KiB
 constexpr int kScanWaveKeys = 16 * kScanTiles;
-constexpr int kChunkKeys = kScanWaveKeys * kScanWaves;  // 256 keys per block iteration
+constexpr int kChunkKeys = kScanWaveKeys * kScanWaves;  // 128 keys per block iteration
+constexpr int kGroupsPerBlock = kScanWaves * kScanTiles;  // group slots per block (times S)
+static_assert(kScanTiles >= 1 && kScanTiles <= 4, "a wave's lane groups take one tile each");
 constexpr int kScanBlocks = 2048;  // blocks per launch the grid aims for (8 per CU)
-constexpr int kGroupsWanted = 4096;
+constexpr int kGroupsWanted = 8192;
 
 struct IndexPlan {
   int qg = 1;             // queries per group (template)
@@ -42,12 +44,12 @@ inline bool index_plan(int32_t T, int32_t q_per_seq, int64_t N, IndexPlan* p) {
   if (want > nchunks) want = nchunks;
   if (want < 1) want = 1;
   p->blocks_x = (int)want;
-  // enough group slots for ~4096 groups, within the registers of the query count
+  // enough group slots for ~8192 groups, within the registers of the query count
   const int max_slots = p->qg == 1 ? 4 : p->qg == 2 ? 2 : 1;
   int slots = 1;
-  while (slots < max_slots && (int64_t)p->blocks_x * 16 * slots < kGroupsWanted) slots *= 2;
+  while (slots < max_slots && (int64_t)p->blocks_x * kGroupsPerBlock * slots < kGroupsWanted) slots *= 2;
   p->slots = slots;
-  p->n_groups = (int64_t)p->blocks_x * 16 * slots;
+  p->n_groups = (int64_t)p->blocks_x * kGroupsPerBlock * slots;
   return p->B <= 65535 && p->groups <= 65535;
 }
 

@@ -5,9 +5,9 @@
 //
 // Per sequence the scan is a [32 heads x 128] x [128 x N] product, far below
 // the MFMA ridge (32 flop per key byte), so the kernel is built around the key
-// stream: each wave pulls four 16-key tiles (16 KiB) per iteration into the B
+// stream: each wave pulls two 16-key tiles (8 KiB) per iteration into the B
 // operands of v_mfma_f32_16x16x32_bf16 (idx_tile.h), with the query in LDS.
-// Blocks take 256-key chunks round-robin, so at any moment the whole grid
+// Blocks take 128-key chunks round-robin, so at any moment the whole grid
 // sweeps one window of each sequence.  Per tile the scan forms the maximum
 // score, and per (block, wave, tile slot, iteration mod S) group the maximum
 // of those; that is all the selection needs (csa2_topk re-derives the few
@@ -23,13 +23,13 @@
 namespace csa2 {
 
 // One block: sequence b = blockIdx.y, query group blockIdx.z (QG queries of
-// that sequence), chunks x, x + gridDim.x, x + 2 gridDim.x, ... of 256 keys;
-// wave w takes keys 64w .. 64w+63 of each chunk.  Group maxima: group
-// ((x * 4 + w) * 4 + u) * S + (i % S) holds the maxima of tile u of wave w in
-// the block's iterations i, so a group samples the whole row and neighbouring
-// tiles never share a group.
+// that sequence), chunks x, x + gridDim.x, x + 2 gridDim.x, ... of 128 keys;
+// wave w takes keys 32w .. 32w+31 of each chunk (kScanWaveKeys per wave).
+// Group maxima: group ((x * 4 + w) * kScanTiles + u) * S + (i % S) holds the
+// maxima of tile u of wave w in the block's iterations i, so a group samples
+// the whole row and neighbouring tiles never share a group.
 template <int QG, int S>
-__global__ __launch_bounds__(kScanThreads, QG == 1 ? 4 : 2) void idx_scan_kernel(
+__global__ __launch_bounds__(kScanThreads, QG == 1 ? 6 : QG == 2 ? 4 : 2) void idx_scan_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos, int ratio,
     int q_per_seq, int64_t N, float* __restrict__ scores, float* __restrict__ tile_max,
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kScanThreads, QG == 1 ? 4 : 2) void idx_scan_kernel
   const int g = lane >> 4;    // channel group
   const int b = blockIdx.y;
   const int64_t ld = tile_ld(N);
-  const int64_t n_groups = (int64_t)gridDim.x * 16 * S;
+  const int64_t n_groups = (int64_t)gridDim.x * kGroupsPerBlock * S;
 
   int64_t nvis[QG];
   int64_t trow[QG];
@@ -116,8 +116,8 @@ __global__ __launch_bounds__(kScanThreads, QG == 1 ? 4 : 2) void idx_scan_kernel
         sc[qq][u] = (s < nvis[qq]) ? part : -INFINITY;
       }
     }
-    // Every lane holds the score of key `col` of each tile.  Lane l stores
-    // key l of the 64 (one 256-byte store) and lanes 0..3 the tile maxima.
+    // Every lane holds the score of key `col` of each tile.  Lane l < 32 stores
+    // key l of the wave's 32 (one 128-byte store) and lanes 0..1 the tile maxima.
     const int64_t so = base + lane;
     const int64_t tile = base / kTileKeys + lane;
 #pragma unroll
@@ -125,18 +125,19 @@ __global__ __launch_bounds__(kScanThreads, QG == 1 ? 4 : 2) void idx_scan_kernel
       float v = sc[qq][0], m = -INFINITY;
 #pragma unroll
       for (int u = 0; u < kScanTiles; ++u) {
+        // maximum over the 16 keys of the tile (one 16-lane row) with DPP moves
         float tm = sc[qq][u];
-        tm = fmaxf(tm, __shfl_xor(tm, 1, 64));
-        tm = fmaxf(tm, __shfl_xor(tm, 2, 64));
-        tm = fmaxf(tm, __shfl_xor(tm, 4, 64));
-        tm = fmaxf(tm, __shfl_xor(tm, 8, 64));
+        tm = fmaxf(tm, dpp_f32<kDppXor1>(tm));
+        tm = fmaxf(tm, dpp_f32<kDppXor2>(tm));
+        tm = fmaxf(tm, dpp_f32<kDppHalfMirror>(tm));
+        tm = fmaxf(tm, dpp_f32<kDppMirror>(tm));
         if (u > 0) v = g == u ? sc[qq][u] : v;
         m = lane == u ? tm : m;
       }
 #pragma unroll
       for (int r = 0; r < S; ++r) gm[qq][r] = (it % S == r) ? fmaxf(gm[qq][r], m) : gm[qq][r];
       if (!valid[qq]) continue;
-      if (scores != nullptr && so < N) scores[trow[qq] * N + so] = v;
+      if (scores != nullptr && lane < kScanWaveKeys && so < N) scores[trow[qq] * N + so] = v;
       if (lane < kScanTiles && tile * kTileKeys < N) tile_max[trow[qq] * ld + tile] = m;
     }
   }

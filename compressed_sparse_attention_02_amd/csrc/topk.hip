@@ -595,7 +595,7 @@ struct alignas(16) FloorLds {
 // entries (each maximum is a distinct visible entry); -inf when fewer than
 // CSA2_TOPK of those maxima are finite.  The maxima ranked are the tile maxima
 // when the row has at most kFloorVals tiles, else the scan's group maxima (when
-// there are at least 4096 of them) or the tile maxima; past kFloorVals values
+// there are at least kGroupsWanted of them) or the tile maxima; past kFloorVals values
 // they are folded (value j is the maximum over j, j + kFloorVals, ...), and
 // folding unions groups, which keeps them disjoint.
 //
