@@ -18,10 +18,15 @@ constexpr int kScanWaves = kScanThreads / 64;
 constexpr int kScanTiles = 2;      // 16-key tiles per wave per iteration: 32 keys, 8 KiB
 constexpr int kScanWaveKeys = 16 * kScanTiles;
 constexpr int kChunkKeys = kScanWaveKeys * kScanWaves;  // 128 keys per block iteration
-constexpr int kGroupsPerBlock = kScanWaves * kScanTiles;  // group slots per block (times S)
 static_assert(kScanTiles >= 1 && kScanTiles <= 4, "a wave's lane groups take one tile each");
-constexpr int kScanBlocks = 2048;  // blocks per launch the grid aims for (8 per CU)
-constexpr int kGroupsWanted = 8192;
+constexpr int kScanBlocks = 16384;  // blocks per launch the grid aims for: short blocks balance the load
+constexpr int kGroupsWanted = 4096;
+
+// Group maxima per query: kScanTiles * S per block, rounded up to a multiple of
+// four (16-byte rows); the scan writes -inf to the padding.
+__host__ __device__ inline int64_t group_count(int64_t blocks_x, int S) {
+  return (blocks_x * kScanTiles * S + 3) / 4 * 4;
+}
 
 struct IndexPlan {
   int qg = 1;             // queries per group (template)
@@ -38,18 +43,19 @@ inline bool index_plan(int32_t T, int32_t q_per_seq, int64_t N, IndexPlan* p) {
   p->qg = q_per_seq == 1 ? 1 : q_per_seq == 2 ? 2 : 4;
   p->groups = (q_per_seq + p->qg - 1) / p->qg;
   p->B = T / q_per_seq;
-  // aim for ~2048 blocks over 256 CUs, each with at least one chunk
+  // aim for ~16384 blocks over 256 CUs (a few chunks each), each with at least one chunk
   const int64_t nchunks = (N + kChunkKeys - 1) / kChunkKeys;
   int64_t want = (kScanBlocks + (int64_t)p->B * p->groups - 1) / ((int64_t)p->B * p->groups);
   if (want > nchunks) want = nchunks;
   if (want < 1) want = 1;
   p->blocks_x = (int)want;
-  // enough group slots for ~8192 groups, within the registers of the query count
+  // enough group slots for at least 4096 groups (kScanTiles per block and slot), within
+  // the registers of the query count
   const int max_slots = p->qg == 1 ? 4 : p->qg == 2 ? 2 : 1;
   int slots = 1;
-  while (slots < max_slots && (int64_t)p->blocks_x * kGroupsPerBlock * slots < kGroupsWanted) slots *= 2;
+  while (slots < max_slots && (int64_t)p->blocks_x * kScanTiles * slots < kGroupsWanted) slots *= 2;
   p->slots = slots;
-  p->n_groups = (int64_t)p->blocks_x * kGroupsPerBlock * slots;
+  p->n_groups = group_count(p->blocks_x, slots);
   return p->B <= 65535 && p->groups <= 65535;
 }
 

@@ -25,9 +25,9 @@ namespace csa2 {
 // One block: sequence b = blockIdx.y, query group blockIdx.z (QG queries of
 // that sequence), chunks x, x + gridDim.x, x + 2 gridDim.x, ... of 128 keys;
 // wave w takes keys 32w .. 32w+31 of each chunk (kScanWaveKeys per wave).
-// Group maxima: group ((x * 4 + w) * kScanTiles + u) * S + (i % S) holds the
-// maxima of tile u of wave w in the block's iterations i, so a group samples
-// the whole row and neighbouring tiles never share a group.
+// Group maxima: group (x * kScanTiles + u) * S + (i % S) holds the maxima of
+// tile u of every wave in the block's iterations i, so a group samples the
+// whole row and neighbouring tiles never share a group.
 template <int QG, int S>
 __global__ __launch_bounds__(kScanThreads, QG == 1 ? 6 : QG == 2 ? 4 : 2) void idx_scan_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kScanThreads, QG == 1 ? 6 : QG == 2 ? 4 : 2) void i
   const int g = lane >> 4;    // channel group
   const int b = blockIdx.y;
   const int64_t ld = tile_ld(N);
-  const int64_t n_groups = (int64_t)gridDim.x * kGroupsPerBlock * S;
+  const int64_t n_groups = group_count(gridDim.x, S);
 
   int64_t nvis[QG];
   int64_t trow[QG];
@@ -141,20 +141,32 @@ __global__ __launch_bounds__(kScanThreads, QG == 1 ? 6 : QG == 2 ? 4 : 2) void i
       if (lane < kScanTiles && tile * kTileKeys < N) tile_max[trow[qq] * ld + tile] = m;
     }
   }
+  // group maxima merged over the block's waves (LDS), and the block's max ||K||^2
+  constexpr int kPer = kScanTiles * S;  // groups per block and query
+  __shared__ float gml[kScanWaves][QG][kPer];
   if (lane < kScanTiles) {
 #pragma unroll
-    for (int qq = 0; qq < QG; ++qq) {
-      if (!valid[qq]) continue;
+    for (int qq = 0; qq < QG; ++qq)
 #pragma unroll
-      for (int r = 0; r < S; ++r)
-        group_max[trow[qq] * n_groups + (((int64_t)blockIdx.x * kScanWaves + wave) * kScanTiles + lane) * S + r] =
-            gm[qq][r];
-    }
+      for (int r = 0; r < S; ++r) gml[wave][qq][lane * S + r] = gm[qq][r];
   }
-
-  maxn2 = wave_max(maxn2);
+  maxn2 = wave_max_dpp(maxn2);
   if (lane == 0) red[wave] = maxn2;
   __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int qq = 0; qq < QG; ++qq) {
+      if (lane < kPer && valid[qq]) {
+        float m = gml[0][qq][lane];
+#pragma unroll
+        for (int i = 1; i < kScanWaves; ++i) m = fmaxf(m, gml[i][qq][lane]);
+        group_max[trow[qq] * n_groups + (int64_t)blockIdx.x * kPer + lane] = m;
+      }
+      // padding of the row to a multiple of four
+      const int64_t used = (int64_t)gridDim.x * kPer;
+      if (blockIdx.x == 0 && valid[qq] && lane < n_groups - used) group_max[trow[qq] * n_groups + used + lane] = -INFINITY;
+    }
+  }
   if (threadIdx.x == 0) {
     float m = red[0];
 #pragma unroll
