@@ -61,6 +61,11 @@ struct AttnShared {
   int valid[kChunk];
 };
 
+// Wave index over the 64 heads (16 heads per wave): a block of W waves takes
+// head group blockIdx.z (grids with W = 1 split a work item's heads over four
+// blocks).
+__device__ __forceinline__ int head_wave() { return (int)(blockIdx.z * (blockDim.x >> 6) + (threadIdx.x >> 6)); }
+
 // 16-byte LDS operand read (the offsets used are multiples of 16 bytes).
 __device__ __forceinline__ bf16x8 lds_read16(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(__builtin_assume_aligned(p, 16));
@@ -87,53 +92,17 @@ __device__ __forceinline__ uint4 dequant8(uint32_t codes, uint32_t sbyte) {
 // (rows 8d + i for the 64 lanes d) spread over the LDS banks.
 __device__ __forceinline__ int xt_off(int row, int blk) { return row * kXTStride + 8 * ((blk + (row >> 3)) & 3); }
 
-// Stage chunk `c` of query t (layer `layer` for window chunks) into LDS.
-// Thread (g = wave, d = lane) loads 8 rows x 8 channels: rows {4g..4g+3,
-// 16+4g..16+4g+3} (the 8 rows that form XT column group g), channels 8d..8d+7.
-__device__ void stage_chunk(const AttnArgs& a, AttnShared& sh, int t, int b, int c, int layer) {
-  const int g = threadIdx.x >> 6, d = threadIdx.x & 63;
-  uint32_t v[8][4];
-  int okr[8];
-  if (c < a.n_main) {
-    // all index loads, then all code / scale loads (rows of -1 slots read row 0
-    // and are zeroed), so that every load of the chunk is in flight together
-    int32_t idx[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int e = r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4);
-      idx[r] = a.indices[(size_t)t * a.k + c * kChunk + e];
-    }
-    uint32_t codes[8], sbyte[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const size_t rowid = (size_t)b * a.N + (idx[r] >= 0 ? idx[r] : 0);
-      codes[r] = *reinterpret_cast<const uint32_t*>(a.kv_fp4 + rowid * 256 + 4 * d);
-      sbyte[r] = a.kv_scale[rowid * 16 + (d >> 2)];
-    }
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      okr[r] = idx[r] >= 0;
-      const uint4 o = dequant8(codes[r], sbyte[r]);
-      v[r][0] = okr[r] ? o.x : 0u; v[r][1] = okr[r] ? o.y : 0u;
-      v[r][2] = okr[r] ? o.z : 0u; v[r][3] = okr[r] ? o.w : 0u;
-    }
-  } else {
-    const int we = a.swa_end[t];
-    const int ws = we - a.window > 0 ? we - a.window : 0;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int e = r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4);
-      const int row = ws + (c - a.n_main) * kChunk + e;
-      okr[r] = row < we;
-      const int rr = okr[r] ? row : (we > 0 ? we - 1 : 0);
-      const uint4 x = *reinterpret_cast<const uint4*>(a.swa + (((size_t)layer * a.B + b) * a.S + rr) * kDim + 8 * d);
-      v[r][0] = okr[r] ? x.x : 0u; v[r][1] = okr[r] ? x.y : 0u;
-      v[r][2] = okr[r] ? x.z : 0u; v[r][3] = okr[r] ? x.w : 0u;
-    }
-  }
+// Chunk `c` of query t (layer `layer` for window chunks) in LDS: row group g
+// (0..3), lane d holds 8 rows x 8 channels, rows {4g..4g+3, 16+4g..16+4g+3}
+// (the 8 rows that form XT column group g), channels 8d..8d+7.
+__device__ __forceinline__ int group_row(int g, int r) { return r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4); }
+
+// Write row group g (v: bf16 words, okr: row valid) to X and, transposed, to XT.
+__device__ __forceinline__ void write_group(AttnShared& sh, int g, int d, const uint32_t (&v)[8][4],
+                                            const int (&okr)[8]) {
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    const int e = r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4);
+    const int e = group_row(g, r);
     *reinterpret_cast<uint4*>(&sh.X[e * kXStride + 8 * d]) = make_uint4(v[r][0], v[r][1], v[r][2], v[r][3]);
     if (d == 0) sh.valid[e] = okr[r];
   }
@@ -151,6 +120,81 @@ __device__ void stage_chunk(const AttnArgs& a, AttnShared& sh, int t, int b, int
   }
 }
 
+// Row group g of a selected-row chunk from its codes and scale bytes (rows of
+// -1 slots were read from row 0 and are zeroed here).
+__device__ __forceinline__ void dequant_group(AttnShared& sh, int g, int d, const int32_t* idx, const uint32_t* codes,
+                                              const uint32_t* sbyte) {
+  uint32_t v[8][4];
+  int okr[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    okr[r] = idx[r] >= 0;
+    const uint4 o = dequant8(codes[r], sbyte[r]);
+    v[r][0] = okr[r] ? o.x : 0u; v[r][1] = okr[r] ? o.y : 0u;
+    v[r][2] = okr[r] ? o.z : 0u; v[r][3] = okr[r] ? o.w : 0u;
+  }
+  write_group(sh, g, d, v, okr);
+}
+
+// NG row groups g0, g0 + 1, ... staged by one wave, every load of a kind in
+// flight together: the indices, then the codes and scales (selected rows), or
+// the window rows.
+template <int NG>
+__device__ __forceinline__ void stage_groups(const AttnArgs& a, AttnShared& sh, int t, int b, int c, int layer,
+                                             int g0) {
+  const int d = threadIdx.x & 63;
+  if (c < a.n_main) {
+    int32_t idx[NG][8];
+#pragma unroll
+    for (int j = 0; j < NG; ++j)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) idx[j][r] = a.indices[(size_t)t * a.k + c * kChunk + group_row(g0 + j, r)];
+    uint32_t codes[NG][8], sbyte[NG][8];
+#pragma unroll
+    for (int j = 0; j < NG; ++j)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const size_t rowid = (size_t)b * a.N + (idx[j][r] >= 0 ? idx[j][r] : 0);
+        codes[j][r] = *reinterpret_cast<const uint32_t*>(a.kv_fp4 + rowid * 256 + 4 * d);
+        sbyte[j][r] = a.kv_scale[rowid * 16 + (d >> 2)];
+      }
+#pragma unroll
+    for (int j = 0; j < NG; ++j) dequant_group(sh, g0 + j, d, idx[j], codes[j], sbyte[j]);
+  } else {
+    const int we = a.swa_end[t];
+    const int ws = we - a.window > 0 ? we - a.window : 0;
+    // window rows two groups at a time (32 registers per group)
+#pragma unroll
+    for (int j0 = 0; j0 < NG; j0 += 2) {
+      uint32_t v[2][8][4];
+      int okr[2][8];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (j0 + j >= NG) continue;  // compile-time
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int row = ws + (c - a.n_main) * kChunk + group_row(g0 + j0 + j, r);
+          okr[j][r] = row < we;
+          const int rr = okr[j][r] ? row : (we > 0 ? we - 1 : 0);
+          const uint4 x = *reinterpret_cast<const uint4*>(a.swa + (((size_t)layer * a.B + b) * a.S + rr) * kDim + 8 * d);
+          v[j][r][0] = okr[j][r] ? x.x : 0u; v[j][r][1] = okr[j][r] ? x.y : 0u;
+          v[j][r][2] = okr[j][r] ? x.z : 0u; v[j][r][3] = okr[j][r] ? x.w : 0u;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (j0 + j < NG) write_group(sh, g0 + j0 + j, d, v[j], okr[j]);
+    }
+  }
+}
+
+// Stage chunk `c` into LDS: wave g of a 4-wave block takes row group g, a
+// one-wave block all four.
+__device__ void stage_chunk(const AttnArgs& a, AttnShared& sh, int t, int b, int c, int layer) {
+  if (blockDim.x == 64) stage_groups<4>(a, sh, t, b, c, layer, 0);
+  else stage_groups<1>(a, sh, t, b, c, layer, threadIdx.x >> 6);
+}
+
 struct HeadState {
   floatx4 o[32];   // O^T: o[mb][i] = O[head][16*mb + 4*g + i]
   float m;         // running max (log2 units)
@@ -158,8 +202,8 @@ struct HeadState {
 };
 
 __device__ __forceinline__ void load_q(const AttnArgs& a, int layer, int t, bf16x8* qb) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int head = 16 * wave + (lane & 15), g = lane >> 4;
+  const int lane = threadIdx.x & 63;
+  const int head = 16 * head_wave() + (lane & 15), g = lane >> 4;
   const uint4* qp = reinterpret_cast<const uint4*>(a.q + (((size_t)layer * a.T + t) * kHeads + head) * kDim + 8 * g);
 #pragma unroll
   for (int j = 0; j < 16; ++j) qb[j] = as_bf16x8(qp[4 * j]);  // channels 32j + 8g .. +8
@@ -227,8 +271,8 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const AttnShared
 
 // Write the final output of one (layer, query) from a complete state.
 __device__ void write_final(const AttnArgs& a, const HeadState& st, int layer, int t) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int head = 16 * wave + (lane & 15), g = lane >> 4;
+  const int lane = threadIdx.x & 63;
+  const int head = 16 * head_wave() + (lane & 15), g = lane >> 4;
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
@@ -256,8 +300,8 @@ __device__ void write_final(const AttnArgs& a, const HeadState& st, int layer, i
 }
 
 __device__ void write_partial(const AttnArgs& a, const HeadState& st, int layer, int t, int slot) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int head = 16 * wave + (lane & 15), g = lane >> 4;
+  const int lane = threadIdx.x & 63;
+  const int head = 16 * head_wave() + (lane & 15), g = lane >> 4;
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
@@ -278,7 +322,8 @@ __device__ void write_partial(const AttnArgs& a, const HeadState& st, int layer,
 //   L  > 1: i < n_main: selected-row chunk i for every layer (slot i);
 //           otherwise window chunk j of layer l, i = n_main + l*n_swa + j
 //           (slot n_main + j of layer l).
-__global__ __launch_bounds__(kAttnThreads) void attend_kernel(AttnArgs a) {
+template <int W>
+__global__ __launch_bounds__(64 * W) void attend_kernel(AttnArgs a) {
   __shared__ AttnShared sh;
   const int item = blockIdx.x, t = blockIdx.y;
   const int b = t / a.q_per_seq;
@@ -442,7 +487,12 @@ static csa2_status attend_launch(int32_t L, const void* q, const uint8_t* kv_fp4
   a.part_ml = need ? (float*)((char*)workspace + align_up(slots * kHeads * kDim * sizeof(float), 256)) : nullptr;
   hipStream_t st = (hipStream_t)hip_stream;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(attend_kernel, dim3(p.n_items, T), dim3(kAttnThreads), 0, st, a);
+  // small batches: one wave per block and four blocks per work item (16 heads
+  // each), so that the work and the partial writes spread over four times the CUs
+  if ((int64_t)p.n_items * T * 4 <= 4096)
+    hipLaunchKernelGGL(attend_kernel<1>, dim3(p.n_items, T, 4), dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL(attend_kernel<4>, dim3(p.n_items, T, 1), dim3(kAttnThreads), 0, st, a);
   if (need) hipLaunchKernelGGL(attend_combine_kernel, dim3(kHeads, T, L), dim3(128), 0, st, a);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   return CSA2_OK;
