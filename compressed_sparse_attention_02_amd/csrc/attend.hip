@@ -51,7 +51,7 @@ struct AttnArgs {
   int n_slots;              // partial slots per (layer, query)
   uint16_t* out;            // [L][T][64][512]
   float* lse;               // [L][T][64] or null
-  float* part_o;            // [L][T][n_slots][64][512]
+  uint16_t* part_o;         // [L][T][n_slots][64][512], bf16
   float* part_ml;           // [L][T][n_slots][64][2]  (max in log2 units, sum)
 };
 
@@ -306,10 +306,16 @@ __device__ void write_partial(const AttnArgs& a, const HeadState& st, int layer,
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
   const size_t base = (((size_t)layer * a.T + t) * a.n_slots + slot) * kHeads + head;
-  float* op = a.part_o + base * kDim + 4 * g;
-  // streaming stores: the partials are read once, by the combine kernel
+  uint16_t* op = a.part_o + base * kDim + 4 * g;
+  // bf16 partials (the combine accumulates in fp32); streaming stores: they
+  // are read once, by the combine kernel
 #pragma unroll
-  for (int mb = 0; mb < 32; ++mb) __builtin_nontemporal_store(st.o[mb], reinterpret_cast<floatx4*>(op + 16 * mb));
+  for (int mb = 0; mb < 32; ++mb) {
+    const uint32_t w0 = f32_to_bf16_rne(st.o[mb][0]) | (f32_to_bf16_rne(st.o[mb][1]) << 16);
+    const uint32_t w1 = f32_to_bf16_rne(st.o[mb][2]) | (f32_to_bf16_rne(st.o[mb][3]) << 16);
+    const u32x2 w = {w0, w1};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(op + 16 * mb));
+  }
   if (g == 0) {
     a.part_ml[base * 2 + 0] = st.m;
     a.part_ml[base * 2 + 1] = l;
@@ -374,10 +380,10 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a) {
   __shared__ float fac[64];
   __shared__ float s_inv;
   // all slot loads in flight at once (at most kMaxSlots slots), before the weights are known
-  floatx4 o[kMaxSlots];
+  uint2 o[kMaxSlots];
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s)
-    if (s < a.n_slots) o[s] = *reinterpret_cast<const floatx4*>(a.part_o + ((base + s) * kHeads + h) * kDim + 4 * tid);
+    if (s < a.n_slots) o[s] = *reinterpret_cast<const uint2*>(a.part_o + ((base + s) * kHeads + h) * kDim + 4 * tid);
   if (tid < 64) {
     // one lane per slot (n_slots <= 64): max, then weighted sum, by wave reductions
     const bool has = tid < a.n_slots;
@@ -402,7 +408,10 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a) {
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s)
-    if (s < a.n_slots && fac[s] != 0.f) acc += o[s] * fac[s];
+    if (s < a.n_slots && fac[s] != 0.f) {
+      const floatx4 v = {bf16lo(o[s].x), bf16hi(o[s].x), bf16lo(o[s].y), bf16hi(o[s].y)};
+      acc += v * fac[s];
+    }
   const float iv = s_inv;
   uint16_t* op = a.out + (((size_t)layer * a.T + t) * kHeads + h) * kDim + 4 * tid;
   const uint32_t w0 = f32_to_bf16_rne(acc[0] * iv) | (f32_to_bf16_rne(acc[1] * iv) << 16);
@@ -438,7 +447,7 @@ static AttendPlan attend_plan(int32_t T, int32_t k, int32_t window, int32_t L) {
 static size_t attend_ws_bytes(int32_t T, const AttendPlan& p, int32_t L) {
   if (p.n_items == 1 && L == 1) return 0;
   const size_t slots = (size_t)L * T * p.n_slots;
-  return align_up(slots * kHeads * kDim * sizeof(float), 256) + align_up(slots * kHeads * 2 * sizeof(float), 256);
+  return align_up(slots * kHeads * kDim * sizeof(uint16_t), 256) + align_up(slots * kHeads * 2 * sizeof(float), 256);
 }
 
 static csa2_status attend_launch(int32_t L, const void* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
@@ -483,8 +492,8 @@ static csa2_status attend_launch(int32_t L, const void* q, const uint8_t* kv_fp4
   a.out = (uint16_t*)out;
   a.lse = lse;
   const size_t slots = (size_t)L * T * p.n_slots;
-  a.part_o = need ? (float*)workspace : nullptr;
-  a.part_ml = need ? (float*)((char*)workspace + align_up(slots * kHeads * kDim * sizeof(float), 256)) : nullptr;
+  a.part_o = need ? (uint16_t*)workspace : nullptr;
+  a.part_ml = need ? (float*)((char*)workspace + align_up(slots * kHeads * kDim * sizeof(uint16_t), 256)) : nullptr;
   hipStream_t st = (hipStream_t)hip_stream;
   (void)hipGetLastError();
   // small batches: one wave per block and four blocks per work item (16 heads
