@@ -231,9 +231,12 @@ def test_attend_split_plans(T_q):
         assert_close_bf16(out[t], ref[t][0], what=f"T={T_q} t={t}")
 
 
-def test_reuse_layers_match_oracle_and_attend():
-    log("[reuse] 3 layers")
-    c = G.make_case("reuse", B=3, N=1200, n_layers=4, seed=21, device=DEV)
+# 3 sequences: one-wave blocks (each work item's heads split over four blocks);
+# 48 sequences: more work items than that split takes, four-wave blocks
+@pytest.mark.parametrize("B", [3, 48])
+def test_reuse_layers_match_oracle_and_attend(B):
+    log(f"[reuse] 3 layers, {B} sequences")
+    c = G.make_case("reuse", B=B, N=1200, n_layers=4, seed=21, device=DEV)
     idx = run_topk(c, run_index(c, want_scores=False))
     full = _attend(c, idx, layer=0, lse=False)
     q = c.q[1:].view(torch.bfloat16).contiguous()
