@@ -94,7 +94,8 @@ __global__ __launch_bounds__(kScanThreads, QG == 1 ? 6 : QG == 2 ? 4 : 2) void i
       for (int qq = 0; qq < QG; ++qq) sc[qq][u] = -INFINITY;
       const int64_t s = base + u * kTileKeys + col;
       if (base + u * kTileKeys >= nvis_max) continue;  // no query of the group sees this tile
-      // ||K_s||^2: 32 channels per lane with bf16 dot2, then the other three groups
+      // this lane's 32 channels of ||K_s||^2 (bf16 dot2); the block sums the four
+      // channel groups' maxima over its keys, an upper bound of max_s ||K_s||^2
       float n2 = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -106,8 +107,6 @@ __global__ __launch_bounds__(kScanThreads, QG == 1 ? 6 : QG == 2 ? 4 : 2) void i
           n2 = __builtin_amdgcn_fdot2_f32_bf16(p, p, n2, false);
         }
       }
-      n2 += __shfl_xor(n2, 16, 64);
-      n2 += __shfl_xor(n2, 32, 64);
       if (s < N) maxn2 = fmaxf(maxn2, n2);
 #pragma unroll
       for (int qq = 0; qq < QG; ++qq) {
@@ -150,7 +149,13 @@ __global__ __launch_bounds__(kScanThreads, QG == 1 ? 6 : QG == 2 ? 4 : 2) void i
 #pragma unroll
       for (int r = 0; r < S; ++r) gml[wave][qq][lane * S + r] = gm[qq][r];
   }
-  maxn2 = wave_max_dpp(maxn2);
+  // row g of the wave holds channel group g: its maximum over the wave's keys,
+  // then the sum over the four groups
+  maxn2 = fmaxf(maxn2, dpp_f32<kDppXor1>(maxn2));
+  maxn2 = fmaxf(maxn2, dpp_f32<kDppXor2>(maxn2));
+  maxn2 = fmaxf(maxn2, dpp_f32<kDppHalfMirror>(maxn2));
+  maxn2 = fmaxf(maxn2, dpp_f32<kDppMirror>(maxn2));
+  maxn2 = ((lane_f32(maxn2, 0) + lane_f32(maxn2, 16)) + lane_f32(maxn2, 32)) + lane_f32(maxn2, 48);
   if (lane == 0) red[wave] = maxn2;
   __syncthreads();
   if (wave == 0) {

@@ -72,7 +72,9 @@ __device__ __forceinline__ double next_up(double x) { return -next_down(-x); }
 // 2^-19.9 sum_h |w_h| |dot_h|; the fp64 reference itself is within 2^-44 of
 // the exact value.  The sum is below 1.1 * 2^-15; 2^-14 leaves a factor 1.8
 // of margin.  The absolute term covers products that flush to zero.
-// ||K||^2 is accumulated by the scan with bf16 dot2 steps in fp32 over
+// The scan's value for max_s ||K_s||^2 is the sum over the four 32-channel
+// groups of each group's maximum over the keys, which is at least the maximum
+// of the sums; each group is accumulated with bf16 dot2 steps in fp32 over
 // nonnegative terms (relative error below 2^-16 even with two roundings per
 // step), so it is inflated by (1 + 2^-10) before the square root.  ||q_h||^2
 // is summed in fp64 (relative error below 2^-45 in any order), covered by
