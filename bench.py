@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 WORKLOADS = {
     "long_decode": dict(B=4, N=1 << 20),
     "batched_decode": dict(B=64, N=131072),
@@ -42,9 +43,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run torch.neg over 1 GiB of fp32 (reads and writes 1 GiB: the reference dispatch "
                          "that scales rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to bytes)")
-    ap.add_argument("--summarize", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="print the profile summary of rocprofv3 CSV output (kernel stats, then the FETCH_SIZE and "
-                         "WRITE_SIZE runs) instead of benchmarking")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="print the profile summary of rocprofv3 CSV output (kernel stats, the FETCH_SIZE run, the "
+                         "WRITE_SIZE run and optionally the MFMA-counter run) instead of benchmarking")
     return ap.parse_args()
 
 
@@ -81,7 +82,7 @@ def recorded_traffic():
         return None
 
 
-def summarize(stats_dir, fetch_dir, write_dir):
+def summarize(stats_dir, fetch_dir, write_dir, mfma_dir=None):
     """Markdown summary of rocprofv3 CSV output: per-kernel durations of the bench run and the
     per-dispatch FETCH_SIZE / WRITE_SIZE of the scan, scaled by the calibration dispatch."""
     import csv
@@ -106,7 +107,9 @@ def summarize(stats_dir, fetch_dir, write_dir):
         for r in rows(d, "counter_collection.csv"):
             if r["Counter_Name"] != counter:
                 continue
-            key = "scan" if "idx_scan_kernel" in r["Kernel_Name"] else ("cal" if "neg_kernel" in r["Kernel_Name"] else None)
+            name = r["Kernel_Name"]
+            key = ("scan" if "idx_scan_kernel" in name else "cal" if "neg_kernel" in name else
+                   "attend" if "attend_kernel" in name else "combine" if "attend_combine" in name else None)
             if key:
                 acc.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
                 acc[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
@@ -126,6 +129,32 @@ def summarize(stats_dir, fetch_dir, write_dir):
     print(f"- WRITE scale: {w_scale:.4f}")
     print(f"- HBM bytes per launch: {traffic:.0f}")
     print(f"- scan sources sha256: `{scan_sources_sha256()}`")
+    # attention kernels, split by grid size (the single-layer call and the
+    # three-layer Reuse call launch different grids)
+    def by_grid(d, counter, kernel):
+        acc = {}
+        for r in rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] == counter and kernel in r["Kernel_Name"] and "combine" not in r["Kernel_Name"]:
+                g = acc.setdefault(int(r["Grid_Size"]), {})
+                v = g.setdefault(r["Dispatch_Id"], [0.0, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])])
+                v[0] += float(r["Counter_Value"])
+        return {k: (sum(x[0] for x in v.values()) / len(v), sum(x[1] for x in v.values()) / len(v), len(v))
+                for k, v in acc.items()}
+
+    print("\n### attend_kernel per launch shape (same FETCH / WRITE runs and scales)\n")
+    fa, wa = by_grid(fetch_dir, "FETCH_SIZE", "attend_kernel"), by_grid(write_dir, "WRITE_SIZE", "attend_kernel")
+    for grid in sorted(fa):
+        if grid in wa:
+            print(f"- grid {grid} threads: FETCH {fa[grid][0] * 1024 * f_scale:.0f} B, "
+                  f"WRITE {wa[grid][0] * 1024 * w_scale:.0f} B per dispatch (means of {fa[grid][2]})")
+    if mfma_dir:
+        print("\n### MFMA work of attend_kernel (rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16)\n")
+        mo = by_grid(mfma_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16", "attend_kernel")
+        for grid in sorted(mo):
+            flops, ns, n = mo[grid][0] * 512, mo[grid][1], mo[grid][2]
+            print(f"- grid {grid} threads: {flops:.4g} bf16 MFMA flop per dispatch, {ns / 1e3:.1f} us per dispatch "
+                  f"under counter collection -> {flops / ns / 1e3:.2f} TFLOP/s = {flops / ns / 1e3 / MFMA_BF16_PEAK_TFLOPS:.4f} "
+                  f"of 2.5 PFLOP/s (means of {n})")
     return 0
 
 
@@ -219,7 +248,7 @@ def main():
     reps = max(10, args.steps)
     idx_med, idx_avg = timed(do_index, reps)
     topk_med, _ = timed(do_topk, reps)
-    att_med, _ = timed(do_attend, reps)
+    att_med, att_avg = timed(do_attend, reps)
     do_reuse()
     reuse_med, _ = timed(do_reuse, reps)
 
@@ -231,6 +260,14 @@ def main():
     idx_bytes = B * N * 256 + T * (8192 + 128 + 16) + T * csa.tile_max_ld(N) * 4 + (T * N * 4 if rows else 0)
     achieved = idx_bytes / (idx_avg * 1e-6) / 1e9
     step_bytes = T * G.algorithmic_bytes_decode_query(N)
+
+    # the attention call (gather + dequant + attention, plus its merge): per
+    # query 512 FP4 rows (272 B), 128 window rows (1 KiB), q and out (64 KiB
+    # each), the indices (2 KiB); 2 x 64 heads x 640 rows x 512 x 2 flop
+    att_bytes = T * (512 * 272 + 128 * 1024 + 65536 + 65536 + 512 * 4)
+    att_flops = T * 2 * (2 * 64 * 640 * 512)
+    att_gbps = att_bytes / (att_avg * 1e-6) / 1e9
+    att_tflops = att_flops / (att_avg * 1e-6) / 1e12
 
     # plain copy bandwidth of this machine (context for the roofline fraction)
     x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -269,6 +306,9 @@ def main():
                      "traffic": recorded_traffic() if args.workload == "long_decode" else None,
                      "algorithmic_bytes_per_launch": idx_bytes, "avg_launch_us": idx_avg},
         "stages_us": {"index": idx_med, "topk": topk_med, "attend": att_med, "reuse_3_layers": reuse_med},
+        "attention": {"call": "csa2_attend_fp4 (attend + merge kernels)", "avg_us": att_avg,
+                      "algorithmic_bytes": att_bytes, "GBps": att_gbps, "frac_hbm": att_gbps / HBM_PEAK_GBPS,
+                      "flops": att_flops, "TFLOPs": att_tflops, "frac_mfma_bf16": att_tflops / MFMA_BF16_PEAK_TFLOPS},
         "copy_GBps": copy_gbps,
     }
 
