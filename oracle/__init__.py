@@ -5,7 +5,7 @@ ctypes wrapper over numpy arrays.  Only the tests, ``__graft_entry__.smoke()``
 and the CPU-baseline leg of ``bench.py`` may import this package; the product
 library never does.  It shares no code with the HIP library.
 
-Functions follow the DeepSeek-V4.1-Flash report (sec. 2.3, 2.3.1, 2.4.4,
+Functions follow the DeepSeek-V4.1-Flash report (sec. 2.3, 2.3.1, 2.3.2, 2.4.4,
 3.2.2, 4.2.1) and the gzher.com reading of DeepSeek-V4 (sec. 4.1, 4.3); the
 C source cites the passage for each step.
 """
@@ -56,6 +56,9 @@ def lib():
         L.csa2o_topk.argtypes, L.csa2o_topk.restype = [vp, vp, i32, i32, i64, i32, vp], None
         L.csa2o_attend.argtypes = [vp, vp, vp, vp, vp, vp, vp, dbl, i32, i32, i64, i32, i32, i32, vp, vp]
         L.csa2o_attend.restype = None
+        L.csa2o_hsi_pool_row.argtypes, L.csa2o_hsi_pool_row.restype = [vp, i64, i32, i32, vp], i32
+        L.csa2o_hsi_pool.argtypes, L.csa2o_hsi_pool.restype = [vp, vp, i32, i32, i64, i32, i32, vp], None
+        L.csa2o_reindex_topk.argtypes, L.csa2o_reindex_topk.restype = [vp, vp, i32, i64, i64, i32, vp], None
         _lib = L
     return _lib
 
@@ -129,6 +132,30 @@ def topk(scores, q_pos, ratio, k):
     qp = None if q_pos is None else _c(q_pos, np.int32)
     out = np.empty((T, k), np.int32)
     lib().csa2o_topk(_ptr(scores), _ptr(qp), ratio, T, N, k, _ptr(out))
+    return out
+
+
+HSI_BLOCK, HSI_BLOCKS = 8, 2048  # report sec. 4.2.1: at most 2048 blocks of 8 positions
+
+
+def hsi_pool(scores, q_pos, ratio, block=HSI_BLOCK, n_blocks=HSI_BLOCKS):
+    """Candidate pool of the hierarchical sparse indexer (report sec. 2.3.2):
+    scores float64 [T][N] (a Full layer's) -> int32 [T][n_blocks*block], ascending, -1 padded."""
+    scores = _c(scores, np.float64)
+    T, N = scores.shape
+    qp = None if q_pos is None else _c(q_pos, np.int32)
+    out = np.empty((T, n_blocks * block), np.int32)
+    lib().csa2o_hsi_pool(_ptr(scores), _ptr(qp), ratio, T, N, block, n_blocks, _ptr(out))
+    return out
+
+
+def reindex_topk(scores, pool, k):
+    """Reindex selection (report sec. 2.3.2): top-k of the pool entries by (score desc,
+    index asc); scores float64 [T][N] (the Reindex layer's), pool int32 [T][P] -> int32 [T][k]."""
+    scores, pool = _c(scores, np.float64), _c(pool, np.int32)
+    T, N = scores.shape
+    out = np.empty((T, k), np.int32)
+    lib().csa2o_reindex_topk(_ptr(scores), _ptr(pool), T, N, pool.shape[1], k, _ptr(out))
     return out
 
 

@@ -167,6 +167,79 @@ void csa2o_topk(const double* scores, const int32_t* q_pos, int32_t ratio, int32
     }
 }
 
+/* ---- hierarchical sparse indexer (candidate pool) and Reindex -------------- */
+
+/* DeepSeek-V4.1-Flash report sec. 2.3.2: the first Full layer also selects
+ * blocks; each block gets the maximum index score among its positions, the
+ * highest-scoring blocks are kept, and the positions they cover form the
+ * candidate pool (sec. 4.2.1: at most 2048 blocks of 8 positions, 16384
+ * candidates).  Readings: blocks are the aligned runs [block*b, block*b+block)
+ * of compressed entries; only visible entries count toward a block's score and
+ * its share of the pool; ties between block scores go to the lower block;
+ * the pool is written ascending and padded with -1.  Returns the pool size. */
+int32_t csa2o_hsi_pool_row(const double* scores, int64_t n_vis, int32_t block, int32_t n_blocks, int32_t* pool) {
+    int64_t nb = (n_vis + block - 1) / block;
+    scored_t* blk = (scored_t*)malloc((size_t)(nb > 0 ? nb : 1) * sizeof(scored_t));
+    for (int64_t b = 0; b < nb; ++b) {
+        double m = -INFINITY;
+        for (int64_t e = b * block; e < (b + 1) * block && e < n_vis; ++e)
+            if (scores[e] > m) m = scores[e];
+        blk[b].score = m;
+        blk[b].idx = b;
+    }
+    qsort(blk, (size_t)nb, sizeof(scored_t), cmp_score_desc_idx_asc);
+    int64_t n_sel = nb < n_blocks ? nb : n_blocks;
+    int32_t* sel = (int32_t*)malloc((size_t)(n_sel > 0 ? n_sel : 1) * sizeof(int32_t));
+    for (int64_t j = 0; j < n_sel; ++j) sel[j] = (int32_t)blk[j].idx;
+    qsort(sel, (size_t)n_sel, sizeof(int32_t), cmp_i32);
+    int32_t cnt = 0;
+    for (int64_t j = 0; j < n_sel; ++j)
+        for (int64_t e = (int64_t)sel[j] * block; e < ((int64_t)sel[j] + 1) * block && e < n_vis; ++e) pool[cnt++] = (int32_t)e;
+    for (int64_t j = cnt; j < (int64_t)n_blocks * block; ++j) pool[j] = -1;
+    free(sel);
+    free(blk);
+    return cnt;
+}
+
+void csa2o_hsi_pool(const double* scores, const int32_t* q_pos, int32_t ratio, int32_t T, int64_t N,
+                    int32_t block, int32_t n_blocks, int32_t* pool) {
+    const int64_t P = (int64_t)n_blocks * block;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t t = 0; t < T; ++t) {
+        int64_t n_vis = q_pos ? csa2o_n_visible(q_pos[t], ratio, N) : N;
+        csa2o_hsi_pool_row(scores + (int64_t)t * N, n_vis, block, n_blocks, pool + (int64_t)t * P);
+    }
+}
+
+/* Report sec. 2.3.2: a Reindex layer scores only the pool positions of its
+ * query (with its own indexer query, over the shared keys, sec. 2.3) and
+ * selects its own top-k within the pool, by (score desc, index asc), written
+ * ascending and padded with -1.  scores: the Reindex layer's scores of all
+ * entries of the row (only pool entries are read). */
+void csa2o_reindex_topk(const double* scores, const int32_t* pool, int32_t T, int64_t N, int64_t P, int32_t k,
+                        int32_t* out) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t t = 0; t < T; ++t) {
+        const int32_t* pl = pool + (int64_t)t * P;
+        const double* row = scores + (int64_t)t * N;
+        scored_t* cand = (scored_t*)malloc((size_t)(P > 0 ? P : 1) * sizeof(scored_t));
+        int64_t n = 0;
+        for (int64_t j = 0; j < P; ++j)
+            if (pl[j] >= 0) {
+                cand[n].score = row[pl[j]];
+                cand[n].idx = pl[j];
+                ++n;
+            }
+        qsort(cand, (size_t)n, sizeof(scored_t), cmp_score_desc_idx_asc);
+        int32_t n_sel = (int64_t)k < n ? k : (int32_t)n;
+        int32_t* o = out + (int64_t)t * k;
+        for (int32_t j = 0; j < n_sel; ++j) o[j] = (int32_t)cand[j].idx;
+        qsort(o, (size_t)n_sel, sizeof(int32_t), cmp_i32);
+        for (int32_t j = n_sel; j < k; ++j) o[j] = -1;
+        free(cand);
+    }
+}
+
 /* ---- attention ----------------------------------------------------------- */
 
 /* V4 reading sec. 4.1: shared-KV MQA, the selected compressed entry is both

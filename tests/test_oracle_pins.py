@@ -371,3 +371,100 @@ def test_reuse_is_attention_with_new_query(oracle_lib):
     other, _ = oracle_lib.attend(c.q[1].numpy().view(np.uint16), *args, c.swa[1].numpy().view(np.uint16),
                                  c.swa_end.numpy(), None, 0.04, 1, 8)
     assert np.array_equal(full, again) and not np.allclose(full, other)
+
+
+# ---- hierarchical sparse indexer (candidate pool) and Reindex, report sec. 2.3.2
+
+def test_hsi_pool_hand_example(oracle_lib):
+    import oracle
+    row = np.zeros(27, np.float64)
+    row[[3, 9, 14, 20, 24, 26]] = [5, 7, 7, 5, -1, 6]
+    for r in _golden("hsi_pool_example.txt"):
+        n_vis, n_blocks = int(r[0]), int(r[1])
+        want = [int(x) for x in r[3:]]
+        out = np.empty(n_blocks * 8, np.int32)
+        cnt = oracle.lib().csa2o_hsi_pool_row(oracle._ptr(row), n_vis, 8, n_blocks, oracle._ptr(out))
+        assert cnt == len(want) and list(out[:cnt]) == want and np.all(out[cnt:] == -1), (n_vis, n_blocks)
+
+
+def _pool_brute(row, n_vis, block, n_blocks):
+    """Independent loops: block scores, then blocks ranked by (score desc, block asc)."""
+    nb = -(-n_vis // block)
+    best = []
+    for b in range(nb):
+        m = max(row[e] for e in range(b * block, min(b * block + block, n_vis)))
+        best.append((-m, b))
+    chosen = sorted(b for _, b in sorted(best)[:n_blocks])
+    return [e for b in chosen for e in range(b * block, min(b * block + block, n_vis))]
+
+
+def test_hsi_pool_brute_force_small(oracle_lib):
+    import oracle
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        N = int(rng.integers(1, 200))
+        n_blocks = int(rng.integers(1, 12))
+        # coarse values so that block scores tie often
+        s = rng.integers(-3, 4, size=(3, N)).astype(np.float64)
+        q_pos = np.array([N - 1, int(rng.integers(-1, N)), int(rng.integers(0, 2 * N))], np.int32)
+        pool = oracle.hsi_pool(s, q_pos, 1, 8, n_blocks)
+        for t in range(3):
+            nv = max(0, min(N, int(q_pos[t]) + 1))
+            want = _pool_brute(s[t], nv, 8, n_blocks) if nv else []
+            got = pool[t][pool[t] >= 0]
+            assert list(got) == want and np.all(pool[t][len(want):] == -1), (trial, t)
+
+
+def test_hsi_pool_small_rows_are_everything(oracle_lib):
+    import oracle
+    rng = np.random.default_rng(6)
+    s = rng.standard_normal((2, 16384))
+    pool = oracle.hsi_pool(s, np.array([16383, 9000], np.int32), 1)
+    assert np.array_equal(pool[0], np.arange(16384))
+    assert np.array_equal(pool[1][:9001], np.arange(9001)) and np.all(pool[1][9001:] == -1)
+
+
+def test_hsi_pool_planted_blocks(oracle_lib):
+    import oracle
+    rng = np.random.default_rng(7)
+    N = 50000
+    s = rng.standard_normal((1, N))
+    planted = [17, 900, 3000, 6249]
+    for b in planted:
+        s[0, 8 * b + int(rng.integers(0, 8))] = 100.0 + b
+    pool = oracle.hsi_pool(s, None, 1, 8, len(planted))
+    want = [e for b in sorted(planted) for e in range(8 * b, 8 * b + 8)]
+    assert list(pool[0][pool[0] >= 0]) == want
+
+
+def test_reindex_with_full_query_reproduces_full_topk(oracle_lib):
+    """The pool contains every block holding a Full top-k entry (at most k <= 2048 blocks,
+    and each of them outranks every block without one), so a Reindex layer that scored
+    with the Full layer's own query would select exactly the Full top-k."""
+    import oracle
+    rng = np.random.default_rng(8)
+    for N, ties in [(40000, False), (30000, True), (20000, True)]:
+        s = rng.standard_normal((3, N))
+        if ties:
+            s = np.round(s, 1)  # many equal scores, also across block boundaries
+        q_pos = np.array([N - 1, N // 2, 16000], np.int32)
+        full = oracle.topk(s, q_pos, 1, 512)
+        pool = oracle.hsi_pool(s, q_pos, 1)
+        for t in range(3):
+            assert set(full[t][full[t] >= 0]) <= set(pool[t][pool[t] >= 0])
+        assert np.array_equal(oracle.reindex_topk(s, pool, 512), full)
+
+
+def test_reindex_topk_brute_force(oracle_lib):
+    import oracle
+    rng = np.random.default_rng(9)
+    N, k = 3000, 64
+    s_full = rng.standard_normal((2, N))
+    s_re = np.round(rng.standard_normal((2, N)), 1)
+    pool = oracle.hsi_pool(s_full, None, 1, 8, 40)
+    got = oracle.reindex_topk(s_re, pool, k)
+    for t in range(2):
+        cand = [int(e) for e in pool[t] if e >= 0]
+        want = sorted(sorted(cand, key=lambda e: (-s_re[t, e], e))[:k])
+        assert list(got[t][:len(want)]) == want and np.all(got[t][len(want):] == -1)
+        assert set(want) <= set(cand)
