@@ -18,11 +18,14 @@ __all__ = [
     "Csa2Error", "IndexResult", "lib", "library_path", "csa2_index", "csa2_topk", "csa2_attend_fp4",
     "csa2_reuse_attend", "tile_max_ld", "index_stats_bytes", "topk_workspace_bytes", "topk_min_workspace_bytes",
     "attend_workspace_bytes", "IDX_HEADS", "IDX_DIM", "HEADS", "DIM", "TOPK", "MAX_WINDOW", "MAX_LAYERS", "TILE",
-    "TOPK_ROW_MAX", "STATS_WORDS",
+    "TOPK_ROW_MAX", "STATS_WORDS", "csa2_hsi_pool", "csa2_reindex", "hsi_pool_workspace_bytes",
+    "reindex_workspace_bytes", "HSI_BLOCK", "HSI_BLOCKS", "HSI_POOL",
 ]
 
 IDX_HEADS, IDX_DIM, HEADS, DIM, TOPK, MAX_WINDOW, MAX_LAYERS = 32, 128, 64, 512, 512, 128, 8
 TILE, TOPK_ROW_MAX, STATS_WORDS = 16, 36864, 4
+HSI_BLOCK, HSI_BLOCKS = 8, 2048
+HSI_POOL = HSI_BLOCK * HSI_BLOCKS
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libcsa2.so")
@@ -40,6 +43,10 @@ _SIGNATURES = {
     "csa2_topk_min_workspace_bytes": ([_i32, _i64, _i32], _sz),
     "csa2_topk": ([_vp, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp, _vp, _sz, _vp],
                   _i32),
+    "csa2_hsi_pool_workspace_bytes": ([_i32, _i64], _sz),
+    "csa2_hsi_pool": ([_vp, _vp, _sz, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _sz, _vp], _i32),
+    "csa2_reindex_workspace_bytes": ([_i32, _i32], _sz),
+    "csa2_reindex": ([_vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _vp, _vp, _sz, _vp], _i32),
     "csa2_attend_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
     "csa2_attend_fp4": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp,
                          _vp, _sz, _vp], _i32),
@@ -164,6 +171,14 @@ def topk_min_workspace_bytes(T: int, N: int, k: int = TOPK) -> int:
     return lib().csa2_topk_min_workspace_bytes(T, N, k)
 
 
+def hsi_pool_workspace_bytes(T: int, N: int) -> int:
+    return lib().csa2_hsi_pool_workspace_bytes(T, N)
+
+
+def reindex_workspace_bytes(T: int, k: int = TOPK) -> int:
+    return lib().csa2_reindex_workspace_bytes(T, k)
+
+
 def attend_workspace_bytes(T: int, k: int = TOPK, window: int = MAX_WINDOW, n_layers: int = 1) -> int:
     return lib().csa2_attend_workspace_bytes(T, k, window, n_layers)
 
@@ -226,6 +241,56 @@ def csa2_topk(scores, tile_max, stats, q_idx, w_idx, k_idx, q_pos=None, ratio=1,
                          _p(q_pos), ratio, T, q_per_seq, N, k, _p(indices), _p(workspace), _nbytes(workspace),
                          _stream(q_idx))
     _raise(st, "csa2_topk")
+    return indices
+
+
+def csa2_hsi_pool(tile_max, stats, q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, pool=None,
+                  workspace=None):
+    """Candidate pool of a Full layer (hierarchical sparse indexer) -> int32 [T][HSI_POOL]:
+    the visible entries of its top HSI_BLOCKS blocks of HSI_BLOCK entries, ascending, -1 padded.
+    tile_max and stats are csa2_index's outputs for the same arguments (stats is only read)."""
+    T = q_idx.shape[0]
+    B, N = k_idx.shape[0], k_idx.shape[1]
+    dev = q_idx.device
+    _check(tile_max, "tile_max", (T, tile_max_ld(N)), dtype=torch.float32, device=dev)
+    _check_stats(stats, T, q_per_seq, N, dev)
+    _check(q_idx, "q_idx", (T, IDX_HEADS, IDX_DIM), elem_size=2, device=dev)
+    _check(w_idx, "w_idx", (T, IDX_HEADS), dtype=torch.float32, device=dev)
+    _check(k_idx, "k_idx", (B, N, IDX_DIM), elem_size=2, device=dev)
+    if q_pos is not None:
+        _check(q_pos, "q_pos", (T,), dtype=torch.int32, device=dev)
+    if B * q_per_seq != T:
+        raise ValueError(f"T={T} must equal B*q_per_seq={B}*{q_per_seq}")
+    if pool is None:
+        pool = torch.empty((T, HSI_POOL), dtype=torch.int32, device=dev)
+    _check(pool, "pool", (T, HSI_POOL), dtype=torch.int32, device=dev)
+    workspace = _ws(hsi_pool_workspace_bytes(T, N), dev, workspace)
+    st = lib().csa2_hsi_pool(_p(tile_max), _p(stats), stats.numel() * 4, _p(q_idx), _p(w_idx), _p(k_idx),
+                             _p(q_pos), ratio, T, q_per_seq, N, _p(pool), _p(workspace), _nbytes(workspace),
+                             _stream(q_idx))
+    _raise(st, "csa2_hsi_pool")
+    return pool
+
+
+def csa2_reindex(pool, q_idx, w_idx, k_idx, q_per_seq=1, k=TOPK, indices=None, workspace=None):
+    """Reindex selection: top-k of each query's pool entries by its own indexer query
+    (ascending entry ids, -1 padded) -> int32 [T][k]."""
+    T = q_idx.shape[0]
+    B, N = k_idx.shape[0], k_idx.shape[1]
+    dev = q_idx.device
+    _check(pool, "pool", (T, HSI_POOL), dtype=torch.int32, device=dev)
+    _check(q_idx, "q_idx", (T, IDX_HEADS, IDX_DIM), elem_size=2, device=dev)
+    _check(w_idx, "w_idx", (T, IDX_HEADS), dtype=torch.float32, device=dev)
+    _check(k_idx, "k_idx", (B, N, IDX_DIM), elem_size=2, device=dev)
+    if B * q_per_seq != T:
+        raise ValueError(f"T={T} must equal B*q_per_seq={B}*{q_per_seq}")
+    if indices is None:
+        indices = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _check(indices, "indices", (T, k), dtype=torch.int32, device=dev)
+    workspace = _ws(reindex_workspace_bytes(T, k), dev, workspace)
+    st = lib().csa2_reindex(_p(pool), _p(q_idx), _p(w_idx), _p(k_idx), T, q_per_seq, N, k, _p(indices),
+                            _p(workspace), _nbytes(workspace), _stream(q_idx))
+    _raise(st, "csa2_reindex")
     return indices
 
 

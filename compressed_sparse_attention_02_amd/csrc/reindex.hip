@@ -1,0 +1,134 @@
+// Reindex selection (csa2_reindex).
+//
+// A Reindex layer (report sec. 2.3.2) scores only the candidate pool the
+// preceding Full layer left for its query, with its own indexer query over the
+// shared indexer keys, and keeps its own top-k within the pool.  The pool rows
+// are gathered into a contiguous key block per query (zero rows past the pool's
+// end), which turns the call into the regular scan and the row-regime
+// selection over P = CSA2_HSI_POOL keys per "sequence" of one query, with the
+// pool size as the visible count; the selected pool positions are mapped back
+// to entry ids.  The pool is ascending, so position order is entry order: the
+// tie rule (lower index first) and the ascending output carry over unchanged,
+// and the fp64 scores are those of the original rows (same bf16 values, same
+// operation order).
+#include "csa2_common.h"
+
+namespace csa2 {
+
+constexpr int kPool = CSA2_HSI_POOL;
+constexpr int kGatherThreads = 256;
+constexpr int kGatherRows = 64;                          // pool rows per block
+constexpr int kRowVecs = kIdxDim * 2 / 16;               // 16-byte vectors per key row (16)
+
+struct ReindexWs {
+  uint16_t* keys;    // [T][kPool][128] gathered keys
+  int32_t* qpos;     // [T]: pool size - 1
+  float* scores;     // [T][kPool]
+  float* tile_max;   // [T][tile_ld]
+  uint32_t* stats;   // csa2_index summary for (T, 1, kPool)
+  int32_t* pos;      // [T][k] selected pool positions
+  size_t stats_bytes;
+};
+
+static ReindexWs reindex_ws(void* base, int T, int k, size_t* total) {
+  ReindexWs w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const uintptr_t p = (uintptr_t)base + off;
+    off += align_up(bytes, 256);
+    return (void*)p;
+  };
+  w.keys = (uint16_t*)take((size_t)T * kPool * kIdxDim * 2);
+  w.qpos = (int32_t*)take((size_t)T * 4);
+  w.scores = (float*)take((size_t)T * kPool * 4);
+  w.tile_max = (float*)take((size_t)T * (size_t)csa2_tile_max_ld(kPool) * 4);
+  w.stats_bytes = csa2_index_stats_bytes(T, 1, kPool);
+  w.stats = (uint32_t*)take(w.stats_bytes);
+  w.pos = (int32_t*)take((size_t)T * k * 4);
+  *total = off;
+  return w;
+}
+
+// Block (x, t): pool rows [x*64, x*64+64) of query t into keys[t]; zeros for
+// pad slots (-1).  Block (0, t) also writes qpos[t] = (number of pool entries) - 1.
+__global__ __launch_bounds__(kGatherThreads) void reindex_gather_kernel(const int32_t* __restrict__ pool,
+                                                                        const uint16_t* __restrict__ k_idx,
+                                                                        int q_per_seq, int64_t N,
+                                                                        uint16_t* __restrict__ keys,
+                                                                        int32_t* __restrict__ qpos) {
+  const int t = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int32_t* pl = pool + (size_t)t * kPool;
+  const uint4* kseq = reinterpret_cast<const uint4*>(k_idx + (size_t)(t / q_per_seq) * N * kIdxDim);
+  uint4* dst = reinterpret_cast<uint4*>(keys + ((size_t)t * kPool + (size_t)blockIdx.x * kGatherRows) * kIdxDim);
+  const int r0 = blockIdx.x * kGatherRows;
+#pragma unroll
+  for (int u = 0; u < kGatherRows * kRowVecs / kGatherThreads; ++u) {
+    const int i = u * kGatherThreads + tid;
+    const int r = i / kRowVecs, c = i % kRowVecs;
+    const int32_t e = pl[r0 + r];
+    dst[i] = e >= 0 ? kseq[(size_t)e * kRowVecs + c] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (blockIdx.x == 0) {
+    __shared__ uint32_t part[kGatherThreads / 64];
+    uint32_t n = 0;
+    for (int i = tid; i < kPool; i += kGatherThreads) n += pl[i] >= 0 ? 1u : 0u;
+    n = wave_sum_u32_dpp(n);
+    if ((tid & 63) == 0) part[tid >> 6] = n;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t s = 0;
+      for (int i = 0; i < kGatherThreads / 64; ++i) s += part[i];
+      qpos[t] = (int32_t)s - 1;
+    }
+  }
+}
+
+// indices[t][j] = pool[t][pos[t][j]] (-1 stays -1).
+__global__ __launch_bounds__(256) void reindex_map_kernel(const int32_t* __restrict__ pool,
+                                                          const int32_t* __restrict__ pos, int k,
+                                                          int32_t* __restrict__ indices) {
+  const int t = blockIdx.x;
+  for (int j = threadIdx.x; j < k; j += blockDim.x) {
+    const int32_t p = pos[(size_t)t * k + j];
+    indices[(size_t)t * k + j] = p >= 0 ? pool[(size_t)t * kPool + p] : -1;
+  }
+}
+
+}  // namespace csa2
+
+using namespace csa2;
+
+extern "C" size_t csa2_reindex_workspace_bytes(int32_t T, int32_t k) {
+  if (T < 1 || T > 65535 || k != kTopK) return 0;
+  size_t total;
+  reindex_ws(nullptr, T, k, &total);
+  return total;
+}
+
+extern "C" csa2_status csa2_reindex(const int32_t* pool, const void* q_idx, const float* w_idx, const void* k_idx,
+                                    int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices,
+                                    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!pool || !q_idx || !w_idx || !k_idx || !indices) return CSA2_ERR_INVALID_ARG;
+  if (!aligned16(pool) || !aligned16(q_idx) || !aligned16(w_idx) || !aligned16(k_idx) || !aligned16(indices))
+    return CSA2_ERR_INVALID_ARG;
+  if (T < 1 || q_per_seq < 1 || T % q_per_seq != 0 || N < 1) return CSA2_ERR_INVALID_ARG;
+  if (k != kTopK || N >= ((int64_t)1 << 31) || T > 65535) return CSA2_ERR_UNSUPPORTED;
+  size_t need;
+  ReindexWs w = reindex_ws(workspace, T, k, &need);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)hip_stream;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(reindex_gather_kernel, dim3(kPool / kGatherRows, T), dim3(kGatherThreads), 0, st, pool,
+                     (const uint16_t*)k_idx, q_per_seq, N, w.keys, w.qpos);
+  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
+  csa2_status s = csa2_index(q_idx, w_idx, w.keys, w.qpos, 1, T, 1, kPool, w.scores, w.tile_max, w.stats,
+                             w.stats_bytes, hip_stream);
+  if (s != CSA2_OK) return s;
+  s = csa2_topk(w.scores, w.tile_max, w.stats, w.stats_bytes, q_idx, w_idx, w.keys, w.qpos, 1, T, 1, kPool, k,
+                w.pos, nullptr, 0, hip_stream);
+  if (s != CSA2_OK) return s;
+  hipLaunchKernelGGL(reindex_map_kernel, dim3(T), dim3(256), 0, st, pool, w.pos, k, indices);
+  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
+  return CSA2_OK;
+}

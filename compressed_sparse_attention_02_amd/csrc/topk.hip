@@ -591,26 +591,31 @@ struct alignas(16) FloorLds {
   uint32_t res;
 };
 
-// Query t (grid T, kFloorThreads threads): stats[t] = {eps, tau, 0, 0}.
-// tau: at least CSA2_TOPK visible fp32 scores are >= tau, because it bounds
-// from below the CSA2_TOPK-th largest of a set of maxima of disjoint groups of
-// entries (each maximum is a distinct visible entry); -inf when fewer than
-// CSA2_TOPK of those maxima are finite.  The maxima ranked are the tile maxima
+// Query t (grid T, kFloorThreads threads): stats[t] = {eps, tau} (words 0, 1).
+// tau: at least `rank` visible fp32 scores are >= tau, because it bounds from
+// below the rank-th largest of a set of maxima of disjoint groups of entries
+// (each maximum is a distinct visible entry -- and the maximum of a distinct
+// block of 8 entries, since groups are unions of 16-entry tiles); -inf when
+// fewer than `rank` of those maxima are finite or when the row has at most
+// `all_below` visible entries (everything is selected then).  The top-k uses
+// rank = all_below = CSA2_TOPK; the candidate pool rank = 2048 blocks and
+// all_below = 16384 entries.  The maxima ranked are the tile maxima
 // when the row has at most kFloorVals tiles, else the scan's group maxima (when
 // there are at least kGroupsWanted of them) or the tile maxima; past kFloorVals values
 // they are folded (value j is the maximum over j, j + kFloorVals, ...), and
 // folding unions groups, which keeps them disjoint.
 //
 // Ranking: each thread holds 16 of the maxima; the smallest per-thread
-// maximum L0 is already a valid lower bound when at least CSA2_TOPK threads
+// maximum L0 is already a valid lower bound when at least `rank` threads
 // hold one (that many distinct maxima reach it), so only values >= L0 enter a
 // histogram of 256 bins over [L0, max] that also keeps each bin's minimum.
-// The bins at and above the one holding the CSA2_TOPK-th largest hold at least
-// CSA2_TOPK values, and tau is the smallest of them.
+// The bins at and above the one holding the rank-th largest hold at least
+// `rank` values, and tau is the smallest of them.
 __global__ __launch_bounds__(kFloorThreads) void topk_floor_kernel(
     const float* __restrict__ tile_max, uint32_t* __restrict__ stats, const float* __restrict__ gmax,
     int64_t n_groups, const float* __restrict__ parts, int64_t n_parts, const uint16_t* __restrict__ q_idx,
-    const float* __restrict__ w_idx, const int32_t* __restrict__ q_pos, int ratio, int q_per_seq, int64_t N) {
+    const float* __restrict__ w_idx, const int32_t* __restrict__ q_pos, int ratio, int q_per_seq, int64_t N,
+    int rank, int64_t all_below) {
   __shared__ FloorLds F;
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -619,7 +624,7 @@ __global__ __launch_bounds__(kFloorThreads) void topk_floor_kernel(
   const int64_t ntv = (nv + kTileKeys - 1) / kTileKeys;
   const bool use_groups = ntv > kFloorVals && n_groups >= kGroupsWanted;
   const float* src = use_groups ? gmax + (size_t)t * n_groups : tile_max + (size_t)t * tile_ld(N);
-  const int64_t nsrc = nv > kTopK ? (use_groups ? n_groups : ntv) : 0;
+  const int64_t nsrc = nv > all_below ? (use_groups ? n_groups : ntv) : 0;
   // value j = src[j] (rows are 16-byte aligned: four per load)
   float v[kFloorPer];
 #pragma unroll
@@ -677,8 +682,8 @@ __global__ __launch_bounds__(kFloorThreads) void topk_floor_kernel(
     qf += F.dred[0][i]; sw += F.dred[1][i]; tfin += F.ured[i] & 0xFFFFu; tthr += F.ured[i] >> 16;
   }
   float tau = -INFINITY;
-  if (tfin >= (uint32_t)kTopK) {
-    const float lo = tthr >= (uint32_t)kTopK ? l0 : gmin;
+  if (tfin >= (uint32_t)rank) {
+    const float lo = tthr >= (uint32_t)rank ? l0 : gmin;
     const float scale = mx > lo ? 255.99f / (mx - lo) : 0.f;
 #pragma unroll
     for (int m = 0; m < kFloorPer; ++m) {
@@ -693,7 +698,7 @@ __global__ __launch_bounds__(kFloorThreads) void topk_floor_kernel(
       // lane owns bins 255-4*lane .. 252-4*lane (descending); the bins at or
       // above the one holding the rank-th largest are those whose exclusive
       // count from the top is below rank
-      const uint32_t rank = (uint32_t)kTopK;
+      const uint32_t rk = (uint32_t)rank;
       uint32_t c[4], sum = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) { c[i] = F.hist[255 - 4 * lane - i]; sum += c[i]; }
@@ -706,7 +711,7 @@ __global__ __launch_bounds__(kFloorThreads) void topk_floor_kernel(
       uint32_t cum = incl - sum, kmin = 0xFFFFFFFFu;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (cum < rank) kmin = min(kmin, F.bmin[255 - 4 * lane - i]);
+        if (cum < rk) kmin = min(kmin, F.bmin[255 - 4 * lane - i]);
         cum += c[i];
       }
       kmin = wave_min_u32_dpp(kmin);
@@ -719,6 +724,87 @@ __global__ __launch_bounds__(kFloorThreads) void topk_floor_kernel(
     uint32_t* st = stats + (size_t)t * CSA2_STATS_WORDS;
     st[0] = __float_as_uint(bound_eps(m2, qf, sw));
     st[1] = __float_as_uint(tau);
+  }
+}
+
+// fp32 scores of candidate tiles ctile[0..n_tiles) (offsets from tile0) with
+// the scan's arithmetic; cmask[c] gets the entries of tile c that are visible
+// and reach thr.  Wave w takes tiles w, w + 4, ...; the rows of up to four of
+// its tiles are requested before any is scored.
+__device__ __forceinline__ void cand_tile_masks(const uint16_t* __restrict__ sq, const float* __restrict__ w,
+                                                const uint16_t* __restrict__ ctile, uint16_t* __restrict__ cmask,
+                                                uint32_t n_tiles, int64_t tile0, const uint16_t* __restrict__ kseq,
+                                                int64_t nv, double thr) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  constexpr int kWaves = kCandThreads / 64;
+  float wr[8];
+  load_head_weights(w, g, wr);
+  for (uint32_t c0 = wave; c0 < n_tiles; c0 += 4 * kWaves) {
+    uint4 kv[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t ci = c0 + u * kWaves;
+      if (ci < n_tiles) {
+        const int64_t s = (tile0 + ctile[ci]) * kTileKeys + col;
+        load_key_slices(kseq, s < nv ? s : nv - 1, g, kv[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t ci = c0 + u * kWaves;
+      if (ci >= n_tiles) break;
+      const int64_t s = (tile0 + ctile[ci]) * kTileKeys + col;
+      const float sc = tile_score(sq, kv[u], wr, col, g);
+      const uint64_t bal = __ballot(s < nv && (double)sc >= thr);
+      if (lane == 0) cmask[ci] = (uint16_t)(bal & 0xFFFFu);
+    }
+  }
+}
+
+// fp64 scores of entries eidx[0..n) in the reference's operation order: lane
+// (e = lane / 32, h = lane % 32) forms dot(q_h, K_e) with 128 sequential fmas,
+// then lane h == 0 folds the entry's 32 heads in order from LDS (hrel: this
+// wave's 64 doubles).  Two entries per wave and round; put(e, score) receives
+// each result.
+template <class Put>
+__device__ __forceinline__ void exact_entry_scores(const uint16_t* __restrict__ sq, const float* __restrict__ w,
+                                                   const uint32_t* __restrict__ eidx, uint32_t n,
+                                                   const uint16_t* __restrict__ kseq, double* hrel, Put put) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane & 31;
+  for (uint32_t e0 = 2 * wave; e0 < n; e0 += 2 * (kCandThreads / 64)) {
+    const uint32_t e = e0 + (lane >> 5);
+    const uint32_t ee = e < n ? e : e0;
+    const uint16_t* kr = kseq + (size_t)eidx[ee] * kIdxDim;
+    const uint16_t* qr = &sq[h * kQRowPad];
+    double d = 0.0;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const uint4 kq = *reinterpret_cast<const uint4*>(kr + 8 * i);
+      const uint4 qq = *reinterpret_cast<const uint4*>(qr + 8 * i);
+      const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
+      const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        d = fma((double)bf16lo(qw[c]), (double)bf16lo(kw[c]), d);
+        d = fma((double)bf16hi(qw[c]), (double)bf16hi(kw[c]), d);
+      }
+    }
+    hrel[lane] = d > 0.0 ? d : 0.0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (h == 0 && e < n) {
+      const double* hr = &hrel[lane & 32];
+      double sc = 0.0;
+#pragma unroll
+      for (int hh = 0; hh < kIdxHeads; ++hh) sc = fma((double)w[hh], hr[hh], sc);
+      put(e, sc);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -744,8 +830,7 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   __shared__ CandLds L;
   const int t = blockIdx.y;
   const int x = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, wave = tid >> 6;
   TileWs w = tile_ws(ws, T, N, cap);
   uint32_t* st = stats + (size_t)t * CSA2_STATS_WORDS;
   uint2* rec = w.table + (size_t)t * cand_blocks(N) + x;
@@ -772,35 +857,9 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   if (cand) L.ctile[p] = (uint16_t)tid;
   __syncthreads();
 
-  // 2. fp32 scores of the candidate tiles (the scan's arithmetic): wave w takes
-  //    tiles w, w + 4, ...; the rows of up to four of its tiles are requested
-  //    before any is scored
+  // 2. fp32 scores of the candidate tiles (the scan's arithmetic)
   const uint16_t* kseq = k_idx + (size_t)(t / q_per_seq) * N * kIdxDim;
-  {
-    float wr[8];
-    load_head_weights(L.w, g, wr);
-    constexpr int kWaves = kCandThreads / 64;
-    for (uint32_t c0 = wave; c0 < n_tiles; c0 += 4 * kWaves) {
-      uint4 kv[4][4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t ci = c0 + u * kWaves;
-        if (ci < n_tiles) {
-          const int64_t s = (tile0 + L.ctile[ci]) * kTileKeys + col;
-          load_key_slices(kseq, s < nv ? s : nv - 1, g, kv[u]);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t ci = c0 + u * kWaves;
-        if (ci >= n_tiles) break;
-        const int64_t s = (tile0 + L.ctile[ci]) * kTileKeys + col;
-        const float sc = tile_score(L.sq, kv[u], wr, col, g);
-        const uint64_t bal = __ballot(s < nv && (double)sc >= thr);
-        if (lane == 0) L.cmask[ci] = (uint16_t)(bal & 0xFFFFu);
-      }
-    }
-  }
+  cand_tile_masks(L.sq, L.w, L.ctile, L.cmask, n_tiles, tile0, kseq, nv, thr);
   __syncthreads();
 
   // 3. output slots in (tile, entry) order: thread ci expands candidate tile ci
@@ -825,46 +884,8 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   }
   __syncthreads();
 
-  // 4. fp64 scores of the passing entries, reference operation order:
-  //    lane (e = lane / 32, h = lane % 32) forms dot(q_h, K_e) with 128
-  //    sequential fmas, then the wave folds the 32 heads in order.
-  {
-    const int h = lane & 31;
-    for (uint32_t e0 = 2 * wave; e0 < n_pass; e0 += 2 * (kCandThreads / 64)) {
-      const uint32_t e = e0 + (lane >> 5);
-      const uint32_t ee = e < n_pass ? e : e0;
-      const uint16_t* kr = kseq + (size_t)L.eidx[ee] * kIdxDim;
-      const uint16_t* qr = &L.sq[h * kQRowPad];
-      double d = 0.0;
-#pragma unroll 4
-      for (int i = 0; i < 16; ++i) {
-        const uint4 kq = *reinterpret_cast<const uint4*>(kr + 8 * i);
-        const uint4 qq = *reinterpret_cast<const uint4*>(qr + 8 * i);
-        const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
-        const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          d = fma((double)bf16lo(qw[c]), (double)bf16lo(kw[c]), d);
-          d = fma((double)bf16hi(qw[c]), (double)bf16hi(kw[c]), d);
-        }
-      }
-      // the heads are folded in order by lane h == 0 of each entry, from LDS
-      L.hrel[wave][lane] = d > 0.0 ? d : 0.0;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      if (h == 0 && e < n_pass) {
-        const double* hr = &L.hrel[wave][lane & 32];
-        double sc = 0.0;
-#pragma unroll
-        for (int hh = 0; hh < kIdxHeads; ++hh) sc = fma((double)L.w[hh], hr[hh], sc);
-        L.escore[e] = sc;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-  }
+  // 4. fp64 scores of the passing entries, reference operation order
+  exact_entry_scores(L.sq, L.w, L.eidx, n_pass, kseq, L.hrel[wave], [&](uint32_t e, double sc) { L.escore[e] = sc; });
   __syncthreads();
 
   // 5. the block's fixed slots, or a reserved run of shared ones, and copy out
@@ -1335,6 +1356,284 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   if (tid == 0) st[2] = 0u;
 }
 
+// ======================================== hierarchical sparse indexer: pool
+
+// Report sec. 2.3.2 (and sec. 4.2.1 for the sizes): blocks of 8 entries get
+// the maximum score of their visible entries; the first 2048 blocks in the
+// order (fp64 block score desc, block asc) are kept and their visible entries,
+// ascending, are the candidate pool.  The fp32 scores decide only which blocks
+// are examined: with tau a floor (at least 2048 blocks have an fp32 maximum
+// >= tau), every block that can be kept has an fp64 maximum >= tau - eps,
+// reached by an entry whose fp32 score is >= tau - 2 eps.  So the fp64
+// maximum over the entries that reach tau - 2 eps equals the true fp64 block
+// score of every block that can be kept, and is below the 2048th block score
+// for every other block: ranking blocks by it gives the exact selection.
+constexpr int kHsiBlock = CSA2_HSI_BLOCK;                        // 8
+constexpr int kHsiBlocks = CSA2_HSI_BLOCKS;                      // 2048
+constexpr int kHsiPool = kHsiBlock * kHsiBlocks;                 // 16384
+constexpr int kHsiPerCand = kCandTiles * kTileKeys / kHsiBlock;  // 512 blocks per candidate block
+
+// Workspace of the pool, per query: {eps, tau, -, -}, one record count per
+// candidate block and kHsiPerCand fixed records (block, fp64 maximum) each.
+struct HsiWs {
+  uint32_t* hdr;     // [T][4]
+  uint32_t* count;   // [T][nblk]
+  uint32_t* rblk;    // [T][nblk][kHsiPerCand]
+  double* rmax;      // [T][nblk][kHsiPerCand]
+};
+__host__ __device__ __forceinline__ size_t hsi_ws_bytes(int T, int64_t N) {
+  const size_t nb = (size_t)cand_blocks(N);
+  return align_up((size_t)T * 16, 256) + align_up((size_t)T * nb * 4, 256) +
+         align_up((size_t)T * nb * kHsiPerCand * 4, 256) + (size_t)T * nb * kHsiPerCand * 8;
+}
+__device__ __forceinline__ HsiWs hsi_ws(void* base, int T, int64_t N) {
+  const size_t nb = (size_t)cand_blocks(N);
+  HsiWs w;
+  char* p = (char*)base;
+  w.hdr = (uint32_t*)p;
+  p += align_up((size_t)T * 16, 256);
+  w.count = (uint32_t*)p;
+  p += align_up((size_t)T * nb * 4, 256);
+  w.rblk = (uint32_t*)p;
+  p += align_up((size_t)T * nb * kHsiPerCand * 4, 256);
+  w.rmax = (double*)p;
+  return w;
+}
+
+struct alignas(16) HsiCandLds {
+  uint16_t sq[kIdxHeads * kQRowPad];
+  float w[kIdxHeads];
+  uint32_t wsum[2][kCandThreads / 64];
+  uint32_t total;
+  uint16_t ctile[kCandTiles];
+  uint16_t cmask[kCandTiles];
+  uint32_t tpre[kCandTiles];               // passing entries before candidate tile c
+  uint32_t eidx[kCandMax];                 // one round of passing entries
+  unsigned long long bkey[kHsiPerCand];    // per block: largest fp64 key so far (0: none)
+  double hrel[kCandThreads / 64][64];
+};
+
+// Candidate blocks of tiles [x*kCandTiles, (x+1)*kCandTiles) of query t
+// (grid (nblk, T)): per block of 8 entries, the fp64 maximum over the entries
+// whose fp32 score reaches tau - 2 eps, written as records in block order.
+// Passing entries are scored in rounds of kCandMax, so that any number of
+// them (ties included) is handled.
+__global__ __launch_bounds__(kCandThreads, 4) void hsi_cand_kernel(
+    const float* __restrict__ tile_max, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
+    const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos, int ratio, int q_per_seq, int64_t N,
+    void* ws, int T) {
+  __shared__ HsiCandLds L;
+  const int t = blockIdx.y;
+  const int x = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int64_t nblk = cand_blocks(N);
+  HsiWs w = hsi_ws(ws, T, N);
+  uint32_t* cnt = w.count + (size_t)t * nblk + x;
+  const int64_t nv = n_visible(q_pos, t, ratio, N);
+  const int64_t ntv = (nv + kTileKeys - 1) / kTileKeys;
+  const int64_t tile0 = (int64_t)x * kCandTiles;
+  if (nv <= kHsiPool || tile0 >= ntv) {
+    if (tid == 0) *cnt = 0u;
+    return;
+  }
+  const int64_t my_tile = tile0 + tid;
+  const float tm = my_tile < ntv ? tile_max[(size_t)t * tile_ld(N) + my_tile] : -INFINITY;
+  const float eps = __uint_as_float(w.hdr[(size_t)t * 4]);
+  const float tau = __uint_as_float(w.hdr[(size_t)t * 4 + 1]);
+  stage_query(L.sq, q_idx + (size_t)t * kIdxHeads * kIdxDim, tid, kCandThreads);
+  if (tid < kIdxHeads) L.w[tid] = w_idx[(size_t)t * kIdxHeads + tid];
+  for (int i = tid; i < kHsiPerCand; i += kCandThreads) L.bkey[i] = 0ull;
+  const double thr = next_down((double)tau - 2.0 * (double)eps);
+
+  // candidate tiles in order, then their passing entries (fp32, the scan's arithmetic)
+  const bool cand = my_tile < ntv && (double)tm >= thr;
+  uint32_t n_tiles;
+  const uint32_t p = block_flag_scan(cand, L.wsum[0], &n_tiles);
+  if (cand) L.ctile[p] = (uint16_t)tid;
+  __syncthreads();
+  const uint16_t* kseq = k_idx + (size_t)(t / q_per_seq) * N * kIdxDim;
+  cand_tile_masks(L.sq, L.w, L.ctile, L.cmask, n_tiles, tile0, kseq, nv, thr);
+  __syncthreads();
+  const uint32_t mine = (uint32_t)tid < n_tiles ? (uint32_t)__popc((uint32_t)L.cmask[tid]) : 0u;
+  uint32_t n_pass;
+  const uint32_t pre = block_excl_scan(mine, L.wsum[1], &n_pass);
+  if ((uint32_t)tid < n_tiles) L.tpre[tid] = pre;
+  __syncthreads();
+
+  // rounds of passing entries: fp64 scores in the reference order, block maxima
+  const int64_t e_base = tile0 * kTileKeys;
+  for (uint32_t r0 = 0; r0 < n_pass; r0 += kCandMax) {
+    if ((uint32_t)tid < n_tiles) {
+      uint32_t m = L.cmask[tid];
+      uint32_t r = L.tpre[tid];
+      const int64_t e0 = (tile0 + L.ctile[tid]) * kTileKeys;
+      while (m && r < r0 + kCandMax) {
+        const int c = __ffs(m) - 1;
+        m &= m - 1;
+        if (r >= r0) L.eidx[r - r0] = (uint32_t)(e0 + c);
+        ++r;
+      }
+    }
+    __syncthreads();
+    const uint32_t n = n_pass - r0 < (uint32_t)kCandMax ? n_pass - r0 : (uint32_t)kCandMax;
+    exact_entry_scores(L.sq, L.w, L.eidx, n, kseq, L.hrel[wave], [&](uint32_t e, double sc) {
+      atomicMax(&L.bkey[(L.eidx[e] - (uint32_t)e_base) / kHsiBlock], (unsigned long long)f64_key(sc));
+    });
+    __syncthreads();
+  }
+
+  // records of the blocks that have a passing entry, in block order
+  uint32_t done = 0;
+  for (int i0 = 0; i0 < kHsiPerCand; i0 += kCandThreads) {
+    const int i = i0 + tid;
+    const unsigned long long key = L.bkey[i];
+    uint32_t tot;
+    const uint32_t q = done + block_flag_scan(key != 0ull, L.wsum[i0 / kCandThreads & 1], &tot);
+    if (key != 0ull) {
+      const size_t slot = ((size_t)t * nblk + x) * kHsiPerCand + q;
+      w.rblk[slot] = (uint32_t)(e_base / kHsiBlock) + (uint32_t)i;
+      w.rmax[slot] = key_f64(key);
+    }
+    done += tot;
+  }
+  if (tid == 0) *cnt = done;
+}
+
+// Order-preserving key of (fp64 block score, block index): larger is earlier
+// in the order (score desc, block asc).
+__device__ __forceinline__ void hsi_key(double v, uint32_t blk, unsigned long long* hi, uint32_t* lo) {
+  *hi = f64_key(v);
+  *lo = ~blk;
+}
+
+// Pool of query t (grid T, kSelThreads threads): over the records of all
+// candidate blocks, the 2048th block in the order (score desc, block asc) is
+// found by radix passes over the 96-bit keys (score key, ~block); the pool is
+// the visible entries of every block at or before it, ascending.
+__global__ __launch_bounds__(kSelThreads) void hsi_select_kernel(const int32_t* __restrict__ q_pos, int ratio,
+                                                                 int64_t N, void* ws, int T,
+                                                                 int32_t* __restrict__ pool) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wsum[2][kSelThreads / 64];
+  __shared__ uint32_t pick[3];
+  __shared__ unsigned long long found_hi;
+  __shared__ uint32_t found_lo;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t nv = n_visible(q_pos, t, ratio, N);
+  int32_t* out = pool + (size_t)t * kHsiPool;
+  if (nv <= kHsiPool) {  // every visible block is kept
+    for (int i = tid; i < kHsiPool; i += kSelThreads) out[i] = i < nv ? i : -1;
+    return;
+  }
+  const int64_t nblk = cand_blocks(N);
+  HsiWs w = hsi_ws(ws, T, N);
+  const uint32_t* cnt = w.count + (size_t)t * nblk;
+  const uint32_t* rb = w.rblk + (size_t)t * nblk * kHsiPerCand;
+  const double* rv = w.rmax + (size_t)t * nblk * kHsiPerCand;
+  // thread tid visits candidate blocks x = tid, tid + kSelThreads, ...; record j
+  // of block x is at [x * kHsiPerCand + j]
+
+  // radix passes: 8 bits at a time over the 96-bit key, most significant
+  // first, until the chosen bin holds a single record (that record is then
+  // the 2048th) or all 96 bits are fixed
+  unsigned long long pre_hi = 0, mask_hi = 0;
+  uint32_t pre_lo = 0, mask_lo = 0;
+  uint32_t rank = kHsiBlocks;  // rank (1-based, from the top) still to find among the keys with the prefix
+  for (int pass = 0; pass < 12; ++pass) {
+    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0u;
+    __syncthreads();
+    const int sh = pass < 8 ? 56 - 8 * pass : 24 - 8 * (pass - 8);
+    for (int64_t x = tid; x < nblk; x += kSelThreads) {
+      const uint32_t c = cnt[x];
+      for (uint32_t j = 0; j < c; ++j) {
+        unsigned long long hi;
+        uint32_t lo;
+        hsi_key(rv[x * kHsiPerCand + j], rb[x * kHsiPerCand + j], &hi, &lo);
+        if ((hi & mask_hi) == pre_hi && (lo & mask_lo) == pre_lo) {
+          const uint32_t d = pass < 8 ? (uint32_t)(hi >> sh) & 255u : (lo >> sh) & 255u;
+          atomicAdd(&hist[d], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < 64) {
+      uint32_t b, left;
+      wave_pick(hist, rank, &b, &left);
+      if (tid == 0) { pick[0] = b; pick[1] = left; pick[2] = hist[b]; }
+    }
+    __syncthreads();
+    const uint32_t d = pick[0];
+    rank = pick[1];
+    const bool single = pick[2] == 1u;
+    if (pass < 8) {
+      pre_hi |= (unsigned long long)d << sh;
+      mask_hi |= 255ull << sh;
+    } else {
+      pre_lo |= d << sh;
+      mask_lo |= 255u << sh;
+    }
+    __syncthreads();
+    if (single) {
+      // the one record with this prefix: its whole key
+      for (int64_t x = tid; x < nblk; x += kSelThreads) {
+        const uint32_t c = cnt[x];
+        for (uint32_t j = 0; j < c; ++j) {
+          unsigned long long hi;
+          uint32_t lo;
+          hsi_key(rv[x * kHsiPerCand + j], rb[x * kHsiPerCand + j], &hi, &lo);
+          if ((hi & mask_hi) == pre_hi && (lo & mask_lo) == pre_lo) { found_hi = hi; found_lo = lo; }
+        }
+      }
+      __syncthreads();
+      pre_hi = found_hi;
+      pre_lo = found_lo;
+      break;
+    }
+  }
+  // (pre_hi, pre_lo) is the key of the 2048th block; keys are unique (block
+  // indices differ), so the kept blocks are exactly those with key >= it.
+  // Visible entries of the kept blocks, in block order: per candidate block,
+  // count the entries of its kept records, then an ordered scan gives offsets.
+  uint32_t written = 0;
+  for (int64_t x0 = 0; x0 < nblk; x0 += kSelThreads) {
+    const int64_t x = x0 + tid;
+    uint32_t mine = 0;
+    if (x < nblk) {
+      const uint32_t c = cnt[x];
+      for (uint32_t j = 0; j < c; ++j) {
+        unsigned long long hi;
+        uint32_t lo;
+        const uint32_t blk = rb[x * kHsiPerCand + j];
+        hsi_key(rv[x * kHsiPerCand + j], blk, &hi, &lo);
+        if (hi > pre_hi || (hi == pre_hi && lo >= pre_lo)) {
+          const int64_t e0 = (int64_t)blk * kHsiBlock;
+          mine += (uint32_t)(nv - e0 < kHsiBlock ? nv - e0 : kHsiBlock);
+        }
+      }
+    }
+    uint32_t tot;
+    uint32_t o = written + block_excl_scan(mine, wsum[0], &tot);
+    if (x < nblk) {
+      const uint32_t c = cnt[x];
+      for (uint32_t j = 0; j < c; ++j) {
+        unsigned long long hi;
+        uint32_t lo;
+        const uint32_t blk = rb[x * kHsiPerCand + j];
+        hsi_key(rv[x * kHsiPerCand + j], blk, &hi, &lo);
+        if (hi > pre_hi || (hi == pre_hi && lo >= pre_lo)) {
+          const int64_t e0 = (int64_t)blk * kHsiBlock;
+          const int64_t e1 = nv - e0 < kHsiBlock ? nv : e0 + kHsiBlock;
+          for (int64_t e = e0; e < e1; ++e)
+            if (o < (uint32_t)kHsiPool) out[o++] = (int32_t)e;
+        }
+      }
+    }
+    written += tot;
+  }
+  for (int64_t i = (int64_t)written + tid; i < kHsiPool; i += kSelThreads) out[i] = -1;
+}
+
 }  // namespace csa2
 
 using namespace csa2;
@@ -1405,11 +1704,46 @@ extern "C" csa2_status csa2_topk(const float* scores, const float* tile_max, uin
   if (!topk_layout(workspace_bytes, T, N, &slots, &cap)) return CSA2_ERR_WORKSPACE;
   const int64_t nblk = cand_blocks(N);
   hipLaunchKernelGGL(topk_floor_kernel, dim3(T), dim3(kFloorThreads), 0, st, tile_max, stats, gmax, p.n_groups,
-                     parts, p.parts(), q, w_idx, q_pos, ratio, q_per_seq, N);
+                     parts, p.parts(), q, w_idx, q_pos, ratio, q_per_seq, N, kTopK, (int64_t)kTopK);
   hipLaunchKernelGGL(topk_cand_kernel, dim3((unsigned)nblk, T), dim3(kCandThreads), 0, st, tile_max, stats, q,
                      w_idx, kx, q_pos, ratio, q_per_seq, N, k, workspace, T, cap, slots);
   hipLaunchKernelGGL(topk_select_kernel, dim3(T), dim3(kSelThreads), 0, st, tile_max, stats, q, w_idx, kx, q_pos,
                      ratio, q_per_seq, N, k, indices, workspace, T, cap);
+  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
+  return CSA2_OK;
+}
+
+extern "C" size_t csa2_hsi_pool_workspace_bytes(int32_t T, int64_t N) {
+  if (T < 1 || N < 1) return 0;
+  return hsi_ws_bytes(T, N);
+}
+
+extern "C" csa2_status csa2_hsi_pool(const float* tile_max, const uint32_t* stats, size_t stats_bytes,
+                                     const void* q_idx, const float* w_idx, const void* k_idx, const int32_t* q_pos,
+                                     int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N, int32_t* pool,
+                                     void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!tile_max || !stats || !q_idx || !w_idx || !k_idx || !pool) return CSA2_ERR_INVALID_ARG;
+  if (!aligned16(tile_max) || !aligned16(stats) || !aligned16(q_idx) || !aligned16(w_idx) || !aligned16(k_idx) ||
+      !aligned16(pool) || (q_pos && !aligned16(q_pos)))
+    return CSA2_ERR_INVALID_ARG;
+  if (T < 1 || q_per_seq < 1 || T % q_per_seq != 0 || N < 1 || ratio < 1) return CSA2_ERR_INVALID_ARG;
+  if (N >= ((int64_t)1 << 31) || T > 65535) return CSA2_ERR_UNSUPPORTED;
+  IndexPlan p;
+  if (!index_plan(T, q_per_seq, N, &p)) return CSA2_ERR_UNSUPPORTED;
+  if (stats_bytes < stats_words(T, p) * sizeof(uint32_t)) return CSA2_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < hsi_ws_bytes(T, N)) return CSA2_ERR_WORKSPACE;
+  const float* gmax = (const float*)(stats + stats_groups_off(T));
+  const float* parts = (const float*)(stats + stats_parts_off(T, p.n_groups));
+  hipStream_t st = (hipStream_t)hip_stream;
+  (void)hipGetLastError();
+  const uint16_t* q = (const uint16_t*)q_idx;
+  const uint16_t* kx = (const uint16_t*)k_idx;
+  uint32_t* hdr = (uint32_t*)workspace;  // HsiWs::hdr is at the start of the workspace
+  hipLaunchKernelGGL(topk_floor_kernel, dim3(T), dim3(kFloorThreads), 0, st, tile_max, hdr, gmax, p.n_groups, parts,
+                     p.parts(), q, w_idx, q_pos, ratio, q_per_seq, N, kHsiBlocks, (int64_t)kHsiPool);
+  hipLaunchKernelGGL(hsi_cand_kernel, dim3((unsigned)cand_blocks(N), T), dim3(kCandThreads), 0, st, tile_max, q,
+                     w_idx, kx, q_pos, ratio, q_per_seq, N, workspace, T);
+  hipLaunchKernelGGL(hsi_select_kernel, dim3(T), dim3(kSelThreads), 0, st, q_pos, ratio, N, workspace, T, pool);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   return CSA2_OK;
 }

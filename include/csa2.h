@@ -152,6 +152,59 @@ csa2_status csa2_topk(const float* scores, const float* tile_max, uint32_t* stat
                       int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices,
                       void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* --------------------------------------------------------------- hsi pool
+ * Candidate pool of the hierarchical sparse indexer (report sec. 2.3.2; block
+ * size 8 and 2048 blocks per sec. 4.2.1).  A Full layer's visible entries
+ * are cut into aligned blocks of CSA2_HSI_BLOCK; a block's score is the
+ * largest I_fp64 (as under csa2_index) of its visible entries.  The first
+ * min(CSA2_HSI_BLOCKS, number of visible blocks) blocks of the order (block
+ * score descending, block index ascending) are kept, and their visible
+ * entries, ascending, are written to pool[t][0..]; the remaining slots are
+ * set to -1.  A query with at most CSA2_HSI_POOL visible entries keeps all of
+ * them.  Later Reindex layers select their own top-k within the pool.
+ *
+ *  tile_max, stats, stats_bytes   outputs of csa2_index for the same
+ *             arguments (read only; the header words are not touched)
+ *  q_idx, w_idx, k_idx, q_pos, ratio, T, q_per_seq, N   as passed to csa2_index
+ *  pool       int32 [T][CSA2_HSI_POOL] out
+ *  workspace >= csa2_hsi_pool_workspace_bytes(T, N); its first 16*T bytes
+ *             hold {eps_t, floor_t, 0, 0} per query afterwards (as the stats
+ *             header of csa2_topk, with floor_t ranking CSA2_HSI_BLOCKS
+ *             distinct blocks)
+ *  Three kernels; requires 1 <= N < 2^31, T <= 65535.
+ */
+#define CSA2_HSI_BLOCK 8
+#define CSA2_HSI_BLOCKS 2048
+#define CSA2_HSI_POOL (CSA2_HSI_BLOCK * CSA2_HSI_BLOCKS)
+size_t csa2_hsi_pool_workspace_bytes(int32_t T, int64_t N);
+csa2_status csa2_hsi_pool(const float* tile_max, const uint32_t* stats, size_t stats_bytes,
+                          const void* q_idx, const float* w_idx, const void* k_idx, const int32_t* q_pos,
+                          int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N, int32_t* pool,
+                          void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------- reindex
+ * Reindex selection (report sec. 2.3.2): a Reindex layer scores only the
+ * entries of the candidate pool (csa2_hsi_pool of the preceding Full layer)
+ * with its own indexer query over the shared indexer keys, and keeps the first
+ * min(k, pool size) pool entries of the order (I_fp64 descending, index
+ * ascending), written ASCENDING into indices[t][0..], -1 padded.  I_fp64 is
+ * defined as under csa2_index (the Reindex layer's q_idx, w_idx).
+ *
+ *  pool     int32 [T][CSA2_HSI_POOL]  ascending entry ids in [0, N), then -1
+ *           (as csa2_hsi_pool writes it); the visible set is the pool itself
+ *  q_idx    bf16 [T][32][128], w_idx fp32 [T][32]: the Reindex layer's query
+ *  k_idx    bf16 [B][N][128]: the shared indexer keys
+ *  k        must be CSA2_TOPK;  indices int32 [T][k] out
+ *  workspace >= csa2_reindex_workspace_bytes(T, k) (about 4.2 MiB per query:
+ *           the gathered pool keys, their scores and the selection's summary)
+ *  Runs a gather kernel, csa2_index and csa2_topk (row regime) over the
+ *  gathered keys, and a map kernel, all on hip_stream.
+ */
+size_t csa2_reindex_workspace_bytes(int32_t T, int32_t k);
+csa2_status csa2_reindex(const int32_t* pool, const void* q_idx, const float* w_idx, const void* k_idx,
+                         int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices,
+                         void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* ----------------------------------------------------------------- attend
  * Joint sparse + sliding-window attention over an FP4 main-KV cache.  For
  * query t (sequence b) and head h, over the set E_t of

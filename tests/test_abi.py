@@ -27,7 +27,8 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert {"csa2_index", "csa2_topk", "csa2_attend_fp4", "csa2_reuse_attend"} <= set(names)
+    assert {"csa2_index", "csa2_topk", "csa2_attend_fp4", "csa2_reuse_attend", "csa2_hsi_pool",
+            "csa2_reindex"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -51,6 +52,12 @@ def test_workspace_queries(L):
     assert csa.attend_workspace_bytes(4) > 0
     assert csa.attend_workspace_bytes(4, window=129) == 0
     assert csa.attend_workspace_bytes(4, n_layers=9) == 0
+    # pool: per candidate block of 4096 entries one count and 512 (block, fp64 max) records
+    assert csa.hsi_pool_workspace_bytes(4, 1 << 20) >= 4 * 256 * 512 * 12
+    assert csa.hsi_pool_workspace_bytes(0, 1 << 20) == 0
+    # reindex: the gathered pool keys (16384 x 256 B per query) dominate
+    assert csa.reindex_workspace_bytes(4) >= 4 * csa.HSI_POOL * 256
+    assert csa.reindex_workspace_bytes(4, 256) == 0
 
 
 # Fake, never-dereferenced, 16-byte-aligned addresses: every call below must be
@@ -138,6 +145,41 @@ def test_reuse_host_validation(L):
     small = list(args)
     small[17] = csa.attend_workspace_bytes(4, n_layers=3) - 1
     assert L.csa2_reuse_attend(3, *small) == WORKSPACE
+
+
+def _hsi(L, tm=P, e=P, eb=1 << 30, q=P, w=P, k_idx=P, pos=None, ratio=1, T=4, qps=1, N=1 << 20, out=P, ws=P,
+         wsb=None):
+    if wsb is None:
+        wsb = csa.hsi_pool_workspace_bytes(T, N) or 1
+    return L.csa2_hsi_pool(tm, e, eb, q, w, k_idx, pos, ratio, T, qps, N, out, ws, wsb, None)
+
+
+def test_hsi_pool_host_validation(L):
+    assert _hsi(L, tm=None) == INVALID
+    assert _hsi(L, e=None) == INVALID
+    assert _hsi(L, eb=csa.index_stats_bytes(4, 1, 1 << 20) - 1) == INVALID
+    assert _hsi(L, out=MIS) == INVALID
+    assert _hsi(L, T=5, qps=2) == INVALID
+    assert _hsi(L, ratio=0) == INVALID
+    assert _hsi(L, N=1 << 31) == UNSUPPORTED
+    assert _hsi(L, ws=None) == WORKSPACE
+    assert _hsi(L, wsb=csa.hsi_pool_workspace_bytes(4, 1 << 20) - 1) == WORKSPACE
+
+
+def _reindex(L, pool=P, q=P, w=P, k_idx=P, T=4, qps=1, N=1 << 20, k=512, out=P, ws=P, wsb=None):
+    if wsb is None:
+        wsb = csa.reindex_workspace_bytes(T, 512) or 1
+    return L.csa2_reindex(pool, q, w, k_idx, T, qps, N, k, out, ws, wsb, None)
+
+
+def test_reindex_host_validation(L):
+    assert _reindex(L, pool=None) == INVALID
+    assert _reindex(L, pool=MIS) == INVALID
+    assert _reindex(L, T=0) == INVALID
+    assert _reindex(L, T=5, qps=2) == INVALID
+    assert _reindex(L, k=256) == UNSUPPORTED
+    assert _reindex(L, ws=None) == WORKSPACE
+    assert _reindex(L, wsb=csa.reindex_workspace_bytes(4) - 1) == WORKSPACE
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
