@@ -49,7 +49,8 @@ def parse():
     return ap.parse_args()
 
 
-# Sources of the scan kernel: the recorded traffic holds only while they are unchanged.
+# Sources of the scan kernel: the recorded traffic holds only while they are unchanged (of the
+# public header, only its constants count: its documentation does not change the kernel).
 SCAN_SOURCES = ["compressed_sparse_attention_02_amd/csrc/index.hip", "compressed_sparse_attention_02_amd/csrc/idx_tile.h",
                 "compressed_sparse_attention_02_amd/csrc/idx_plan.h",
                 "compressed_sparse_attention_02_amd/csrc/csa2_common.h", "include/csa2.h"]
@@ -61,7 +62,10 @@ def scan_sources_sha256():
     import hashlib
     h = hashlib.sha256()
     for f in SCAN_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        data = open(os.path.join(ROOT, f), "rb").read()
+        if f.endswith("csa2.h"):
+            data = b"".join(l for l in data.splitlines(keepends=True) if l.lstrip().startswith(b"#define"))
+        h.update(data)
     return h.hexdigest()
 
 
@@ -104,11 +108,13 @@ def summarize(stats_dir, fetch_dir, write_dir, mfma_dir=None):
 
     def per_dispatch(d, counter):
         acc = {}
-        for r in rows(d, "counter_collection.csv"):
-            if r["Counter_Name"] != counter:
-                continue
+        data = [r for r in rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
+        # the benchmarked scan is the largest-grid one (a Reindex pass scans its pools with a smaller grid)
+        scan_grid = max((int(r["Grid_Size"]) for r in data if "idx_scan_kernel" in r["Kernel_Name"]), default=0)
+        for r in data:
             name = r["Kernel_Name"]
-            key = ("scan" if "idx_scan_kernel" in name else "cal" if "neg_kernel" in name else
+            key = ("scan" if "idx_scan_kernel" in name and int(r["Grid_Size"]) == scan_grid else
+                   "cal" if "neg_kernel" in name else
                    "attend" if "attend_kernel" in name else "combine" if "attend_combine" in name else None)
             if key:
                 acc.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
@@ -216,6 +222,22 @@ def main():
         csa.csa2_reuse_attend(q_re, c.kv_codes, c.kv_scales, idx, swa_re, c.swa_end, None, c.softmax_scale, 1,
                               128, out=out_re, workspace=ws_r)
 
+    # hierarchical sparse indexer: the Full layer's candidate pool, then a Reindex layer's
+    # own top-512 within it (its indexer query drawn under another seed)
+    pool = torch.empty((T, csa.HSI_POOL), dtype=torch.int32, device=dev)
+    ws_p = torch.empty(csa.hsi_pool_workspace_bytes(T, N), dtype=torch.uint8, device=dev)
+    ws_x = torch.empty(csa.reindex_workspace_bytes(T), dtype=torch.uint8, device=dev)
+    idx_x = torch.empty((T, 512), dtype=torch.int32, device=dev)
+    q_x = G.normal_bf16(1, G.ST_QIDX, 0, T * csa.IDX_HEADS * csa.IDX_DIM, dev).view(
+        T, csa.IDX_HEADS, csa.IDX_DIM).view(torch.bfloat16)
+    w_x = G.uniform_f32(1, G.ST_W, 0, T * csa.IDX_HEADS, dev).view(T, csa.IDX_HEADS)
+
+    def do_pool():
+        csa.csa2_hsi_pool(tile_max, stats, q_idx, c.w_idx, k_idx, c.q_pos, 1, 1, pool=pool, workspace=ws_p)
+
+    def do_reindex():
+        csa.csa2_reindex(pool, q_x, w_x, k_idx, 1, indices=idx_x, workspace=ws_x)
+
     def step():
         do_index()
         do_topk()
@@ -251,6 +273,11 @@ def main():
     att_med, att_avg = timed(do_attend, reps)
     do_reuse()
     reuse_med, _ = timed(do_reuse, reps)
+    do_index()
+    do_pool()
+    do_reindex()
+    pool_med, _ = timed(do_pool, reps)
+    reindex_med, _ = timed(do_reindex, reps)
 
     # dominant kernel: the indexer scan (csa2_index is that one kernel).
     # Algorithmic bytes per launch: each sequence's keys once (256 B/entry),
@@ -306,6 +333,9 @@ def main():
                      "traffic": recorded_traffic() if args.workload == "long_decode" else None,
                      "algorithmic_bytes_per_launch": idx_bytes, "avg_launch_us": idx_avg},
         "stages_us": {"index": idx_med, "topk": topk_med, "attend": att_med, "reuse_3_layers": reuse_med},
+        "hierarchical_us": {"pool": pool_med, "reindex": reindex_med,
+                            "note": "outside the step: a Full layer's 16384-entry candidate pool (after its scan) "
+                                    "and one Reindex layer's top-512 within it"},
         "attention": {"call": "csa2_attend_fp4 (attend + merge kernels)", "avg_us": att_avg,
                       "algorithmic_bytes": att_bytes, "GBps": att_gbps, "frac_hbm": att_gbps / HBM_PEAK_GBPS,
                       "flops": att_flops, "TFLOPs": att_tflops, "frac_mfma_bf16": att_tflops / MFMA_BF16_PEAK_TFLOPS},

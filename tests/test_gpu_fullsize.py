@@ -103,3 +103,45 @@ def test_causal_prefill_sampled(path):
     log(f"[full] causal_prefill 4096 queries, 34816 entries, ratio 2 ({path})")
     c = G.make_case("causal_prefill", **G.CONFIGS["causal_prefill"], seed=0, device=DEV)
     check_sampled(c, [0, 1, 2047, 4094, 4095], path=path)
+
+
+def check_hierarchical(c, ts):
+    """Candidate pool and Reindex selection at full size: exact against the oracle on queries ts;
+    Reindex with the Full query equals the Full top-512 on every query (a property at any size)."""
+    import oracle
+    from _ref import u16
+    bf = (c.q_idx.view(BF), c.w_idx, c.k_idx.view(BF), c.q_pos, c.ratio, c.q_per_seq)
+    ix = csa.csa2_index(*bf, want_scores=False)
+    pool = csa.csa2_hsi_pool(ix.tile_max, ix.stats, *bf)
+    full = csa.csa2_topk(None, ix.tile_max, ix.stats, *bf)
+    same = csa.csa2_reindex(pool, c.q_idx.view(BF), c.w_idx, c.k_idx.view(BF), c.q_per_seq)
+    q2 = G.normal_bf16(1, G.ST_QIDX, 0, c.T * csa.IDX_HEADS * csa.IDX_DIM, DEV).view(c.T, csa.IDX_HEADS,
+                                                                                    csa.IDX_DIM)
+    w2 = G.uniform_f32(1, G.ST_W, 0, c.T * csa.IDX_HEADS, DEV).view(c.T, csa.IDX_HEADS)
+    re = csa.csa2_reindex(pool, q2.view(BF), w2, c.k_idx.view(BF), c.q_per_seq)
+    torch.cuda.synchronize()
+    assert torch.equal(full, same), "Reindex with the Full query must return the Full top-512"
+    log(f"  GPU path done; oracle on queries {ts}")
+    ref_s = oracle_scores(c, ts)
+    p_np, r_np = npy(pool), npy(re)
+    for t in ts:
+        b = t // c.q_per_seq
+        ref_p = oracle.hsi_pool(ref_s[t][None, :], npy(c.q_pos[t:t + 1]), c.ratio)[0]
+        assert np.array_equal(p_np[t], ref_p), f"t={t}: pool differs"
+        s2 = oracle.index(u16(q2[t:t + 1]), npy(w2[t:t + 1]), u16(c.k_idx[b:b + 1]), npy(c.q_pos[t:t + 1]),
+                          c.ratio, 1)
+        ref_r = oracle.reindex_topk(s2, ref_p[None, :], c.k)[0]
+        assert np.array_equal(r_np[t], ref_r), f"t={t}: Reindex top-512 differs"
+        log(f"  t={t}: pool of {int((ref_p >= 0).sum())} entries and Reindex top-512 exact")
+
+
+def test_long_decode_hierarchical_sampled():
+    log("[full] long_decode 4 x 1M: candidate pool + Reindex")
+    c = G.make_case("long_decode", **G.CONFIGS["long_decode"], seed=0, device=DEV, with_kv=False)
+    check_hierarchical(c, [1, 2])
+
+
+def test_causal_prefill_hierarchical_sampled():
+    log("[full] causal_prefill 4096 queries: candidate pool + Reindex")
+    c = G.make_case("causal_prefill", **G.CONFIGS["causal_prefill"], seed=0, device=DEV, with_kv=False)
+    check_hierarchical(c, [0, 2048, 4095])
