@@ -86,7 +86,7 @@ def recorded_traffic():
         return None
 
 
-def summarize(stats_dir, fetch_dir, write_dir, mfma_dir=None):
+def summarize(stats_dir, fetch_dir=None, write_dir=None, mfma_dir=None):
     """Markdown summary of rocprofv3 CSV output: per-kernel durations of the bench run and the
     per-dispatch FETCH_SIZE / WRITE_SIZE of the scan, scaled by the calibration dispatch."""
     import csv
@@ -121,6 +121,8 @@ def summarize(stats_dir, fetch_dir, write_dir, mfma_dir=None):
                 acc[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
         return {k: sum(v.values()) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
 
+    if not fetch_dir or not write_dir:
+        return 0
     f, fn = per_dispatch(fetch_dir, "FETCH_SIZE")
     w, wn = per_dispatch(write_dir, "WRITE_SIZE")
     f_scale = CAL_BYTES / (f["cal"] * 1024)

@@ -71,8 +71,15 @@ __global__ __launch_bounds__(kGatherThreads) void reindex_gather_kernel(const in
   }
   if (blockIdx.x == 0) {
     __shared__ uint32_t part[kGatherThreads / 64];
+    // 64 entries per thread, as 16 loads of four issued together
+    const int4* p4 = reinterpret_cast<const int4*>(pl);
+    int4 v[kPool / 4 / kGatherThreads];
+#pragma unroll
+    for (int u = 0; u < kPool / 4 / kGatherThreads; ++u) v[u] = p4[u * kGatherThreads + tid];
     uint32_t n = 0;
-    for (int i = tid; i < kPool; i += kGatherThreads) n += pl[i] >= 0 ? 1u : 0u;
+#pragma unroll
+    for (int u = 0; u < kPool / 4 / kGatherThreads; ++u)
+      n += (v[u].x >= 0) + (v[u].y >= 0) + (v[u].z >= 0) + (v[u].w >= 0);
     n = wave_sum_u32_dpp(n);
     if ((tid & 63) == 0) part[tid >> 6] = n;
     __syncthreads();

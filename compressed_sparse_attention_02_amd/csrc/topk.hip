@@ -187,7 +187,8 @@ __device__ __forceinline__ void pick_digit(const uint32_t* hist, uint32_t rank, 
 // Selection scratch shared by the bracketing helpers.
 struct alignas(16) SelLds {
   uint32_t hist[256];
-  uint32_t pick[2];
+  uint32_t bmin[256];
+  uint32_t pick[3];
   float red[2][kFinThreads / 64];
 };
 
@@ -221,45 +222,70 @@ __device__ __forceinline__ void for_each4(int64_t n, Get get, F f) {
 }
 
 // Bracket lo <= T <= hi of T = the rank-th largest (1-based) of the n values
-// get(i): two levels of 256 value bins over [min, max]; lo and hi are the
-// smallest and largest values sharing T's final bin.  With `loose`, stop after
-// the first level and return lo = the smallest value in T's bin or above
-// (a lower bound with at least `rank` values >= lo).  All threads participate.
+// get(i), rank < n.  Thread j's values are get(j), get(j + blockDim), ...;
+// the per-thread maxima are distinct values, so the rank-th largest of them,
+// L, has at least rank values >= L and T >= L (with n > rank every thread
+// up to rank holds a value when blockDim >= rank).  L comes from a 256-bin
+// histogram of the per-thread maxima that keeps each bin's minimum; then two
+// levels of 256 value bins over [L, max], counting only values >= L, narrow T
+// to one bin; lo and hi are the smallest and largest values in it.  The value
+// histograms thus see a few times rank values, not n.  All threads call this.
 template <typename Get>
-__device__ void bracket_kth(SelLds& s, int64_t n, uint32_t rank, Get get, bool loose, float* lo, float* hi) {
+__device__ void bracket_kth(SelLds& s, int64_t n, uint32_t rank, Get get, float* lo, float* hi) {
   const float inf = INFINITY;
-  float mn = inf, mx = -inf;
-  for_each4(n, get, [&](float v) { mn = fminf(mn, v); mx = fmaxf(mx, v); });
-  float2 r = block_minmax(s, mn, mx);
-  const float a1 = r.x, s1 = r.y > r.x ? 255.99f / (r.y - r.x) : 0.f;
+  float tmax = -inf, mx = -inf;
+  for_each4(n, get, [&](float v) { tmax = fmaxf(tmax, v); });
+  // 1. L from the per-thread maxima
+  float2 r = block_minmax(s, tmax > -inf ? tmax : inf, tmax);
+  mx = r.y;
+  {
+    const float a0 = r.x, s0 = r.y > r.x ? 255.99f / (r.y - r.x) : 0.f;
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) { s.hist[i] = 0; s.bmin[i] = 0xFFFFFFFFu; }
+    __syncthreads();
+    if (tmax > -inf) {
+      const uint32_t bin = value_bin(tmax, a0, s0);
+      atomicAdd(&s.hist[bin], 1u);
+      atomicMin(&s.bmin[bin], f32_key(tmax));
+    }
+    pick_digit(s.hist, rank, s.pick);
+    // the smallest per-thread maximum in the chosen bin or above
+    if (threadIdx.x < 64) {
+      uint32_t m = 0xFFFFFFFFu;
+      for (int i = threadIdx.x; i < 256; i += 64)
+        if ((uint32_t)i >= s.pick[0]) m = min(m, s.bmin[i]);
+      m = wave_min_u32_dpp(m);
+      if (threadIdx.x == 0) s.pick[2] = m;
+    }
+    __syncthreads();
+  }
+  const float L = key_f32(s.pick[2]);
+  // 2. first level over [L, max]
+  const float a1 = L, s1 = mx > L ? 255.99f / (mx - L) : 0.f;
   for (int i = threadIdx.x; i < 256; i += blockDim.x) s.hist[i] = 0;
   __syncthreads();
-  for_each4(n, get, [&](float v) { atomicAdd(&s.hist[value_bin(v, a1, s1)], 1u); });
+  for_each4(n, get, [&](float v) { if (v >= L) atomicAdd(&s.hist[value_bin(v, a1, s1)], 1u); });
   pick_digit(s.hist, rank, s.pick);
   const uint32_t b1 = s.pick[0];
   rank = s.pick[1];
-  if (loose) {
-    mn = inf;
-    for_each4(n, get, [&](float v) { if (value_bin(v, a1, s1) >= b1) mn = fminf(mn, v); });
-    r = block_minmax(s, mn, -inf);
-    *lo = r.x;
-    *hi = inf;
-    return;
-  }
-  mn = inf; mx = -inf;
-  for_each4(n, get, [&](float v) { if (value_bin(v, a1, s1) == b1) { mn = fminf(mn, v); mx = fmaxf(mx, v); } });
+  float mn = inf;
+  mx = -inf;
+  for_each4(n, get, [&](float v) {
+    if (v >= L && value_bin(v, a1, s1) == b1) { mn = fminf(mn, v); mx = fmaxf(mx, v); }
+  });
   r = block_minmax(s, mn, mx);
+  // 3. second level within that bin
   const float a2 = r.x, s2 = r.y > r.x ? 255.99f / (r.y - r.x) : 0.f;
   for (int i = threadIdx.x; i < 256; i += blockDim.x) s.hist[i] = 0;
   __syncthreads();
   for_each4(n, get, [&](float v) {
-    if (value_bin(v, a1, s1) == b1) atomicAdd(&s.hist[value_bin(v, a2, s2)], 1u);
+    if (v >= L && value_bin(v, a1, s1) == b1) atomicAdd(&s.hist[value_bin(v, a2, s2)], 1u);
   });
   pick_digit(s.hist, rank, s.pick);
   const uint32_t b2 = s.pick[0];
-  mn = inf; mx = -inf;
+  mn = inf;
+  mx = -inf;
   for_each4(n, get, [&](float v) {
-    if (value_bin(v, a1, s1) == b1 && value_bin(v, a2, s2) == b2) { mn = fminf(mn, v); mx = fmaxf(mx, v); }
+    if (v >= L && value_bin(v, a1, s1) == b1 && value_bin(v, a2, s2) == b2) { mn = fminf(mn, v); mx = fmaxf(mx, v); }
   });
   r = block_minmax(s, mn, mx);
   *lo = r.x;
@@ -466,8 +492,22 @@ __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
   const uint16_t* kb = k_idx + (size_t)b * N * kIdxDim;
   const float* row = scores + (size_t)t * N;
   if (tid == 0) { sh.n_out = 0; sh.n_band = 0; }
-  if (nv > k)
-    for (int64_t i = tid; i < nv; i += kFinThreads) L.u.v[i] = row[i];
+  if (nv > k) {
+    // eight loads in flight per thread (indices past the row re-read its last score)
+    for (int64_t i0 = tid; i0 < nv; i0 += 8 * kFinThreads) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = i0 + (int64_t)u * kFinThreads;
+        v[u] = row[i < nv ? i : nv - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = i0 + (int64_t)u * kFinThreads;
+        if (i < nv) L.u.v[i] = v[u];
+      }
+    }
+  }
   {
     float m2;
     double qf, sw;
@@ -491,7 +531,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
     return;
   }
   float t_lo, t_hi;
-  bracket_kth(sh.sel, nv, kk, [&](int64_t i) { return L.u.v[i]; }, false, &t_lo, &t_hi);
+  bracket_kth(sh.sel, nv, kk, [&](int64_t i) { return L.u.v[i]; }, &t_lo, &t_hi);
   double lo, hi;
   band_bounds(t_lo, t_hi, eps, &lo, &hi);
   for (int64_t i = tid; i < nv; i += kFinThreads) {
@@ -727,23 +767,43 @@ __global__ __launch_bounds__(kFloorThreads) void topk_floor_kernel(
   }
 }
 
+// fp64 scores of entries eidx[0..n) in the reference's operation order,
+// 32 entries per round: the block stages their key rows in LDS (all loads in
+// flight at once; with erow given and n <= kExactRound the rows are already
+// there, row erow[e] for entry e), then entry j of the round goes to wave j % 4, slot j / 4;
+// lane (half = lane / 32, h = lane % 32) forms dot(q_h, K) with 128 sequential
+// fmas for slots half, half + 2, ... (up to four independent chains), and
+// lane s then folds slot s's 32 heads in order.  put(e, score) receives each
+// result.  All threads of the block call this.
+constexpr int kExactRound = 32;
+struct alignas(16) ExactLds {
+  uint16_t krows[kExactRound][kIdxDim];
+  double dots[kCandThreads / 64][kExactRound / (kCandThreads / 64)][kIdxHeads + 1];
+};
+
 // fp32 scores of candidate tiles ctile[0..n_tiles) (offsets from tile0) with
 // the scan's arithmetic; cmask[c] gets the entries of tile c that are visible
-// and reach thr.  Wave w takes tiles w, w + 4, ...; the rows of up to four of
-// its tiles are requested before any is scored.
+// and reach thr.  Wave w takes tiles w, w + 4, ...; the rows of up to kMaskTiles of
+// its tiles are requested before any is scored.  The rows of the passing
+// entries, already in registers, are also written to X.krows for the fp64
+// rescoring: tile c's passing entries take rows rowbase[c], rowbase[c] + 1, ...
+// in entry order (rows reserved with an LDS counter, n_staged, that must be zero
+// on entry; rows past kExactRound are not written).
+constexpr int kMaskTiles = 3;
 __device__ __forceinline__ void cand_tile_masks(const uint16_t* __restrict__ sq, const float* __restrict__ w,
                                                 const uint16_t* __restrict__ ctile, uint16_t* __restrict__ cmask,
                                                 uint32_t n_tiles, int64_t tile0, const uint16_t* __restrict__ kseq,
-                                                int64_t nv, double thr) {
+                                                int64_t nv, double thr, ExactLds& X, uint16_t* __restrict__ rowbase,
+                                                uint32_t* n_staged) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
   constexpr int kWaves = kCandThreads / 64;
   float wr[8];
   load_head_weights(w, g, wr);
-  for (uint32_t c0 = wave; c0 < n_tiles; c0 += 4 * kWaves) {
-    uint4 kv[4][4];
+  for (uint32_t c0 = wave; c0 < n_tiles; c0 += kMaskTiles * kWaves) {
+    uint4 kv[kMaskTiles][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kMaskTiles; ++u) {
       const uint32_t ci = c0 + u * kWaves;
       if (ci < n_tiles) {
         const int64_t s = (tile0 + ctile[ci]) * kTileKeys + col;
@@ -751,60 +811,98 @@ __device__ __forceinline__ void cand_tile_masks(const uint16_t* __restrict__ sq,
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kMaskTiles; ++u) {
       const uint32_t ci = c0 + u * kWaves;
       if (ci >= n_tiles) break;
       const int64_t s = (tile0 + ctile[ci]) * kTileKeys + col;
       const float sc = tile_score(sq, kv[u], wr, col, g);
-      const uint64_t bal = __ballot(s < nv && (double)sc >= thr);
-      if (lane == 0) cmask[ci] = (uint16_t)(bal & 0xFFFFu);
+      const uint32_t m16 = (uint32_t)(__ballot(s < nv && (double)sc >= thr) & 0xFFFFull);
+      uint32_t base = 0;
+      if (lane == 0 && m16) base = atomicAdd(n_staged, (uint32_t)__popc(m16));
+      base = (uint32_t)__shfl((int)base, 0, 64);
+      if (lane == 0) {
+        cmask[ci] = (uint16_t)m16;
+        rowbase[ci] = (uint16_t)(base < (uint32_t)kExactRound ? base : (uint32_t)kExactRound);
+      }
+      const uint32_t row = base + (uint32_t)__popc(m16 & ((1u << col) - 1u));
+      if (((m16 >> col) & 1u) && row < (uint32_t)kExactRound) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&X.krows[row][32 * j + 8 * g]) = kv[u][j];
+      }
     }
   }
 }
 
-// fp64 scores of entries eidx[0..n) in the reference's operation order: lane
-// (e = lane / 32, h = lane % 32) forms dot(q_h, K_e) with 128 sequential fmas,
-// then lane h == 0 folds the entry's 32 heads in order from LDS (hrel: this
-// wave's 64 doubles).  Two entries per wave and round; put(e, score) receives
-// each result.
-template <class Put>
-__device__ __forceinline__ void exact_entry_scores(const uint16_t* __restrict__ sq, const float* __restrict__ w,
-                                                   const uint32_t* __restrict__ eidx, uint32_t n,
-                                                   const uint16_t* __restrict__ kseq, double* hrel, Put put) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = lane & 31;
-  for (uint32_t e0 = 2 * wave; e0 < n; e0 += 2 * (kCandThreads / 64)) {
-    const uint32_t e = e0 + (lane >> 5);
-    const uint32_t ee = e < n ? e : e0;
-    const uint16_t* kr = kseq + (size_t)eidx[ee] * kIdxDim;
-    const uint16_t* qr = &sq[h * kQRowPad];
-    double d = 0.0;
-#pragma unroll 4
-    for (int i = 0; i < 16; ++i) {
-      const uint4 kq = *reinterpret_cast<const uint4*>(kr + 8 * i);
-      const uint4 qq = *reinterpret_cast<const uint4*>(qr + 8 * i);
-      const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
+template <int C>
+__device__ __forceinline__ void exact_dots(const uint16_t* __restrict__ sq, ExactLds& X, const uint8_t* erow,
+                                           int wave, int lane) {
+  const int h = lane & 31, half = lane >> 5;
+  const uint16_t* qr = &sq[h * kQRowPad];
+  const uint16_t* kr[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    const int j = 4 * (half + 2 * i) + wave;
+    kr[i] = X.krows[erow ? (erow[j] & (kExactRound - 1)) : j];
+  }
+  double d[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) d[i] = 0.0;
+#pragma unroll 2
+  for (int c = 0; c < 16; ++c) {
+    const uint4 qq = *reinterpret_cast<const uint4*>(qr + 8 * c);
+    const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const uint4 kq = *reinterpret_cast<const uint4*>(kr[i] + 8 * c);
       const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        d = fma((double)bf16lo(qw[c]), (double)bf16lo(kw[c]), d);
-        d = fma((double)bf16hi(qw[c]), (double)bf16hi(kw[c]), d);
+      for (int p = 0; p < 4; ++p) {
+        d[i] = fma((double)bf16lo(qw[p]), (double)bf16lo(kw[p]), d[i]);
+        d[i] = fma((double)bf16hi(qw[p]), (double)bf16hi(kw[p]), d[i]);
       }
     }
-    hrel[lane] = d > 0.0 ? d : 0.0;
+  }
+#pragma unroll
+  for (int i = 0; i < C; ++i) X.dots[wave][half + 2 * i][h] = d[i];
+}
+
+template <class Put>
+__device__ __forceinline__ void exact_entry_scores(const uint16_t* __restrict__ sq, const float* __restrict__ w,
+                                                   const uint32_t* __restrict__ eidx, const uint8_t* erow,
+                                                   uint32_t n, const uint16_t* __restrict__ kseq, ExactLds& X,
+                                                   Put put) {
+  static_assert(kCandThreads == 256, "four waves, two 16-byte pieces of the round's rows per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // all rows already in X.krows (erow[e]: the row of entry e): one round, no loads
+  const bool staged = erow != nullptr && n <= (uint32_t)kExactRound;
+  for (uint32_t r0 = 0; r0 < n; r0 += kExactRound) {
+    const uint32_t m = n - r0 < (uint32_t)kExactRound ? n - r0 : (uint32_t)kExactRound;
+    if (!staged) {
+      // both pieces requested before either is stored (rows past the round's end re-read row 0)
+      const uint32_t row0 = tid >> 4, row1 = (kCandThreads + tid) >> 4, c8 = 8 * (tid & 15);
+      const uint4 v0 = *reinterpret_cast<const uint4*>(kseq + (size_t)eidx[r0 + (row0 < m ? row0 : 0)] * kIdxDim + c8);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(kseq + (size_t)eidx[r0 + (row1 < m ? row1 : 0)] * kIdxDim + c8);
+      if (row0 < m) *reinterpret_cast<uint4*>(&X.krows[row0][c8]) = v0;
+      if (row1 < m) *reinterpret_cast<uint4*>(&X.krows[row1][c8]) = v1;
+      __syncthreads();
+    }
+    const uint8_t* rows = staged ? erow : nullptr;
+    const int nslot = (int)m > wave ? ((int)m - wave + 3) / 4 : 0;  // this wave's entries this round
+    const int chains = (nslot + 1) / 2;
+    if (chains == 1) exact_dots<1>(sq, X, rows, wave, lane);
+    else if (chains == 2) exact_dots<2>(sq, X, rows, wave, lane);
+    else if (chains > 2) exact_dots<4>(sq, X, rows, wave, lane);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (h == 0 && e < n) {
-      const double* hr = &hrel[lane & 32];
+    if (lane < nslot) {
+      const double* dr = X.dots[wave][lane];
       double sc = 0.0;
 #pragma unroll
-      for (int hh = 0; hh < kIdxHeads; ++hh) sc = fma((double)w[hh], hr[hh], sc);
-      put(e, sc);
+      for (int hh = 0; hh < kIdxHeads; ++hh) sc = fma((double)w[hh], dr[hh] > 0.0 ? dr[hh] : 0.0, sc);
+      put(r0 + 4 * lane + wave, sc);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __syncthreads();
   }
 }
 
@@ -817,8 +915,10 @@ struct alignas(16) CandLds {
   uint16_t ctile[kCandTiles];   // candidate tiles (offset in the block's range), ascending
   uint16_t cmask[kCandTiles];   // entries of each candidate tile that reach the threshold
   uint32_t eidx[kCandMax];      // passing entries, ascending
-  double escore[kCandMax];      // their fp64 scores
-  double hrel[kCandThreads / 64][64];  // per wave: ReLU(dot) of (entry, head) for the in-order head fold
+  uint16_t rowbase[kCandTiles]; // first staged row of each candidate tile's passing entries
+  uint8_t erow[kCandMax];       // staged row of each passing entry
+  uint32_t n_staged;
+  ExactLds x;                   // rows and per-head dots of the fp64 rescoring
 };
 
 // Candidates of tiles [x*kCandTiles, (x+1)*kCandTiles) of query t
@@ -830,7 +930,7 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   __shared__ CandLds L;
   const int t = blockIdx.y;
   const int x = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x;
   TileWs w = tile_ws(ws, T, N, cap);
   uint32_t* st = stats + (size_t)t * CSA2_STATS_WORDS;
   uint2* rec = w.table + (size_t)t * cand_blocks(N) + x;
@@ -848,6 +948,7 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   const float tau = __uint_as_float(st[1]);
   stage_query(L.sq, q_idx + (size_t)t * kIdxHeads * kIdxDim, tid, kCandThreads);
   if (tid < kIdxHeads) L.w[tid] = w_idx[(size_t)t * kIdxHeads + tid];
+  if (tid == 0) L.n_staged = 0u;
   const double thr = next_down((double)tau - 2.0 * (double)eps);
 
   // 1. candidate tiles in order
@@ -857,9 +958,9 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   if (cand) L.ctile[p] = (uint16_t)tid;
   __syncthreads();
 
-  // 2. fp32 scores of the candidate tiles (the scan's arithmetic)
+  // 2. fp32 scores of the candidate tiles (the scan's arithmetic); passing rows staged
   const uint16_t* kseq = k_idx + (size_t)(t / q_per_seq) * N * kIdxDim;
-  cand_tile_masks(L.sq, L.w, L.ctile, L.cmask, n_tiles, tile0, kseq, nv, thr);
+  cand_tile_masks(L.sq, L.w, L.ctile, L.cmask, n_tiles, tile0, kseq, nv, thr, L.x, L.rowbase, &L.n_staged);
   __syncthreads();
 
   // 3. output slots in (tile, entry) order: thread ci expands candidate tile ci
@@ -875,20 +976,17 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   }
   if ((uint32_t)tid < n_tiles) {
     uint32_t m = L.cmask[tid];
+    uint32_t row = L.rowbase[tid];
     const int64_t e0 = (tile0 + L.ctile[tid]) * kTileKeys;
     while (m) {
       const int c = __ffs(m) - 1;
       m &= m - 1;
+      L.erow[q0] = (uint8_t)(row < (uint32_t)kExactRound ? row : 0u);
       L.eidx[q0++] = (uint32_t)(e0 + c);
+      ++row;
     }
   }
-  __syncthreads();
-
-  // 4. fp64 scores of the passing entries, reference operation order
-  exact_entry_scores(L.sq, L.w, L.eidx, n_pass, kseq, L.hrel[wave], [&](uint32_t e, double sc) { L.escore[e] = sc; });
-  __syncthreads();
-
-  // 5. the block's fixed slots, or a reserved run of shared ones, and copy out
+  // 4. the block's fixed slots, or a reserved run of shared ones
   if (tid == 0) {
     uint32_t off = (uint32_t)x * (uint32_t)slots;
     if (n_pass > (uint32_t)slots) {
@@ -903,11 +1001,14 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   const uint32_t base = L.base;
   for (uint32_t e = tid; e < n_pass; e += kCandThreads) {
     const uint64_t pos = (uint64_t)base + e;
-    if (pos < (uint64_t)cap) {
-      w.cscore[(size_t)t * cap + pos] = L.escore[e];
-      w.cidx[(size_t)t * cap + pos] = L.eidx[e];
-    }
+    if (pos < (uint64_t)cap) w.cidx[(size_t)t * cap + pos] = L.eidx[e];
   }
+
+  // 5. fp64 scores of the passing entries, reference operation order, into the slots
+  double* cs = w.cscore + (size_t)t * cap;
+  exact_entry_scores(L.sq, L.w, L.eidx, L.erow, n_pass, kseq, L.x, [&](uint32_t e, double sc) {
+    if ((uint64_t)base + e < (uint64_t)cap) cs[base + e] = sc;
+  });
 }
 
 // LDS of a select block.
@@ -968,12 +1069,14 @@ __device__ __forceinline__ void wave_pick(const uint32_t* hist, uint32_t rank, u
   *left = (uint32_t)__shfl((int)l, src, 64);
 }
 
-// The kk-th largest of L.v[0..n) (1 <= kk <= n), given their range [lo, hi]:
+// The kk-th largest of L.v[0..n) (1 <= kk <= n), given their range [lo, hi]
+// (NT threads; L: the LDS layout of the caller, with the members used here):
 // value-binned levels (each keeps the chosen bin's min and max) narrow it to
 // at most 64 members, which one wave ranks directly; a bin that stays larger
 // is resolved exactly by radix passes over the 64-bit order keys.
 // L.hist / L.bmin / L.bmax must be cleared on entry.
-__device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk, double lo, double hi, uint32_t* n_gt,
+template <int NT, class Lds>
+__device__ double kth_largest_f64(Lds& L, uint32_t n, uint32_t kk, double lo, double hi, uint32_t* n_gt,
                                  uint32_t* n_eq) {
   const int tid = threadIdx.x;
   uint32_t r = kk;
@@ -984,7 +1087,7 @@ __device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk, double 
   // below narrow the range with per-bin minima and maxima.
   if (lo < hi && n > 64) {
     const double scale = 256.0 / (hi - lo);
-    for (uint32_t i = tid; i < n; i += kSelThreads) atomicAdd(&L.hist[bin_f64(L.v[i], lo, scale)], 1u);
+    for (uint32_t i = tid; i < n; i += NT) atomicAdd(&L.hist[bin_f64(L.v[i], lo, scale)], 1u);
     __syncthreads();
     if (tid < 64) {
       uint32_t b, left;
@@ -1002,7 +1105,7 @@ __device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk, double 
     __syncthreads();
     if (L.pick[0] <= 64) {
       const uint32_t bsel = L.pick2, cnt_b = L.pick[0], rr = L.pick[1];
-      for (uint32_t i = tid; i < n; i += kSelThreads) {
+      for (uint32_t i = tid; i < n; i += NT) {
         const double v = L.v[i];
         if (bin_f64(v, lo, scale) == bsel) L.bin_vals[atomicAdd(&L.n_bin, 1u)] = v;
       }
@@ -1030,7 +1133,7 @@ __device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk, double 
   }
   for (int level = 0; level < 6 && lo < hi && count > 64; ++level) {
     const double scale = 256.0 / (hi - lo);
-    for (uint32_t i = tid; i < n; i += kSelThreads) {
+    for (uint32_t i = tid; i < n; i += NT) {
       const double v = L.v[i];
       if (v >= lo && v <= hi) {
         const uint32_t b = bin_f64(v, lo, scale);
@@ -1069,7 +1172,7 @@ __device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk, double 
   if (count <= 64) {
     if (tid == 0) L.n_bin = 0;
     __syncthreads();
-    for (uint32_t i = tid; i < n; i += kSelThreads) {
+    for (uint32_t i = tid; i < n; i += NT) {
       const double v = L.v[i];
       if (v >= lo && v <= hi) {
         const uint32_t p = atomicAdd(&L.n_bin, 1u);
@@ -1098,7 +1201,7 @@ __device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk, double 
   }
   unsigned long long pre = 0, mask = 0;
   for (int pass = 0; pass < 8; ++pass) {
-    for (uint32_t i = tid; i < n; i += kSelThreads) {
+    for (uint32_t i = tid; i < n; i += NT) {
       const double v = L.v[i];
       const unsigned long long key = f64_key(v);
       if (v >= lo && v <= hi && (key & mask) == pre)
@@ -1119,7 +1222,7 @@ __device__ double kth_largest_f64(SelectLds& L, uint32_t n, uint32_t kk, double 
   }
   const double V = key_f64(pre);
   uint32_t gt = 0, eq = 0;
-  for (uint32_t i = tid; i < n; i += kSelThreads) {
+  for (uint32_t i = tid; i < n; i += NT) {
     gt += L.v[i] > V;
     eq += L.v[i] == V;
   }
@@ -1298,7 +1401,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     for (int i = 1; i < kSelThreads / 64; ++i) { lo = fmin(lo, L.red[0][i]); hi = fmax(hi, L.red[1][i]); }
   }
   uint32_t n_gt, n_eq;
-  const double V = kth_largest_f64(L, cnt, kk, lo, hi, &n_gt, &n_eq);
+  const double V = kth_largest_f64<kSelThreads>(L, cnt, kk, lo, hi, &n_gt, &n_eq);
 
   // Entries above V are in; of those equal to V, the lowest indices (first in
   // order).  Selection masks per 64 consecutive candidates (word j covers
@@ -1409,8 +1512,11 @@ struct alignas(16) HsiCandLds {
   uint16_t cmask[kCandTiles];
   uint32_t tpre[kCandTiles];               // passing entries before candidate tile c
   uint32_t eidx[kCandMax];                 // one round of passing entries
+  uint16_t rowbase[kCandTiles];            // first staged row of each candidate tile's passing entries
+  uint8_t erow[kCandMax];                  // staged row of each passing entry (first round)
+  uint32_t n_staged;
   unsigned long long bkey[kHsiPerCand];    // per block: largest fp64 key so far (0: none)
-  double hrel[kCandThreads / 64][64];
+  ExactLds x;
 };
 
 // Candidate blocks of tiles [x*kCandTiles, (x+1)*kCandTiles) of query t
@@ -1425,7 +1531,7 @@ __global__ __launch_bounds__(kCandThreads, 4) void hsi_cand_kernel(
   __shared__ HsiCandLds L;
   const int t = blockIdx.y;
   const int x = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int64_t nblk = cand_blocks(N);
   HsiWs w = hsi_ws(ws, T, N);
   uint32_t* cnt = w.count + (size_t)t * nblk + x;
@@ -1443,6 +1549,7 @@ __global__ __launch_bounds__(kCandThreads, 4) void hsi_cand_kernel(
   stage_query(L.sq, q_idx + (size_t)t * kIdxHeads * kIdxDim, tid, kCandThreads);
   if (tid < kIdxHeads) L.w[tid] = w_idx[(size_t)t * kIdxHeads + tid];
   for (int i = tid; i < kHsiPerCand; i += kCandThreads) L.bkey[i] = 0ull;
+  if (tid == 0) L.n_staged = 0u;
   const double thr = next_down((double)tau - 2.0 * (double)eps);
 
   // candidate tiles in order, then their passing entries (fp32, the scan's arithmetic)
@@ -1452,7 +1559,7 @@ __global__ __launch_bounds__(kCandThreads, 4) void hsi_cand_kernel(
   if (cand) L.ctile[p] = (uint16_t)tid;
   __syncthreads();
   const uint16_t* kseq = k_idx + (size_t)(t / q_per_seq) * N * kIdxDim;
-  cand_tile_masks(L.sq, L.w, L.ctile, L.cmask, n_tiles, tile0, kseq, nv, thr);
+  cand_tile_masks(L.sq, L.w, L.ctile, L.cmask, n_tiles, tile0, kseq, nv, thr, L.x, L.rowbase, &L.n_staged);
   __syncthreads();
   const uint32_t mine = (uint32_t)tid < n_tiles ? (uint32_t)__popc((uint32_t)L.cmask[tid]) : 0u;
   uint32_t n_pass;
@@ -1466,17 +1573,22 @@ __global__ __launch_bounds__(kCandThreads, 4) void hsi_cand_kernel(
     if ((uint32_t)tid < n_tiles) {
       uint32_t m = L.cmask[tid];
       uint32_t r = L.tpre[tid];
+      uint32_t row = L.rowbase[tid];
       const int64_t e0 = (tile0 + L.ctile[tid]) * kTileKeys;
       while (m && r < r0 + kCandMax) {
         const int c = __ffs(m) - 1;
         m &= m - 1;
-        if (r >= r0) L.eidx[r - r0] = (uint32_t)(e0 + c);
+        if (r >= r0) {
+          L.eidx[r - r0] = (uint32_t)(e0 + c);
+          L.erow[r - r0] = (uint8_t)(row < (uint32_t)kExactRound ? row : 0u);
+        }
         ++r;
+        ++row;
       }
     }
     __syncthreads();
     const uint32_t n = n_pass - r0 < (uint32_t)kCandMax ? n_pass - r0 : (uint32_t)kCandMax;
-    exact_entry_scores(L.sq, L.w, L.eidx, n, kseq, L.hrel[wave], [&](uint32_t e, double sc) {
+    exact_entry_scores(L.sq, L.w, L.eidx, r0 == 0 ? L.erow : nullptr, n, kseq, L.x, [&](uint32_t e, double sc) {
       atomicMax(&L.bkey[(L.eidx[e] - (uint32_t)e_base) / kHsiBlock], (unsigned long long)f64_key(sc));
     });
     __syncthreads();
@@ -1506,66 +1618,61 @@ __device__ __forceinline__ void hsi_key(double v, uint32_t blk, unsigned long lo
   *lo = ~blk;
 }
 
-// Pool of query t (grid T, kSelThreads threads): over the records of all
-// candidate blocks, the 2048th block in the order (score desc, block asc) is
-// found by radix passes over the 96-bit keys (score key, ~block); the pool is
-// the visible entries of every block at or before it, ascending.
-__global__ __launch_bounds__(kSelThreads) void hsi_select_kernel(const int32_t* __restrict__ q_pos, int ratio,
-                                                                 int64_t N, void* ws, int T,
-                                                                 int32_t* __restrict__ pool) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wsum[2][kSelThreads / 64];
-  __shared__ uint32_t pick[3];
-  __shared__ unsigned long long found_hi;
-  __shared__ uint32_t found_lo;
-  const int t = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int64_t nv = n_visible(q_pos, t, ratio, N);
-  int32_t* out = pool + (size_t)t * kHsiPool;
-  if (nv <= kHsiPool) {  // every visible block is kept
-    for (int i = tid; i < kHsiPool; i += kSelThreads) out[i] = i < nv ? i : -1;
-    return;
-  }
-  const int64_t nblk = cand_blocks(N);
-  HsiWs w = hsi_ws(ws, T, N);
-  const uint32_t* cnt = w.count + (size_t)t * nblk;
-  const uint32_t* rb = w.rblk + (size_t)t * nblk * kHsiPerCand;
-  const double* rv = w.rmax + (size_t)t * nblk * kHsiPerCand;
-  // thread tid visits candidate blocks x = tid, tid + kSelThreads, ...; record j
-  // of block x is at [x * kHsiPerCand + j]
+constexpr int kHsiSelThreads = 1024;
+constexpr int kHsiSelLds = 4096;  // records ranked in LDS; more go through the global-memory passes
 
-  // radix passes: 8 bits at a time over the 96-bit key, most significant
-  // first, until the chosen bin holds a single record (that record is then
-  // the 2048th) or all 96 bits are fixed
+struct alignas(16) HsiSelLds {
+  double v[kHsiSelLds];               // record block scores, ascending by block
+  uint32_t blk[kHsiSelLds];           // record blocks
+  uint32_t off[kHsiSelThreads];       // record offsets of a chunk of candidate blocks
+  uint32_t kblk[kHsiBlocks];          // kept blocks, ascending
+  unsigned long long bmin[256], bmax[256];
+  uint32_t hist[256];
+  uint32_t wsum[2][kHsiSelThreads / 64];
+  uint32_t pick[3];
+  uint32_t pick2;
+  uint32_t n_bin;
+  double red[2][kHsiSelThreads / 64];
+  double range[2];
+  double bin_vals[64];
+  double result;
+  uint64_t selm[kHsiSelLds / 64], eqm[kHsiSelLds / 64];
+  uint32_t wbase[kHsiSelLds / 64];
+  unsigned long long found_hi;
+  uint32_t found_lo;
+};
+
+// The 96-bit key of the rank-th record (1-based, from the top) among n records
+// read through rec(i, &hi, &lo): radix passes of 8 bits, most significant
+// first, until the chosen bin holds a single record (that record is the
+// answer) or all 96 bits are fixed.  Keys are distinct (block indices are).
+template <class Rec>
+__device__ void hsi_kth_key(HsiSelLds& L, int64_t n, uint32_t rank, Rec rec, unsigned long long* key_hi,
+                            uint32_t* key_lo) {
+  const int tid = threadIdx.x;
   unsigned long long pre_hi = 0, mask_hi = 0;
   uint32_t pre_lo = 0, mask_lo = 0;
-  uint32_t rank = kHsiBlocks;  // rank (1-based, from the top) still to find among the keys with the prefix
   for (int pass = 0; pass < 12; ++pass) {
-    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0u;
+    for (int i = tid; i < 256; i += blockDim.x) L.hist[i] = 0u;
     __syncthreads();
     const int sh = pass < 8 ? 56 - 8 * pass : 24 - 8 * (pass - 8);
-    for (int64_t x = tid; x < nblk; x += kSelThreads) {
-      const uint32_t c = cnt[x];
-      for (uint32_t j = 0; j < c; ++j) {
-        unsigned long long hi;
-        uint32_t lo;
-        hsi_key(rv[x * kHsiPerCand + j], rb[x * kHsiPerCand + j], &hi, &lo);
-        if ((hi & mask_hi) == pre_hi && (lo & mask_lo) == pre_lo) {
-          const uint32_t d = pass < 8 ? (uint32_t)(hi >> sh) & 255u : (lo >> sh) & 255u;
-          atomicAdd(&hist[d], 1u);
-        }
-      }
+    for (int64_t i = tid; i < n; i += blockDim.x) {
+      unsigned long long hi;
+      uint32_t lo;
+      rec(i, &hi, &lo);
+      if ((hi & mask_hi) == pre_hi && (lo & mask_lo) == pre_lo)
+        atomicAdd(&L.hist[pass < 8 ? (uint32_t)(hi >> sh) & 255u : (lo >> sh) & 255u], 1u);
     }
     __syncthreads();
     if (tid < 64) {
-      uint32_t b, left;
-      wave_pick(hist, rank, &b, &left);
-      if (tid == 0) { pick[0] = b; pick[1] = left; pick[2] = hist[b]; }
+      uint32_t bsel, left;
+      wave_pick(L.hist, rank, &bsel, &left);
+      if (tid == 0) { L.pick[0] = bsel; L.pick[1] = left; L.pick[2] = L.hist[bsel]; }
     }
     __syncthreads();
-    const uint32_t d = pick[0];
-    rank = pick[1];
-    const bool single = pick[2] == 1u;
+    const uint32_t d = L.pick[0];
+    rank = L.pick[1];
+    const bool single = L.pick[2] == 1u;
     if (pass < 8) {
       pre_hi |= (unsigned long long)d << sh;
       mask_hi |= 255ull << sh;
@@ -1575,63 +1682,210 @@ __global__ __launch_bounds__(kSelThreads) void hsi_select_kernel(const int32_t* 
     }
     __syncthreads();
     if (single) {
-      // the one record with this prefix: its whole key
-      for (int64_t x = tid; x < nblk; x += kSelThreads) {
-        const uint32_t c = cnt[x];
-        for (uint32_t j = 0; j < c; ++j) {
-          unsigned long long hi;
-          uint32_t lo;
-          hsi_key(rv[x * kHsiPerCand + j], rb[x * kHsiPerCand + j], &hi, &lo);
-          if ((hi & mask_hi) == pre_hi && (lo & mask_lo) == pre_lo) { found_hi = hi; found_lo = lo; }
-        }
+      for (int64_t i = tid; i < n; i += blockDim.x) {
+        unsigned long long hi;
+        uint32_t lo;
+        rec(i, &hi, &lo);
+        if ((hi & mask_hi) == pre_hi && (lo & mask_lo) == pre_lo) { L.found_hi = hi; L.found_lo = lo; }
       }
       __syncthreads();
-      pre_hi = found_hi;
-      pre_lo = found_lo;
+      pre_hi = L.found_hi;
+      pre_lo = L.found_lo;
+      __syncthreads();
       break;
     }
   }
-  // (pre_hi, pre_lo) is the key of the 2048th block; keys are unique (block
-  // indices differ), so the kept blocks are exactly those with key >= it.
-  // Visible entries of the kept blocks, in block order: per candidate block,
-  // count the entries of its kept records, then an ordered scan gives offsets.
-  uint32_t written = 0;
-  for (int64_t x0 = 0; x0 < nblk; x0 += kSelThreads) {
+  *key_hi = pre_hi;
+  *key_lo = pre_lo;
+}
+
+// Pool of query t (grid T, kHsiSelThreads threads): over the records of all
+// candidate blocks, the 2048th block in the order (score desc, block asc) is
+// found by radix passes over the 96-bit keys (score key, ~block); the pool is
+// the visible entries of every block at or before it, ascending.  The records
+// (ascending by block: candidate blocks in order, each in block order) are
+// first copied to LDS when they fit.
+__global__ __launch_bounds__(kHsiSelThreads) void hsi_select_kernel(const int32_t* __restrict__ q_pos, int ratio,
+                                                                    int64_t N, void* ws, int T,
+                                                                    int32_t* __restrict__ pool) {
+  __shared__ HsiSelLds L;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t nv = n_visible(q_pos, t, ratio, N);
+  int32_t* out = pool + (size_t)t * kHsiPool;
+  if (nv <= kHsiPool) {  // every visible block is kept
+    for (int i = tid; i < kHsiPool; i += kHsiSelThreads) out[i] = i < nv ? i : -1;
+    return;
+  }
+  const int64_t nblk = cand_blocks(N);
+  HsiWs w = hsi_ws(ws, T, N);
+  const uint32_t* cnt = w.count + (size_t)t * nblk;
+  const uint32_t* rb = w.rblk + (size_t)t * nblk * kHsiPerCand;
+  const double* rv = w.rmax + (size_t)t * nblk * kHsiPerCand;
+
+  // 1. records into LDS, chunk by chunk of candidate blocks
+  uint32_t n_rec = 0;
+  bool in_lds = true;
+  for (int64_t x0 = 0; x0 < nblk && in_lds; x0 += kHsiSelThreads) {
     const int64_t x = x0 + tid;
-    uint32_t mine = 0;
-    if (x < nblk) {
-      const uint32_t c = cnt[x];
-      for (uint32_t j = 0; j < c; ++j) {
-        unsigned long long hi;
-        uint32_t lo;
-        const uint32_t blk = rb[x * kHsiPerCand + j];
-        hsi_key(rv[x * kHsiPerCand + j], blk, &hi, &lo);
-        if (hi > pre_hi || (hi == pre_hi && lo >= pre_lo)) {
-          const int64_t e0 = (int64_t)blk * kHsiBlock;
-          mine += (uint32_t)(nv - e0 < kHsiBlock ? nv - e0 : kHsiBlock);
+    const uint32_t c = x < nblk ? cnt[x] : 0u;
+    uint32_t tot;
+    const uint32_t o = block_excl_scan(c, L.wsum[0], &tot);
+    L.off[tid] = o;
+    __syncthreads();
+    if (n_rec + tot > (uint32_t)kHsiSelLds) {
+      in_lds = false;
+      break;
+    }
+    // record p of the chunk: its candidate block is the last one whose offset is <= p
+    for (uint32_t p0 = 0; p0 < tot; p0 += 4 * kHsiSelThreads) {
+      double v[4];
+      uint32_t bk[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t p = p0 + u * kHsiSelThreads + tid;
+        const uint32_t pp = p < tot ? p : 0u;
+        int lo = 0, hi = kHsiSelThreads - 1;  // largest xi with off[xi] <= pp (counts may be zero)
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (L.off[mid] <= pp) lo = mid; else hi = mid - 1;
+        }
+        const size_t r = (size_t)(x0 + lo) * kHsiPerCand + (pp - L.off[lo]);
+        v[u] = rv[r];
+        bk[u] = rb[r];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t p = p0 + u * kHsiSelThreads + tid;
+        if (p < tot) {
+          L.v[n_rec + p] = v[u];
+          L.blk[n_rec + p] = bk[u];
         }
       }
     }
-    uint32_t tot;
-    uint32_t o = written + block_excl_scan(mine, wsum[0], &tot);
-    if (x < nblk) {
-      const uint32_t c = cnt[x];
-      for (uint32_t j = 0; j < c; ++j) {
-        unsigned long long hi;
-        uint32_t lo;
-        const uint32_t blk = rb[x * kHsiPerCand + j];
-        hsi_key(rv[x * kHsiPerCand + j], blk, &hi, &lo);
-        if (hi > pre_hi || (hi == pre_hi && lo >= pre_lo)) {
-          const int64_t e0 = (int64_t)blk * kHsiBlock;
-          const int64_t e1 = nv - e0 < kHsiBlock ? nv : e0 + kHsiBlock;
-          for (int64_t e = e0; e < e1; ++e)
-            if (o < (uint32_t)kHsiPool) out[o++] = (int32_t)e;
+    n_rec += tot;
+    __syncthreads();
+  }
+
+  if (in_lds) {
+    // 2. the 2048th largest block score V (value bins, then a direct rank)
+    double lo = INFINITY, hi = -INFINITY;
+    for (uint32_t i = tid; i < n_rec; i += kHsiSelThreads) { lo = fmin(lo, L.v[i]); hi = fmax(hi, L.v[i]); }
+    for (int i = tid; i < 256; i += kHsiSelThreads) { L.hist[i] = 0u; L.bmin[i] = ~0ull; L.bmax[i] = 0ull; }
+    {
+      const int lane = tid & 63, wv = tid >> 6;
+      lo = wave_min_f64_dpp(lo);
+      hi = wave_max_f64_dpp(hi);
+      if (lane == 0) { L.red[0][wv] = lo; L.red[1][wv] = hi; }
+      __syncthreads();
+      lo = L.red[0][0];
+      hi = L.red[1][0];
+      for (int i = 1; i < kHsiSelThreads / 64; ++i) { lo = fmin(lo, L.red[0][i]); hi = fmax(hi, L.red[1][i]); }
+    }
+    uint32_t n_gt, n_eq;
+    const double V = kth_largest_f64<kHsiSelThreads>(L, n_rec, kHsiBlocks, lo, hi, &n_gt, &n_eq);
+    // 3. kept: scores above V, and of those equal to V the lowest blocks (first in
+    // record order).  Masks per 64 records, then one wave turns them into ranks.
+    const int lane = tid & 63, wv = tid >> 6;
+    const uint32_t need_eq = kHsiBlocks - n_gt;
+    const int nwords = (int)((n_rec + 63) / 64);
+    for (int j = wv; j < nwords; j += kHsiSelThreads / 64) {
+      const uint32_t i = 64u * j + lane;
+      const double v = i < n_rec ? L.v[i] : -INFINITY;
+      const uint64_t gt = __ballot(v > V), eq = __ballot(v == V);
+      if (lane == 0) { L.selm[j] = gt; L.eqm[j] = eq; }
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const int j = tid;
+      uint64_t sel = j < nwords ? L.selm[j] : 0ull, eq = j < nwords ? L.eqm[j] : 0ull;
+      if (need_eq >= n_eq) {
+        sel |= eq;
+      } else {
+        const uint32_t c = (uint32_t)__popcll(eq);
+        uint32_t incl = c;
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t x = __shfl_up(incl, o, 64);
+          if (j >= o) incl += x;
+        }
+        uint32_t take = incl - c < need_eq ? need_eq - (incl - c) : 0u;
+        while (eq && take) {
+          const uint64_t low = eq & (~eq + 1ull);
+          sel |= low;
+          eq ^= low;
+          --take;
         }
       }
+      const uint32_t c = (uint32_t)__popcll(sel);
+      uint32_t incl = c;
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t x = __shfl_up(incl, o, 64);
+        if (j >= o) incl += x;
+      }
+      if (j < nwords) { L.selm[j] = sel; L.wbase[j] = incl - c; }
+    }
+    __syncthreads();
+    for (int j = wv; j < nwords; j += kHsiSelThreads / 64) {
+      const uint64_t sel = L.selm[j];
+      if ((sel >> lane) & 1ull) {
+        const uint32_t r = L.wbase[j] + (uint32_t)__popcll(sel & ((1ull << lane) - 1ull));
+        if (r < (uint32_t)kHsiBlocks) L.kblk[r] = L.blk[64 * j + lane];
+      }
+    }
+    __syncthreads();
+    // 4. every kept block but the last visible one is full, so kept block r fills
+    // pool slots 8r .. 8r + 7 (slots past n_vis in the last block get -1)
+    for (int i = tid; i < kHsiPool; i += kHsiSelThreads) {
+      const int64_t e = (int64_t)L.kblk[i / kHsiBlock] * kHsiBlock + (i % kHsiBlock);
+      out[i] = e < nv ? (int32_t)e : -1;
+    }
+    return;
+  }
+
+  // beyond LDS: radix passes over every record slot where the candidate blocks left them
+  unsigned long long piv_hi;
+  uint32_t piv_lo;
+  hsi_kth_key(L, nblk * kHsiPerCand, kHsiBlocks, [&](int64_t i, unsigned long long* hi, uint32_t* lo) {
+    const int64_t x = i / kHsiPerCand;
+    const uint32_t j = (uint32_t)(i % kHsiPerCand);
+    if (j < cnt[x]) hsi_key(rv[i], rb[i], hi, lo);
+    else { *hi = 0ull; *lo = 0u; }  // below every record's key: never counted
+  }, &piv_hi, &piv_lo);
+
+  // visible entries of the kept blocks (key >= pivot), ascending: per chunk of candidate
+  // blocks, an ordered scan of their kept entries gives the offsets
+  const auto kept = [&](unsigned long long hi, uint32_t lo) { return hi > piv_hi || (hi == piv_hi && lo >= piv_lo); };
+  const auto entries = [&](uint32_t blk) {
+    const int64_t e0 = (int64_t)blk * kHsiBlock;
+    return (uint32_t)(nv - e0 < kHsiBlock ? nv - e0 : kHsiBlock);
+  };
+  uint32_t written = 0;
+  for (int64_t x0 = 0; x0 < nblk; x0 += kHsiSelThreads) {
+    const int64_t x = x0 + tid;
+    const uint32_t c = x < nblk ? cnt[x] : 0u;
+    uint32_t mine = 0;
+    for (uint32_t j = 0; j < c; ++j) {
+      unsigned long long hi;
+      uint32_t lo;
+      hsi_key(rv[x * kHsiPerCand + j], rb[x * kHsiPerCand + j], &hi, &lo);
+      if (kept(hi, lo)) mine += entries(rb[x * kHsiPerCand + j]);
+    }
+    uint32_t tot;
+    uint32_t o = written + block_excl_scan(mine, L.wsum[1], &tot);
+    for (uint32_t j = 0; j < c; ++j) {
+      unsigned long long hi;
+      uint32_t lo;
+      const uint32_t blk = rb[x * kHsiPerCand + j];
+      hsi_key(rv[x * kHsiPerCand + j], blk, &hi, &lo);
+      if (!kept(hi, lo)) continue;
+      const uint32_t ne = entries(blk);
+      for (uint32_t e = 0; e < ne; ++e)
+        if (o + e < (uint32_t)kHsiPool) out[o + e] = (int32_t)(blk * kHsiBlock + e);
+      o += ne;
     }
     written += tot;
   }
-  for (int64_t i = (int64_t)written + tid; i < kHsiPool; i += kSelThreads) out[i] = -1;
+  for (int64_t i = (int64_t)written + tid; i < kHsiPool; i += kHsiSelThreads) out[i] = -1;
 }
 
 }  // namespace csa2
@@ -1743,7 +1997,7 @@ extern "C" csa2_status csa2_hsi_pool(const float* tile_max, const uint32_t* stat
                      p.parts(), q, w_idx, q_pos, ratio, q_per_seq, N, kHsiBlocks, (int64_t)kHsiPool);
   hipLaunchKernelGGL(hsi_cand_kernel, dim3((unsigned)cand_blocks(N), T), dim3(kCandThreads), 0, st, tile_max, q,
                      w_idx, kx, q_pos, ratio, q_per_seq, N, workspace, T);
-  hipLaunchKernelGGL(hsi_select_kernel, dim3(T), dim3(kSelThreads), 0, st, q_pos, ratio, N, workspace, T, pool);
+  hipLaunchKernelGGL(hsi_select_kernel, dim3(T), dim3(kHsiSelThreads), 0, st, q_pos, ratio, N, workspace, T, pool);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   return CSA2_OK;
 }
