@@ -784,16 +784,17 @@ struct alignas(16) ExactLds {
 // fp32 scores of candidate tiles ctile[0..n_tiles) (offsets from tile0) with
 // the scan's arithmetic; cmask[c] gets the entries of tile c that are visible
 // and reach thr.  Wave w takes tiles w, w + 4, ...; the rows of up to kMaskTiles of
-// its tiles are requested before any is scored.  The rows of the passing
-// entries, already in registers, are also written to X.krows for the fp64
-// rescoring: tile c's passing entries take rows rowbase[c], rowbase[c] + 1, ...
-// in entry order (rows reserved with an LDS counter, n_staged, that must be zero
-// on entry; rows past kExactRound are not written).
+// its tiles are requested before any is scored.  With kStage the rows of the
+// passing entries, already in registers, are also written to X->krows for the
+// fp64 rescoring: tile c's passing entries take rows rowbase[c], rowbase[c] + 1,
+// ... in entry order (rows reserved with an LDS counter, n_staged, that must be
+// zero on entry; rows past kExactRound are not written).
 constexpr int kMaskTiles = 3;
+template <bool kStage>
 __device__ __forceinline__ void cand_tile_masks(const uint16_t* __restrict__ sq, const float* __restrict__ w,
                                                 const uint16_t* __restrict__ ctile, uint16_t* __restrict__ cmask,
                                                 uint32_t n_tiles, int64_t tile0, const uint16_t* __restrict__ kseq,
-                                                int64_t nv, double thr, ExactLds& X, uint16_t* __restrict__ rowbase,
+                                                int64_t nv, double thr, ExactLds* X, uint16_t* __restrict__ rowbase,
                                                 uint32_t* n_staged) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, g = lane >> 4;
@@ -817,17 +818,17 @@ __device__ __forceinline__ void cand_tile_masks(const uint16_t* __restrict__ sq,
       const int64_t s = (tile0 + ctile[ci]) * kTileKeys + col;
       const float sc = tile_score(sq, kv[u], wr, col, g);
       const uint32_t m16 = (uint32_t)(__ballot(s < nv && (double)sc >= thr) & 0xFFFFull);
-      uint32_t base = 0;
-      if (lane == 0 && m16) base = atomicAdd(n_staged, (uint32_t)__popc(m16));
-      base = (uint32_t)__shfl((int)base, 0, 64);
-      if (lane == 0) {
-        cmask[ci] = (uint16_t)m16;
-        rowbase[ci] = (uint16_t)(base < (uint32_t)kExactRound ? base : (uint32_t)kExactRound);
-      }
-      const uint32_t row = base + (uint32_t)__popc(m16 & ((1u << col) - 1u));
-      if (((m16 >> col) & 1u) && row < (uint32_t)kExactRound) {
+      if (lane == 0) cmask[ci] = (uint16_t)m16;
+      if (kStage) {
+        uint32_t base = 0;
+        if (lane == 0 && m16) base = atomicAdd(n_staged, (uint32_t)__popc(m16));
+        base = (uint32_t)__shfl((int)base, 0, 64);
+        if (lane == 0) rowbase[ci] = (uint16_t)(base < (uint32_t)kExactRound ? base : (uint32_t)kExactRound);
+        const uint32_t row = base + (uint32_t)__popc(m16 & ((1u << col) - 1u));
+        if (((m16 >> col) & 1u) && row < (uint32_t)kExactRound) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&X.krows[row][32 * j + 8 * g]) = kv[u][j];
+          for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&X->krows[row][32 * j + 8 * g]) = kv[u][j];
+        }
       }
     }
   }
@@ -906,6 +907,52 @@ __device__ __forceinline__ void exact_entry_scores(const uint16_t* __restrict__ 
   }
 }
 
+// fp64 scores of entries eidx[0..n) in the reference's operation order, one
+// wave per two entries and no block barrier (the top-k candidates: a few per
+// block): lane (e = lane / 32, h = lane % 32) forms dot(q_h, K_e) with 128
+// sequential fmas, reading the key row straight from memory (the tile pass has
+// just brought it on chip), then lane h == 0 folds the entry's 32 heads in order
+// from hrel (this wave's 64 doubles in LDS).  put(e, score) receives each result.
+template <class Put>
+__device__ __forceinline__ void exact_entry_scores_wave(const uint16_t* __restrict__ sq, const float* __restrict__ w,
+                                                        const uint32_t* __restrict__ eidx, uint32_t n,
+                                                        const uint16_t* __restrict__ kseq, double* hrel, Put put) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane & 31;
+  for (uint32_t e0 = 2 * wave; e0 < n; e0 += 2 * (kCandThreads / 64)) {
+    const uint32_t e = e0 + (lane >> 5);
+    const uint16_t* kr = kseq + (size_t)eidx[e < n ? e : e0] * kIdxDim;
+    const uint16_t* qr = &sq[h * kQRowPad];
+    double d = 0.0;
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+      const uint4 kq = *reinterpret_cast<const uint4*>(kr + 8 * i);
+      const uint4 qq = *reinterpret_cast<const uint4*>(qr + 8 * i);
+      const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
+      const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        d = fma((double)bf16lo(qw[c]), (double)bf16lo(kw[c]), d);
+        d = fma((double)bf16hi(qw[c]), (double)bf16hi(kw[c]), d);
+      }
+    }
+    hrel[lane] = d > 0.0 ? d : 0.0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (h == 0 && e < n) {
+      const double* hr = &hrel[lane & 32];
+      double sc = 0.0;
+#pragma unroll
+      for (int hh = 0; hh < kIdxHeads; ++hh) sc = fma((double)w[hh], hr[hh], sc);
+      put(e, sc);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
 // LDS of a candidate block.
 struct alignas(16) CandLds {
   uint16_t sq[kIdxHeads * kQRowPad];
@@ -915,10 +962,7 @@ struct alignas(16) CandLds {
   uint16_t ctile[kCandTiles];   // candidate tiles (offset in the block's range), ascending
   uint16_t cmask[kCandTiles];   // entries of each candidate tile that reach the threshold
   uint32_t eidx[kCandMax];      // passing entries, ascending
-  uint16_t rowbase[kCandTiles]; // first staged row of each candidate tile's passing entries
-  uint8_t erow[kCandMax];       // staged row of each passing entry
-  uint32_t n_staged;
-  ExactLds x;                   // rows and per-head dots of the fp64 rescoring
+  double hrel[kCandThreads / 64][64];  // per wave: ReLU(dot) of (entry, head) for the in-order head fold
 };
 
 // Candidates of tiles [x*kCandTiles, (x+1)*kCandTiles) of query t
@@ -948,7 +992,6 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   const float tau = __uint_as_float(st[1]);
   stage_query(L.sq, q_idx + (size_t)t * kIdxHeads * kIdxDim, tid, kCandThreads);
   if (tid < kIdxHeads) L.w[tid] = w_idx[(size_t)t * kIdxHeads + tid];
-  if (tid == 0) L.n_staged = 0u;
   const double thr = next_down((double)tau - 2.0 * (double)eps);
 
   // 1. candidate tiles in order
@@ -958,9 +1001,9 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   if (cand) L.ctile[p] = (uint16_t)tid;
   __syncthreads();
 
-  // 2. fp32 scores of the candidate tiles (the scan's arithmetic); passing rows staged
+  // 2. fp32 scores of the candidate tiles (the scan's arithmetic)
   const uint16_t* kseq = k_idx + (size_t)(t / q_per_seq) * N * kIdxDim;
-  cand_tile_masks(L.sq, L.w, L.ctile, L.cmask, n_tiles, tile0, kseq, nv, thr, L.x, L.rowbase, &L.n_staged);
+  cand_tile_masks<false>(L.sq, L.w, L.ctile, L.cmask, n_tiles, tile0, kseq, nv, thr, nullptr, nullptr, nullptr);
   __syncthreads();
 
   // 3. output slots in (tile, entry) order: thread ci expands candidate tile ci
@@ -976,14 +1019,11 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   }
   if ((uint32_t)tid < n_tiles) {
     uint32_t m = L.cmask[tid];
-    uint32_t row = L.rowbase[tid];
     const int64_t e0 = (tile0 + L.ctile[tid]) * kTileKeys;
     while (m) {
       const int c = __ffs(m) - 1;
       m &= m - 1;
-      L.erow[q0] = (uint8_t)(row < (uint32_t)kExactRound ? row : 0u);
       L.eidx[q0++] = (uint32_t)(e0 + c);
-      ++row;
     }
   }
   // 4. the block's fixed slots, or a reserved run of shared ones
@@ -1006,7 +1046,7 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
 
   // 5. fp64 scores of the passing entries, reference operation order, into the slots
   double* cs = w.cscore + (size_t)t * cap;
-  exact_entry_scores(L.sq, L.w, L.eidx, L.erow, n_pass, kseq, L.x, [&](uint32_t e, double sc) {
+  exact_entry_scores_wave(L.sq, L.w, L.eidx, n_pass, kseq, L.hrel[tid >> 6], [&](uint32_t e, double sc) {
     if ((uint64_t)base + e < (uint64_t)cap) cs[base + e] = sc;
   });
 }
@@ -1559,7 +1599,7 @@ __global__ __launch_bounds__(kCandThreads, 4) void hsi_cand_kernel(
   if (cand) L.ctile[p] = (uint16_t)tid;
   __syncthreads();
   const uint16_t* kseq = k_idx + (size_t)(t / q_per_seq) * N * kIdxDim;
-  cand_tile_masks(L.sq, L.w, L.ctile, L.cmask, n_tiles, tile0, kseq, nv, thr, L.x, L.rowbase, &L.n_staged);
+  cand_tile_masks<true>(L.sq, L.w, L.ctile, L.cmask, n_tiles, tile0, kseq, nv, thr, &L.x, L.rowbase, &L.n_staged);
   __syncthreads();
   const uint32_t mine = (uint32_t)tid < n_tiles ? (uint32_t)__popc((uint32_t)L.cmask[tid]) : 0u;
   uint32_t n_pass;
