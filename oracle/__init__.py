@@ -51,6 +51,8 @@ def lib():
         L.csa2o_n_visible.argtypes, L.csa2o_n_visible.restype = [i64, i32, i64], i64
         L.csa2o_index_score.argtypes, L.csa2o_index_score.restype = [vp, vp, vp], dbl
         L.csa2o_index.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, vp]
+        L.csa2o_index_score_deq.argtypes, L.csa2o_index_score_deq.restype = [vp, vp, vp], dbl
+        L.csa2o_index_mx.argtypes, L.csa2o_index_mx.restype = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, vp], None
         L.csa2o_index.restype = None
         L.csa2o_topk_row.argtypes, L.csa2o_topk_row.restype = [vp, i64, i32, vp], i32
         L.csa2o_topk.argtypes, L.csa2o_topk.restype = [vp, vp, i32, i32, i64, i32, vp], None
@@ -116,6 +118,20 @@ def index(q_idx, w_idx, k_idx, q_pos, ratio, q_per_seq):
     qp = None if q_pos is None else _c(q_pos, np.int32)
     out = np.empty((T, N), np.float64)
     lib().csa2o_index(_ptr(q_idx), _ptr(w_idx), _ptr(k_idx), _ptr(qp), ratio, T, q_per_seq, N, _ptr(out))
+    return out
+
+
+def index_mx(q_codes, q_scales, w_idx, k_codes, k_scales, q_pos, ratio, q_per_seq):
+    """MXFP4 indexer (report sec. 2.4.4): q_codes uint8 [T][32][64], q_scales uint8 [T][32][4],
+    w float32 [T][32], k_codes uint8 [B][N][64], k_scales uint8 [B][N][4], q_pos int32 [T] or None
+    -> float64 scores [T][N] of the dequantised vectors (-inf beyond visibility)."""
+    q_codes, q_scales = _c(q_codes, np.uint8), _c(q_scales, np.uint8)
+    k_codes, k_scales, w_idx = _c(k_codes, np.uint8), _c(k_scales, np.uint8), _c(w_idx, np.float32)
+    T, N = q_codes.shape[0], k_codes.shape[1]
+    qp = None if q_pos is None else _c(q_pos, np.int32)
+    out = np.empty((T, N), np.float64)
+    lib().csa2o_index_mx(_ptr(q_codes), _ptr(q_scales), _ptr(w_idx), _ptr(k_codes), _ptr(k_scales), _ptr(qp), ratio,
+                         T, q_per_seq, N, _ptr(out))
     return out
 
 

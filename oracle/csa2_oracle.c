@@ -120,6 +120,44 @@ void csa2o_index(const uint16_t* q_idx, const float* w_idx, const uint16_t* k_id
     free(n_vis);
 }
 
+/* V4.1 report sec. 2.4.4: DeepSeek-V4 trains its indexer queries and keys for
+ * FP4, in the MXFP4 format.  The score is the lightning-indexer score above,
+ * evaluated on the dequantised vectors (csa2o_dequant_row, 128 channels, one
+ * scale per 32) in the same fp64 operation order. */
+double csa2o_index_score_deq(const double* q, const float* w, const double* key) {
+    double score = 0.0;
+    for (int h = 0; h < IDX_HEADS; ++h) {
+        double dot = 0.0;
+        for (int c = 0; c < IDX_DIM; ++c) dot = fma(q[h * IDX_DIM + c], key[c], dot);
+        double relu = dot > 0.0 ? dot : 0.0;
+        score = fma((double)w[h], relu, score);
+    }
+    return score;
+}
+
+void csa2o_index_mx(const uint8_t* q_codes, const uint8_t* q_scales, const float* w_idx,
+                    const uint8_t* k_codes, const uint8_t* k_scales, const int32_t* q_pos, int32_t ratio,
+                    int32_t T, int32_t q_per_seq, int64_t N, double* scores) {
+    const int64_t row_bytes = IDX_DIM / 2, row_scales = IDX_DIM / MX_BLOCK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t t = 0; t < T; ++t) {
+        double q[IDX_HEADS * IDX_DIM], key[IDX_DIM];
+        for (int h = 0; h < IDX_HEADS; ++h)
+            csa2o_dequant_row(q_codes + ((int64_t)t * IDX_HEADS + h) * row_bytes,
+                              q_scales + ((int64_t)t * IDX_HEADS + h) * row_scales, IDX_DIM, q + h * IDX_DIM);
+        int64_t n_vis = q_pos ? csa2o_n_visible(q_pos[t], ratio, N) : N;
+        int64_t b = t / q_per_seq;
+        for (int64_t s = 0; s < N; ++s) {
+            double v = -INFINITY;
+            if (s < n_vis) {
+                csa2o_dequant_row(k_codes + (b * N + s) * row_bytes, k_scales + (b * N + s) * row_scales, IDX_DIM, key);
+                v = csa2o_index_score_deq(q, w_idx + (int64_t)t * IDX_HEADS, key);
+            }
+            scores[(int64_t)t * N + s] = v;
+        }
+    }
+}
+
 /* ---- top-k --------------------------------------------------------------- */
 
 typedef struct {

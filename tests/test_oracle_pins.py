@@ -468,3 +468,76 @@ def test_reindex_topk_brute_force(oracle_lib):
         want = sorted(sorted(cand, key=lambda e: (-s_re[t, e], e))[:k])
         assert list(got[t][:len(want)]) == want and np.all(got[t][len(want):] == -1)
         assert set(want) <= set(cand)
+
+
+# ---- MXFP4 indexer queries and keys (report sec. 2.4.4: FP4 indexer q/K, MXFP4)
+
+def _mx_vec(values_by_channel, scales):
+    """Hand-built 128-channel MXFP4 vector: {channel: E2M1 code}, 4 scale bytes."""
+    codes = np.zeros(64, np.uint8)
+    for c, code in values_by_channel.items():
+        codes[c // 2] |= np.uint8(code << (4 * (c % 2)))
+    return codes, np.array(scales, np.uint8)
+
+
+def test_index_mx_hand_worked_channel_placement(oracle_lib):
+    # q head 0: channel 33 = E2M1 code 7 (6.0) in scale block 1 (2^(128-127) = 2) -> 12.0
+    # key:      channel 33 = code 3 (1.5), block 1 scale 2^(126-127) -> 0.75; dot = 9.0
+    # a key holding the same value at channel 32 instead contributes nothing
+    import oracle
+    qc = np.zeros((1, 32, 64), np.uint8)
+    qs = np.full((1, 32, 4), 127, np.uint8)
+    c0, s0 = _mx_vec({33: 7}, [127, 128, 127, 127])
+    qc[0, 0], qs[0, 0] = c0, s0
+    w = np.zeros((1, 32), np.float32)
+    w[0, 0] = 1.0
+    kc = np.zeros((1, 2, 64), np.uint8)
+    ks = np.full((1, 2, 4), 127, np.uint8)
+    kc[0, 0], ks[0, 0] = _mx_vec({33: 3}, [127, 126, 127, 127])
+    kc[0, 1], ks[0, 1] = _mx_vec({32: 3}, [127, 126, 127, 127])
+    s = oracle.index_mx(qc, qs, w, kc, ks, None, 1, 1)
+    assert s[0, 0] == 9.0 and s[0, 1] == 0.0
+
+
+def test_index_mx_closed_form(oracle_lib):
+    # every channel of head h is 1.0 (code 2) times 2^a_h with sign (-1)^h, every channel
+    # of key s is 0.5 (code 1) times 2^b_s: dot = +-128 * 0.5 * 2^(a_h + b_s);
+    # score = sum over even heads of w_h * 64 * 2^(a_h + b_s) (odd heads are negative -> 0)
+    import oracle
+    rng = np.random.default_rng(3)
+    a = rng.integers(-6, 7, 32)
+    b = rng.integers(-6, 7, 5)
+    qc = np.zeros((1, 32, 64), np.uint8)
+    qs = np.zeros((1, 32, 4), np.uint8)
+    for h in range(32):
+        code = 2 | (8 if h % 2 else 0)
+        qc[0, h] = code | (code << 4)
+        qs[0, h] = 127 + a[h]
+    kc = np.full((1, 5, 64), 1 | (1 << 4), np.uint8)
+    ks = np.zeros((1, 5, 4), np.uint8)
+    for s in range(5):
+        ks[0, s] = 127 + b[s]
+    w = (rng.integers(1, 9, (1, 32)) / 8.0).astype(np.float32)
+    got = oracle.index_mx(qc, qs, w, kc, ks, None, 1, 1)[0]
+    for s in range(5):
+        exact = sum(Fraction(float(w[0, h])) * 64 * Fraction(2) ** int(a[h] + b[s]) for h in range(0, 32, 2))
+        assert got[s] == float(exact)
+
+
+def test_index_mx_is_bf16_index_of_dequantised_values(oracle_lib):
+    # the FP4 path is the bf16 path on the dequantised vectors (every E2M1 value times a
+    # moderate power of two is exact in bf16): the generator's quantised N(0,1) data
+    import oracle
+    x = G.normal_bf16(7, 1, 0, 3 * 32 * 128).view(3 * 32, 128)
+    k = G.normal_bf16(7, 3, 0, 40 * 128).view(40, 128)
+    qc, qs = G.mxfp4_quantize(x)
+    kc, ks = G.mxfp4_quantize(k)
+    deq_q = oracle.dequant_rows(qc.numpy(), qs.numpy())
+    deq_k = oracle.dequant_rows(kc.numpy(), ks.numpy())
+    to_bf16 = lambda d: np.array([_bf16(v) for v in d.reshape(-1)], np.uint16).reshape(d.shape)
+    w = G.uniform_f32(7, 2, 0, 3 * 32).view(3, 32).numpy()
+    pos = np.array([39, 20, 7], np.int32)
+    ref = oracle.index(to_bf16(deq_q).reshape(3, 32, 128), w, to_bf16(deq_k).reshape(1, 40, 128), pos, 1, 3)
+    got = oracle.index_mx(qc.numpy().reshape(3, 32, 64), qs.numpy().reshape(3, 32, 4), w,
+                          kc.numpy().reshape(1, 40, 64), ks.numpy().reshape(1, 40, 4), pos, 1, 3)
+    assert np.array_equal(got, ref)
