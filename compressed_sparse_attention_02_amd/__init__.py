@@ -19,7 +19,8 @@ __all__ = [
     "csa2_reuse_attend", "tile_max_ld", "index_stats_bytes", "topk_workspace_bytes", "topk_min_workspace_bytes",
     "attend_workspace_bytes", "IDX_HEADS", "IDX_DIM", "HEADS", "DIM", "TOPK", "MAX_WINDOW", "MAX_LAYERS", "TILE",
     "TOPK_ROW_MAX", "STATS_WORDS", "csa2_hsi_pool", "csa2_reindex", "hsi_pool_workspace_bytes",
-    "reindex_workspace_bytes", "HSI_BLOCK", "HSI_BLOCKS", "HSI_POOL",
+    "reindex_workspace_bytes", "HSI_BLOCK", "HSI_BLOCKS", "HSI_POOL", "csa2_index_mxfp4", "csa2_topk_mxfp4",
+    "csa2_hsi_pool_mxfp4", "csa2_reindex_mxfp4", "index_mxfp4_stats_bytes",
 ]
 
 IDX_HEADS, IDX_DIM, HEADS, DIM, TOPK, MAX_WINDOW, MAX_LAYERS = 32, 128, 64, 512, 512, 128, 8
@@ -47,6 +48,12 @@ _SIGNATURES = {
     "csa2_hsi_pool": ([_vp, _vp, _sz, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _sz, _vp], _i32),
     "csa2_reindex_workspace_bytes": ([_i32, _i32], _sz),
     "csa2_reindex": ([_vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _vp, _vp, _sz, _vp], _i32),
+    "csa2_index_mxfp4_stats_bytes": ([_i32, _i32, _i64], _sz),
+    "csa2_index_mxfp4": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _sz, _vp], _i32),
+    "csa2_topk_mxfp4": ([_vp, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp, _vp, _sz, _vp],
+                        _i32),
+    "csa2_hsi_pool_mxfp4": ([_vp, _vp, _sz, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _sz, _vp], _i32),
+    "csa2_reindex_mxfp4": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _vp, _vp, _sz, _vp], _i32),
     "csa2_attend_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
     "csa2_attend_fp4": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp,
                          _vp, _sz, _vp], _i32),
@@ -291,6 +298,127 @@ def csa2_reindex(pool, q_idx, w_idx, k_idx, q_per_seq=1, k=TOPK, indices=None, w
     st = lib().csa2_reindex(_p(pool), _p(q_idx), _p(w_idx), _p(k_idx), T, q_per_seq, N, k, _p(indices),
                             _p(workspace), _nbytes(workspace), _stream(q_idx))
     _raise(st, "csa2_reindex")
+    return indices
+
+
+def index_mxfp4_stats_bytes(T: int, q_per_seq: int, N: int) -> int:
+    return lib().csa2_index_mxfp4_stats_bytes(T, q_per_seq, N)
+
+
+def _check_mx_keys(k_codes, k_scales, dev):
+    B, N = k_codes.shape[0], k_codes.shape[1]
+    _check(k_codes, "k_codes", (B, N, IDX_DIM // 2), dtype=torch.uint8, device=dev)
+    _check(k_scales, "k_scales", (B, N, IDX_DIM // 32), dtype=torch.uint8, device=dev)
+    return B, N
+
+
+def _check_mx_stats(stats, T, q_per_seq, N, device):
+    need = index_mxfp4_stats_bytes(T, q_per_seq, N)
+    if not isinstance(stats, torch.Tensor) or stats.dtype != torch.int32 or stats.dim() != 1:
+        raise ValueError("stats must be a 1-D int32 tensor")
+    if stats.device != device or not stats.is_contiguous() or stats.numel() * 4 < need:
+        raise ValueError(f"stats must be a contiguous int32 tensor of at least {need} bytes on {device}")
+
+
+def csa2_index_mxfp4(q_codes, q_scales, w_idx, k_codes, k_scales, q_pos=None, ratio=1, q_per_seq=1,
+                     want_scores=True, scores=None, tile_max=None, stats=None) -> IndexResult:
+    """Indexer scan over MXFP4 queries (codes uint8 [T][32][64], scales uint8 [T][32][4]) and
+    keys (codes uint8 [B][N][64], scales uint8 [B][N][4]); w_idx fp32 [T][32]."""
+    T = q_codes.shape[0]
+    dev = q_codes.device
+    B, N = _check_mx_keys(k_codes, k_scales, dev)
+    _check(q_codes, "q_codes", (T, IDX_HEADS, IDX_DIM // 2), dtype=torch.uint8)
+    _check(q_scales, "q_scales", (T, IDX_HEADS, IDX_DIM // 32), dtype=torch.uint8, device=dev)
+    _check(w_idx, "w_idx", (T, IDX_HEADS), dtype=torch.float32, device=dev)
+    if q_pos is not None:
+        _check(q_pos, "q_pos", (T,), dtype=torch.int32, device=dev)
+    if B * q_per_seq != T:
+        raise ValueError(f"T={T} must equal B*q_per_seq={B}*{q_per_seq}")
+    if scores is None and want_scores:
+        scores = torch.empty((T, N), dtype=torch.float32, device=dev)
+    if tile_max is None:
+        tile_max = torch.empty((T, tile_max_ld(N)), dtype=torch.float32, device=dev)
+    if stats is None:
+        stats = torch.empty((index_mxfp4_stats_bytes(T, q_per_seq, N) + 3) // 4, dtype=torch.int32, device=dev)
+    if scores is not None:
+        _check(scores, "scores", (T, N), dtype=torch.float32, device=dev)
+    _check(tile_max, "tile_max", (T, tile_max_ld(N)), dtype=torch.float32, device=dev)
+    _check_mx_stats(stats, T, q_per_seq, N, dev)
+    st = lib().csa2_index_mxfp4(_p(q_codes), _p(q_scales), _p(w_idx), _p(k_codes), _p(k_scales), _p(q_pos), ratio,
+                                T, q_per_seq, N, _p(scores), _p(tile_max), _p(stats), stats.numel() * 4,
+                                _stream(q_codes))
+    _raise(st, "csa2_index_mxfp4")
+    return IndexResult(scores, tile_max, stats)
+
+
+def csa2_topk_mxfp4(scores, tile_max, stats, w_idx, k_codes, k_scales, q_pos=None, ratio=1, q_per_seq=1, k=TOPK,
+                    indices=None, workspace=None):
+    """Exact top-k over the MXFP4 scan's outputs (the queries come from its summary)."""
+    T = w_idx.shape[0]
+    dev = w_idx.device
+    B, N = _check_mx_keys(k_codes, k_scales, dev)
+    if scores is not None:
+        _check(scores, "scores", (T, N), dtype=torch.float32, device=dev)
+    _check(tile_max, "tile_max", (T, tile_max_ld(N)), dtype=torch.float32, device=dev)
+    _check_mx_stats(stats, T, q_per_seq, N, dev)
+    _check(w_idx, "w_idx", (T, IDX_HEADS), dtype=torch.float32, device=dev)
+    if q_pos is not None:
+        _check(q_pos, "q_pos", (T,), dtype=torch.int32, device=dev)
+    if indices is None:
+        indices = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _check(indices, "indices", (T, k), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = _ws(topk_workspace_bytes(T, N, k), dev, None)
+    elif _nbytes(workspace) < topk_min_workspace_bytes(T, N, k):
+        raise ValueError("workspace below csa2_topk_min_workspace_bytes")
+    st = lib().csa2_topk_mxfp4(_p(scores), _p(tile_max), _p(stats), stats.numel() * 4, _p(w_idx), _p(k_codes),
+                               _p(k_scales), _p(q_pos), ratio, T, q_per_seq, N, k, _p(indices), _p(workspace),
+                               _nbytes(workspace), _stream(w_idx))
+    _raise(st, "csa2_topk_mxfp4")
+    return indices
+
+
+def csa2_hsi_pool_mxfp4(tile_max, stats, w_idx, k_codes, k_scales, q_pos=None, ratio=1, q_per_seq=1, pool=None,
+                        workspace=None):
+    """Candidate pool over the MXFP4 scan's outputs -> int32 [T][HSI_POOL]."""
+    T = w_idx.shape[0]
+    dev = w_idx.device
+    B, N = _check_mx_keys(k_codes, k_scales, dev)
+    _check(tile_max, "tile_max", (T, tile_max_ld(N)), dtype=torch.float32, device=dev)
+    _check_mx_stats(stats, T, q_per_seq, N, dev)
+    _check(w_idx, "w_idx", (T, IDX_HEADS), dtype=torch.float32, device=dev)
+    if q_pos is not None:
+        _check(q_pos, "q_pos", (T,), dtype=torch.int32, device=dev)
+    if pool is None:
+        pool = torch.empty((T, HSI_POOL), dtype=torch.int32, device=dev)
+    _check(pool, "pool", (T, HSI_POOL), dtype=torch.int32, device=dev)
+    workspace = _ws(hsi_pool_workspace_bytes(T, N), dev, workspace)
+    st = lib().csa2_hsi_pool_mxfp4(_p(tile_max), _p(stats), stats.numel() * 4, _p(w_idx), _p(k_codes), _p(k_scales),
+                                   _p(q_pos), ratio, T, q_per_seq, N, _p(pool), _p(workspace), _nbytes(workspace),
+                                   _stream(w_idx))
+    _raise(st, "csa2_hsi_pool_mxfp4")
+    return pool
+
+
+def csa2_reindex_mxfp4(pool, q_codes, q_scales, w_idx, k_codes, k_scales, q_per_seq=1, k=TOPK, indices=None,
+                       workspace=None):
+    """Reindex selection with an MXFP4 query over MXFP4 keys -> int32 [T][k]."""
+    T = q_codes.shape[0]
+    dev = q_codes.device
+    B, N = _check_mx_keys(k_codes, k_scales, dev)
+    _check(pool, "pool", (T, HSI_POOL), dtype=torch.int32, device=dev)
+    _check(q_codes, "q_codes", (T, IDX_HEADS, IDX_DIM // 2), dtype=torch.uint8, device=dev)
+    _check(q_scales, "q_scales", (T, IDX_HEADS, IDX_DIM // 32), dtype=torch.uint8, device=dev)
+    _check(w_idx, "w_idx", (T, IDX_HEADS), dtype=torch.float32, device=dev)
+    if B * q_per_seq != T:
+        raise ValueError(f"T={T} must equal B*q_per_seq={B}*{q_per_seq}")
+    if indices is None:
+        indices = torch.empty((T, k), dtype=torch.int32, device=dev)
+    _check(indices, "indices", (T, k), dtype=torch.int32, device=dev)
+    workspace = _ws(reindex_workspace_bytes(T, k), dev, workspace)
+    st = lib().csa2_reindex_mxfp4(_p(pool), _p(q_codes), _p(q_scales), _p(w_idx), _p(k_codes), _p(k_scales), T,
+                                  q_per_seq, N, k, _p(indices), _p(workspace), _nbytes(workspace), _stream(q_codes))
+    _raise(st, "csa2_reindex_mxfp4")
     return indices
 
 

@@ -22,7 +22,7 @@
 // Chunks of one query are split over work items (split-K); partial (max,
 // sum, O) are merged by a combine kernel.  For Reuse with several layers,
 // each selected-row chunk is staged once and used by every layer.
-#include "csa2_common.h"
+#include "mxfp4.h"
 
 namespace csa2 {
 
@@ -69,22 +69,6 @@ __device__ __forceinline__ int head_wave() { return (int)(blockIdx.z * (blockDim
 // 16-byte LDS operand read (the offsets used are multiples of 16 bytes).
 __device__ __forceinline__ bf16x8 lds_read16(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(__builtin_assume_aligned(p, 16));
-}
-
-// 8 FP4 codes (one 32-bit word, element 2i in the low nibble of byte i) times
-// the block scale 2^(s-127) -> 8 bf16 (4 words, element 2i in the low half).
-// v_cvt_scalef32_pk_bf16_fp4 converts the two codes of one byte with an fp32
-// scale; every E2M1 value times a power of two is exact in bf16 (at most two
-// significant bits), and the scale byte s maps to the fp32 2^(s-127) (s = 0:
-// the subnormal 2^-127; s = 255 is not a valid E8M0 scale).
-__device__ __forceinline__ uint4 dequant8(uint32_t codes, uint32_t sbyte) {
-  const float sc = __uint_as_float(sbyte == 0 ? 0x00400000u : (sbyte << 23));
-  uint4 r;
-  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
-  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
-  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
-  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
-  return r;
 }
 
 // XT rows hold 32 bf16 in four 16-byte blocks; block b of row r is stored at

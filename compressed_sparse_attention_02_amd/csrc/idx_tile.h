@@ -33,6 +33,22 @@ __device__ __forceinline__ void load_head_weights(const float* __restrict__ w_t,
   for (int r = 0; r < 8; ++r) wr[r] = w_t[16 * (r >> 2) + 4 * g + (r & 3)];
 }
 
+// The score of key l % 16 from the two 16-head accumulator halves (register i
+// of half m: head 16m + 4(l/16) + i): ReLU, times the head's weight, summed
+// over the lane's 8 heads and then over the four lane groups of the column.
+// Returned in every lane of that column.
+__device__ __forceinline__ float fold_heads(const floatx4& acc0, const floatx4& acc1, const float (&wr)[8]) {
+  float part = 0.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    part = fmaf(wr[r], fmaxf(acc0[r], 0.f), part);
+    part = fmaf(wr[4 + r], fmaxf(acc1[r], 0.f), part);
+  }
+  part += __shfl_xor(part, 16, 64);
+  part += __shfl_xor(part, 32, 64);
+  return part;
+}
+
 // fp32 score of key `col` of the tile, returned in every lane of that column
 // (all four lane groups).  sq_t: the query's 32 rows in LDS.
 __device__ __forceinline__ float tile_score(const uint16_t* __restrict__ sq_t, const uint4 (&kv)[4],
@@ -46,15 +62,7 @@ __device__ __forceinline__ float tile_score(const uint16_t* __restrict__ sq_t, c
     acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(q0 + 32 * j), bk, acc0, 0, 0, 0);
     acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(q1 + 32 * j), bk, acc1, 0, 0, 0);
   }
-  float part = 0.f;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    part = fmaf(wr[r], fmaxf(acc0[r], 0.f), part);
-    part = fmaf(wr[4 + r], fmaxf(acc1[r], 0.f), part);
-  }
-  part += __shfl_xor(part, 16, 64);
-  part += __shfl_xor(part, 32, 64);
-  return part;
+  return fold_heads(acc0, acc1, wr);
 }
 
 // Stage q[t] (32 x 128 bf16) into LDS rows of kQRowPad: 512 chunks of 16 B.

@@ -11,7 +11,7 @@
 // tie rule (lower index first) and the ascending output carry over unchanged,
 // and the fp64 scores are those of the original rows (same bf16 values, same
 // operation order).
-#include "csa2_common.h"
+#include "mxfp4.h"
 
 namespace csa2 {
 
@@ -21,7 +21,8 @@ constexpr int kGatherRows = 64;                          // pool rows per block
 constexpr int kRowVecs = kIdxDim * 2 / 16;               // 16-byte vectors per key row (16)
 
 struct ReindexWs {
-  uint16_t* keys;    // [T][kPool][128] gathered keys
+  uint16_t* keys;    // [T][kPool][128] gathered keys (bf16)
+  uint16_t* q;       // [T][32][128] the Reindex queries in bf16 (MXFP4 variant)
   int32_t* qpos;     // [T]: pool size - 1
   float* scores;     // [T][kPool]
   float* tile_max;   // [T][tile_ld]
@@ -39,6 +40,7 @@ static ReindexWs reindex_ws(void* base, int T, int k, size_t* total) {
     return (void*)p;
   };
   w.keys = (uint16_t*)take((size_t)T * kPool * kIdxDim * 2);
+  w.q = (uint16_t*)take((size_t)T * kIdxHeads * kIdxDim * 2);
   w.qpos = (int32_t*)take((size_t)T * 4);
   w.scores = (float*)take((size_t)T * kPool * 4);
   w.tile_max = (float*)take((size_t)T * (size_t)csa2_tile_max_ld(kPool) * 4);
@@ -49,17 +51,22 @@ static ReindexWs reindex_ws(void* base, int T, int k, size_t* total) {
   return w;
 }
 
-// Block (x, t): pool rows [x*64, x*64+64) of query t into keys[t]; zeros for
-// pad slots (-1).  Block (0, t) also writes qpos[t] = (number of pool entries) - 1.
-__global__ __launch_bounds__(kGatherThreads) void reindex_gather_kernel(const int32_t* __restrict__ pool,
-                                                                        const uint16_t* __restrict__ k_idx,
+// Block (x, t): pool rows [x*64, x*64+64) of query t into keys[t] as bf16
+// (MXFP4 rows dequantised, exactly); zeros for pad slots (-1).  Block (0, t)
+// also writes qpos[t] = (number of pool entries) - 1, and block (1, t) the
+// query dequantised to bf16 when MXFP4 query codes are given.
+template <class Keys>
+__global__ __launch_bounds__(kGatherThreads) void reindex_gather_kernel(const int32_t* __restrict__ pool, Keys k_all,
                                                                         int q_per_seq, int64_t N,
                                                                         uint16_t* __restrict__ keys,
-                                                                        int32_t* __restrict__ qpos) {
+                                                                        int32_t* __restrict__ qpos,
+                                                                        const uint8_t* __restrict__ q_codes,
+                                                                        const uint8_t* __restrict__ q_scales,
+                                                                        uint16_t* __restrict__ q_out) {
   const int t = blockIdx.y;
   const int tid = threadIdx.x;
   const int32_t* pl = pool + (size_t)t * kPool;
-  const uint4* kseq = reinterpret_cast<const uint4*>(k_idx + (size_t)(t / q_per_seq) * N * kIdxDim);
+  const Keys kseq = k_all.seq(t / q_per_seq, N);
   uint4* dst = reinterpret_cast<uint4*>(keys + ((size_t)t * kPool + (size_t)blockIdx.x * kGatherRows) * kIdxDim);
   const int r0 = blockIdx.x * kGatherRows;
 #pragma unroll
@@ -67,7 +74,17 @@ __global__ __launch_bounds__(kGatherThreads) void reindex_gather_kernel(const in
     const int i = u * kGatherThreads + tid;
     const int r = i / kRowVecs, c = i % kRowVecs;
     const int32_t e = pl[r0 + r];
-    dst[i] = e >= 0 ? kseq[(size_t)e * kRowVecs + c] : make_uint4(0u, 0u, 0u, 0u);
+    dst[i] = e >= 0 ? kseq.piece(e, c) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (blockIdx.x == 1 && q_codes != nullptr) {
+    // thread i: 8 code bytes (16 channels) of head i / 8
+    const int h = tid >> 3, c16 = tid & 7;
+    const uint8_t* qc = q_codes + ((size_t)t * kIdxHeads + h) * kMxRowBytes;
+    const uint2 cw = *reinterpret_cast<const uint2*>(qc + 8 * c16);
+    const uint32_t sb = q_scales[((size_t)t * kIdxHeads + h) * kMxScales + (c16 >> 1)];
+    uint4* qd = reinterpret_cast<uint4*>(q_out + ((size_t)t * kIdxHeads + h) * kIdxDim + 16 * c16);
+    qd[0] = dequant8(cw.x, sb);
+    qd[1] = dequant8(cw.y, sb);
   }
   if (blockIdx.x == 0) {
     __shared__ uint32_t part[kGatherThreads / 64];
@@ -113,6 +130,21 @@ extern "C" size_t csa2_reindex_workspace_bytes(int32_t T, int32_t k) {
   return total;
 }
 
+// The gathered pool keys as a batch of T one-query "sequences" of kPool keys:
+// the regular scan and row-regime selection, then positions -> entry ids.
+static csa2_status reindex_finish(const ReindexWs& w, const void* q_bf16, const float* w_idx, const int32_t* pool,
+                                  int32_t T, int32_t k, int32_t* indices, void* hip_stream) {
+  csa2_status s = csa2_index(q_bf16, w_idx, w.keys, w.qpos, 1, T, 1, kPool, w.scores, w.tile_max, w.stats,
+                             w.stats_bytes, hip_stream);
+  if (s != CSA2_OK) return s;
+  s = csa2_topk(w.scores, w.tile_max, w.stats, w.stats_bytes, q_bf16, w_idx, w.keys, w.qpos, 1, T, 1, kPool, k,
+                w.pos, nullptr, 0, hip_stream);
+  if (s != CSA2_OK) return s;
+  hipLaunchKernelGGL(reindex_map_kernel, dim3(T), dim3(256), 0, (hipStream_t)hip_stream, pool, w.pos, k, indices);
+  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
+  return CSA2_OK;
+}
+
 extern "C" csa2_status csa2_reindex(const int32_t* pool, const void* q_idx, const float* w_idx, const void* k_idx,
                                     int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices,
                                     void* workspace, size_t workspace_bytes, void* hip_stream) {
@@ -124,18 +156,31 @@ extern "C" csa2_status csa2_reindex(const int32_t* pool, const void* q_idx, cons
   size_t need;
   ReindexWs w = reindex_ws(workspace, T, k, &need);
   if (!workspace || !aligned16(workspace) || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)hip_stream;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(reindex_gather_kernel, dim3(kPool / kGatherRows, T), dim3(kGatherThreads), 0, st, pool,
-                     (const uint16_t*)k_idx, q_per_seq, N, w.keys, w.qpos);
+  hipLaunchKernelGGL(reindex_gather_kernel<Bf16Keys>, dim3(kPool / kGatherRows, T), dim3(kGatherThreads), 0,
+                     (hipStream_t)hip_stream, pool, Bf16Keys{(const uint16_t*)k_idx}, q_per_seq, N, w.keys, w.qpos,
+                     nullptr, nullptr, nullptr);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
-  csa2_status s = csa2_index(q_idx, w_idx, w.keys, w.qpos, 1, T, 1, kPool, w.scores, w.tile_max, w.stats,
-                             w.stats_bytes, hip_stream);
-  if (s != CSA2_OK) return s;
-  s = csa2_topk(w.scores, w.tile_max, w.stats, w.stats_bytes, q_idx, w_idx, w.keys, w.qpos, 1, T, 1, kPool, k,
-                w.pos, nullptr, 0, hip_stream);
-  if (s != CSA2_OK) return s;
-  hipLaunchKernelGGL(reindex_map_kernel, dim3(T), dim3(256), 0, st, pool, w.pos, k, indices);
+  return reindex_finish(w, q_idx, w_idx, pool, T, k, indices, hip_stream);
+}
+
+extern "C" csa2_status csa2_reindex_mxfp4(const int32_t* pool, const uint8_t* q_codes, const uint8_t* q_scales,
+                                          const float* w_idx, const uint8_t* k_codes, const uint8_t* k_scales,
+                                          int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices,
+                                          void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!pool || !q_codes || !q_scales || !w_idx || !k_codes || !k_scales || !indices) return CSA2_ERR_INVALID_ARG;
+  if (!aligned16(pool) || !aligned16(q_codes) || !aligned16(q_scales) || !aligned16(w_idx) || !aligned16(k_codes) ||
+      !aligned16(k_scales) || !aligned16(indices))
+    return CSA2_ERR_INVALID_ARG;
+  if (T < 1 || q_per_seq < 1 || T % q_per_seq != 0 || N < 1) return CSA2_ERR_INVALID_ARG;
+  if (k != kTopK || N >= ((int64_t)1 << 31) || T > 65535) return CSA2_ERR_UNSUPPORTED;
+  size_t need;
+  ReindexWs w = reindex_ws(workspace, T, k, &need);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(reindex_gather_kernel<Mx4Keys>, dim3(kPool / kGatherRows, T), dim3(kGatherThreads), 0,
+                     (hipStream_t)hip_stream, pool, Mx4Keys{k_codes, k_scales}, q_per_seq, N, w.keys, w.qpos, q_codes,
+                     q_scales, w.q);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
-  return CSA2_OK;
+  return reindex_finish(w, w.q, w_idx, pool, T, k, indices, hip_stream);
 }

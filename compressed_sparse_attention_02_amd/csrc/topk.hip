@@ -32,7 +32,7 @@
 //    entries above hi + 2 eps, rescores the band [lo - 2 eps, hi + 2 eps] in
 //    fp64 and takes the rest by (fp64 score desc, index asc).
 #include "idx_plan.h"
-#include "idx_tile.h"
+#include "mxfp4.h"
 
 namespace csa2 {
 
@@ -140,12 +140,21 @@ __device__ __forceinline__ float bound_eps(float m2, double qf, double sw) {
 
 // fp64 score with the reference's exact operation sequence (global operands;
 // used by the streaming fallback only).
-__device__ double exact_score(const uint16_t* __restrict__ q, const float* __restrict__ w,
-                              const uint16_t* __restrict__ key) {
+template <class Keys>
+__device__ double exact_score(const uint16_t* __restrict__ q, const float* __restrict__ w, const Keys& keys,
+                              int64_t row) {
   double sc = 0.0;
   for (int h = 0; h < kIdxHeads; ++h) {
     double d = 0.0;
-    for (int c = 0; c < kIdxDim; ++c) d = fma(bf16_to_f64(q[h * kIdxDim + c]), bf16_to_f64(key[c]), d);
+    for (int i = 0; i < 16; ++i) {
+      const uint4 kp = keys.piece(row, i);
+      const uint32_t kw[4] = {kp.x, kp.y, kp.z, kp.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        d = fma(bf16_to_f64(q[h * kIdxDim + 8 * i + 2 * c]), (double)bf16lo(kw[c]), d);
+        d = fma(bf16_to_f64(q[h * kIdxDim + 8 * i + 2 * c + 1]), (double)bf16hi(kw[c]), d);
+      }
+    }
     sc = fma((double)w[h], d > 0.0 ? d : 0.0, sc);
   }
   return sc;
@@ -314,8 +323,9 @@ struct alignas(16) FinLds {
 // fp64 scores of the band (reference operation order): thread (e = tid/32,
 // h = tid%32) forms dot(q[h], K[e]) with 128 sequential fmas from LDS, then 32
 // threads fold the heads in order.
+template <class Keys>
 __device__ void rescore_band(FinLds& sh, FinTail& tl, uint32_t nb, const uint16_t* __restrict__ qt,
-                             const float* __restrict__ wt, const uint16_t* __restrict__ kb) {
+                             const float* __restrict__ wt, const Keys& kb) {
   const int tid = threadIdx.x;
   const int e = tid >> 5, h = tid & 31;
   for (int i = tid; i < kIdxHeads * 16; i += kFinThreads) {
@@ -327,7 +337,7 @@ __device__ void rescore_band(FinLds& sh, FinTail& tl, uint32_t nb, const uint16_
     {
       const int r = tid >> 4, c = tid & 15;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (base + r < nb) v = *reinterpret_cast<const uint4*>(kb + (size_t)sh.band_idx[base + r] * kIdxDim + 8 * c);
+      if (base + r < nb) v = kb.piece(sh.band_idx[base + r], c);
       *reinterpret_cast<uint4*>(&tl.krows[r][8 * c]) = v;
     }
     __syncthreads();
@@ -365,8 +375,9 @@ __device__ void rescore_band(FinLds& sh, FinTail& tl, uint32_t nb, const uint16_
 
 // Complete the selection once T^ is known and the sure entries and band are
 // in sh.out / sh.band_idx (n_band <= kBandLds): rescore and pick the band's share.
+template <class Keys>
 __device__ void finish_band(FinLds& sh, FinTail& tl, uint32_t kk, const uint16_t* qt, const float* wt,
-                            const uint16_t* kb) {
+                            const Keys& kb) {
   const uint32_t nb = sh.n_band;
   rescore_band(sh, tl, nb, qt, wt, kb);
   const uint32_t r = kk - sh.n_out;
@@ -388,8 +399,9 @@ __device__ void finish_band(FinLds& sh, FinTail& tl, uint32_t kk, const uint16_t
 // Exact streaming fallback over the whole visible row (capacity overflow).
 // Gathers sure entries, then radix-selects the band's share over the 96-bit
 // composite (fp64 key, ~index), recomputing each band member's fp64 score.
+template <class Keys>
 __device__ void finish_streaming(FinLds& sh, uint32_t kk, const float* row, int64_t nv, double lo, double hi,
-                                 const uint16_t* qt, const float* wt, const uint16_t* kb) {
+                                 const uint16_t* qt, const float* wt, const Keys& kb) {
   const int tid = threadIdx.x;
   if (tid == 0) sh.n_out = 0;
   __syncthreads();
@@ -405,7 +417,7 @@ __device__ void finish_streaming(FinLds& sh, uint32_t kk, const float* row, int6
     for (int64_t s = tid; s < nv; s += kFinThreads) {
       const double v = (double)row[s];
       if (v < lo || v > hi) continue;
-      const uint64_t key = f64_key(exact_score(qt, wt, kb + (size_t)s * kIdxDim));
+      const uint64_t key = f64_key(exact_score(qt, wt, kb, s));
       const uint32_t low = ~(uint32_t)s;
       if ((key & mhi) != phi || (low & mlo) != plo) continue;
       const uint32_t digit = pass < 8 ? (uint32_t)(key >> (56 - 8 * pass)) & 255u
@@ -426,7 +438,7 @@ __device__ void finish_streaming(FinLds& sh, uint32_t kk, const float* row, int6
   for (int64_t s = tid; s < nv; s += kFinThreads) {
     const double v = (double)row[s];
     if (v < lo || v > hi) continue;
-    const uint64_t key = f64_key(exact_score(qt, wt, kb + (size_t)s * kIdxDim));
+    const uint64_t key = f64_key(exact_score(qt, wt, kb, s));
     const uint32_t low = ~(uint32_t)s;
     if (key > phi || (key == phi && low >= plo)) sh.out[atomicAdd(&sh.n_out, 1u)] = (uint32_t)s;
   }
@@ -473,11 +485,11 @@ struct SmallLds {
   double bq[kFinThreads / 64], bs[kFinThreads / 64];
 };
 
+template <class Keys>
 __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
     const float* __restrict__ scores, uint32_t* __restrict__ stats, const float* __restrict__ parts,
-    int64_t n_parts, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
-    const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos, int ratio, int q_per_seq, int64_t N,
-    int k, int32_t* __restrict__ indices) {
+    int64_t n_parts, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, Keys keys,
+    const int32_t* __restrict__ q_pos, int ratio, int q_per_seq, int64_t N, int k, int32_t* __restrict__ indices) {
   __shared__ SmallLds L;
   FinLds& sh = L.f;
   FinTail& tl = L.u.tail;
@@ -489,7 +501,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
   const int b = t / q_per_seq;
   const uint16_t* qt = q_idx + (size_t)t * kIdxHeads * kIdxDim;
   const float* wt = w_idx + (size_t)t * kIdxHeads;
-  const uint16_t* kb = k_idx + (size_t)b * N * kIdxDim;
+  const Keys kb = keys.seq(b, N);
   const float* row = scores + (size_t)t * N;
   if (tid == 0) { sh.n_out = 0; sh.n_band = 0; }
   if (nv > k) {
@@ -790,10 +802,10 @@ struct alignas(16) ExactLds {
 // ... in entry order (rows reserved with an LDS counter, n_staged, that must be
 // zero on entry; rows past kExactRound are not written).
 constexpr int kMaskTiles = 3;
-template <bool kStage>
+template <bool kStage, class Keys>
 __device__ __forceinline__ void cand_tile_masks(const uint16_t* __restrict__ sq, const float* __restrict__ w,
                                                 const uint16_t* __restrict__ ctile, uint16_t* __restrict__ cmask,
-                                                uint32_t n_tiles, int64_t tile0, const uint16_t* __restrict__ kseq,
+                                                uint32_t n_tiles, int64_t tile0, const Keys& kseq,
                                                 int64_t nv, double thr, ExactLds* X, uint16_t* __restrict__ rowbase,
                                                 uint32_t* n_staged) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -808,7 +820,7 @@ __device__ __forceinline__ void cand_tile_masks(const uint16_t* __restrict__ sq,
       const uint32_t ci = c0 + u * kWaves;
       if (ci < n_tiles) {
         const int64_t s = (tile0 + ctile[ci]) * kTileKeys + col;
-        load_key_slices(kseq, s < nv ? s : nv - 1, g, kv[u]);
+        kseq.slices(s < nv ? s : nv - 1, g, kv[u]);
       }
     }
 #pragma unroll
@@ -867,11 +879,10 @@ __device__ __forceinline__ void exact_dots(const uint16_t* __restrict__ sq, Exac
   for (int i = 0; i < C; ++i) X.dots[wave][half + 2 * i][h] = d[i];
 }
 
-template <class Put>
+template <class Keys, class Put>
 __device__ __forceinline__ void exact_entry_scores(const uint16_t* __restrict__ sq, const float* __restrict__ w,
                                                    const uint32_t* __restrict__ eidx, const uint8_t* erow,
-                                                   uint32_t n, const uint16_t* __restrict__ kseq, ExactLds& X,
-                                                   Put put) {
+                                                   uint32_t n, const Keys& kseq, ExactLds& X, Put put) {
   static_assert(kCandThreads == 256, "four waves, two 16-byte pieces of the round's rows per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // all rows already in X.krows (erow[e]: the row of entry e): one round, no loads
@@ -881,8 +892,8 @@ __device__ __forceinline__ void exact_entry_scores(const uint16_t* __restrict__ 
     if (!staged) {
       // both pieces requested before either is stored (rows past the round's end re-read row 0)
       const uint32_t row0 = tid >> 4, row1 = (kCandThreads + tid) >> 4, c8 = 8 * (tid & 15);
-      const uint4 v0 = *reinterpret_cast<const uint4*>(kseq + (size_t)eidx[r0 + (row0 < m ? row0 : 0)] * kIdxDim + c8);
-      const uint4 v1 = *reinterpret_cast<const uint4*>(kseq + (size_t)eidx[r0 + (row1 < m ? row1 : 0)] * kIdxDim + c8);
+      const uint4 v0 = kseq.piece(eidx[r0 + (row0 < m ? row0 : 0)], tid & 15);
+      const uint4 v1 = kseq.piece(eidx[r0 + (row1 < m ? row1 : 0)], tid & 15);
       if (row0 < m) *reinterpret_cast<uint4*>(&X.krows[row0][c8]) = v0;
       if (row1 < m) *reinterpret_cast<uint4*>(&X.krows[row1][c8]) = v1;
       __syncthreads();
@@ -913,20 +924,20 @@ __device__ __forceinline__ void exact_entry_scores(const uint16_t* __restrict__ 
 // sequential fmas, reading the key row straight from memory (the tile pass has
 // just brought it on chip), then lane h == 0 folds the entry's 32 heads in order
 // from hrel (this wave's 64 doubles in LDS).  put(e, score) receives each result.
-template <class Put>
+template <class Keys, class Put>
 __device__ __forceinline__ void exact_entry_scores_wave(const uint16_t* __restrict__ sq, const float* __restrict__ w,
                                                         const uint32_t* __restrict__ eidx, uint32_t n,
-                                                        const uint16_t* __restrict__ kseq, double* hrel, Put put) {
+                                                        const Keys& kseq, double* hrel, Put put) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane & 31;
   for (uint32_t e0 = 2 * wave; e0 < n; e0 += 2 * (kCandThreads / 64)) {
     const uint32_t e = e0 + (lane >> 5);
-    const uint16_t* kr = kseq + (size_t)eidx[e < n ? e : e0] * kIdxDim;
+    const int64_t kr = eidx[e < n ? e : e0];
     const uint16_t* qr = &sq[h * kQRowPad];
     double d = 0.0;
 #pragma unroll 4
     for (int i = 0; i < 16; ++i) {
-      const uint4 kq = *reinterpret_cast<const uint4*>(kr + 8 * i);
+      const uint4 kq = kseq.piece(kr, i);
       const uint4 qq = *reinterpret_cast<const uint4*>(qr + 8 * i);
       const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
       const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
@@ -967,9 +978,10 @@ struct alignas(16) CandLds {
 
 // Candidates of tiles [x*kCandTiles, (x+1)*kCandTiles) of query t
 // (grid (nblk, T), one thread per tile).  Every block writes its table record.
+template <class Keys>
 __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
     const float* __restrict__ tile_max, uint32_t* __restrict__ stats, const uint16_t* __restrict__ q_idx,
-    const float* __restrict__ w_idx, const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
+    const float* __restrict__ w_idx, Keys keys, const int32_t* __restrict__ q_pos,
     int ratio, int q_per_seq, int64_t N, int k, void* ws, int T, int64_t cap, int slots) {
   __shared__ CandLds L;
   const int t = blockIdx.y;
@@ -1002,7 +1014,7 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   __syncthreads();
 
   // 2. fp32 scores of the candidate tiles (the scan's arithmetic)
-  const uint16_t* kseq = k_idx + (size_t)(t / q_per_seq) * N * kIdxDim;
+  const Keys kseq = keys.seq(t / q_per_seq, N);
   cand_tile_masks<false>(L.sq, L.w, L.ctile, L.cmask, n_tiles, tile0, kseq, nv, thr, nullptr, nullptr, nullptr);
   __syncthreads();
 
@@ -1276,11 +1288,12 @@ __device__ double kth_largest_f64(Lds& L, uint32_t n, uint32_t kk, double lo, do
 
 // fp64 score of one key row with the reference's operation sequence, query
 // and weights in LDS (fallback path).
-__device__ double exact_score_lds(const uint16_t* __restrict__ sq, const float* __restrict__ w,
-                                  const uint16_t* __restrict__ key) {
+template <class Keys>
+__device__ double exact_score_lds(const uint16_t* __restrict__ sq, const float* __restrict__ w, const Keys& keys,
+                                  int64_t row) {
   uint4 kr[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) kr[i] = *reinterpret_cast<const uint4*>(key + 8 * i);
+  for (int i = 0; i < 16; ++i) kr[i] = keys.piece(row, i);
   double sc = 0.0;
   for (int h = 0; h < kIdxHeads; ++h) {
     const uint16_t* qr = sq + h * kQRowPad;
@@ -1304,8 +1317,9 @@ __device__ double exact_score_lds(const uint16_t* __restrict__ sq, const float* 
 // Exact fallback of the tile regime: radix passes over the 96-bit composite
 // (fp64 key, ~index) of every visible entry of the candidate tiles, fp64
 // scores recomputed in each pass, then an ordered gather.
+template <class Keys>
 __device__ void select_streaming(SelectLds& L, uint32_t kk, const float* tm_row, int64_t nv, double thr,
-                                 const uint16_t* qt, const float* wt, const uint16_t* kb, int32_t* out) {
+                                 const uint16_t* qt, const float* wt, const Keys& kb, int32_t* out) {
   const int tid = threadIdx.x;
   stage_query(L.sq, qt, tid, kSelThreads);
   if (tid < kIdxHeads) L.w[tid] = wt[tid];
@@ -1318,7 +1332,7 @@ __device__ void select_streaming(SelectLds& L, uint32_t kk, const float* tm_row,
     __syncthreads();
     for (int64_t s = tid; s < nv; s += kSelThreads) {
       if (!((double)tm_row[s / kTileKeys] >= thr)) continue;
-      const uint64_t key = f64_key(exact_score_lds(L.sq, L.w, kb + (size_t)s * kIdxDim));
+      const uint64_t key = f64_key(exact_score_lds(L.sq, L.w, kb, s));
       const uint32_t low = ~(uint32_t)s;
       if ((key & mhi) != phi || (low & mlo) != plo) continue;
       const uint32_t digit = pass < 8 ? (uint32_t)(key >> (56 - 8 * pass)) & 255u
@@ -1342,7 +1356,7 @@ __device__ void select_streaming(SelectLds& L, uint32_t kk, const float* tm_row,
     const int64_t s = s0 + tid;
     bool keep = false;
     if (s < nv && (double)tm_row[s / kTileKeys] >= thr) {
-      const uint64_t key = f64_key(exact_score_lds(L.sq, L.w, kb + (size_t)s * kIdxDim));
+      const uint64_t key = f64_key(exact_score_lds(L.sq, L.w, kb, s));
       const uint32_t low = ~(uint32_t)s;
       keep = key > phi || (key == phi && low >= plo);
     }
@@ -1355,9 +1369,10 @@ __device__ void select_streaming(SelectLds& L, uint32_t kk, const float* tm_row,
 
 // Final selection of query t (grid T, 256 threads): the k largest fp64 keys
 // among the candidates, written ascending by index.
+template <class Keys>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ tile_max, uint32_t* __restrict__ stats, const uint16_t* __restrict__ q_idx,
-    const float* __restrict__ w_idx, const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos,
+    const float* __restrict__ w_idx, Keys keys, const int32_t* __restrict__ q_pos,
     int ratio, int q_per_seq, int64_t N, int k, int32_t* __restrict__ indices, void* ws, int T, int64_t cap) {
   __shared__ SelectLds L;
   const int t = blockIdx.x;
@@ -1397,7 +1412,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float tau = __uint_as_float(st[1]);
     const double thr = next_down((double)tau - 2.0 * (double)__uint_as_float(st[0]));
     select_streaming(L, kk, tile_max + (size_t)t * tile_ld(N), nv, thr, q_idx + (size_t)t * kIdxHeads * kIdxDim,
-                     w_idx + (size_t)t * kIdxHeads, k_idx + (size_t)(t / q_per_seq) * N * kIdxDim, out);
+                     w_idx + (size_t)t * kIdxHeads, keys.seq(t / q_per_seq, N), out);
     if (tid == 0) st[2] = 0u;
     return;
   }
@@ -1564,10 +1579,10 @@ struct alignas(16) HsiCandLds {
 // whose fp32 score reaches tau - 2 eps, written as records in block order.
 // Passing entries are scored in rounds of kCandMax, so that any number of
 // them (ties included) is handled.
+template <class Keys>
 __global__ __launch_bounds__(kCandThreads, 4) void hsi_cand_kernel(
     const float* __restrict__ tile_max, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
-    const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos, int ratio, int q_per_seq, int64_t N,
-    void* ws, int T) {
+    Keys keys, const int32_t* __restrict__ q_pos, int ratio, int q_per_seq, int64_t N, void* ws, int T) {
   __shared__ HsiCandLds L;
   const int t = blockIdx.y;
   const int x = blockIdx.x;
@@ -1598,7 +1613,7 @@ __global__ __launch_bounds__(kCandThreads, 4) void hsi_cand_kernel(
   const uint32_t p = block_flag_scan(cand, L.wsum[0], &n_tiles);
   if (cand) L.ctile[p] = (uint16_t)tid;
   __syncthreads();
-  const uint16_t* kseq = k_idx + (size_t)(t / q_per_seq) * N * kIdxDim;
+  const Keys kseq = keys.seq(t / q_per_seq, N);
   cand_tile_masks<true>(L.sq, L.w, L.ctile, L.cmask, n_tiles, tile0, kseq, nv, thr, &L.x, L.rowbase, &L.n_staged);
   __syncthreads();
   const uint32_t mine = (uint32_t)tid < n_tiles ? (uint32_t)__popc((uint32_t)L.cmask[tid]) : 0u;
@@ -1964,6 +1979,69 @@ extern "C" size_t csa2_topk_min_workspace_bytes(int32_t T, int64_t N, int32_t k)
   return tile_ws_fixed(T, N);
 }
 
+// What the selection reads from a scan's summary: group maxima, norm partials
+// and the (bf16) indexer queries.
+struct Summary {
+  const float* gmax;
+  int64_t n_groups;
+  const float* parts;
+  int64_t n_parts;
+  const uint16_t* q;
+};
+
+static bool summary_bf16(const uint32_t* stats, size_t stats_bytes, const void* q_idx, int32_t T, int32_t q_per_seq,
+                         int64_t N, Summary* sm) {
+  IndexPlan p;
+  if (!index_plan(T, q_per_seq, N, &p) || stats_bytes < stats_words(T, p) * sizeof(uint32_t)) return false;
+  sm->gmax = (const float*)(stats + stats_groups_off(T));
+  sm->n_groups = p.n_groups;
+  sm->parts = (const float*)(stats + stats_parts_off(T, p.n_groups));
+  sm->n_parts = p.parts();
+  sm->q = (const uint16_t*)q_idx;
+  return true;
+}
+
+static bool summary_mx(const uint32_t* stats, size_t stats_bytes, int32_t T, int32_t q_per_seq, int64_t N,
+                       Summary* sm) {
+  MxPlan p;
+  if (!mx_plan(T, q_per_seq, N, &p) || stats_bytes < mx_stats_words(T, p) * sizeof(uint32_t)) return false;
+  sm->gmax = (const float*)(stats + (size_t)T * CSA2_STATS_WORDS);
+  sm->n_groups = p.n_groups;
+  sm->parts = sm->gmax + (size_t)T * p.n_groups;
+  sm->n_parts = p.parts();
+  sm->q = (const uint16_t*)(stats + mx_qdeq_off(T, p));
+  return true;
+}
+
+template <class Keys>
+static csa2_status topk_launch(const float* scores, const float* tile_max, uint32_t* stats, const Summary& sm,
+                               const float* w_idx, Keys keys, const int32_t* q_pos, int32_t ratio, int32_t T,
+                               int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices, void* workspace,
+                               size_t workspace_bytes, hipStream_t st) {
+  (void)hipGetLastError();
+  if (topk_row_regime(scores, N)) {
+    hipLaunchKernelGGL(topk_small_kernel<Keys>, dim3(T), dim3(kFinThreads), 0, st, scores, stats, sm.parts,
+                       sm.n_parts, sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, k, indices);
+    if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
+    return CSA2_OK;
+  }
+  if (!tile_max) return CSA2_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace) || workspace_bytes < csa2_topk_min_workspace_bytes(T, N, k))
+    return CSA2_ERR_WORKSPACE;
+  int slots;
+  int64_t cap;
+  if (!topk_layout(workspace_bytes, T, N, &slots, &cap)) return CSA2_ERR_WORKSPACE;
+  const int64_t nblk = cand_blocks(N);
+  hipLaunchKernelGGL(topk_floor_kernel, dim3(T), dim3(kFloorThreads), 0, st, tile_max, stats, sm.gmax, sm.n_groups,
+                     sm.parts, sm.n_parts, sm.q, w_idx, q_pos, ratio, q_per_seq, N, kTopK, (int64_t)kTopK);
+  hipLaunchKernelGGL(topk_cand_kernel<Keys>, dim3((unsigned)nblk, T), dim3(kCandThreads), 0, st, tile_max, stats,
+                     sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, k, workspace, T, cap, slots);
+  hipLaunchKernelGGL(topk_select_kernel<Keys>, dim3(T), dim3(kSelThreads), 0, st, tile_max, stats, sm.q, w_idx, keys,
+                     q_pos, ratio, q_per_seq, N, k, indices, workspace, T, cap);
+  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
+  return CSA2_OK;
+}
+
 extern "C" csa2_status csa2_topk(const float* scores, const float* tile_max, uint32_t* stats, size_t stats_bytes,
                                  const void* q_idx, const float* w_idx, const void* k_idx, const int32_t* q_pos,
                                  int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N, int32_t k,
@@ -1977,39 +2055,51 @@ extern "C" csa2_status csa2_topk(const float* scores, const float* tile_max, uin
   if (k != kTopK || N >= ((int64_t)1 << 31) || T > 65535) return CSA2_ERR_UNSUPPORTED;
   IndexPlan p;
   if (!index_plan(T, q_per_seq, N, &p)) return CSA2_ERR_UNSUPPORTED;
-  if (stats_bytes < stats_words(T, p) * sizeof(uint32_t)) return CSA2_ERR_INVALID_ARG;
-  const float* gmax = (const float*)(stats + stats_groups_off(T));
-  const float* parts = (const float*)(stats + stats_parts_off(T, p.n_groups));
-  hipStream_t st = (hipStream_t)hip_stream;
-  (void)hipGetLastError();
-  const uint16_t* q = (const uint16_t*)q_idx;
-  const uint16_t* kx = (const uint16_t*)k_idx;
-  if (topk_row_regime(scores, N)) {
-    hipLaunchKernelGGL(topk_small_kernel, dim3(T), dim3(kFinThreads), 0, st, scores, stats, parts, p.parts(), q,
-                       w_idx, kx, q_pos, ratio, q_per_seq, N, k, indices);
-    if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
-    return CSA2_OK;
-  }
-  if (!tile_max) return CSA2_ERR_INVALID_ARG;
-  if (!workspace || !aligned16(workspace) || workspace_bytes < csa2_topk_min_workspace_bytes(T, N, k))
-    return CSA2_ERR_WORKSPACE;
-  int slots;
-  int64_t cap;
-  if (!topk_layout(workspace_bytes, T, N, &slots, &cap)) return CSA2_ERR_WORKSPACE;
-  const int64_t nblk = cand_blocks(N);
-  hipLaunchKernelGGL(topk_floor_kernel, dim3(T), dim3(kFloorThreads), 0, st, tile_max, stats, gmax, p.n_groups,
-                     parts, p.parts(), q, w_idx, q_pos, ratio, q_per_seq, N, kTopK, (int64_t)kTopK);
-  hipLaunchKernelGGL(topk_cand_kernel, dim3((unsigned)nblk, T), dim3(kCandThreads), 0, st, tile_max, stats, q,
-                     w_idx, kx, q_pos, ratio, q_per_seq, N, k, workspace, T, cap, slots);
-  hipLaunchKernelGGL(topk_select_kernel, dim3(T), dim3(kSelThreads), 0, st, tile_max, stats, q, w_idx, kx, q_pos,
-                     ratio, q_per_seq, N, k, indices, workspace, T, cap);
-  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
-  return CSA2_OK;
+  Summary sm;
+  if (!summary_bf16(stats, stats_bytes, q_idx, T, q_per_seq, N, &sm)) return CSA2_ERR_INVALID_ARG;
+  return topk_launch(scores, tile_max, stats, sm, w_idx, Bf16Keys{(const uint16_t*)k_idx}, q_pos, ratio, T,
+                     q_per_seq, N, k, indices, workspace, workspace_bytes, (hipStream_t)hip_stream);
+}
+
+extern "C" csa2_status csa2_topk_mxfp4(const float* scores, const float* tile_max, uint32_t* stats,
+                                       size_t stats_bytes, const float* w_idx, const uint8_t* k_codes,
+                                       const uint8_t* k_scales, const int32_t* q_pos, int32_t ratio, int32_t T,
+                                       int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices, void* workspace,
+                                       size_t workspace_bytes, void* hip_stream) {
+  if (!stats || !w_idx || !k_codes || !k_scales || !indices) return CSA2_ERR_INVALID_ARG;
+  if ((scores && !aligned16(scores)) || (tile_max && !aligned16(tile_max)) || !aligned16(stats) ||
+      !aligned16(w_idx) || !aligned16(k_codes) || !aligned16(k_scales) || !aligned16(indices) ||
+      (q_pos && !aligned16(q_pos)))
+    return CSA2_ERR_INVALID_ARG;
+  if (T < 1 || q_per_seq < 1 || T % q_per_seq != 0 || N < 1 || ratio < 1) return CSA2_ERR_INVALID_ARG;
+  if (k != kTopK || N >= ((int64_t)1 << 31) || T > 65535) return CSA2_ERR_UNSUPPORTED;
+  MxPlan p;
+  if (!mx_plan(T, q_per_seq, N, &p)) return CSA2_ERR_UNSUPPORTED;
+  Summary sm;
+  if (!summary_mx(stats, stats_bytes, T, q_per_seq, N, &sm)) return CSA2_ERR_INVALID_ARG;
+  return topk_launch(scores, tile_max, stats, sm, w_idx, Mx4Keys{k_codes, k_scales}, q_pos, ratio, T, q_per_seq, N,
+                     k, indices, workspace, workspace_bytes, (hipStream_t)hip_stream);
 }
 
 extern "C" size_t csa2_hsi_pool_workspace_bytes(int32_t T, int64_t N) {
   if (T < 1 || N < 1) return 0;
   return hsi_ws_bytes(T, N);
+}
+
+template <class Keys>
+static csa2_status hsi_launch(const float* tile_max, const Summary& sm, const float* w_idx, Keys keys,
+                              const int32_t* q_pos, int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N,
+                              int32_t* pool, void* workspace, size_t workspace_bytes, hipStream_t st) {
+  if (!workspace || !aligned16(workspace) || workspace_bytes < hsi_ws_bytes(T, N)) return CSA2_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  uint32_t* hdr = (uint32_t*)workspace;  // HsiWs::hdr is at the start of the workspace
+  hipLaunchKernelGGL(topk_floor_kernel, dim3(T), dim3(kFloorThreads), 0, st, tile_max, hdr, sm.gmax, sm.n_groups,
+                     sm.parts, sm.n_parts, sm.q, w_idx, q_pos, ratio, q_per_seq, N, kHsiBlocks, (int64_t)kHsiPool);
+  hipLaunchKernelGGL(hsi_cand_kernel<Keys>, dim3((unsigned)cand_blocks(N), T), dim3(kCandThreads), 0, st, tile_max,
+                     sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, workspace, T);
+  hipLaunchKernelGGL(hsi_select_kernel, dim3(T), dim3(kHsiSelThreads), 0, st, q_pos, ratio, N, workspace, T, pool);
+  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
+  return CSA2_OK;
 }
 
 extern "C" csa2_status csa2_hsi_pool(const float* tile_max, const uint32_t* stats, size_t stats_bytes,
@@ -2024,20 +2114,27 @@ extern "C" csa2_status csa2_hsi_pool(const float* tile_max, const uint32_t* stat
   if (N >= ((int64_t)1 << 31) || T > 65535) return CSA2_ERR_UNSUPPORTED;
   IndexPlan p;
   if (!index_plan(T, q_per_seq, N, &p)) return CSA2_ERR_UNSUPPORTED;
-  if (stats_bytes < stats_words(T, p) * sizeof(uint32_t)) return CSA2_ERR_INVALID_ARG;
-  if (!workspace || !aligned16(workspace) || workspace_bytes < hsi_ws_bytes(T, N)) return CSA2_ERR_WORKSPACE;
-  const float* gmax = (const float*)(stats + stats_groups_off(T));
-  const float* parts = (const float*)(stats + stats_parts_off(T, p.n_groups));
-  hipStream_t st = (hipStream_t)hip_stream;
-  (void)hipGetLastError();
-  const uint16_t* q = (const uint16_t*)q_idx;
-  const uint16_t* kx = (const uint16_t*)k_idx;
-  uint32_t* hdr = (uint32_t*)workspace;  // HsiWs::hdr is at the start of the workspace
-  hipLaunchKernelGGL(topk_floor_kernel, dim3(T), dim3(kFloorThreads), 0, st, tile_max, hdr, gmax, p.n_groups, parts,
-                     p.parts(), q, w_idx, q_pos, ratio, q_per_seq, N, kHsiBlocks, (int64_t)kHsiPool);
-  hipLaunchKernelGGL(hsi_cand_kernel, dim3((unsigned)cand_blocks(N), T), dim3(kCandThreads), 0, st, tile_max, q,
-                     w_idx, kx, q_pos, ratio, q_per_seq, N, workspace, T);
-  hipLaunchKernelGGL(hsi_select_kernel, dim3(T), dim3(kHsiSelThreads), 0, st, q_pos, ratio, N, workspace, T, pool);
-  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
-  return CSA2_OK;
+  Summary sm;
+  if (!summary_bf16(stats, stats_bytes, q_idx, T, q_per_seq, N, &sm)) return CSA2_ERR_INVALID_ARG;
+  return hsi_launch(tile_max, sm, w_idx, Bf16Keys{(const uint16_t*)k_idx}, q_pos, ratio, T, q_per_seq, N, pool,
+                    workspace, workspace_bytes, (hipStream_t)hip_stream);
+}
+
+extern "C" csa2_status csa2_hsi_pool_mxfp4(const float* tile_max, const uint32_t* stats, size_t stats_bytes,
+                                           const float* w_idx, const uint8_t* k_codes, const uint8_t* k_scales,
+                                           const int32_t* q_pos, int32_t ratio, int32_t T, int32_t q_per_seq,
+                                           int64_t N, int32_t* pool, void* workspace, size_t workspace_bytes,
+                                           void* hip_stream) {
+  if (!tile_max || !stats || !w_idx || !k_codes || !k_scales || !pool) return CSA2_ERR_INVALID_ARG;
+  if (!aligned16(tile_max) || !aligned16(stats) || !aligned16(w_idx) || !aligned16(k_codes) || !aligned16(k_scales) ||
+      !aligned16(pool) || (q_pos && !aligned16(q_pos)))
+    return CSA2_ERR_INVALID_ARG;
+  if (T < 1 || q_per_seq < 1 || T % q_per_seq != 0 || N < 1 || ratio < 1) return CSA2_ERR_INVALID_ARG;
+  if (N >= ((int64_t)1 << 31) || T > 65535) return CSA2_ERR_UNSUPPORTED;
+  MxPlan p;
+  if (!mx_plan(T, q_per_seq, N, &p)) return CSA2_ERR_UNSUPPORTED;
+  Summary sm;
+  if (!summary_mx(stats, stats_bytes, T, q_per_seq, N, &sm)) return CSA2_ERR_INVALID_ARG;
+  return hsi_launch(tile_max, sm, w_idx, Mx4Keys{k_codes, k_scales}, q_pos, ratio, T, q_per_seq, N, pool, workspace,
+                    workspace_bytes, (hipStream_t)hip_stream);
 }

@@ -225,6 +225,22 @@ def make_case(name, B, N, q_per_seq=1, ratio=1, prefix=None, window=128, k=512, 
     return c
 
 
+def mx_indexer(c: "Case", chunk_rows: int = 1 << 16):
+    """MXFP4 indexer operands quantised from the case's bf16 indexer queries and keys
+    -> (q_codes uint8 [T][32][64], q_scales uint8 [T][32][4], k_codes uint8 [B][N][64],
+    k_scales uint8 [B][N][4]), on the case's device."""
+    T, B, N = c.T, c.B, c.N
+    qc, qs = mxfp4_quantize(c.q_idx.reshape(T * IDX_HEADS, IDX_DIM))
+    kc = torch.empty((B * N, IDX_DIM // 2), dtype=torch.uint8, device=c.k_idx.device)
+    ks = torch.empty((B * N, IDX_DIM // MX_BLOCK), dtype=torch.uint8, device=c.k_idx.device)
+    flat = c.k_idx.reshape(B * N, IDX_DIM)
+    for r0 in range(0, B * N, chunk_rows):
+        r1 = min(B * N, r0 + chunk_rows)
+        kc[r0:r1], ks[r0:r1] = mxfp4_quantize(flat[r0:r1])
+    return (qc.view(T, IDX_HEADS, IDX_DIM // 2), qs.view(T, IDX_HEADS, IDX_DIM // MX_BLOCK),
+            kc.view(B, N, IDX_DIM // 2), ks.view(B, N, IDX_DIM // MX_BLOCK))
+
+
 def kv_rows(seed: int, rows: torch.Tensor):
     """Regenerate selected flat KV rows (b*N + s) -> (codes, scales)."""
     x = normal_bf16_rows(seed, ST_KV, rows, DIM)

@@ -205,6 +205,47 @@ csa2_status csa2_reindex(const int32_t* pool, const void* q_idx, const float* w_
                          int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices,
                          void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* ---------------------------------------------------------- MXFP4 indexer
+ * The indexer with FP4 queries and keys (report sec. 2.4.4: DeepSeek-V4 trains
+ * its indexer queries and keys for FP4, in the MXFP4 format).  A 128-channel
+ * vector is 64 code bytes (E2M1, element 2i in the low nibble of byte i) and
+ * 4 E8M0 scale bytes (scale b covers channels 32b .. 32b + 31):
+ *   deq(x)[c] = E2M1(code[c]) * 2^(scale[c / 32] - 127)   (scale 255 invalid).
+ * Scores, I_fp64, selection order and outputs are those of the bf16 entry
+ * points evaluated on the dequantised values (each exact in bf16).  The key
+ * stream is 68 bytes per entry instead of 256.
+ *
+ * csa2_index_mxfp4    as csa2_index, with
+ *     q_codes uint8 [T][32][64], q_scales uint8 [T][32][4],
+ *     k_codes uint8 [B][N][64],  k_scales uint8 [B][N][4];
+ *     stats >= csa2_index_mxfp4_stats_bytes(T, q_per_seq, N): the summary for
+ *     csa2_topk_mxfp4 / csa2_hsi_pool_mxfp4, which also carries the
+ *     dequantised queries (those calls take no query argument).  One kernel.
+ * csa2_topk_mxfp4     as csa2_topk (stats header written the same way).
+ * csa2_hsi_pool_mxfp4 as csa2_hsi_pool.
+ * csa2_reindex_mxfp4  as csa2_reindex, with the Reindex layer's FP4 query
+ *     (q_codes [T][32][64], q_scales [T][32][4]) and the FP4 keys; workspace
+ *     >= csa2_reindex_workspace_bytes(T, k).
+ */
+size_t csa2_index_mxfp4_stats_bytes(int32_t T, int32_t q_per_seq, int64_t N);
+csa2_status csa2_index_mxfp4(const uint8_t* q_codes, const uint8_t* q_scales, const float* w_idx,
+                             const uint8_t* k_codes, const uint8_t* k_scales, const int32_t* q_pos,
+                             int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N, float* scores,
+                             float* tile_max, uint32_t* stats, size_t stats_bytes, void* hip_stream);
+csa2_status csa2_topk_mxfp4(const float* scores, const float* tile_max, uint32_t* stats, size_t stats_bytes,
+                            const float* w_idx, const uint8_t* k_codes, const uint8_t* k_scales,
+                            const int32_t* q_pos, int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N,
+                            int32_t k, int32_t* indices, void* workspace, size_t workspace_bytes,
+                            void* hip_stream);
+csa2_status csa2_hsi_pool_mxfp4(const float* tile_max, const uint32_t* stats, size_t stats_bytes,
+                                const float* w_idx, const uint8_t* k_codes, const uint8_t* k_scales,
+                                const int32_t* q_pos, int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N,
+                                int32_t* pool, void* workspace, size_t workspace_bytes, void* hip_stream);
+csa2_status csa2_reindex_mxfp4(const int32_t* pool, const uint8_t* q_codes, const uint8_t* q_scales,
+                               const float* w_idx, const uint8_t* k_codes, const uint8_t* k_scales, int32_t T,
+                               int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices, void* workspace,
+                               size_t workspace_bytes, void* hip_stream);
+
 /* ----------------------------------------------------------------- attend
  * Joint sparse + sliding-window attention over an FP4 main-KV cache.  For
  * query t (sequence b) and head h, over the set E_t of

@@ -28,7 +28,8 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"csa2_index", "csa2_topk", "csa2_attend_fp4", "csa2_reuse_attend", "csa2_hsi_pool",
-            "csa2_reindex"} <= set(names)
+            "csa2_reindex", "csa2_index_mxfp4", "csa2_topk_mxfp4", "csa2_hsi_pool_mxfp4",
+            "csa2_reindex_mxfp4"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -180,6 +181,38 @@ def test_reindex_host_validation(L):
     assert _reindex(L, k=256) == UNSUPPORTED
     assert _reindex(L, ws=None) == WORKSPACE
     assert _reindex(L, wsb=csa.reindex_workspace_bytes(4) - 1) == WORKSPACE
+
+
+def test_mxfp4_host_validation(L):
+    T, N = 4, 1 << 20
+    sb = csa.index_mxfp4_stats_bytes(T, 1, N)
+    # summary: header, at least 4096 group maxima per query, then the dequantised queries
+    assert sb >= T * 16 + T * 4096 * 4 + T * 32 * 128 * 2
+    assert csa.index_mxfp4_stats_bytes(4, 3, 100) == 0
+    ix = lambda **kw: L.csa2_index_mxfp4(kw.get("qc", P), kw.get("qs", P), P, kw.get("kc", P), kw.get("ks", P), None,
+                                         1, kw.get("T", T), 1, kw.get("N", N), None, P, P, kw.get("sb", sb), None)
+    assert ix(qc=None) == INVALID
+    assert ix(ks=MIS) == INVALID
+    assert ix(T=0) == INVALID
+    assert ix(N=1 << 31) == UNSUPPORTED
+    assert ix(sb=sb - 1) == INVALID
+    tk = lambda **kw: L.csa2_topk_mxfp4(None, kw.get("tm", P), P, kw.get("sb", sb), P, kw.get("kc", P), P, None, 1, T,
+                                        1, N, kw.get("k", 512), P, kw.get("ws", P),
+                                        kw.get("wsb", csa.topk_workspace_bytes(T, N)), None)
+    assert tk(kc=None) == INVALID
+    assert tk(tm=None) == INVALID
+    assert tk(sb=sb - 1) == INVALID
+    assert tk(k=256) == UNSUPPORTED
+    assert tk(ws=None) == WORKSPACE
+    hp = lambda **kw: L.csa2_hsi_pool_mxfp4(P, P, kw.get("sb", sb), P, P, P, None, 1, T, 1, N, P, kw.get("ws", P),
+                                            csa.hsi_pool_workspace_bytes(T, N), None)
+    assert hp(sb=sb - 1) == INVALID
+    assert hp(ws=None) == WORKSPACE
+    rx = lambda **kw: L.csa2_reindex_mxfp4(kw.get("pool", P), P, P, P, P, P, T, 1, N, kw.get("k", 512), P,
+                                           kw.get("ws", P), csa.reindex_workspace_bytes(T), None)
+    assert rx(pool=None) == INVALID
+    assert rx(k=256) == UNSUPPORTED
+    assert rx(ws=None) == WORKSPACE
 
 
 def test_binding_fails_loudly_without_gpu_tensors():

@@ -145,3 +145,30 @@ def test_causal_prefill_hierarchical_sampled():
     log("[full] causal_prefill 4096 queries: candidate pool + Reindex")
     c = G.make_case("causal_prefill", **G.CONFIGS["causal_prefill"], seed=0, device=DEV, with_kv=False)
     check_hierarchical(c, [0, 2048, 4095])
+
+
+def test_long_decode_mxfp4_indexer_sampled():
+    # the MXFP4 indexer at the long-decode shape: scores within the bound and the exact
+    # top-512 on sampled queries; attention over that selection within tolerance
+    import oracle
+    log("[full] long_decode 4 x 1M, MXFP4 indexer")
+    c = G.make_case("long_decode", **G.CONFIGS["long_decode"], seed=0, device=DEV)
+    qc, qs, kc, ks = G.mx_indexer(c)
+    ix = csa.csa2_index_mxfp4(qc, qs, c.w_idx, kc, ks, c.q_pos, 1, 1, want_scores=False)
+    idx = csa.csa2_topk_mxfp4(None, ix.tile_max, ix.stats, c.w_idx, kc, ks, c.q_pos, 1, 1)
+    out = csa.csa2_attend_fp4(c.q[0].view(BF), c.kv_codes, c.kv_scales, idx, c.swa[0].view(BF), c.swa_end, None,
+                              c.softmax_scale, 1, c.window)
+    full = csa.csa2_index_mxfp4(qc, qs, c.w_idx, kc, ks, c.q_pos, 1, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(full.tile_max, ix.tile_max)
+    eps = npy(ix.err_bound)
+    for t in [0, 3]:
+        ref = oracle.index_mx(npy(qc[t:t + 1]), npy(qs[t:t + 1]), npy(c.w_idx[t:t + 1]), npy(kc[t:t + 1]),
+                              npy(ks[t:t + 1]), npy(c.q_pos[t:t + 1]), 1, 1)
+        err = np.abs(npy(full.scores[t]).astype(np.float64) - ref[0])
+        assert np.all(err <= eps[t]), f"t={t}: {err.max()} > {eps[t]}"
+        ref_i = oracle.topk(ref, npy(c.q_pos[t:t + 1]), 1, 512)[0]
+        assert np.array_equal(npy(idx[t]), ref_i), f"t={t}: top-512 differs"
+        ref_o = oracle_attend(c, {t: ref_i})
+        assert_close_bf16(out[t], ref_o[t][0], what=f"mx t={t}")
+        log(f"  t={t}: max|err|/eps={err.max() / eps[t]:.2e}, indices exact, attention within tolerance")
