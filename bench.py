@@ -114,6 +114,7 @@ def summarize(stats_dir, fetch_dir=None, write_dir=None, mfma_dir=None):
         for r in data:
             name = r["Kernel_Name"]
             key = ("scan" if "idx_scan_kernel" in name and int(r["Grid_Size"]) == scan_grid else
+                   "scan_mx" if "idx_scan_mx_kernel" in name else
                    "cal" if "neg_kernel" in name else
                    "attend" if "attend_kernel" in name else "combine" if "attend_combine" in name else None)
             if key:
@@ -137,6 +138,12 @@ def summarize(stats_dir, fetch_dir=None, write_dir=None, mfma_dir=None):
     print(f"- WRITE scale: {w_scale:.4f}")
     print(f"- HBM bytes per launch: {traffic:.0f}")
     print(f"- scan sources sha256: `{scan_sources_sha256()}`")
+    if "scan_mx" in f and "scan_mx" in w:
+        mx = f["scan_mx"] * 1024 * f_scale + w["scan_mx"] * 1024 * w_scale
+        print("\n### HBM traffic of idx_scan_mx_kernel (MXFP4 indexer, same runs and scales)\n")
+        print(f"- FETCH_SIZE KiB per dispatch: {f['scan_mx']:.0f} (mean of {fn['scan_mx']})")
+        print(f"- WRITE_SIZE KiB per dispatch: {w['scan_mx']:.0f} (mean of {wn['scan_mx']})")
+        print(f"- HBM bytes per launch: {mx:.0f}")
     # attention kernels, split by grid size (the single-layer call and the
     # three-layer Reuse call launch different grids)
     def by_grid(d, counter, kernel):
@@ -298,6 +305,9 @@ def main():
     att_gbps = att_bytes / (att_avg * 1e-6) / 1e9
     att_tflops = att_flops / (att_avg * 1e-6) / 1e12
 
+    # ---- the same step with the MXFP4 indexer (FP4 queries and keys, 68 B per key)
+    mx = mxfp4_step(c, G, csa, args, stream, timed, idx, out, ws_t, ws_a)
+
     # plain copy bandwidth of this machine (context for the roofline fraction)
     x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     y = torch.empty_like(x)
@@ -341,6 +351,7 @@ def main():
         "attention": {"call": "csa2_attend_fp4 (attend + merge kernels)", "avg_us": att_avg,
                       "algorithmic_bytes": att_bytes, "GBps": att_gbps, "frac_hbm": att_gbps / HBM_PEAK_GBPS,
                       "flops": att_flops, "TFLOPs": att_tflops, "frac_mfma_bf16": att_tflops / MFMA_BF16_PEAK_TFLOPS},
+        "mxfp4_indexer": mx,
         "copy_GBps": copy_gbps,
     }
 
@@ -348,6 +359,59 @@ def main():
         line["cpu_baseline"] = cpu_baseline(c, G)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def mxfp4_step(c, G, csa, args, stream, timed, idx, out, ws_t, ws_a):
+    """The decode step with MXFP4 indexer queries and keys (the generator's quantisation of
+    the same bf16 ones): csa2_index_mxfp4 + csa2_topk_mxfp4 + csa2_attend_fp4."""
+    import torch
+    B, N, T = c.B, c.N, c.T
+    qc, qs, kc, ks = G.mx_indexer(c)
+    dev = qc.device
+    tile_max = torch.empty((T, csa.tile_max_ld(N)), dtype=torch.float32, device=dev)
+    stats = torch.empty(csa.index_mxfp4_stats_bytes(T, 1, N) // 4, dtype=torch.int32, device=dev)
+    q0 = c.q[0].view(torch.bfloat16)
+    swa0 = c.swa[0].view(torch.bfloat16)
+
+    def do_index():
+        csa.csa2_index_mxfp4(qc, qs, c.w_idx, kc, ks, c.q_pos, 1, 1, want_scores=False, tile_max=tile_max,
+                             stats=stats)
+
+    def do_topk():
+        csa.csa2_topk_mxfp4(None, tile_max, stats, c.w_idx, kc, ks, c.q_pos, 1, 1, indices=idx, workspace=ws_t)
+
+    def step():
+        do_index()
+        do_topk()
+        csa.csa2_attend_fp4(q0, c.kv_codes, c.kv_scales, idx, swa0, c.swa_end, None, c.softmax_scale, 1, 128,
+                            out=out, workspace=ws_a)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    reps = max(10, args.steps)
+    idx_med, idx_avg = timed(do_index, reps)
+    topk_med, _ = timed(do_topk, reps)
+    # algorithmic bytes of the FP4 scan per launch: 68 B per key, per query the FP4 query
+    # (2048 + 128 B), w (128 B), the header (16 B), the dequantised query it leaves for the
+    # selection (8192 B) and its tile maxima
+    scan_bytes = B * N * 68 + T * (2048 + 128 + 128 + 16 + 8192) + T * csa.tile_max_ld(N) * 4
+    step_bytes = T * (68 * N + 2048 + 128 + 128 + 512 * 272 + 128 * 1024 + 65536 + 65536 + 512 * 4)
+    scan_gbps = scan_bytes / (idx_avg * 1e-6) / 1e9
+    return {"value": T / (ms_step * 1e-3), "unit": "queries/s", "ms_per_step": ms_step,
+            "indexer": "32x128 MXFP4 (E2M1 + E8M0/32), 68 B per key",
+            "scan": {"kernel": "idx_scan_mx_kernel (all of csa2_index_mxfp4)", "bound": "hbm",
+                     "achieved": scan_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": scan_gbps / HBM_PEAK_GBPS,
+                     "algorithmic_bytes_per_launch": scan_bytes, "avg_launch_us": idx_avg},
+            "stages_us": {"index": idx_med, "topk": topk_med},
+            "step_hbm_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
+            "step_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "note": "same workload and selection semantics with FP4 indexer operands; not the headline"}
 
 
 def cpu_baseline(c, G, min_seconds=10.0, max_seconds=30.0):

@@ -21,6 +21,8 @@ namespace csa2 {
 // chunks x, x + gridDim.x, ... of 512 keys; wave w takes keys 128w .. 128w+127
 // of each chunk.  Group (x * kMxTiles + u) * S + (i % S) holds the maxima of
 // tile u of every wave in the block's iterations i.
+static_assert(kMxTiles == 8, "lane l stores keys l and 64 + l of the wave's 128");
+
 template <int QG, int S>
 __global__ __launch_bounds__(kMxThreads) void idx_scan_mx_kernel(
     const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, const float* __restrict__ w_idx,

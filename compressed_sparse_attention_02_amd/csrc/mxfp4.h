@@ -127,10 +127,10 @@ __device__ __forceinline__ float mx_block_norm2_bound(uint32_t s) {
 
 constexpr int kMxThreads = 256;                 // 4 waves
 constexpr int kMxWaves = kMxThreads / 64;
-constexpr int kMxTiles = 8;                     // 16-key tiles per wave per iteration
+constexpr int kMxTiles = 8;                     // 16-key tiles per wave per iteration (the score store assumes 8)
 constexpr int kMxWaveKeys = 16 * kMxTiles;      // 128
 constexpr int kMxChunkKeys = kMxWaveKeys * kMxWaves;  // 512 keys per block iteration
-constexpr int kMxBlocks = 8192;                 // blocks per launch the grid aims for
+constexpr int kMxBlocks = 2048;                 // blocks per launch the grid aims for (measured: 2048-4096 best)
 constexpr int kMxGroupsWanted = 4096;
 
 struct MxPlan {

@@ -693,11 +693,22 @@ __global__ __launch_bounds__(kFloorThreads) void topk_floor_kernel(
   double qf, sw;
   bound_terms(q_idx + (size_t)t * kIdxHeads * kIdxDim, w_idx + (size_t)t * kIdxHeads,
               parts + (size_t)(t / q_per_seq) * n_parts, n_parts, tid, kFloorThreads, &m2, &qf, &sw);
-  if (nsrc > kFloorVals) {
+  // folding: one level of kFloorVals values at a time, each level's loads issued together
+  for (int64_t lvl = kFloorVals; lvl < nsrc; lvl += kFloorVals) {
+    float4 x[kFloorPer / 4];
 #pragma unroll
-    for (int m = 0; m < kFloorPer; ++m) {
-      const int64_t j = 4 * ((int64_t)(m / 4) * kFloorThreads + tid) + (m % 4);
-      for (int64_t i = j + kFloorVals; i < nsrc; i += kFloorVals) v[m] = fmaxf(v[m], src[i]);
+    for (int m = 0; m < kFloorPer / 4; ++m) {
+      const int64_t j = lvl + 4 * ((int64_t)m * kFloorThreads + tid);
+      x[m] = j < nsrc ? *reinterpret_cast<const float4*>(src + j)
+                      : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+#pragma unroll
+    for (int m = 0; m < kFloorPer / 4; ++m) {
+      const int64_t j = lvl + 4 * ((int64_t)m * kFloorThreads + tid);
+      v[4 * m] = fmaxf(v[4 * m], x[m].x);
+      v[4 * m + 1] = fmaxf(v[4 * m + 1], j + 1 < nsrc ? x[m].y : -INFINITY);
+      v[4 * m + 2] = fmaxf(v[4 * m + 2], j + 2 < nsrc ? x[m].z : -INFINITY);
+      v[4 * m + 3] = fmaxf(v[4 * m + 3], j + 3 < nsrc ? x[m].w : -INFINITY);
     }
   }
   float lmax = -INFINITY, lmin = INFINITY;
