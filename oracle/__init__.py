@@ -57,6 +57,13 @@ def lib():
         L.csa2o_topk_row.argtypes, L.csa2o_topk_row.restype = [vp, i64, i32, vp], i32
         L.csa2o_topk.argtypes, L.csa2o_topk.restype = [vp, vp, i32, i32, i64, i32, vp], None
         L.csa2o_attend.argtypes = [vp, vp, vp, vp, vp, vp, vp, dbl, i32, i32, i64, i32, i32, i32, vp, vp]
+        L.csa2o_attend_ex.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, dbl, i32, i32, i64, i32, i32,
+                                      i32, vp, dbl, vp, vp]
+        L.csa2o_attend_ex.restype = None
+        L.csa2o_e4m3.argtypes, L.csa2o_e4m3.restype = [ctypes.c_uint32], dbl
+        L.csa2o_dequant_row_e4m3.argtypes, L.csa2o_dequant_row_e4m3.restype = [vp, vp, i32, vp], None
+        L.csa2o_dequant_swa_fp8_row.argtypes, L.csa2o_dequant_swa_fp8_row.restype = [vp, vp, vp, vp], None
+        L.csa2o_rope_rotate.argtypes, L.csa2o_rope_rotate.restype = [vp, dbl, dbl], None
         L.csa2o_attend.restype = None
         L.csa2o_hsi_pool_row.argtypes, L.csa2o_hsi_pool_row.restype = [vp, i64, i32, i32, vp], i32
         L.csa2o_hsi_pool.argtypes, L.csa2o_hsi_pool.restype = [vp, vp, i32, i32, i64, i32, i32, vp], None
@@ -173,6 +180,63 @@ def reindex_topk(scores, pool, k):
     out = np.empty((T, k), np.int32)
     lib().csa2o_reindex_topk(_ptr(scores), _ptr(pool), T, N, pool.shape[1], k, _ptr(out))
     return out
+
+
+def e4m3(code: int) -> float:
+    return lib().csa2o_e4m3(code)
+
+
+def dequant_rows_e4m3(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """E2M1 codes uint8 [R][D/2] with E4M3 scales uint8 [R][D/16] -> float64 [R][D]."""
+    codes, scales = _c(codes, np.uint8), _c(scales, np.uint8)
+    R, D = codes.shape[0], codes.shape[1] * 2
+    out = np.empty((R, D), np.float64)
+    for r in range(R):
+        lib().csa2o_dequant_row_e4m3(_ptr(codes[r]), _ptr(scales[r]), D, _ptr(out[r]))
+    return out
+
+
+def dequant_swa_fp8(fp8: np.ndarray, rope: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """FP8 window rows: fp8 uint8 [R][448], rope uint16 [R][64], scales uint8 [R][8] -> float64 [R][512]."""
+    fp8, rope, scales = _c(fp8, np.uint8), _c(rope, np.uint16), _c(scales, np.uint8)
+    out = np.empty((fp8.shape[0], DIM), np.float64)
+    for r in range(fp8.shape[0]):
+        lib().csa2o_dequant_swa_fp8_row(_ptr(fp8[r]), _ptr(rope[r]), _ptr(scales[r]), _ptr(out[r]))
+    return out
+
+
+def rope_rotate(v: np.ndarray, pos: float, base: float) -> np.ndarray:
+    """Rotate channels 448..511 of a 512-vector by RoPE at position pos (returns a copy)."""
+    v = np.array(v, np.float64)
+    lib().csa2o_rope_rotate(_ptr(v), float(pos), float(base))
+    return v
+
+
+def attend_ex(q, kv_codes, kv_scales, indices, swa_end, sink, softmax_scale, q_per_seq, window, kv_format=0,
+              swa=None, swa_fp8=None, swa_rope=None, swa_scales=None, rope_pos=None, rope_base=10000.0):
+    """attend with the main-KV format (0: MXFP4 scales [B][N][16]; 1: E4M3 per 16, scales [B][N][32]),
+    the window as bf16 rows (swa uint16 [B][S][512]) or FP8 rows (swa_fp8 uint8 [B][S][448],
+    swa_rope uint16 [B][S][64], swa_scales uint8 [B][S][8]), and the optional inverse RoPE of the
+    output at -rope_pos[t]."""
+    q = _c(q, np.uint16)
+    kv_codes, kv_scales = _c(kv_codes, np.uint8), _c(kv_scales, np.uint8)
+    indices, swa_end = _c(indices, np.int32), _c(swa_end, np.int32)
+    sk = None if sink is None else _c(np.asarray(sink, np.float64), np.float64)
+    T, N, k = q.shape[0], kv_codes.shape[1], indices.shape[1]
+    if swa is not None:
+        swa = _c(swa, np.uint16)
+        S, swa_format = swa.shape[1], 0
+    else:
+        swa_fp8, swa_rope, swa_scales = _c(swa_fp8, np.uint8), _c(swa_rope, np.uint16), _c(swa_scales, np.uint8)
+        S, swa_format = swa_fp8.shape[1], 1
+    rp = None if rope_pos is None else _c(rope_pos, np.int32)
+    out = np.empty((T, HEADS, DIM), np.float64)
+    lse = np.empty((T, HEADS), np.float64)
+    lib().csa2o_attend_ex(_ptr(q), _ptr(kv_codes), _ptr(kv_scales), kv_format, _ptr(indices), _ptr(swa),
+                          _ptr(swa_fp8), _ptr(swa_rope), _ptr(swa_scales), swa_format, _ptr(swa_end), _ptr(sk),
+                          float(softmax_scale), T, q_per_seq, N, S, window, k, _ptr(rp), float(rope_base), _ptr(out),
+                          _ptr(lse))
+    return out, lse
 
 
 def attend(q, kv_codes, kv_scales, indices, swa, swa_end, sink, softmax_scale, q_per_seq, window):

@@ -67,6 +67,38 @@ void csa2o_dequant_row(const uint8_t* codes, const uint8_t* scales, int32_t dim,
     }
 }
 
+/* OCP 8-bit floating point (OFP8) E4M3: 1 sign bit, 4 exponent bits (bias 7),
+ * 3 mantissa bits; exponent field 0 holds subnormals m/8 * 2^-6; S.1111.111
+ * is NaN (no infinities), so the largest magnitude is 1.75 * 2^8 = 448. */
+double csa2o_e4m3(uint32_t code) {
+    double sign = (code & 0x80u) ? -1.0 : 1.0;
+    uint32_t e = (code >> 3) & 15u, m = code & 7u;
+    if (e == 15u && m == 7u) return NAN;
+    if (e == 0u) return sign * ldexp((double)m, -9);
+    return sign * ldexp(8.0 + (double)m, (int)e - 10);
+}
+
+/* V4.1 report sec. 2.4.4 (the evaluated format it selects for the main KV):
+ * E2M1 elements with one E4M3 scale per 16 channels and no global scale.
+ * x[c] = E2M1(code[c]) * E4M3(scale[c / 16]). */
+void csa2o_dequant_row_e4m3(const uint8_t* codes, const uint8_t* scales, int32_t dim, double* out) {
+    for (int32_t c = 0; c < dim; ++c) {
+        uint8_t byte = codes[c / 2];
+        uint32_t code = (c % 2 == 0) ? (byte & 0x0Fu) : (byte >> 4);
+        out[c] = csa2o_e2m1(code) * csa2o_e4m3(scales[c / 16]);
+    }
+}
+
+/* V4.1 report sec. 2.4.4: the SWA KV stays FP8; the V4 reading (sec. 4.3) keeps
+ * the RoPE channels in BF16 and the others in FP8, 448 + 64 channels per entry
+ * with 8 scale bytes (584 B).  Reading: channels 0..447 are E4M3 with one E8M0
+ * scale per 64 channels (scale bytes 0..6; byte 7 unused), channels 448..511
+ * bf16. */
+void csa2o_dequant_swa_fp8_row(const uint8_t* fp8, const uint16_t* rope, const uint8_t* scales, double* out) {
+    for (int c = 0; c < 448; ++c) out[c] = csa2o_e4m3(fp8[c]) * csa2o_e8m0(scales[c / 64]);
+    for (int c = 448; c < DIM; ++c) out[c] = bf16_to_double(rope[c - 448]);
+}
+
 /* ---- visibility ---------------------------------------------------------- */
 
 /* V4 reading sec. 4.3: the compressed branch sees a compressed block only once
@@ -280,17 +312,37 @@ void csa2o_reindex_topk(const double* scores, const int32_t* pool, int32_t T, in
 
 /* ---- attention ----------------------------------------------------------- */
 
+/* V4 reading sec. 4.3: RoPE on the last 64 channels of q, KV entries and the
+ * core-attention output, the output rotated at position -i so that it carries
+ * relative positions.  Reading: pairs (448 + 2j, 449 + 2j), angle
+ * p * base^(-2j/64) for position p; rotation (x, y) -> (x cos - y sin,
+ * x sin + y cos). */
+void csa2o_rope_rotate(double* v, double pos, double base) {
+    for (int j = 0; j < 32; ++j) {
+        double theta = pow(base, -2.0 * j / 64.0);
+        double phi = pos * theta;
+        double x = v[448 + 2 * j], y = v[449 + 2 * j];
+        v[448 + 2 * j] = x * cos(phi) - y * sin(phi);
+        v[449 + 2 * j] = x * sin(phi) + y * cos(phi);
+    }
+}
+
 /* V4 reading sec. 4.1: shared-KV MQA, the selected compressed entry is both
  * key and value; sec. 4.3: an SWA branch of the 128 most recent tokens and an
  * optional per-head sink exp(z'_h) in the softmax denominator.  V4.1 report
  * sec. 2.3: each query attends to the selected entries together with the
  * layer-local SWA KV; sec. 3.2.2: window [max(s, i-W+1), i].
  * One softmax over the union (the neshdevtech reading, sec. 3.3.1/3.3.2,
- * concatenates SWA and selected main KV into a single readout). */
-void csa2o_attend(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_scales,
-                  const int32_t* indices, const uint16_t* swa, const int32_t* swa_end,
-                  const double* sink, double softmax_scale, int32_t T, int32_t q_per_seq,
-                  int64_t N, int32_t S, int32_t window, int32_t k, double* out, double* lse) {
+ * concatenates SWA and selected main KV into a single readout).
+ * kv_format 0: MXFP4 rows (E8M0 per 32, scales [B][N][16]); 1: E2M1 with E4M3
+ * per 16 (scales [B][N][32]).  swa_format 0: bf16 rows [B][S][512]; 1: FP8 rows
+ * (swa_fp8 [B][S][448], swa_rope [B][S][64], swa_scales [B][S][8]).  With
+ * rope_pos, each output row is rotated at -rope_pos[t] (csa2o_rope_rotate). */
+void csa2o_attend_ex(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_scales, int32_t kv_format,
+                     const int32_t* indices, const uint16_t* swa, const uint8_t* swa_fp8, const uint16_t* swa_rope,
+                     const uint8_t* swa_scales, int32_t swa_format, const int32_t* swa_end, const double* sink,
+                     double softmax_scale, int32_t T, int32_t q_per_seq, int64_t N, int32_t S, int32_t window,
+                     int32_t k, const int32_t* rope_pos, double rope_base, double* out, double* lse) {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int32_t t = 0; t < T; ++t) {
         int64_t b = t / q_per_seq;
@@ -308,13 +360,22 @@ void csa2o_attend(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_
         for (int32_t j = 0; j < k; ++j) {
             int64_t s = indices[(int64_t)t * k + j];
             if (s < 0) continue;
-            csa2o_dequant_row(kv_codes + (b * N + s) * (DIM / 2), kv_scales + (b * N + s) * (DIM / MX_BLOCK),
-                              DIM, rows + (int64_t)r * DIM);
+            if (kv_format == 0)
+                csa2o_dequant_row(kv_codes + (b * N + s) * (DIM / 2), kv_scales + (b * N + s) * (DIM / MX_BLOCK),
+                                  DIM, rows + (int64_t)r * DIM);
+            else
+                csa2o_dequant_row_e4m3(kv_codes + (b * N + s) * (DIM / 2), kv_scales + (b * N + s) * (DIM / 16),
+                                       DIM, rows + (int64_t)r * DIM);
             ++r;
         }
-        for (int32_t i = start; i < end; ++i, ++r)
-            for (int c = 0; c < DIM; ++c)
-                rows[(int64_t)r * DIM + c] = bf16_to_double(swa[(b * S + i) * DIM + c]);
+        for (int32_t i = start; i < end; ++i, ++r) {
+            if (swa_format == 0) {
+                for (int c = 0; c < DIM; ++c) rows[(int64_t)r * DIM + c] = bf16_to_double(swa[(b * S + i) * DIM + c]);
+            } else {
+                csa2o_dequant_swa_fp8_row(swa_fp8 + (b * S + i) * 448, swa_rope + (b * S + i) * 64,
+                                          swa_scales + (b * S + i) * 8, rows + (int64_t)r * DIM);
+            }
+        }
 
         double* z = (double*)malloc((size_t)(n_rows > 0 ? n_rows : 1) * sizeof(double));
         for (int h = 0; h < HEADS; ++h) {
@@ -341,9 +402,18 @@ void csa2o_attend(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_
             }
             if (sink) den += exp(sink[h] - m);
             for (int c = 0; c < DIM; ++c) o[c] /= den;
+            if (rope_pos) csa2o_rope_rotate(o, -(double)rope_pos[t], rope_base);
             if (lse) lse[(int64_t)t * HEADS + h] = m + log(den);
         }
         free(z);
         free(rows);
     }
+}
+
+void csa2o_attend(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                  const int32_t* indices, const uint16_t* swa, const int32_t* swa_end,
+                  const double* sink, double softmax_scale, int32_t T, int32_t q_per_seq,
+                  int64_t N, int32_t S, int32_t window, int32_t k, double* out, double* lse) {
+    csa2o_attend_ex(q, kv_codes, kv_scales, 0, indices, swa, NULL, NULL, NULL, 0, swa_end, sink, softmax_scale, T,
+                    q_per_seq, N, S, window, k, NULL, 0.0, out, lse);
 }

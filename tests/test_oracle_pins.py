@@ -541,3 +541,142 @@ def test_index_mx_is_bf16_index_of_dequantised_values(oracle_lib):
     got = oracle.index_mx(qc.numpy().reshape(3, 32, 64), qs.numpy().reshape(3, 32, 4), w,
                           kc.numpy().reshape(1, 40, 64), ks.numpy().reshape(1, 40, 4), pos, 1, 3)
     assert np.array_equal(got, ref)
+
+
+# ---- the pages' main-KV format, FP8 window rows, inverse RoPE of the output
+
+def test_e4m3_table_matches_spec(oracle_lib):
+    import oracle
+    for code, val in _golden("e4m3_values.txt"):
+        got = oracle.e4m3(int(code, 16))
+        if val == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == float(val) and math.copysign(1.0, got) == math.copysign(1.0, float(val)), (code, got)
+    # every finite positive code is larger than the one before; negatives mirror them
+    pos = [oracle.e4m3(c) for c in range(0x7F)]
+    assert all(b > a for a, b in zip(pos, pos[1:]))
+    assert all(oracle.e4m3(0x80 | c) == -oracle.e4m3(c) for c in range(1, 0x7F))
+
+
+def test_dequant_e4m3_worked_example(oracle_lib):
+    # channel 0: code 15 (-6) with scale 0x7E (448) -> -2688, the largest magnitude of the
+    # format (report sec. 2.4.4); channel 17 (block 1, high nibble of byte 8): code 5 (3.0)
+    # with scale 0x39 (1.125) -> 3.375
+    import oracle
+    codes = np.zeros((1, 256), np.uint8)
+    scales = np.full((1, 32), 0x38, np.uint8)
+    codes[0, 0] = 15
+    scales[0, 0] = 0x7E
+    codes[0, 8] = 5 << 4
+    scales[0, 1] = 0x39
+    x = oracle.dequant_rows_e4m3(codes, scales)[0]
+    want = np.zeros(512)
+    want[0], want[17] = -2688.0, 3.375
+    assert np.array_equal(x, want)
+
+
+def test_dequant_swa_fp8_worked_example(oracle_lib):
+    # channel 70 (scale block 1): 0x40 (2.0) x 2^(126-127) = 1.0; channel 447 (block 6):
+    # 0xB8 (-1.0) x 2^3 = -8; channel 448: bf16 1.5 (the RoPE channels are bf16)
+    import oracle
+    fp8 = np.zeros((1, 448), np.uint8)
+    rope = np.zeros((1, 64), np.uint16)
+    sc = np.full((1, 8), 127, np.uint8)
+    fp8[0, 70], sc[0, 1] = 0x40, 126
+    fp8[0, 447], sc[0, 6] = 0xB8, 130
+    rope[0, 0] = _bf16(1.5)
+    x = oracle.dequant_swa_fp8(fp8, rope, sc)[0]
+    want = np.zeros(512)
+    want[70], want[447], want[448] = 1.0, -8.0, 1.5
+    assert np.array_equal(x, want)
+
+
+def _rope_np(v, pos, base):
+    """Forward RoPE on channels 448..511 (independent numpy statement of the reading)."""
+    v = np.array(v, np.float64)
+    j = np.arange(32)
+    phi = pos * base ** (-2.0 * j / 64.0)
+    x, y = v[..., 448::2].copy(), v[..., 449::2].copy()
+    v[..., 448::2] = x * np.cos(phi) - y * np.sin(phi)
+    v[..., 449::2] = x * np.sin(phi) + y * np.cos(phi)
+    return v
+
+
+def test_rope_rotate_cases(oracle_lib):
+    import oracle
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal(512)
+    assert np.array_equal(oracle.rope_rotate(v, 0.0, 10000.0), v)           # position 0: identity
+    e = np.zeros(512)
+    e[448] = 1.0                                                             # pair 0, theta = 1
+    r = oracle.rope_rotate(e, 1.0, 10000.0)
+    assert r[448] == math.cos(1.0) and r[449] == math.sin(1.0)
+    e = np.zeros(512)
+    e[449 + 32] = 1.0                                                        # pair 16: theta = 10000^-0.5
+    r = oracle.rope_rotate(e, 3.0, 10000.0)
+    assert abs(r[448 + 32] + math.sin(0.03)) < 1e-15 and abs(r[449 + 32] - math.cos(0.03)) < 1e-15
+    r = oracle.rope_rotate(v, 12345.0, 10000.0)
+    assert np.array_equal(r[:448], v[:448])                                  # only the last 64 channels
+    n = lambda a: np.hypot(a[448::2], a[449::2])
+    assert np.allclose(n(r), n(v), rtol=1e-14)                               # pairs keep their norms
+    assert np.allclose(oracle.rope_rotate(r, -12345.0, 10000.0), v, atol=1e-12)
+    assert np.allclose(r, _rope_np(v, 12345.0, 10000.0), atol=1e-12)
+
+
+def test_attend_inverse_rope_gives_relative_positions(oracle_lib):
+    # every attention row is a value rotated at its own position p_j and the query is rotated
+    # at i: scores depend on i - p_j only, and the output rotated at -i is a sum of values
+    # rotated by p_j - i.  Shifting every position by the same amount changes nothing.
+    import oracle
+    rng = np.random.default_rng(9)
+    n, W = 6, 4
+    base_rows = rng.standard_normal((n + W, 512)) * 0.5
+    q_base = rng.standard_normal((64, 512)) * 0.3
+    pos_main = rng.integers(0, 50, n)
+    pos_win = np.arange(60, 60 + W)
+    outs = []
+    for shift in (0, 1000):
+        i = 70 + shift
+        rows = np.stack([_rope_np(base_rows[j], (pos_main[j] if j < n else pos_win[j - n]) + shift, 10000.0)
+                         for j in range(n + W)])
+        # every row goes through the bf16 window path (n + W window rows, no selected rows):
+        # FP4 codes could not hold rotated values
+        q = _rope_np(q_base, i, 10000.0)
+        to_b = lambda a: (np.asarray(a, np.float32).view(np.uint32) + 0x8000 >> 16).astype(np.uint16)
+        swa = to_b(rows)[None]
+        qb = to_b(q)[None]
+        idx = np.full((1, 512), -1, np.int32)
+        kvc = np.zeros((1, 1, 256), np.uint8)
+        kvs = np.full((1, 1, 16), 127, np.uint8)
+        out, _ = oracle.attend_ex(qb, kvc, kvs, idx, np.array([n + W], np.int32), None, 0.05, 1, n + W, swa=swa,
+                                  rope_pos=np.array([i], np.int32), rope_base=10000.0)
+        outs.append(out)
+    # bf16 rounding of the rotated inputs differs between the two shifts: compare loosely
+    assert np.allclose(outs[0], outs[1], atol=2e-2, rtol=2e-2)
+    # and without the inverse rotation the last 64 channels do depend on the shift
+    assert not np.allclose(_rope_np(outs[0], 70, 10000.0)[..., 448:], _rope_np(outs[1], 1070, 10000.0)[..., 448:],
+                           atol=2e-2)
+
+
+def test_attend_ex_formats_reduce_to_known_cases(oracle_lib):
+    # E4M3 scales of exactly 1.0 give the MXFP4 rows with scale 2^0; FP8 window rows whose values
+    # are exact with scale 2^0 give the bf16 window path
+    import oracle
+    rng = np.random.default_rng(11)
+    T, B, N, S = 2, 1, 40, 8
+    q = (rng.uniform(-1, 1, (T, 64, 512)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    codes = rng.integers(0, 256, (B, N, 256)).astype(np.uint8)
+    idx = np.stack([rng.permutation(N)[:12] for _ in range(T)]).astype(np.int32)
+    idx = np.concatenate([idx, np.full((T, 500), -1, np.int32)], axis=1)
+    swa_end = np.array([8, 5], np.int32)
+    fp8 = rng.integers(0, 0x7F, (B, S, 448)).astype(np.uint8)             # finite E4M3 codes
+    rope = (rng.uniform(-2, 2, (B, S, 64)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    swa_vals = np.concatenate([np.vectorize(oracle.e4m3)(fp8), np.zeros((B, S, 64))], axis=2)
+    swa_bf = (swa_vals.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    swa_bf[..., 448:] = rope
+    a, la = oracle.attend_ex(q, codes, np.full((B, N, 16), 127, np.uint8), idx, swa_end, None, 0.04, 2, 8,
+                             kv_format=0, swa=swa_bf)
+    b, lb = oracle.attend_ex(q, codes, np.full((B, N, 32), 0x38, np.uint8), idx, swa_end, None, 0.04, 2, 8,
+                             kv_format=1, swa_fp8=fp8, swa_rope=rope, swa_scales=np.full((B, S, 8), 127, np.uint8))
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
