@@ -20,12 +20,14 @@ __all__ = [
     "attend_workspace_bytes", "IDX_HEADS", "IDX_DIM", "HEADS", "DIM", "TOPK", "MAX_WINDOW", "MAX_LAYERS", "TILE",
     "TOPK_ROW_MAX", "STATS_WORDS", "csa2_hsi_pool", "csa2_reindex", "hsi_pool_workspace_bytes",
     "reindex_workspace_bytes", "HSI_BLOCK", "HSI_BLOCKS", "HSI_POOL", "csa2_index_mxfp4", "csa2_topk_mxfp4",
-    "csa2_hsi_pool_mxfp4", "csa2_reindex_mxfp4", "index_mxfp4_stats_bytes",
+    "csa2_hsi_pool_mxfp4", "csa2_reindex_mxfp4", "index_mxfp4_stats_bytes", "csa2_attend_ex", "KV_MXFP4",
+    "KV_E4M3_16", "SWA_BF16", "SWA_FP8",
 ]
 
 IDX_HEADS, IDX_DIM, HEADS, DIM, TOPK, MAX_WINDOW, MAX_LAYERS = 32, 128, 64, 512, 512, 128, 8
 TILE, TOPK_ROW_MAX, STATS_WORDS = 16, 36864, 4
 HSI_BLOCK, HSI_BLOCKS = 8, 2048
+KV_MXFP4, KV_E4M3_16, SWA_BF16, SWA_FP8 = 0, 1, 0, 1
 HSI_POOL = HSI_BLOCK * HSI_BLOCKS
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +35,12 @@ library_path = os.path.join(_HERE, "libcsa2.so")
 _lib = None
 
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+class _AttendOpts(ctypes.Structure):
+    _fields_ = [("kv_format", ctypes.c_int32), ("swa_format", ctypes.c_int32), ("swa_fp8", ctypes.c_void_p),
+                ("swa_rope", ctypes.c_void_p), ("swa_scales", ctypes.c_void_p), ("rope_pos", ctypes.c_void_p),
+                ("rope_base", ctypes.c_float)]
+
 
 _SIGNATURES = {
     "csa2_status_string": ([_i32], ctypes.c_char_p),
@@ -55,6 +63,8 @@ _SIGNATURES = {
     "csa2_hsi_pool_mxfp4": ([_vp, _vp, _sz, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _sz, _vp], _i32),
     "csa2_reindex_mxfp4": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _vp, _vp, _sz, _vp], _i32),
     "csa2_attend_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
+    "csa2_attend_ex": ([_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i64, _i32, _i32, _i32,
+                        ctypes.POINTER(_AttendOpts), _vp, _vp, _vp, _sz, _vp], _i32),
     "csa2_attend_fp4": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp,
                          _vp, _sz, _vp], _i32),
     "csa2_reuse_attend": ([_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i64, _i32, _i32, _i32, _vp,
@@ -485,3 +495,55 @@ def csa2_reuse_attend(q, kv_fp4, kv_scale, indices, swa, swa_end, sink=None, sof
                                  _p(workspace), _nbytes(workspace), _stream(q))
     _raise(st, "csa2_reuse_attend")
     return (out, lse) if (want_lse or lse is not None) else out
+
+
+def csa2_attend_ex(q, kv_codes, kv_scales, indices, swa_end, sink=None, softmax_scale=DIM ** -0.5, q_per_seq=1,
+                   window=MAX_WINDOW, kv_format=KV_MXFP4, swa=None, swa_fp8=None, swa_rope=None, swa_scales=None,
+                   rope_pos=None, rope_base=10000.0, out=None, lse=None, workspace=None, want_lse=False):
+    """Joint sparse + window attention with the deployed formats: q bf16 [T][64][512] (one layer)
+    or [L][T][64][512] (L layers over the same selection); kv_codes uint8 [B][N][256] with
+    kv_scales E8M0 [B][N][16] (KV_MXFP4) or E4M3 [B][N][32] (KV_E4M3_16); the window as bf16
+    swa [(L)][B][S][512] or FP8 (swa_fp8 uint8 [(L)][B][S][448], swa_rope bf16 [(L)][B][S][64],
+    swa_scales E8M0 uint8 [(L)][B][S][8]); rope_pos int32 [T] rotates the output's last 64
+    channels at -rope_pos[t].  Returns out (same shape as q) or (out, lse)."""
+    layered = q.dim() == 4
+    L = q.shape[0] if layered else 1
+    T = q.shape[1] if layered else q.shape[0]
+    B, N = kv_codes.shape[0], kv_codes.shape[1]
+    dev = q.device
+    lay = (L,) if layered else ()
+    _check(q, "q", lay + (T, HEADS, DIM), elem_size=2)
+    _check(kv_codes, "kv_codes", (B, N, DIM // 2), dtype=torch.uint8, device=dev)
+    _check(kv_scales, "kv_scales", (B, N, DIM // (32 if kv_format == KV_MXFP4 else 16)), dtype=torch.uint8, device=dev)
+    _check(indices, "indices", (T, TOPK), dtype=torch.int32, device=dev)
+    _check(swa_end, "swa_end", (T,), dtype=torch.int32, device=dev)
+    if swa is not None:
+        S = swa.shape[-2]
+        _check(swa, "swa", lay + (B, S, DIM), elem_size=2, device=dev)
+        fmt = SWA_BF16
+    else:
+        S = swa_fp8.shape[-2]
+        _check(swa_fp8, "swa_fp8", lay + (B, S, 448), dtype=torch.uint8, device=dev)
+        _check(swa_rope, "swa_rope", lay + (B, S, 64), elem_size=2, device=dev)
+        _check(swa_scales, "swa_scales", lay + (B, S, 8), dtype=torch.uint8, device=dev)
+        fmt = SWA_FP8
+    if sink is not None:
+        _check(sink, "sink", lay + (HEADS,), dtype=torch.float32, device=dev)
+    if rope_pos is not None:
+        _check(rope_pos, "rope_pos", (T,), dtype=torch.int32, device=dev)
+    if B * q_per_seq != T:
+        raise ValueError(f"T={T} must equal B*q_per_seq={B}*{q_per_seq}")
+    if out is None:
+        out = torch.empty(lay + (T, HEADS, DIM), dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(lay + (T, HEADS), dtype=torch.float32, device=dev)
+    workspace = _ws(attend_workspace_bytes(T, TOPK, window, L), dev, workspace)
+    opts = _AttendOpts(kv_format, fmt, None if swa_fp8 is None else swa_fp8.data_ptr(),
+                       None if swa_rope is None else swa_rope.data_ptr(),
+                       None if swa_scales is None else swa_scales.data_ptr(),
+                       None if rope_pos is None else rope_pos.data_ptr(), float(rope_base))
+    st = lib().csa2_attend_ex(L, _p(q), _p(kv_codes), _p(kv_scales), _p(indices), _p(swa), _p(swa_end), _p(sink),
+                              float(softmax_scale), T, q_per_seq, N, S, window, TOPK, ctypes.byref(opts), _p(out),
+                              _p(lse), _p(workspace), _nbytes(workspace), _stream(q))
+    _raise(st, "csa2_attend_ex")
+    return (out, lse) if want_lse else out

@@ -37,9 +37,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 struct AttnArgs {
   const uint16_t* q;        // [L][T][64][512]
   const uint8_t* kv_fp4;    // [B][N][256]
-  const uint8_t* kv_scale;  // [B][N][16]
+  const uint8_t* kv_scale;  // [B][N][16] E8M0 (kv_format 0) or [B][N][32] E4M3 (kv_format 1)
   const int32_t* indices;   // [T][k]
-  const uint16_t* swa;      // [L][B][S][512]
+  const uint16_t* swa;      // [L][B][S][512] (swa_format 0)
+  const uint8_t* swa_fp8;   // [L][B][S][448] E4M3 (swa_format 1)
+  const uint16_t* swa_rope; // [L][B][S][64] bf16, channels 448..511 (swa_format 1)
+  const uint8_t* swa_sc;    // [L][B][S][8] E8M0 per 64 channels (swa_format 1)
+  const int32_t* rope_pos;  // [T] or null: the output's last 64 channels rotated at -rope_pos[t]
+  double rope_log2_base;
   const int32_t* swa_end;   // [T]
   const float* sink;        // [L][64] or null
   float scale_log2;         // softmax_scale * log2(e)
@@ -59,6 +64,7 @@ struct AttnShared {
   alignas(16) uint16_t X[kChunk * kXStride];
   alignas(16) uint16_t XT[kDim * kXTStride];
   int valid[kChunk];
+  float rope[32][2];  // (cos, sin) of the output rotation of pair j (final outputs written here)
 };
 
 // Wave index over the 64 heads (16 heads per wave): a block of W waves takes
@@ -69,6 +75,58 @@ __device__ __forceinline__ int head_wave() { return (int)(blockIdx.z * (blockDim
 // 16-byte LDS operand read (the offsets used are multiples of 16 bytes).
 __device__ __forceinline__ bf16x8 lds_read16(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(__builtin_assume_aligned(p, 16));
+}
+
+// OCP E4M3 byte -> fp32 (bias 7, exponent field 0 subnormal; S.1111.111, NaN,
+// is not a valid scale and decodes to 480 here).
+__device__ __forceinline__ float e4m3_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float mag = e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (b & 0x80u) ? -mag : mag;
+}
+
+// 8 E2M1 codes times an E4M3 scale -> 8 bf16.  The conversion instruction
+// applies only the exponent of its scale, so the codes are converted at scale 1
+// and multiplied in fp32: an E2M1 value times an E4M3 value has at most 6
+// significant bits, exact in fp32 and in bf16, so dropping the low half is exact.
+__device__ __forceinline__ uint4 dequant8_e4m3(uint32_t codes, uint32_t sbyte) {
+  const float sc = e4m3_f32(sbyte);
+  const uint4 u = dequant8(codes, 127u);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  uint32_t r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = (__float_as_uint(bf16lo(w[i]) * sc) >> 16) | (__float_as_uint(bf16hi(w[i]) * sc) & 0xFFFF0000u);
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+// Channels 8d .. 8d + 7 of window row `row` (flat [L][B][S] index) as bf16:
+// a bf16 row, or an FP8 row (E4M3 with an E8M0 scale per 64 channels below
+// channel 448, bf16 above; the scale is a power of two, so the conversion
+// instruction's scaling is exact).
+template <int SWF>
+__device__ __forceinline__ uint4 window_piece(const AttnArgs& a, size_t row, int d) {
+  if (SWF == CSA2_SWA_BF16) return *reinterpret_cast<const uint4*>(a.swa + row * kDim + 8 * d);
+  if (d >= 56) return *reinterpret_cast<const uint4*>(a.swa_rope + row * 64 + 8 * (d - 56));
+  const uint2 c = *reinterpret_cast<const uint2*>(a.swa_fp8 + row * 448 + 8 * d);
+  const float sc = e8m0_f32(a.swa_sc[row * 8 + (d >> 3)]);
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, sc, true));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, false));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, sc, true));
+  return r;
+}
+
+// cos and sin of the inverse-RoPE angle -pos * base^(-2j/64) of pair j: the
+// angle in revolutions is formed in fp64 (positions up to 2^31 times
+// frequencies up to 1) and reduced to [-1/2, 1/2] there, then v_sin_f32 /
+// v_cos_f32, which take revolutions, give the fp32 values.
+__device__ __forceinline__ void rope_cs(const AttnArgs& a, int t, int j, float* c, float* s) {
+  const double rev = -(double)a.rope_pos[t] * exp2(-a.rope_log2_base * (j / 32.0)) * 0.15915494309189535;
+  const float fr = (float)(rev - rint(rev));
+  *c = __builtin_amdgcn_cosf(fr);
+  *s = __builtin_amdgcn_sinf(fr);
 }
 
 // XT rows hold 32 bf16 in four 16-byte blocks; block b of row r is stored at
@@ -106,6 +164,7 @@ __device__ __forceinline__ void write_group(AttnShared& sh, int g, int d, const 
 
 // Row group g of a selected-row chunk from its codes and scale bytes (rows of
 // -1 slots were read from row 0 and are zeroed here).
+template <int KVF>
 __device__ __forceinline__ void dequant_group(AttnShared& sh, int g, int d, const int32_t* idx, const uint32_t* codes,
                                               const uint32_t* sbyte) {
   uint32_t v[8][4];
@@ -113,7 +172,7 @@ __device__ __forceinline__ void dequant_group(AttnShared& sh, int g, int d, cons
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     okr[r] = idx[r] >= 0;
-    const uint4 o = dequant8(codes[r], sbyte[r]);
+    const uint4 o = KVF == CSA2_KV_MXFP4 ? dequant8(codes[r], sbyte[r]) : dequant8_e4m3(codes[r], sbyte[r]);
     v[r][0] = okr[r] ? o.x : 0u; v[r][1] = okr[r] ? o.y : 0u;
     v[r][2] = okr[r] ? o.z : 0u; v[r][3] = okr[r] ? o.w : 0u;
   }
@@ -123,7 +182,7 @@ __device__ __forceinline__ void dequant_group(AttnShared& sh, int g, int d, cons
 // NG row groups g0, g0 + 1, ... staged by one wave, every load of a kind in
 // flight together: the indices, then the codes and scales (selected rows), or
 // the window rows.
-template <int NG>
+template <int NG, int KVF, int SWF>
 __device__ __forceinline__ void stage_groups(const AttnArgs& a, AttnShared& sh, int t, int b, int c, int layer,
                                              int g0) {
   const int d = threadIdx.x & 63;
@@ -140,10 +199,10 @@ __device__ __forceinline__ void stage_groups(const AttnArgs& a, AttnShared& sh, 
       for (int r = 0; r < 8; ++r) {
         const size_t rowid = (size_t)b * a.N + (idx[j][r] >= 0 ? idx[j][r] : 0);
         codes[j][r] = *reinterpret_cast<const uint32_t*>(a.kv_fp4 + rowid * 256 + 4 * d);
-        sbyte[j][r] = a.kv_scale[rowid * 16 + (d >> 2)];
+        sbyte[j][r] = KVF == CSA2_KV_MXFP4 ? a.kv_scale[rowid * 16 + (d >> 2)] : a.kv_scale[rowid * 32 + (d >> 1)];
       }
 #pragma unroll
-    for (int j = 0; j < NG; ++j) dequant_group(sh, g0 + j, d, idx[j], codes[j], sbyte[j]);
+    for (int j = 0; j < NG; ++j) dequant_group<KVF>(sh, g0 + j, d, idx[j], codes[j], sbyte[j]);
   } else {
     const int we = a.swa_end[t];
     const int ws = we - a.window > 0 ? we - a.window : 0;
@@ -160,7 +219,7 @@ __device__ __forceinline__ void stage_groups(const AttnArgs& a, AttnShared& sh, 
           const int row = ws + (c - a.n_main) * kChunk + group_row(g0 + j0 + j, r);
           okr[j][r] = row < we;
           const int rr = okr[j][r] ? row : (we > 0 ? we - 1 : 0);
-          const uint4 x = *reinterpret_cast<const uint4*>(a.swa + (((size_t)layer * a.B + b) * a.S + rr) * kDim + 8 * d);
+          const uint4 x = window_piece<SWF>(a, ((size_t)layer * a.B + b) * a.S + rr, d);
           v[j][r][0] = okr[j][r] ? x.x : 0u; v[j][r][1] = okr[j][r] ? x.y : 0u;
           v[j][r][2] = okr[j][r] ? x.z : 0u; v[j][r][3] = okr[j][r] ? x.w : 0u;
         }
@@ -174,9 +233,10 @@ __device__ __forceinline__ void stage_groups(const AttnArgs& a, AttnShared& sh, 
 
 // Stage chunk `c` into LDS: wave g of a 4-wave block takes row group g, a
 // one-wave block all four.
+template <int KVF, int SWF>
 __device__ void stage_chunk(const AttnArgs& a, AttnShared& sh, int t, int b, int c, int layer) {
-  if (blockDim.x == 64) stage_groups<4>(a, sh, t, b, c, layer, 0);
-  else stage_groups<1>(a, sh, t, b, c, layer, threadIdx.x >> 6);
+  if (blockDim.x == 64) stage_groups<4, KVF, SWF>(a, sh, t, b, c, layer, 0);
+  else stage_groups<1, KVF, SWF>(a, sh, t, b, c, layer, threadIdx.x >> 6);
 }
 
 struct HeadState {
@@ -253,8 +313,9 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const AttnShared
   }
 }
 
-// Write the final output of one (layer, query) from a complete state.
-__device__ void write_final(const AttnArgs& a, const HeadState& st, int layer, int t) {
+// Write the final output of one (layer, query) from a complete state (the
+// rotation's (cos, sin) pairs already in sh.rope when a.rope_pos is given).
+__device__ void write_final(const AttnArgs& a, const AttnShared& sh, const HeadState& st, int layer, int t) {
   const int lane = threadIdx.x & 63;
   const int head = 16 * head_wave() + (lane & 15), g = lane >> 4;
   float l = st.l;
@@ -275,8 +336,19 @@ __device__ void write_final(const AttnArgs& a, const HeadState& st, int layer, i
   uint16_t* op = a.out + (((size_t)layer * a.T + t) * kHeads + head) * kDim + 4 * g;
 #pragma unroll
   for (int mb = 0; mb < 32; ++mb) {
-    const uint32_t w0 = f32_to_bf16_rne(st.o[mb][0] * inv) | (f32_to_bf16_rne(st.o[mb][1] * inv) << 16);
-    const uint32_t w1 = f32_to_bf16_rne(st.o[mb][2] * inv) | (f32_to_bf16_rne(st.o[mb][3] * inv) << 16);
+    float v[4] = {st.o[mb][0] * inv, st.o[mb][1] * inv, st.o[mb][2] * inv, st.o[mb][3] * inv};
+    if (mb >= 28 && a.rope_pos) {  // channels 448..511: pairs (v0, v1), (v2, v3)
+      const int j0 = 8 * (mb - 28) + 2 * g;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const float c = sh.rope[j0 + p][0], sn = sh.rope[j0 + p][1];
+        const float x = v[2 * p], y = v[2 * p + 1];
+        v[2 * p] = x * c - y * sn;
+        v[2 * p + 1] = x * sn + y * c;
+      }
+    }
+    const uint32_t w0 = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+    const uint32_t w1 = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
     *reinterpret_cast<uint2*>(op + 16 * mb) = make_uint2(w0, w1);
   }
   if (a.lse && g == 0)
@@ -312,7 +384,7 @@ __device__ void write_partial(const AttnArgs& a, const HeadState& st, int layer,
 //   L  > 1: i < n_main: selected-row chunk i for every layer (slot i);
 //           otherwise window chunk j of layer l, i = n_main + l*n_swa + j
 //           (slot n_main + j of layer l).
-template <int W>
+template <int W, int KVF, int SWF>
 __global__ __launch_bounds__(64 * W) void attend_kernel(AttnArgs a) {
   __shared__ AttnShared sh;
   const int item = blockIdx.x, t = blockIdx.y;
@@ -323,18 +395,24 @@ __global__ __launch_bounds__(64 * W) void attend_kernel(AttnArgs a) {
     const int n_chunks = a.n_main + a.n_swa;
     const int c0 = item * a.cpw;
     const int c1 = c0 + a.cpw < n_chunks ? c0 + a.cpw : n_chunks;
+    if (a.n_items == 1 && a.rope_pos && threadIdx.x < 32) {
+      float c, sn;
+      rope_cs(a, t, threadIdx.x, &c, &sn);
+      sh.rope[threadIdx.x][0] = c;
+      sh.rope[threadIdx.x][1] = sn;
+    }
     load_q(a, 0, t, qb);
     state_init(st);
     for (int c = c0; c < c1; ++c) {
-      stage_chunk(a, sh, t, b, c, 0);
+      stage_chunk<KVF, SWF>(a, sh, t, b, c, 0);
       __syncthreads();
       attend_chunk(a, sh, qb, st);
       __syncthreads();
     }
-    if (a.n_items == 1) write_final(a, st, 0, t);
+    if (a.n_items == 1) write_final(a, sh, st, 0, t);
     else write_partial(a, st, 0, t, item);
   } else if (item < a.n_main) {
-    stage_chunk(a, sh, t, b, item, 0);
+    stage_chunk<KVF, SWF>(a, sh, t, b, item, 0);
     __syncthreads();
     for (int l = 0; l < a.L; ++l) {
       load_q(a, l, t, qb);
@@ -347,7 +425,7 @@ __global__ __launch_bounds__(64 * W) void attend_kernel(AttnArgs a) {
     const int l = rest / a.n_swa, j = rest % a.n_swa;
     load_q(a, l, t, qb);
     state_init(st);
-    stage_chunk(a, sh, t, b, a.n_main + j, l);
+    stage_chunk<KVF, SWF>(a, sh, t, b, a.n_main + j, l);
     __syncthreads();
     attend_chunk(a, sh, qb, st);
     write_partial(a, st, l, t, a.n_main + j);
@@ -398,8 +476,19 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a) {
     }
   const float iv = s_inv;
   uint16_t* op = a.out + (((size_t)layer * a.T + t) * kHeads + h) * kDim + 4 * tid;
-  const uint32_t w0 = f32_to_bf16_rne(acc[0] * iv) | (f32_to_bf16_rne(acc[1] * iv) << 16);
-  const uint32_t w1 = f32_to_bf16_rne(acc[2] * iv) | (f32_to_bf16_rne(acc[3] * iv) << 16);
+  float v[4] = {acc[0] * iv, acc[1] * iv, acc[2] * iv, acc[3] * iv};
+  if (tid >= 112 && a.rope_pos) {  // channels 448..511: pairs (v0, v1), (v2, v3)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      float c, sn;
+      rope_cs(a, t, 2 * (tid - 112) + p, &c, &sn);
+      const float x = v[2 * p], y = v[2 * p + 1];
+      v[2 * p] = x * c - y * sn;
+      v[2 * p + 1] = x * sn + y * c;
+    }
+  }
+  const uint32_t w0 = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+  const uint32_t w1 = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
   *reinterpret_cast<uint2*>(op) = make_uint2(w0, w1);
 }
 
@@ -437,12 +526,21 @@ static size_t attend_ws_bytes(int32_t T, const AttendPlan& p, int32_t L) {
 static csa2_status attend_launch(int32_t L, const void* q, const uint8_t* kv_fp4, const uint8_t* kv_scale,
                                  const int32_t* indices, const void* swa, const int32_t* swa_end,
                                  const float* sink, float softmax_scale, int32_t T, int32_t q_per_seq,
-                                 int64_t N, int32_t S, int32_t window, int32_t k, void* out, float* lse,
-                                 void* workspace, size_t workspace_bytes, void* hip_stream) {
-  if (!q || !kv_fp4 || !kv_scale || !indices || !swa || !swa_end || !out) return CSA2_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(kv_fp4) || !aligned16(kv_scale) || !aligned16(indices) || !aligned16(swa) ||
-      !aligned16(swa_end) || !aligned16(out) || (sink && !aligned16(sink)) || (lse && !aligned16(lse)))
+                                 int64_t N, int32_t S, int32_t window, int32_t k, const csa2_attend_opts* opts,
+                                 void* out, float* lse, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  const csa2_attend_opts o = opts ? *opts : csa2_attend_opts{};
+  if (o.kv_format != CSA2_KV_MXFP4 && o.kv_format != CSA2_KV_E4M3_16) return CSA2_ERR_UNSUPPORTED;
+  if (o.swa_format != CSA2_SWA_BF16 && o.swa_format != CSA2_SWA_FP8) return CSA2_ERR_UNSUPPORTED;
+  const bool fp8w = o.swa_format == CSA2_SWA_FP8;
+  if (!q || !kv_fp4 || !kv_scale || !indices || !swa_end || !out) return CSA2_ERR_INVALID_ARG;
+  if (fp8w ? (!o.swa_fp8 || !o.swa_rope || !o.swa_scales) : !swa) return CSA2_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kv_fp4) || !aligned16(kv_scale) || !aligned16(indices) ||
+      (!fp8w && !aligned16(swa)) ||
+      (fp8w && (!aligned16(o.swa_fp8) || !aligned16(o.swa_rope) || !aligned16(o.swa_scales))) ||
+      !aligned16(swa_end) || !aligned16(out) || (sink && !aligned16(sink)) || (lse && !aligned16(lse)) ||
+      (o.rope_pos && !aligned16(o.rope_pos)))
     return CSA2_ERR_INVALID_ARG;
+  if (o.rope_pos && !(o.rope_base > 1.f && o.rope_base < INFINITY)) return CSA2_ERR_INVALID_ARG;
   if (T < 1 || q_per_seq < 1 || T % q_per_seq != 0 || N < 1 || S < 1) return CSA2_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || !(softmax_scale < INFINITY)) return CSA2_ERR_INVALID_ARG;
   if (k != kTopK || window < 1 || window > CSA2_MAX_WINDOW || L < 1 || L > CSA2_MAX_LAYERS || T > 65535 ||
@@ -456,7 +554,12 @@ static csa2_status attend_launch(int32_t L, const void* q, const uint8_t* kv_fp4
   a.kv_fp4 = kv_fp4;
   a.kv_scale = kv_scale;
   a.indices = indices;
-  a.swa = (const uint16_t*)swa;
+  a.swa = fp8w ? nullptr : (const uint16_t*)swa;
+  a.swa_fp8 = fp8w ? o.swa_fp8 : nullptr;
+  a.swa_rope = fp8w ? (const uint16_t*)o.swa_rope : nullptr;
+  a.swa_sc = fp8w ? o.swa_scales : nullptr;
+  a.rope_pos = o.rope_pos;
+  a.rope_log2_base = o.rope_pos ? log2((double)o.rope_base) : 0.0;
   a.swa_end = swa_end;
   a.sink = sink;
   a.scale_log2 = softmax_scale * kLog2e;
@@ -482,10 +585,22 @@ static csa2_status attend_launch(int32_t L, const void* q, const uint8_t* kv_fp4
   (void)hipGetLastError();
   // small batches: one wave per block and four blocks per work item (16 heads
   // each), so that the work and the partial writes spread over four times the CUs
-  if ((int64_t)p.n_items * T * 4 <= 4096)
-    hipLaunchKernelGGL(attend_kernel<1>, dim3(p.n_items, T, 4), dim3(64), 0, st, a);
-  else
-    hipLaunchKernelGGL(attend_kernel<4>, dim3(p.n_items, T, 1), dim3(kAttnThreads), 0, st, a);
+  const bool one = (int64_t)p.n_items * T * 4 <= 4096;
+  const dim3 grid(p.n_items, T, one ? 4 : 1), block(one ? 64 : kAttnThreads);
+  const int fmt = 2 * o.kv_format + o.swa_format;
+#define CSA2_ATTEND(W, KVF, SWF) hipLaunchKernelGGL((attend_kernel<W, KVF, SWF>), grid, block, 0, st, a)
+  if (one) {
+    if (fmt == 0) CSA2_ATTEND(1, 0, 0);
+    else if (fmt == 1) CSA2_ATTEND(1, 0, 1);
+    else if (fmt == 2) CSA2_ATTEND(1, 1, 0);
+    else CSA2_ATTEND(1, 1, 1);
+  } else {
+    if (fmt == 0) CSA2_ATTEND(4, 0, 0);
+    else if (fmt == 1) CSA2_ATTEND(4, 0, 1);
+    else if (fmt == 2) CSA2_ATTEND(4, 1, 0);
+    else CSA2_ATTEND(4, 1, 1);
+  }
+#undef CSA2_ATTEND
   if (need) hipLaunchKernelGGL(attend_combine_kernel, dim3(kHeads, T, L), dim3(128), 0, st, a);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   return CSA2_OK;
@@ -508,7 +623,7 @@ extern "C" csa2_status csa2_attend_fp4(const void* q, const uint8_t* kv_fp4, con
                                        int64_t N, int32_t S, int32_t window, int32_t k, void* out, float* lse,
                                        void* workspace, size_t workspace_bytes, void* hip_stream) {
   return attend_launch(1, q, kv_fp4, kv_scale, indices, swa, swa_end, sink, softmax_scale, T, q_per_seq, N, S,
-                       window, k, out, lse, workspace, workspace_bytes, hip_stream);
+                       window, k, nullptr, out, lse, workspace, workspace_bytes, hip_stream);
 }
 
 extern "C" csa2_status csa2_reuse_attend(int32_t n_layers, const void* q, const uint8_t* kv_fp4,
@@ -519,5 +634,15 @@ extern "C" csa2_status csa2_reuse_attend(int32_t n_layers, const void* q, const 
                                          void* hip_stream) {
   if (n_layers < 1 || n_layers > CSA2_MAX_LAYERS) return CSA2_ERR_UNSUPPORTED;
   return attend_launch(n_layers, q, kv_fp4, kv_scale, indices, swa, swa_end, sink, softmax_scale, T, q_per_seq, N,
-                       S, window, k, out, lse, workspace, workspace_bytes, hip_stream);
+                       S, window, k, nullptr, out, lse, workspace, workspace_bytes, hip_stream);
+}
+
+extern "C" csa2_status csa2_attend_ex(int32_t n_layers, const void* q, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                                      const int32_t* indices, const void* swa, const int32_t* swa_end,
+                                      const float* sink, float softmax_scale, int32_t T, int32_t q_per_seq, int64_t N,
+                                      int32_t S, int32_t window, int32_t k, const csa2_attend_opts* opts, void* out,
+                                      float* lse, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (n_layers < 1 || n_layers > CSA2_MAX_LAYERS) return CSA2_ERR_UNSUPPORTED;
+  return attend_launch(n_layers, q, kv_codes, kv_scales, indices, swa, swa_end, sink, softmax_scale, T, q_per_seq,
+                       N, S, window, k, opts, out, lse, workspace, workspace_bytes, hip_stream);
 }

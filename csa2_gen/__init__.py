@@ -225,6 +225,94 @@ def make_case(name, B, N, q_per_seq=1, ratio=1, prefix=None, window=128, k=512, 
     return c
 
 
+def e4m3_encode(v: torch.Tensor) -> torch.Tensor:
+    """Nearest OCP E4M3 code of float64 values (ties to the even code), saturating at 448."""
+    a = v.abs().clamp(max=448.0)
+    sign = (v < 0).to(torch.int32) << 7
+    _, ex = torch.frexp(a)                         # a = f * 2^ex, f in [0.5, 1)
+    e = (ex - 1).clamp(min=-6)                     # unbiased exponent, subnormals share 2^-6
+    step = torch.ldexp(torch.ones_like(a), (e - 3).to(torch.int32))   # spacing of codes at that exponent
+    q = a / step                                   # exact: step is a power of two
+    r = torch.floor(q)
+    frac = q - r
+    r = r + ((frac > 0.5) | ((frac == 0.5) & (r.remainder(2) == 1))).to(r.dtype)
+    # r counts steps: subnormal codes are r (0..8), normal codes (e + 7) * 8 + (r - 8)
+    normal = e > -6
+    code = torch.where(normal, (e + 7) * 8 + (r.to(torch.int32) - 8), r.to(torch.int32))
+    code = torch.where(a == 0, torch.zeros_like(code), code).clamp(max=0x7E)
+    return (code | sign).to(torch.uint8)
+
+
+def e4m3_decode(code: torch.Tensor) -> torch.Tensor:
+    c = code.to(torch.int32)
+    e, m = (c >> 3) & 15, c & 7
+    mag = torch.where(e == 0, m.to(torch.float64) * 2.0 ** -9,
+                      torch.ldexp(8.0 + m.to(torch.float64), (e - 10).to(torch.int32)))
+    return torch.where((c & 0x80) != 0, -mag, mag)
+
+
+def _e2m1_codes(scaled: torch.Tensor) -> torch.Tensor:
+    """RNE to E2M1 (ties to the even code), saturating at 6; scaled float64 -> int32 codes."""
+    a = scaled.abs()
+    mag = ((a > 0.25).to(torch.int32) + (a >= 0.75).to(torch.int32) + (a > 1.25).to(torch.int32)
+           + (a >= 1.75).to(torch.int32) + (a > 2.5).to(torch.int32) + (a >= 3.5).to(torch.int32)
+           + (a > 5.0).to(torch.int32))
+    return mag | ((scaled < 0).to(torch.int32) << 3)
+
+
+def e4m3_16_quantize(x_bits: torch.Tensor):
+    """bf16 bits int16 [R][D] -> (E2M1 codes uint8 [R][D/2], E4M3 scales uint8 [R][D/16]).
+    Per block of 16: scale = E4M3 nearest to amax / 6, elements x / scale rounded to E2M1."""
+    R, D = x_bits.shape
+    x = bf16_bits_to_float(x_bits).to(torch.float64).view(R, D // 16, 16)
+    amax = x.abs().amax(dim=2)
+    sc_code = e4m3_encode(amax / 6.0)
+    sc = e4m3_decode(sc_code)
+    scaled = torch.where(sc[:, :, None] > 0, x / torch.where(sc > 0, sc, 1.0)[:, :, None], torch.zeros_like(x))
+    code = _e2m1_codes(scaled).view(R, D // 2, 2)
+    packed = (code[:, :, 0] | (code[:, :, 1] << 4)).to(torch.uint8)
+    return packed, sc_code.view(R, D // 16)
+
+
+def fp8_window_quantize(x_bits: torch.Tensor):
+    """bf16 bits int16 [R][512] -> (E4M3 uint8 [R][448], bf16 bits int16 [R][64], E8M0 uint8 [R][8]).
+    Channels 0..447 in blocks of 64: shared exponent floor(log2 amax) - 8 (the E4M3 maximum
+    exponent), elements rounded to E4M3 (saturating at 448); channels 448..511 kept as bf16."""
+    R = x_bits.shape[0]
+    x = bf16_bits_to_float(x_bits[:, :448]).to(torch.float64).view(R, 7, 64)
+    amax = x.abs().amax(dim=2)
+    _, ex = torch.frexp(amax)
+    shared = torch.where(amax > 0, ex - 1 - 8, torch.zeros_like(ex))
+    scale_code = (shared + 127).clamp(0, 254)
+    pow2 = ((1023 - (scale_code.to(torch.int64) - 127)) << 52).view(torch.float64)
+    fp8 = e4m3_encode(x * pow2[:, :, None]).view(R, 448)
+    scales = torch.zeros((R, 8), dtype=torch.uint8, device=x_bits.device)
+    scales[:, :7] = scale_code.to(torch.uint8)
+    return fp8, x_bits[:, 448:].contiguous(), scales
+
+
+def kv_e4m3_16(c: "Case", chunk_rows: int = 1 << 16):
+    """The case's main KV (the same seeded bf16 rows its MXFP4 cache quantises) in the E2M1 +
+    E4M3/16 format -> (codes uint8 [B][N][256], scales uint8 [B][N][32])."""
+    rows = c.B * c.N
+    dev = c.kv_codes.device
+    codes = torch.empty((rows, DIM // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, DIM // 16), dtype=torch.uint8, device=dev)
+    for r0 in range(0, rows, chunk_rows):
+        n = min(chunk_rows, rows - r0)
+        x = normal_bf16(c.seed, ST_KV, r0 * DIM, n * DIM, dev).view(n, DIM)
+        codes[r0:r0 + n], scales[r0:r0 + n] = e4m3_16_quantize(x)
+    return codes.view(c.B, c.N, DIM // 2), scales.view(c.B, c.N, DIM // 16)
+
+
+def window_fp8(c: "Case"):
+    """The case's window rows (every layer) in the FP8 layout -> (fp8 [L][B][S][448],
+    rope bf16 bits [L][B][S][64], scales [L][B][S][8])."""
+    L, B, S = c.swa.shape[0], c.swa.shape[1], c.swa.shape[2]
+    f, r, s = fp8_window_quantize(c.swa.reshape(L * B * S, DIM))
+    return f.view(L, B, S, 448), r.view(L, B, S, 64), s.view(L, B, S, 8)
+
+
 def mx_indexer(c: "Case", chunk_rows: int = 1 << 16):
     """MXFP4 indexer operands quantised from the case's bf16 indexer queries and keys
     -> (q_codes uint8 [T][32][64], q_scales uint8 [T][32][4], k_codes uint8 [B][N][64],

@@ -303,6 +303,50 @@ csa2_status csa2_reuse_attend(int32_t n_layers, const void* q, const uint8_t* kv
                               int32_t k, void* out, float* lse, void* workspace,
                               size_t workspace_bytes, void* hip_stream);
 
+/* -------------------------------------------------------- attend, extended
+ * csa2_attend_fp4 / csa2_reuse_attend (n_layers as there) with the formats the
+ * report deploys and the fused output rotation; opts NULL gives exactly
+ * csa2_reuse_attend.
+ *
+ *  kv_format  CSA2_KV_MXFP4: kv_scales E8M0 [B][N][16] (one per 32 channels);
+ *             CSA2_KV_E4M3_16 (report sec. 2.4.4: E2M1 with one E4M3 scale per
+ *             16 channels, no global scale; 288 B per entry): kv_scales E4M3
+ *             [B][N][32], x[c] = E2M1(code[c]) * E4M3(scale[c / 16]).
+ *  swa_format CSA2_SWA_BF16: swa bf16 [L][B][S][512] as before;
+ *             CSA2_SWA_FP8 (report sec. 2.4.4 keeps the window KV in FP8; the
+ *             V4 layout of 448 FP8 + 64 bf16 channels and 8 scale bytes, 584 B
+ *             per row): swa is not read; swa_fp8 E4M3 [L][B][S][448] with
+ *             swa_scales E8M0 [L][B][S][8] (scale j for channels 64j..64j+63,
+ *             j < 7; byte 7 unused), swa_rope bf16 [L][B][S][64] (channels
+ *             448..511).
+ *  rope_pos   int32 [T] or NULL: the output's channels 448..511 are rotated
+ *             by RoPE at position -rope_pos[t] before the bf16 cast (gzher.com
+ *             reading sec. 4.3): pair j = (448 + 2j, 449 + 2j), angle
+ *             phi = -pos * rope_base^(-2j/64), (x, y) -> (x cos phi - y sin phi,
+ *             x sin phi + y cos phi); rope_base > 1 (e.g. 10000).  lse is not
+ *             affected.
+ * The window tensors, like swa, start at the replay start; all other
+ * arguments, the workspace and the errors are those of csa2_reuse_attend.
+ */
+#define CSA2_KV_MXFP4 0
+#define CSA2_KV_E4M3_16 1
+#define CSA2_SWA_BF16 0
+#define CSA2_SWA_FP8 1
+typedef struct csa2_attend_opts {
+    int32_t kv_format;
+    int32_t swa_format;
+    const uint8_t* swa_fp8;
+    const void* swa_rope;
+    const uint8_t* swa_scales;
+    const int32_t* rope_pos;
+    float rope_base;
+} csa2_attend_opts;
+csa2_status csa2_attend_ex(int32_t n_layers, const void* q, const uint8_t* kv_codes, const uint8_t* kv_scales,
+                           const int32_t* indices, const void* swa, const int32_t* swa_end, const float* sink,
+                           float softmax_scale, int32_t T, int32_t q_per_seq, int64_t N, int32_t S,
+                           int32_t window, int32_t k, const csa2_attend_opts* opts, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

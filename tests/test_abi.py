@@ -215,6 +215,22 @@ def test_mxfp4_host_validation(L):
     assert rx(ws=None) == WORKSPACE
 
 
+def test_attend_ex_host_validation(L):
+    O = csa._AttendOpts
+    args = lambda opts, swa=P: [1, P, P, P, P, swa, P, None, 0.044, 4, 1, 4096, 128, 128, 512, opts, P, None, P,
+                                1 << 30, None]
+    assert L.csa2_attend_ex(*args(O(2, 0, None, None, None, None, 0.0))) == UNSUPPORTED     # unknown KV format
+    assert L.csa2_attend_ex(*args(O(0, 2, None, None, None, None, 0.0))) == UNSUPPORTED     # unknown window format
+    assert L.csa2_attend_ex(*args(O(0, 1, None, None, None, None, 0.0))) == INVALID         # FP8 window arrays missing
+    assert L.csa2_attend_ex(*args(O(0, 1, 0x10004, 0x20000, 0x30000, None, 0.0), None)) == INVALID  # misaligned
+    assert L.csa2_attend_ex(*args(O(0, 0, None, None, None, None, 0.0), None)) == INVALID   # bf16 window missing
+    assert L.csa2_attend_ex(*args(O(0, 0, None, None, None, 0x40000, 1.0))) == INVALID      # rope base must be > 1
+    assert L.csa2_attend_ex(*args(O(0, 0, None, None, None, 0x40000, float("inf")))) == INVALID
+    bad = args(O(0, 0, None, None, None, None, 0.0))
+    bad[0] = 9
+    assert L.csa2_attend_ex(*bad) == UNSUPPORTED
+
+
 def test_binding_fails_loudly_without_gpu_tensors():
     import torch
     with pytest.raises(ValueError):
