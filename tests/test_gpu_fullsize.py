@@ -172,3 +172,28 @@ def test_long_decode_mxfp4_indexer_sampled():
         ref_o = oracle_attend(c, {t: ref_i})
         assert_close_bf16(out[t], ref_o[t][0], what=f"mx t={t}")
         log(f"  t={t}: max|err|/eps={err.max() / eps[t]:.2e}, indices exact, attention within tolerance")
+
+
+def test_long_decode_deployed_formats_sampled():
+    # the report's deployed formats at the long-decode shape: E4M3/16 main KV, FP8 windows and
+    # the output rotation, over the exact selection of sampled queries
+    import oracle
+    from _ref import u16
+    log("[full] long_decode 4 x 1M, E4M3/16 KV + FP8 window + inverse RoPE")
+    c = G.make_case("long_decode", **G.CONFIGS["long_decode"], seed=0, device=DEV)
+    bf = (c.q_idx.view(BF), c.w_idx, c.k_idx.view(BF), c.q_pos, 1, 1)
+    ix = csa.csa2_index(*bf, want_scores=False)
+    idx = csa.csa2_topk(None, ix.tile_max, ix.stats, *bf)
+    nc, ns = G.kv_e4m3_16(c)
+    f8, rp, s8 = (x[0].contiguous() for x in G.window_fp8(c))
+    out = csa.csa2_attend_ex(c.q[0].view(BF), nc, ns, idx, c.swa_end, None, c.softmax_scale, 1, c.window,
+                             kv_format=csa.KV_E4M3_16, swa_fp8=f8, swa_rope=rp.view(BF), swa_scales=s8,
+                             rope_pos=c.q_pos)
+    torch.cuda.synchronize()
+    for t in [1, 2]:
+        o, _ = oracle.attend_ex(u16(c.q[0, t:t + 1]), npy(nc[t:t + 1]), npy(ns[t:t + 1]), npy(idx[t:t + 1]),
+                                npy(c.swa_end[t:t + 1]), None, c.softmax_scale, 1, c.window, kv_format=1,
+                                swa_fp8=npy(f8[t:t + 1]), swa_rope=u16(rp[t:t + 1]), swa_scales=npy(s8[t:t + 1]),
+                                rope_pos=npy(c.q_pos[t:t + 1]))
+        assert_close_bf16(out[t], o[0], what=f"deployed formats t={t}")
+        log(f"  t={t}: within tolerance")
