@@ -64,6 +64,12 @@ def lib():
         L.csa2o_dequant_row_e4m3.argtypes, L.csa2o_dequant_row_e4m3.restype = [vp, vp, i32, vp], None
         L.csa2o_dequant_swa_fp8_row.argtypes, L.csa2o_dequant_swa_fp8_row.restype = [vp, vp, vp, vp], None
         L.csa2o_rope_rotate.argtypes, L.csa2o_rope_rotate.restype = [vp, dbl, dbl], None
+        L.csa2o_e2m1_encode.argtypes, L.csa2o_e2m1_encode.restype = [dbl], ctypes.c_uint32
+        L.csa2o_e4m3_encode.argtypes, L.csa2o_e4m3_encode.restype = [dbl], ctypes.c_uint32
+        L.csa2o_quantize_mx_block.argtypes, L.csa2o_quantize_mx_block.restype = [vp, vp, vp], None
+        L.csa2o_quantize_e4m3_block.argtypes, L.csa2o_quantize_e4m3_block.restype = [vp, vp, vp], None
+        L.csa2o_kv_write.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, dbl, i32, vp, vp, vp, vp, vp]
+        L.csa2o_kv_write.restype = None
         L.csa2o_attend.restype = None
         L.csa2o_hsi_pool_row.argtypes, L.csa2o_hsi_pool_row.restype = [vp, i64, i32, i32, vp], i32
         L.csa2o_hsi_pool.argtypes, L.csa2o_hsi_pool.restype = [vp, vp, i32, i32, i64, i32, i32, vp], None
@@ -256,3 +262,49 @@ def attend(q, kv_codes, kv_scales, indices, swa, swa_end, sink, softmax_scale, q
     lib().csa2o_attend(_ptr(q), _ptr(kv_codes), _ptr(kv_scales), _ptr(indices), _ptr(swa), _ptr(swa_end),
                        _ptr(sk), float(softmax_scale), T, q_per_seq, N, S, window, k, _ptr(out), _ptr(lse))
     return out, lse
+
+
+def e2m1_encode(v: float) -> int:
+    return lib().csa2o_e2m1_encode(float(v))
+
+
+def e4m3_encode(v: float) -> int:
+    return lib().csa2o_e4m3_encode(float(v))
+
+
+def quantize_mx_row(x: np.ndarray):
+    """float64 [512] -> (codes uint8 [256], E8M0 scales uint8 [16]) by the OCP MX rule."""
+    x = _c(np.asarray(x, np.float64), np.float64)
+    codes, scales = np.zeros(x.size // 2, np.uint8), np.zeros(x.size // 32, np.uint8)
+    for b in range(x.size // 32):
+        lib().csa2o_quantize_mx_block(_ptr(x[32 * b:]), _ptr(codes[16 * b:]), _ptr(scales[b:]))
+    return codes, scales
+
+
+def quantize_e4m3_row(x: np.ndarray):
+    """float64 [512] -> (codes uint8 [256], E4M3 scales uint8 [32])."""
+    x = _c(np.asarray(x, np.float64), np.float64)
+    codes, scales = np.zeros(x.size // 2, np.uint8), np.zeros(x.size // 16, np.uint8)
+    for b in range(x.size // 16):
+        lib().csa2o_quantize_e4m3_block(_ptr(x[16 * b:]), _ptr(codes[8 * b:]), _ptr(scales[b:]))
+    return codes, scales
+
+
+def kv_write(h, w_kv, w_z, w_ik, m, pos, rope_base=10000.0, kv_format=0):
+    """CSA2 compressor + indexer-K projection + RoPE + cache quantisation (report sec. 2.3, 2.4.4):
+    h uint16 [n_ent*m][d], w_kv / w_z uint16 [d][512] (w_z None for m = 1), w_ik uint16 [512][128],
+    pos int32 [n_ent] -> dict(entry fp64 [n][512] after RoPE, codes uint8 [n][256], scales uint8
+    [n][16 or 32], k fp64 [n][128], k_bf16 uint16 [n][128])."""
+    h, w_kv, w_ik = _c(h, np.uint16), _c(w_kv, np.uint16), _c(w_ik, np.uint16)
+    wz = None if w_z is None else _c(w_z, np.uint16)
+    pos = _c(pos, np.int32)
+    d = h.shape[1]
+    n = h.shape[0] // m
+    entry = np.empty((n, DIM), np.float64)
+    codes = np.empty((n, DIM // 2), np.uint8)
+    scales = np.empty((n, DIM // (32 if kv_format == 0 else 16)), np.uint8)
+    k = np.empty((n, IDX_DIM), np.float64)
+    kb = np.empty((n, IDX_DIM), np.uint16)
+    lib().csa2o_kv_write(_ptr(h), _ptr(w_kv), _ptr(wz), _ptr(w_ik), d, n, m, _ptr(pos), float(rope_base), kv_format,
+                         _ptr(entry), _ptr(codes), _ptr(scales), _ptr(k), _ptr(kb))
+    return dict(entry=entry, codes=codes, scales=scales, k=k, k_bf16=kb)

@@ -417,3 +417,139 @@ void csa2o_attend(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_
     csa2o_attend_ex(q, kv_codes, kv_scales, 0, indices, swa, NULL, NULL, NULL, 0, swa_end, sink, softmax_scale, T,
                     q_per_seq, N, S, window, k, NULL, 0.0, out, lse);
 }
+
+/* ---- KV write path ------------------------------------------------------- */
+
+/* OCP MX (v1.0) conversion of one value already divided by its block scale to
+ * E2M1: round to the nearest of {0, 0.5, 1, 1.5, 2, 3, 4, 6}, ties to the code
+ * with a zero mantissa bit, saturating at 6.  Returns the 4-bit code. */
+uint32_t csa2o_e2m1_encode(double v) {
+    static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    double a = fabs(v);
+    uint32_t best = 0;
+    for (uint32_t c = 1; c < 8; ++c) {
+        double dc = fabs(a - grid[c]), db = fabs(a - grid[best]);
+        if (dc < db || (dc == db && (c & 1u) == 0u)) best = c;
+    }
+    return best | (v < 0.0 ? 8u : 0u);
+}
+
+/* OFP8 E4M3 encoding: the nearest finite E4M3 value, ties to the even code,
+ * saturating at 448. */
+uint32_t csa2o_e4m3_encode(double v) {
+    uint32_t best = 0;
+    double a = fabs(v);
+    for (uint32_t c = 1; c < 0x7F; ++c) {
+        double dc = fabs(a - csa2o_e4m3(c)), db = fabs(a - csa2o_e4m3(best));
+        if (dc < db || (dc == db && (c & 1u) == 0u)) best = c;
+    }
+    return best | (v < 0.0 && best != 0 ? 0x80u : 0u);
+}
+
+/* MXFP4 block of 32 (OCP MX): shared exponent floor(log2 amax) - 2 (the E2M1
+ * maximum exponent), E8M0 code clamped to [0, 254]; an all-zero block gets 127. */
+void csa2o_quantize_mx_block(const double* x, uint8_t* codes, uint8_t* scale) {
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(x[i]));
+    int e = 127;
+    if (amax > 0.0) {
+        int ex;
+        frexp(amax, &ex);               /* amax = f * 2^ex, f in [0.5, 1) */
+        e = (ex - 1) - 2 + 127;
+        if (e < 0) e = 0;
+        if (e > 254) e = 254;
+    }
+    *scale = (uint8_t)e;
+    for (int i = 0; i < 32; i += 2) {
+        uint32_t lo = csa2o_e2m1_encode(ldexp(x[i], 127 - e));
+        uint32_t hi = csa2o_e2m1_encode(ldexp(x[i + 1], 127 - e));
+        codes[i / 2] = (uint8_t)(lo | (hi << 4));
+    }
+}
+
+/* E2M1 block of 16 with an E4M3 scale (the report's main-KV format, sec. 2.4.4;
+ * reading: the scale is the E4M3 value nearest to amax / 6, the elements x /
+ * scale rounded to E2M1). */
+void csa2o_quantize_e4m3_block(const double* x, uint8_t* codes, uint8_t* scale) {
+    double amax = 0.0;
+    for (int i = 0; i < 16; ++i) amax = fmax(amax, fabs(x[i]));
+    uint32_t sc = csa2o_e4m3_encode(amax / 6.0);
+    double s = csa2o_e4m3(sc);
+    *scale = (uint8_t)sc;
+    for (int i = 0; i < 16; i += 2) {
+        uint32_t lo = s > 0.0 ? csa2o_e2m1_encode(x[i] / s) : 0u;
+        uint32_t hi = s > 0.0 ? csa2o_e2m1_encode(x[i + 1] / s) : 0u;
+        codes[i / 2] = (uint8_t)(lo | (hi << 4));
+    }
+}
+
+/* V4.1 report sec. 2.3: the CSA2 compressor keeps CSA's gated pooling of m
+ * tokens into one main-KV entry without CSA's overlap and absolute positional
+ * embedding; the V4 reading (sec. 4.2) gives the pooling: C = H W_kv, Z = H W_z,
+ * S = softmax over the m tokens of a block (per channel), entry = sum_j S_j C_j
+ * (HCA's form; CSA2 drops its bias B); with m = 1 the entry is C.  Indexer K is
+ * a projection of the main-KV entry (sec. 2.3); reading: of the pooled entry
+ * before RoPE, K = entry W_ik.  RoPE on the last 64 channels at the entry's
+ * position (V4 reading sec. 4.3), then the cache is quantised (sec. 2.4.4,
+ * after RoPE).  Every step fp64; sums over k in order.
+ * h bf16 [n_ent*m][d]; w_kv, w_z bf16 [d][512] (w_z unused when m = 1);
+ * w_ik bf16 [512][128]; pos int32 [n_ent].
+ * Outputs: entry fp64 [n_ent][512] (after RoPE, before quantisation), the cache
+ * (kv_format 0: MXFP4 codes [n][256] + scales [n][16]; 1: E4M3/16 scales [n][32]),
+ * k fp64 [n_ent][128] and k_bf16 (nearest even). */
+void csa2o_kv_write(const uint16_t* h, const uint16_t* w_kv, const uint16_t* w_z, const uint16_t* w_ik, int32_t d,
+                    int32_t n_ent, int32_t m, const int32_t* pos, double rope_base, int32_t kv_format,
+                    double* entry, uint8_t* kv_codes, uint8_t* kv_scales, double* k, uint16_t* k_bf16) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t e = 0; e < n_ent; ++e) {
+        double* c = entry + (int64_t)e * DIM;
+        double* cj = (double*)malloc((size_t)m * DIM * sizeof(double));
+        double* zj = (double*)malloc((size_t)m * DIM * sizeof(double));
+        for (int j = 0; j < m; ++j) {
+            const uint16_t* hr = h + ((int64_t)e * m + j) * d;
+            for (int ch = 0; ch < DIM; ++ch) {
+                double acc = 0.0, accz = 0.0;
+                for (int32_t kk = 0; kk < d; ++kk) {
+                    double hv = bf16_to_double(hr[kk]);
+                    acc += hv * bf16_to_double(w_kv[(int64_t)kk * DIM + ch]);
+                    if (m > 1) accz += hv * bf16_to_double(w_z[(int64_t)kk * DIM + ch]);
+                }
+                cj[j * DIM + ch] = acc;
+                zj[j * DIM + ch] = accz;
+            }
+        }
+        for (int ch = 0; ch < DIM; ++ch) {
+            if (m == 1) { c[ch] = cj[ch]; continue; }
+            double zmax = -INFINITY, den = 0.0, num = 0.0;
+            for (int j = 0; j < m; ++j) zmax = fmax(zmax, zj[j * DIM + ch]);
+            for (int j = 0; j < m; ++j) {
+                double p = exp(zj[j * DIM + ch] - zmax);
+                den += p;
+                num += p * cj[j * DIM + ch];
+            }
+            c[ch] = num / den;
+        }
+        for (int o = 0; o < IDX_DIM; ++o) {
+            double acc = 0.0;
+            for (int ch = 0; ch < DIM; ++ch) acc += c[ch] * bf16_to_double(w_ik[(int64_t)ch * IDX_DIM + o]);
+            k[(int64_t)e * IDX_DIM + o] = acc;
+            /* nearest bf16, ties to even, via float (every double here is a sum of products of bf16 values) */
+            float f = (float)acc;
+            uint32_t u;
+            memcpy(&u, &f, 4);
+            k_bf16[(int64_t)e * IDX_DIM + o] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+        }
+        csa2o_rope_rotate(c, (double)pos[e], rope_base);
+        if (kv_format == 0) {
+            for (int b = 0; b < DIM / 32; ++b)
+                csa2o_quantize_mx_block(c + 32 * b, kv_codes + (int64_t)e * (DIM / 2) + 16 * b,
+                                        kv_scales + (int64_t)e * (DIM / 32) + b);
+        } else {
+            for (int b = 0; b < DIM / 16; ++b)
+                csa2o_quantize_e4m3_block(c + 16 * b, kv_codes + (int64_t)e * (DIM / 2) + 8 * b,
+                                          kv_scales + (int64_t)e * (DIM / 16) + b);
+        }
+        free(cj);
+        free(zj);
+    }
+}

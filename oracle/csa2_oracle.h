@@ -85,6 +85,45 @@ void csa2o_attend(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_
                   const double* sink, double softmax_scale, int32_t T, int32_t q_per_seq,
                   int64_t N, int32_t S, int32_t window, int32_t k, double* out, double* lse);
 
+
+/* ---- further formats (report sec. 2.4.4) */
+/* OFP8 E4M3 value of a code (bias 7, subnormals, S.1111.111 NaN). */
+double csa2o_e4m3(uint32_t code);
+/* E2M1 row with one E4M3 scale per 16 channels. */
+void csa2o_dequant_row_e4m3(const uint8_t* codes, const uint8_t* scales, int32_t dim, double* out);
+/* FP8 window row: 448 E4M3 channels with an E8M0 scale per 64, then 64 bf16 channels. */
+void csa2o_dequant_swa_fp8_row(const uint8_t* fp8, const uint16_t* rope, const uint8_t* scales, double* out);
+
+/* ---- MXFP4 indexer (report sec. 2.4.4) */
+double csa2o_index_score_deq(const double* q /*[32][128]*/, const float* w, const double* key /*[128]*/);
+void csa2o_index_mx(const uint8_t* q_codes, const uint8_t* q_scales, const float* w_idx, const uint8_t* k_codes,
+                    const uint8_t* k_scales, const int32_t* q_pos, int32_t ratio, int32_t T, int32_t q_per_seq,
+                    int64_t N, double* scores);
+
+/* ---- hierarchical sparse indexer and Reindex (report sec. 2.3.2) */
+int32_t csa2o_hsi_pool_row(const double* scores, int64_t n_vis, int32_t block, int32_t n_blocks, int32_t* pool);
+void csa2o_hsi_pool(const double* scores, const int32_t* q_pos, int32_t ratio, int32_t T, int64_t N, int32_t block,
+                    int32_t n_blocks, int32_t* pool);
+void csa2o_reindex_topk(const double* scores, const int32_t* pool, int32_t T, int64_t N, int64_t P, int32_t k,
+                        int32_t* out);
+
+/* ---- output rotation and attention with formats (V4 reading sec. 4.3) */
+void csa2o_rope_rotate(double* v /*[512]*/, double pos, double base);
+void csa2o_attend_ex(const uint16_t* q, const uint8_t* kv_codes, const uint8_t* kv_scales, int32_t kv_format,
+                     const int32_t* indices, const uint16_t* swa, const uint8_t* swa_fp8, const uint16_t* swa_rope,
+                     const uint8_t* swa_scales, int32_t swa_format, const int32_t* swa_end, const double* sink,
+                     double softmax_scale, int32_t T, int32_t q_per_seq, int64_t N, int32_t S, int32_t window,
+                     int32_t k, const int32_t* rope_pos, double rope_base, double* out, double* lse);
+
+/* ---- KV write path (report sec. 2.3 compressor, sec. 2.4.4 quantisation) */
+uint32_t csa2o_e2m1_encode(double v);
+uint32_t csa2o_e4m3_encode(double v);
+void csa2o_quantize_mx_block(const double* x /*[32]*/, uint8_t* codes /*[16]*/, uint8_t* scale);
+void csa2o_quantize_e4m3_block(const double* x /*[16]*/, uint8_t* codes /*[8]*/, uint8_t* scale);
+void csa2o_kv_write(const uint16_t* h, const uint16_t* w_kv, const uint16_t* w_z, const uint16_t* w_ik, int32_t d,
+                    int32_t n_ent, int32_t m, const int32_t* pos, double rope_base, int32_t kv_format,
+                    double* entry, uint8_t* kv_codes, uint8_t* kv_scales, double* k, uint16_t* k_bf16);
+
 #ifdef __cplusplus
 }
 #endif

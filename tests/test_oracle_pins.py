@@ -680,3 +680,96 @@ def test_attend_ex_formats_reduce_to_known_cases(oracle_lib):
     b, lb = oracle.attend_ex(q, codes, np.full((B, N, 32), 0x38, np.uint8), idx, swa_end, None, 0.04, 2, 8,
                              kv_format=1, swa_fp8=fp8, swa_rope=rope, swa_scales=np.full((B, S, 8), 127, np.uint8))
     assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+# ---- KV write path: compressor, indexer-K projection, RoPE, cache quantisation
+
+def test_e2m1_encode_matches_ocp_ties(oracle_lib):
+    import oracle
+    grid = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    for inp, exp in _golden("e2m1_rounding.txt"):
+        code = oracle.e2m1_encode(float(inp))
+        val = grid[code & 7] * (-1 if code & 8 else 1)
+        assert val == float(exp), (inp, val)
+
+
+def test_e4m3_encode_roundtrip_and_ties(oracle_lib):
+    import oracle
+    for c in range(0x7F):
+        v = oracle.e4m3(c)
+        assert oracle.e4m3_encode(v) == c
+        if c:
+            assert oracle.e4m3_encode(-v) == c | 0x80
+    for c in range(0x7E):
+        mid = (oracle.e4m3(c) + oracle.e4m3(c + 1)) / 2
+        assert oracle.e4m3_encode(mid) == (c if c % 2 == 0 else c + 1)
+    assert oracle.e4m3_encode(1e9) == 0x7E and oracle.e4m3_encode(-1e9) == 0xFE
+
+
+def test_quantizers_agree_with_generator_rules(oracle_lib):
+    # two independent statements of the same published rules: the generator's (torch) and
+    # the oracle's (C) quantisers give identical bytes on N(0,1) bf16 data
+    import oracle
+    x = G.normal_bf16(13, 5, 0, 16 * 512).view(16, 512)
+    xf = G.bf16_bits_to_float(x).double().numpy()
+    gc, gs = G.mxfp4_quantize(x)
+    ec, es = G.e4m3_16_quantize(x)
+    for r in range(16):
+        c, s = oracle.quantize_mx_row(xf[r])
+        assert np.array_equal(c, gc[r].numpy()) and np.array_equal(s, gs[r].numpy())
+        c, s = oracle.quantize_e4m3_row(xf[r])
+        assert np.array_equal(c, ec[r].numpy()) and np.array_equal(s, es[r].numpy())
+    # a block whose largest magnitude is 6 * 2^k gets scale code 127 + k and is represented exactly
+    v = np.zeros(512)
+    v[:32] = 6.0 * 2.0 ** -3
+    v[1] = -1.5 * 2.0 ** -3
+    c, s = oracle.quantize_mx_row(v)
+    assert s[0] == 124 and np.array_equal(oracle.dequant_rows(c[None], s[None])[0][:32], v[:32])
+
+
+def _bits(a):
+    return (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_kv_write_closed_forms(oracle_lib):
+    import oracle
+    rng = np.random.default_rng(21)
+    d, n = 512, 6
+    eye = _bits(np.eye(d, 512))
+    w_ik = np.zeros((512, 128), np.float32)
+    w_ik[:128, :] = np.eye(128)
+    w_ik = _bits(w_ik)
+    h1 = _bits(rng.uniform(-2, 2, (n, d)))
+    hval = (h1.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    pos0 = np.zeros(n, np.int32)
+    # m = 1, W_kv = I, position 0: the entry is the token's vector; K its first 128 channels
+    r = oracle.kv_write(h1, eye, None, w_ik, 1, pos0)
+    assert np.array_equal(r["entry"], hval) and np.array_equal(r["k"], hval[:, :128])
+    assert np.array_equal(r["k_bf16"], h1[:, :128])
+    # the cache holds the OCP MX quantisation of the entry
+    for e in range(n):
+        c, s = oracle.quantize_mx_row(r["entry"][e])
+        assert np.array_equal(c, r["codes"][e]) and np.array_equal(s, r["scales"][e])
+    # RoPE at the entry's position on the last 64 channels only, after K is taken
+    pos = rng.integers(0, 100000, n).astype(np.int32)
+    rp = oracle.kv_write(h1, eye, None, w_ik, 1, pos, 10000.0, 1)
+    for e in range(n):
+        assert np.array_equal(rp["entry"][e], oracle.rope_rotate(hval[e], float(pos[e]), 10000.0))
+        c, s = oracle.quantize_e4m3_row(rp["entry"][e])
+        assert np.array_equal(c, rp["codes"][e]) and np.array_equal(s, rp["scales"][e])
+    assert np.array_equal(rp["k"], hval[:, :128])
+    # m = 2 with zero gate weights: equal weights, the entry is the mean of the two tokens
+    h2 = _bits(rng.uniform(-2, 2, (2 * n, d)))
+    h2v = (h2.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    zero = np.zeros((d, 512), np.uint16)
+    r2 = oracle.kv_write(h2, eye, zero, w_ik, 2, pos0)
+    assert np.allclose(r2["entry"], (h2v[0::2] + h2v[1::2]) / 2, rtol=1e-15, atol=0)
+    # a gate that strongly prefers the first token of each pair: the entry is that token
+    gate = np.zeros((d, 512), np.float32)
+    gate[0, :] = 1.0
+    h3 = h2v.copy()
+    h3[0::2, 0], h3[1::2, 0] = 60.0, -60.0
+    h3b = _bits(h3)
+    h3v = (h3b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    r3 = oracle.kv_write(h3b, eye, _bits(gate), w_ik, 2, pos0)
+    assert np.allclose(r3["entry"], h3v[0::2], rtol=1e-12, atol=1e-12)
