@@ -21,13 +21,14 @@ __all__ = [
     "TOPK_ROW_MAX", "STATS_WORDS", "csa2_hsi_pool", "csa2_reindex", "hsi_pool_workspace_bytes",
     "reindex_workspace_bytes", "HSI_BLOCK", "HSI_BLOCKS", "HSI_POOL", "csa2_index_mxfp4", "csa2_topk_mxfp4",
     "csa2_hsi_pool_mxfp4", "csa2_reindex_mxfp4", "index_mxfp4_stats_bytes", "csa2_attend_ex", "KV_MXFP4",
-    "KV_E4M3_16", "SWA_BF16", "SWA_FP8",
+    "KV_E4M3_16", "SWA_BF16", "SWA_FP8", "csa2_kv_write", "kv_write_workspace_bytes", "K_BF16", "K_MXFP4",
 ]
 
 IDX_HEADS, IDX_DIM, HEADS, DIM, TOPK, MAX_WINDOW, MAX_LAYERS = 32, 128, 64, 512, 512, 128, 8
 TILE, TOPK_ROW_MAX, STATS_WORDS = 16, 36864, 4
 HSI_BLOCK, HSI_BLOCKS = 8, 2048
 KV_MXFP4, KV_E4M3_16, SWA_BF16, SWA_FP8 = 0, 1, 0, 1
+K_BF16, K_MXFP4 = 0, 1
 HSI_POOL = HSI_BLOCK * HSI_BLOCKS
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +68,9 @@ _SIGNATURES = {
                         ctypes.POINTER(_AttendOpts), _vp, _vp, _vp, _sz, _vp], _i32),
     "csa2_attend_fp4": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i64, _i32, _i32, _i32, _vp, _vp,
                          _vp, _sz, _vp], _i32),
+    "csa2_kv_write_workspace_bytes": ([_i32, _i32, _i32], _sz),
+    "csa2_kv_write": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _f32, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _sz,
+                       _vp], _i32),
     "csa2_reuse_attend": ([_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i64, _i32, _i32, _i32, _vp,
                            _vp, _vp, _sz, _vp], _i32),
 }
@@ -547,3 +551,51 @@ def csa2_attend_ex(q, kv_codes, kv_scales, indices, swa_end, sink=None, softmax_
                               _p(lse), _p(workspace), _nbytes(workspace), _stream(q))
     _raise(st, "csa2_attend_ex")
     return (out, lse) if want_lse else out
+
+
+def kv_write_workspace_bytes(n_ent: int, m: int, d: int) -> int:
+    return lib().csa2_kv_write_workspace_bytes(n_ent, m, d)
+
+
+def csa2_kv_write(h, w_kv, w_ik, pos, m=1, w_z=None, rope_base=10000.0, kv_format=KV_MXFP4, k_format=K_BF16,
+                  kv_codes=None, kv_scales=None, k_out=None, k_scales=None, workspace=None):
+    """KV write for n_ent = h.shape[0] / m new entries: gated pooling of m tokens, indexer-K
+    projection of the pooled entry, RoPE of channels 448..511 at pos, cache quantisation.
+    h bf16 [n_ent*m][d]; w_kv, w_z bf16 [512][d]; w_ik bf16 [128][512]; pos int32 [n_ent].
+    Returns (kv_codes uint8 [n][256], kv_scales uint8 [n][16 or 32], k_out, k_scales) with k_out
+    bf16 [n][128] (k_format K_BF16, k_scales None) or uint8 [n][64] plus k_scales uint8 [n][4]."""
+    dev = h.device
+    if h.dim() != 2 or h.shape[0] % m != 0:
+        raise ValueError("h must be [n_ent*m][d]")
+    n, d = h.shape[0] // m, h.shape[1]
+    _check(h, "h", (n * m, d), elem_size=2, device=dev)
+    _check(w_kv, "w_kv", (DIM, d), elem_size=2, device=dev)
+    if m > 1:
+        _check(w_z, "w_z", (DIM, d), elem_size=2, device=dev)
+    _check(w_ik, "w_ik", (IDX_DIM, DIM), elem_size=2, device=dev)
+    _check(pos, "pos", (n,), dtype=torch.int32, device=dev)
+    sc_cols = DIM // 32 if kv_format == KV_MXFP4 else DIM // 16
+    if kv_codes is None:
+        kv_codes = torch.empty((n, DIM // 2), dtype=torch.uint8, device=dev)
+    if kv_scales is None:
+        kv_scales = torch.empty((n, sc_cols), dtype=torch.uint8, device=dev)
+    _check(kv_codes, "kv_codes", (n, DIM // 2), dtype=torch.uint8, device=dev)
+    _check(kv_scales, "kv_scales", (n, sc_cols), dtype=torch.uint8, device=dev)
+    if k_format == K_BF16:
+        if k_out is None:
+            k_out = torch.empty((n, IDX_DIM), dtype=torch.bfloat16, device=dev)
+        _check(k_out, "k_out", (n, IDX_DIM), elem_size=2, device=dev)
+        k_scales = None
+    else:
+        if k_out is None:
+            k_out = torch.empty((n, IDX_DIM // 2), dtype=torch.uint8, device=dev)
+        if k_scales is None:
+            k_scales = torch.empty((n, IDX_DIM // 32), dtype=torch.uint8, device=dev)
+        _check(k_out, "k_out", (n, IDX_DIM // 2), dtype=torch.uint8, device=dev)
+        _check(k_scales, "k_scales", (n, IDX_DIM // 32), dtype=torch.uint8, device=dev)
+    workspace = _ws(kv_write_workspace_bytes(n, m, d), dev, workspace)
+    st = lib().csa2_kv_write(_p(h), _p(w_kv), _p(w_z) if m > 1 else None, _p(w_ik), d, n, m, _p(pos),
+                             float(rope_base), kv_format, _p(kv_codes), _p(kv_scales), k_format, _p(k_out),
+                             _p(k_scales), _p(workspace), _nbytes(workspace), _stream(h))
+    _raise(st, "csa2_kv_write")
+    return kv_codes, kv_scales, k_out, k_scales

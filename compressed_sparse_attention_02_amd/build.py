@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa2.so")
-SOURCES = ["abi.hip", "index.hip", "index_mx.hip", "topk.hip", "reindex.hip", "attend.hip"]
+SOURCES = ["abi.hip", "index.hip", "index_mx.hip", "topk.hip", "reindex.hip", "attend.hip", "kvwrite.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Wall", "-Werror", "-Wno-unused-command-line-argument",

@@ -335,6 +335,29 @@ def kv_rows(seed: int, rows: torch.Tensor):
     return mxfp4_quantize(x)
 
 
+# Streams of the KV-write inputs (hidden states, projection weights, positions).
+ST_H, ST_WKV, ST_WZ, ST_WIK, ST_POS = 200, 201, 202, 203, 204
+
+
+def _scaled_normal_bf16(seed: int, stream: int, count: int, exp2: int, device) -> torch.Tensor:
+    """N(0,1) bf16 bits times 2^exp2 (exact: only the exponent changes)."""
+    f = bf16_bits_to_float(normal_bf16(seed, stream, 0, count, device)) * (2.0 ** exp2)
+    return (f.view(torch.int32) >> 16).to(torch.int16)
+
+
+def kv_write_inputs(seed: int, n_ent: int, m: int, d: int, device="cpu", max_pos: int = 1 << 20):
+    """Inputs of the KV write for n_ent entries of m tokens with hidden size d (bf16 bits as int16):
+    h [n_ent*m][d] ~ N(0,1); w_kv, w_z [512][d] ~ N(0,1) * 2^-6 (w_z None when m == 1);
+    w_ik [128][512] ~ N(0,1) * 2^-4; pos int32 [n_ent] uniform in [0, max_pos).  The weight
+    scales keep the pooled entries and the indexer keys of order one for d near 5120."""
+    h = normal_bf16(seed, ST_H, 0, n_ent * m * d, device).view(n_ent * m, d)
+    w_kv = _scaled_normal_bf16(seed, ST_WKV, DIM * d, -6, device).view(DIM, d)
+    w_z = _scaled_normal_bf16(seed, ST_WZ, DIM * d, -6, device).view(DIM, d) if m > 1 else None
+    w_ik = _scaled_normal_bf16(seed, ST_WIK, IDX_DIM * DIM, -4, device).view(IDX_DIM, DIM)
+    pos = (uniform_f32(seed, ST_POS, 0, n_ent, device) * max_pos).to(torch.int32)
+    return dict(h=h, w_kv=w_kv, w_z=w_z, w_ik=w_ik, pos=pos)
+
+
 # Workloads named by what they are (batch, entries, mode).
 CONFIGS = {
     "tiny_decode": dict(B=1, N=2048),

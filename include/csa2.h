@@ -347,6 +347,58 @@ csa2_status csa2_attend_ex(int32_t n_layers, const void* q, const uint8_t* kv_co
                            int32_t window, int32_t k, const csa2_attend_opts* opts, void* out, float* lse,
                            void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* -------------------------------------------------------------- KV write
+ * The write side of the main-KV cache for n_ent new compressed entries: the
+ * CSA2 compressor, the indexer-K projection, RoPE and the cache quantisation.
+ * DeepSeek-V4.1-Flash report sec. 2.3: CSA2 pools m tokens into one entry
+ * without CSA's overlap between neighbouring entries and without its absolute
+ * positional embedding, and obtains indexer K by projecting main-KV entries;
+ * sec. 2.4.4: the cache is quantised to FP4 after RoPE.  The pooling form is
+ * the gated one of the gzher.com DeepSeek-V4 reading (sec. 4.2, HCA) without
+ * its bias: for entry e with tokens t = e*m + j, j < m,
+ *   C_t = h_t W_kv^T,  Z_t = h_t W_z^T,
+ *   pre[e][c] = sum_j softmax_j(Z_{e*m+j}[c]) C_{e*m+j}[c]   (m = 1: pre = C),
+ *   k[e] = pre[e] W_ik^T                         (indexer K, before RoPE),
+ *   entry[e] = pre[e] with channels 448..511 rotated at position pos[e]:
+ *     pair (448 + 2j, 449 + 2j), phi = pos * rope_base^(-2j/64),
+ *     (x, y) -> (x cos phi - y sin phi, x sin phi + y cos phi),
+ * and entry[e] is quantised into the cache row:
+ *   kv_format CSA2_KV_MXFP4: per 32 channels an E8M0 scale 2^(floor(log2 amax) - 2)
+ *     (code clamped to 0..254, 127 for an all-zero block), elements x / scale
+ *     to the nearest E2M1 value (ties to the even code, saturating at 6);
+ *   kv_format CSA2_KV_E4M3_16: per 16 channels the E4M3 value nearest to
+ *     amax / 6 (ties to even, saturating at 448), elements x / scale to E2M1
+ *     (all codes 0 when the scale is 0).
+ * Indexer K is written as bf16 (k_format 0, nearest even) or as an MXFP4 row
+ * (k_format 1: 64 code bytes + 4 E8M0 scales per entry, the same rule).
+ * Products and sums are fp32 (projections on bf16 matrix cores); a code may
+ * differ from the exact-arithmetic result only where the exact value lies
+ * within fp32 rounding of a decision boundary.
+ *
+ *  h        bf16  [n_ent * m][d]     token hidden states, entry e = rows e*m .. e*m + m - 1
+ *  w_kv     bf16  [512][d]           row c = weights of output channel c
+ *  w_z      bf16  [512][d]           gate weights; ignored (may be NULL) when m == 1
+ *  w_ik     bf16  [128][512]         row o = weights of indexer-K channel o
+ *  pos      int32 [n_ent]            RoPE position of each entry
+ *  rope_base > 1 and finite
+ *  m in {1, 2, 4, 8};  d a positive multiple of 32;  n_ent >= 1
+ *  kv_codes uint8 [n_ent][256] out;  kv_scales uint8 [n_ent][16] (MXFP4) or [n_ent][32] (E4M3/16) out
+ *  k_out    bf16 [n_ent][128] (k_format 0) or uint8 [n_ent][64] (k_format 1) out
+ *  k_scales uint8 [n_ent][4] out (k_format 1; ignored otherwise)
+ *  workspace >= csa2_kv_write_workspace_bytes(n_ent, m, d), 16-byte aligned;
+ *            its contents on entry do not matter
+ * Returns CSA2_ERR_INVALID_ARG for a NULL or misaligned pointer or a bad
+ * rope_base, CSA2_ERR_UNSUPPORTED for m, d or a format outside the lists,
+ * CSA2_ERR_WORKSPACE for a short workspace.  Outputs may not alias inputs.
+ */
+#define CSA2_K_BF16 0
+#define CSA2_K_MXFP4 1
+size_t csa2_kv_write_workspace_bytes(int32_t n_ent, int32_t m, int32_t d);
+csa2_status csa2_kv_write(const void* h, const void* w_kv, const void* w_z, const void* w_ik, int32_t d,
+                          int32_t n_ent, int32_t m, const int32_t* pos, float rope_base, int32_t kv_format,
+                          uint8_t* kv_codes, uint8_t* kv_scales, int32_t k_format, void* k_out,
+                          uint8_t* k_scales, void* workspace, size_t workspace_bytes, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

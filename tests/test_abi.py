@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"csa2_index", "csa2_topk", "csa2_attend_fp4", "csa2_reuse_attend", "csa2_hsi_pool",
             "csa2_reindex", "csa2_index_mxfp4", "csa2_topk_mxfp4", "csa2_hsi_pool_mxfp4",
-            "csa2_reindex_mxfp4"} <= set(names)
+            "csa2_reindex_mxfp4", "csa2_attend_ex", "csa2_kv_write"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -229,6 +229,37 @@ def test_attend_ex_host_validation(L):
     bad = args(O(0, 0, None, None, None, None, 0.0))
     bad[0] = 9
     assert L.csa2_attend_ex(*bad) == UNSUPPORTED
+
+
+def _kv_write(L, h=P, w_kv=P, w_z=P, w_ik=P, d=5120, n=4, m=2, pos=P, base=10000.0, kvf=0, codes=P,
+              scales=P, kf=0, k_out=P, k_sc=None, ws=Q, wsb=None):
+    if wsb is None:
+        wsb = max(L.csa2_kv_write_workspace_bytes(n, m, d), 1)
+    return L.csa2_kv_write(h, w_kv, w_z, w_ik, d, n, m, pos, base, kvf, codes, scales, kf, k_out, k_sc, ws, wsb,
+                           None)
+
+
+def test_kv_write_host_validation(L):
+    # workspace: per-slice sums of C and Z, the 8 per-chunk key shares, one counter per 16 tokens
+    assert csa.kv_write_workspace_bytes(4, 1, 5120) >= 4 * 512 * 4
+    assert csa.kv_write_workspace_bytes(300, 2, 5120) >= 2 * 600 * 512 * 4 + 8 * 300 * 128 * 4
+    assert csa.kv_write_workspace_bytes(4, 3, 5120) == 0      # m in {1, 2, 4, 8}
+    assert csa.kv_write_workspace_bytes(4, 1, 100) == 0       # d a multiple of 32
+    assert csa.kv_write_workspace_bytes(0, 1, 512) == 0
+    assert _kv_write(L, h=None) == INVALID
+    assert _kv_write(L, w_z=None) == INVALID                  # gate weights needed for m > 1
+    assert _kv_write(L, w_z=None, m=1, wsb=1) == WORKSPACE   # m = 1 takes no gate weights
+    assert _kv_write(L, k_out=MIS) == INVALID
+    assert _kv_write(L, kf=1) == INVALID                      # MXFP4 keys need their scale array
+    assert _kv_write(L, base=1.0) == INVALID
+    assert _kv_write(L, base=float("nan")) == INVALID
+    assert _kv_write(L, n=0) == INVALID
+    assert _kv_write(L, m=3) == UNSUPPORTED
+    assert _kv_write(L, d=100) == UNSUPPORTED
+    assert _kv_write(L, kvf=2) == UNSUPPORTED
+    assert _kv_write(L, kf=2) == UNSUPPORTED
+    assert _kv_write(L, ws=None) == WORKSPACE
+    assert _kv_write(L, wsb=L.csa2_kv_write_workspace_bytes(4, 2, 5120) - 1) == WORKSPACE
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
