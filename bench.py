@@ -308,6 +308,10 @@ def main():
     # ---- the same step with the MXFP4 indexer (FP4 queries and keys, 68 B per key)
     mx = mxfp4_step(c, G, csa, args, stream, timed, idx, out, ws_t, ws_a)
 
+    # ---- the KV write (compressor, indexer-K projection, RoPE, FP4 cache) for this batch's new
+    # entries and for a prefill chunk
+    kvw = kv_write_section(csa, G, dev, B)
+
     # plain copy bandwidth of this machine (context for the roofline fraction)
     x = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     y = torch.empty_like(x)
@@ -352,6 +356,7 @@ def main():
                       "algorithmic_bytes": att_bytes, "GBps": att_gbps, "frac_hbm": att_gbps / HBM_PEAK_GBPS,
                       "flops": att_flops, "TFLOPs": att_tflops, "frac_mfma_bf16": att_tflops / MFMA_BF16_PEAK_TFLOPS},
         "mxfp4_indexer": mx,
+        "kv_write": kvw,
         "copy_GBps": copy_gbps,
     }
 
@@ -446,6 +451,54 @@ def mxfp4_step(c, G, csa, args, stream, timed, idx, out, ws_t, ws_a):
             "step_frac_of_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "deployed_formats_step": dep,
             "note": "same workload and selection semantics with FP4 indexer operands; not the headline"}
+
+
+def kv_write_section(csa, G, dev, B, d=5120, reps=50):
+    """csa2_kv_write at the model's hidden size: one decode step's new entries (one per sequence,
+    the decoder's ratio m = 1) and a 4096-token prefill chunk at the encoder's ratio m = 2.
+    Each call is captured once in a graph and replayed, so the time is the GPU's (both kernels
+    and the gap between them), not the binding's."""
+    import torch
+    res = {}
+    for name, (n, m) in {"decode": (B, 1), "prefill_chunk": (2048, 2)}.items():
+        inp = G.kv_write_inputs(3, n, m, d, device=dev)
+        bf = lambda t: None if t is None else t.view(torch.bfloat16)
+        codes = torch.empty((n, 256), dtype=torch.uint8, device=dev)
+        scales = torch.empty((n, 16), dtype=torch.uint8, device=dev)
+        k = torch.empty((n, 128), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(csa.kv_write_workspace_bytes(n, m, d), dtype=torch.uint8, device=dev)
+
+        def call():
+            csa.csa2_kv_write(bf(inp["h"]), bf(inp["w_kv"]), bf(inp["w_ik"]), inp["pos"], m=m, w_z=bf(inp["w_z"]),
+                              kv_codes=codes, kv_scales=scales, k_out=k, workspace=ws)
+
+        call()
+        torch.cuda.synchronize()
+        ref = (codes.clone(), scales.clone(), k.clone())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call()
+        g.replay()
+        torch.cuda.synchronize()
+        same = all(torch.equal(a, b) for a, b in zip(ref, (codes, scales, k)))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        nproj = 2 if m > 1 else 1
+        byts = n * m * d * 2 + nproj * 512 * d * 2 + 128 * 512 * 2 + 4 * n + n * (256 + 16 + 256)
+        flops = 2 * n * m * d * 512 * nproj + 2 * n * 512 * 128
+        res[name] = {"entries": n, "m": m, "d": d, "us": us, "algorithmic_bytes": byts,
+                     "GBps": byts / (us * 1e-6) / 1e9, "frac_hbm": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+                     "flops": flops, "TFLOPs": flops / (us * 1e-6) / 1e12,
+                     "frac_mfma_bf16": flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                     "graph_replay_matches_eager": same}
+        del g
+    res["formats"] = "MXFP4 cache (E2M1 + E8M0/32), bf16 indexer K"
+    return res
 
 
 def cpu_baseline(c, G, min_seconds=10.0, max_seconds=30.0):

@@ -9,45 +9,47 @@
 // 64 channels at the entry's position (reading sec. 4.3); the cache is
 // quantised after RoPE (report sec. 2.4.4).
 //
-// Two kernels.
-//  kvw_proj_kernel   C (and Z) on v_mfma_f32_16x16x32_bf16.  A wave owns 16
-//                    tokens x 64 channels over a slice of the hidden
-//                    dimension.  Many tokens (prefill): the 4 waves of a block
-//                    take 4 token tiles of one channel chunk and share its
-//                    weight rows through the caches.  Few tokens (decode): the
-//                    hidden dimension is split over waves and blocks so that
-//                    the weight stream (512 x d x 2 B per projection) is in
-//                    flight on the whole GPU at once; per-slice sums go to the
-//                    workspace.
-//  kvw_finish_kernel one block per (16-token tile, 64-channel chunk): adds the
-//                    slice sums, pools, rotates and quantises the chunk (64
-//                    channels hold whole 16- and 32-channel scale blocks),
-//                    and writes the chunk's share of indexer K.  The last of
-//                    the 8 chunk blocks of a tile (an arrival counter, zeroed
-//                    by the projection kernel) adds the 8 shares in chunk order
-//                    and writes K.  Every sum has a fixed order: results do not
-//                    depend on scheduling.
+// Two kernels, no cross-block synchronisation inside either:
+//  projection  C (and Z) on v_mfma_f32_16x16x32_bf16.
+//              Many tokens (prefill, kvw_proj_many_kernel): an LDS-tiled GEMM,
+//              128 tokens x 128 channels per block, double-buffered k steps.
+//              Few tokens (decode, kvw_proj_few_kernel): the weight stream
+//              (512 x d x 2 B per projection) must be in flight on the whole
+//              GPU at once, so the hidden dimension is split: the 4 waves of
+//              a block take 4 sub-slices and add them in LDS, and blocks take
+//              slices whose sums go to the workspace.
+//  kvw_finish_kernel  one block per tile of FT tokens (FT/m whole entries):
+//              adds the slice sums in slice order, pools, rotates, quantises
+//              the cache rows and computes indexer K from the pooled entries
+//              held in LDS.  Every sum has a fixed order: the results do not
+//              depend on scheduling.
 #include "mxfp4.h"
 
 namespace csa2 {
 
-constexpr int kKvwTok = 16;                     // tokens per tile (MFMA rows)
-constexpr int kKvwChunk = 64;                   // channels per chunk
+constexpr int kKvwTok = 16;                     // tokens per MFMA tile
+constexpr int kKvwChunk = 64;                   // channels per projection wave
 constexpr int kKvwChunks = kDim / kKvwChunk;    // 8
 constexpr int kKvwThreads = 256;                // projection block: 4 waves
-constexpr int kKvwFinThreads = 1024;            // finish block: 16 waves, one token each
-constexpr int kKvwMinSlice = 128;               // smallest hidden-dimension slice per wave
-constexpr int kKvwWantWaves = 1024;             // projection waves aimed at for few tokens
-constexpr int kKvwWikStride = kKvwChunk + 2;    // LDS row of W_ik (bf16): 33 words, rows on distinct banks
+constexpr int kGemmM = 128, kGemmN = 128, kGemmK = 64;  // many-token projection tile
+constexpr int kGemmLd = kGemmK + 8;             // LDS row (bf16): 144 B, rows start on different banks
+constexpr int kKvwFinThreads = 1024;            // finish block
+constexpr int kKvwFinMaxTok = 16;               // largest finish tile (many tokens)
+constexpr int kKvwFewMaxTok = 8;                // largest finish tile (few tokens)
+constexpr int kKvwFewMaxSplit = 8;              // most hidden-dimension slices (few tokens)
+constexpr int kKvwMinWaveSlice = 128;           // smallest hidden-dimension slice per wave (few tokens)
+constexpr int kKvwWantWaves = 1024;             // projection waves aimed at (few tokens)
+constexpr int kKvwManyMin = 1024;               // tokens from which the many-token projection is used
 
 struct KvwPlan {
   int64_t n_tok;
-  int tok_tiles;
-  int tw;       // token tiles per projection block (4) or 1 (waves split the hidden dimension)
-  int ksplit;   // hidden-dimension slices
-  int kper;     // slice length (multiple of 32)
-  int gx, gz;   // projection grid x and z (y = chunks)
-  size_t off_z, off_kp, off_cnt, total;  // workspace layout (bytes)
+  bool many;
+  int tok_tiles;  // 16-token tiles
+  int ksplit;     // hidden-dimension slices (blocks along z), 1 for many tokens
+  int kper;       // slice length per block (multiple of 128 for few tokens)
+  int ft;         // finish tile (tokens): 16 for many tokens, max(4, m) otherwise
+  int fin_blocks;
+  size_t off_z, total;  // workspace layout (bytes)
 };
 
 static size_t kvw_round(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -56,122 +58,229 @@ static KvwPlan kvw_plan(int32_t n_ent, int32_t m, int32_t d) {
   KvwPlan p;
   p.n_tok = (int64_t)n_ent * m;
   p.tok_tiles = (int)((p.n_tok + kKvwTok - 1) / kKvwTok);
-  const int steps = d / 32;
-  if (p.tok_tiles >= 64) {
-    p.tw = 4;
+  p.many = p.n_tok >= kKvwManyMin;
+  if (p.many) {
     p.ksplit = 1;
     p.kper = d;
-    p.gx = (p.tok_tiles + 3) / 4;
-    p.gz = 1;
+    p.ft = kKvwFinMaxTok;
   } else {
-    p.tw = 1;
-    int64_t ks = (kKvwWantWaves + (int64_t)p.tok_tiles * kKvwChunks - 1) / ((int64_t)p.tok_tiles * kKvwChunks);
-    const int kmax = d / kKvwMinSlice > 0 ? d / kKvwMinSlice : 1;
+    // blocks along the hidden dimension: ~kKvwWantWaves waves, each at least kKvwMinWaveSlice long
+    const int64_t per_split = (int64_t)p.tok_tiles * kKvwChunks * 4;
+    int64_t ks = (kKvwWantWaves + per_split - 1) / per_split;
+    const int64_t kmax = d / (4 * kKvwMinWaveSlice) > 0 ? d / (4 * kKvwMinWaveSlice) : 1;
     if (ks > kmax) ks = kmax;
-    if (ks < 1) ks = 1;
-    p.kper = (int)((steps + ks - 1) / ks) * 32;
-    p.ksplit = (d + p.kper - 1) / p.kper;  // every slice non-empty
-    p.gx = p.tok_tiles;
-    p.gz = (p.ksplit + 3) / 4;
+    if (ks > kKvwFewMaxSplit) ks = kKvwFewMaxSplit;
+    const int q = (d + 127) / 128;  // 128-wide groups
+    p.kper = (int)((q + ks - 1) / ks) * 128;
+    p.ksplit = (d + p.kper - 1) / p.kper;
+    p.ft = m > 4 ? m : 4;
   }
+  p.fin_blocks = (int)((p.n_tok + p.ft - 1) / p.ft);
   const size_t part = (size_t)p.ksplit * p.n_tok * kDim * sizeof(float);
   p.off_z = kvw_round(part);
-  p.off_kp = p.off_z + (m > 1 ? kvw_round(part) : 0);
-  p.off_cnt = p.off_kp + kvw_round((size_t)kKvwChunks * n_ent * kIdxDim * sizeof(float));
-  p.total = p.off_cnt + kvw_round((size_t)p.tok_tiles * sizeof(uint32_t));
+  p.total = p.off_z + (m > 1 ? kvw_round(part) : 0);
   return p;
 }
 
-// part[split][token][channel]: the sum over slice `split` of h[token][k] * w[channel][k]
-// (C), and at part + zoff the same for W_z.  Register i of lane l holds token 4(l/16) + i of
-// the tile and channel l % 16 of each 16-channel group.
-__global__ __launch_bounds__(kKvwThreads) void kvw_proj_kernel(const uint16_t* __restrict__ h,
-                                                               const uint16_t* __restrict__ w_kv,
-                                                               const uint16_t* __restrict__ w_z, int64_t n_tok,
-                                                               int32_t d, int tok_tiles, int tw, int ksplit,
-                                                               int kper, float* __restrict__ part, size_t zoff,
-                                                               uint32_t* __restrict__ cnt) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tile = tw == 4 ? 4 * blockIdx.x + wave : blockIdx.x;
-  const int split = tw == 4 ? blockIdx.z : 4 * blockIdx.z + wave;
-  if (tile >= tok_tiles || split >= ksplit) return;
-  if (blockIdx.y == 0 && split == 0 && lane == 0) cnt[tile] = 0u;  // arrival counter of the finish kernel
-  const int r16 = lane & 15, g = lane >> 4;
-  const int64_t tok = (int64_t)tile * kKvwTok + r16;
-  const int ch0 = blockIdx.y * kKvwChunk + r16;
-  const int k0 = split * kper;
-  const int k1 = k0 + kper < d ? k0 + kper : d;
-  // rows past n_tok read the last token again; their sums are not stored
-  const uint16_t* hr = h + (size_t)(tok < n_tok ? tok : n_tok - 1) * d + 8 * g;
-  const uint16_t* wr = w_kv + (size_t)ch0 * d + 8 * g;
-  const uint16_t* zr = w_z ? w_z + (size_t)ch0 * d + 8 * g : nullptr;
-  const size_t g16 = (size_t)16 * d;  // next 16-channel group
-  floatx4 acc[4], accz[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
-    accz[c] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
+// One 32-wide step of a wave's 16-token tile(s) x 64 channels: A rows from hr
+// (token rows of kTT tiles, 16 * d apart), B rows from wr / zr (16-channel
+// groups 16 * d apart).
+template <int kTT, bool kZ>
+__device__ __forceinline__ void proj_steps(const uint16_t* const* hr, const uint16_t* wr, const uint16_t* zr,
+                                           size_t g16, int k0, int k1, floatx4 (&acc)[kTT][4],
+                                           floatx4 (&accz)[kTT][4]) {
+  constexpr int U = kZ ? 2 : (kTT == 1 ? 4 : 2);  // steps per group of loads
   int k = k0;
-  if (zr) {
-    for (; k + 64 <= k1; k += 64) {
-      uint4 a[2], b[2][4], z[2][4];
+  for (; k + 32 * U <= k1; k += 32 * U) {
+    uint4 a[U][kTT], b[U][4], z[U][kZ ? 4 : 1];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        a[u] = *reinterpret_cast<const uint4*>(hr + k + 32 * u);
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int t = 0; t < kTT; ++t) a[u][t] = *reinterpret_cast<const uint4*>(hr[t] + k + 32 * u);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        b[u][c] = *reinterpret_cast<const uint4*>(wr + c * g16 + k + 32 * u);
+        if constexpr (kZ) z[u][c] = *reinterpret_cast<const uint4*>(zr + c * g16 + k + 32 * u);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the group in flight before the first product
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int t = 0; t < kTT; ++t)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          b[u][c] = *reinterpret_cast<const uint4*>(wr + c * g16 + k + 32 * u);
-          z[u][c] = *reinterpret_cast<const uint4*>(zr + c * g16 + k + 32 * u);
+          acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][t]), as_bf16x8(b[u][c]), acc[t][c], 0,
+                                                              0, 0);
+          if constexpr (kZ)
+            accz[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u][t]), as_bf16x8(z[u][c]), accz[t][c],
+                                                                 0, 0, 0);
         }
-      }
-      __builtin_amdgcn_sched_barrier(0);  // every load of the step group in flight before the first product
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u]), as_bf16x8(b[u][c]), acc[c], 0, 0, 0);
-          accz[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u]), as_bf16x8(z[u][c]), accz[c], 0, 0, 0);
-        }
-    }
-  } else {
-    for (; k + 128 <= k1; k += 128) {
-      uint4 a[4], b[4][4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[u] = *reinterpret_cast<const uint4*>(hr + k + 32 * u);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) b[u][c] = *reinterpret_cast<const uint4*>(wr + c * g16 + k + 32 * u);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[u]), as_bf16x8(b[u][c]), acc[c], 0, 0, 0);
-    }
   }
   for (; k < k1; k += 32) {
-    const uint4 a = *reinterpret_cast<const uint4*>(hr + k);
+    uint4 a[kTT];
+#pragma unroll
+    for (int t = 0; t < kTT; ++t) a[t] = *reinterpret_cast<const uint4*>(hr[t] + k);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint4 b = *reinterpret_cast<const uint4*>(wr + c * g16 + k);
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), acc[c], 0, 0, 0);
-      if (zr) {
+#pragma unroll
+      for (int t = 0; t < kTT; ++t)
+        acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[t]), as_bf16x8(b), acc[t][c], 0, 0, 0);
+      if constexpr (kZ) {
         const uint4 z = *reinterpret_cast<const uint4*>(zr + c * g16 + k);
-        accz[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(z), accz[c], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < kTT; ++t)
+          accz[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[t]), as_bf16x8(z), accz[t][c], 0, 0, 0);
       }
     }
   }
-  float* out = part + (size_t)split * n_tok * kDim;
+}
+
+// part[split][token][channel] (and at part + zoff for Z): register i of lane l
+// of tile t holds token 16t + 4(l/16) + i and channel l % 16 of each 16-channel group.
+
+// Many tokens: an LDS-tiled GEMM.  Block tile 128 tokens x 128 output channels
+// (C channels, then Z channels for m > 1), k in steps of 64 through two LDS
+// buffers (the next step's global loads are in flight while the current one is
+// multiplied); the 4 waves hold 64 x 64 sub-tiles (4 x 4 MFMA tiles each).
+// grid (ceil(n_tok / 128), 512 * projections / 128).
+template <bool kZ>
+__global__ __launch_bounds__(kKvwThreads) void kvw_proj_many_kernel(const uint16_t* __restrict__ h,
+                                                                    const uint16_t* __restrict__ w_kv,
+                                                                    const uint16_t* __restrict__ w_z, int64_t n_tok,
+                                                                    int32_t d, float* __restrict__ part, size_t zoff) {
+  __shared__ __align__(16) uint16_t As[2][kGemmM * kGemmLd];
+  __shared__ __align__(16) uint16_t Bs[2][kGemmN * kGemmLd];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, r16 = lane & 15, g = lane >> 4;
+  const int64_t m0 = (int64_t)blockIdx.x * kGemmM;
+  const int n0 = blockIdx.y * kGemmN;  // 0..1023: C channels, then Z channels
+  const uint16_t* W = (kZ && n0 >= kDim) ? w_z : w_kv;
+  const int c0 = n0 & (kDim - 1);
+  // global -> LDS: thread tid moves 16 B of rows tid / 8 + 32 j (j < 4), columns 8 (tid % 8) ..
+  const int lr = tid >> 3, lc = 8 * (tid & 7);
+  const uint16_t* ha[4];
+  const uint16_t* wb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t row = m0 + lr + 32 * j;  // rows past n_tok read the last token; not stored
+    ha[j] = h + (size_t)(row < n_tok ? row : n_tok - 1) * d + lc;
+    wb[j] = W + (size_t)(c0 + lr + 32 * j) * d + lc;
+  }
+  uint4 ra[4], rb[4];
+  auto gload = [&](int k) {
+    const bool in = k + lc < d;  // d is a multiple of 32: a 16-byte piece is wholly in or out
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ra[j] = in ? *reinterpret_cast<const uint4*>(ha[j] + k) : uint4{0u, 0u, 0u, 0u};
+      rb[j] = in ? *reinterpret_cast<const uint4*>(wb[j] + k) : uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<uint4*>(&As[buf][(lr + 32 * j) * kGemmLd + lc]) = ra[j];
+      *reinterpret_cast<uint4*>(&Bs[buf][(lr + 32 * j) * kGemmLd + lc]) = rb[j];
+    }
+  };
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  const int nk = (d + kGemmK - 1) / kGemmK;
+  for (int t = 0; t < nk; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < nk) gload((t + 1) * kGemmK);
+#pragma unroll
+    for (int ks = 0; ks < kGemmK / 32; ++ks) {
+      uint4 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        af[i] = *reinterpret_cast<const uint4*>(&As[buf][(64 * wm + 16 * i + r16) * kGemmLd + 32 * ks + 8 * g]);
+        bf[i] = *reinterpret_cast<const uint4*>(&Bs[buf][(64 * wn + 16 * i + r16) * kGemmLd + 32 * ks + 8 * g]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[i]), as_bf16x8(bf[j]), acc[i][j], 0, 0, 0);
+    }
+    // the other buffer was last read in step t - 1, before the barrier that ended it
+    if (t + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+  float* out = (kZ && n0 >= kDim) ? part + zoff : part;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t tk = m0 + 64 * wm + 16 * i + 4 * g + r;
+      if (tk < n_tok) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[(size_t)tk * kDim + c0 + 64 * wn + 16 * j + r16] = acc[i][j][r];
+      }
+    }
+}
+
+// Few tokens: grid (tok_tiles, 8, ksplit); the block's slice [z * kper, +kper) is
+// cut into 4 sub-slices (multiples of 32), one per wave, added in LDS in wave order.
+template <bool kZ>
+__global__ __launch_bounds__(kKvwThreads) void kvw_proj_few_kernel(const uint16_t* __restrict__ h,
+                                                                   const uint16_t* __restrict__ w_kv,
+                                                                   const uint16_t* __restrict__ w_z, int64_t n_tok,
+                                                                   int32_t d, int kper, float* __restrict__ part,
+                                                                   size_t zoff) {
+  __shared__ float red[3][kZ ? 2 : 1][16][64];  // waves 1..3: their 16 x 4 x 4 (+ Z) sums by lane
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t tok = (int64_t)blockIdx.x * kKvwTok + r16;
+  const int ch0 = blockIdx.y * kKvwChunk + r16;
+  const int sub = kper / 4;
+  int k0 = blockIdx.z * kper + wave * sub;
+  int k1 = k0 + sub;
+  if (k1 > d) k1 = d;
+  if (k0 > k1) k0 = k1;
+  const uint16_t* hr[1] = {h + (size_t)(tok < n_tok ? tok : n_tok - 1) * d + 8 * g};
+  const uint16_t* wr = w_kv + (size_t)ch0 * d + 8 * g;
+  const uint16_t* zr = kZ ? w_z + (size_t)ch0 * d + 8 * g : nullptr;
+  floatx4 acc[1][4], accz[1][4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[0][c] = accz[0][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+  proj_steps<1, kZ>(hr, wr, zr, (size_t)16 * d, k0, k1, acc, accz);
+  if (wave > 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        red[wave - 1][0][4 * c + i][lane] = acc[0][c][i];
+        if constexpr (kZ) red[wave - 1][kZ ? 1 : 0][4 * c + i][lane] = accz[0][c][i];
+      }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[0][c][i] += red[w][0][4 * c + i][lane];
+        if constexpr (kZ) accz[0][c][i] += red[w][kZ ? 1 : 0][4 * c + i][lane];
+      }
+  float* out = part + (size_t)blockIdx.z * n_tok * kDim;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t t = (int64_t)tile * kKvwTok + 4 * g + i;
-    if (t < n_tok) {
+    const int64_t tk = (int64_t)blockIdx.x * kKvwTok + 4 * g + i;
+    if (tk < n_tok) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        out[(size_t)t * kDim + ch0 + 16 * c] = acc[c][i];
-        if (zr) out[zoff + (size_t)t * kDim + ch0 + 16 * c] = accz[c][i];
+        out[(size_t)tk * kDim + ch0 + 16 * c] = acc[0][c][i];
+        if constexpr (kZ) out[zoff + (size_t)tk * kDim + ch0 + 16 * c] = accz[0][c][i];
       }
     }
   }
@@ -250,133 +359,149 @@ __device__ __forceinline__ uint32_t e4m3_quant_lane(float v, uint32_t* scale) {
   return code | (dpp_u32<kDppXor1>(code) << 4);
 }
 
+// One block per tile of ft tokens (ft / m whole entries).  kFew: ft <= 8 and up
+// to kKvwFewMaxSplit slices; otherwise ft <= 16 and one slice.
+template <bool kFew>
 __global__ __launch_bounds__(kKvwFinThreads) void kvw_finish_kernel(
-    const float* __restrict__ part, size_t zoff, int ksplit, int64_t n_tok, int m,
+    const float* __restrict__ part, size_t zoff, int ksplit, int64_t n_tok, int m, int ft,
     const uint16_t* __restrict__ w_ik, const int32_t* __restrict__ pos, double log2_base, int kv_format,
     uint8_t* __restrict__ kv_codes, uint8_t* __restrict__ kv_scales, int k_format, void* __restrict__ k_out,
-    uint8_t* __restrict__ k_scales, float* __restrict__ kp, int32_t n_ent, uint32_t* __restrict__ cnt) {
-  __shared__ float cz[2][kKvwTok][kKvwChunk];
-  __shared__ float pre[kKvwTok][kKvwChunk];
-  __shared__ uint16_t wik[kIdxDim * kKvwWikStride];
-  __shared__ int is_last;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tile = blockIdx.x, chunk = blockIdx.y;
-  const int64_t t0 = (int64_t)tile * kKvwTok;
-  const int valid = n_tok - t0 < kKvwTok ? (int)(n_tok - t0) : kKvwTok;
-  const int n_e = valid / m;            // entries of this tile (whole: m divides 16)
-  const int e0 = tile * (kKvwTok / m);  // first entry of the tile
-  {
-    // W_ik columns of this chunk: row o, channels chunk*64 .. +63 -> LDS row o
-    const int o = tid >> 3, seg = tid & 7;
-    const uint4 w = *reinterpret_cast<const uint4*>(w_ik + (size_t)o * kDim + chunk * kKvwChunk + 8 * seg);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(wik + o * kKvwWikStride + 8 * seg);
-    dst[0] = w.x;
-    dst[1] = w.y;
-    dst[2] = w.z;
-    dst[3] = w.w;
-  }
-  // slice sums: wave = token of the tile, lane = channel of the chunk
-  if (wave < valid) {
-    const size_t off = (size_t)(t0 + wave) * kDim + chunk * kKvwChunk + lane;
-    const size_t sstride = (size_t)n_tok * kDim;
-    float c = 0.f, z = 0.f;
-    int s = 0;
-    for (; s + 8 <= ksplit; s += 8) {
-      float v[8], u[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v[i] = part[(size_t)(s + i) * sstride + off];
-        u[i] = m > 1 ? part[zoff + (size_t)(s + i) * sstride + off] : 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        c += v[i];
-        z += u[i];
-      }
-    }
-    for (; s < ksplit; ++s) {
-      c += part[(size_t)s * sstride + off];
-      if (m > 1) z += part[zoff + (size_t)s * sstride + off];
-    }
-    cz[0][wave][lane] = c;
-    cz[1][wave][lane] = z;
-  }
-  __syncthreads();
-  // pooling, RoPE, quantisation: wave = entry of the tile, lane = channel
-  if (wave < n_e) {
-    const int e = e0 + wave;
-    float v;
-    if (m == 1) {
-      v = cz[0][wave][lane];
-    } else {
-      float zmax = -INFINITY;
-      for (int j = 0; j < m; ++j) zmax = fmaxf(zmax, cz[1][wave * m + j][lane]);
-      float den = 0.f, num = 0.f;
-      for (int j = 0; j < m; ++j) {
-        const float p = expf(cz[1][wave * m + j][lane] - zmax);
-        den += p;
-        num += p * cz[0][wave * m + j][lane];
-      }
-      v = num / den;
-    }
-    pre[wave][lane] = v;
-    if (chunk == kKvwChunks - 1) {
-      // channel 448 + lane: pair j = lane / 2 with partner lane ^ 1
-      const int j = lane >> 1;
-      const double rev = (double)pos[e] * exp2(-log2_base * (j / 32.0)) * 0.15915494309189535;
-      const float fr = (float)(rev - rint(rev));
-      const float cs = __builtin_amdgcn_cosf(fr), sn = __builtin_amdgcn_sinf(fr);
-      const float o = dpp_f32<kDppXor1>(v);
-      v = (lane & 1) ? o * sn + v * cs : v * cs - o * sn;
-    }
-    uint32_t sc;
-    const size_t cb = (size_t)e * (kDim / 2) + chunk * (kKvwChunk / 2) + (lane >> 1);
-    if (kv_format == CSA2_KV_MXFP4) {
-      const uint32_t byte = mx_quant_lane(v, &sc);
-      if (!(lane & 1)) kv_codes[cb] = (uint8_t)byte;
-      if (!(lane & 31)) kv_scales[(size_t)e * (kDim / 32) + chunk * 2 + (lane >> 5)] = (uint8_t)sc;
-    } else {
-      const uint32_t byte = e4m3_quant_lane(v, &sc);
-      if (!(lane & 1)) kv_codes[cb] = (uint8_t)byte;
-      if (!(lane & 15)) kv_scales[(size_t)e * (kDim / 16) + chunk * 4 + (lane >> 4)] = (uint8_t)sc;
-    }
-  }
-  __syncthreads();
-  // this chunk's share of indexer K: thread (o, g) for entries g, g + 8
-  {
-    const int o = tid & (kIdxDim - 1), g = tid >> 7;
-    const uint32_t* wr = reinterpret_cast<const uint32_t*>(wik + o * kKvwWikStride);
-    for (int el = g; el < n_e; el += 8) {
-      float acc = 0.f;
-#pragma unroll 8
-      for (int c2 = 0; c2 < kKvwChunk / 2; ++c2) {
-        const uint32_t w = wr[c2];
-        acc = fmaf(pre[el][2 * c2], bf16lo(w), acc);
-        acc = fmaf(pre[el][2 * c2 + 1], bf16hi(w), acc);
-      }
-      kp[((size_t)chunk * n_ent + e0 + el) * kIdxDim + o] = acc;
-    }
-  }
-  // the last chunk block of the tile adds the shares in chunk order
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) is_last = atomicAdd(&cnt[tile], 1u) == kKvwChunks - 1;
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
+    uint8_t* __restrict__ k_scales) {
+  constexpr int kFt = kFew ? kKvwFewMaxTok : kKvwFinMaxTok;   // largest tile
+  constexpr int kS = kFew ? kKvwFewMaxSplit : 1;              // largest slice count
+  constexpr int kP = kFt * kDim / kKvwFinThreads;             // (token, channel) pairs per thread
+  // slice sums of C and Z; after pooling the same memory holds the K partials [8][kFt][128]
+  __shared__ float sc[2][kFt][kDim];
+  __shared__ __align__(16) float pre[kFt][kDim];  // pooled entries before RoPE
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t t0 = (int64_t)blockIdx.x * ft;
+  const int valid = n_tok - t0 < ft ? (int)(n_tok - t0) : ft;
+  const int n_e = valid / m;  // m divides ft
+  const int64_t e0 = (int64_t)blockIdx.x * (ft / m);
+  // W_ik row o, channels 64 g .. 64 g + 63 (for the K stage), loaded first
   const int o = tid & (kIdxDim - 1), g = tid >> 7;
-  for (int el = g; el < n_e; el += 8) {  // uniform per wave: a wave holds 64 outputs of one entry
-    const int e = e0 + el;
-    float kv = 0.f;
+  uint4 wq[8];
 #pragma unroll
-    for (int c = 0; c < kKvwChunks; ++c) kv += __builtin_nontemporal_load(&kp[((size_t)c * n_ent + e) * kIdxDim + o]);
-    if (k_format == CSA2_K_BF16) {
-      reinterpret_cast<uint16_t*>(k_out)[(size_t)e * kIdxDim + o] = (uint16_t)f32_to_bf16_rne(kv);
-    } else {
-      uint32_t sc;
-      const uint32_t byte = mx_quant_lane(kv, &sc);
-      if (!(lane & 1)) reinterpret_cast<uint8_t*>(k_out)[(size_t)e * kMxRowBytes + (o >> 1)] = (uint8_t)byte;
-      if (!(lane & 31)) k_scales[(size_t)e * kMxScales + (o >> 5)] = (uint8_t)sc;
+  for (int i = 0; i < 8; ++i) wq[i] = *reinterpret_cast<const uint4*>(w_ik + (size_t)o * kDim + 64 * g + 8 * i);
+  // slice sums of pair p = (token p / 512, channel p % 512), slices in order.  Every
+  // load is issued before the first add: addresses are clamped into range and the
+  // values past the tile or the slice count are dropped.
+  {
+    const size_t sstride = (size_t)n_tok * kDim;
+    const float* pc = part + (size_t)t0 * kDim;
+    const int lim = valid * kDim;
+    float v[kS][kP], u[kS][kP];
+#pragma unroll
+    for (int s = 0; s < kS; ++s)
+#pragma unroll
+      for (int i = 0; i < kP; ++i) {
+        const int p = tid + kKvwFinThreads * i < lim ? tid + kKvwFinThreads * i : lim - 1;
+        const size_t off = (size_t)(s < ksplit ? s : 0) * sstride + p;
+        v[s][i] = pc[off];
+        u[s][i] = m > 1 ? pc[zoff + off] : 0.f;
+      }
+#pragma unroll
+    for (int i = 0; i < kP; ++i) {
+      const int p = tid + kKvwFinThreads * i;
+      float c = v[0][i], z = u[0][i];
+#pragma unroll
+      for (int s = 1; s < kS; ++s)
+        if (s < ksplit) {
+          c += v[s][i];
+          z += u[s][i];
+        }
+      if (p < lim) {
+        sc[0][p >> 9][p & (kDim - 1)] = c;
+        sc[1][p >> 9][p & (kDim - 1)] = z;
+      }
+    }
+  }
+  __syncthreads();
+  // pooling, RoPE, quantisation: pair p = (entry p / 512, channel p % 512); a wave holds
+  // 64 consecutive channels of one entry
+#pragma unroll
+  for (int i = 0; i < kP; ++i) {
+    const int p = tid + kKvwFinThreads * i;
+    if (p < n_e * kDim) {  // uniform per wave
+      const int el = p >> 9, ch = p & (kDim - 1);
+      const int64_t e = e0 + el;
+      float v;
+      if (m == 1) {
+        v = sc[0][el][ch];
+      } else {
+        float zmax = -INFINITY;
+        for (int j = 0; j < m; ++j) zmax = fmaxf(zmax, sc[1][el * m + j][ch]);
+        float den = 0.f, num = 0.f;
+        for (int j = 0; j < m; ++j) {
+          const float w = expf(sc[1][el * m + j][ch] - zmax);
+          den += w;
+          num += w * sc[0][el * m + j][ch];
+        }
+        v = num / den;
+      }
+      pre[el][ch] = v;
+      if (ch >= kDim - 64) {
+        // channel 448 + 2j + (lane & 1): pair j with partner lane ^ 1
+        const int j = (ch - (kDim - 64)) >> 1;
+        const double rev = (double)pos[e] * exp2(-log2_base * (j / 32.0)) * 0.15915494309189535;
+        const float fr = (float)(rev - rint(rev));
+        const float cs = __builtin_amdgcn_cosf(fr), sn = __builtin_amdgcn_sinf(fr);
+        const float ov = dpp_f32<kDppXor1>(v);
+        v = (lane & 1) ? ov * sn + v * cs : v * cs - ov * sn;
+      }
+      uint32_t scl;
+      const size_t cb = (size_t)e * (kDim / 2) + (ch >> 1);
+      if (kv_format == CSA2_KV_MXFP4) {
+        const uint32_t byte = mx_quant_lane(v, &scl);
+        if (!(lane & 1)) kv_codes[cb] = (uint8_t)byte;
+        if (!(lane & 31)) kv_scales[(size_t)e * (kDim / 32) + (ch >> 5)] = (uint8_t)scl;
+      } else {
+        const uint32_t byte = e4m3_quant_lane(v, &scl);
+        if (!(lane & 1)) kv_codes[cb] = (uint8_t)byte;
+        if (!(lane & 15)) kv_scales[(size_t)e * (kDim / 16) + (ch >> 4)] = (uint8_t)scl;
+      }
+    }
+  }
+  __syncthreads();
+  // indexer K: thread (o, g) adds channels 64 g .. +63 for every entry of the tile
+  float (*kred)[kFt][kIdxDim] = reinterpret_cast<float (*)[kFt][kIdxDim]>(&sc[0][0][0]);
+  static_assert(sizeof(sc) == 8 * kFt * kIdxDim * sizeof(float), "K partials reuse the slice-sum memory");
+  for (int el = 0; el < n_e; ++el) {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 x0 = *reinterpret_cast<const float4*>(&pre[el][64 * g + 8 * i]);
+      const float4 x1 = *reinterpret_cast<const float4*>(&pre[el][64 * g + 8 * i + 4]);
+      a = fmaf(x0.x, bf16lo(wq[i].x), a);
+      a = fmaf(x0.y, bf16hi(wq[i].x), a);
+      a = fmaf(x0.z, bf16lo(wq[i].y), a);
+      a = fmaf(x0.w, bf16hi(wq[i].y), a);
+      a = fmaf(x1.x, bf16lo(wq[i].z), a);
+      a = fmaf(x1.y, bf16hi(wq[i].z), a);
+      a = fmaf(x1.z, bf16lo(wq[i].w), a);
+      a = fmaf(x1.w, bf16hi(wq[i].w), a);
+    }
+    kred[g][el][o] = a;
+  }
+  __syncthreads();
+  // K[e][o] = sum over the 8 channel groups in order; a wave holds 64 outputs of one entry
+#pragma unroll
+  for (int i = 0; i < (kFt * kIdxDim + kKvwFinThreads - 1) / kKvwFinThreads; ++i) {
+    const int q = tid + kKvwFinThreads * i;
+    const int el = q >> 7, oo = q & (kIdxDim - 1);
+    if (el < n_e) {  // uniform per wave
+      float kv = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < 8; ++gg) kv += kred[gg][el][oo];
+      const int64_t e = e0 + el;
+      if (k_format == CSA2_K_BF16) {
+        reinterpret_cast<uint16_t*>(k_out)[(size_t)e * kIdxDim + oo] = (uint16_t)f32_to_bf16_rne(kv);
+      } else {
+        uint32_t scl;
+        const uint32_t byte = mx_quant_lane(kv, &scl);
+        if (!(lane & 1)) reinterpret_cast<uint8_t*>(k_out)[(size_t)e * kMxRowBytes + (oo >> 1)] = (uint8_t)byte;
+        if (!(lane & 31)) k_scales[(size_t)e * kMxScales + (oo >> 5)] = (uint8_t)scl;
+      }
     }
   }
 }
@@ -414,19 +539,31 @@ extern "C" csa2_status csa2_kv_write(const void* h, const void* w_kv, const void
   const KvwPlan p = kvw_plan(n_ent, m, d);
   if (!workspace || !aligned16(workspace) || workspace_bytes < p.total) return CSA2_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)hip_stream;
-  char* ws = (char*)workspace;
-  float* part = (float*)ws;
+  float* part = (float*)workspace;
   const size_t zoff = p.off_z / sizeof(float);
-  float* kp = (float*)(ws + p.off_kp);
-  uint32_t* cnt = (uint32_t*)(ws + p.off_cnt);
+  const uint16_t *hh = (const uint16_t*)h, *wk = (const uint16_t*)w_kv, *wz = (const uint16_t*)w_z;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(kvw_proj_kernel, dim3(p.gx, kKvwChunks, p.gz), dim3(kKvwThreads), 0, st, (const uint16_t*)h,
-                     (const uint16_t*)w_kv, m > 1 ? (const uint16_t*)w_z : nullptr, p.n_tok, d, p.tok_tiles, p.tw,
-                     p.ksplit, p.kper, part, zoff, cnt);
-  hipLaunchKernelGGL(kvw_finish_kernel, dim3(p.tok_tiles, kKvwChunks), dim3(kKvwFinThreads), 0, st,
-                     (const float*)part, zoff, p.ksplit, p.n_tok, m, (const uint16_t*)w_ik, pos,
-                     log2((double)rope_base), kv_format, kv_codes, kv_scales, k_format, k_out, k_scales, kp, n_ent,
-                     cnt);
+  if (p.many) {
+    const dim3 grid((unsigned)((p.n_tok + kGemmM - 1) / kGemmM), (m > 1 ? 2 : 1) * kDim / kGemmN);
+    if (m > 1)
+      hipLaunchKernelGGL(kvw_proj_many_kernel<true>, grid, dim3(kKvwThreads), 0, st, hh, wk, wz, p.n_tok, d, part,
+                         zoff);
+    else
+      hipLaunchKernelGGL(kvw_proj_many_kernel<false>, grid, dim3(kKvwThreads), 0, st, hh, wk, nullptr, p.n_tok, d,
+                         part, zoff);
+  } else {
+    const dim3 grid(p.tok_tiles, kKvwChunks, p.ksplit);
+    if (m > 1)
+      hipLaunchKernelGGL(kvw_proj_few_kernel<true>, grid, dim3(kKvwThreads), 0, st, hh, wk, wz, p.n_tok, d, p.kper,
+                         part, zoff);
+    else
+      hipLaunchKernelGGL(kvw_proj_few_kernel<false>, grid, dim3(kKvwThreads), 0, st, hh, wk, nullptr, p.n_tok, d,
+                         p.kper, part, zoff);
+  }
+  auto fin = p.many ? kvw_finish_kernel<false> : kvw_finish_kernel<true>;
+  hipLaunchKernelGGL(fin, dim3(p.fin_blocks), dim3(kKvwFinThreads), 0, st, (const float*)part, zoff, p.ksplit,
+                     p.n_tok, m, p.ft, (const uint16_t*)w_ik, pos, log2((double)rope_base), kv_format, kv_codes,
+                     kv_scales, k_format, k_out, k_scales);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   return CSA2_OK;
 }
