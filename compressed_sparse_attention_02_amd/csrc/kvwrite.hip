@@ -13,6 +13,9 @@
 //  projection  C (and Z) on v_mfma_f32_16x16x32_bf16.
 //              Many tokens (prefill, kvw_proj_many_kernel): an LDS-tiled GEMM,
 //              128 tokens x 128 channels per block, double-buffered k steps.
+//              (Measured on 4096 x 5120 x 1024: 128 x 128 tiles with 4 or 8
+//              waves, 64 x 128 tiles, and global prefetch 2-4 steps ahead all
+//              land within 71-85 us; this layout was the fastest.)
 //              Few tokens (decode, kvw_proj_few_kernel): the weight stream
 //              (512 x d x 2 B per projection) must be in flight on the whole
 //              GPU at once, so the hidden dimension is split: the 4 waves of
@@ -33,6 +36,7 @@ constexpr int kKvwChunks = kDim / kKvwChunk;    // 8
 constexpr int kKvwThreads = 256;                // projection block: 4 waves
 constexpr int kGemmM = 128, kGemmN = 128, kGemmK = 64;  // many-token projection tile
 constexpr int kGemmLd = kGemmK + 8;             // LDS row (bf16): 144 B, rows start on different banks
+constexpr int kGemmThreads = 512;               // many-token projection block: 8 waves
 constexpr int kKvwFinThreads = 1024;            // finish block
 constexpr int kKvwFinMaxTok = 16;               // largest finish tile (many tokens)
 constexpr int kKvwFewMaxTok = 8;                // largest finish tile (few tokens)
@@ -143,86 +147,105 @@ __device__ __forceinline__ void proj_steps(const uint16_t* const* hr, const uint
 // Many tokens: an LDS-tiled GEMM.  Block tile 128 tokens x 128 output channels
 // (C channels, then Z channels for m > 1), k in steps of 64 through two LDS
 // buffers (the next step's global loads are in flight while the current one is
-// multiplied); the 4 waves hold 64 x 64 sub-tiles (4 x 4 MFMA tiles each).
+// multiplied); 8 waves in 2 x 4, each 64 tokens x 32 channels (4 x 2 MFMA
+// tiles), both 32-wide halves of a step read from LDS before the products.
 // grid (ceil(n_tok / 128), 512 * projections / 128).
+template <int PA, int PB>
+__device__ __forceinline__ void gemm_gload(uint4 (&ra)[PA], uint4 (&rb)[PB], const uint16_t* const (&ha)[PA],
+                                           const uint16_t* const (&wb)[PB], int k, bool in) {
+#pragma unroll
+  for (int j = 0; j < PA; ++j) ra[j] = in ? *reinterpret_cast<const uint4*>(ha[j] + k) : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < PB; ++j) rb[j] = in ? *reinterpret_cast<const uint4*>(wb[j] + k) : uint4{0u, 0u, 0u, 0u};
+}
+
+template <int PA, int PB>
+__device__ __forceinline__ void gemm_lstore(const uint4 (&ra)[PA], const uint4 (&rb)[PB], uint16_t* A, uint16_t* B,
+                                            int lr, int lc) {
+#pragma unroll
+  for (int j = 0; j < PA; ++j) *reinterpret_cast<uint4*>(&A[(lr + (kGemmThreads / 8) * j) * kGemmLd + lc]) = ra[j];
+#pragma unroll
+  for (int j = 0; j < PB; ++j) *reinterpret_cast<uint4*>(&B[(lr + (kGemmThreads / 8) * j) * kGemmLd + lc]) = rb[j];
+}
+
 template <bool kZ>
-__global__ __launch_bounds__(kKvwThreads) void kvw_proj_many_kernel(const uint16_t* __restrict__ h,
-                                                                    const uint16_t* __restrict__ w_kv,
-                                                                    const uint16_t* __restrict__ w_z, int64_t n_tok,
-                                                                    int32_t d, float* __restrict__ part, size_t zoff) {
+__global__ __launch_bounds__(kGemmThreads) void kvw_proj_many_kernel(const uint16_t* __restrict__ h,
+                                                                     const uint16_t* __restrict__ w_kv,
+                                                                     const uint16_t* __restrict__ w_z, int64_t n_tok,
+                                                                     int32_t d, float* __restrict__ part, size_t zoff) {
+  constexpr int PA = kGemmM * 8 / kGemmThreads, PB = kGemmN * 8 / kGemmThreads;  // 16-byte pieces per thread
+  constexpr int TI = 4, TJ = 2;                                                   // MFMA tiles per wave
   __shared__ __align__(16) uint16_t As[2][kGemmM * kGemmLd];
   __shared__ __align__(16) uint16_t Bs[2][kGemmN * kGemmLd];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, r16 = lane & 15, g = lane >> 4;
+  const int wm = wave >> 2, wn = wave & 3, r16 = lane & 15, g = lane >> 4;
   const int64_t m0 = (int64_t)blockIdx.x * kGemmM;
   const int n0 = blockIdx.y * kGemmN;  // 0..1023: C channels, then Z channels
   const uint16_t* W = (kZ && n0 >= kDim) ? w_z : w_kv;
   const int c0 = n0 & (kDim - 1);
-  // global -> LDS: thread tid moves 16 B of rows tid / 8 + 32 j (j < 4), columns 8 (tid % 8) ..
+  // global -> LDS: thread tid moves 16 B of rows tid / 8 + 64 j, columns 8 (tid % 8) ..
   const int lr = tid >> 3, lc = 8 * (tid & 7);
-  const uint16_t* ha[4];
-  const uint16_t* wb[4];
+  const uint16_t* ha_[PA];
+  const uint16_t* wb_[PB];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t row = m0 + lr + 32 * j;  // rows past n_tok read the last token; not stored
-    ha[j] = h + (size_t)(row < n_tok ? row : n_tok - 1) * d + lc;
-    wb[j] = W + (size_t)(c0 + lr + 32 * j) * d + lc;
+  for (int j = 0; j < PA; ++j) {
+    const int64_t row = m0 + lr + (kGemmThreads / 8) * j;  // rows past n_tok read the last token; not stored
+    ha_[j] = h + (size_t)(row < n_tok ? row : n_tok - 1) * d + lc;
   }
-  uint4 ra[4], rb[4];
-  auto gload = [&](int k) {
-    const bool in = k + lc < d;  // d is a multiple of 32: a 16-byte piece is wholly in or out
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ra[j] = in ? *reinterpret_cast<const uint4*>(ha[j] + k) : uint4{0u, 0u, 0u, 0u};
-      rb[j] = in ? *reinterpret_cast<const uint4*>(wb[j] + k) : uint4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto lstore = [&](int buf) {
+  for (int j = 0; j < PB; ++j) wb_[j] = W + (size_t)(c0 + lr + (kGemmThreads / 8) * j) * d + lc;
+  const uint16_t* const (&ha)[PA] = ha_;
+  const uint16_t* const (&wb)[PB] = wb_;
+  uint4 ra[PA], rb[PB];
+  floatx4 acc[TI][TJ];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<uint4*>(&As[buf][(lr + 32 * j) * kGemmLd + lc]) = ra[j];
-      *reinterpret_cast<uint4*>(&Bs[buf][(lr + 32 * j) * kGemmLd + lc]) = rb[j];
-    }
-  };
-  floatx4 acc[4][4];
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-  gload(0);
-  lstore(0);
+    for (int j = 0; j < TJ; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // d is a multiple of 32: a 16-byte piece is wholly inside or past the end (zeros)
+  gemm_gload<PA, PB>(ra, rb, ha, wb, 0, lc < d);
+  gemm_lstore<PA, PB>(ra, rb, As[0], Bs[0], lr, lc);
   __syncthreads();
   const int nk = (d + kGemmK - 1) / kGemmK;
   for (int t = 0; t < nk; ++t) {
     const int buf = t & 1;
-    if (t + 1 < nk) gload((t + 1) * kGemmK);
+    if (t + 1 < nk) gemm_gload<PA, PB>(ra, rb, ha, wb, (t + 1) * kGemmK, (t + 1) * kGemmK + lc < d);
+    uint4 a0[TI], a1[TI], b0[TJ], b1[TJ];
 #pragma unroll
-    for (int ks = 0; ks < kGemmK / 32; ++ks) {
-      uint4 af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[i] = *reinterpret_cast<const uint4*>(&As[buf][(64 * wm + 16 * i + r16) * kGemmLd + 32 * ks + 8 * g]);
-        bf[i] = *reinterpret_cast<const uint4*>(&Bs[buf][(64 * wn + 16 * i + r16) * kGemmLd + 32 * ks + 8 * g]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(af[i]), as_bf16x8(bf[j]), acc[i][j], 0, 0, 0);
+    for (int i = 0; i < TI; ++i) {
+      const uint16_t* row = &As[buf][(64 * wm + 16 * i + r16) * kGemmLd + 8 * g];
+      a0[i] = *reinterpret_cast<const uint4*>(row);
+      a1[i] = *reinterpret_cast<const uint4*>(row + 32);
     }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const uint16_t* row = &Bs[buf][(32 * wn + 16 * j + r16) * kGemmLd + 8 * g];
+      b0[j] = *reinterpret_cast<const uint4*>(row);
+      b1[j] = *reinterpret_cast<const uint4*>(row + 32);
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0[i]), as_bf16x8(b0[j]), acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1[i]), as_bf16x8(b1[j]), acc[i][j], 0, 0, 0);
     // the other buffer was last read in step t - 1, before the barrier that ended it
-    if (t + 1 < nk) lstore(buf ^ 1);
+    if (t + 1 < nk) gemm_lstore<PA, PB>(ra, rb, As[buf ^ 1], Bs[buf ^ 1], lr, lc);
     __syncthreads();
   }
   float* out = (kZ && n0 >= kDim) ? part + zoff : part;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t tk = m0 + 64 * wm + 16 * i + 4 * g + r;
       if (tk < n_tok) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out[(size_t)tk * kDim + c0 + 64 * wn + 16 * j + r16] = acc[i][j][r];
+        for (int j = 0; j < TJ; ++j) out[(size_t)tk * kDim + c0 + 32 * wn + 16 * j + r16] = acc[i][j][r];
       }
     }
 }
@@ -546,10 +569,10 @@ extern "C" csa2_status csa2_kv_write(const void* h, const void* w_kv, const void
   if (p.many) {
     const dim3 grid((unsigned)((p.n_tok + kGemmM - 1) / kGemmM), (m > 1 ? 2 : 1) * kDim / kGemmN);
     if (m > 1)
-      hipLaunchKernelGGL(kvw_proj_many_kernel<true>, grid, dim3(kKvwThreads), 0, st, hh, wk, wz, p.n_tok, d, part,
+      hipLaunchKernelGGL(kvw_proj_many_kernel<true>, grid, dim3(kGemmThreads), 0, st, hh, wk, wz, p.n_tok, d, part,
                          zoff);
     else
-      hipLaunchKernelGGL(kvw_proj_many_kernel<false>, grid, dim3(kKvwThreads), 0, st, hh, wk, nullptr, p.n_tok, d,
+      hipLaunchKernelGGL(kvw_proj_many_kernel<false>, grid, dim3(kGemmThreads), 0, st, hh, wk, nullptr, p.n_tok, d,
                          part, zoff);
   } else {
     const dim3 grid(p.tok_tiles, kKvwChunks, p.ksplit);
