@@ -56,6 +56,8 @@ def lib():
         L.csa2o_index.restype = None
         L.csa2o_topk_row.argtypes, L.csa2o_topk_row.restype = [vp, i64, i32, vp], i32
         L.csa2o_topk.argtypes, L.csa2o_topk.restype = [vp, vp, i32, i32, i64, i32, vp], None
+        L.csa2o_topk_bf16.argtypes, L.csa2o_topk_bf16.restype = [vp, vp, i32, i32, i64, i32, vp], None
+        L.csa2o_bf16_round.argtypes, L.csa2o_bf16_round.restype = [dbl], dbl
         L.csa2o_attend.argtypes = [vp, vp, vp, vp, vp, vp, vp, dbl, i32, i32, i64, i32, i32, i32, vp, vp]
         L.csa2o_attend_ex.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, dbl, i32, i32, i64, i32, i32,
                                       i32, vp, dbl, vp, vp]
@@ -161,6 +163,21 @@ def topk(scores, q_pos, ratio, k):
     qp = None if q_pos is None else _c(q_pos, np.int32)
     out = np.empty((T, k), np.int32)
     lib().csa2o_topk(_ptr(scores), _ptr(qp), ratio, T, N, k, _ptr(out))
+    return out
+
+
+def bf16_round(x: float) -> float:
+    """The nearest bf16 value of x (ties to even), as a float."""
+    return lib().csa2o_bf16_round(float(x))
+
+
+def topk_bf16(scores, q_pos, ratio, k):
+    """Top-k of the bf16-rounded scores (value desc, index asc), ascending, -1 padded."""
+    scores = _c(scores, np.float64)
+    T, N = scores.shape
+    qp = None if q_pos is None else _c(q_pos, np.int32)
+    out = np.empty((T, k), np.int32)
+    lib().csa2o_topk_bf16(_ptr(scores), _ptr(qp), ratio, T, N, k, _ptr(out))
     return out
 
 

@@ -237,6 +237,31 @@ void csa2o_topk(const double* scores, const int32_t* q_pos, int32_t ratio, int32
     }
 }
 
+/* gzher.com reading of DeepSeek-V4, FP4 QAT section: the index scores are
+ * quantised from FP32 to BF16 before the top-k selector.  Reading: the exact
+ * score rounded to the nearest bf16 value (8 significant bits, ties to the
+ * even significand; below 2^-126 a fixed quantum of 2^-133; beyond the largest
+ * bf16 value, infinity), returned as a double. */
+double csa2o_bf16_round(double x) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    double f = frexp(x, &e);                 /* x = f * 2^e, 0.5 <= |f| < 1 */
+    if (e - 1 < -126) return ldexp(rint(ldexp(x, 133)), -133);
+    double r = ldexp(rint(ldexp(f, 8)), e - 8);
+    if (fabs(r) > 0x1.FEp127) return copysign(INFINITY, r);
+    return r;
+}
+
+/* Top-k on bf16-rounded scores: every score rounded (csa2o_bf16_round), then
+ * csa2o_topk's order (value descending, index ascending). */
+void csa2o_topk_bf16(const double* scores, const int32_t* q_pos, int32_t ratio, int32_t T,
+                     int64_t N, int32_t k, int32_t* indices) {
+    double* r = (double*)malloc((size_t)T * (size_t)N * sizeof(double));
+    for (int64_t i = 0; i < (int64_t)T * N; ++i) r[i] = csa2o_bf16_round(scores[i]);
+    csa2o_topk(r, q_pos, ratio, T, N, k, indices);
+    free(r);
+}
+
 /* ---- hierarchical sparse indexer (candidate pool) and Reindex -------------- */
 
 /* DeepSeek-V4.1-Flash report sec. 2.3.2: the first Full layer also selects

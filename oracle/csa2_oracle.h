@@ -71,6 +71,13 @@ int32_t csa2o_topk_row(const double* scores, int64_t n_vis, int32_t k, int32_t* 
 void csa2o_topk(const double* scores, const int32_t* q_pos, int32_t ratio, int32_t T,
                 int64_t N, int32_t k, int32_t* indices /*[T][k]*/);
 
+/* A double rounded to the nearest bf16 value (ties to even), as a double. */
+double csa2o_bf16_round(double x);
+
+/* Top-k of the bf16-rounded scores (csa2o_bf16_round, then csa2o_topk). */
+void csa2o_topk_bf16(const double* scores, const int32_t* q_pos, int32_t ratio, int32_t T,
+                     int64_t N, int32_t k, int32_t* indices /*[T][k]*/);
+
 /* Joint sparse + sliding-window attention for T queries.
  *  q      bf16 [T][64][512]
  *  kv     MXFP4 codes [B][N][256], scales [B][N][16]

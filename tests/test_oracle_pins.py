@@ -773,3 +773,50 @@ def test_kv_write_closed_forms(oracle_lib):
     h3v = (h3b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     r3 = oracle.kv_write(h3b, eye, _bits(gate), w_ik, 2, pos0)
     assert np.allclose(r3["entry"], h3v[0::2], rtol=1e-12, atol=1e-12)
+
+
+def test_bf16_round_golden(oracle_lib):
+    """The score rounding of the BF16 selector: hand-worked values, ties, the binade carry,
+    the sub-normal quantum, overflow, and one case that fp32-then-bf16 would round differently."""
+    import oracle
+    for inp, exp, *_ in _golden("bf16_rounding.txt"):
+        x = float.fromhex(inp)
+        want = float("inf") if exp == "inf" else float.fromhex(exp)
+        assert oracle.bf16_round(x) == want, (inp, oracle.bf16_round(x), exp)
+        assert oracle.bf16_round(-x) == -want
+
+
+def test_bf16_round_matches_torch_on_fp32_values(oracle_lib):
+    """On fp32 inputs direct rounding equals torch's float32 -> bfloat16 conversion (nearest even),
+    including planted exact ties (low 16 bits 0x8000) and their neighbours."""
+    import oracle
+    import torch
+    rng = np.random.default_rng(33)
+    u = rng.integers(0x00800000, 0x7F000000, 4000, dtype=np.uint32)
+    u[:1000] = (u[:1000] & 0xFFFF0000) | 0x8000
+    u[1000:1500] = (u[1000:1500] & 0xFFFF0000) | 0x7FFF
+    u[1500:2000] = (u[1500:2000] & 0xFFFF0000) | 0x8001
+    sign = rng.integers(0, 2, u.size).astype(np.uint32) << 31
+    x = (u | sign).view(np.float32)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.bf16_round(float(v)) for v in x])
+    assert np.array_equal(got, ref)
+
+
+def test_topk_bf16_ties_go_to_lower_index(oracle_lib):
+    """Scores that differ only below bf16 resolution tie after rounding, and the lower index
+    wins; scores a bf16 step apart keep their order."""
+    import oracle
+    N, k = 40, 6
+    s = np.full(N, 0.25)                        # clearly out
+    s[[3, 30]] = [8.0, 4.0]                     # clearly in
+    tied = [5, 9, 17, 22, 35, 38]               # all round to 2.0
+    s[tied] = 2.0 + np.array([1, 6, 2, 5, 7, 3]) * 2.0 ** -12
+    sel = oracle.topk_bf16(s[None, :], None, 1, k)[0]
+    assert list(sel) == [3, 5, 9, 17, 22, 30]   # the four lowest tied indices
+    exact = oracle.topk(s[None, :], None, 1, k)[0]
+    assert list(exact) == [3, 9, 22, 30, 35, 38]  # exact order takes the largest offsets
+    # one bf16 step above the tie keeps its place
+    s2 = s.copy()
+    s2[38] = 2.0 + 2.0 ** -6
+    assert list(oracle.topk_bf16(s2[None, :], None, 1, k)[0]) == [3, 5, 9, 17, 30, 38]
