@@ -209,6 +209,7 @@ def main():
     tile_max = torch.empty((T, csa.tile_max_ld(N)), dtype=torch.float32, device=dev)
     stats = torch.empty(csa.index_stats_bytes(T, 1, N) // 4, dtype=torch.int32, device=dev)
     idx = torch.empty((T, 512), dtype=torch.int32, device=dev)
+    idx_b = torch.empty((T, 512), dtype=torch.int32, device=dev)
     out = torch.empty((T, 64, 512), dtype=torch.bfloat16, device=dev)
     out_re = torch.empty((3, T, 64, 512), dtype=torch.bfloat16, device=dev)
     ws_t = torch.empty(max(1, csa.topk_workspace_bytes(T, N)), dtype=torch.uint8, device=dev)
@@ -222,6 +223,10 @@ def main():
 
     def do_topk():
         csa.csa2_topk(scores, tile_max, stats, q_idx, c.w_idx, k_idx, c.q_pos, 1, 1, indices=idx, workspace=ws_t)
+
+    def do_topk_bf16():
+        csa.csa2_topk(scores, tile_max, stats, q_idx, c.w_idx, k_idx, c.q_pos, 1, 1, indices=idx_b, workspace=ws_t,
+                      select=csa.SELECT_BF16)
 
     def do_attend():
         csa.csa2_attend_fp4(q0, c.kv_codes, c.kv_scales, idx, swa0, c.swa_end, None, c.softmax_scale, 1, 128,
@@ -279,6 +284,10 @@ def main():
     reps = max(10, args.steps)
     idx_med, idx_avg = timed(do_index, reps)
     topk_med, _ = timed(do_topk, reps)
+    do_index()
+    topk_bf16_med, _ = timed(do_topk_bf16, reps)
+    do_index()
+    do_topk()
     att_med, att_avg = timed(do_attend, reps)
     do_reuse()
     reuse_med, _ = timed(do_reuse, reps)
@@ -348,7 +357,8 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": recorded_traffic() if args.workload == "long_decode" else None,
                      "algorithmic_bytes_per_launch": idx_bytes, "avg_launch_us": idx_avg},
-        "stages_us": {"index": idx_med, "topk": topk_med, "attend": att_med, "reuse_3_layers": reuse_med},
+        "stages_us": {"index": idx_med, "topk": topk_med, "attend": att_med, "reuse_3_layers": reuse_med,
+                      "topk_bf16_select": topk_bf16_med},
         "hierarchical_us": {"pool": pool_med, "reindex": reindex_med,
                             "note": "outside the step: a Full layer's 16384-entry candidate pool (after its scan) "
                                     "and one Reindex layer's top-512 within it"},

@@ -22,6 +22,7 @@ __all__ = [
     "reindex_workspace_bytes", "HSI_BLOCK", "HSI_BLOCKS", "HSI_POOL", "csa2_index_mxfp4", "csa2_topk_mxfp4",
     "csa2_hsi_pool_mxfp4", "csa2_reindex_mxfp4", "index_mxfp4_stats_bytes", "csa2_attend_ex", "KV_MXFP4",
     "KV_E4M3_16", "SWA_BF16", "SWA_FP8", "csa2_kv_write", "kv_write_workspace_bytes", "K_BF16", "K_MXFP4",
+    "SELECT_EXACT", "SELECT_BF16",
 ]
 
 IDX_HEADS, IDX_DIM, HEADS, DIM, TOPK, MAX_WINDOW, MAX_LAYERS = 32, 128, 64, 512, 512, 128, 8
@@ -29,6 +30,7 @@ TILE, TOPK_ROW_MAX, STATS_WORDS = 16, 36864, 4
 HSI_BLOCK, HSI_BLOCKS = 8, 2048
 KV_MXFP4, KV_E4M3_16, SWA_BF16, SWA_FP8 = 0, 1, 0, 1
 K_BF16, K_MXFP4 = 0, 1
+SELECT_EXACT, SELECT_BF16 = 0, 1
 HSI_POOL = HSI_BLOCK * HSI_BLOCKS
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +61,10 @@ _SIGNATURES = {
     "csa2_reindex": ([_vp, _vp, _vp, _vp, _i32, _i32, _i64, _i32, _vp, _vp, _sz, _vp], _i32),
     "csa2_index_mxfp4_stats_bytes": ([_i32, _i32, _i64], _sz),
     "csa2_index_mxfp4": ([_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _vp, _sz, _vp], _i32),
+    "csa2_topk_ex": ([_vp, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _i32, _vp, _vp, _sz,
+                      _vp], _i32),
+    "csa2_topk_mxfp4_ex": ([_vp, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _i32, _vp, _vp,
+                            _sz, _vp], _i32),
     "csa2_topk_mxfp4": ([_vp, _vp, _vp, _sz, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp, _vp, _sz, _vp],
                         _i32),
     "csa2_hsi_pool_mxfp4": ([_vp, _vp, _sz, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i64, _vp, _vp, _sz, _vp], _i32),
@@ -235,10 +241,12 @@ def csa2_index(q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, want_score
 
 
 def csa2_topk(scores, tile_max, stats, q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, k=TOPK,
-              indices=None, workspace=None):
+              indices=None, workspace=None, select=SELECT_EXACT):
     """Exact top-k (ascending indices, -1 padded) -> int32 [T][k].  scores may be None (the
     selection then works from tile_max and the keys); stats is csa2_index's summary (eps and the
-    floor are written into its header, its counter words are used and left zero)."""
+    floor are written into its header, its counter words are used and left zero).  select:
+    SELECT_EXACT orders by the exact score, SELECT_BF16 by its nearest bf16 value (ties to the
+    lower index)."""
     T = q_idx.shape[0]
     B, N = k_idx.shape[0], k_idx.shape[1]
     dev = q_idx.device
@@ -258,9 +266,9 @@ def csa2_topk(scores, tile_max, stats, q_idx, w_idx, k_idx, q_pos=None, ratio=1,
         workspace = _ws(topk_workspace_bytes(T, N, k), dev, None)
     elif _nbytes(workspace) < topk_min_workspace_bytes(T, N, k):
         raise ValueError("workspace below csa2_topk_min_workspace_bytes")
-    st = lib().csa2_topk(_p(scores), _p(tile_max), _p(stats), stats.numel() * 4, _p(q_idx), _p(w_idx), _p(k_idx),
-                         _p(q_pos), ratio, T, q_per_seq, N, k, _p(indices), _p(workspace), _nbytes(workspace),
-                         _stream(q_idx))
+    st = lib().csa2_topk_ex(_p(scores), _p(tile_max), _p(stats), stats.numel() * 4, _p(q_idx), _p(w_idx),
+                            _p(k_idx), _p(q_pos), ratio, T, q_per_seq, N, k, select, _p(indices), _p(workspace),
+                            _nbytes(workspace), _stream(q_idx))
     _raise(st, "csa2_topk")
     return indices
 
@@ -366,8 +374,9 @@ def csa2_index_mxfp4(q_codes, q_scales, w_idx, k_codes, k_scales, q_pos=None, ra
 
 
 def csa2_topk_mxfp4(scores, tile_max, stats, w_idx, k_codes, k_scales, q_pos=None, ratio=1, q_per_seq=1, k=TOPK,
-                    indices=None, workspace=None):
-    """Exact top-k over the MXFP4 scan's outputs (the queries come from its summary)."""
+                    indices=None, workspace=None, select=SELECT_EXACT):
+    """Exact top-k over the MXFP4 scan's outputs (the queries come from its summary); select as
+    for csa2_topk."""
     T = w_idx.shape[0]
     dev = w_idx.device
     B, N = _check_mx_keys(k_codes, k_scales, dev)
@@ -385,9 +394,9 @@ def csa2_topk_mxfp4(scores, tile_max, stats, w_idx, k_codes, k_scales, q_pos=Non
         workspace = _ws(topk_workspace_bytes(T, N, k), dev, None)
     elif _nbytes(workspace) < topk_min_workspace_bytes(T, N, k):
         raise ValueError("workspace below csa2_topk_min_workspace_bytes")
-    st = lib().csa2_topk_mxfp4(_p(scores), _p(tile_max), _p(stats), stats.numel() * 4, _p(w_idx), _p(k_codes),
-                               _p(k_scales), _p(q_pos), ratio, T, q_per_seq, N, k, _p(indices), _p(workspace),
-                               _nbytes(workspace), _stream(w_idx))
+    st = lib().csa2_topk_mxfp4_ex(_p(scores), _p(tile_max), _p(stats), stats.numel() * 4, _p(w_idx), _p(k_codes),
+                                  _p(k_scales), _p(q_pos), ratio, T, q_per_seq, N, k, select, _p(indices),
+                                  _p(workspace), _nbytes(workspace), _stream(w_idx))
     _raise(st, "csa2_topk_mxfp4")
     return indices
 

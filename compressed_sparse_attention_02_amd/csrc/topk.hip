@@ -62,6 +62,55 @@ __device__ __forceinline__ double next_down(double x) {
 }
 __device__ __forceinline__ double next_up(double x) { return -next_down(-x); }
 
+// ---- the BF16 selector (gzher.com reading of DeepSeek-V4, FP4 QAT section:
+// index scores are quantised to BF16 before the top-k).  The selection order
+// is (bf16 rounding of the exact score desc, index asc).
+
+// Nearest bf16 value of x, ties to the even significand (quantum 2^-133 below
+// 2^-126, infinity past 0x1.FEp127), as a double.
+__device__ __forceinline__ double bf16_round_f64(double x) {
+  if (x == 0.0 || !(fabs(x) < INFINITY)) return x;
+  int e;
+  const double f = frexp(x, &e);
+  if (e - 1 < -126) return ldexp(rint(ldexp(x, 133)), -133);
+  const double r = ldexp(rint(ldexp(f, 8)), e - 8);
+  return fabs(r) > 0x1.FEp127 ? copysign((double)INFINITY, r) : r;
+}
+
+// The bf16 value below (above) a finite bf16 value b, from its bit pattern.
+__device__ __forceinline__ double bf16_below(double b) {
+  const uint32_t u = __float_as_uint((float)b) >> 16;
+  uint32_t p;
+  if (b == 0.0) p = 0x8001u;            // -2^-133
+  else if (b > 0.0) p = u - 1u;
+  else p = u + 1u;                      // -max - 1 step is -infinity (0xFF80)
+  return (double)__uint_as_float(p << 16);
+}
+__device__ __forceinline__ double bf16_above(double b) { return -bf16_below(-b); }
+
+// Rounding boundaries of a bf16 value b: every x >= lower_mid rounds to b or
+// above, every x > upper_mid strictly above b (midpoints are exact in fp64).
+__device__ __forceinline__ double bf16_lower_mid(double b) {
+  return (fabs(b) < INFINITY) ? 0.5 * (bf16_below(b) + b) : b;
+}
+__device__ __forceinline__ double bf16_upper_mid(double b) {
+  return (fabs(b) < INFINITY) ? 0.5 * (b + bf16_above(b)) : b;
+}
+
+// The value an entry is ranked by: its exact score, or that score's bf16 rounding.
+__device__ __forceinline__ double sel_value(double s, int bsel) { return bsel ? bf16_round_f64(s) : s; }
+
+// Candidate threshold of the tile regime.  At least k entries have an fp32
+// score >= tau, so the k-th exact score S is >= tau - eps and every selected
+// entry has an exact score >= S (exact order) or >= the lower rounding boundary
+// of bf16(S) (bf16 order; rounding is monotone): its fp32 score is at least
+// that minus eps.
+__device__ __forceinline__ double cand_threshold(float tau, float eps, int bsel) {
+  if (!bsel) return next_down((double)tau - 2.0 * (double)eps);
+  const double lb = next_down((double)tau - (double)eps);
+  return next_down(bf16_lower_mid(bf16_round_f64(lb)) - (double)eps);
+}
+
 // eps_t = 2^-14 * sum_h |w_h| ||q_h||_2 * max_s ||K_s||_2 + 2^-100 (1 + sum_h |w_h|), rounded up.
 //
 // Derivation: the bf16 products are exact in fp32; four chained MFMA steps
@@ -325,7 +374,7 @@ struct alignas(16) FinLds {
 // threads fold the heads in order.
 template <class Keys>
 __device__ void rescore_band(FinLds& sh, FinTail& tl, uint32_t nb, const uint16_t* __restrict__ qt,
-                             const float* __restrict__ wt, const Keys& kb) {
+                             const float* __restrict__ wt, const Keys& kb, int bsel) {
   const int tid = threadIdx.x;
   const int e = tid >> 5, h = tid & 31;
   for (int i = tid; i < kIdxHeads * 16; i += kFinThreads) {
@@ -366,7 +415,7 @@ __device__ void rescore_band(FinLds& sh, FinTail& tl, uint32_t nb, const uint16_
           const double d = tl.dots[tid][hh];
           sc = fma((double)wt[hh], d > 0.0 ? d : 0.0, sc);
         }
-        tl.band_key[base + half + tid] = f64_key(sc);
+        tl.band_key[base + half + tid] = f64_key(sel_value(sc, bsel));
       }
       __syncthreads();
     }
@@ -377,9 +426,9 @@ __device__ void rescore_band(FinLds& sh, FinTail& tl, uint32_t nb, const uint16_
 // in sh.out / sh.band_idx (n_band <= kBandLds): rescore and pick the band's share.
 template <class Keys>
 __device__ void finish_band(FinLds& sh, FinTail& tl, uint32_t kk, const uint16_t* qt, const float* wt,
-                            const Keys& kb) {
+                            const Keys& kb, int bsel) {
   const uint32_t nb = sh.n_band;
-  rescore_band(sh, tl, nb, qt, wt, kb);
+  rescore_band(sh, tl, nb, qt, wt, kb, bsel);
   const uint32_t r = kk - sh.n_out;
   const uint32_t base_out = sh.n_out;
   for (uint32_t i = threadIdx.x; i < nb; i += kFinThreads) {
@@ -401,7 +450,7 @@ __device__ void finish_band(FinLds& sh, FinTail& tl, uint32_t kk, const uint16_t
 // composite (fp64 key, ~index), recomputing each band member's fp64 score.
 template <class Keys>
 __device__ void finish_streaming(FinLds& sh, uint32_t kk, const float* row, int64_t nv, double lo, double hi,
-                                 const uint16_t* qt, const float* wt, const Keys& kb) {
+                                 const uint16_t* qt, const float* wt, const Keys& kb, int bsel) {
   const int tid = threadIdx.x;
   if (tid == 0) sh.n_out = 0;
   __syncthreads();
@@ -417,7 +466,7 @@ __device__ void finish_streaming(FinLds& sh, uint32_t kk, const float* row, int6
     for (int64_t s = tid; s < nv; s += kFinThreads) {
       const double v = (double)row[s];
       if (v < lo || v > hi) continue;
-      const uint64_t key = f64_key(exact_score(qt, wt, kb, s));
+      const uint64_t key = f64_key(sel_value(exact_score(qt, wt, kb, s), bsel));
       const uint32_t low = ~(uint32_t)s;
       if ((key & mhi) != phi || (low & mlo) != plo) continue;
       const uint32_t digit = pass < 8 ? (uint32_t)(key >> (56 - 8 * pass)) & 255u
@@ -438,7 +487,7 @@ __device__ void finish_streaming(FinLds& sh, uint32_t kk, const float* row, int6
   for (int64_t s = tid; s < nv; s += kFinThreads) {
     const double v = (double)row[s];
     if (v < lo || v > hi) continue;
-    const uint64_t key = f64_key(exact_score(qt, wt, kb, s));
+    const uint64_t key = f64_key(sel_value(exact_score(qt, wt, kb, s), bsel));
     const uint32_t low = ~(uint32_t)s;
     if (key > phi || (key == phi && low >= plo)) sh.out[atomicAdd(&sh.n_out, 1u)] = (uint32_t)s;
   }
@@ -464,9 +513,20 @@ __device__ void write_sorted(FinLds& sh, FinTail& tl, uint32_t kk, int k, int32_
 }
 
 // Band bounds around the bracket [t_lo, t_hi] of T^ (rounded outwards in fp64).
-__device__ __forceinline__ void band_bounds(float t_lo, float t_hi, float eps, double* lo, double* hi) {
-  *lo = next_down((double)t_lo - 2.0 * (double)eps);
-  *hi = next_up((double)t_hi + 2.0 * (double)eps);
+// The k-th exact score S lies in [t_lo - eps, t_hi + eps].  Exact order: an
+// entry whose fp32 score is above t_hi + 2 eps is in, below t_lo - 2 eps out.
+// BF16 order: in only when its exact score rounds strictly above
+// bf16(t_hi + eps) >= bf16(S), out when below the lower rounding boundary of
+// bf16(t_lo - eps) <= bf16(S); everything between is ranked exactly.
+__device__ __forceinline__ void band_bounds(float t_lo, float t_hi, float eps, int bsel, double* lo, double* hi) {
+  if (bsel) {
+    const double a = next_down((double)t_lo - (double)eps), b = next_up((double)t_hi + (double)eps);
+    *lo = next_down(bf16_lower_mid(bf16_round_f64(a)) - (double)eps);
+    *hi = next_up(bf16_upper_mid(bf16_round_f64(b)) + (double)eps);
+  } else {
+    *lo = next_down((double)t_lo - 2.0 * (double)eps);
+    *hi = next_up((double)t_hi + 2.0 * (double)eps);
+  }
   if (!(*lo <= (double)t_lo)) *lo = -INFINITY;   // eps not finite: everything is in the band
   if (!(*hi >= (double)t_hi)) *hi = INFINITY;
 }
@@ -489,7 +549,8 @@ template <class Keys>
 __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
     const float* __restrict__ scores, uint32_t* __restrict__ stats, const float* __restrict__ parts,
     int64_t n_parts, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, Keys keys,
-    const int32_t* __restrict__ q_pos, int ratio, int q_per_seq, int64_t N, int k, int32_t* __restrict__ indices) {
+    const int32_t* __restrict__ q_pos, int ratio, int q_per_seq, int64_t N, int k, int32_t* __restrict__ indices,
+    int bsel) {
   __shared__ SmallLds L;
   FinLds& sh = L.f;
   FinTail& tl = L.u.tail;
@@ -545,7 +606,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
   float t_lo, t_hi;
   bracket_kth(sh.sel, nv, kk, [&](int64_t i) { return L.u.v[i]; }, &t_lo, &t_hi);
   double lo, hi;
-  band_bounds(t_lo, t_hi, eps, &lo, &hi);
+  band_bounds(t_lo, t_hi, eps, bsel, &lo, &hi);
   for (int64_t i = tid; i < nv; i += kFinThreads) {
     const double v = (double)L.u.v[i];
     if (v > hi) sh.out[atomicAdd(&sh.n_out, 1u)] = (uint32_t)i;
@@ -557,8 +618,8 @@ __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
   __syncthreads();
   const bool fast = sh.n_band <= kBandLds;
   __syncthreads();
-  if (fast) finish_band(sh, tl, kk, qt, wt, kb);
-  else finish_streaming(sh, kk, row, nv, lo, hi, qt, wt, kb);
+  if (fast) finish_band(sh, tl, kk, qt, wt, kb, bsel);
+  else finish_streaming(sh, kk, row, nv, lo, hi, qt, wt, kb, bsel);
   write_sorted(sh, tl, kk, k, out);
 }
 
@@ -993,7 +1054,7 @@ template <class Keys>
 __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
     const float* __restrict__ tile_max, uint32_t* __restrict__ stats, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w_idx, Keys keys, const int32_t* __restrict__ q_pos,
-    int ratio, int q_per_seq, int64_t N, int k, void* ws, int T, int64_t cap, int slots) {
+    int ratio, int q_per_seq, int64_t N, int k, void* ws, int T, int64_t cap, int slots, int bsel) {
   __shared__ CandLds L;
   const int t = blockIdx.y;
   const int x = blockIdx.x;
@@ -1015,7 +1076,7 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   const float tau = __uint_as_float(st[1]);
   stage_query(L.sq, q_idx + (size_t)t * kIdxHeads * kIdxDim, tid, kCandThreads);
   if (tid < kIdxHeads) L.w[tid] = w_idx[(size_t)t * kIdxHeads + tid];
-  const double thr = next_down((double)tau - 2.0 * (double)eps);
+  const double thr = cand_threshold(tau, eps, bsel);
 
   // 1. candidate tiles in order
   const bool cand = my_tile < ntv && (double)tm >= thr;
@@ -1070,7 +1131,7 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   // 5. fp64 scores of the passing entries, reference operation order, into the slots
   double* cs = w.cscore + (size_t)t * cap;
   exact_entry_scores_wave(L.sq, L.w, L.eidx, n_pass, kseq, L.hrel[tid >> 6], [&](uint32_t e, double sc) {
-    if ((uint64_t)base + e < (uint64_t)cap) cs[base + e] = sc;
+    if ((uint64_t)base + e < (uint64_t)cap) cs[base + e] = sel_value(sc, bsel);
   });
 }
 
@@ -1330,7 +1391,7 @@ __device__ double exact_score_lds(const uint16_t* __restrict__ sq, const float* 
 // scores recomputed in each pass, then an ordered gather.
 template <class Keys>
 __device__ void select_streaming(SelectLds& L, uint32_t kk, const float* tm_row, int64_t nv, double thr,
-                                 const uint16_t* qt, const float* wt, const Keys& kb, int32_t* out) {
+                                 const uint16_t* qt, const float* wt, const Keys& kb, int32_t* out, int bsel) {
   const int tid = threadIdx.x;
   stage_query(L.sq, qt, tid, kSelThreads);
   if (tid < kIdxHeads) L.w[tid] = wt[tid];
@@ -1343,7 +1404,7 @@ __device__ void select_streaming(SelectLds& L, uint32_t kk, const float* tm_row,
     __syncthreads();
     for (int64_t s = tid; s < nv; s += kSelThreads) {
       if (!((double)tm_row[s / kTileKeys] >= thr)) continue;
-      const uint64_t key = f64_key(exact_score_lds(L.sq, L.w, kb, s));
+      const uint64_t key = f64_key(sel_value(exact_score_lds(L.sq, L.w, kb, s), bsel));
       const uint32_t low = ~(uint32_t)s;
       if ((key & mhi) != phi || (low & mlo) != plo) continue;
       const uint32_t digit = pass < 8 ? (uint32_t)(key >> (56 - 8 * pass)) & 255u
@@ -1367,7 +1428,7 @@ __device__ void select_streaming(SelectLds& L, uint32_t kk, const float* tm_row,
     const int64_t s = s0 + tid;
     bool keep = false;
     if (s < nv && (double)tm_row[s / kTileKeys] >= thr) {
-      const uint64_t key = f64_key(exact_score_lds(L.sq, L.w, kb, s));
+      const uint64_t key = f64_key(sel_value(exact_score_lds(L.sq, L.w, kb, s), bsel));
       const uint32_t low = ~(uint32_t)s;
       keep = key > phi || (key == phi && low >= plo);
     }
@@ -1384,7 +1445,8 @@ template <class Keys>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
     const float* __restrict__ tile_max, uint32_t* __restrict__ stats, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w_idx, Keys keys, const int32_t* __restrict__ q_pos,
-    int ratio, int q_per_seq, int64_t N, int k, int32_t* __restrict__ indices, void* ws, int T, int64_t cap) {
+    int ratio, int q_per_seq, int64_t N, int k, int32_t* __restrict__ indices, void* ws, int T, int64_t cap,
+    int bsel) {
   __shared__ SelectLds L;
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
@@ -1421,9 +1483,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(
   const bool fits = ovf == 0u && small_table && cnt <= kSelLds && cnt >= kk;
   if (!fits) {
     const float tau = __uint_as_float(st[1]);
-    const double thr = next_down((double)tau - 2.0 * (double)__uint_as_float(st[0]));
+    const double thr = cand_threshold(tau, __uint_as_float(st[0]), bsel);
     select_streaming(L, kk, tile_max + (size_t)t * tile_ld(N), nv, thr, q_idx + (size_t)t * kIdxHeads * kIdxDim,
-                     w_idx + (size_t)t * kIdxHeads, keys.seq(t / q_per_seq, N), out);
+                     w_idx + (size_t)t * kIdxHeads, keys.seq(t / q_per_seq, N), out, bsel);
     if (tid == 0) st[2] = 0u;
     return;
   }
@@ -2028,11 +2090,11 @@ template <class Keys>
 static csa2_status topk_launch(const float* scores, const float* tile_max, uint32_t* stats, const Summary& sm,
                                const float* w_idx, Keys keys, const int32_t* q_pos, int32_t ratio, int32_t T,
                                int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices, void* workspace,
-                               size_t workspace_bytes, hipStream_t st) {
+                               size_t workspace_bytes, hipStream_t st, int bsel) {
   (void)hipGetLastError();
   if (topk_row_regime(scores, N)) {
     hipLaunchKernelGGL(topk_small_kernel<Keys>, dim3(T), dim3(kFinThreads), 0, st, scores, stats, sm.parts,
-                       sm.n_parts, sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, k, indices);
+                       sm.n_parts, sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, k, indices, bsel);
     if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
     return CSA2_OK;
   }
@@ -2046,18 +2108,20 @@ static csa2_status topk_launch(const float* scores, const float* tile_max, uint3
   hipLaunchKernelGGL(topk_floor_kernel, dim3(T), dim3(kFloorThreads), 0, st, tile_max, stats, sm.gmax, sm.n_groups,
                      sm.parts, sm.n_parts, sm.q, w_idx, q_pos, ratio, q_per_seq, N, kTopK, (int64_t)kTopK);
   hipLaunchKernelGGL(topk_cand_kernel<Keys>, dim3((unsigned)nblk, T), dim3(kCandThreads), 0, st, tile_max, stats,
-                     sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, k, workspace, T, cap, slots);
+                     sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, k, workspace, T, cap, slots, bsel);
   hipLaunchKernelGGL(topk_select_kernel<Keys>, dim3(T), dim3(kSelThreads), 0, st, tile_max, stats, sm.q, w_idx, keys,
-                     q_pos, ratio, q_per_seq, N, k, indices, workspace, T, cap);
+                     q_pos, ratio, q_per_seq, N, k, indices, workspace, T, cap, bsel);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   return CSA2_OK;
 }
 
-extern "C" csa2_status csa2_topk(const float* scores, const float* tile_max, uint32_t* stats, size_t stats_bytes,
-                                 const void* q_idx, const float* w_idx, const void* k_idx, const int32_t* q_pos,
-                                 int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N, int32_t k,
-                                 int32_t* indices, void* workspace, size_t workspace_bytes, void* hip_stream) {
+extern "C" csa2_status csa2_topk_ex(const float* scores, const float* tile_max, uint32_t* stats,
+                                    size_t stats_bytes, const void* q_idx, const float* w_idx, const void* k_idx,
+                                    const int32_t* q_pos, int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N,
+                                    int32_t k, int32_t select, int32_t* indices, void* workspace,
+                                    size_t workspace_bytes, void* hip_stream) {
   if (!stats || !q_idx || !w_idx || !k_idx || !indices) return CSA2_ERR_INVALID_ARG;
+  if (select != CSA2_SELECT_EXACT && select != CSA2_SELECT_BF16) return CSA2_ERR_UNSUPPORTED;
   if ((scores && !aligned16(scores)) || (tile_max && !aligned16(tile_max)) || !aligned16(stats) ||
       !aligned16(q_idx) || !aligned16(w_idx) || !aligned16(k_idx) || !aligned16(indices) ||
       (q_pos && !aligned16(q_pos)))
@@ -2069,15 +2133,26 @@ extern "C" csa2_status csa2_topk(const float* scores, const float* tile_max, uin
   Summary sm;
   if (!summary_bf16(stats, stats_bytes, q_idx, T, q_per_seq, N, &sm)) return CSA2_ERR_INVALID_ARG;
   return topk_launch(scores, tile_max, stats, sm, w_idx, Bf16Keys{(const uint16_t*)k_idx}, q_pos, ratio, T,
-                     q_per_seq, N, k, indices, workspace, workspace_bytes, (hipStream_t)hip_stream);
+                     q_per_seq, N, k, indices, workspace, workspace_bytes, (hipStream_t)hip_stream,
+                     select == CSA2_SELECT_BF16);
 }
 
-extern "C" csa2_status csa2_topk_mxfp4(const float* scores, const float* tile_max, uint32_t* stats,
-                                       size_t stats_bytes, const float* w_idx, const uint8_t* k_codes,
-                                       const uint8_t* k_scales, const int32_t* q_pos, int32_t ratio, int32_t T,
-                                       int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices, void* workspace,
-                                       size_t workspace_bytes, void* hip_stream) {
+extern "C" csa2_status csa2_topk(const float* scores, const float* tile_max, uint32_t* stats, size_t stats_bytes,
+                                 const void* q_idx, const float* w_idx, const void* k_idx, const int32_t* q_pos,
+                                 int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N, int32_t k,
+                                 int32_t* indices, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return csa2_topk_ex(scores, tile_max, stats, stats_bytes, q_idx, w_idx, k_idx, q_pos, ratio, T, q_per_seq, N, k,
+                      CSA2_SELECT_EXACT, indices, workspace, workspace_bytes, hip_stream);
+}
+
+extern "C" csa2_status csa2_topk_mxfp4_ex(const float* scores, const float* tile_max, uint32_t* stats,
+                                          size_t stats_bytes, const float* w_idx, const uint8_t* k_codes,
+                                          const uint8_t* k_scales, const int32_t* q_pos, int32_t ratio, int32_t T,
+                                          int32_t q_per_seq, int64_t N, int32_t k, int32_t select,
+                                          int32_t* indices, void* workspace, size_t workspace_bytes,
+                                          void* hip_stream) {
   if (!stats || !w_idx || !k_codes || !k_scales || !indices) return CSA2_ERR_INVALID_ARG;
+  if (select != CSA2_SELECT_EXACT && select != CSA2_SELECT_BF16) return CSA2_ERR_UNSUPPORTED;
   if ((scores && !aligned16(scores)) || (tile_max && !aligned16(tile_max)) || !aligned16(stats) ||
       !aligned16(w_idx) || !aligned16(k_codes) || !aligned16(k_scales) || !aligned16(indices) ||
       (q_pos && !aligned16(q_pos)))
@@ -2089,7 +2164,16 @@ extern "C" csa2_status csa2_topk_mxfp4(const float* scores, const float* tile_ma
   Summary sm;
   if (!summary_mx(stats, stats_bytes, T, q_per_seq, N, &sm)) return CSA2_ERR_INVALID_ARG;
   return topk_launch(scores, tile_max, stats, sm, w_idx, Mx4Keys{k_codes, k_scales}, q_pos, ratio, T, q_per_seq, N,
-                     k, indices, workspace, workspace_bytes, (hipStream_t)hip_stream);
+                     k, indices, workspace, workspace_bytes, (hipStream_t)hip_stream, select == CSA2_SELECT_BF16);
+}
+
+extern "C" csa2_status csa2_topk_mxfp4(const float* scores, const float* tile_max, uint32_t* stats,
+                                       size_t stats_bytes, const float* w_idx, const uint8_t* k_codes,
+                                       const uint8_t* k_scales, const int32_t* q_pos, int32_t ratio, int32_t T,
+                                       int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices, void* workspace,
+                                       size_t workspace_bytes, void* hip_stream) {
+  return csa2_topk_mxfp4_ex(scores, tile_max, stats, stats_bytes, w_idx, k_codes, k_scales, q_pos, ratio, T,
+                            q_per_seq, N, k, CSA2_SELECT_EXACT, indices, workspace, workspace_bytes, hip_stream);
 }
 
 extern "C" size_t csa2_hsi_pool_workspace_bytes(int32_t T, int64_t N) {

@@ -152,6 +152,27 @@ csa2_status csa2_topk(const float* scores, const float* tile_max, uint32_t* stat
                       int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices,
                       void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* ------------------------------------------------------ selection order
+ * csa2_topk_ex / csa2_topk_mxfp4_ex: csa2_topk / csa2_topk_mxfp4 with a
+ * choice of the order the k entries are taken in.
+ *  CSA2_SELECT_EXACT  (I_fp64 descending, index ascending): csa2_topk.
+ *  CSA2_SELECT_BF16   (bf16(I_fp64) descending, index ascending), where bf16()
+ *                     is rounding to the nearest bf16 value, ties to the even
+ *                     significand (quantum 2^-133 below 2^-126).  The
+ *                     gzher.com DeepSeek-V4 reading (FP4 QAT section) states
+ *                     that the index scores are quantised to BF16 before the
+ *                     top-k selector; entries whose scores round to the same
+ *                     bf16 value tie, and the lower index wins.
+ * Any other value of select returns CSA2_ERR_UNSUPPORTED; all other arguments,
+ * outputs, workspace and errors are those of csa2_topk (csa2_topk_mxfp4).
+ */
+#define CSA2_SELECT_EXACT 0
+#define CSA2_SELECT_BF16 1
+csa2_status csa2_topk_ex(const float* scores, const float* tile_max, uint32_t* stats, size_t stats_bytes,
+                         const void* q_idx, const float* w_idx, const void* k_idx, const int32_t* q_pos,
+                         int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t select,
+                         int32_t* indices, void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* --------------------------------------------------------------- hsi pool
  * Candidate pool of the hierarchical sparse indexer (report sec. 2.3.2; block
  * size 8 and 2048 blocks per sec. 4.2.1).  A Full layer's visible entries
@@ -237,6 +258,11 @@ csa2_status csa2_topk_mxfp4(const float* scores, const float* tile_max, uint32_t
                             const int32_t* q_pos, int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N,
                             int32_t k, int32_t* indices, void* workspace, size_t workspace_bytes,
                             void* hip_stream);
+csa2_status csa2_topk_mxfp4_ex(const float* scores, const float* tile_max, uint32_t* stats, size_t stats_bytes,
+                               const float* w_idx, const uint8_t* k_codes, const uint8_t* k_scales,
+                               const int32_t* q_pos, int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N,
+                               int32_t k, int32_t select, int32_t* indices, void* workspace, size_t workspace_bytes,
+                               void* hip_stream);
 csa2_status csa2_hsi_pool_mxfp4(const float* tile_max, const uint32_t* stats, size_t stats_bytes,
                                 const float* w_idx, const uint8_t* k_codes, const uint8_t* k_scales,
                                 const int32_t* q_pos, int32_t ratio, int32_t T, int32_t q_per_seq, int64_t N,

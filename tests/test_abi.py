@@ -29,7 +29,8 @@ def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
     assert {"csa2_index", "csa2_topk", "csa2_attend_fp4", "csa2_reuse_attend", "csa2_hsi_pool",
             "csa2_reindex", "csa2_index_mxfp4", "csa2_topk_mxfp4", "csa2_hsi_pool_mxfp4",
-            "csa2_reindex_mxfp4", "csa2_attend_ex", "csa2_kv_write"} <= set(names)
+            "csa2_reindex_mxfp4", "csa2_attend_ex", "csa2_kv_write", "csa2_topk_ex",
+            "csa2_topk_mxfp4_ex"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -115,6 +116,21 @@ def test_topk_host_validation(L):
     assert _topk(L, k=256) == UNSUPPORTED
     assert _topk(L, ws=None) == WORKSPACE
     assert _topk(L, wsb=csa.topk_min_workspace_bytes(4, 1 << 20) - 1) == WORKSPACE
+
+
+def test_topk_select_mode_validation(L):
+    def ex(select, ws=P, tm=P):
+        wsb = csa.topk_workspace_bytes(4, 1 << 20, 512)
+        return L.csa2_topk_ex(None, tm, P, 1 << 30, P, P, P, None, 1, 4, 1, 1 << 20, 512, select, P, ws, wsb, None)
+
+    def ex_mx(select, ws=P):
+        wsb = csa.topk_workspace_bytes(4, 1 << 20, 512)
+        return L.csa2_topk_mxfp4_ex(None, P, P, 1 << 30, P, P, P, None, 1, 4, 1, 1 << 20, 512, select, P, ws, wsb,
+                                    None)
+    assert ex(2) == UNSUPPORTED and ex(-1) == UNSUPPORTED and ex_mx(2) == UNSUPPORTED
+    # a valid mode reaches the usual checks (stopped here before any launch)
+    assert ex(1, ws=None) == WORKSPACE and ex(0, ws=None) == WORKSPACE and ex_mx(1, ws=None) == WORKSPACE
+    assert ex(1, tm=None) == INVALID
 
 
 def _attend(L, q=P, kv=P, sc=P, idx=P, swa=P, end=P, sink=None, scale=0.044, T=4, qps=1, N=4096, S=128, W=128,
