@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 from typing import NamedTuple, Optional
 
 import torch
@@ -22,7 +23,7 @@ __all__ = [
     "reindex_workspace_bytes", "HSI_BLOCK", "HSI_BLOCKS", "HSI_POOL", "csa2_index_mxfp4", "csa2_topk_mxfp4",
     "csa2_hsi_pool_mxfp4", "csa2_reindex_mxfp4", "index_mxfp4_stats_bytes", "csa2_attend_ex", "KV_MXFP4",
     "KV_E4M3_16", "SWA_BF16", "SWA_FP8", "csa2_kv_write", "kv_write_workspace_bytes", "K_BF16", "K_MXFP4",
-    "SELECT_EXACT", "SELECT_BF16",
+    "SELECT_EXACT", "SELECT_BF16", "bind", "BoundCall",
 ]
 
 IDX_HEADS, IDX_DIM, HEADS, DIM, TOPK, MAX_WINDOW, MAX_LAYERS = 32, 128, 64, 512, 512, 128, 8
@@ -128,8 +129,67 @@ def lib():
     return _lib
 
 
+# Recording state of bind() (per thread): the launches a wrapper makes and the
+# tensors whose device pointers it passed.
+_rec = threading.local()
+
+
 def _p(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    if t is None:
+        return None
+    keep = getattr(_rec, "keep", None)
+    if keep is not None:
+        keep.append(t)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _call(name, *args):
+    """Launch entry point `name` with marshalled arguments, or record it while bind() runs."""
+    fn = getattr(lib(), name)
+    calls = getattr(_rec, "calls", None)
+    if calls is not None:
+        calls.append((fn, args, name))
+        return 0
+    return fn(*args)
+
+
+class BoundCall:
+    """A wrapper call validated and marshalled once by bind().  Calling it issues the same
+    library launch again: same device pointers, sizes and stream, no Python-side checks.
+    `result` is what the wrapper returned (its output tensors, which every call rewrites).
+    The tensors whose pointers were passed, including outputs and workspaces the wrapper
+    allocated, are held here, so their storage stays valid; their contents may change
+    between calls."""
+
+    def __init__(self, calls, result, tensors):
+        self._calls = tuple(calls)
+        self._tensors = tuple(tensors)
+        self.result = result
+
+    def __call__(self):
+        for fn, args, name in self._calls:
+            st = fn(*args)
+            if st != 0:
+                raise Csa2Error(st, name)
+        return self.result
+
+
+def bind(wrapper, *args, **kwargs) -> BoundCall:
+    """Check and marshal `wrapper(*args, **kwargs)` (one of the csa2_* functions of this module)
+    without launching it, for repeated launches in a loop where per-call argument checks would
+    cost host time.  Outputs and workspaces the wrapper allocates are allocated now and reused
+    by every call; the stream is the one current at bind time."""
+    if getattr(_rec, "calls", None) is not None:
+        raise RuntimeError("bind() does not nest")
+    _rec.calls, _rec.keep = [], []
+    try:
+        result = wrapper(*args, **kwargs)
+        calls, tensors = _rec.calls, _rec.keep
+    finally:
+        _rec.calls, _rec.keep = None, None
+    if not calls:
+        raise ValueError(f"{getattr(wrapper, '__name__', wrapper)} makes no library launch")
+    return BoundCall(calls, result, tensors)
 
 
 def _stream(t: torch.Tensor):
@@ -234,7 +294,7 @@ def csa2_index(q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_per_seq=1, want_score
         _check(scores, "scores", (T, N), dtype=torch.float32, device=dev)
     _check(tile_max, "tile_max", (T, tile_max_ld(N)), dtype=torch.float32, device=dev)
     _check_stats(stats, T, q_per_seq, N, dev)
-    st = lib().csa2_index(_p(q_idx), _p(w_idx), _p(k_idx), _p(q_pos), ratio, T, q_per_seq, N, _p(scores),
+    st = _call("csa2_index", _p(q_idx), _p(w_idx), _p(k_idx), _p(q_pos), ratio, T, q_per_seq, N, _p(scores),
                           _p(tile_max), _p(stats), stats.numel() * 4, _stream(q_idx))
     _raise(st, "csa2_index")
     return IndexResult(scores, tile_max, stats)
@@ -266,7 +326,7 @@ def csa2_topk(scores, tile_max, stats, q_idx, w_idx, k_idx, q_pos=None, ratio=1,
         workspace = _ws(topk_workspace_bytes(T, N, k), dev, None)
     elif _nbytes(workspace) < topk_min_workspace_bytes(T, N, k):
         raise ValueError("workspace below csa2_topk_min_workspace_bytes")
-    st = lib().csa2_topk_ex(_p(scores), _p(tile_max), _p(stats), stats.numel() * 4, _p(q_idx), _p(w_idx),
+    st = _call("csa2_topk_ex", _p(scores), _p(tile_max), _p(stats), stats.numel() * 4, _p(q_idx), _p(w_idx),
                             _p(k_idx), _p(q_pos), ratio, T, q_per_seq, N, k, select, _p(indices), _p(workspace),
                             _nbytes(workspace), _stream(q_idx))
     _raise(st, "csa2_topk")
@@ -294,7 +354,7 @@ def csa2_hsi_pool(tile_max, stats, q_idx, w_idx, k_idx, q_pos=None, ratio=1, q_p
         pool = torch.empty((T, HSI_POOL), dtype=torch.int32, device=dev)
     _check(pool, "pool", (T, HSI_POOL), dtype=torch.int32, device=dev)
     workspace = _ws(hsi_pool_workspace_bytes(T, N), dev, workspace)
-    st = lib().csa2_hsi_pool(_p(tile_max), _p(stats), stats.numel() * 4, _p(q_idx), _p(w_idx), _p(k_idx),
+    st = _call("csa2_hsi_pool", _p(tile_max), _p(stats), stats.numel() * 4, _p(q_idx), _p(w_idx), _p(k_idx),
                              _p(q_pos), ratio, T, q_per_seq, N, _p(pool), _p(workspace), _nbytes(workspace),
                              _stream(q_idx))
     _raise(st, "csa2_hsi_pool")
@@ -317,7 +377,7 @@ def csa2_reindex(pool, q_idx, w_idx, k_idx, q_per_seq=1, k=TOPK, indices=None, w
         indices = torch.empty((T, k), dtype=torch.int32, device=dev)
     _check(indices, "indices", (T, k), dtype=torch.int32, device=dev)
     workspace = _ws(reindex_workspace_bytes(T, k), dev, workspace)
-    st = lib().csa2_reindex(_p(pool), _p(q_idx), _p(w_idx), _p(k_idx), T, q_per_seq, N, k, _p(indices),
+    st = _call("csa2_reindex", _p(pool), _p(q_idx), _p(w_idx), _p(k_idx), T, q_per_seq, N, k, _p(indices),
                             _p(workspace), _nbytes(workspace), _stream(q_idx))
     _raise(st, "csa2_reindex")
     return indices
@@ -366,7 +426,7 @@ def csa2_index_mxfp4(q_codes, q_scales, w_idx, k_codes, k_scales, q_pos=None, ra
         _check(scores, "scores", (T, N), dtype=torch.float32, device=dev)
     _check(tile_max, "tile_max", (T, tile_max_ld(N)), dtype=torch.float32, device=dev)
     _check_mx_stats(stats, T, q_per_seq, N, dev)
-    st = lib().csa2_index_mxfp4(_p(q_codes), _p(q_scales), _p(w_idx), _p(k_codes), _p(k_scales), _p(q_pos), ratio,
+    st = _call("csa2_index_mxfp4", _p(q_codes), _p(q_scales), _p(w_idx), _p(k_codes), _p(k_scales), _p(q_pos), ratio,
                                 T, q_per_seq, N, _p(scores), _p(tile_max), _p(stats), stats.numel() * 4,
                                 _stream(q_codes))
     _raise(st, "csa2_index_mxfp4")
@@ -394,7 +454,7 @@ def csa2_topk_mxfp4(scores, tile_max, stats, w_idx, k_codes, k_scales, q_pos=Non
         workspace = _ws(topk_workspace_bytes(T, N, k), dev, None)
     elif _nbytes(workspace) < topk_min_workspace_bytes(T, N, k):
         raise ValueError("workspace below csa2_topk_min_workspace_bytes")
-    st = lib().csa2_topk_mxfp4_ex(_p(scores), _p(tile_max), _p(stats), stats.numel() * 4, _p(w_idx), _p(k_codes),
+    st = _call("csa2_topk_mxfp4_ex", _p(scores), _p(tile_max), _p(stats), stats.numel() * 4, _p(w_idx), _p(k_codes),
                                   _p(k_scales), _p(q_pos), ratio, T, q_per_seq, N, k, select, _p(indices),
                                   _p(workspace), _nbytes(workspace), _stream(w_idx))
     _raise(st, "csa2_topk_mxfp4")
@@ -416,7 +476,7 @@ def csa2_hsi_pool_mxfp4(tile_max, stats, w_idx, k_codes, k_scales, q_pos=None, r
         pool = torch.empty((T, HSI_POOL), dtype=torch.int32, device=dev)
     _check(pool, "pool", (T, HSI_POOL), dtype=torch.int32, device=dev)
     workspace = _ws(hsi_pool_workspace_bytes(T, N), dev, workspace)
-    st = lib().csa2_hsi_pool_mxfp4(_p(tile_max), _p(stats), stats.numel() * 4, _p(w_idx), _p(k_codes), _p(k_scales),
+    st = _call("csa2_hsi_pool_mxfp4", _p(tile_max), _p(stats), stats.numel() * 4, _p(w_idx), _p(k_codes), _p(k_scales),
                                    _p(q_pos), ratio, T, q_per_seq, N, _p(pool), _p(workspace), _nbytes(workspace),
                                    _stream(w_idx))
     _raise(st, "csa2_hsi_pool_mxfp4")
@@ -439,7 +499,7 @@ def csa2_reindex_mxfp4(pool, q_codes, q_scales, w_idx, k_codes, k_scales, q_per_
         indices = torch.empty((T, k), dtype=torch.int32, device=dev)
     _check(indices, "indices", (T, k), dtype=torch.int32, device=dev)
     workspace = _ws(reindex_workspace_bytes(T, k), dev, workspace)
-    st = lib().csa2_reindex_mxfp4(_p(pool), _p(q_codes), _p(q_scales), _p(w_idx), _p(k_codes), _p(k_scales), T,
+    st = _call("csa2_reindex_mxfp4", _p(pool), _p(q_codes), _p(q_scales), _p(w_idx), _p(k_codes), _p(k_scales), T,
                                   q_per_seq, N, k, _p(indices), _p(workspace), _nbytes(workspace), _stream(q_codes))
     _raise(st, "csa2_reindex_mxfp4")
     return indices
@@ -479,7 +539,7 @@ def csa2_attend_fp4(q, kv_fp4, kv_scale, indices, swa, swa_end, sink=None, softm
         _check(lse, "lse", (T, HEADS), dtype=torch.float32, device=dev)
     nbytes = attend_workspace_bytes(T, k, window, 1)
     workspace = _ws(nbytes, dev, workspace)
-    st = lib().csa2_attend_fp4(_p(q), _p(kv_fp4), _p(kv_scale), _p(indices), _p(swa), _p(swa_end), _p(sink),
+    st = _call("csa2_attend_fp4", _p(q), _p(kv_fp4), _p(kv_scale), _p(indices), _p(swa), _p(swa_end), _p(sink),
                                float(softmax_scale), T, q_per_seq, N, S, window, k, _p(out), _p(lse),
                                _p(workspace), _nbytes(workspace), _stream(q))
     _raise(st, "csa2_attend_fp4")
@@ -503,7 +563,7 @@ def csa2_reuse_attend(q, kv_fp4, kv_scale, indices, swa, swa_end, sink=None, sof
         _check(lse, "lse", (L, T, HEADS), dtype=torch.float32, device=dev)
     nbytes = attend_workspace_bytes(T, k, window, L)
     workspace = _ws(nbytes, dev, workspace)
-    st = lib().csa2_reuse_attend(L, _p(q), _p(kv_fp4), _p(kv_scale), _p(indices), _p(swa), _p(swa_end), _p(sink),
+    st = _call("csa2_reuse_attend", L, _p(q), _p(kv_fp4), _p(kv_scale), _p(indices), _p(swa), _p(swa_end), _p(sink),
                                  float(softmax_scale), T, q_per_seq, N, S, window, k, _p(out), _p(lse),
                                  _p(workspace), _nbytes(workspace), _stream(q))
     _raise(st, "csa2_reuse_attend")
@@ -555,7 +615,7 @@ def csa2_attend_ex(q, kv_codes, kv_scales, indices, swa_end, sink=None, softmax_
                        None if swa_rope is None else swa_rope.data_ptr(),
                        None if swa_scales is None else swa_scales.data_ptr(),
                        None if rope_pos is None else rope_pos.data_ptr(), float(rope_base))
-    st = lib().csa2_attend_ex(L, _p(q), _p(kv_codes), _p(kv_scales), _p(indices), _p(swa), _p(swa_end), _p(sink),
+    st = _call("csa2_attend_ex", L, _p(q), _p(kv_codes), _p(kv_scales), _p(indices), _p(swa), _p(swa_end), _p(sink),
                               float(softmax_scale), T, q_per_seq, N, S, window, TOPK, ctypes.byref(opts), _p(out),
                               _p(lse), _p(workspace), _nbytes(workspace), _stream(q))
     _raise(st, "csa2_attend_ex")
@@ -603,7 +663,7 @@ def csa2_kv_write(h, w_kv, w_ik, pos, m=1, w_z=None, rope_base=10000.0, kv_forma
         _check(k_out, "k_out", (n, IDX_DIM // 2), dtype=torch.uint8, device=dev)
         _check(k_scales, "k_scales", (n, IDX_DIM // 32), dtype=torch.uint8, device=dev)
     workspace = _ws(kv_write_workspace_bytes(n, m, d), dev, workspace)
-    st = lib().csa2_kv_write(_p(h), _p(w_kv), _p(w_z) if m > 1 else None, _p(w_ik), d, n, m, _p(pos),
+    st = _call("csa2_kv_write", _p(h), _p(w_kv), _p(w_z) if m > 1 else None, _p(w_ik), d, n, m, _p(pos),
                              float(rope_base), kv_format, _p(kv_codes), _p(kv_scales), k_format, _p(k_out),
                              _p(k_scales), _p(workspace), _nbytes(workspace), _stream(h))
     _raise(st, "csa2_kv_write")

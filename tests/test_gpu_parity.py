@@ -2,6 +2,7 @@
 at sizes the oracle finishes in seconds that still span several tiles and a
 ragged tail.  Indices must match bit-exactly; attention outputs within
 1e-2 absolute + 2e-2 relative (bf16 outputs)."""
+import dataclasses
 import math
 import sys
 
@@ -284,3 +285,40 @@ def test_generator_is_device_independent():
     cb, sb = G.mxfp4_quantize(x.to(DEV))
     assert torch.equal(ca, cb.cpu()) and torch.equal(sa, sb.cpu())
     assert torch.equal(G.uniform_f32(0, G.ST_W, 0, 5000, "cpu"), G.uniform_f32(0, G.ST_W, 0, 5000, DEV).cpu())
+
+
+def test_bound_calls_replay_the_wrappers():
+    """bind(): the recorded launches reproduce the wrapper calls bit for bit, read the bound
+    tensors' current contents on every call, and keep the storage they allocated alive."""
+    log("[bind] index -> topk -> attend, bound vs wrapped")
+    c = case("large_rows_ragged")
+    bf = torch.bfloat16
+    q_idx = c.q_idx.view(bf).clone()
+    ix = csa.bind(csa.csa2_index, q_idx, c.w_idx, c.k_idx.view(bf), c.q_pos, c.ratio, c.q_per_seq,
+                  want_scores=False)
+    tk = csa.bind(csa.csa2_topk, None, ix.result.tile_max, ix.result.stats, q_idx, c.w_idx, c.k_idx.view(bf),
+                  c.q_pos, c.ratio, c.q_per_seq)
+    at = csa.bind(csa.csa2_attend_fp4, c.q[0].view(bf), c.kv_codes, c.kv_scales, tk.result, c.swa[0].view(bf),
+                  c.swa_end, None, c.softmax_scale, c.q_per_seq, 128)
+    assert len(ix._calls) == 1 and ix._calls[0][2] == "csa2_index"
+    for round_ in range(2):
+        if round_ == 1:  # new query contents in the same storage
+            q_idx.copy_(G.normal_bf16(3, G.ST_QIDX, 0, q_idx.numel(), DEV).view(q_idx.shape).view(bf))
+        ix(), tk(), at()
+        w_ix = run_index(Ccase(c, q_idx), want_scores=False)
+        w_i = csa.csa2_topk(None, w_ix.tile_max, w_ix.stats, q_idx, c.w_idx, c.k_idx.view(bf), c.q_pos, c.ratio,
+                            c.q_per_seq)
+        w_o = csa.csa2_attend_fp4(c.q[0].view(bf), c.kv_codes, c.kv_scales, w_i, c.swa[0].view(bf), c.swa_end,
+                                  None, c.softmax_scale, c.q_per_seq, 128)
+        torch.cuda.synchronize()
+        assert torch.equal(tk.result, w_i), f"round {round_}: bound indices differ"
+        assert torch.equal(at.result, w_o), f"round {round_}: bound attention differs"
+    cc = Ccase(c, q_idx)
+    ref = oracle_topk(cc, oracle_scores(cc, range(c.T)))
+    for t in range(c.T):
+        assert np.array_equal(npy(tk.result[t]), ref[t]), f"t={t}: bound indices differ from the oracle"
+
+
+def Ccase(c, q_idx):
+    """Case c with another indexer query (same storage layout)."""
+    return dataclasses.replace(c, q_idx=q_idx.view(c.q_idx.dtype))
