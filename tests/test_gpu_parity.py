@@ -322,3 +322,57 @@ def test_bound_calls_replay_the_wrappers():
 def Ccase(c, q_idx):
     """Case c with another indexer query (same storage layout)."""
     return dataclasses.replace(c, q_idx=q_idx.view(c.q_idx.dtype))
+
+
+def test_step_graph_replays_match_eager():
+    """The decode step (scan -> top-k from tile maxima -> attention -> three Reuse layers)
+    captured in a HIP graph: every replay, with eager work and synchronisations between
+    replays, reproduces the eager outputs bit for bit (the library records no memset and
+    no host synchronisation, and resets its counters in-kernel)."""
+    log("[graph] step capture and replays")
+    c = G.make_case("graph", B=2, N=40001, n_layers=4, seed=11, device=DEV)
+    bf = torch.bfloat16
+    T, N = c.T, c.N
+    tile_max = torch.empty((T, csa.tile_max_ld(N)), dtype=torch.float32, device=DEV)
+    stats = torch.empty(csa.index_stats_bytes(T, c.q_per_seq, N) // 4, dtype=torch.int32, device=DEV)
+    idx = torch.empty((T, 512), dtype=torch.int32, device=DEV)
+    out = torch.empty((T, 64, 512), dtype=bf, device=DEV)
+    out_re = torch.empty((c.n_layers - 1, T, 64, 512), dtype=bf, device=DEV)
+    ws_t = torch.empty(csa.topk_workspace_bytes(T, N), dtype=torch.uint8, device=DEV)
+    ws_a = torch.empty(max(1, csa.attend_workspace_bytes(T)), dtype=torch.uint8, device=DEV)
+    ws_r = torch.empty(max(1, csa.attend_workspace_bytes(T, n_layers=c.n_layers - 1)), dtype=torch.uint8, device=DEV)
+    q_re = c.q[1:].view(bf).contiguous()
+    swa_re = c.swa[1:].view(bf).contiguous()
+
+    def step():
+        csa.csa2_index(c.q_idx.view(bf), c.w_idx, c.k_idx.view(bf), c.q_pos, c.ratio, c.q_per_seq,
+                       want_scores=False, tile_max=tile_max, stats=stats)
+        csa.csa2_topk(None, tile_max, stats, c.q_idx.view(bf), c.w_idx, c.k_idx.view(bf), c.q_pos, c.ratio,
+                      c.q_per_seq, indices=idx, workspace=ws_t)
+        csa.csa2_attend_fp4(c.q[0].view(bf), c.kv_codes, c.kv_scales, idx, c.swa[0].view(bf), c.swa_end, None,
+                            c.softmax_scale, c.q_per_seq, 128, out=out, workspace=ws_a)
+        csa.csa2_reuse_attend(q_re, c.kv_codes, c.kv_scales, idx, swa_re, c.swa_end, None, c.softmax_scale,
+                              c.q_per_seq, 128, out=out_re, workspace=ws_r)
+
+    step()
+    torch.cuda.synchronize()
+    ref = idx.clone(), out.clone(), out_re.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for r in range(4):
+        idx.fill_(-7), out.zero_(), out_re.zero_(), stats.fill_(123)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref[0]), f"replay {r}: indices differ"
+        assert torch.equal(out, ref[1]) and torch.equal(out_re, ref[2]), f"replay {r}: attention differs"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+    ref_idx = oracle_topk(c, oracle_scores(c, range(T)))
+    for t in range(T):
+        assert np.array_equal(npy(idx[t]), ref_idx[t])
