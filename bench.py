@@ -30,6 +30,8 @@ WORKLOADS = {
     "long_decode": dict(B=4, N=1 << 20),
     "batched_decode": dict(B=64, N=131072),
     "tiny_decode": dict(B=1, N=2048),
+    # 4096 query tokens after a 65536-token prefix, compression ratio 2 (not the headline: its own line)
+    "causal_prefill": dict(B=1, N=34816, q_per_seq=4096, ratio=2, prefix=65536),
 }
 
 
@@ -192,6 +194,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "causal_prefill":
+        return prefill_main(args, dev)
     wl = WORKLOADS[args.workload]
     B, N = wl["B"], wl["N"]
     print(f"[bench] generating {args.workload}: B={B} N={N}", file=sys.stderr, flush=True)
@@ -540,6 +544,127 @@ def cpu_baseline(c, G, min_seconds=10.0, max_seconds=30.0):
     return {"value": reps * c.T / dt, "unit": "queries/s", "cores": cores, "kind": "oracle",
             "sample": f"{reps} repetitions of the full {c.T}-query step of the same workload (index over all "
                       f"{c.N} entries per sequence, top-512, attention), {dt:.1f} s wall on {cores} threads"}
+
+
+def prefill_main(args, dev):
+    """The causal prefill chunk: csa2_index (score matrix written) + csa2_topk (row regime) +
+    csa2_attend_fp4 for 4096 queries over 34816 compressed entries (ratio 2); one JSON line with
+    the scan against the bf16 MFMA roofline (the indexer product is a dense GEMM here)."""
+    import torch
+
+    import compressed_sparse_attention_02_amd as csa
+    import csa2_gen as G
+
+    wl = WORKLOADS["causal_prefill"]
+    print("[bench] generating causal_prefill", file=sys.stderr, flush=True)
+    c = G.make_case("causal_prefill", **wl, seed=0, device=dev, chunk_rows=1 << 19)
+    T, N = c.T, c.N
+    bf = torch.bfloat16
+    idx_args = (c.q_idx.view(bf), c.w_idx, c.k_idx.view(bf), c.q_pos, c.ratio, c.q_per_seq)
+    scores = torch.empty((T, N), dtype=torch.float32, device=dev)
+    tile_max = torch.empty((T, csa.tile_max_ld(N)), dtype=torch.float32, device=dev)
+    stats = torch.empty(csa.index_stats_bytes(T, c.q_per_seq, N) // 4, dtype=torch.int32, device=dev)
+    idx = torch.empty((T, 512), dtype=torch.int32, device=dev)
+    out = torch.empty((T, 64, 512), dtype=bf, device=dev)
+    ws_t = torch.empty(csa.topk_workspace_bytes(T, N), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(1, csa.attend_workspace_bytes(T)), dtype=torch.uint8, device=dev)
+    do_index = csa.bind(csa.csa2_index, *idx_args, want_scores=True, scores=scores, tile_max=tile_max, stats=stats)
+    do_topk = csa.bind(csa.csa2_topk, scores, tile_max, stats, *idx_args, indices=idx, workspace=ws_t)
+    do_attend = csa.bind(csa.csa2_attend_fp4, c.q[0].view(bf), c.kv_codes, c.kv_scales, idx, c.swa[0].view(bf),
+                         c.swa_end, None, c.softmax_scale, c.q_per_seq, c.window, out=out, workspace=ws_a)
+
+    def step():
+        do_index()
+        do_topk()
+        do_attend()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    print(f"[bench] {args.steps} steps timed: {ms_step:.4f} ms per step", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        return ts[len(ts) // 2], sum(ts) / len(ts)
+
+    reps = max(5, min(args.steps, 20))
+    idx_med, idx_avg = timed(do_index, reps)
+    topk_med, _ = timed(do_topk, reps)
+    att_med, att_avg = timed(do_attend, reps)
+    # the indexer GEMM: 2 x 32 heads x 128 channels per visible (query, entry) pair
+    n_vis = sum(min(N, (p + 1) // c.ratio) for p in c.q_pos.tolist())
+    idx_flops = 2 * 32 * 128 * n_vis
+    att_flops = T * 2 * (2 * 64 * (512 + c.window) * 512)
+    idx_tflops = idx_flops / (idx_avg * 1e-6) / 1e12
+    line = {
+        "metric": "decode queries/s + achieved HBM GB/s (% peak), CSA2 top-512 FP4 attn at 1 GPU",
+        "value": T / (ms_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "causal_prefill", "queries": T, "prefix_tokens": 65536, "ratio": c.ratio,
+                   "entries": N, "indexer": "32x128 bf16", "topk": 512, "heads": 64, "head_dim": 512,
+                   "window": c.window, "main_kv": "MXFP4 E2M1+E8M0/32", "parallelism": "none (1 GPU)"},
+        "roofline": {"kernel": "idx_scan_kernel (all of csa2_index, score matrix written)", "bound": "mfma",
+                     "achieved": idx_tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": idx_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "algorithmic_flops_per_launch": idx_flops, "avg_launch_us": idx_avg},
+        "stages_us": {"index": idx_med, "topk_rows": topk_med, "attend": att_med},
+        "attention": {"call": "csa2_attend_fp4 (one work item per query)", "avg_us": att_avg, "flops": att_flops,
+                      "TFLOPs": att_flops / (att_avg * 1e-6) / 1e12,
+                      "frac_mfma_bf16": att_flops / (att_avg * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "mfma_bound_ms": (idx_flops + att_flops) / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_prefill(c, G)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline_prefill(c, G, n_sample=8, min_seconds=10.0, max_seconds=30.0):
+    """The oracle (as is) on this host's cores over a sample of the chunk's queries (the last
+    n_sample, which see the most entries): index, row top-512, attention."""
+    import numpy as np
+
+    import oracle
+
+    def u16(t):
+        return np.ascontiguousarray(t.cpu().view(__import__("torch").int16).numpy().view(np.uint16))
+
+    t0_q = c.T - n_sample
+    q_idx, w = u16(c.q_idx[t0_q:]), c.w_idx[t0_q:].cpu().numpy()
+    k = u16(c.k_idx)
+    q_pos = c.q_pos[t0_q:].cpu().numpy()
+    q, swa = u16(c.q[0][t0_q:]), u16(c.swa[0])
+    codes, scales = c.kv_codes.cpu().numpy(), c.kv_scales.cpu().numpy()
+    swa_end = c.swa_end[t0_q:].cpu().numpy()
+    oracle.lib()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        sc = oracle.index(q_idx, w, k, q_pos, c.ratio, n_sample)
+        sel = oracle.topk(sc, q_pos, c.ratio, c.k)
+        oracle.attend(q, codes, scales, sel, swa, swa_end, None, c.softmax_scale, n_sample, c.window)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or dt * (reps + 1) / reps > max_seconds:
+            break
+    cores = min(n_sample, oracle.max_threads())
+    return {"value": reps * n_sample / dt, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} repetitions of the chunk's last {n_sample} queries (index over their "
+                      f"{int(q_pos[-1] + 1) // c.ratio} visible entries, top-512, attention), {dt:.1f} s wall "
+                      f"on {cores} threads"}
 
 
 if __name__ == "__main__":
