@@ -33,6 +33,7 @@ constexpr int kXTStride = kChunk + 8;   // bf16 elements per XT row (80 B)
 constexpr int kMaxSlots = (CSA2_TOPK + kChunk - 1) / kChunk + (CSA2_MAX_WINDOW + kChunk - 1) / kChunk;  // 20
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.f;  // log2 units: O and l rescaled only when the maximum grows by 2^8
 
 struct AttnArgs {
   const uint16_t* q;        // [L][T][64][512]
@@ -285,16 +286,22 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const AttnShared
   for (int i = 1; i < 8; ++i) cm = fmaxf(cm, z[i]);
   cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
   cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-  const float mn = fmaxf(st.m, cm);
-  if (mn == -INFINITY) return;  // nothing valid so far for this head (uniform per head)
-  const float alpha = exp2f(st.m - mn);  // st.m == -inf -> 0
+  const float mtrue = fmaxf(st.m, cm);
+  if (mtrue == -INFINITY) return;  // nothing valid so far for this head (uniform per head)
+  // Lazy rescaling: the reference maximum st.m stays while this chunk's scores
+  // exceed it by at most kRescaleSlack (log2 units), so p <= 2^kRescaleSlack,
+  // which bf16 and fp32 hold at full relative precision; (m, l, O) stay
+  // consistent, since l and O are both taken relative to st.m.
+  const bool grow = mtrue > st.m + kRescaleSlack;  // always on the first valid chunk
+  const float mn = grow ? mtrue : st.m;
+  const float alpha = exp2f(st.m - mn);  // st.m == -inf -> 0; 1 where the reference stays
   uint32_t pb[4];
   float psum = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float p0 = exp2f(z[2 * i] - mn), p1 = exp2f(z[2 * i + 1] - mn);
     psum += p0 + p1;
-    pb[i] = f32_to_bf16_rne(p0) | (f32_to_bf16_rne(p1) << 16);
+    pb[i] = pack_bf16x2_rne(p0, p1);
   }
   // a state with nothing folded in yet (every head of the wave) holds zeros: no rescale
   const bool fresh = __ballot(st.m != -INFINITY) == 0ull;
@@ -302,7 +309,7 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const AttnShared
   st.m = mn;
   bf16x8 pv;
   __builtin_memcpy(&pv, pb, 16);
-  if (!fresh) {
+  if (!fresh && __ballot(grow) != 0ull) {
 #pragma unroll
     for (int mb = 0; mb < 32; ++mb) st.o[mb] *= alpha;
   }
@@ -347,8 +354,8 @@ __device__ void write_final(const AttnArgs& a, const AttnShared& sh, const HeadS
         v[2 * p + 1] = x * sn + y * c;
       }
     }
-    const uint32_t w0 = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-    const uint32_t w1 = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+    const uint32_t w0 = pack_bf16x2_rne(v[0], v[1]);
+    const uint32_t w1 = pack_bf16x2_rne(v[2], v[3]);
     *reinterpret_cast<uint2*>(op + 16 * mb) = make_uint2(w0, w1);
   }
   if (a.lse && g == 0)
@@ -367,8 +374,8 @@ __device__ void write_partial(const AttnArgs& a, const HeadState& st, int layer,
   // are read once, by the combine kernel
 #pragma unroll
   for (int mb = 0; mb < 32; ++mb) {
-    const uint32_t w0 = f32_to_bf16_rne(st.o[mb][0]) | (f32_to_bf16_rne(st.o[mb][1]) << 16);
-    const uint32_t w1 = f32_to_bf16_rne(st.o[mb][2]) | (f32_to_bf16_rne(st.o[mb][3]) << 16);
+    const uint32_t w0 = pack_bf16x2_rne(st.o[mb][0], st.o[mb][1]);
+    const uint32_t w1 = pack_bf16x2_rne(st.o[mb][2], st.o[mb][3]);
     const u32x2 w = {w0, w1};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(op + 16 * mb));
   }
@@ -487,8 +494,8 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a) {
       v[2 * p + 1] = x * sn + y * c;
     }
   }
-  const uint32_t w0 = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-  const uint32_t w1 = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+  const uint32_t w0 = pack_bf16x2_rne(v[0], v[1]);
+  const uint32_t w1 = pack_bf16x2_rne(v[2], v[3]);
   *reinterpret_cast<uint2*>(op) = make_uint2(w0, w1);
 }
 
