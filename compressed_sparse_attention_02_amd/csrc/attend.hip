@@ -73,6 +73,13 @@ struct AttnShared {
 // blocks).
 __device__ __forceinline__ int head_wave() { return (int)(blockIdx.z * (blockDim.x >> 6) + (threadIdx.x >> 6)); }
 
+// Two fp32 values rounded to nearest-even bf16 and packed, lo in the low half
+// (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
 // 16-byte LDS operand read (the offsets used are multiples of 16 bytes).
 __device__ __forceinline__ bf16x8 lds_read16(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8*>(__builtin_assume_aligned(p, 16));

@@ -37,13 +37,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Two fp32 values rounded to nearest-even bf16 and packed, lo in the low half
-// (one v_cvt_pk_bf16_f32 on gfx950).
-__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
-
 // Order-preserving maps: larger float <-> larger unsigned key.
 __device__ __forceinline__ uint32_t f32_key(float f) {
   uint32_t u = __float_as_uint(f);
