@@ -33,6 +33,23 @@ __device__ __forceinline__ void load_head_weights(const float* __restrict__ w_t,
   for (int r = 0; r < 8; ++r) wr[r] = w_t[16 * (r >> 2) + 4 * g + (r & 3)];
 }
 
+// ReLU of a finite float as one integer maximum on its bits (negative values,
+// -0 included, have the sign bit set and become +0).
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// x + (x of lane l ^ 16), and x + (x of lane l ^ 32), with the gfx950 lane
+// swaps (v_permlane16_swap / v_permlane32_swap: after swapping a copy of x
+// with x, the two registers hold a lane's value and its partner's, so their sum
+// is the pairwise sum, the same in both lanes of a pair).
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // The score of key l % 16 from the two 16-head accumulator halves (register i
 // of half m: head 16m + 4(l/16) + i): ReLU, times the head's weight, summed
 // over the lane's 8 heads and then over the four lane groups of the column.
@@ -41,12 +58,10 @@ __device__ __forceinline__ float fold_heads(const floatx4& acc0, const floatx4& 
   float part = 0.f;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    part = fmaf(wr[r], fmaxf(acc0[r], 0.f), part);
-    part = fmaf(wr[4 + r], fmaxf(acc1[r], 0.f), part);
+    part = fmaf(wr[r], relu_bits(acc0[r]), part);
+    part = fmaf(wr[4 + r], relu_bits(acc1[r]), part);
   }
-  part += __shfl_xor(part, 16, 64);
-  part += __shfl_xor(part, 32, 64);
-  return part;
+  return sum_xor32(sum_xor16(part));
 }
 
 // fp32 score of key `col` of the tile, returned in every lane of that column
