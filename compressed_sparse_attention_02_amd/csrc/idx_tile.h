@@ -50,6 +50,24 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Maximum over each 16-lane row of scores (finite or -inf, never -0 or NaN),
+// in every lane of the row.  The scores go through order-preserving signed
+// keys (a float's bits, the magnitude bits flipped when negative), whose
+// maximum needs no canonicalisation, so each DPP row move (old value INT_MIN, the
+// identity) folds into one v_max_i32_dpp.  Partners i^1, i^2, 7-i within 8, 15-i within 16.
+__device__ __forceinline__ int score_key(float x) {
+  const int k = __float_as_int(x);
+  return k ^ ((k >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float row_max16(float x) {
+  int k = score_key(x);
+  k = max(k, __builtin_amdgcn_update_dpp(INT_MIN, k, kDppXor1, 0xF, 0xF, false));
+  k = max(k, __builtin_amdgcn_update_dpp(INT_MIN, k, kDppXor2, 0xF, 0xF, false));
+  k = max(k, __builtin_amdgcn_update_dpp(INT_MIN, k, kDppHalfMirror, 0xF, 0xF, false));
+  k = max(k, __builtin_amdgcn_update_dpp(INT_MIN, k, kDppMirror, 0xF, 0xF, false));
+  return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF));
+}
+
 // The score of key l % 16 from the two 16-head accumulator halves (register i
 // of half m: head 16m + 4(l/16) + i): ReLU, times the head's weight, summed
 // over the lane's 8 heads and then over the four lane groups of the column.

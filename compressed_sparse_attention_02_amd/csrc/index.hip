@@ -125,11 +125,7 @@ __global__ __launch_bounds__(kScanThreads, QG == 1 ? 6 : QG == 2 ? 4 : 2) void i
 #pragma unroll
       for (int u = 0; u < kScanTiles; ++u) {
         // maximum over the 16 keys of the tile (one 16-lane row) with DPP moves
-        float tm = sc[qq][u];
-        tm = fmaxf(tm, dpp_f32<kDppXor1>(tm));
-        tm = fmaxf(tm, dpp_f32<kDppXor2>(tm));
-        tm = fmaxf(tm, dpp_f32<kDppHalfMirror>(tm));
-        tm = fmaxf(tm, dpp_f32<kDppMirror>(tm));
+        const float tm = row_max16(sc[qq][u]);
         if (u > 0) v = g == u ? sc[qq][u] : v;
         m = lane == u ? tm : m;
       }

@@ -117,11 +117,7 @@ __global__ __launch_bounds__(kMxThreads) void idx_scan_mx_kernel(
       float v0 = sc[qq][0], v1 = sc[qq][4], m = -INFINITY;
 #pragma unroll
       for (int u = 0; u < kMxTiles; ++u) {
-        float tm = sc[qq][u];
-        tm = fmaxf(tm, dpp_f32<kDppXor1>(tm));
-        tm = fmaxf(tm, dpp_f32<kDppXor2>(tm));
-        tm = fmaxf(tm, dpp_f32<kDppHalfMirror>(tm));
-        tm = fmaxf(tm, dpp_f32<kDppMirror>(tm));
+        const float tm = row_max16(sc[qq][u]);
         if (u > 0 && u < 4) v0 = g == u ? sc[qq][u] : v0;
         if (u > 4) v1 = g == u - 4 ? sc[qq][u] : v1;
         m = lane == u ? tm : m;
