@@ -558,11 +558,14 @@ void csa2o_kv_write(const uint16_t* h, const uint16_t* w_kv, const uint16_t* w_z
             double acc = 0.0;
             for (int ch = 0; ch < DIM; ++ch) acc += c[ch] * bf16_to_double(w_ik[(int64_t)ch * IDX_DIM + o]);
             k[(int64_t)e * IDX_DIM + o] = acc;
-            /* nearest bf16, ties to even, via float (every double here is a sum of products of bf16 values) */
-            float f = (float)acc;
+            /* nearest bf16, ties to even, taken once from the fp64 sum (a 512-term sum
+             * can carry more significant bits than fp32 holds, so no fp32 step in
+             * between); the rounded value is a bf16 value, so the float conversion of
+             * it is exact and its top 16 bits are the bf16 pattern */
+            float f = (float)csa2o_bf16_round(acc);
             uint32_t u;
             memcpy(&u, &f, 4);
-            k_bf16[(int64_t)e * IDX_DIM + o] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+            k_bf16[(int64_t)e * IDX_DIM + o] = (uint16_t)(u >> 16);
         }
         csa2o_rope_rotate(c, (double)pos[e], rope_base);
         if (kv_format == 0) {

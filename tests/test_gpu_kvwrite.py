@@ -105,15 +105,26 @@ def bf16_to_f64(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def nearest_even_bf16_bits(x):
+    """bf16 bit patterns of the fp64 values x rounded once to 8 significant bits, ties to
+    the even significand (normal range only, which holds for these keys)."""
+    f, e = np.frexp(x)
+    r = np.ldexp(np.rint(np.ldexp(f, 8)), e - 8)
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
 def check_k_bf16(k_gpu_bits, k_exact, k_or_bits, what, atol=1e-6):
     """Device keys (bf16) against the exact keys: within bf16 rounding plus atol (the
     fp32 accumulation error, which dominates for keys near zero), and equal to the
-    oracle's bf16 except where the exact key is that close to a rounding midpoint."""
+    direct nearest-even rounding of the exact key (which the oracle's bf16 keys are)
+    except where the exact key is that close to a rounding midpoint."""
+    direct = nearest_even_bf16_bits(k_exact)
+    assert np.array_equal(k_or_bits, direct), f"{what}: oracle keys are not the direct rounding"
     kg = bf16_to_f64(k_gpu_bits)
     err = np.abs(kg - k_exact) - 2.0 ** -8 * np.abs(k_exact)
     worst = np.unravel_index(np.argmax(err), err.shape)
     assert err.max() <= atol, f"{what}: at {worst} device {kg[worst]!r} exact {k_exact[worst]!r}"
-    diff = k_gpu_bits != k_or_bits
+    diff = k_gpu_bits != direct
     if diff.any():
         k = np.abs(k_exact[diff])
         ulp = np.exp2(np.floor(np.log2(k)) - 7)

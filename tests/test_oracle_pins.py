@@ -775,6 +775,40 @@ def test_kv_write_closed_forms(oracle_lib):
     assert np.allclose(r3["entry"], h3v[0::2], rtol=1e-12, atol=1e-12)
 
 
+def test_kv_write_key_rounds_once_from_the_exact_sum(oracle_lib):
+    """The bf16 indexer key is the nearest-even rounding of the exact (fp64) projection,
+    taken once.  Keys built from three exact terms (identity W_kv, unit W_ik weights on
+    channels 0..2) land on either side of bf16 midpoints by 2^-30, an offset that fp32
+    cannot hold: rounding through fp32 first would turn them into ties and pick the even
+    neighbour instead.  Expected bit patterns worked by hand (bf16 of 1 is 0x3F80, one
+    bf16 step at 1 is 2^-7)."""
+    import oracle
+    d = 512
+    eye = _bits(np.eye(d, 512))
+    cases = [  # (channel 0, 1, 2 of the entry) -> key bits
+        ((1.0, 2.0 ** -8, 2.0 ** -30), 0x3F81),      # just above the midpoint 1 + 2^-8: up
+        ((1.0, 2.0 ** -8, -2.0 ** -30), 0x3F80),     # just below it: down
+        ((1.0, 2.0 ** -8, 0.0), 0x3F80),             # the midpoint itself: to the even 1.0
+        ((1.0, 3 * 2.0 ** -8, 0.0), 0x3F82),         # midpoint 1 + 3*2^-8: to the even 1 + 2^-6
+        ((1.0, 3 * 2.0 ** -8, -2.0 ** -30), 0x3F81), # just below that midpoint: down to 1 + 2^-7
+        ((-1.0, -2.0 ** -8, -2.0 ** -30), 0xBF81),   # the sign is symmetric
+        ((2.0 ** 20, 2.0 ** 12, 2.0 ** -8), 0x4981),  # 2^20 + 2^12 + 2^-8: above the tie, up to 2^20 + 2^13
+    ]
+    n = len(cases)
+    h = np.zeros((n, d), np.float32)
+    for e, (vals, _) in enumerate(cases):
+        h[e, :3] = vals
+    hb = _bits(h)
+    assert np.array_equal((hb.astype(np.uint32) << 16).view(np.float32), h)   # the terms are bf16 values
+    w_ik = np.zeros((512, 128), np.float32)
+    w_ik[:3, 0] = 1.0
+    r = oracle.kv_write(hb, eye, None, _bits(w_ik), 1, np.zeros(n, np.int32))
+    for e, (vals, want) in enumerate(cases):
+        assert r["k"][e, 0] == sum(vals)
+        assert int(r["k_bf16"][e, 0]) == want, (vals, hex(int(r["k_bf16"][e, 0])), hex(want))
+    assert not r["k_bf16"][:, 1:].any()
+
+
 def test_bf16_round_golden(oracle_lib):
     """The score rounding of the BF16 selector: hand-worked values, ties, the binade carry,
     the sub-normal quantum, overflow, and one case that fp32-then-bf16 would round differently."""
