@@ -590,6 +590,8 @@ def csa2_attend_ex(q, kv_codes, kv_scales, indices, swa_end, sink=None, softmax_
     _check(kv_scales, "kv_scales", (B, N, DIM // (32 if kv_format == KV_MXFP4 else 16)), dtype=torch.uint8, device=dev)
     _check(indices, "indices", (T, TOPK), dtype=torch.int32, device=dev)
     _check(swa_end, "swa_end", (T,), dtype=torch.int32, device=dev)
+    if (swa is None) == (swa_fp8 is None):
+        raise ValueError("give the window either as bf16 rows (swa) or as FP8 rows (swa_fp8, swa_rope, swa_scales)")
     if swa is not None:
         S = swa.shape[-2]
         _check(swa, "swa", lay + (B, S, DIM), elem_size=2, device=dev)
@@ -608,18 +610,22 @@ def csa2_attend_ex(q, kv_codes, kv_scales, indices, swa_end, sink=None, softmax_
         raise ValueError(f"T={T} must equal B*q_per_seq={B}*{q_per_seq}")
     if out is None:
         out = torch.empty(lay + (T, HEADS, DIM), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", lay + (T, HEADS, DIM), elem_size=2, device=dev)
     if lse is None and want_lse:
         lse = torch.empty(lay + (T, HEADS), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", lay + (T, HEADS), dtype=torch.float32, device=dev)
     workspace = _ws(attend_workspace_bytes(T, TOPK, window, L), dev, workspace)
-    opts = _AttendOpts(kv_format, fmt, None if swa_fp8 is None else swa_fp8.data_ptr(),
-                       None if swa_rope is None else swa_rope.data_ptr(),
-                       None if swa_scales is None else swa_scales.data_ptr(),
-                       None if rope_pos is None else rope_pos.data_ptr(), float(rope_base))
+
+    def ptr(t):  # through _p, so that bind() keeps these tensors alive too
+        return None if t is None else _p(t).value
+
+    opts = _AttendOpts(kv_format, fmt, ptr(swa_fp8), ptr(swa_rope), ptr(swa_scales), ptr(rope_pos), float(rope_base))
     st = _call("csa2_attend_ex", L, _p(q), _p(kv_codes), _p(kv_scales), _p(indices), _p(swa), _p(swa_end), _p(sink),
                               float(softmax_scale), T, q_per_seq, N, S, window, TOPK, ctypes.byref(opts), _p(out),
                               _p(lse), _p(workspace), _nbytes(workspace), _stream(q))
     _raise(st, "csa2_attend_ex")
-    return (out, lse) if want_lse else out
+    return (out, lse) if (want_lse or lse is not None) else out
 
 
 def kv_write_workspace_bytes(n_ent: int, m: int, d: int) -> int:

@@ -283,3 +283,95 @@ def test_binding_fails_loudly_without_gpu_tensors():
     with pytest.raises(ValueError):
         csa.csa2_index(torch.zeros(1, 32, 128, dtype=torch.bfloat16), torch.zeros(1, 32),
                        torch.zeros(1, 64, 128, dtype=torch.bfloat16))
+
+
+def _attend_ex_cpu_args(T=2, N=64, S=130, fp8=True):
+    """Host tensors shaped as csa2_attend_ex expects (one layer, MXFP4 main KV)."""
+    import torch
+    bf = torch.bfloat16
+    a = dict(q=torch.zeros(T, csa.HEADS, csa.DIM, dtype=bf),
+             kv_codes=torch.zeros(T, N, csa.DIM // 2, dtype=torch.uint8),
+             kv_scales=torch.zeros(T, N, csa.DIM // 32, dtype=torch.uint8),
+             indices=torch.zeros(T, csa.TOPK, dtype=torch.int32), swa_end=torch.zeros(T, dtype=torch.int32),
+             rope_pos=torch.zeros(T, dtype=torch.int32))
+    if fp8:
+        a.update(swa_fp8=torch.zeros(T, S, 448, dtype=torch.uint8), swa_rope=torch.zeros(T, S, 64, dtype=bf),
+                 swa_scales=torch.zeros(T, S, 8, dtype=torch.uint8))
+    else:
+        a.update(swa=torch.zeros(T, S, csa.DIM, dtype=bf))
+    return a
+
+
+@pytest.fixture
+def host_binding(monkeypatch):
+    """The binding with its device-type test and stream lookup taken out, so that its argument
+    checks and marshalling can be exercised on host tensors (nothing is launched: calls are
+    only recorded through bind())."""
+    import torch
+    seen = {}
+    orig = csa._check
+
+    def check(t, name, shape, elem_size=None, dtype=None, device=None):
+        seen[name] = tuple(shape)
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(name)
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(name)
+        if elem_size is not None and t.element_size() != elem_size:
+            raise TypeError(name)
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+    monkeypatch.setattr(csa, "_check", check)
+    monkeypatch.setattr(csa, "_stream", lambda t: None)
+    assert orig is not check
+    return seen
+
+
+def test_attend_ex_checks_caller_outputs(host_binding):
+    import torch
+    a = _attend_ex_cpu_args()
+    b = csa.bind(csa.csa2_attend_ex, **a, out=torch.zeros(2, csa.HEADS, csa.DIM, dtype=torch.bfloat16),
+                 lse=torch.zeros(2, csa.HEADS))
+    assert host_binding["out"] == (2, csa.HEADS, csa.DIM) and host_binding["lse"] == (2, csa.HEADS)
+    assert isinstance(b.result, tuple)                      # a caller-supplied lse is returned
+    with pytest.raises(ValueError):                          # short output buffer
+        csa.bind(csa.csa2_attend_ex, **a, out=torch.zeros(1, csa.HEADS, csa.DIM, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):                           # wrong element size
+        csa.bind(csa.csa2_attend_ex, **a, out=torch.zeros(2, csa.HEADS, csa.DIM))
+    with pytest.raises(ValueError):                          # not contiguous
+        o = torch.zeros(2, csa.DIM, csa.HEADS, dtype=torch.bfloat16).transpose(1, 2)
+        csa.bind(csa.csa2_attend_ex, **a, out=o)
+    with pytest.raises(ValueError):                          # lse of another layout
+        csa.bind(csa.csa2_attend_ex, **a, lse=torch.zeros(2, csa.HEADS + 1))
+    with pytest.raises(TypeError):
+        csa.bind(csa.csa2_attend_ex, **a, lse=torch.zeros(2, csa.HEADS, dtype=torch.float64))
+
+
+def test_attend_ex_window_must_be_given_once(host_binding):
+    import torch
+    a = _attend_ex_cpu_args()
+    for k in ("swa_fp8", "swa_rope", "swa_scales"):
+        a.pop(k)
+    with pytest.raises(ValueError, match="window"):
+        csa.bind(csa.csa2_attend_ex, **a)
+    a["swa"] = torch.zeros(2, 130, csa.DIM, dtype=torch.bfloat16)
+    a["swa_fp8"] = torch.zeros(2, 130, 448, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="window"):
+        csa.bind(csa.csa2_attend_ex, **a)
+
+
+def test_attend_ex_bind_keeps_option_tensors(host_binding):
+    """The FP8 window arrays and the rotation positions travel in an options struct; bind()
+    must hold them like every other tensor whose pointer it passes."""
+    a = _attend_ex_cpu_args()
+    b = csa.bind(csa.csa2_attend_ex, **a)
+    held = {id(t) for t in b._tensors}
+    for k in ("swa_fp8", "swa_rope", "swa_scales", "rope_pos", "q", "indices"):
+        assert id(a[k]) in held, k
+    (fn, args, name), = b._calls
+    opts = args[15]._obj
+    assert name == "csa2_attend_ex" and opts.swa_fp8 == a["swa_fp8"].data_ptr()
+    assert opts.rope_pos == a["rope_pos"].data_ptr() and opts.swa_format == csa.SWA_FP8
