@@ -35,7 +35,10 @@ SELECT_EXACT, SELECT_BF16 = 0, 1
 HSI_POOL = HSI_BLOCK * HSI_BLOCKS
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libcsa2.so")
+# CSA2_SANITIZE=1 loads the build whose host code carries AddressSanitizer and
+# UndefinedBehaviorSanitizer (build.py --sanitize; clang's runtime must be preloaded)
+library_path = os.path.join(_HERE, "libcsa2_san.so" if os.environ.get("CSA2_SANITIZE", "") not in ("", "0")
+                            else "libcsa2.so")
 _lib = None
 
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t

@@ -17,18 +17,28 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra=()) -> str:
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer (the argument checks and launch code of
+# every entry point; device code is built as usual), for CPU test runs with clang's runtime
+# preloaded.  Each sanitizer flag applies to the host compilation only.
+LIB_SAN = os.path.join(HERE, "libcsa2_san.so")
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g0"]
+
+
+def build(verbose: bool = False, extra=(), sanitize: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    cmd = [hipcc, *FLAGS, *extra, *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
+    out = LIB_SAN if sanitize else LIB
+    san = HOST_SANITIZE if sanitize else []
+    cmd = [hipcc, *FLAGS, *san, *extra, *[os.path.join(CSRC, s) for s in SOURCES], "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{errs}")
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

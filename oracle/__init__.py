@@ -19,22 +19,36 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csa2_oracle.c")
-LIB = os.path.join(HERE, "libcsa2_oracle.so")
+LIB_PLAIN = os.path.join(HERE, "libcsa2_oracle.so")
+# AddressSanitizer + UndefinedBehaviorSanitizer build (clang, its runtime preloaded into the
+# test process): CSA2_SANITIZE=1 selects it, for the oracle and the HIP library's host code alike
+LIB_SAN = os.path.join(HERE, "libcsa2_oracle_san.so")
+SANITIZE = os.environ.get("CSA2_SANITIZE", "") not in ("", "0")
+LIB = LIB_SAN if SANITIZE else LIB_PLAIN
+CLANG = "/opt/rocm/llvm/bin/clang"
 
 IDX_HEADS, IDX_DIM, HEADS, DIM = 32, 128, 64, 512
 
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (fp64, no fast-math, no contraction)."""
-    if force or not os.path.exists(LIB):
-        cmd = ["gcc", "-O2", "-mfma", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
-               "-shared", "-fPIC", "-std=c11", "-Wall", "-Wextra", "-Werror",
-               SRC, "-o", LIB + ".tmp", "-lm"]
+def build(force: bool = True, sanitize: bool = None) -> str:
+    """Compile the oracle with gcc (fp64, no fast-math, no contraction); with sanitize (default:
+    CSA2_SANITIZE set) the same flags under clang with AddressSanitizer and UndefinedBehavior-
+    Sanitizer (any report aborts)."""
+    san = SANITIZE if sanitize is None else sanitize
+    out = LIB_SAN if san else LIB_PLAIN
+    if force or not os.path.exists(out):
+        common = ["-O2", "-mfma", "-ffp-contract=off", "-fno-fast-math", "-shared", "-fPIC", "-std=c11",
+                  "-Wall", "-Wextra", "-Werror"]
+        if san:
+            cmd = [CLANG, *common, "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                   "-fno-sanitize-recover=all", "-fopenmp", SRC, "-o", out + ".tmp", "-lm"]
+        else:
+            cmd = ["gcc", *common, "-fopenmp", SRC, "-o", out + ".tmp", "-lm"]
         subprocess.check_call(cmd)
-        os.replace(LIB + ".tmp", LIB)
-    return LIB
+        os.replace(out + ".tmp", out)
+    return out
 
 
 def lib():
@@ -45,6 +59,7 @@ def lib():
         L = ctypes.CDLL(LIB)
         vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         L.csa2o_max_threads.argtypes, L.csa2o_max_threads.restype = [], i32
+        L.csa2o_set_threads.argtypes, L.csa2o_set_threads.restype = [i32], i32
         L.csa2o_e2m1.argtypes, L.csa2o_e2m1.restype = [ctypes.c_uint32], dbl
         L.csa2o_e8m0.argtypes, L.csa2o_e8m0.restype = [ctypes.c_uint32], dbl
         L.csa2o_dequant_row.argtypes, L.csa2o_dequant_row.restype = [vp, vp, i32, vp], None
@@ -92,6 +107,11 @@ def _c(a, dtype):
 
 def max_threads() -> int:
     return lib().csa2o_max_threads()
+
+
+def set_threads(n: int) -> int:
+    """Thread count of the oracle's OpenMP loops; returns the previous one."""
+    return lib().csa2o_set_threads(int(n))
 
 
 def e2m1(code: int) -> float:

@@ -32,6 +32,18 @@ int32_t csa2o_max_threads(void) {
 #endif
 }
 
+/* Set the thread count of the OpenMP loops below (n >= 1); returns the previous one.  The
+ * results do not depend on it: threads only split independent queries or score chunks. */
+int32_t csa2o_set_threads(int32_t n) {
+    int32_t prev = csa2o_max_threads();
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+    return prev;
+}
+
 /* ---- formats ------------------------------------------------------------ */
 
 /* bf16 bit pattern -> double (exact). */

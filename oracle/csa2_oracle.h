@@ -35,6 +35,7 @@ extern "C" {
 
 /* Threads the oracle's parallel loops use. */
 int32_t csa2o_max_threads(void);
+int32_t csa2o_set_threads(int32_t n);
 
 /* Value of one E2M1 code (OCP MX): sign bit 3, magnitudes {0,.5,1,1.5,2,3,4,6}. */
 double csa2o_e2m1(uint32_t code);

@@ -375,3 +375,15 @@ def test_attend_ex_bind_keeps_option_tensors(host_binding):
     opts = args[15]._obj
     assert name == "csa2_attend_ex" and opts.swa_fp8 == a["swa_fp8"].data_ptr()
     assert opts.rope_pos == a["rope_pos"].data_ptr() and opts.swa_format == csa.SWA_FP8
+
+
+@pytest.mark.skipif(os.environ.get("CSA2_SANITIZE", "") in ("", "0"), reason="sanitized CPU run not requested")
+def test_sanitized_builds_are_loaded():
+    """Under CSA2_SANITIZE=1 (with clang's ASan runtime preloaded) the suite runs the oracle and
+    the library's host code built with AddressSanitizer and UndefinedBehaviorSanitizer."""
+    import oracle
+    csa.lib()
+    oracle.lib()
+    maps = open("/proc/self/maps").read()
+    assert "libcsa2_san.so" in maps and "libcsa2_oracle_san.so" in maps
+    assert "libclang_rt.asan" in maps
