@@ -30,9 +30,13 @@ WORKLOADS = {
     "long_decode": dict(B=4, N=1 << 20),
     "batched_decode": dict(B=64, N=131072),
     "tiny_decode": dict(B=1, N=2048),
-    # 4096 query tokens after a 65536-token prefix, compression ratio 2 (not the headline: its own line)
+    # one Full layer (index, top-512, attention) and three Reuse layers over its selection
+    "reuse_group": dict(B=32, N=262144),
+    # 4096 query tokens after a 65536-token prefix, compression ratio 2
     "causal_prefill": dict(B=1, N=34816, q_per_seq=4096, ratio=2, prefix=65536),
 }
+# the workloads reported beside the headline in the default run (sub-objects of its line)
+SIDE_WORKLOADS = ("batched_decode", "reuse_group", "causal_prefill")
 
 
 def parse():
@@ -42,6 +46,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--no-side-workloads", action="store_true",
+                    help="time only the headline workload (by default the batched-decode, reuse-group and "
+                         "causal-prefill workloads follow it as sub-objects of the same line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run torch.neg over 1 GiB of fp32 (reads and writes 1 GiB: the reference dispatch "
                          "that scales rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -196,6 +203,10 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload == "causal_prefill":
         return prefill_main(args, dev)
+    if args.workload == "reuse_group":
+        line = {"metric": METRIC, **reuse_group_section(args, dev)}
+        print(json.dumps(line), flush=True)
+        return 0
     wl = WORKLOADS[args.workload]
     B, N = wl["B"], wl["N"]
     print(f"[bench] generating {args.workload}: B={B} N={N}", file=sys.stderr, flush=True)
@@ -341,7 +352,7 @@ def main():
         del xf, yf
 
     line = {
-        "metric": "decode queries/s + achieved HBM GB/s (% peak), CSA2 top-512 FP4 attn at 1 GPU",
+        "metric": METRIC,
         "value": T / (ms_step * 1e-3),
         "unit": "queries/s",
         "n_gpus": 1,
@@ -377,8 +388,209 @@ def main():
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(c, G)
+    if args.workload == "long_decode" and not args.no_side_workloads:
+        # the other workloads, each on its own inputs (the headline's are freed first)
+        del c, q_idx, k_idx, q0, swa0, q_re, swa_re, scores, tile_max, stats, out, out_re, ws_t, ws_a, ws_r
+        del pool, ws_p, ws_x, q_x, w_x, do_index, do_topk, do_topk_bf16, do_attend, do_reuse, do_pool, do_reindex
+        torch.cuda.empty_cache()
+        side = {}
+        for name in SIDE_WORKLOADS:
+            print(f"[bench] side workload {name}", file=sys.stderr, flush=True)
+            if name == "causal_prefill":
+                side[name] = prefill_section(args, dev)
+            elif name == "reuse_group":
+                side[name] = reuse_group_section(args, dev)
+            else:
+                side[name] = decode_section(args, dev, name)
+            torch.cuda.empty_cache()
+            print(f"[bench] side workload {name}: {side[name]['ms_per_step']:.4f} ms per step", file=sys.stderr,
+                  flush=True)
+        line["workloads"] = side
     print(json.dumps(line), flush=True)
     return 0
+
+
+METRIC = "decode queries/s + achieved HBM GB/s (% peak), CSA2 top-512 FP4 attn at 1 GPU"
+
+
+def _timer(stream):
+    """Median and mean duration (us) of fn() over reps runs, from HIP events recorded on the
+    launch stream around each run."""
+    import torch
+
+    def timed(fn, reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        return ts[len(ts) // 2], sum(ts) / len(ts)
+    return timed
+
+
+def _wall_ms(step, steps, warmup):
+    """Wall-clock ms per step over `steps` steps after `warmup`, between synchronisations."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def _full_layer(csa, c, dev, T, N, n_layers_reuse=0):
+    """Bound calls of one Full layer over case c (index -> top-512 -> attention), and the
+    buffers they write; long rows take the tile regime (no score matrix)."""
+    import torch
+    bf = torch.bfloat16
+    rows = N <= csa.TOPK_ROW_MAX
+    scores = torch.empty((T, N), dtype=torch.float32, device=dev) if rows else None
+    tile_max = torch.empty((T, csa.tile_max_ld(N)), dtype=torch.float32, device=dev)
+    stats = torch.empty(csa.index_stats_bytes(T, c.q_per_seq, N) // 4, dtype=torch.int32, device=dev)
+    idx = torch.empty((T, 512), dtype=torch.int32, device=dev)
+    out = torch.empty((T, 64, 512), dtype=bf, device=dev)
+    ws_t = torch.empty(max(1, csa.topk_workspace_bytes(T, N)), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(1, csa.attend_workspace_bytes(T)), dtype=torch.uint8, device=dev)
+    ix = (c.q_idx.view(bf), c.w_idx, c.k_idx.view(bf), c.q_pos, c.ratio, c.q_per_seq)
+    calls = dict(
+        index=csa.bind(csa.csa2_index, *ix, want_scores=rows, scores=scores, tile_max=tile_max, stats=stats),
+        topk=csa.bind(csa.csa2_topk, scores, tile_max, stats, *ix, indices=idx, workspace=ws_t),
+        attend=csa.bind(csa.csa2_attend_fp4, c.q[0].view(bf), c.kv_codes, c.kv_scales, idx, c.swa[0].view(bf),
+                        c.swa_end, None, c.softmax_scale, c.q_per_seq, c.window, out=out, workspace=ws_a))
+    return calls, idx, rows
+
+
+def decode_section(args, dev, name):
+    """A decode workload other than the headline (batched decode: 64 sequences x 131072 entries):
+    the same Full-layer step, timed the same way, with the step's algorithmic bytes against 8 TB/s."""
+    import torch
+
+    import compressed_sparse_attention_02_amd as csa
+    import csa2_gen as G
+
+    wl = WORKLOADS[name]
+    B, N = wl["B"], wl["N"]
+    c = G.make_case(name, B=B, N=N, n_layers=1, seed=0, device=dev, chunk_rows=1 << 19)
+    T = c.T
+    calls, idx, rows = _full_layer(csa, c, dev, T, N)
+
+    def step():
+        calls["index"]()
+        calls["topk"]()
+        calls["attend"]()
+
+    ms = _wall_ms(step, args.steps, args.warmup)
+    timed = _timer(torch.cuda.current_stream(dev))
+    reps = max(10, args.steps)
+    st = {k: timed(calls[k], reps) for k in ("index", "topk", "attend")}
+    step_bytes = T * G.algorithmic_bytes_decode_query(N)
+    idx_bytes = B * N * 256 + T * (8192 + 128 + 16) + T * csa.tile_max_ld(N) * 4 + (T * N * 4 if rows else 0)
+    scan_gbps = idx_bytes / (st["index"][1] * 1e-6) / 1e9
+    att_bytes = T * (512 * 272 + 128 * 1024 + 65536 + 65536 + 512 * 4)
+    return {
+        "value": T / (ms * 1e-3), "unit": "queries/s", "ms_per_step": ms, "steps": args.steps,
+        "config": {"workload": name, "batch": B, "entries_per_seq": N, "queries_per_seq": 1, "topk": 512,
+                   "main_kv": "MXFP4 E2M1+E8M0/32", "indexer": "32x128 bf16"},
+        "algorithmic_bytes_per_step": step_bytes,
+        "step_hbm_GBps": step_bytes / (ms * 1e-3) / 1e9,
+        "step_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "roofline": {"kernel": "idx_scan_kernel (all of csa2_index)", "bound": "hbm", "achieved": scan_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": scan_gbps / HBM_PEAK_GBPS,
+                     "algorithmic_bytes_per_launch": idx_bytes, "avg_launch_us": st["index"][1]},
+        "stages_us": {k: v[0] for k, v in st.items()},
+        "attention": {"avg_us": st["attend"][1], "algorithmic_bytes": att_bytes,
+                      "GBps": att_bytes / (st["attend"][1] * 1e-6) / 1e9,
+                      "frac_hbm": att_bytes / (st["attend"][1] * 1e-6) / 1e9 / HBM_PEAK_GBPS},
+    }
+
+
+def reuse_group_section(args, dev):
+    """The cross-layer reuse group (report sec. 2.3.1): one Full layer (index, top-512, attention)
+    over 32 sequences x 262144 entries, then three Reuse layers, each with its own queries and
+    window, attending over the Full layer's selection and KV.  Timed two ways: as the model runs
+    them (three single-layer calls, since a Reuse layer's query depends on the previous layer's
+    output) and as one fused three-layer call (each selected row gathered once)."""
+    import torch
+
+    import compressed_sparse_attention_02_amd as csa
+    import csa2_gen as G
+
+    wl = WORKLOADS["reuse_group"]
+    B, N = wl["B"], wl["N"]
+    c = G.make_case("reuse_group", B=B, N=N, n_layers=4, seed=0, device=dev, chunk_rows=1 << 19)
+    T = c.T
+    bf = torch.bfloat16
+    calls, idx, rows = _full_layer(csa, c, dev, T, N)
+    ws_1 = torch.empty(max(1, csa.attend_workspace_bytes(T)), dtype=torch.uint8, device=dev)
+    ws_3 = torch.empty(max(1, csa.attend_workspace_bytes(T, n_layers=3)), dtype=torch.uint8, device=dev)
+    out_1 = torch.empty((3, 1, T, 64, 512), dtype=bf, device=dev)
+    out_3 = torch.empty((3, T, 64, 512), dtype=bf, device=dev)
+    single = [csa.bind(csa.csa2_reuse_attend, c.q[l:l + 1].view(bf), c.kv_codes, c.kv_scales, idx,
+                       c.swa[l:l + 1].view(bf), c.swa_end, None, c.softmax_scale, 1, 128, out=out_1[l - 1],
+                       workspace=ws_1) for l in (1, 2, 3)]
+    fused = csa.bind(csa.csa2_reuse_attend, c.q[1:].view(bf).contiguous(), c.kv_codes, c.kv_scales, idx,
+                     c.swa[1:].view(bf).contiguous(), c.swa_end, None, c.softmax_scale, 1, 128, out=out_3,
+                     workspace=ws_3)
+
+    def full():
+        calls["index"]()
+        calls["topk"]()
+        calls["attend"]()
+
+    def step():  # as the model runs it: Full, then three single-layer Reuse calls
+        full()
+        for s in single:
+            s()
+
+    def step_fused():
+        full()
+        fused()
+
+    ms = _wall_ms(step, args.steps, args.warmup)
+    ms_fused = _wall_ms(step_fused, args.steps, args.warmup)
+    same = torch.equal(out_3, out_1[:, 0])     # both forms give the same outputs
+    timed = _timer(torch.cuda.current_stream(dev))
+    reps = max(10, args.steps)
+    st = {k: timed(calls[k], reps) for k in ("index", "topk", "attend")}
+    st["reuse_l1_x3"] = timed(lambda: [s() for s in single], reps)
+    st["reuse_l3"] = timed(fused, reps)
+    full_bytes = T * G.algorithmic_bytes_decode_query(N)
+    layer_bytes = T * (512 * 272 + 128 * 1024 + 65536 + 65536 + 512 * 4)   # 403,456 B per query
+    step_bytes = full_bytes + 3 * layer_bytes
+    reuse_flops = 3 * T * 2 * (2 * 64 * 640 * 512)
+
+    def att(us, nbytes, flops):
+        return {"avg_us": us, "algorithmic_bytes": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9,
+                "frac_hbm": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, "flops": flops,
+                "TFLOPs": flops / (us * 1e-6) / 1e12,
+                "frac_mfma_bf16": flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+
+    idx_bytes = B * N * 256 + T * (8192 + 128 + 16) + T * csa.tile_max_ld(N) * 4
+    scan_gbps = idx_bytes / (st["index"][1] * 1e-6) / 1e9
+    return {
+        "value": T / (ms * 1e-3), "unit": "queries/s (groups of 1 Full + 3 Reuse layers)", "ms_per_step": ms,
+        "steps": args.steps,
+        "config": {"workload": "reuse_group", "batch": B, "entries_per_seq": N, "queries_per_seq": 1,
+                   "layers": "1 Full + 3 Reuse", "topk": 512, "main_kv": "MXFP4 E2M1+E8M0/32",
+                   "indexer": "32x128 bf16"},
+        "algorithmic_bytes_per_step": step_bytes,
+        "step_hbm_GBps": step_bytes / (ms * 1e-3) / 1e9,
+        "step_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "fused_reuse_step": {"ms_per_step": ms_fused, "value": T / (ms_fused * 1e-3),
+                             "step_frac_of_peak": step_bytes / (ms_fused * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                             "outputs_equal_to_single_layer_calls": same},
+        "roofline": {"kernel": "idx_scan_kernel (all of csa2_index)", "bound": "hbm", "achieved": scan_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": scan_gbps / HBM_PEAK_GBPS,
+                     "algorithmic_bytes_per_launch": idx_bytes, "avg_launch_us": st["index"][1]},
+        "stages_us": {k: v[0] for k, v in st.items()},
+        "reuse_attention": {"3 x L=1": att(st["reuse_l1_x3"][1], 3 * layer_bytes, reuse_flops),
+                            "1 x L=3": att(st["reuse_l3"][1], 3 * layer_bytes, reuse_flops)},
+    }
 
 
 def mxfp4_step(c, G, csa, args, stream, timed, idx, out, ws_t, ws_a):
@@ -515,9 +727,32 @@ def kv_write_section(csa, G, dev, B, d=5120, calls=20, reps=5):
     return res
 
 
-def cpu_baseline(c, G, min_seconds=10.0, max_seconds=30.0):
-    """The oracle (as is) on this host's cores: the same 4-query step (index over every visible
-    entry, top-512, attention), repeated until about min_seconds of wall time have passed."""
+def host_cpu():
+    """This host's logical CPU count, the CPUs this process may run on, and the CPU model name."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    if model is None:
+        try:
+            import subprocess
+            out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+            model = next((l.split(":", 1)[1].strip() for l in out.splitlines() if l.startswith("Model name")), None)
+        except (OSError, subprocess.SubprocessError):
+            pass
+    return {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "model": model}
+
+
+def cpu_baseline(c, G, min_seconds=10.0, max_seconds=30.0, one_core_seconds=4.0):
+    """The oracle (as is) on this host's cores: the same step (index over every visible entry,
+    top-512, attention), repeated for about min_seconds with all of its OpenMP threads, then on
+    one thread over the first query only (the same per-query work) for about one_core_seconds.
+    The index phase spreads (query, 4096-entry chunk) pairs over every thread; top-512 and
+    attention run one thread per query."""
     import numpy as np
 
     import oracle
@@ -530,26 +765,53 @@ def cpu_baseline(c, G, min_seconds=10.0, max_seconds=30.0):
     q, swa = u16(c.q[0]), u16(c.swa[0])
     codes, scales, swa_end = c.kv_codes.cpu().numpy(), c.kv_scales.cpu().numpy(), c.swa_end.cpu().numpy()
     oracle.lib()
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        sc = oracle.index(q_idx, w, k, q_pos, c.ratio, c.q_per_seq)
-        sel = oracle.topk(sc, q_pos, c.ratio, c.k)
-        oracle.attend(q, codes, scales, sel, swa, swa_end, None, c.softmax_scale, c.q_per_seq, c.window)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds or dt * (reps + 1) / reps > max_seconds:
-            break
-    # the oracle's threads run over independent queries: at most T of them are busy
-    cores = min(c.T, oracle.max_threads())
-    return {"value": reps * c.T / dt, "unit": "queries/s", "cores": cores, "kind": "oracle",
+    threads = oracle.max_threads()
+
+    def run(nq, seconds, cap):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            sc = oracle.index(q_idx[:nq], w[:nq], k[:nq], q_pos[:nq], c.ratio, c.q_per_seq)
+            sel = oracle.topk(sc, q_pos[:nq], c.ratio, c.k)
+            oracle.attend(q[:nq], codes[:nq], scales[:nq], sel, swa[:nq], swa_end[:nq], None, c.softmax_scale,
+                          c.q_per_seq, c.window)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= seconds or dt * (reps + 1) / reps > cap:
+                return reps, dt
+
+    reps, dt = run(c.T, min_seconds, max_seconds)
+    prev = oracle.set_threads(1)
+    try:
+        reps1, dt1 = run(1, one_core_seconds, 3 * one_core_seconds)
+    finally:
+        oracle.set_threads(prev)
+    cpu = host_cpu()
+    return {"value": reps * c.T / dt, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "one_core": {"value": reps1 / dt1, "unit": "queries/s", "cores": 1,
+                         "sample": f"{reps1} repetitions of the first query's step, {dt1:.1f} s wall"},
+            "threads_by_phase": {"index": threads, "topk": min(c.T, threads), "attention": min(c.T, threads)},
+            "host": cpu,
             "sample": f"{reps} repetitions of the full {c.T}-query step of the same workload (index over all "
-                      f"{c.N} entries per sequence, top-512, attention), {dt:.1f} s wall on {cores} threads"}
+                      f"{c.N} entries per sequence, top-512, attention), {dt:.1f} s wall with {threads} OpenMP "
+                      f"threads on {cpu['affinity']} of {cpu['nproc']} CPUs ({cpu['model']})"}
 
 
 def prefill_main(args, dev):
+    """The causal prefill chunk as its own line (--workload causal_prefill)."""
+    sec = prefill_section(args, dev)
+    line = {"metric": METRIC, "value": sec.pop("value"), "unit": sec.pop("unit"), "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": sec.pop("ms_per_step"),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic", **sec}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def prefill_section(args, dev):
     """The causal prefill chunk: csa2_index (score matrix written) + csa2_topk (row regime) +
-    csa2_attend_fp4 for 4096 queries over 34816 compressed entries (ratio 2); one JSON line with
-    the scan against the bf16 MFMA roofline (the indexer product is a dense GEMM here)."""
+    csa2_attend_fp4 for 4096 queries over 34816 compressed entries (ratio 2), with the scan
+    and the attention against the bf16 MFMA roofline (both are dense products here) and the
+    step against the MFMA bound of their flops."""
     import torch
 
     import compressed_sparse_attention_02_amd as csa
@@ -559,61 +821,29 @@ def prefill_main(args, dev):
     print("[bench] generating causal_prefill", file=sys.stderr, flush=True)
     c = G.make_case("causal_prefill", **wl, seed=0, device=dev, chunk_rows=1 << 19)
     T, N = c.T, c.N
-    bf = torch.bfloat16
-    idx_args = (c.q_idx.view(bf), c.w_idx, c.k_idx.view(bf), c.q_pos, c.ratio, c.q_per_seq)
-    scores = torch.empty((T, N), dtype=torch.float32, device=dev)
-    tile_max = torch.empty((T, csa.tile_max_ld(N)), dtype=torch.float32, device=dev)
-    stats = torch.empty(csa.index_stats_bytes(T, c.q_per_seq, N) // 4, dtype=torch.int32, device=dev)
-    idx = torch.empty((T, 512), dtype=torch.int32, device=dev)
-    out = torch.empty((T, 64, 512), dtype=bf, device=dev)
-    ws_t = torch.empty(csa.topk_workspace_bytes(T, N), dtype=torch.uint8, device=dev)
-    ws_a = torch.empty(max(1, csa.attend_workspace_bytes(T)), dtype=torch.uint8, device=dev)
-    do_index = csa.bind(csa.csa2_index, *idx_args, want_scores=True, scores=scores, tile_max=tile_max, stats=stats)
-    do_topk = csa.bind(csa.csa2_topk, scores, tile_max, stats, *idx_args, indices=idx, workspace=ws_t)
-    do_attend = csa.bind(csa.csa2_attend_fp4, c.q[0].view(bf), c.kv_codes, c.kv_scales, idx, c.swa[0].view(bf),
-                         c.swa_end, None, c.softmax_scale, c.q_per_seq, c.window, out=out, workspace=ws_a)
+    calls, idx, rows = _full_layer(csa, c, dev, T, N)
 
     def step():
-        do_index()
-        do_topk()
-        do_attend()
+        calls["index"]()
+        calls["topk"]()
+        calls["attend"]()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    print(f"[bench] {args.steps} steps timed: {ms_step:.4f} ms per step", file=sys.stderr, flush=True)
-    stream = torch.cuda.current_stream(dev)
-
-    def timed(fn, reps):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for a, b in ev:
-            a.record(stream)
-            fn()
-            b.record(stream)
-        torch.cuda.synchronize()
-        ts = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
-        return ts[len(ts) // 2], sum(ts) / len(ts)
-
+    steps = max(3, min(args.steps, 20))
+    ms_step = _wall_ms(step, steps, max(1, min(args.warmup, 3)))
+    print(f"[bench] prefill: {steps} steps timed: {ms_step:.4f} ms per step", file=sys.stderr, flush=True)
+    timed = _timer(torch.cuda.current_stream(dev))
     reps = max(5, min(args.steps, 20))
-    idx_med, idx_avg = timed(do_index, reps)
-    topk_med, _ = timed(do_topk, reps)
-    att_med, att_avg = timed(do_attend, reps)
+    idx_med, idx_avg = timed(calls["index"], reps)
+    topk_med, _ = timed(calls["topk"], reps)
+    att_med, att_avg = timed(calls["attend"], reps)
     # the indexer GEMM: 2 x 32 heads x 128 channels per visible (query, entry) pair
     n_vis = sum(min(N, (p + 1) // c.ratio) for p in c.q_pos.tolist())
     idx_flops = 2 * 32 * 128 * n_vis
     att_flops = T * 2 * (2 * 64 * (512 + c.window) * 512)
     idx_tflops = idx_flops / (idx_avg * 1e-6) / 1e12
-    line = {
-        "metric": "decode queries/s + achieved HBM GB/s (% peak), CSA2 top-512 FP4 attn at 1 GPU",
-        "value": T / (ms_step * 1e-3),
-        "unit": "queries/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+    bound_ms = (idx_flops + att_flops) / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3
+    sec = {
+        "value": T / (ms_step * 1e-3), "unit": "query tokens/s", "ms_per_step": ms_step, "steps": steps,
         "config": {"workload": "causal_prefill", "queries": T, "prefix_tokens": 65536, "ratio": c.ratio,
                    "entries": N, "indexer": "32x128 bf16", "topk": 512, "heads": 64, "head_dim": 512,
                    "window": c.window, "main_kv": "MXFP4 E2M1+E8M0/32", "parallelism": "none (1 GPU)"},
@@ -622,15 +852,15 @@ def prefill_main(args, dev):
                      "frac": idx_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
                      "algorithmic_flops_per_launch": idx_flops, "avg_launch_us": idx_avg},
         "stages_us": {"index": idx_med, "topk_rows": topk_med, "attend": att_med},
-        "attention": {"call": "csa2_attend_fp4 (one work item per query)", "avg_us": att_avg, "flops": att_flops,
+        "attention": {"call": "csa2_attend_fp4", "avg_us": att_avg, "flops": att_flops,
                       "TFLOPs": att_flops / (att_avg * 1e-6) / 1e12,
                       "frac_mfma_bf16": att_flops / (att_avg * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
-        "mfma_bound_ms": (idx_flops + att_flops) / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3,
+        "mfma_bound_ms": bound_ms,
+        "step_frac_of_mfma_bound": bound_ms / ms_step,
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_prefill(c, G)
-    print(json.dumps(line), flush=True)
-    return 0
+    if args.workload == "causal_prefill" and not args.no_cpu_baseline:
+        sec["cpu_baseline"] = cpu_baseline_prefill(c, G)
+    return sec
 
 
 def cpu_baseline_prefill(c, G, n_sample=8, min_seconds=10.0, max_seconds=30.0):
@@ -660,8 +890,8 @@ def cpu_baseline_prefill(c, G, n_sample=8, min_seconds=10.0, max_seconds=30.0):
         dt = time.perf_counter() - t0
         if dt >= min_seconds or dt * (reps + 1) / reps > max_seconds:
             break
-    cores = min(n_sample, oracle.max_threads())
-    return {"value": reps * n_sample / dt, "unit": "queries/s", "cores": cores, "kind": "oracle",
+    cores = oracle.max_threads()      # the index phase spreads (query, entry chunk) pairs over all threads
+    return {"value": reps * n_sample / dt, "unit": "queries/s", "cores": cores, "kind": "oracle", "host": host_cpu(),
             "sample": f"{reps} repetitions of the chunk's last {n_sample} queries (index over their "
                       f"{int(q_pos[-1] + 1) // c.ratio} visible entries, top-512, attention), {dt:.1f} s wall "
                       f"on {cores} threads"}
