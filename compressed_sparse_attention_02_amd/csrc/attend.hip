@@ -20,13 +20,15 @@
 // statistics live in the same lanes as that head's O^T accumulators, so no
 // cross-lane shuffles are needed except the 4-lane row reductions.
 // Chunks of one query are split over work items (split-K); partial (max,
-// sum, O) are merged by a combine kernel.  For Reuse with several layers,
-// each selected-row chunk is staged once and used by every layer.
+// sum, O) are merged by a combine kernel.  The split depends on the number of
+// queries only; Reuse with several layers runs the layers as independent
+// query-layers of one launch (each stages its own chunks: the selected rows
+// are the same for every layer, so their second and later reads hit the L2),
+// so layer l's result is bit-identical to a single-layer call with q[l].
 #include "mxfp4.h"
 
 namespace csa2 {
 
-constexpr int kAttnThreads = 256;
 constexpr int kChunk = 32;
 constexpr int kXStride = kDim + 8;      // bf16 elements per X row (1040 B)
 constexpr int kXTStride = kChunk + 8;   // bf16 elements per XT row (80 B)
@@ -52,13 +54,12 @@ struct AttnArgs {
   int T, q_per_seq, B, S, window, k, L;
   int64_t N;
   int n_main, n_swa;        // chunks of selected rows / of window rows
-  int cpw;                  // chunks per work item (single layer)
-  int n_items;              // work items per query
-  int n_slots;              // partial slots per (layer, query)
+  int cpw;                  // chunks per work item
+  int n_items;              // work items per query-layer (partial slots when > 1)
   uint16_t* out;            // [L][T][64][512]
   float* lse;               // [L][T][64] or null
-  uint16_t* part_o;         // [L][T][n_slots][64][512], bf16
-  float* part_ml;           // [L][T][n_slots][64][2]  (max in log2 units, sum)
+  uint16_t* part_o;         // [L][T][n_items][64][512], bf16
+  float* part_ml;           // [L][T][n_items][64][2]  (max in log2 units, sum)
 };
 
 struct AttnShared {
@@ -68,10 +69,14 @@ struct AttnShared {
   float rope[32][2];  // (cos, sin) of the output rotation of pair j (final outputs written here)
 };
 
-// Wave index over the 64 heads (16 heads per wave): a block of W waves takes
-// head group blockIdx.z (grids with W = 1 split a work item's heads over four
-// blocks).
-__device__ __forceinline__ int head_wave() { return (int)(blockIdx.z * (blockDim.x >> 6) + (threadIdx.x >> 6)); }
+// Head group (16 heads) of this wave and layer of this block: a four-wave
+// block covers the four head groups of one query-layer (wave w takes group
+// w, blockIdx.z is the layer); one-wave blocks split a work item's heads over
+// four blocks (blockIdx.z = 4 * layer + group).
+template <int W>
+__device__ __forceinline__ int head_group() { return W == 1 ? (int)(blockIdx.z & 3u) : (int)(threadIdx.x >> 6); }
+template <int W>
+__device__ __forceinline__ int block_layer() { return W == 1 ? (int)(blockIdx.z >> 2) : (int)blockIdx.z; }
 
 // Two fp32 values rounded to nearest-even bf16 and packed, lo in the low half
 // (one v_cvt_pk_bf16_f32 on gfx950).
@@ -239,6 +244,85 @@ __device__ __forceinline__ void stage_groups(const AttnArgs& a, AttnShared& sh, 
   }
 }
 
+// Software-pipelined staging of four-wave blocks: wave g requests the raw
+// bytes of its row group of the next chunk (and the indices of the one after)
+// before the current chunk's products, and converts them into LDS after.
+// Selected rows keep each row's code word (v.x) and scale byte (v.y); window
+// rows their 16-byte piece (bf16), or for FP8 rows below channel 448 the
+// 8 code bytes (v.x, v.y) and the scale byte (v.z).  Bit r of ok: row r valid.
+struct RawGroup {
+  uint4 v[8];
+  uint32_t ok;
+};
+
+__device__ __forceinline__ void load_indices(const AttnArgs& a, int t, int c, int g, int32_t (&idx)[8]) {
+  if (c < a.n_main) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) idx[r] = a.indices[(size_t)t * a.k + c * kChunk + group_row(g, r)];
+  }
+}
+
+template <int KVF, int SWF>
+__device__ __forceinline__ void load_group_raw(const AttnArgs& a, int t, int b, int c, int layer, int g,
+                                               const int32_t (&idx)[8], RawGroup& rg) {
+  const int d = threadIdx.x & 63;
+  uint32_t ok = 0;
+  if (c < a.n_main) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      ok |= (idx[r] >= 0 ? 1u : 0u) << r;
+      const size_t rowid = (size_t)b * a.N + (idx[r] >= 0 ? idx[r] : 0);
+      rg.v[r].x = *reinterpret_cast<const uint32_t*>(a.kv_fp4 + rowid * 256 + 4 * d);
+      rg.v[r].y = KVF == CSA2_KV_MXFP4 ? a.kv_scale[rowid * 16 + (d >> 2)] : a.kv_scale[rowid * 32 + (d >> 1)];
+    }
+  } else {
+    const int we = a.swa_end[t];
+    const int ws = we - a.window > 0 ? we - a.window : 0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int row = ws + (c - a.n_main) * kChunk + group_row(g, r);
+      ok |= (row < we ? 1u : 0u) << r;
+      const size_t rr = ((size_t)layer * a.B + b) * a.S + (row < we ? row : (we > 0 ? we - 1 : 0));
+      if (SWF == CSA2_SWA_BF16) {
+        rg.v[r] = *reinterpret_cast<const uint4*>(a.swa + rr * kDim + 8 * d);
+      } else if (d >= 56) {
+        rg.v[r] = *reinterpret_cast<const uint4*>(a.swa_rope + rr * 64 + 8 * (d - 56));
+      } else {
+        const uint2 cw = *reinterpret_cast<const uint2*>(a.swa_fp8 + rr * 448 + 8 * d);
+        rg.v[r] = make_uint4(cw.x, cw.y, a.swa_sc[rr * 8 + (d >> 3)], 0u);
+      }
+    }
+  }
+  rg.ok = ok;
+}
+
+// Convert wave g's raw row group of chunk c to bf16 and write it to X and XT.
+template <int KVF, int SWF>
+__device__ __forceinline__ void store_group_raw(const AttnArgs& a, AttnShared& sh, int c, int g, const RawGroup& rg) {
+  const int d = threadIdx.x & 63;
+  uint32_t v[8][4];
+  int okr[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    okr[r] = (rg.ok >> r) & 1u;
+    uint4 o;
+    if (c < a.n_main) {
+      o = KVF == CSA2_KV_MXFP4 ? dequant8(rg.v[r].x, rg.v[r].y) : dequant8_e4m3(rg.v[r].x, rg.v[r].y);
+    } else if (SWF == CSA2_SWA_BF16 || d >= 56) {
+      o = rg.v[r];
+    } else {
+      const float sc = e8m0_f32(rg.v[r].z);
+      o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(rg.v[r].x, sc, false));
+      o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(rg.v[r].x, sc, true));
+      o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(rg.v[r].y, sc, false));
+      o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(rg.v[r].y, sc, true));
+    }
+    v[r][0] = okr[r] ? o.x : 0u; v[r][1] = okr[r] ? o.y : 0u;
+    v[r][2] = okr[r] ? o.z : 0u; v[r][3] = okr[r] ? o.w : 0u;
+  }
+  write_group(sh, g, d, v, okr);
+}
+
 // Stage chunk `c` into LDS: wave g of a 4-wave block takes row group g, a
 // one-wave block all four.
 template <int KVF, int SWF>
@@ -253,9 +337,9 @@ struct HeadState {
   float l;         // running sum (this lane's rows only)
 };
 
-__device__ __forceinline__ void load_q(const AttnArgs& a, int layer, int t, bf16x8* qb) {
+__device__ __forceinline__ void load_q(const AttnArgs& a, int layer, int t, int hg, bf16x8* qb) {
   const int lane = threadIdx.x & 63;
-  const int head = 16 * head_wave() + (lane & 15), g = lane >> 4;
+  const int head = 16 * hg + (lane & 15), g = lane >> 4;
   const uint4* qp = reinterpret_cast<const uint4*>(a.q + (((size_t)layer * a.T + t) * kHeads + head) * kDim + 8 * g);
 #pragma unroll
   for (int j = 0; j < 16; ++j) qb[j] = as_bf16x8(qp[4 * j]);  // channels 32j + 8g .. +8
@@ -329,9 +413,10 @@ __device__ __forceinline__ void attend_chunk(const AttnArgs& a, const AttnShared
 
 // Write the final output of one (layer, query) from a complete state (the
 // rotation's (cos, sin) pairs already in sh.rope when a.rope_pos is given).
-__device__ void write_final(const AttnArgs& a, const AttnShared& sh, const HeadState& st, int layer, int t) {
+__device__ void write_final(const AttnArgs& a, const AttnShared& sh, const HeadState& st, int layer, int t,
+                            int hg) {
   const int lane = threadIdx.x & 63;
-  const int head = 16 * head_wave() + (lane & 15), g = lane >> 4;
+  const int head = 16 * hg + (lane & 15), g = lane >> 4;
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
@@ -369,13 +454,13 @@ __device__ void write_final(const AttnArgs& a, const AttnShared& sh, const HeadS
     a.lse[((size_t)layer * a.T + t) * kHeads + head] = (m == -INFINITY) ? -INFINITY : (m + log2f(den)) * kLn2;
 }
 
-__device__ void write_partial(const AttnArgs& a, const HeadState& st, int layer, int t, int slot) {
+__device__ void write_partial(const AttnArgs& a, const HeadState& st, int layer, int t, int slot, int hg) {
   const int lane = threadIdx.x & 63;
-  const int head = 16 * head_wave() + (lane & 15), g = lane >> 4;
+  const int head = 16 * hg + (lane & 15), g = lane >> 4;
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  const size_t base = (((size_t)layer * a.T + t) * a.n_slots + slot) * kHeads + head;
+  const size_t base = (((size_t)layer * a.T + t) * a.n_items + slot) * kHeads + head;
   uint16_t* op = a.part_o + base * kDim + 4 * g;
   // bf16 partials (the combine accumulates in fp32); streaming stores: they
   // are read once, by the combine kernel
@@ -392,57 +477,449 @@ __device__ void write_partial(const AttnArgs& a, const HeadState& st, int layer,
   }
 }
 
-// grid (n_items, T).  Work item i of query t:
-//   L == 1: chunks [i*cpw, min((i+1)*cpw, n_main+n_swa)); if n_items == 1 the
-//           result is final, otherwise it is partial slot i.
-//   L  > 1: i < n_main: selected-row chunk i for every layer (slot i);
-//           otherwise window chunk j of layer l, i = n_main + l*n_swa + j
-//           (slot n_main + j of layer l).
-template <int W, int KVF, int SWF>
-__global__ __launch_bounds__(64 * W) void attend_kernel(AttnArgs a) {
+// grid (n_items, T, L) with four-wave blocks, (n_items, T, 4 L) with one-wave
+// blocks.  Work item i of query-layer (t, l) covers chunks [i*cpw,
+// min((i+1)*cpw, n_main+n_swa)) (selected rows, then the layer's window
+// rows); with FINAL (one item per query-layer) it writes the output, else
+// partial slot i.  One-wave blocks take one chunk each (the plan makes it
+// so): they stage before the query and the running state are live.
+#ifndef CSA2_ATTN_WAVES_PER_SIMD
+#define CSA2_ATTN_WAVES_PER_SIMD 1
+#endif
+template <int W, int KVF, int SWF, bool FINAL>
+__global__ __launch_bounds__(64 * W, W == 1 ? 1 : CSA2_ATTN_WAVES_PER_SIMD) void attend_kernel(AttnArgs a) {
   __shared__ AttnShared sh;
   const int item = blockIdx.x, t = blockIdx.y;
+  const int layer = block_layer<W>(), hg = head_group<W>();
   const int b = t / a.q_per_seq;
+  const int n_chunks = a.n_main + a.n_swa;
+  const int c0 = item * a.cpw;
+  const int c1 = c0 + a.cpw < n_chunks ? c0 + a.cpw : n_chunks;
+  if (FINAL && a.rope_pos && threadIdx.x < 32) {
+    float c, sn;
+    rope_cs(a, t, threadIdx.x, &c, &sn);
+    sh.rope[threadIdx.x][0] = c;
+    sh.rope[threadIdx.x][1] = sn;
+  }
   bf16x8 qb[16];
   HeadState st;
-  if (a.L == 1) {
-    const int n_chunks = a.n_main + a.n_swa;
-    const int c0 = item * a.cpw;
-    const int c1 = c0 + a.cpw < n_chunks ? c0 + a.cpw : n_chunks;
-    if (a.n_items == 1 && a.rope_pos && threadIdx.x < 32) {
-      float c, sn;
-      rope_cs(a, t, threadIdx.x, &c, &sn);
-      sh.rope[threadIdx.x][0] = c;
-      sh.rope[threadIdx.x][1] = sn;
-    }
-    load_q(a, 0, t, qb);
+  if (W == 1) {
+    stage_chunk<KVF, SWF>(a, sh, t, b, c0, layer);
+    load_q(a, layer, t, hg, qb);
     state_init(st);
-    for (int c = c0; c < c1; ++c) {
-      stage_chunk<KVF, SWF>(a, sh, t, b, c, 0);
-      __syncthreads();
-      attend_chunk(a, sh, qb, st);
-      __syncthreads();
-    }
-    if (a.n_items == 1) write_final(a, sh, st, 0, t);
-    else write_partial(a, st, 0, t, item);
-  } else if (item < a.n_main) {
-    stage_chunk<KVF, SWF>(a, sh, t, b, item, 0);
-    __syncthreads();
-    for (int l = 0; l < a.L; ++l) {
-      load_q(a, l, t, qb);
-      state_init(st);
-      attend_chunk(a, sh, qb, st);
-      write_partial(a, st, l, t, item);
-    }
-  } else {
-    const int rest = item - a.n_main;
-    const int l = rest / a.n_swa, j = rest % a.n_swa;
-    load_q(a, l, t, qb);
-    state_init(st);
-    stage_chunk<KVF, SWF>(a, sh, t, b, a.n_main + j, l);
     __syncthreads();
     attend_chunk(a, sh, qb, st);
-    write_partial(a, st, l, t, a.n_main + j);
+  } else {
+    // wave hg stages row group hg; the next chunk's bytes are in flight
+    // during this chunk's products
+    int32_t idx[8];
+    RawGroup rg;
+    load_indices(a, t, c0, hg, idx);
+    load_group_raw<KVF, SWF>(a, t, b, c0, layer, hg, idx, rg);
+    if (c0 + 1 < c1) load_indices(a, t, c0 + 1, hg, idx);
+    load_q(a, layer, t, hg, qb);
+    state_init(st);
+    for (int c = c0; c < c1; ++c) {
+      store_group_raw<KVF, SWF>(a, sh, c, hg, rg);
+      __syncthreads();
+      if (c + 1 < c1) {
+        load_group_raw<KVF, SWF>(a, t, b, c + 1, layer, hg, idx, rg);
+        if (c + 2 < c1) load_indices(a, t, c + 2, hg, idx);
+      }
+      attend_chunk(a, sh, qb, st);
+      __syncthreads();
+    }
+  }
+  if (FINAL) write_final(a, sh, st, layer, t, hg);
+  else write_partial(a, st, layer, t, item, hg);
+}
+
+// ---------------------------------------------------------------------------
+// Eight-wave blocks: one query-layer per block, the work of a chunk split so
+// that every wave touches only a slice of it and holds half a wave's worth of
+// state (two waves per SIMD):
+//   S^T = X Q^T: wave w takes heads 16 (w & 3) .. +15 over channels
+//     256 (w >> 2) .. +255.  For selected rows the A operands come straight
+//     from memory into registers: lane (r, g) holds rows r and 16 + r,
+//     channels 256 (w >> 2) + 64 g .. +63, k-step j taking channels + 8 j ..
+//     + 8 (the order of the channels along k does not change the products;
+//     the query operand uses the same order).  Window chunks (bf16 or FP8
+//     rows, four times the bytes of FP4 ones) take them from a row-major copy
+//     in LDS.  The two channel halves of a head group add their partial S^T
+//     through LDS (2 KB per wave).
+//   O^T += X^T P^T: wave w takes channels 64 w .. +63 of all 64 heads; its A
+//     operand is its own transposed slice of the chunk in LDS (staged by the
+//     wave itself), the B operand P^T of head group G is published in LDS by
+//     wave G.
+// Every element of a selected-row chunk is written to LDS once and read
+// back once.
+
+constexpr int kCsThreads = 512;
+constexpr int kCsSlice = kDim / 8;  // output channels per wave
+
+struct CsShared {
+  alignas(16) uint16_t xt[8][kCsSlice * kXTStride];  // per wave: channel c of its slice, 32 rows (k order)
+  alignas(16) uint16_t x[kChunk * kXStride];          // window chunks: row-major rows (S operand)
+  alignas(16) floatx4 sx[8][2][64];                   // partial S^T [wave][m-tile][lane]
+  alignas(16) bf16x8 p[4][64];                        // P^T of head group G, B-operand layout
+  float alpha[kHeads];                                // this chunk's rescale factor per head
+  int grow[4];                                        // head group G rescales this chunk
+  float fin_m[kHeads], fin_l[kHeads];                 // final (max, sum) per head
+  int valid[kChunk];
+  float rope[32][2];
+};
+
+// XT slice layout: row c (channel), four 16-byte blocks of 8 rows (k order),
+// block b stored at position (b + c / 16) % 4: the O loop's reads (16
+// consecutive channels, one block) hit 16 distinct bank groups.
+__device__ __forceinline__ int cs_xt_off(int c, int blk) { return c * kXTStride + 8 * ((blk + (c >> 4)) & 3); }
+
+// Maximum with the lane l ^ 16 / l ^ 32 (gfx950 lane swaps).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Slice-layout rows of lane l: k-block l / 16 holds rows group_row(b, 0..7);
+// lane l takes k positions 4 (l >> 3) .. +3, i.e. rows group_row(l >> 4,
+// 4 ((l >> 3) & 1) + i), channels 64 w + 8 (l & 7) .. +7.
+__device__ __forceinline__ int cs_slice_row(int lane, int i) { return group_row(lane >> 4, 4 * ((lane >> 3) & 1) + i); }
+
+// Raw bytes of a chunk for one wave.  S layout, selected rows only (lane
+// (r, g), rows r and 16 + r, channels 256 (w >> 2) + 64 g .. +63): s[m][0..1]
+// the 32 code bytes, s[m][2].x the scale bytes (two E8M0 or four E4M3).
+// Slice layout: x[i] for row cs_slice_row(lane, i) (selected rows: code word,
+// scale byte; window rows: the 16-byte piece, or FP8 code bytes and scale).
+struct CsRaw {
+  uint4 s[2][3];
+  uint4 x[4];
+  uint32_t ok_x;  // bit i: slice row i valid
+};
+
+struct CsIdx {
+  int32_t s[2], x[4];
+};
+
+__device__ __forceinline__ void cs_load_indices(const AttnArgs& a, int t, int c, CsIdx& ix) {
+  if (c >= a.n_main) return;
+  const int lane = threadIdx.x & 63, r16 = lane & 15;
+  const int32_t* ip = a.indices + (size_t)t * a.k + c * kChunk;
+  ix.s[0] = ip[r16];
+  ix.s[1] = ip[16 + r16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ix.x[i] = ip[cs_slice_row(lane, i)];
+}
+
+template <int KVF, int SWF>
+__device__ __forceinline__ void cs_load_raw(const AttnArgs& a, int t, int b, int c, int layer, const CsIdx& ix,
+                                            CsRaw& raw) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int sc0 = 256 * (w >> 2) + 64 * g;       // S-layout channels sc0 .. sc0 + 63
+  const int xc0 = kCsSlice * w + 8 * (lane & 7);  // slice-layout channels xc0 .. xc0 + 7
+  uint32_t ok_x = 0;
+  if (c < a.n_main) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const size_t rowid = (size_t)b * a.N + (ix.s[m] >= 0 ? ix.s[m] : 0);
+      const uint4* cp = reinterpret_cast<const uint4*>(a.kv_fp4 + rowid * 256 + sc0 / 2);
+      raw.s[m][0] = cp[0];
+      raw.s[m][1] = cp[1];
+      raw.s[m][2].x = KVF == CSA2_KV_MXFP4
+                          ? (uint32_t)*reinterpret_cast<const uint16_t*>(a.kv_scale + rowid * 16 + sc0 / 32)
+                          : *reinterpret_cast<const uint32_t*>(a.kv_scale + rowid * 32 + sc0 / 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ok_x |= (ix.x[i] >= 0 ? 1u : 0u) << i;
+      const size_t rowid = (size_t)b * a.N + (ix.x[i] >= 0 ? ix.x[i] : 0);
+      raw.x[i].x = *reinterpret_cast<const uint32_t*>(a.kv_fp4 + rowid * 256 + xc0 / 2);
+      raw.x[i].y = KVF == CSA2_KV_MXFP4 ? a.kv_scale[rowid * 16 + xc0 / 32] : a.kv_scale[rowid * 32 + xc0 / 16];
+    }
+  } else {
+    const int we = a.swa_end[t];
+    const int ws = we - a.window > 0 ? we - a.window : 0;
+    const int row0 = ws + (c - a.n_main) * kChunk;
+    const size_t base = ((size_t)layer * a.B + b) * a.S;
+    const int last = we > 0 ? we - 1 : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = row0 + cs_slice_row(lane, i);
+      ok_x |= (row < we ? 1u : 0u) << i;
+      const size_t rr = base + (row < we ? row : last);
+      if (SWF == CSA2_SWA_BF16) {
+        raw.x[i] = *reinterpret_cast<const uint4*>(a.swa + rr * kDim + xc0);
+      } else if (xc0 >= 448) {
+        raw.x[i] = *reinterpret_cast<const uint4*>(a.swa_rope + rr * 64 + (xc0 - 448));
+      } else {
+        const uint2 cw = *reinterpret_cast<const uint2*>(a.swa_fp8 + rr * 448 + xc0);
+        raw.x[i] = make_uint4(cw.x, cw.y, a.swa_sc[rr * 8 + xc0 / 64], 0u);
+      }
+    }
+  }
+  raw.ok_x = ok_x;
+}
+
+// The wave's transposed slice of chunk c into LDS (with the row validity,
+// written by wave 0); for window chunks also its part of the row-major copy.
+template <int KVF, int SWF>
+__device__ __forceinline__ void cs_store_slice(const AttnArgs& a, CsShared& sh, int c, const CsRaw& raw) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int cg = lane & 7, kb = lane >> 3;
+  const int xc0 = kCsSlice * w + 8 * cg;
+  uint32_t v[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint4 o;
+    if (c < a.n_main) {
+      o = KVF == CSA2_KV_MXFP4 ? dequant8(raw.x[i].x, raw.x[i].y) : dequant8_e4m3(raw.x[i].x, raw.x[i].y);
+    } else if (SWF == CSA2_SWA_BF16 || xc0 >= 448) {
+      o = raw.x[i];
+    } else {
+      const float sc = e8m0_f32(raw.x[i].z);
+      o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x[i].x, sc, false));
+      o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x[i].x, sc, true));
+      o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x[i].y, sc, false));
+      o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x[i].y, sc, true));
+    }
+    v[i][0] = o.x; v[i][1] = o.y; v[i][2] = o.z; v[i][3] = o.w;
+  }
+  if (c >= a.n_main) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(&sh.x[cs_slice_row(lane, i) * kXStride + xc0]) =
+          make_uint4(v[i][0], v[i][1], v[i][2], v[i][3]);
+  }
+  // channel 8 cg + e of the slice, k positions 4 kb .. 4 kb + 3
+  uint16_t* xt = sh.xt[w];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint32_t wd[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const uint32_t lo = (v[2 * p][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      const uint32_t hi = (v[2 * p + 1][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      wd[p] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint2*>(&xt[cs_xt_off(8 * cg + e, kb >> 1) + 4 * (kb & 1)]) = make_uint2(wd[0], wd[1]);
+  }
+  if (w == 0 && cg == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sh.valid[cs_slice_row(lane, i)] = (raw.ok_x >> i) & 1u;
+  }
+}
+
+// S^T partial product of the wave's 16 heads over its 256 channels: A
+// operands of selected-row chunks from the raw S-layout bytes, of window
+// chunks from the row-major LDS copy (rows r and 16 + r, channels sc0 + 8 j).
+template <int KVF, bool WIN>
+__device__ __forceinline__ void cs_s_product(const CsShared& sh, const CsRaw& raw, const bf16x8 (&qb)[8],
+                                             floatx4 (&acc)[2], int sc0) {
+  const int r16 = threadIdx.x & 15;
+  acc[0] = floatx4{0.f, 0.f, 0.f, 0.f};
+  acc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      bf16x8 av;
+      if (WIN) {
+        av = lds_read16(&sh.x[(16 * m + r16) * kXStride + sc0 + 8 * j]);
+      } else {
+        const uint32_t* cw = reinterpret_cast<const uint32_t*>(&raw.s[m][0]);
+        const uint32_t sb = KVF == CSA2_KV_MXFP4 ? (raw.s[m][2].x >> (8 * (j >> 2))) & 255u
+                                                 : (raw.s[m][2].x >> (8 * (j >> 1))) & 255u;
+        av = as_bf16x8(KVF == CSA2_KV_MXFP4 ? dequant8(cw[j], sb) : dequant8_e4m3(cw[j], sb));
+      }
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[j], acc[m], 0, 0, 0);
+    }
+  }
+}
+
+struct CsState {
+  floatx4 o[4][4];  // O^T: o[mb][G][i] = O[16 G + lane % 16][64 w + 16 mb + 4 (lane / 16) + i]
+  float m;          // running max (log2 units) of head 16 (w & 3) + lane % 16
+  float l;          // running sum over this lane's rows
+  bool started;     // o holds something
+};
+
+// grid (n_items, T, L), 512 threads; chunks and outputs as attend_kernel.
+template <int KVF, int SWF, bool FINAL>
+__global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
+  __shared__ CsShared sh;
+  const int item = blockIdx.x, t = blockIdx.y, layer = blockIdx.z;
+  const int b = t / a.q_per_seq;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r16 = lane & 15, g = lane >> 4, hg = w & 3, h = w >> 2;
+  const int sc0 = 256 * h + 64 * g;
+  const int n_chunks = a.n_main + a.n_swa;
+  const int c0 = item * a.cpw;
+  const int c1 = c0 + a.cpw < n_chunks ? c0 + a.cpw : n_chunks;
+  if (FINAL && a.rope_pos && threadIdx.x < 32) {
+    float cv, sv;
+    rope_cs(a, t, threadIdx.x, &cv, &sv);
+    sh.rope[threadIdx.x][0] = cv;
+    sh.rope[threadIdx.x][1] = sv;
+  }
+  CsIdx ix;
+  CsRaw raw;
+  cs_load_indices(a, t, c0, ix);
+  cs_load_raw<KVF, SWF>(a, t, b, c0, layer, ix, raw);
+  if (c0 + 1 < c1) cs_load_indices(a, t, c0 + 1, ix);
+  // the query operand: head 16 hg + r16, channels sc0 + 8 j .. + 8
+  bf16x8 qb[8];
+  {
+    const uint4* qp = reinterpret_cast<const uint4*>(
+        a.q + (((size_t)layer * a.T + t) * kHeads + 16 * hg + r16) * kDim + sc0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qb[j] = as_bf16x8(qp[j]);
+  }
+  CsState st;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int G = 0; G < 4; ++G) st.o[mb][G] = floatx4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  st.started = false;
+
+  for (int c = c0; c < c1; ++c) {
+    cs_store_slice<KVF, SWF>(a, sh, c, raw);
+    floatx4 acc[2];
+    if (c < a.n_main) {
+      cs_s_product<KVF, false>(sh, raw, qb, acc, sc0);
+    } else {
+      __syncthreads();  // the window rows of every wave in sh.x
+      cs_s_product<KVF, true>(sh, raw, qb, acc, sc0);
+    }
+    sh.sx[w][0][lane] = acc[0];
+    sh.sx[w][1][lane] = acc[1];
+    if (c + 1 < c1) {
+      cs_load_raw<KVF, SWF>(a, t, b, c + 1, layer, ix, raw);
+      if (c + 2 < c1) cs_load_indices(a, t, c + 2, ix);
+    }
+    __syncthreads();
+    // full S^T of the group's 16 heads (own + partner half: the same sum in both waves)
+    acc[0] += sh.sx[w ^ 4][0][lane];
+    acc[1] += sh.sx[w ^ 4][1][lane];
+    // acc[m][i]: row 16 m + 4 g + i, head 16 hg + r16
+    float z[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = sh.valid[4 * g + i] ? acc[0][i] * a.scale_log2 : -INFINITY;
+      z[4 + i] = sh.valid[16 + 4 * g + i] ? acc[1][i] * a.scale_log2 : -INFINITY;
+    }
+    float cm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+    cm = max_xor16(cm);
+    cm = max_xor32(cm);
+    // lazy rescaling: the reference maximum stays while the chunk's scores
+    // exceed it by at most kRescaleSlack (log2 units)
+    const float mtrue = fmaxf(st.m, cm);
+    const bool grow = mtrue > st.m + kRescaleSlack;
+    const float mn = grow ? mtrue : st.m;
+    const float alpha = grow ? exp2f(st.m - mn) : 1.f;
+    uint32_t pb[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p0 = z[2 * i] == -INFINITY ? 0.f : exp2f(z[2 * i] - mn);
+      const float p1 = z[2 * i + 1] == -INFINITY ? 0.f : exp2f(z[2 * i + 1] - mn);
+      psum += p0 + p1;
+      pb[i] = pack_bf16x2_rne(p0, p1);
+    }
+    st.l = st.l * alpha + psum;
+    st.m = mn;
+    if (h == 0) {  // wave hg publishes head group hg
+      bf16x8 pv;
+      __builtin_memcpy(&pv, pb, 16);
+      sh.p[hg][lane] = pv;
+      if (g == 0) sh.alpha[16 * hg + r16] = alpha;
+      const bool any = __ballot(grow) != 0ull;
+      if (lane == 0) sh.grow[hg] = any ? 1 : 0;
+    }
+    __syncthreads();
+    // O^T of this wave's channels, all four head groups
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      if (st.started && sh.grow[G]) {
+        const float al = sh.alpha[16 * G + r16];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) st.o[mb][G] *= al;
+      }
+      const bf16x8 pv = sh.p[G][lane];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const bf16x8 xa = lds_read16(&sh.xt[w][cs_xt_off(16 * mb + r16, g)]);
+        st.o[mb][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, pv, st.o[mb][G], 0, 0, 0);
+      }
+    }
+    st.started = true;
+  }
+  // (max, sum) of each head from its publishing wave
+  {
+    float l = st.l;
+    l = sum_xor16(l);
+    l = sum_xor32(l);
+    if (h == 0 && g == 0) {
+      sh.fin_m[16 * hg + r16] = st.m;
+      sh.fin_l[16 * hg + r16] = l;
+    }
+  }
+  __syncthreads();
+  const size_t qrow = ((size_t)layer * a.T + t) * kHeads;
+#pragma unroll
+  for (int G = 0; G < 4; ++G) {
+    const int head = 16 * G + r16;
+    float m = sh.fin_m[head];
+    const float l = sh.fin_l[head];
+    if (FINAL) {
+      float den = l, f = 1.f;
+      if (a.sink) {
+        const float sk = a.sink[(size_t)layer * kHeads + head] * kLog2e;
+        const float M = fmaxf(m, sk);
+        if (M != -INFINITY) {
+          f = (m == -INFINITY) ? 0.f : exp2f(m - M);
+          den = l * f + exp2f(sk - M);
+          m = M;
+        }
+      }
+      const float inv = (m == -INFINITY || den == 0.f) ? 0.f : f / den;
+      uint16_t* op = a.out + (qrow + head) * kDim + kCsSlice * w + 4 * g;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        float v[4] = {st.o[mb][G][0] * inv, st.o[mb][G][1] * inv, st.o[mb][G][2] * inv, st.o[mb][G][3] * inv};
+        if (w == 7 && a.rope_pos) {  // channels 448..511: pairs (v0, v1), (v2, v3)
+          const int j0 = 8 * mb + 2 * g;
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const float cv = sh.rope[j0 + p][0], sv = sh.rope[j0 + p][1];
+            const float x = v[2 * p], y = v[2 * p + 1];
+            v[2 * p] = x * cv - y * sv;
+            v[2 * p + 1] = x * sv + y * cv;
+          }
+        }
+        *reinterpret_cast<uint2*>(op + 16 * mb) = make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
+      }
+      if (a.lse && w == 0 && g == 0)
+        a.lse[qrow + head] = (m == -INFINITY) ? -INFINITY : (m + log2f(den)) * kLn2;
+    } else {
+      const size_t base = (((size_t)layer * a.T + t) * a.n_items + item) * kHeads + head;
+      uint16_t* op = a.part_o + base * kDim + kCsSlice * w + 4 * g;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const u32x2 wv = {pack_bf16x2_rne(st.o[mb][G][0], st.o[mb][G][1]),
+                          pack_bf16x2_rne(st.o[mb][G][2], st.o[mb][G][3])};
+        __builtin_nontemporal_store(wv, reinterpret_cast<u32x2*>(op + 16 * mb));
+      }
+      if (w == 0 && g == 0) {
+        a.part_ml[base * 2 + 0] = m;
+        a.part_ml[base * 2 + 1] = l;
+      }
+    }
   }
 }
 
@@ -452,17 +929,17 @@ __global__ __launch_bounds__(64 * W) void attend_kernel(AttnArgs a) {
 __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a) {
   const int h = blockIdx.x, t = blockIdx.y, layer = blockIdx.z;
   const int tid = threadIdx.x;
-  const size_t base = ((size_t)layer * a.T + t) * a.n_slots;
+  const size_t base = ((size_t)layer * a.T + t) * a.n_items;
   __shared__ float fac[64];
   __shared__ float s_inv;
   // all slot loads in flight at once (at most kMaxSlots slots), before the weights are known
   uint2 o[kMaxSlots];
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s)
-    if (s < a.n_slots) o[s] = *reinterpret_cast<const uint2*>(a.part_o + ((base + s) * kHeads + h) * kDim + 4 * tid);
+    if (s < a.n_items) o[s] = *reinterpret_cast<const uint2*>(a.part_o + ((base + s) * kHeads + h) * kDim + 4 * tid);
   if (tid < 64) {
-    // one lane per slot (n_slots <= 64): max, then weighted sum, by wave reductions
-    const bool has = tid < a.n_slots;
+    // one lane per slot (n_items <= 64): max, then weighted sum, by wave reductions
+    const bool has = tid < a.n_items;
     const float ms = has ? a.part_ml[((base + tid) * kHeads + h) * 2] : -INFINITY;
     const float ls = has ? a.part_ml[((base + tid) * kHeads + h) * 2 + 1] : 0.f;
     float M = wave_max_dpp(ms);
@@ -484,7 +961,7 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a) {
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s)
-    if (s < a.n_slots && fac[s] != 0.f) {
+    if (s < a.n_items && fac[s] != 0.f) {
       const floatx4 v = {bf16lo(o[s].x), bf16hi(o[s].x), bf16lo(o[s].y), bf16hi(o[s].y)};
       acc += v * fac[s];
     }
@@ -507,33 +984,36 @@ __global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a) {
 }
 
 struct AttendPlan {
-  int n_main, n_swa, cpw, n_items, n_slots;
+  int n_main, n_swa, cpw, n_items;
 };
 
-static AttendPlan attend_plan(int32_t T, int32_t k, int32_t window, int32_t L) {
+// Work items per launch the split aims at (about one round of resident blocks).
+#ifndef CSA2_ATTN_TARGET_ITEMS
+#define CSA2_ATTN_TARGET_ITEMS 256
+#endif
+constexpr int kTargetItems = CSA2_ATTN_TARGET_ITEMS;
+// One-wave blocks (a work item's four head groups on four CUs) while the
+// whole launch fits in one round of them (two per CU, by their LDS).
+constexpr int kOneWaveBlocks = 512;
+
+// The split of one query's chunks over work items.  It depends on T only,
+// so the result of a query-layer is the same whatever L a launch has.
+static AttendPlan attend_plan(int32_t T, int32_t k, int32_t window) {
   AttendPlan p;
   p.n_main = (k + kChunk - 1) / kChunk;
   p.n_swa = (window + kChunk - 1) / kChunk;
   const int n_chunks = p.n_main + p.n_swa;
-  if (L == 1) {
-    // enough work items to cover the GPU (~1024 blocks), merged back by the combine
-    int64_t want = (1024 + T - 1) / T;
-    if (want > n_chunks) want = n_chunks;
-    if (want < 1) want = 1;
-    p.cpw = (int)((n_chunks + want - 1) / want);
-    p.n_items = (n_chunks + p.cpw - 1) / p.cpw;
-    p.n_slots = p.n_items;
-  } else {
-    p.cpw = 1;
-    p.n_items = p.n_main + L * p.n_swa;
-    p.n_slots = n_chunks;
-  }
+  int64_t want = (kTargetItems + T - 1) / T;
+  if (want > n_chunks) want = n_chunks;
+  if (want < 1) want = 1;
+  p.cpw = (int)((n_chunks + want - 1) / want);
+  p.n_items = (n_chunks + p.cpw - 1) / p.cpw;
   return p;
 }
 
 static size_t attend_ws_bytes(int32_t T, const AttendPlan& p, int32_t L) {
-  if (p.n_items == 1 && L == 1) return 0;
-  const size_t slots = (size_t)L * T * p.n_slots;
+  if (p.n_items == 1) return 0;
+  const size_t slots = (size_t)L * T * p.n_items;
   return align_up(slots * kHeads * kDim * sizeof(uint16_t), 256) + align_up(slots * kHeads * 2 * sizeof(float), 256);
 }
 
@@ -560,7 +1040,7 @@ static csa2_status attend_launch(int32_t L, const void* q, const uint8_t* kv_fp4
   if (k != kTopK || window < 1 || window > CSA2_MAX_WINDOW || L < 1 || L > CSA2_MAX_LAYERS || T > 65535 ||
       N >= ((int64_t)1 << 31))
     return CSA2_ERR_UNSUPPORTED;
-  const AttendPlan p = attend_plan(T, k, window, L);
+  const AttendPlan p = attend_plan(T, k, window);
   const size_t need = attend_ws_bytes(T, p, L);
   if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
   AttnArgs a;
@@ -589,32 +1069,35 @@ static csa2_status attend_launch(int32_t L, const void* q, const uint8_t* kv_fp4
   a.n_swa = p.n_swa;
   a.cpw = p.cpw;
   a.n_items = p.n_items;
-  a.n_slots = p.n_slots;
   a.out = (uint16_t*)out;
   a.lse = lse;
-  const size_t slots = (size_t)L * T * p.n_slots;
+  const size_t slots = (size_t)L * T * p.n_items;
   a.part_o = need ? (uint16_t*)workspace : nullptr;
   a.part_ml = need ? (float*)((char*)workspace + align_up(slots * kHeads * kDim * sizeof(uint16_t), 256)) : nullptr;
   hipStream_t st = (hipStream_t)hip_stream;
   (void)hipGetLastError();
-  // small batches: one wave per block and four blocks per work item (16 heads
-  // each), so that the work and the partial writes spread over four times the CUs
-  const bool one = (int64_t)p.n_items * T * 4 <= 4096;
-  const dim3 grid(p.n_items, T, one ? 4 : 1), block(one ? 64 : kAttnThreads);
+  // small launches: one wave per block and four blocks per work item (16
+  // heads each), so that the work and the partial writes spread over four
+  // times the CUs; otherwise four-wave blocks that stage each chunk once
+  const bool one = p.cpw == 1 && (int64_t)L * T * p.n_items * 4 <= kOneWaveBlocks;
+  const bool fin = p.n_items == 1;
+  const dim3 grid(p.n_items, T, one ? 4 * L : L), block(one ? 64 : kCsThreads);
   const int fmt = 2 * o.kv_format + o.swa_format;
-#define CSA2_ATTEND(W, KVF, SWF) hipLaunchKernelGGL((attend_kernel<W, KVF, SWF>), grid, block, 0, st, a)
-  if (one) {
-    if (fmt == 0) CSA2_ATTEND(1, 0, 0);
-    else if (fmt == 1) CSA2_ATTEND(1, 0, 1);
-    else if (fmt == 2) CSA2_ATTEND(1, 1, 0);
-    else CSA2_ATTEND(1, 1, 1);
-  } else {
-    if (fmt == 0) CSA2_ATTEND(4, 0, 0);
-    else if (fmt == 1) CSA2_ATTEND(4, 0, 1);
-    else if (fmt == 2) CSA2_ATTEND(4, 1, 0);
-    else CSA2_ATTEND(4, 1, 1);
-  }
-#undef CSA2_ATTEND
+#define CSA2_ATTEND1(KVF, SWF) hipLaunchKernelGGL((attend_kernel<1, KVF, SWF, false>), grid, block, 0, st, a)
+#define CSA2_ATTEND4(KVF, SWF, F) hipLaunchKernelGGL((attend_cs_kernel<KVF, SWF, F>), grid, block, 0, st, a)
+#define CSA2_ATTEND_FMT(M, ...)                 \
+  do {                                          \
+    if (fmt == 0) M(0, 0 __VA_ARGS__);          \
+    else if (fmt == 1) M(0, 1 __VA_ARGS__);     \
+    else if (fmt == 2) M(1, 0 __VA_ARGS__);     \
+    else M(1, 1 __VA_ARGS__);                   \
+  } while (0)
+  if (one) CSA2_ATTEND_FMT(CSA2_ATTEND1);
+  else if (fin) CSA2_ATTEND_FMT(CSA2_ATTEND4, , true);
+  else CSA2_ATTEND_FMT(CSA2_ATTEND4, , false);
+#undef CSA2_ATTEND_FMT
+#undef CSA2_ATTEND4
+#undef CSA2_ATTEND1
   if (need) hipLaunchKernelGGL(attend_combine_kernel, dim3(kHeads, T, L), dim3(128), 0, st, a);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   return CSA2_OK;
@@ -627,7 +1110,7 @@ using namespace csa2;
 extern "C" size_t csa2_attend_workspace_bytes(int32_t T, int32_t k, int32_t window, int32_t n_layers) {
   if (T < 1 || k != kTopK || window < 1 || window > CSA2_MAX_WINDOW || n_layers < 1 || n_layers > CSA2_MAX_LAYERS)
     return 0;
-  const AttendPlan p = attend_plan(T, k, window, n_layers);
+  const AttendPlan p = attend_plan(T, k, window);
   return attend_ws_bytes(T, p, n_layers);
 }
 
