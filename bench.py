@@ -223,7 +223,9 @@ def main():
     swa_re = c.swa[1:].view(torch.bfloat16).contiguous()
 
     # long rows: the scan writes only tile maxima and the selection re-derives candidate
-    # scores; short rows keep the score matrix and select in LDS
+    # scores (a score matrix would save the candidate pass its key re-reads, but writing it
+    # slows the scan by more at every batch measured); short rows keep the score matrix and
+    # select in LDS
     rows = N <= csa.TOPK_ROW_MAX
     scores = torch.empty((T, N), dtype=torch.float32, device=dev) if rows else None
     tile_max = torch.empty((T, csa.tile_max_ld(N)), dtype=torch.float32, device=dev)
@@ -449,7 +451,8 @@ def _full_layer(csa, c, dev, T, N, n_layers_reuse=0):
     import torch
     bf = torch.bfloat16
     rows = N <= csa.TOPK_ROW_MAX
-    scores = torch.empty((T, N), dtype=torch.float32, device=dev) if rows else None
+    with_scores = rows
+    scores = torch.empty((T, N), dtype=torch.float32, device=dev) if with_scores else None
     tile_max = torch.empty((T, csa.tile_max_ld(N)), dtype=torch.float32, device=dev)
     stats = torch.empty(csa.index_stats_bytes(T, c.q_per_seq, N) // 4, dtype=torch.int32, device=dev)
     idx = torch.empty((T, 512), dtype=torch.int32, device=dev)
@@ -458,11 +461,11 @@ def _full_layer(csa, c, dev, T, N, n_layers_reuse=0):
     ws_a = torch.empty(max(1, csa.attend_workspace_bytes(T)), dtype=torch.uint8, device=dev)
     ix = (c.q_idx.view(bf), c.w_idx, c.k_idx.view(bf), c.q_pos, c.ratio, c.q_per_seq)
     calls = dict(
-        index=csa.bind(csa.csa2_index, *ix, want_scores=rows, scores=scores, tile_max=tile_max, stats=stats),
+        index=csa.bind(csa.csa2_index, *ix, want_scores=with_scores, scores=scores, tile_max=tile_max, stats=stats),
         topk=csa.bind(csa.csa2_topk, scores, tile_max, stats, *ix, indices=idx, workspace=ws_t),
         attend=csa.bind(csa.csa2_attend_fp4, c.q[0].view(bf), c.kv_codes, c.kv_scales, idx, c.swa[0].view(bf),
                         c.swa_end, None, c.softmax_scale, c.q_per_seq, c.window, out=out, workspace=ws_a))
-    return calls, idx, rows
+    return calls, idx, with_scores
 
 
 def decode_section(args, dev, name):
@@ -570,7 +573,7 @@ def reuse_group_section(args, dev):
                 "TFLOPs": flops / (us * 1e-6) / 1e12,
                 "frac_mfma_bf16": flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
-    idx_bytes = B * N * 256 + T * (8192 + 128 + 16) + T * csa.tile_max_ld(N) * 4
+    idx_bytes = B * N * 256 + T * (8192 + 128 + 16) + T * csa.tile_max_ld(N) * 4 + (T * N * 4 if rows else 0)
     scan_gbps = idx_bytes / (st["index"][1] * 1e-6) / 1e9
     return {
         "value": T / (ms * 1e-3), "unit": "queries/s (groups of 1 Full + 3 Reuse layers)", "ms_per_step": ms,

@@ -1045,16 +1045,23 @@ struct alignas(16) CandLds {
   uint16_t ctile[kCandTiles];   // candidate tiles (offset in the block's range), ascending
   uint16_t cmask[kCandTiles];   // entries of each candidate tile that reach the threshold
   uint32_t eidx[kCandMax];      // passing entries, ascending
-  double hrel[kCandThreads / 64][64];  // per wave: ReLU(dot) of (entry, head) for the in-order head fold
+  union {
+    double hrel[kCandThreads / 64][64];  // per wave: ReLU(dot) of (entry, head) for the in-order head fold
+    ExactLds ex;                         // score-matrix path: key rows staged per round of 32 entries
+  };
 };
 
 // Candidates of tiles [x*kCandTiles, (x+1)*kCandTiles) of query t
 // (grid (nblk, T), one thread per tile).  Every block writes its table record.
+// With the scan's score matrix (scores non-null) the candidate tiles' fp32
+// scores are read from it (the values the scan computed, 64 bytes per tile)
+// instead of re-derived from the keys (4 KiB per tile).
 template <class Keys>
 __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
-    const float* __restrict__ tile_max, uint32_t* __restrict__ stats, const uint16_t* __restrict__ q_idx,
-    const float* __restrict__ w_idx, Keys keys, const int32_t* __restrict__ q_pos,
-    int ratio, int q_per_seq, int64_t N, int k, void* ws, int T, int64_t cap, int slots, int bsel) {
+    const float* __restrict__ scores, const float* __restrict__ tile_max, uint32_t* __restrict__ stats,
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, Keys keys,
+    const int32_t* __restrict__ q_pos, int ratio, int q_per_seq, int64_t N, int k, void* ws, int T, int64_t cap,
+    int slots, int bsel) {
   __shared__ CandLds L;
   const int t = blockIdx.y;
   const int x = blockIdx.x;
@@ -1085,9 +1092,25 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
   if (cand) L.ctile[p] = (uint16_t)tid;
   __syncthreads();
 
-  // 2. fp32 scores of the candidate tiles (the scan's arithmetic)
+  // 2. fp32 scores of the candidate tiles: the scan's, from its score matrix
+  // (16 lanes per tile) or re-derived with its arithmetic
   const Keys kseq = keys.seq(t / q_per_seq, N);
-  cand_tile_masks<false>(L.sq, L.w, L.ctile, L.cmask, n_tiles, tile0, kseq, nv, thr, nullptr, nullptr, nullptr);
+  if (scores) {
+    const float* srow = scores + (size_t)t * N;
+    const int e = tid & 15;
+    for (uint32_t c0 = 0; c0 < n_tiles; c0 += kCandThreads / 16) {
+      const uint32_t ci = c0 + (uint32_t)(tid >> 4);
+      bool pass = false;
+      if (ci < n_tiles) {
+        const int64_t s = (tile0 + L.ctile[ci]) * kTileKeys + e;
+        pass = s < nv && (double)srow[s] >= thr;
+      }
+      const uint64_t bal = __ballot(pass);
+      if (e == 0 && ci < n_tiles) L.cmask[ci] = (uint16_t)((bal >> (tid & 48)) & 0xFFFFull);
+    }
+  } else {
+    cand_tile_masks<false>(L.sq, L.w, L.ctile, L.cmask, n_tiles, tile0, kseq, nv, thr, nullptr, nullptr, nullptr);
+  }
   __syncthreads();
 
   // 3. output slots in (tile, entry) order: thread ci expands candidate tile ci
@@ -1128,11 +1151,16 @@ __global__ __launch_bounds__(kCandThreads, 4) void topk_cand_kernel(
     if (pos < (uint64_t)cap) w.cidx[(size_t)t * cap + pos] = L.eidx[e];
   }
 
-  // 5. fp64 scores of the passing entries, reference operation order, into the slots
+  // 5. fp64 scores of the passing entries, reference operation order, into the
+  // slots.  After the tile pass the key rows are on chip and each wave reads its
+  // entries' rows directly; with the score matrix they are not, so the rows of
+  // each round of 32 entries are requested together and staged in LDS.
   double* cs = w.cscore + (size_t)t * cap;
-  exact_entry_scores_wave(L.sq, L.w, L.eidx, n_pass, kseq, L.hrel[tid >> 6], [&](uint32_t e, double sc) {
+  auto put = [&](uint32_t e, double sc) {
     if ((uint64_t)base + e < (uint64_t)cap) cs[base + e] = sel_value(sc, bsel);
-  });
+  };
+  if (scores) exact_entry_scores(L.sq, L.w, L.eidx, nullptr, n_pass, kseq, L.ex, put);
+  else exact_entry_scores_wave(L.sq, L.w, L.eidx, n_pass, kseq, L.hrel[tid >> 6], put);
 }
 
 // LDS of a select block.
@@ -2107,8 +2135,8 @@ static csa2_status topk_launch(const float* scores, const float* tile_max, uint3
   const int64_t nblk = cand_blocks(N);
   hipLaunchKernelGGL(topk_floor_kernel, dim3(T), dim3(kFloorThreads), 0, st, tile_max, stats, sm.gmax, sm.n_groups,
                      sm.parts, sm.n_parts, sm.q, w_idx, q_pos, ratio, q_per_seq, N, kTopK, (int64_t)kTopK);
-  hipLaunchKernelGGL(topk_cand_kernel<Keys>, dim3((unsigned)nblk, T), dim3(kCandThreads), 0, st, tile_max, stats,
-                     sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, k, workspace, T, cap, slots, bsel);
+  hipLaunchKernelGGL(topk_cand_kernel<Keys>, dim3((unsigned)nblk, T), dim3(kCandThreads), 0, st, scores, tile_max,
+                     stats, sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, k, workspace, T, cap, slots, bsel);
   hipLaunchKernelGGL(topk_select_kernel<Keys>, dim3(T), dim3(kSelThreads), 0, st, tile_max, stats, sm.q, w_idx, keys,
                      q_pos, ratio, q_per_seq, N, k, indices, workspace, T, cap, bsel);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;

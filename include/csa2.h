@@ -121,7 +121,13 @@ csa2_status csa2_index(const void* q_idx, const float* w_idx, const void* k_idx,
  *
  *  scores     the scores output of csa2_index, or NULL.  When given and
  *             N <= CSA2_TOPK_ROW_MAX, each query's row is selected in LDS in one
- *             pass; otherwise the selection works from tile_max and the keys.
+ *             pass; otherwise the selection works from tile_max and the keys,
+ *             and when given it reads the fp32 scores of the candidate tiles
+ *             from the matrix (64 bytes per tile) instead of re-deriving them
+ *             from the keys (4 KiB per tile).  Writing the matrix slows the
+ *             scan by more than this saves at the decode shapes measured, so
+ *             it pays only where the matrix exists anyway.  The indices are
+ *             the same either way.
  *  tile_max, stats, stats_bytes   outputs of csa2_index for the same
  *             arguments (T, q_per_seq, N as passed to it).  For every query
  *             csa2_topk writes into the stats header:

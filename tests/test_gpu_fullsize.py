@@ -30,9 +30,11 @@ def log(msg):
 def run_full(c, layers=1, path="tiles"):
     """The benchmarked pipeline: with path "tiles" the scan writes no score matrix and the
     selection works from tile maxima and keys; with "rows" the scores are materialised and
-    selected in LDS.  A second scan with scores provides them for the bound check."""
+    selected in LDS; with "scores" (rows past CSA2_TOPK_ROW_MAX, the many-query decode
+    workloads) the scan writes the matrix and the tile regime reads candidate scores from it.
+    Without a matrix a second scan provides the scores for the bound check."""
     bf = (c.q_idx.view(BF), c.w_idx, c.k_idx.view(BF), c.q_pos, c.ratio, c.q_per_seq)
-    ix = csa.csa2_index(*bf, want_scores=(path == "rows"))
+    ix = csa.csa2_index(*bf, want_scores=(path != "tiles"))
     idx = csa.csa2_topk(ix.scores, ix.tile_max, ix.stats, *bf)
     out = csa.csa2_attend_fp4(c.q[0].view(BF), c.kv_codes, c.kv_scales, idx, c.swa[0].view(BF), c.swa_end, None,
                               c.softmax_scale, c.q_per_seq, c.window)
@@ -41,7 +43,7 @@ def run_full(c, layers=1, path="tiles"):
         re = csa.csa2_reuse_attend(c.q[1:].view(BF).contiguous(), c.kv_codes, c.kv_scales, idx,
                                    c.swa[1:].view(BF).contiguous(), c.swa_end, None, c.softmax_scale, c.q_per_seq,
                                    c.window)
-    full = ix if path == "rows" else csa.csa2_index(*bf)
+    full = ix if path != "tiles" else csa.csa2_index(*bf)
     torch.cuda.synchronize()
     nt, h = -(-c.N // 16), c.T * csa.STATS_WORDS
     # same tile maxima and summary (past the header, which csa2_topk fills) with and without scores
@@ -96,6 +98,13 @@ def test_reuse_group_sampled():
     log("[full] reuse_group 32 x 256K, Full + 3 Reuse")
     c = G.make_case("reuse_group", **G.CONFIGS["reuse_group"], seed=0, device=DEV)
     check_sampled(c, [0, 31], layers=4)
+
+
+def test_batched_decode_score_matrix_sampled():
+    """The tile regime reading candidate scores from a score matrix, at the batched shape."""
+    log("[full] batched_decode 64 x 128K, score matrix given")
+    c = G.make_case("batched_decode", **G.CONFIGS["batched_decode"], seed=0, device=DEV)
+    check_sampled(c, [5, 62], path="scores")
 
 
 @pytest.mark.parametrize("path", ["rows", "tiles"])

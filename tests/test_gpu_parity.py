@@ -27,7 +27,11 @@ SMALL = {
     "prefill_small": dict(B=1, N=998, q_per_seq=96, ratio=2, prefix=1900),
     "large_rows": dict(B=2, N=40000),
     "large_rows_ragged": dict(B=2, N=40001),
+    "large_qps3": dict(B=2, N=40003, q_per_seq=3),
+    "prefill_large": dict(B=1, N=37500, q_per_seq=16, ratio=2, prefix=74984),
 }
+# rows past CSA2_TOPK_ROW_MAX: with a score matrix the tile regime reads candidate scores from it
+LARGE = [n for n, v in SMALL.items() if v["N"] > csa.TOPK_ROW_MAX]
 
 
 def log(msg):
@@ -51,8 +55,9 @@ def run_index(c, want_scores=True):
 
 def run_topk(c, ix, path="tiles", workspace=None):
     """path "rows": scores given (one-pass LDS selection when N <= 36864); "tiles": no score
-    matrix, selection from tile maxima and the keys."""
-    return csa.csa2_topk(ix.scores if path == "rows" else None, ix.tile_max, ix.stats,
+    matrix, selection from tile maxima and the keys; "tiles_scores" (N > 36864): the tile
+    regime with the score matrix, candidate tiles' scores read from it."""
+    return csa.csa2_topk(ix.scores if path in ("rows", "tiles_scores") else None, ix.tile_max, ix.stats,
                          c.q_idx.view(torch.bfloat16), c.w_idx, c.k_idx.view(torch.bfloat16), c.q_pos, c.ratio,
                          c.q_per_seq, workspace=workspace)
 
@@ -107,12 +112,14 @@ def test_index_scores_within_bound(name):
     log(f"  max |fp32 - fp64| / eps = {worst:.2e}")
 
 
-@pytest.mark.parametrize("path", ["rows", "tiles"])
+@pytest.mark.parametrize("path", ["rows", "tiles", "tiles_scores"])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_topk_bit_exact(name, path):
+    if path == "tiles_scores" and name not in LARGE:
+        pytest.skip("rows within CSA2_TOPK_ROW_MAX: a score matrix selects in the row regime (path rows)")
     log(f"[topk] {name} ({path})")
     c = case(name)
-    ix = run_index(c, want_scores=(path == "rows"))
+    ix = run_index(c, want_scores=(path != "tiles"))
     idx = run_topk(c, ix, path)
     torch.cuda.synchronize()
     assert np.all(npy(ix.header)[:, 2:] == 0), "csa2_topk must leave its counters zero"
@@ -135,9 +142,11 @@ def test_topk_streaming_fallback_matches():
         assert np.array_equal(npy(idx)[t], ref[t])
 
 
-@pytest.mark.parametrize("path", ["rows", "tiles"])
+@pytest.mark.parametrize("path", ["rows", "tiles", "tiles_scores"])
 @pytest.mark.parametrize("mode", ["all_equal", "all_equal_overflow", "all_equal_large", "tie_block", "tie_block_large"])
 def test_topk_planted_ties(mode, path):
+    if path == "tiles_scores" and not mode.endswith("_large"):
+        pytest.skip("rows within CSA2_TOPK_ROW_MAX: a score matrix selects in the row regime (path rows)")
     log(f"[topk] ties {mode} ({path})")
     N = {"all_equal_overflow": 3000, "all_equal_large": 40000, "tie_block_large": 40000}.get(mode, 2048)
     c = G.make_case("ties", B=1, N=N, seed=5, device=DEV, with_kv=False)
@@ -149,7 +158,7 @@ def test_topk_planted_ties(mode, path):
         order = np.argsort(-sc, kind="stable")
         src = int(order[500])
         c.k_idx[0, 1000:1100] = c.k_idx[0, src]
-    ix = run_index(c, want_scores=(path == "rows"))
+    ix = run_index(c, want_scores=(path != "tiles"))
     idx = run_topk(c, ix, path)
     torch.cuda.synchronize()
     ref = oracle_topk(c, oracle_scores(c, [0]))
