@@ -23,7 +23,7 @@ __all__ = [
     "reindex_workspace_bytes", "HSI_BLOCK", "HSI_BLOCKS", "HSI_POOL", "csa2_index_mxfp4", "csa2_topk_mxfp4",
     "csa2_hsi_pool_mxfp4", "csa2_reindex_mxfp4", "index_mxfp4_stats_bytes", "csa2_attend_ex", "KV_MXFP4",
     "KV_E4M3_16", "SWA_BF16", "SWA_FP8", "csa2_kv_write", "kv_write_workspace_bytes", "K_BF16", "K_MXFP4",
-    "SELECT_EXACT", "SELECT_BF16", "bind", "BoundCall",
+    "SELECT_EXACT", "SELECT_BF16", "bind", "BoundCall", "csa2_reuse_attend_static", "STATIC_SCRATCH_BYTES",
 ]
 
 IDX_HEADS, IDX_DIM, HEADS, DIM, TOPK, MAX_WINDOW, MAX_LAYERS = 32, 128, 64, 512, 512, 128, 8
@@ -33,6 +33,7 @@ KV_MXFP4, KV_E4M3_16, SWA_BF16, SWA_FP8 = 0, 1, 0, 1
 K_BF16, K_MXFP4 = 0, 1
 SELECT_EXACT, SELECT_BF16 = 0, 1
 HSI_POOL = HSI_BLOCK * HSI_BLOCKS
+STATIC_SCRATCH_BYTES = 34603008   # csa2_reuse_attend_static's per-GPU scratch (CSA2_STATIC_SCRATCH_BYTES)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 # CSA2_SANITIZE=1 loads the build whose host code carries AddressSanitizer and
@@ -83,6 +84,8 @@ _SIGNATURES = {
                        _vp], _i32),
     "csa2_reuse_attend": ([_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i64, _i32, _i32, _i32, _vp,
                            _vp, _vp, _sz, _vp], _i32),
+    "csa2_reuse_attend_static": ([_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _i32, _i32, _i64, _i32, _i32, _i32,
+                                  _vp, _vp, _vp], _i32),
 }
 
 
@@ -570,6 +573,29 @@ def csa2_reuse_attend(q, kv_fp4, kv_scale, indices, swa, swa_end, sink=None, sof
                                  float(softmax_scale), T, q_per_seq, N, S, window, k, _p(out), _p(lse),
                                  _p(workspace), _nbytes(workspace), _stream(q))
     _raise(st, "csa2_reuse_attend")
+    return (out, lse) if (want_lse or lse is not None) else out
+
+
+def csa2_reuse_attend_static(q, kv_fp4, kv_scale, indices, swa, swa_end, sink=None, softmax_scale=DIM ** -0.5,
+                             q_per_seq=1, window=MAX_WINDOW, out=None, lse=None, want_lse=False):
+    """csa2_reuse_attend without a workspace: the library's per-GPU static scratch holds the
+    split-K partials (for callers that cannot allocate; calls that overlap on one GPU race).
+    Arguments and results as csa2_reuse_attend; out and lse must be given by a caller that
+    cannot allocate (the wrapper allocates them only when they are None)."""
+    L = q.shape[0]
+    T, k, B, N, S, dev = _attend_common((L,), q, kv_fp4, kv_scale, indices, swa, swa_end, sink)
+    if B * q_per_seq != T:
+        raise ValueError(f"T={T} must equal B*q_per_seq={B}*{q_per_seq}")
+    if out is None:
+        out = torch.empty((L, T, HEADS, DIM), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", (L, T, HEADS, DIM), elem_size=2, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((L, T, HEADS), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", (L, T, HEADS), dtype=torch.float32, device=dev)
+    st = _call("csa2_reuse_attend_static", L, _p(q), _p(kv_fp4), _p(kv_scale), _p(indices), _p(swa), _p(swa_end),
+               _p(sink), float(softmax_scale), T, q_per_seq, N, S, window, k, _p(out), _p(lse), _stream(q))
+    _raise(st, "csa2_reuse_attend_static")
     return (out, lse) if (want_lse or lse is not None) else out
 
 

@@ -25,6 +25,8 @@
 // query-layers of one launch (each stages its own chunks: the selected rows
 // are the same for every layer, so their second and later reads hit the L2),
 // so layer l's result is bit-identical to a single-layer call with q[l].
+#include <mutex>
+
 #include "mxfp4.h"
 
 namespace csa2 {
@@ -1103,6 +1105,37 @@ static csa2_status attend_launch(int32_t L, const void* q, const uint8_t* kv_fp4
   return CSA2_OK;
 }
 
+// ---- csa2_reuse_attend_static: the split-K partials in a file-scope device
+// array instead of a caller's workspace.  Each GPU the library runs on holds
+// its own copy until the process ends.  In host code the array's name is a
+// host-side stand-in, never a device address: each device's address is looked
+// up once (hipGetSymbolAddress, with that device current) and only that
+// pointer reaches kernels.  Every slot a call reads was written by the same
+// call, so nothing in the array needs clearing between calls; calls that
+// overlap on one GPU race on it.
+constexpr size_t kStaticScratchBytes = CSA2_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+constexpr int kMaxStaticDevices = 64;
+static void* g_scratch_ptr[kMaxStaticDevices];
+static std::mutex g_scratch_mu;
+
+// Device address of `scratch` on device dev (looked up on first use), or null.
+static void* static_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxStaticDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace csa2
 
 using namespace csa2;
@@ -1142,4 +1175,24 @@ extern "C" csa2_status csa2_attend_ex(int32_t n_layers, const void* q, const uin
   if (n_layers < 1 || n_layers > CSA2_MAX_LAYERS) return CSA2_ERR_UNSUPPORTED;
   return attend_launch(n_layers, q, kv_codes, kv_scales, indices, swa, swa_end, sink, softmax_scale, T, q_per_seq,
                        N, S, window, k, opts, out, lse, workspace, workspace_bytes, hip_stream);
+}
+
+extern "C" csa2_status csa2_reuse_attend_static(int32_t n_layers, const void* q, const uint8_t* kv_fp4,
+                                                const uint8_t* kv_scale, const int32_t* indices, const void* swa,
+                                                const int32_t* swa_end, const float* sink, float softmax_scale,
+                                                int32_t T, int32_t q_per_seq, int64_t N, int32_t S, int32_t window,
+                                                int32_t k, void* out, float* lse, void* hip_stream) {
+  if (n_layers < 1 || n_layers > CSA2_MAX_LAYERS) return CSA2_ERR_UNSUPPORTED;
+  // the size check comes first: nothing touches a device for a call that cannot fit
+  if (T >= 1 && k == kTopK && window >= 1 && window <= CSA2_MAX_WINDOW &&
+      csa2_attend_workspace_bytes(T, k, window, n_layers) > kStaticScratchBytes)
+    return CSA2_ERR_WORKSPACE;
+  if (!q || !kv_fp4 || !kv_scale || !indices || !swa || !swa_end || !out) return CSA2_ERR_INVALID_ARG;
+  int dev = -1;
+  const hipError_t e = hip_stream ? hipStreamGetDevice((hipStream_t)hip_stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return CSA2_ERR_LAUNCH;
+  void* ws = static_scratch(dev);
+  if (ws == nullptr) return CSA2_ERR_LAUNCH;
+  return attend_launch(n_layers, q, kv_fp4, kv_scale, indices, swa, swa_end, sink, softmax_scale, T, q_per_seq, N,
+                       S, window, k, nullptr, out, lse, ws, kStaticScratchBytes, hip_stream);
 }

@@ -335,6 +335,28 @@ csa2_status csa2_reuse_attend(int32_t n_layers, const void* q, const uint8_t* kv
                               int32_t k, void* out, float* lse, void* workspace,
                               size_t workspace_bytes, void* hip_stream);
 
+/* ------------------------------------------------- reuse attend, no workspace
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * csa2_reuse_attend without the workspace arguments, same arguments
+ * otherwise, same kernels and results.  Its split-K partials live in a
+ * library-owned device array of CSA2_STATIC_SCRATCH_BYTES per GPU, held until
+ * the process ends; the call itself allocates nothing.  Returns
+ * CSA2_ERR_WORKSPACE, before touching any device, when
+ * csa2_attend_workspace_bytes(T, k, window, n_layers) exceeds that size (one
+ * layer always fits).  Every call on a GPU shares that GPU's array: calls
+ * that may overlap on one GPU (different streams, threads) race and must be
+ * serialised by the caller.  The array needs no clearing between calls.
+ * Other errors as csa2_reuse_attend; CSA2_ERR_LAUNCH also when the array's
+ * device address cannot be looked up for the stream's device.
+ */
+#define CSA2_STATIC_SCRATCH_BYTES 34603008  /* 33 MiB: every single-layer call fits */
+csa2_status csa2_reuse_attend_static(int32_t n_layers, const void* q, const uint8_t* kv_fp4,
+                                     const uint8_t* kv_scale, const int32_t* indices, const void* swa,
+                                     const int32_t* swa_end, const float* sink, float softmax_scale,
+                                     int32_t T, int32_t q_per_seq, int64_t N, int32_t S, int32_t window,
+                                     int32_t k, void* out, float* lse, void* hip_stream);
+
 /* -------------------------------------------------------- attend, extended
  * csa2_attend_fp4 / csa2_reuse_attend (n_layers as there) with the formats the
  * report deploys and the fused output rotation; opts NULL gives exactly

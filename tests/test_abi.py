@@ -387,3 +387,15 @@ def test_sanitized_builds_are_loaded():
     maps = open("/proc/self/maps").read()
     assert "libcsa2_san.so" in maps and "libcsa2_oracle_san.so" in maps
     assert "libclang_rt.asan" in maps
+
+
+def test_static_attend_rejects_before_touching_a_device(L):
+    """csa2_reuse_attend_static checks the call against its static scratch size first: on this
+    CPU-only host a call that cannot fit returns WORKSPACE without any device access."""
+    P = ctypes.c_void_p(0x100000)
+    assert csa.attend_workspace_bytes(64, n_layers=8) > csa.STATIC_SCRATCH_BYTES
+    assert csa.attend_workspace_bytes(255, n_layers=1) <= csa.STATIC_SCRATCH_BYTES   # one layer always fits
+    args = lambda nl, T: [nl, P, P, P, P, P, P, None, 0.044, T, 1, 4096, 128, 128, 512, P, None, None]
+    assert L.csa2_reuse_attend_static(*args(8, 64)) == WORKSPACE
+    assert L.csa2_reuse_attend_static(*args(9, 4)) == UNSUPPORTED
+    assert L.csa2_reuse_attend_static(*args(0, 4)) == UNSUPPORTED
