@@ -370,27 +370,29 @@ struct alignas(16) FinLds {
 };
 
 // fp64 scores of the band (reference operation order): thread (e = tid/32,
-// h = tid%32) forms dot(q[h], K[e]) with 128 sequential fmas from LDS, then 32
-// threads fold the heads in order.
+// h = tid%32) forms dot(q[h], K[e]) with 128 sequential fmas from LDS, then
+// one thread per entry folds the heads in order (blockDim / 32 entries per
+// pass, blockDim a multiple of 256).
 template <class Keys>
 __device__ void rescore_band(FinLds& sh, FinTail& tl, uint32_t nb, const uint16_t* __restrict__ qt,
                              const float* __restrict__ wt, const Keys& kb, int bsel) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, nt = (int)blockDim.x;
+  const uint32_t ep = (uint32_t)nt >> 5;
   const int e = tid >> 5, h = tid & 31;
-  for (int i = tid; i < kIdxHeads * 16; i += kFinThreads) {
+  for (int i = tid; i < kIdxHeads * 16; i += nt) {
     const int r = i >> 4, c = i & 15;
     *reinterpret_cast<uint4*>(&tl.qrows[r][8 * c]) = *reinterpret_cast<const uint4*>(qt + r * kIdxDim + 8 * c);
   }
   for (uint32_t base = 0; base < nb; base += 64) {
-    // 64 key rows x 256 B: one 16-byte chunk per thread
-    {
-      const int r = tid >> 4, c = tid & 15;
+    // 64 key rows x 256 B, 16-byte chunks
+    for (int i = tid; i < 64 * 16; i += nt) {
+      const int r = i >> 4, c = i & 15;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (base + r < nb) v = kb.piece(sh.band_idx[base + r], c);
       *reinterpret_cast<uint4*>(&tl.krows[r][8 * c]) = v;
     }
     __syncthreads();
-    for (uint32_t half = 0; half < 64 && base + half < nb; half += 32) {
+    for (uint32_t half = 0; half < 64 && base + half < nb; half += ep) {
       if (base + half + e < nb) {
         double d = 0.0;
 #pragma unroll 4
@@ -408,7 +410,7 @@ __device__ void rescore_band(FinLds& sh, FinTail& tl, uint32_t nb, const uint16_
         tl.dots[e][h] = d;
       }
       __syncthreads();
-      if (tid < 32 && base + half + tid < nb) {
+      if ((uint32_t)tid < ep && base + half + tid < nb) {
         double sc = 0.0;
 #pragma unroll 8
         for (int hh = 0; hh < kIdxHeads; ++hh) {
@@ -431,7 +433,7 @@ __device__ void finish_band(FinLds& sh, FinTail& tl, uint32_t kk, const uint16_t
   rescore_band(sh, tl, nb, qt, wt, kb, bsel);
   const uint32_t r = kk - sh.n_out;
   const uint32_t base_out = sh.n_out;
-  for (uint32_t i = threadIdx.x; i < nb; i += kFinThreads) {
+  for (uint32_t i = threadIdx.x; i < nb; i += blockDim.x) {
     const uint64_t ki = tl.band_key[i];
     const uint32_t ii = sh.band_idx[i];
     uint32_t rank = 0;
@@ -454,16 +456,16 @@ __device__ void finish_streaming(FinLds& sh, uint32_t kk, const float* row, int6
   const int tid = threadIdx.x;
   if (tid == 0) sh.n_out = 0;
   __syncthreads();
-  for (int64_t s = tid; s < nv; s += kFinThreads)
+  for (int64_t s = tid; s < nv; s += (int)blockDim.x)
     if ((double)row[s] > hi) sh.out[atomicAdd(&sh.n_out, 1u)] = (uint32_t)s;
   __syncthreads();
   uint32_t rank = kk - sh.n_out;
   uint64_t phi = 0, mhi = 0;
   uint32_t plo = 0, mlo = 0;
   for (int pass = 0; pass < 12; ++pass) {
-    for (int i = tid; i < 256; i += kFinThreads) sh.sel.hist[i] = 0;
+    for (int i = tid; i < 256; i += (int)blockDim.x) sh.sel.hist[i] = 0;
     __syncthreads();
-    for (int64_t s = tid; s < nv; s += kFinThreads) {
+    for (int64_t s = tid; s < nv; s += (int)blockDim.x) {
       const double v = (double)row[s];
       if (v < lo || v > hi) continue;
       const uint64_t key = f64_key(sel_value(exact_score(qt, wt, kb, s), bsel));
@@ -484,7 +486,7 @@ __device__ void finish_streaming(FinLds& sh, uint32_t kk, const float* row, int6
       mlo |= 255u << (24 - 8 * (pass - 8));
     }
   }
-  for (int64_t s = tid; s < nv; s += kFinThreads) {
+  for (int64_t s = tid; s < nv; s += (int)blockDim.x) {
     const double v = (double)row[s];
     if (v < lo || v > hi) continue;
     const uint64_t key = f64_key(sel_value(exact_score(qt, wt, kb, s), bsel));
@@ -496,9 +498,9 @@ __device__ void finish_streaming(FinLds& sh, uint32_t kk, const float* row, int6
 
 // Ascending output (indices are distinct): rank by comparison, 4 per LDS read.
 __device__ void write_sorted(FinLds& sh, FinTail& tl, uint32_t kk, int k, int32_t* out) {
-  for (uint32_t i = kk + threadIdx.x; i < kTopK; i += kFinThreads) sh.out[i] = 0xFFFFFFFFu;
+  for (uint32_t i = kk + threadIdx.x; i < kTopK; i += (int)blockDim.x) sh.out[i] = 0xFFFFFFFFu;
   __syncthreads();
-  for (uint32_t i = threadIdx.x; i < kk; i += kFinThreads) {
+  for (uint32_t i = threadIdx.x; i < kk; i += (int)blockDim.x) {
     const uint32_t v = sh.out[i];
     uint32_t pos = 0;
 #pragma unroll 8
@@ -509,7 +511,7 @@ __device__ void write_sorted(FinLds& sh, FinTail& tl, uint32_t kk, int k, int32_
     tl.out_sorted[pos] = v;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < k; i += kFinThreads) out[i] = i < (int)kk ? (int32_t)tl.out_sorted[i] : -1;
+  for (int i = threadIdx.x; i < k; i += (int)blockDim.x) out[i] = i < (int)kk ? (int32_t)tl.out_sorted[i] : -1;
 }
 
 // Band bounds around the bracket [t_lo, t_hi] of T^ (rounded outwards in fp64).
@@ -613,6 +615,140 @@ __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
     else if (v >= lo) {
       const uint32_t p = atomicAdd(&sh.n_band, 1u);
       if (p < kBandLds) sh.band_idx[p] = (uint32_t)i;
+    }
+  }
+  __syncthreads();
+  const bool fast = sh.n_band <= kBandLds;
+  __syncthreads();
+  if (fast) finish_band(sh, tl, kk, qt, wt, kb, bsel);
+  else finish_streaming(sh, kk, row, nv, lo, hi, qt, wt, kb, bsel);
+  write_sorted(sh, tl, kk, k, out);
+}
+
+// ------------------------------------------------ row regime, prefiltered
+//
+// The scan's tile maxima give a floor before any score is read: the k-th
+// largest visible tile maximum is at most the k-th largest score (its k tiles
+// each hold a distinct entry at or above it), so, as in the tile regime,
+// every entry that can be selected has fp32 score >= thr = cand_threshold(tau,
+// eps) with tau a lower bracket of that maximum.  Only tiles whose maximum
+// reaches thr are read (64 bytes each), their entries that reach it are
+// compacted into LDS, and the bracket of the k-th score, the band and its fp64
+// rescoring run over that list.  An entry left out has an exact score below the
+// k-th exact score, so the list holds every entry the full-row selection
+// could pick and the result is the same.  More than kPfMax listed entries
+// (planted ties) go to the exact streaming pass over the row.
+
+constexpr int kPfMax = 6144;                                        // listed entries held in LDS
+constexpr int kPfThreads = 512;                                     // two blocks per CU
+constexpr int kPfTiles = (kSmallMax + kTileKeys - 1) / kTileKeys;  // tile maxima of a row
+
+struct PfLds {
+  FinLds f;
+  union {
+    struct {
+      float v[kPfMax];
+      uint32_t i[kPfMax];
+      float tm[kPfTiles];
+    } c;
+    FinTail tail;
+  } u;
+  uint32_t n_c;
+  float bm[kPfThreads / 64];
+  double bq[kPfThreads / 64], bs[kPfThreads / 64];
+};
+
+template <class Keys>
+__global__ __launch_bounds__(kPfThreads) void topk_rows_pf_kernel(
+    const float* __restrict__ scores, const float* __restrict__ tile_max, uint32_t* __restrict__ stats,
+    const float* __restrict__ parts, int64_t n_parts, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ w_idx, Keys keys, const int32_t* __restrict__ q_pos, int ratio, int q_per_seq,
+    int64_t N, int k, int32_t* __restrict__ indices, int bsel) {
+  __shared__ PfLds L;
+  FinLds& sh = L.f;
+  FinTail& tl = L.u.tail;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t nv = n_visible(q_pos, t, ratio, N);
+  int32_t* out = indices + (size_t)t * k;
+  const uint32_t kk = (uint32_t)k;
+  const int b = t / q_per_seq;
+  const uint16_t* qt = q_idx + (size_t)t * kIdxHeads * kIdxDim;
+  const float* wt = w_idx + (size_t)t * kIdxHeads;
+  const Keys kb = keys.seq(b, N);
+  const float* row = scores + (size_t)t * N;
+  const int64_t ntv = (nv + kTileKeys - 1) / kTileKeys;
+  if (tid == 0) { sh.n_out = 0; sh.n_band = 0; L.n_c = 0; }
+  for (int64_t j = tid; j < ntv; j += kPfThreads) L.u.c.tm[j] = tile_max[(size_t)t * tile_ld(N) + j];
+  {
+    float m2;
+    double qf, sw;
+    bound_terms(qt, wt, parts + (size_t)b * n_parts, n_parts, tid, kPfThreads, &m2, &qf, &sw);
+    m2 = wave_max_dpp(m2);
+    qf = wave_sum_groups8_f64(qf);
+    sw = wave_sum_groups8_f64(sw);
+    if ((tid & 63) == 0) { L.bm[tid >> 6] = m2; L.bq[tid >> 6] = qf; L.bs[tid >> 6] = sw; }
+  }
+  __syncthreads();
+  float eps;
+  {
+    float m2 = L.bm[0];
+    double qf = L.bq[0], sw = L.bs[0];
+    for (int i = 1; i < kPfThreads / 64; ++i) { m2 = fmaxf(m2, L.bm[i]); qf += L.bq[i]; sw += L.bs[i]; }
+    eps = bound_eps(m2, qf, sw);
+    if (tid == 0) stats[(size_t)t * CSA2_STATS_WORDS] = __float_as_uint(eps);
+  }
+  if (nv <= k) {
+    for (int i = tid; i < k; i += kPfThreads) out[i] = i < nv ? i : -1;
+    return;
+  }
+  // 1. the floor from the tile maxima (all tiles kept when there are too few)
+  double thr = -INFINITY;
+  if (ntv > k) {
+    float tau, tau_hi;
+    bracket_kth(sh.sel, ntv, kk, [&](int64_t i) { return L.u.c.tm[i]; }, &tau, &tau_hi);
+    thr = cand_threshold(tau, eps, bsel);
+    if (!(thr <= (double)tau)) thr = -INFINITY;  // eps not finite: keep everything
+  }
+  // 2. the entries of the tiles that reach it, compacted (any order: every later
+  // step ranks by value and index)
+  for (int64_t j = tid; j < ntv; j += kPfThreads) {
+    if (!((double)L.u.c.tm[j] >= thr)) continue;
+    const float4* p = reinterpret_cast<const float4*>(row + j * kTileKeys);
+    float4 v4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v4[u] = p[u];
+    const float vs[16] = {v4[0].x, v4[0].y, v4[0].z, v4[0].w, v4[1].x, v4[1].y, v4[1].z, v4[1].w,
+                          v4[2].x, v4[2].y, v4[2].z, v4[2].w, v4[3].x, v4[3].y, v4[3].z, v4[3].w};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t s = j * kTileKeys + e;
+      if (s < nv && (double)vs[e] >= thr) {
+        const uint32_t pos = atomicAdd(&L.n_c, 1u);
+        if (pos < (uint32_t)kPfMax) { L.u.c.v[pos] = vs[e]; L.u.c.i[pos] = (uint32_t)s; }
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t n = L.n_c;
+  if (n > (uint32_t)kPfMax) {  // too many to hold: exact streaming pass over the row
+    __syncthreads();
+    finish_streaming(sh, kk, row, nv, thr, INFINITY, qt, wt, kb, bsel);
+    write_sorted(sh, tl, kk, k, out);
+    return;
+  }
+  // 3. the full-row selection over the list
+  float t_lo, t_hi;
+  bracket_kth(sh.sel, n, kk, [&](int64_t i) { return L.u.c.v[i]; }, &t_lo, &t_hi);
+  double lo, hi;
+  band_bounds(t_lo, t_hi, eps, bsel, &lo, &hi);
+  for (uint32_t i = tid; i < n; i += kPfThreads) {
+    const double v = (double)L.u.c.v[i];
+    const uint32_t idx = L.u.c.i[i];
+    if (v > hi) sh.out[atomicAdd(&sh.n_out, 1u)] = idx;
+    else if (v >= lo) {
+      const uint32_t p = atomicAdd(&sh.n_band, 1u);
+      if (p < kBandLds) sh.band_idx[p] = idx;
     }
   }
   __syncthreads();
@@ -2121,8 +2257,12 @@ static csa2_status topk_launch(const float* scores, const float* tile_max, uint3
                                size_t workspace_bytes, hipStream_t st, int bsel) {
   (void)hipGetLastError();
   if (topk_row_regime(scores, N)) {
-    hipLaunchKernelGGL(topk_small_kernel<Keys>, dim3(T), dim3(kFinThreads), 0, st, scores, stats, sm.parts,
-                       sm.n_parts, sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, k, indices, bsel);
+    if (tile_max)
+      hipLaunchKernelGGL(topk_rows_pf_kernel<Keys>, dim3(T), dim3(kPfThreads), 0, st, scores, tile_max, stats,
+                         sm.parts, sm.n_parts, sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, k, indices, bsel);
+    else
+      hipLaunchKernelGGL(topk_small_kernel<Keys>, dim3(T), dim3(kFinThreads), 0, st, scores, stats, sm.parts,
+                         sm.n_parts, sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, k, indices, bsel);
     if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
     return CSA2_OK;
   }
