@@ -127,7 +127,8 @@ def summarize(stats_dir, fetch_dir=None, write_dir=None, mfma_dir=None):
             key = ("scan" if "idx_scan_kernel" in name and int(r["Grid_Size"]) == scan_grid else
                    "scan_mx" if "idx_scan_mx_kernel" in name else
                    "cal" if "neg_kernel" in name and int(r["Grid_Size"]) == cal_grid else
-                   "attend" if "attend_kernel" in name else "combine" if "attend_combine" in name else None)
+                   "combine" if "attend_combine" in name else
+                   "attend" if ("attend_kernel" in name or "attend_cs_kernel" in name) else None)
             if key:
                 acc.setdefault(key, {}).setdefault(r["Dispatch_Id"], 0.0)
                 acc[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
@@ -160,27 +161,29 @@ def summarize(stats_dir, fetch_dir=None, write_dir=None, mfma_dir=None):
     def by_grid(d, counter, kernel):
         acc = {}
         for r in rows(d, "counter_collection.csv"):
-            if r["Counter_Name"] == counter and kernel in r["Kernel_Name"] and "combine" not in r["Kernel_Name"]:
-                g = acc.setdefault(int(r["Grid_Size"]), {})
+            if r["Counter_Name"] == counter and any(k in r["Kernel_Name"] for k in kernel.split("|")):
+                g = acc.setdefault((r["Kernel_Name"].split("(")[0].replace("void csa2::", "").replace("csa2::", ""),
+                                    int(r["Grid_Size"])), {})
                 v = g.setdefault(r["Dispatch_Id"], [0.0, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])])
                 v[0] += float(r["Counter_Value"])
         return {k: (sum(x[0] for x in v.values()) / len(v), sum(x[1] for x in v.values()) / len(v), len(v))
                 for k, v in acc.items()}
 
-    print("\n### attend_kernel per launch shape (same FETCH / WRITE runs and scales)\n")
-    fa, wa = by_grid(fetch_dir, "FETCH_SIZE", "attend_kernel"), by_grid(write_dir, "WRITE_SIZE", "attend_kernel")
-    for grid in sorted(fa):
-        if grid in wa:
-            print(f"- grid {grid} threads: FETCH {fa[grid][0] * 1024 * f_scale:.0f} B, "
-                  f"WRITE {wa[grid][0] * 1024 * w_scale:.0f} B per dispatch (means of {fa[grid][2]})")
+    kinds = "attend_kernel|attend_cs_kernel|attend_combine_kernel"
+    print("\n### attention kernels per launch shape (same FETCH / WRITE runs and scales)\n")
+    fa, wa = by_grid(fetch_dir, "FETCH_SIZE", kinds), by_grid(write_dir, "WRITE_SIZE", kinds)
+    for key in sorted(fa, key=lambda k: (k[1], k[0])):
+        if key in wa:
+            print(f"- {key[0]}, grid {key[1]} threads: FETCH {fa[key][0] * 1024 * f_scale:.0f} B, "
+                  f"WRITE {wa[key][0] * 1024 * w_scale:.0f} B per dispatch (means of {fa[key][2]})")
     if mfma_dir:
-        print("\n### MFMA work of attend_kernel (rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16)\n")
-        mo = by_grid(mfma_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16", "attend_kernel")
-        for grid in sorted(mo):
-            flops, ns, n = mo[grid][0] * 512, mo[grid][1], mo[grid][2]
-            print(f"- grid {grid} threads: {flops:.4g} bf16 MFMA flop per dispatch, {ns / 1e3:.1f} us per dispatch "
-                  f"under counter collection -> {flops / ns / 1e3:.2f} TFLOP/s = {flops / ns / 1e3 / MFMA_BF16_PEAK_TFLOPS:.4f} "
-                  f"of 2.5 PFLOP/s (means of {n})")
+        print("\n### MFMA work of the attention kernels (rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16)\n")
+        mo = by_grid(mfma_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16", "attend_kernel|attend_cs_kernel")
+        for key in sorted(mo, key=lambda k: (k[1], k[0])):
+            flops, ns, n = mo[key][0] * 512, mo[key][1], mo[key][2]
+            print(f"- {key[0]}, grid {key[1]} threads: {flops:.4g} bf16 MFMA flop per dispatch, {ns / 1e3:.1f} us per "
+                  f"dispatch under counter collection -> {flops / ns / 1e3:.2f} TFLOP/s = "
+                  f"{flops / ns / 1e3 / MFMA_BF16_PEAK_TFLOPS:.4f} of 2.5 PFLOP/s (means of {n})")
     return 0
 
 
@@ -205,6 +208,8 @@ def main():
         return prefill_main(args, dev)
     if args.workload == "reuse_group":
         line = {"metric": METRIC, **reuse_group_section(args, dev)}
+        if args.copy_calibration:
+            copy_calibration(dev)
         print(json.dumps(line), flush=True)
         return 0
     wl = WORKLOADS[args.workload]
@@ -347,11 +352,7 @@ def main():
     copy_gbps = 2 * (1 << 30) / (cp_med * 1e-6) / 1e9
     del x, y
     if args.copy_calibration:
-        xf = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device=dev)
-        yf = torch.empty_like(xf)
-        torch.neg(xf, out=yf)
-        torch.cuda.synchronize()
-        del xf, yf
+        copy_calibration(dev)
 
     line = {
         "metric": METRIC,
@@ -413,6 +414,17 @@ def main():
 
 
 METRIC = "decode queries/s + achieved HBM GB/s (% peak), CSA2 top-512 FP4 attn at 1 GPU"
+
+
+def copy_calibration(dev):
+    """torch.neg over CAL_BYTES of fp32 (reads and writes CAL_BYTES): the reference dispatch
+    that scales rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to bytes."""
+    import torch
+    xf = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device=dev)
+    yf = torch.empty_like(xf)
+    torch.neg(xf, out=yf)
+    torch.cuda.synchronize()
+    del xf, yf
 
 
 def _timer(stream):
