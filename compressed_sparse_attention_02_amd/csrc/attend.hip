@@ -60,7 +60,7 @@ struct AttnArgs {
   int n_items;              // work items per query-layer (partial slots when > 1)
   uint16_t* out;            // [L][T][64][512]
   float* lse;               // [L][T][64] or null
-  uint16_t* part_o;         // [L][T][n_items][64][512], bf16
+  uint16_t* part_o;         // [L][T][n_items] slots of 64 x 512 bf16 in 16 x 16 tiles (part_tile_off)
   float* part_ml;           // [L][T][n_items][64][2]  (max in log2 units, sum)
 };
 
@@ -85,6 +85,15 @@ __device__ __forceinline__ int block_layer() { return W == 1 ? (int)(blockIdx.z 
 __device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
   const __bf16 a = (__bf16)lo, b = (__bf16)hi;
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Split-K partial slot layout: 64 heads x 512 channels as 16 x 16 tiles,
+// head group G (heads 16G..16G+15) outermost, then channel tile ct (channels
+// 16ct..16ct+15), then head, then channel: a wave's store of one tile (lane
+// (r, g): head r, channels 4g..4g+3) is 512 contiguous bytes, and the combine
+// reads whole tiles.  Offset (bf16 elements) of head 16G + r, channel 16ct + c.
+__device__ __forceinline__ size_t part_tile_off(int G, int ct, int r, int c) {
+  return ((size_t)(G * (kDim / 16) + ct) * 16 + r) * 16 + c;
 }
 
 // 16-byte LDS operand read (the offsets used are multiples of 16 bytes).
@@ -462,16 +471,17 @@ __device__ void write_partial(const AttnArgs& a, const HeadState& st, int layer,
   float l = st.l;
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  const size_t base = (((size_t)layer * a.T + t) * a.n_items + slot) * kHeads + head;
-  uint16_t* op = a.part_o + base * kDim + 4 * g;
-  // bf16 partials (the combine accumulates in fp32); streaming stores: they
-  // are read once, by the combine kernel
+  const size_t slot_id = ((size_t)layer * a.T + t) * a.n_items + slot;
+  const size_t base = slot_id * kHeads + head;
+  uint16_t* op = a.part_o + slot_id * kHeads * kDim + part_tile_off(hg, 0, lane & 15, 4 * g);
+  // bf16 partials (the combine accumulates in fp32), one 512-byte tile per
+  // store; streaming stores: they are read once, by the combine kernel
 #pragma unroll
   for (int mb = 0; mb < 32; ++mb) {
     const uint32_t w0 = pack_bf16x2_rne(st.o[mb][0], st.o[mb][1]);
     const uint32_t w1 = pack_bf16x2_rne(st.o[mb][2], st.o[mb][3]);
     const u32x2 w = {w0, w1};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(op + 16 * mb));
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(op + 256 * mb));
   }
   if (g == 0) {
     a.part_ml[base * 2 + 0] = st.m;
@@ -565,9 +575,8 @@ struct CsShared {
   alignas(16) floatx4 sx[8][2][64];                   // partial S^T [wave][m-tile][lane]
   alignas(16) bf16x8 p[4][64];                        // P^T of head group G, B-operand layout
   float alpha[kHeads];                                // this chunk's rescale factor per head
-  int grow[4];                                        // head group G rescales this chunk
+  alignas(16) int grow[4];                            // head group G rescales this chunk
   float fin_m[kHeads], fin_l[kHeads];                 // final (max, sum) per head
-  int valid[kChunk];
   float rope[32][2];
 };
 
@@ -599,7 +608,7 @@ __device__ __forceinline__ int cs_slice_row(int lane, int i) { return group_row(
 struct CsRaw {
   uint4 s[2][3];
   uint4 x[4];
-  uint32_t ok_x;  // bit i: slice row i valid
+  uint32_t ok;  // bit r: row r of the chunk valid (the same in every lane)
 };
 
 struct CsIdx {
@@ -623,8 +632,9 @@ __device__ __forceinline__ void cs_load_raw(const AttnArgs& a, int t, int b, int
   const int g = lane >> 4;
   const int sc0 = 256 * (w >> 2) + 64 * g;       // S-layout channels sc0 .. sc0 + 63
   const int xc0 = kCsSlice * w + 8 * (lane & 7);  // slice-layout channels xc0 .. xc0 + 7
-  uint32_t ok_x = 0;
   if (c < a.n_main) {
+    // row validity of the chunk from the S-layout indices (rows lane % 16 and 16 + lane % 16)
+    raw.ok = (uint32_t)(__ballot(ix.s[0] >= 0) & 0xFFFFull) | ((uint32_t)(__ballot(ix.s[1] >= 0) & 0xFFFFull) << 16);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const size_t rowid = (size_t)b * a.N + (ix.s[m] >= 0 ? ix.s[m] : 0);
@@ -637,7 +647,6 @@ __device__ __forceinline__ void cs_load_raw(const AttnArgs& a, int t, int b, int
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ok_x |= (ix.x[i] >= 0 ? 1u : 0u) << i;
       const size_t rowid = (size_t)b * a.N + (ix.x[i] >= 0 ? ix.x[i] : 0);
       raw.x[i].x = *reinterpret_cast<const uint32_t*>(a.kv_fp4 + rowid * 256 + xc0 / 2);
       raw.x[i].y = KVF == CSA2_KV_MXFP4 ? a.kv_scale[rowid * 16 + xc0 / 32] : a.kv_scale[rowid * 32 + xc0 / 16];
@@ -648,10 +657,11 @@ __device__ __forceinline__ void cs_load_raw(const AttnArgs& a, int t, int b, int
     const int row0 = ws + (c - a.n_main) * kChunk;
     const size_t base = ((size_t)layer * a.B + b) * a.S;
     const int last = we > 0 ? we - 1 : 0;
+    const int nvalid = we - row0 < 0 ? 0 : (we - row0 > kChunk ? kChunk : we - row0);  // rows row0 .. we-1
+    raw.ok = nvalid >= kChunk ? 0xFFFFFFFFu : (1u << nvalid) - 1u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = row0 + cs_slice_row(lane, i);
-      ok_x |= (row < we ? 1u : 0u) << i;
       const size_t rr = base + (row < we ? row : last);
       if (SWF == CSA2_SWA_BF16) {
         raw.x[i] = *reinterpret_cast<const uint4*>(a.swa + rr * kDim + xc0);
@@ -663,11 +673,10 @@ __device__ __forceinline__ void cs_load_raw(const AttnArgs& a, int t, int b, int
       }
     }
   }
-  raw.ok_x = ok_x;
 }
 
-// The wave's transposed slice of chunk c into LDS (with the row validity,
-// written by wave 0); for window chunks also its part of the row-major copy.
+// The wave's transposed slice of chunk c into LDS; for window chunks also its
+// part of the row-major copy.
 template <int KVF, int SWF>
 __device__ __forceinline__ void cs_store_slice(const AttnArgs& a, CsShared& sh, int c, const CsRaw& raw) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -708,10 +717,6 @@ __device__ __forceinline__ void cs_store_slice(const AttnArgs& a, CsShared& sh, 
       wd[p] = lo | (hi << 16);
     }
     *reinterpret_cast<uint2*>(&xt[cs_xt_off(8 * cg + e, kb >> 1) + 4 * (kb & 1)]) = make_uint2(wd[0], wd[1]);
-  }
-  if (w == 0 && cg == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sh.valid[cs_slice_row(lane, i)] = (raw.ok_x >> i) & 1u;
   }
 }
 
@@ -791,6 +796,7 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
 
   for (int c = c0; c < c1; ++c) {
     cs_store_slice<KVF, SWF>(a, sh, c, raw);
+    const uint32_t ok = __builtin_amdgcn_readfirstlane(raw.ok);  // this chunk's valid rows
     floatx4 acc[2];
     if (c < a.n_main) {
       cs_s_product<KVF, false>(sh, raw, qb, acc, sc0);
@@ -810,10 +816,11 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
     acc[1] += sh.sx[w ^ 4][1][lane];
     // acc[m][i]: row 16 m + 4 g + i, head 16 hg + r16
     float z[8];
+    const uint32_t okg = ok >> (4 * g);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      z[i] = sh.valid[4 * g + i] ? acc[0][i] * a.scale_log2 : -INFINITY;
-      z[4 + i] = sh.valid[16 + 4 * g + i] ? acc[1][i] * a.scale_log2 : -INFINITY;
+      z[i] = ((okg >> i) & 1u) ? acc[0][i] * a.scale_log2 : -INFINITY;
+      z[4 + i] = ((okg >> (16 + i)) & 1u) ? acc[1][i] * a.scale_log2 : -INFINITY;
     }
     float cm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
     cm = max_xor16(cm);
@@ -845,9 +852,11 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
     }
     __syncthreads();
     // O^T of this wave's channels, all four head groups
+    const int4 grows = *reinterpret_cast<const int4*>(sh.grow);
+    const int grw[4] = {grows.x, grows.y, grows.z, grows.w};
 #pragma unroll
     for (int G = 0; G < 4; ++G) {
-      if (st.started && sh.grow[G]) {
+      if (st.started && grw[G]) {
         const float al = sh.alpha[16 * G + r16];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) st.o[mb][G] *= al;
@@ -909,13 +918,14 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
       if (a.lse && w == 0 && g == 0)
         a.lse[qrow + head] = (m == -INFINITY) ? -INFINITY : (m + log2f(den)) * kLn2;
     } else {
-      const size_t base = (((size_t)layer * a.T + t) * a.n_items + item) * kHeads + head;
-      uint16_t* op = a.part_o + base * kDim + kCsSlice * w + 4 * g;
+      const size_t slot_id = ((size_t)layer * a.T + t) * a.n_items + item;
+      const size_t base = slot_id * kHeads + head;
+      uint16_t* op = a.part_o + slot_id * kHeads * kDim + part_tile_off(G, 4 * w, r16, 4 * g);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const u32x2 wv = {pack_bf16x2_rne(st.o[mb][G][0], st.o[mb][G][1]),
                           pack_bf16x2_rne(st.o[mb][G][2], st.o[mb][G][3])};
-        __builtin_nontemporal_store(wv, reinterpret_cast<u32x2*>(op + 16 * mb));
+        __builtin_nontemporal_store(wv, reinterpret_cast<u32x2*>(op + 256 * mb));
       }
       if (w == 0 && g == 0) {
         a.part_ml[base * 2 + 0] = m;
@@ -925,64 +935,67 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
   }
 }
 
-// Merge the partial slots of each (layer, query, head): grid (64, T, L),
-// 128 threads x 4 channels.  out = sum_s O_s 2^(m_s - M) / den,
+// Merge the partial slots of each (layer, query): block (32 G + ct, t, layer),
+// one wave, takes partial tile ct of head group G (heads 16G .. 16G+15,
+// channels 16ct .. 16ct+15).  out = sum_s O_s 2^(m_s - M) / den,
 // den = sum_s l_s 2^(m_s - M) (+ 2^(sink - M)), M = max_s m_s (and the sink).
-__global__ __launch_bounds__(128) void attend_combine_kernel(AttnArgs a) {
-  const int h = blockIdx.x, t = blockIdx.y, layer = blockIdx.z;
-  const int tid = threadIdx.x;
-  const size_t base = ((size_t)layer * a.T + t) * a.n_items;
-  __shared__ float fac[64];
-  __shared__ float s_inv;
-  // all slot loads in flight at once (at most kMaxSlots slots), before the weights are known
-  uint2 o[kMaxSlots];
+// Lane (r, g) takes head 16G + r, channels 16ct + 4g .. +3: each slot's tile
+// read is 512 contiguous bytes, and all slots' loads are issued before any is
+// used.  Small blocks spread the reads over every CU: the kernel is bound by
+// how many cache lines each CU can have in flight at small T.
+__global__ __launch_bounds__(64) void attend_combine_kernel(AttnArgs a) {
+  const int G = blockIdx.x >> 5, ct = blockIdx.x & 31, t = blockIdx.y, layer = blockIdx.z;
+  const int lane = threadIdx.x, r = lane >> 2, g = lane & 3;
+  const int head = 16 * G + r;
+  const int n = a.n_items;
+  const size_t slot0 = ((size_t)layer * a.T + t) * n;
+  const size_t toff = part_tile_off(G, ct, r, 4 * g);
+  float2 ml[kMaxSlots];
+  uint2 v[kMaxSlots];
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s)
-    if (s < a.n_items) o[s] = *reinterpret_cast<const uint2*>(a.part_o + ((base + s) * kHeads + h) * kDim + 4 * tid);
-  if (tid < 64) {
-    // one lane per slot (n_items <= 64): max, then weighted sum, by wave reductions
-    const bool has = tid < a.n_items;
-    const float ms = has ? a.part_ml[((base + tid) * kHeads + h) * 2] : -INFINITY;
-    const float ls = has ? a.part_ml[((base + tid) * kHeads + h) * 2 + 1] : 0.f;
-    float M = wave_max_dpp(ms);
-    float sk = -INFINITY;
-    if (a.sink) {
-      sk = a.sink[(size_t)layer * kHeads + h] * kLog2e;
-      M = fmaxf(M, sk);
+    if (s < n) {
+      ml[s] = *reinterpret_cast<const float2*>(a.part_ml + ((slot0 + s) * kHeads + head) * 2);
+      v[s] = *reinterpret_cast<const uint2*>(a.part_o + (slot0 + s) * kHeads * kDim + toff);
     }
-    const float f = (M == -INFINITY || ms == -INFINITY) ? 0.f : exp2f(ms - M);
-    float den = wave_sum_dpp(ls * f);
-    if (a.sink && M != -INFINITY) den += exp2f(sk - M);
-    if (has) fac[tid] = f;
-    if (tid == 0) {
-      s_inv = (M == -INFINITY || den == 0.f) ? 0.f : 1.f / den;
-      if (a.lse) a.lse[((size_t)layer * a.T + t) * kHeads + h] = (M == -INFINITY) ? -INFINITY : (M + log2f(den)) * kLn2;
-    }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxSlots; ++s)
+    if (s < n) M = fmaxf(M, ml[s].x);
+  float sk = -INFINITY;
+  if (a.sink) {
+    sk = a.sink[(size_t)layer * kHeads + head] * kLog2e;
+    M = fmaxf(M, sk);
   }
-  __syncthreads();
+  float den = 0.f;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kMaxSlots; ++s)
-    if (s < a.n_items && fac[s] != 0.f) {
-      const floatx4 v = {bf16lo(o[s].x), bf16hi(o[s].x), bf16lo(o[s].y), bf16hi(o[s].y)};
-      acc += v * fac[s];
+    if (s < n) {
+      const float f = (M == -INFINITY || ml[s].x == -INFINITY) ? 0.f : exp2f(ml[s].x - M);
+      if (f != 0.f) {
+        den += ml[s].y * f;
+        const floatx4 x = {bf16lo(v[s].x), bf16hi(v[s].x), bf16lo(v[s].y), bf16hi(v[s].y)};
+        acc += x * f;
+      }
     }
-  const float iv = s_inv;
-  uint16_t* op = a.out + (((size_t)layer * a.T + t) * kHeads + h) * kDim + 4 * tid;
-  float v[4] = {acc[0] * iv, acc[1] * iv, acc[2] * iv, acc[3] * iv};
-  if (tid >= 112 && a.rope_pos) {  // channels 448..511: pairs (v0, v1), (v2, v3)
+  if (a.sink && M != -INFINITY) den += exp2f(sk - M);
+  const float inv = (M == -INFINITY || den == 0.f) ? 0.f : 1.f / den;
+  if (a.lse && ct == 0 && g == 0)
+    a.lse[((size_t)layer * a.T + t) * kHeads + head] = (M == -INFINITY) ? -INFINITY : (M + log2f(den)) * kLn2;
+  float x[4] = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+  if (ct >= 28 && a.rope_pos) {  // channels 448..511: pairs (x0, x1), (x2, x3)
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      float c, sn;
-      rope_cs(a, t, 2 * (tid - 112) + p, &c, &sn);
-      const float x = v[2 * p], y = v[2 * p + 1];
-      v[2 * p] = x * c - y * sn;
-      v[2 * p + 1] = x * sn + y * c;
+      float cv, sv;
+      rope_cs(a, t, 8 * (ct - 28) + 2 * g + p, &cv, &sv);
+      const float x0 = x[2 * p], x1 = x[2 * p + 1];
+      x[2 * p] = x0 * cv - x1 * sv;
+      x[2 * p + 1] = x0 * sv + x1 * cv;
     }
   }
-  const uint32_t w0 = pack_bf16x2_rne(v[0], v[1]);
-  const uint32_t w1 = pack_bf16x2_rne(v[2], v[3]);
-  *reinterpret_cast<uint2*>(op) = make_uint2(w0, w1);
+  uint16_t* op = a.out + (((size_t)layer * a.T + t) * kHeads + head) * kDim + 16 * ct + 4 * g;
+  *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2_rne(x[0], x[1]), pack_bf16x2_rne(x[2], x[3]));
 }
 
 struct AttendPlan {
@@ -1100,7 +1113,7 @@ static csa2_status attend_launch(int32_t L, const void* q, const uint8_t* kv_fp4
 #undef CSA2_ATTEND_FMT
 #undef CSA2_ATTEND4
 #undef CSA2_ATTEND1
-  if (need) hipLaunchKernelGGL(attend_combine_kernel, dim3(kHeads, T, L), dim3(128), 0, st, a);
+  if (need) hipLaunchKernelGGL(attend_combine_kernel, dim3(4 * (kDim / 16), T, L), dim3(64), 0, st, a);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
   return CSA2_OK;
 }
