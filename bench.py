@@ -568,7 +568,11 @@ def reuse_group_section(args, dev):
 
     ms = _wall_ms(step, args.steps, args.warmup)
     ms_fused = _wall_ms(step_fused, args.steps, args.warmup)
-    same = torch.equal(out_3, out_1[:, 0])     # both forms give the same outputs
+    # both forms compute the same attention; their split-K merges may round differently
+    d3, d1 = out_3.float(), out_1[:, 0].float()
+    same = {"bitwise_equal": bool(torch.equal(out_3, out_1[:, 0])),
+            "max_abs_diff": float((d3 - d1).abs().max()),
+            "within_bf16_tolerance": bool(((d3 - d1).abs() <= 1e-2 + 2e-2 * d1.abs()).all())}
     timed = _timer(torch.cuda.current_stream(dev))
     reps = max(10, args.steps)
     st = {k: timed(calls[k], reps) for k in ("index", "topk", "attend")}
@@ -598,7 +602,7 @@ def reuse_group_section(args, dev):
         "step_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "fused_reuse_step": {"ms_per_step": ms_fused, "value": T / (ms_fused * 1e-3),
                              "step_frac_of_peak": step_bytes / (ms_fused * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                             "outputs_equal_to_single_layer_calls": same},
+                             "outputs_vs_single_layer_calls": same},
         "roofline": {"kernel": "idx_scan_kernel (all of csa2_index)", "bound": "hbm", "achieved": scan_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": scan_gbps / HBM_PEAK_GBPS,
                      "algorithmic_bytes_per_launch": idx_bytes, "avg_launch_us": st["index"][1]},

@@ -20,11 +20,12 @@
 // statistics live in the same lanes as that head's O^T accumulators, so no
 // cross-lane shuffles are needed except the 4-lane row reductions.
 // Chunks of one query are split over work items (split-K); partial (max,
-// sum, O) are merged by a combine kernel.  The split depends on the number of
-// queries only; Reuse with several layers runs the layers as independent
-// query-layers of one launch (each stages its own chunks: the selected rows
-// are the same for every layer, so their second and later reads hit the L2),
-// so layer l's result is bit-identical to a single-layer call with q[l].
+// sum, O) are merged by a combine kernel.  The split is chosen per launch
+// shape (queries x layers).  Reuse with several layers runs the layers as
+// independent query-layers of one launch (each stages its own chunks: the
+// selected rows are the same for every layer, so their second and later
+// reads hit the L2); layer l's result equals a single-layer call with q[l] up
+// to the rounding of the merge.
 #include <mutex>
 
 #include "mxfp4.h"
@@ -1002,27 +1003,48 @@ struct AttendPlan {
   int n_main, n_swa, cpw, n_items;
 };
 
-// Work items per launch the split aims at (about one round of resident blocks).
-#ifndef CSA2_ATTN_TARGET_ITEMS
-#define CSA2_ATTN_TARGET_ITEMS 256
-#endif
-constexpr int kTargetItems = CSA2_ATTN_TARGET_ITEMS;
 // One-wave blocks (a work item's four head groups on four CUs) while the
 // whole launch fits in one round of them (two per CU, by their LDS).
 constexpr int kOneWaveBlocks = 512;
 
-// The split of one query's chunks over work items.  It depends on T only,
-// so the result of a query-layer is the same whatever L a launch has.
-static AttendPlan attend_plan(int32_t T, int32_t k, int32_t window) {
+// Cost model of a split, fitted to timings of these kernels on MI355X
+// (256 CUs).  The eight-wave blocks run one per CU (their LDS), so Q
+// query-layers split into n work items of cpw chunks take ceil(Q n / 256)
+// rounds of cpw chunks, about 3.3 us per chunk; a split (n > 1) adds the
+// combine launch, about 4 us, and a 64 KiB partial per work item, written
+// and read back at about 4 TB/s.
+constexpr int kPlanCUs = 256;
+constexpr double kPlanChunkUs = 3.3;
+constexpr double kPlanCombineUs = 4.0;
+constexpr double kPlanSlotUs = (kHeads * kDim * 2.0) * 2.0 / 4.0e6;  // 64 KiB out and back at 4 TB/s
+
+// The split of each query-layer's chunks over work items for a launch of T
+// query rows x L layers: the item count of least modelled time (ties to
+// fewer items, i.e. less partial traffic).  Launches with at least one
+// query-layer per CU are not split: every CU already has a block.  A
+// query-layer's result depends on the split only through the rounding of the
+// merge, so the same rows can round differently in launches of other shapes.
+static AttendPlan attend_plan(int32_t T, int32_t L, int32_t k, int32_t window) {
   AttendPlan p;
   p.n_main = (k + kChunk - 1) / kChunk;
   p.n_swa = (window + kChunk - 1) / kChunk;
   const int n_chunks = p.n_main + p.n_swa;
-  int64_t want = (kTargetItems + T - 1) / T;
-  if (want > n_chunks) want = n_chunks;
-  if (want < 1) want = 1;
-  p.cpw = (int)((n_chunks + want - 1) / want);
-  p.n_items = (n_chunks + p.cpw - 1) / p.cpw;
+  const int64_t Q = (int64_t)T * L;
+  p.cpw = n_chunks;
+  p.n_items = 1;
+  if (Q >= kPlanCUs) return p;
+  double best = 0.0;
+  // cpw downwards: n grows, and of the cpw giving the same n the last (least) costs least
+  for (int cpw = n_chunks; cpw >= 1; --cpw) {
+    const int n = (n_chunks + cpw - 1) / cpw;
+    const double rounds = (double)((Q * n + kPlanCUs - 1) / kPlanCUs);
+    const double cost = rounds * cpw * kPlanChunkUs + (n == 1 ? 0.0 : kPlanCombineUs + (double)Q * n * kPlanSlotUs);
+    if (cpw == n_chunks || cost < best - 1e-9) {
+      best = cost;
+      p.cpw = cpw;
+      p.n_items = n;
+    }
+  }
   return p;
 }
 
@@ -1055,7 +1077,7 @@ static csa2_status attend_launch(int32_t L, const void* q, const uint8_t* kv_fp4
   if (k != kTopK || window < 1 || window > CSA2_MAX_WINDOW || L < 1 || L > CSA2_MAX_LAYERS || T > 65535 ||
       N >= ((int64_t)1 << 31))
     return CSA2_ERR_UNSUPPORTED;
-  const AttendPlan p = attend_plan(T, k, window);
+  const AttendPlan p = attend_plan(T, L, k, window);
   const size_t need = attend_ws_bytes(T, p, L);
   if (need > 0 && (!workspace || !aligned16(workspace) || workspace_bytes < need)) return CSA2_ERR_WORKSPACE;
   AttnArgs a;
@@ -1156,7 +1178,7 @@ using namespace csa2;
 extern "C" size_t csa2_attend_workspace_bytes(int32_t T, int32_t k, int32_t window, int32_t n_layers) {
   if (T < 1 || k != kTopK || window < 1 || window > CSA2_MAX_WINDOW || n_layers < 1 || n_layers > CSA2_MAX_LAYERS)
     return 0;
-  const AttendPlan p = attend_plan(T, k, window);
+  const AttendPlan p = attend_plan(T, n_layers, k, window);
   return attend_ws_bytes(T, p, n_layers);
 }
 

@@ -319,8 +319,11 @@ csa2_status csa2_attend_fp4(const void* q, const uint8_t* kv_fp4, const uint8_t*
  * the index list and main KV published by the latest Full (or Reindex) layer,
  * each with its own query, window KV and sink; nothing is scored or selected.
  * Layer l's output equals csa2_attend_fp4 called with q[l], swa[l], sink[l]
- * and the shared indices/KV.  With n_layers > 1 every selected main-KV row is
- * gathered and dequantised once for all layers.
+ * and the shared indices/KV, up to rounding: each query-layer's rows are
+ * split over work items whose partial results are merged, and the split is
+ * chosen per launch shape (T x n_layers), so the merge can round differently
+ * from a single-layer call.  The layers run in one launch; their reads of the
+ * shared selected rows after the first come from the L2.
  *
  *  n_layers 1..8
  *  q     bf16 [L][T][64][512];  swa bf16 [L][B][S][512];  sink fp32 [L][64] or NULL
@@ -341,16 +344,17 @@ csa2_status csa2_reuse_attend(int32_t n_layers, const void* q, const uint8_t* kv
  * csa2_reuse_attend without the workspace arguments, same arguments
  * otherwise, same kernels and results.  Its split-K partials live in a
  * library-owned device array of CSA2_STATIC_SCRATCH_BYTES per GPU, held until
- * the process ends; the call itself allocates nothing.  Returns
- * CSA2_ERR_WORKSPACE, before touching any device, when
- * csa2_attend_workspace_bytes(T, k, window, n_layers) exceeds that size (one
- * layer always fits).  Every call on a GPU shares that GPU's array: calls
- * that may overlap on one GPU (different streams, threads) race and must be
- * serialised by the caller.  The array needs no clearing between calls.
+ * the process ends; the call itself allocates nothing.  Every valid call
+ * fits: the split (and its partials) is only used for launches of fewer than
+ * 256 query-layers, whose csa2_attend_workspace_bytes is at most 30.3 MiB;
+ * the call still returns CSA2_ERR_WORKSPACE, before touching any device, if
+ * that size ever exceeded the array.  Every call on a GPU shares that GPU's
+ * array: calls that may overlap on one GPU (different streams, threads) race
+ * and must be serialised by the caller.  The array needs no clearing between calls.
  * Other errors as csa2_reuse_attend; CSA2_ERR_LAUNCH also when the array's
  * device address cannot be looked up for the stream's device.
  */
-#define CSA2_STATIC_SCRATCH_BYTES 34603008  /* 33 MiB: every single-layer call fits */
+#define CSA2_STATIC_SCRATCH_BYTES 34603008  /* 33 MiB: every valid call fits */
 csa2_status csa2_reuse_attend_static(int32_t n_layers, const void* q, const uint8_t* kv_fp4,
                                      const uint8_t* kv_scale, const int32_t* indices, const void* swa,
                                      const int32_t* swa_end, const float* sink, float softmax_scale,

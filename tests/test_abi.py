@@ -389,13 +389,22 @@ def test_sanitized_builds_are_loaded():
     assert "libclang_rt.asan" in maps
 
 
-def test_static_attend_rejects_before_touching_a_device(L):
-    """csa2_reuse_attend_static checks the call against its static scratch size first: on this
-    CPU-only host a call that cannot fit returns WORKSPACE without any device access."""
+def test_static_attend_scratch_covers_every_call(L):
+    """The split (and its partials) is chosen per launch shape and only used below 256
+    query-layers: no valid call of csa2_reuse_attend_static needs more than its static scratch.
+    Invalid layer counts are rejected before any device access (this host has no GPU)."""
+    # one window per count of window chunks (the plan depends on the chunk count only)
+    worst = max(csa.attend_workspace_bytes(T, window=w, n_layers=nl)
+                for nl in range(1, 9) for w in (32, 64, 96, 128) for T in range(1, 300))
+    assert 0 < worst <= 31_771_853 <= csa.STATIC_SCRATCH_BYTES        # 30.3 MiB, as documented
+    assert all(csa.attend_workspace_bytes(T, n_layers=nl) == 0 for T in (256, 4096, 65535) for nl in (1, 8))
+    assert csa.attend_workspace_bytes(128, n_layers=2) == 0             # 256 query-layers: not split
+    # every split slot is one 64 x 512 bf16 partial plus its (max, sum) pair per head
+    slot = 64 * 512 * 2 + 64 * 2 * 4
+    for T, nl in [(4, 1), (4, 3), (32, 1), (32, 3), (64, 1), (160, 1)]:
+        b = csa.attend_workspace_bytes(T, n_layers=nl)
+        assert b % 256 == 0 and slot * T * nl * 2 <= b < slot * T * nl * 21   # 2 .. 20 items (chunks)
     P = ctypes.c_void_p(0x100000)
-    assert csa.attend_workspace_bytes(64, n_layers=8) > csa.STATIC_SCRATCH_BYTES
-    assert csa.attend_workspace_bytes(255, n_layers=1) <= csa.STATIC_SCRATCH_BYTES   # one layer always fits
     args = lambda nl, T: [nl, P, P, P, P, P, P, None, 0.044, T, 1, 4096, 128, 128, 512, P, None, None]
-    assert L.csa2_reuse_attend_static(*args(8, 64)) == WORKSPACE
     assert L.csa2_reuse_attend_static(*args(9, 4)) == UNSUPPORTED
     assert L.csa2_reuse_attend_static(*args(0, 4)) == UNSUPPORTED

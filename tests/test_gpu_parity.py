@@ -241,8 +241,8 @@ def test_attend_split_plans(T_q):
         assert_close_bf16(out[t], ref[t][0], what=f"T={T_q} t={t}")
 
 
-# 3 sequences: one-wave blocks (each work item's heads split over four blocks);
-# 48 sequences: more work items than that split takes, four-wave blocks
+# 3 sequences x 3 layers: 20 single-chunk work items per query-layer;
+# 48 sequences x 3 layers: 3 work items of up to 7 chunks (eight-wave blocks both)
 @pytest.mark.parametrize("B", [3, 48])
 def test_reuse_layers_match_oracle_and_attend(B):
     log(f"[reuse] 3 layers, {B} sequences")
