@@ -153,9 +153,18 @@ __device__ __forceinline__ void bound_terms(const uint16_t* __restrict__ q_t, co
     wh = w_t[tid >> 3];
   }
   float m = 0.f;
-  for (int64_t i = tid + 8 * (int64_t)nthreads; i < n_parts; i += nthreads) m = fmaxf(m, parts_b[i]);
 #pragma unroll
   for (int u = 0; u < 8; ++u) m = fmaxf(m, pm[u]);
+  // the rest eight loads at a time (a maximum: the order does not matter)
+  for (int64_t i0 = 8 * (int64_t)nthreads; i0 < n_parts; i0 += 8 * (int64_t)nthreads) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = i0 + tid + (int64_t)u * nthreads;
+      pm[u] = i < n_parts ? parts_b[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = fmaxf(m, pm[u]);
+  }
   double a = 0.0, s = 0.0;
   if (tid < 256) {
     const uint32_t wd[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
@@ -514,6 +523,84 @@ __device__ void write_sorted(FinLds& sh, FinTail& tl, uint32_t kk, int k, int32_
   for (int i = threadIdx.x; i < k; i += (int)blockDim.x) out[i] = i < (int)kk ? (int32_t)tl.out_sorted[i] : -1;
 }
 
+// Block-wide exclusive prefix sum (all threads, blockDim.x a multiple of 64).
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    const uint32_t c = wsum[i];
+    off += i < wave ? c : 0u;
+    tot += c;
+  }
+  *total = tot;
+  return off + x - v;
+}
+
+// Position of this thread's flag among the block's set flags (ascending
+// thread order) and their total: one ballot per wave and one barrier.
+// `wsum` (one word per wave) must not be read by a previous call any more.
+__device__ __forceinline__ uint32_t block_flag_scan(bool flag, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const uint64_t b = __ballot(flag);
+  const uint32_t below = (uint32_t)__popcll(b & ((1ull << lane) - 1ull));
+  if (lane == 0) wsum[wave] = (uint32_t)__popcll(b);
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    const uint32_t c = wsum[i];
+    off += i < wave ? c : 0u;
+    tot += c;
+  }
+  *total = tot;
+  return off + below;
+}
+
+// Ascending output for rows of at most kSmallMax entries: a bitmap of the
+// selected indices in LDS (over the finishing tail's key-row staging, free by
+// then), word popcounts prefix-summed over the block, and each index stored
+// at its rank.  `wsum`: one word per wave for the block scan.
+constexpr int kBitWords = (kSmallMax + 31) / 32;
+__device__ void write_sorted_bits(FinLds& sh, FinTail& tl, uint32_t kk, int k, int64_t nv, uint32_t* wsum,
+                                  int32_t* out) {
+  static_assert(2 * kBitWords * sizeof(uint32_t) <= sizeof(tl.krows), "bitmap and prefix fit the key rows");
+  uint32_t* bits = reinterpret_cast<uint32_t*>(&tl.krows[0][0]);
+  uint32_t* pre = bits + kBitWords;
+  const int tid = threadIdx.x, bd = (int)blockDim.x;
+  const int nw = (int)((nv + 31) / 32);
+  for (int i = tid; i < nw; i += bd) bits[i] = 0u;
+  __syncthreads();
+  for (uint32_t i = tid; i < kk; i += bd) atomicOr(&bits[sh.out[i] >> 5], 1u << (sh.out[i] & 31u));
+  __syncthreads();
+  // thread j takes words j*per .. j*per + per - 1
+  const int per = (nw + bd - 1) / bd;
+  uint32_t c = 0;
+  for (int u = 0; u < per; ++u) {
+    const int w = tid * per + u;
+    if (w < nw) c += (uint32_t)__popc(bits[w]);
+  }
+  uint32_t tot;
+  uint32_t off = block_excl_scan(c, wsum, &tot);
+  for (int u = 0; u < per; ++u) {
+    const int w = tid * per + u;
+    if (w < nw) { pre[w] = off; off += (uint32_t)__popc(bits[w]); }
+  }
+  __syncthreads();
+  for (uint32_t i = tid; i < kk; i += bd) {
+    const uint32_t v = sh.out[i];
+    out[pre[v >> 5] + (uint32_t)__popc(bits[v >> 5] & ((1u << (v & 31u)) - 1u))] = (int32_t)v;
+  }
+  for (int i = (int)kk + tid; i < k; i += bd) out[i] = -1;
+}
+
 // Band bounds around the bracket [t_lo, t_hi] of T^ (rounded outwards in fp64).
 // The k-th exact score S lies in [t_lo - eps, t_hi + eps].  Exact order: an
 // entry whose fp32 score is above t_hi + 2 eps is in, below t_lo - 2 eps out.
@@ -642,6 +729,8 @@ __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
 constexpr int kPfMax = 6144;                                        // listed entries held in LDS
 constexpr int kPfThreads = 512;                                     // two blocks per CU
 constexpr int kPfTiles = (kSmallMax + kTileKeys - 1) / kTileKeys;  // tile maxima of a row
+constexpr int kPfPer = (kPfTiles + kPfThreads - 1) / kPfThreads;   // tile maxima per thread
+static_assert(kPfTiles <= 65536, "tile ids are listed as 16-bit values");
 
 struct PfLds {
   FinLds f;
@@ -649,13 +738,14 @@ struct PfLds {
     struct {
       float v[kPfMax];
       uint32_t i[kPfMax];
-      float tm[kPfTiles];
+      uint16_t tiles[kPfTiles];  // the tiles that reach the floor
     } c;
     FinTail tail;
   } u;
-  uint32_t n_c;
-  float bm[kPfThreads / 64];
-  double bq[kPfThreads / 64], bs[kPfThreads / 64];
+  float fr[4][kPfThreads / 64];
+  double dr[2][kPfThreads / 64];
+  uint32_t wsum[kPfThreads / 64];
+  uint32_t res;
 };
 
 template <class Keys>
@@ -668,7 +758,7 @@ __global__ __launch_bounds__(kPfThreads) void topk_rows_pf_kernel(
   FinLds& sh = L.f;
   FinTail& tl = L.u.tail;
   const int t = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nv = n_visible(q_pos, t, ratio, N);
   int32_t* out = indices + (size_t)t * k;
   const uint32_t kk = (uint32_t)k;
@@ -678,66 +768,162 @@ __global__ __launch_bounds__(kPfThreads) void topk_rows_pf_kernel(
   const Keys kb = keys.seq(b, N);
   const float* row = scores + (size_t)t * N;
   const int64_t ntv = (nv + kTileKeys - 1) / kTileKeys;
-  if (tid == 0) { sh.n_out = 0; sh.n_band = 0; L.n_c = 0; }
-  for (int64_t j = tid; j < ntv; j += kPfThreads) L.u.c.tm[j] = tile_max[(size_t)t * tile_ld(N) + j];
-  {
-    float m2;
-    double qf, sw;
-    bound_terms(qt, wt, parts + (size_t)b * n_parts, n_parts, tid, kPfThreads, &m2, &qf, &sw);
-    m2 = wave_max_dpp(m2);
-    qf = wave_sum_groups8_f64(qf);
-    sw = wave_sum_groups8_f64(sw);
-    if ((tid & 63) == 0) { L.bm[tid >> 6] = m2; L.bq[tid >> 6] = qf; L.bs[tid >> 6] = sw; }
+  // 1. this thread's tile maxima (tiles tid, tid + kPfThreads, ...) and the bound
+  // terms, every load issued before any is used
+  float tv[kPfPer];
+  const float* tmr = tile_max + (size_t)t * tile_ld(N);
+#pragma unroll
+  for (int r = 0; r < kPfPer; ++r) {
+    const int64_t j = tid + (int64_t)r * kPfThreads;
+    tv[r] = j < ntv ? tmr[j] : -INFINITY;
+  }
+  float m2;
+  double qf, sw;
+  bound_terms(qt, wt, parts + (size_t)b * n_parts, n_parts, tid, kPfThreads, &m2, &qf, &sw);
+  for (int i = tid; i < 256; i += kPfThreads) { sh.sel.hist[i] = 0u; sh.sel.bmin[i] = 0xFFFFFFFFu; }
+  if (tid == 0) { sh.n_out = 0; sh.n_band = 0; }
+  float lmax = -INFINITY, lmin = INFINITY;
+#pragma unroll
+  for (int r = 0; r < kPfPer; ++r) {
+    lmax = fmaxf(lmax, tv[r]);
+    lmin = fminf(lmin, tv[r] > -INFINITY ? tv[r] : INFINITY);
+  }
+  // one block reduction: bound terms, value range, smallest per-thread maximum,
+  // threads holding a tile (every visible tile's maximum is finite)
+  m2 = wave_max_dpp(m2);
+  qf = wave_sum_groups8_f64(qf);
+  sw = wave_sum_groups8_f64(sw);
+  const float wmax = wave_max_dpp(lmax);
+  const float wmin = wave_min_dpp(lmin);
+  const float wl0 = wave_min_dpp(lmax > -INFINITY ? lmax : INFINITY);
+  const uint32_t wthr = (uint32_t)__popcll(__ballot(lmax > -INFINITY));
+  if (lane == 0) {
+    L.fr[0][wave] = m2; L.fr[1][wave] = wmax; L.fr[2][wave] = wmin; L.fr[3][wave] = wl0;
+    L.dr[0][wave] = qf; L.dr[1][wave] = sw;
+    L.wsum[wave] = wthr;
   }
   __syncthreads();
-  float eps;
-  {
-    float m2 = L.bm[0];
-    double qf = L.bq[0], sw = L.bs[0];
-    for (int i = 1; i < kPfThreads / 64; ++i) { m2 = fmaxf(m2, L.bm[i]); qf += L.bq[i]; sw += L.bs[i]; }
-    eps = bound_eps(m2, qf, sw);
-    if (tid == 0) stats[(size_t)t * CSA2_STATS_WORDS] = __float_as_uint(eps);
+  m2 = L.fr[0][0];
+  float mx = L.fr[1][0], gmin = L.fr[2][0], l0 = L.fr[3][0];
+  qf = L.dr[0][0];
+  sw = L.dr[1][0];
+  uint32_t tthr = L.wsum[0];
+  for (int i = 1; i < kPfThreads / 64; ++i) {
+    m2 = fmaxf(m2, L.fr[0][i]); mx = fmaxf(mx, L.fr[1][i]); gmin = fminf(gmin, L.fr[2][i]);
+    l0 = fminf(l0, L.fr[3][i]);
+    qf += L.dr[0][i]; sw += L.dr[1][i]; tthr += L.wsum[i];
   }
+  const float eps = bound_eps(m2, qf, sw);
+  if (tid == 0) stats[(size_t)t * CSA2_STATS_WORDS] = __float_as_uint(eps);
   if (nv <= k) {
     for (int i = tid; i < k; i += kPfThreads) out[i] = i < nv ? i : -1;
     return;
   }
-  // 1. the floor from the tile maxima (all tiles kept when there are too few)
+  // 2. the floor tau from the tile maxima, which are distinct visible entries'
+  // scores: at least k of them are >= tau.  When k threads hold a tile, their
+  // k maxima reach the smallest per-thread maximum l0, so the k-th largest tile
+  // maximum is >= l0 and only values >= l0 enter a 256-bin histogram over
+  // [l0, max] that keeps each bin's minimum; the bins at and above the one
+  // holding the k-th largest hold at least k values, and tau is the smallest of
+  // them.  (All tiles are kept when there are at most k.)
   double thr = -INFINITY;
   if (ntv > k) {
-    float tau, tau_hi;
-    bracket_kth(sh.sel, ntv, kk, [&](int64_t i) { return L.u.c.tm[i]; }, &tau, &tau_hi);
+    const float lo = tthr >= kk ? l0 : gmin;
+    const float scale = mx > lo ? 255.99f / (mx - lo) : 0.f;
+#pragma unroll
+    for (int r = 0; r < kPfPer; ++r) {
+      if (tv[r] >= lo) {
+        const uint32_t bin = value_bin(tv[r], lo, scale);
+        atomicAdd(&sh.sel.hist[bin], 1u);
+        atomicMin(&sh.sel.bmin[bin], f32_key(tv[r]));
+      }
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane owns bins 255-4*lane .. 252-4*lane (descending); the bins at or
+      // above the one holding the k-th largest are those whose exclusive
+      // count from the top is below k
+      uint32_t c[4], sum = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { c[i] = sh.sel.hist[255 - 4 * lane - i]; sum += c[i]; }
+      uint32_t incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t x = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += x;
+      }
+      uint32_t cum = incl - sum, kmin = 0xFFFFFFFFu;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (cum < kk) kmin = min(kmin, sh.sel.bmin[255 - 4 * lane - i]);
+        cum += c[i];
+      }
+      kmin = wave_min_u32_dpp(kmin);
+      if (lane == 0) L.res = kmin;
+    }
+    __syncthreads();
+    const float tau = key_f32(L.res);
     thr = cand_threshold(tau, eps, bsel);
     if (!(thr <= (double)tau)) thr = -INFINITY;  // eps not finite: keep everything
   }
-  // 2. the entries of the tiles that reach it, compacted (any order: every later
-  // step ranks by value and index)
-  for (int64_t j = tid; j < ntv; j += kPfThreads) {
-    if (!((double)L.u.c.tm[j] >= thr)) continue;
-    const float4* p = reinterpret_cast<const float4*>(row + j * kTileKeys);
-    float4 v4[4];
+  // 3. the tiles that reach it, listed in tile order; then their entries that
+  // reach it, compacted (two tiles per thread and round, both loads issued
+  // together; the list's order is immaterial: every later step ranks by value
+  // and index)
+  uint32_t n_t;
+  {
+    uint32_t ct = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v4[u] = p[u];
-    const float vs[16] = {v4[0].x, v4[0].y, v4[0].z, v4[0].w, v4[1].x, v4[1].y, v4[1].z, v4[1].w,
-                          v4[2].x, v4[2].y, v4[2].z, v4[2].w, v4[3].x, v4[3].y, v4[3].z, v4[3].w};
+    for (int r = 0; r < kPfPer; ++r) ct += ((double)tv[r] >= thr && tid + (int64_t)r * kPfThreads < ntv) ? 1u : 0u;
+    uint32_t off = block_excl_scan(ct, L.wsum, &n_t);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int64_t s = j * kTileKeys + e;
-      if (s < nv && (double)vs[e] >= thr) {
-        const uint32_t pos = atomicAdd(&L.n_c, 1u);
-        if (pos < (uint32_t)kPfMax) { L.u.c.v[pos] = vs[e]; L.u.c.i[pos] = (uint32_t)s; }
+    for (int r = 0; r < kPfPer; ++r) {
+      const int64_t j = tid + (int64_t)r * kPfThreads;
+      if ((double)tv[r] >= thr && j < ntv) L.u.c.tiles[off++] = (uint16_t)j;
+    }
+    __syncthreads();
+  }
+  uint32_t n = 0;
+  for (uint32_t p0 = 0; p0 < n_t; p0 += 2 * kPfThreads) {
+    float vs[2][16];
+    int64_t s0[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t p = p0 + h * kPfThreads + tid;
+      s0[h] = p < n_t ? (int64_t)L.u.c.tiles[p] * kTileKeys : -1;
+      if (s0[h] >= 0) {
+        const float4* q4 = reinterpret_cast<const float4*>(row + s0[h]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float4 x = q4[u];
+          vs[h][4 * u] = x.x; vs[h][4 * u + 1] = x.y; vs[h][4 * u + 2] = x.z; vs[h][4 * u + 3] = x.w;
+        }
       }
     }
+    uint32_t c = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) c += (s0[h] >= 0 && s0[h] + e < nv && (double)vs[h][e] >= thr) ? 1u : 0u;
+    uint32_t tot;
+    uint32_t pos = n + block_excl_scan(c, L.wsum, &tot);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (s0[h] >= 0 && s0[h] + e < nv && (double)vs[h][e] >= thr) {
+          if (pos < (uint32_t)kPfMax) { L.u.c.v[pos] = vs[h][e]; L.u.c.i[pos] = (uint32_t)(s0[h] + e); }
+          ++pos;
+        }
+    n += tot;
   }
   __syncthreads();
-  const uint32_t n = L.n_c;
   if (n > (uint32_t)kPfMax) {  // too many to hold: exact streaming pass over the row
-    __syncthreads();
     finish_streaming(sh, kk, row, nv, thr, INFINITY, qt, wt, kb, bsel);
-    write_sorted(sh, tl, kk, k, out);
+    write_sorted_bits(sh, tl, kk, k, nv, L.wsum, out);
     return;
   }
-  // 3. the full-row selection over the list
+  // 4. the full-row selection over the list
   float t_lo, t_hi;
   bracket_kth(sh.sel, n, kk, [&](int64_t i) { return L.u.c.v[i]; }, &t_lo, &t_hi);
   double lo, hi;
@@ -756,7 +942,7 @@ __global__ __launch_bounds__(kPfThreads) void topk_rows_pf_kernel(
   __syncthreads();
   if (fast) finish_band(sh, tl, kk, qt, wt, kb, bsel);
   else finish_streaming(sh, kk, row, nv, lo, hi, qt, wt, kb, bsel);
-  write_sorted(sh, tl, kk, k, out);
+  write_sorted_bits(sh, tl, kk, k, nv, L.wsum, out);
 }
 
 // ------------------------------------------------------------ tile regime
@@ -782,47 +968,6 @@ __device__ __forceinline__ TileWs tile_ws(void* base, int T, int64_t N, int64_t 
   w.cscore = (double*)((char*)base + tile_ws_fixed(T, N));
   w.cidx = (uint32_t*)(w.cscore + (size_t)T * cap);
   return w;
-}
-
-// Block-wide exclusive prefix sum (all threads, blockDim.x a multiple of 64).
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  __syncthreads();
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  uint32_t off = 0, tot = 0;
-  for (int i = 0; i < nw; ++i) {
-    const uint32_t c = wsum[i];
-    off += i < wave ? c : 0u;
-    tot += c;
-  }
-  *total = tot;
-  return off + x - v;
-}
-
-// Position of this thread's flag among the block's set flags (ascending
-// thread order) and their total: one ballot per wave and one barrier.
-// `wsum` (one word per wave) must not be read by a previous call any more.
-__device__ __forceinline__ uint32_t block_flag_scan(bool flag, uint32_t* wsum, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const uint64_t b = __ballot(flag);
-  const uint32_t below = (uint32_t)__popcll(b & ((1ull << lane) - 1ull));
-  if (lane == 0) wsum[wave] = (uint32_t)__popcll(b);
-  __syncthreads();
-  uint32_t off = 0, tot = 0;
-  for (int i = 0; i < nw; ++i) {
-    const uint32_t c = wsum[i];
-    off += i < wave ? c : 0u;
-    tot += c;
-  }
-  *total = tot;
-  return off + below;
 }
 
 // ---- eps and the floor tau: one block per query
