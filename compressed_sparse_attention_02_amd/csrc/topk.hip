@@ -111,6 +111,16 @@ __device__ __forceinline__ double cand_threshold(float tau, float eps, int bsel)
   return next_down(bf16_lower_mid(bf16_round_f64(lb)) - (double)eps);
 }
 
+// The scan's norm partials [B][groups][blocks_x] of query t's group (groups of
+// qg queries of one sequence): their maximum bounds ||K||^2 over every key
+// that a query of the group sees, t's among them.
+__device__ __forceinline__ const float* group_parts(const float* parts, int t, int q_per_seq, int qg,
+                                                    int64_t blocks_x) {
+  const int b = t / q_per_seq, z = (t % q_per_seq) / qg;
+  const int groups = (q_per_seq + qg - 1) / qg;
+  return parts + ((size_t)b * groups + z) * blocks_x;
+}
+
 // eps_t = 2^-14 * sum_h |w_h| ||q_h||_2 * max_s ||K_s||_2 + 2^-100 (1 + sum_h |w_h|), rounded up.
 //
 // Derivation: the bf16 products are exact in fp32; four chained MFMA steps
@@ -256,7 +266,8 @@ struct alignas(16) SelLds {
   uint32_t hist[256];
   uint32_t bmin[256];
   uint32_t pick[3];
-  float red[2][kFinThreads / 64];
+  float red[3][kFinThreads / 64];
+  uint32_t cnt[kFinThreads / 64];
 };
 
 // Block min / max (all threads; returns the same pair everywhere).
@@ -289,23 +300,46 @@ __device__ __forceinline__ void for_each4(int64_t n, Get get, F f) {
 }
 
 // Bracket lo <= T <= hi of T = the rank-th largest (1-based) of the n values
-// get(i), rank < n.  Thread j's values are get(j), get(j + blockDim), ...;
-// the per-thread maxima are distinct values, so the rank-th largest of them,
-// L, has at least rank values >= L and T >= L (with n > rank every thread
-// up to rank holds a value when blockDim >= rank).  L comes from a 256-bin
-// histogram of the per-thread maxima that keeps each bin's minimum; then two
-// levels of 256 value bins over [L, max], counting only values >= L, narrow T
-// to one bin; lo and hi are the smallest and largest values in it.  The value
-// histograms thus see a few times rank values, not n.  All threads call this.
+// get(i), of which at least rank are finite (the others are -inf).  Thread j's
+// values are get(j), get(j + blockDim), ...; when at least rank threads hold
+// a finite value, their maxima are distinct values, so the rank-th largest of
+// them, L, has at least rank values >= L and T >= L; otherwise L is the
+// smallest finite value.  L comes from a 256-bin histogram of the per-thread
+// maxima that keeps each bin's minimum; then two levels of 256 value bins
+// over [L, max], counting only values >= L, narrow T to one bin; lo and hi are
+// the smallest and largest values in it.  The value histograms thus see a few
+// times rank values, not n.  All threads call this.
 template <typename Get>
 __device__ void bracket_kth(SelLds& s, int64_t n, uint32_t rank, Get get, float* lo, float* hi) {
   const float inf = INFINITY;
-  float tmax = -inf, mx = -inf;
-  for_each4(n, get, [&](float v) { tmax = fmaxf(tmax, v); });
-  // 1. L from the per-thread maxima
-  float2 r = block_minmax(s, tmax > -inf ? tmax : inf, tmax);
-  mx = r.y;
+  float tmax = -inf, tmin = inf, mx = -inf;
+  for_each4(n, get, [&](float v) { tmax = fmaxf(tmax, v); tmin = fminf(tmin, v > -inf ? v : inf); });
+  // one reduction: smallest finite per-thread maximum, maximum, smallest
+  // finite value, threads holding a finite value
+  float2 r;
+  float gmin;
+  uint32_t nthr;
   {
+    const float a = -wave_max(-(tmax > -inf ? tmax : inf)), b = wave_max(tmax), c = -wave_max(-tmin);
+    const uint32_t nt = (uint32_t)__popcll(__ballot(tmax > -inf));
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) { s.red[0][w] = a; s.red[1][w] = b; s.red[2][w] = c; s.cnt[w] = nt; }
+    __syncthreads();
+    r = make_float2(s.red[0][0], s.red[1][0]);
+    gmin = s.red[2][0];
+    nthr = s.cnt[0];
+    for (int i = 1; i < nw; ++i) {
+      r.x = fminf(r.x, s.red[0][i]); r.y = fmaxf(r.y, s.red[1][i]); gmin = fminf(gmin, s.red[2][i]);
+      nthr += s.cnt[i];
+    }
+  }
+  mx = r.y;
+  if (nthr < rank) {  // too few per-thread maxima: start from the smallest value
+    if (threadIdx.x == 0) s.pick[2] = f32_key(gmin);
+    __syncthreads();
+  } else {
+    // 1. L from the per-thread maxima
     const float a0 = r.x, s0 = r.y > r.x ? 255.99f / (r.y - r.x) : 0.f;
     for (int i = threadIdx.x; i < 256; i += blockDim.x) { s.hist[i] = 0; s.bmin[i] = 0xFFFFFFFFu; }
     __syncthreads();
@@ -361,70 +395,110 @@ __device__ void bracket_kth(SelLds& s, int64_t n, uint32_t rank, Get get, float*
 
 // --------------------------------------------------------- finish (shared)
 
-// LDS of the finishing block.  FinLds::tail is only touched after the
-// candidates have been classified, so the small regime overlays it on its
-// copy of the scores.
-struct alignas(16) FinTail {
+// LDS of the finishing block, for a band of up to BAND entries resolved in
+// LDS and KROWS key rows staged per rescoring round.  The tail is only
+// touched after the candidates have been classified, so the row kernels
+// overlay it on their copy of the scores or their candidate list.
+template <int BAND, int KROWS>
+struct alignas(16) FinTailT {
+  static constexpr int kKRows = KROWS;
   uint32_t out_sorted[kTopK];
-  uint64_t band_key[kBandLds];
-  uint16_t krows[64][kIdxDim];
-  uint16_t qrows[kIdxHeads][kIdxDim + 8];
+  uint64_t band_key[BAND];
+  uint16_t krows[KROWS][kIdxDim];
+  uint16_t qrows[kIdxHeads][kIdxDim + 8];  // directly after krows (the output bitmap spans both)
   double dots[32][kIdxHeads + 1];
+  float w[kIdxHeads];
 };
-struct alignas(16) FinLds {
+template <int BAND>
+struct alignas(16) FinLdsT {
+  static constexpr int kBand = BAND;
   SelLds sel;
   uint32_t n_out, n_band;
   uint32_t out[kTopK];
-  uint32_t band_idx[kBandLds];
+  uint32_t band_idx[BAND];
 };
+using FinTail = FinTailT<kBandLds, 64>;
+using FinLds = FinLdsT<kBandLds>;
 
-// fp64 scores of the band (reference operation order): thread (e = tid/32,
-// h = tid%32) forms dot(q[h], K[e]) with 128 sequential fmas from LDS, then
-// one thread per entry folds the heads in order (blockDim / 32 entries per
-// pass, blockDim a multiple of 256).
-template <class Keys>
-__device__ void rescore_band(FinLds& sh, FinTail& tl, uint32_t nb, const uint16_t* __restrict__ qt,
+// fp64 scores of the band (reference operation order), 32 entries per pass:
+// thread (e = tid/32, h = tid%32) of an NT-thread block forms dot(q[h], K[x])
+// for entries x = e, e + NT/32, ... of the pass (32 / (NT/32) independent
+// chains of 128 sequential fmas from LDS), then thread x < 32 folds entry x's
+// heads in order.  The query rows, the weights and the first key rows are
+// requested together, and each round's key rows are requested while the
+// previous round is scored.
+template <int NT, class FL, class FT, class Keys>
+__device__ void rescore_band(FL& sh, FT& tl, uint32_t nb, const uint16_t* __restrict__ qt,
                              const float* __restrict__ wt, const Keys& kb, int bsel) {
-  const int tid = threadIdx.x, nt = (int)blockDim.x;
-  const uint32_t ep = (uint32_t)nt >> 5;
+  constexpr int KR = FT::kKRows;                       // key rows per round
+  constexpr int EP = NT / 32;                          // entries per chain round
+  constexpr int C = 32 / EP;                           // chains per thread
+  constexpr int QP = (kIdxHeads * 16 + NT - 1) / NT;   // 16-byte query pieces per thread
+  constexpr int KP = (KR * 16 + NT - 1) / NT;          // 16-byte key pieces per thread and round
+  static_assert(NT % 32 == 0 && 32 % EP == 0 && C >= 1 && KR % 32 == 0, "32 entries per pass");
+  const int tid = threadIdx.x;
   const int e = tid >> 5, h = tid & 31;
-  for (int i = tid; i < kIdxHeads * 16; i += nt) {
-    const int r = i >> 4, c = i & 15;
-    *reinterpret_cast<uint4*>(&tl.qrows[r][8 * c]) = *reinterpret_cast<const uint4*>(qt + r * kIdxDim + 8 * c);
+  uint4 kv[KP];
+  auto load_rows = [&](uint32_t base) {
+#pragma unroll
+    for (int u = 0; u < KP; ++u) {
+      const int i = tid + u * NT, r = i >> 4, c = i & 15;
+      kv[u] = (i < KR * 16 && base + r < nb) ? kb.piece(sh.band_idx[base + r], c) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  load_rows(0);
+  {
+    uint4 qv[QP];
+#pragma unroll
+    for (int u = 0; u < QP; ++u) {
+      const int i = tid + u * NT;
+      if (i < kIdxHeads * 16) qv[u] = *reinterpret_cast<const uint4*>(qt + (i >> 4) * kIdxDim + 8 * (i & 15));
+    }
+    const float wv = tid < kIdxHeads ? wt[tid] : 0.f;
+#pragma unroll
+    for (int u = 0; u < QP; ++u) {
+      const int i = tid + u * NT;
+      if (i < kIdxHeads * 16) *reinterpret_cast<uint4*>(&tl.qrows[i >> 4][8 * (i & 15)]) = qv[u];
+    }
+    if (tid < kIdxHeads) tl.w[tid] = wv;
   }
-  for (uint32_t base = 0; base < nb; base += 64) {
-    // 64 key rows x 256 B, 16-byte chunks
-    for (int i = tid; i < 64 * 16; i += nt) {
-      const int r = i >> 4, c = i & 15;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (base + r < nb) v = kb.piece(sh.band_idx[base + r], c);
-      *reinterpret_cast<uint4*>(&tl.krows[r][8 * c]) = v;
+  for (uint32_t base = 0; base < nb; base += KR) {
+#pragma unroll
+    for (int u = 0; u < KP; ++u) {
+      const int i = tid + u * NT;
+      if (i < KR * 16) *reinterpret_cast<uint4*>(&tl.krows[i >> 4][8 * (i & 15)]) = kv[u];
     }
     __syncthreads();
-    for (uint32_t half = 0; half < 64 && base + half < nb; half += ep) {
-      if (base + half + e < nb) {
-        double d = 0.0;
+    if (base + KR < nb) load_rows(base + KR);
+    for (uint32_t half = 0; half < (uint32_t)KR && base + half < nb; half += 32) {
+      double d[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) d[c] = 0.0;
 #pragma unroll 4
-        for (int i = 0; i < 16; ++i) {
-          const uint4 kq = *reinterpret_cast<const uint4*>(&tl.krows[half + e][8 * i]);
-          const uint4 qq = *reinterpret_cast<const uint4*>(&tl.qrows[h][8 * i]);
-          const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
+      for (int i = 0; i < 16; ++i) {
+        const uint4 qq = *reinterpret_cast<const uint4*>(&tl.qrows[h][8 * i]);
+        const uint32_t qw[4] = {qq.x, qq.y, qq.z, qq.w};
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          const uint4 kq = *reinterpret_cast<const uint4*>(&tl.krows[half + e + c * EP][8 * i]);
           const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            d = fma((double)bf16lo(qw[p]), (double)bf16lo(kw[p]), d);
-            d = fma((double)bf16hi(qw[p]), (double)bf16hi(kw[p]), d);
+            d[c] = fma((double)bf16lo(qw[p]), (double)bf16lo(kw[p]), d[c]);
+            d[c] = fma((double)bf16hi(qw[p]), (double)bf16hi(kw[p]), d[c]);
           }
         }
-        tl.dots[e][h] = d;
       }
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        if (base + half + e + c * EP < nb) tl.dots[e + c * EP][h] = d[c];
       __syncthreads();
-      if ((uint32_t)tid < ep && base + half + tid < nb) {
+      if (tid < 32 && base + half + tid < nb) {
         double sc = 0.0;
 #pragma unroll 8
         for (int hh = 0; hh < kIdxHeads; ++hh) {
-          const double d = tl.dots[tid][hh];
-          sc = fma((double)wt[hh], d > 0.0 ? d : 0.0, sc);
+          const double dd = tl.dots[tid][hh];
+          sc = fma((double)tl.w[hh], dd > 0.0 ? dd : 0.0, sc);
         }
         tl.band_key[base + half + tid] = f64_key(sel_value(sc, bsel));
       }
@@ -434,12 +508,12 @@ __device__ void rescore_band(FinLds& sh, FinTail& tl, uint32_t nb, const uint16_
 }
 
 // Complete the selection once T^ is known and the sure entries and band are
-// in sh.out / sh.band_idx (n_band <= kBandLds): rescore and pick the band's share.
-template <class Keys>
-__device__ void finish_band(FinLds& sh, FinTail& tl, uint32_t kk, const uint16_t* qt, const float* wt,
+// in sh.out / sh.band_idx (n_band <= FL::kBand): rescore and pick the band's share.
+template <int NT, class FL, class FT, class Keys>
+__device__ void finish_band(FL& sh, FT& tl, uint32_t kk, const uint16_t* qt, const float* wt,
                             const Keys& kb, int bsel) {
   const uint32_t nb = sh.n_band;
-  rescore_band(sh, tl, nb, qt, wt, kb, bsel);
+  rescore_band<NT>(sh, tl, nb, qt, wt, kb, bsel);
   const uint32_t r = kk - sh.n_out;
   const uint32_t base_out = sh.n_out;
   for (uint32_t i = threadIdx.x; i < nb; i += blockDim.x) {
@@ -459,8 +533,8 @@ __device__ void finish_band(FinLds& sh, FinTail& tl, uint32_t kk, const uint16_t
 // Exact streaming fallback over the whole visible row (capacity overflow).
 // Gathers sure entries, then radix-selects the band's share over the 96-bit
 // composite (fp64 key, ~index), recomputing each band member's fp64 score.
-template <class Keys>
-__device__ void finish_streaming(FinLds& sh, uint32_t kk, const float* row, int64_t nv, double lo, double hi,
+template <class FL, class Keys>
+__device__ void finish_streaming(FL& sh, uint32_t kk, const float* row, int64_t nv, double lo, double hi,
                                  const uint16_t* qt, const float* wt, const Keys& kb, int bsel) {
   const int tid = threadIdx.x;
   if (tid == 0) sh.n_out = 0;
@@ -506,7 +580,8 @@ __device__ void finish_streaming(FinLds& sh, uint32_t kk, const float* row, int6
 }
 
 // Ascending output (indices are distinct): rank by comparison, 4 per LDS read.
-__device__ void write_sorted(FinLds& sh, FinTail& tl, uint32_t kk, int k, int32_t* out) {
+template <class FL, class FT>
+__device__ void write_sorted(FL& sh, FT& tl, uint32_t kk, int k, int32_t* out) {
   for (uint32_t i = kk + threadIdx.x; i < kTopK; i += (int)blockDim.x) sh.out[i] = 0xFFFFFFFFu;
   __syncthreads();
   for (uint32_t i = threadIdx.x; i < kk; i += (int)blockDim.x) {
@@ -569,9 +644,12 @@ __device__ __forceinline__ uint32_t block_flag_scan(bool flag, uint32_t* wsum, u
 // then), word popcounts prefix-summed over the block, and each index stored
 // at its rank.  `wsum`: one word per wave for the block scan.
 constexpr int kBitWords = (kSmallMax + 31) / 32;
-__device__ void write_sorted_bits(FinLds& sh, FinTail& tl, uint32_t kk, int k, int64_t nv, uint32_t* wsum,
+template <class FL, class FT>
+__device__ void write_sorted_bits(FL& sh, FT& tl, uint32_t kk, int k, int64_t nv, uint32_t* wsum,
                                   int32_t* out) {
-  static_assert(2 * kBitWords * sizeof(uint32_t) <= sizeof(tl.krows), "bitmap and prefix fit the key rows");
+  static_assert(offsetof(FT, qrows) == offsetof(FT, krows) + sizeof(tl.krows) &&
+                    2 * kBitWords * sizeof(uint32_t) <= sizeof(tl.krows) + sizeof(tl.qrows),
+                "bitmap and prefix fit the key and query rows");
   uint32_t* bits = reinterpret_cast<uint32_t*>(&tl.krows[0][0]);
   uint32_t* pre = bits + kBitWords;
   const int tid = threadIdx.x, bd = (int)blockDim.x;
@@ -637,7 +715,7 @@ struct SmallLds {
 template <class Keys>
 __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
     const float* __restrict__ scores, uint32_t* __restrict__ stats, const float* __restrict__ parts,
-    int64_t n_parts, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, Keys keys,
+    int64_t n_parts, int qg, const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, Keys keys,
     const int32_t* __restrict__ q_pos, int ratio, int q_per_seq, int64_t N, int k, int32_t* __restrict__ indices,
     int bsel) {
   __shared__ SmallLds L;
@@ -673,7 +751,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
   {
     float m2;
     double qf, sw;
-    bound_terms(qt, wt, parts + (size_t)b * n_parts, n_parts, tid, kFinThreads, &m2, &qf, &sw);
+    bound_terms(qt, wt, group_parts(parts, t, q_per_seq, qg, n_parts), n_parts, tid, kFinThreads, &m2, &qf, &sw);
     m2 = wave_max_dpp(m2);
     qf = wave_sum_groups8_f64(qf);
     sw = wave_sum_groups8_f64(sw);
@@ -707,7 +785,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
   __syncthreads();
   const bool fast = sh.n_band <= kBandLds;
   __syncthreads();
-  if (fast) finish_band(sh, tl, kk, qt, wt, kb, bsel);
+  if (fast) finish_band<kFinThreads>(sh, tl, kk, qt, wt, kb, bsel);
   else finish_streaming(sh, kk, row, nv, lo, hi, qt, wt, kb, bsel);
   write_sorted(sh, tl, kk, k, out);
 }
@@ -726,37 +804,73 @@ __global__ __launch_bounds__(kFinThreads) void topk_small_kernel(
 // could pick and the result is the same.  More than kPfMax listed entries
 // (planted ties) go to the exact streaming pass over the row.
 
-constexpr int kPfMax = 6144;                                        // listed entries held in LDS
-constexpr int kPfThreads = 512;                                     // two blocks per CU
+#ifndef CSA2_PF_THREADS
+#define CSA2_PF_THREADS 256
+#endif
+constexpr int kPfThreads = CSA2_PF_THREADS;                         // four blocks per CU (256)
+constexpr int kPfMax = 2048;                                        // listed entries held in LDS
+constexpr int kPfBand = 512;                                        // band entries resolved in LDS
 constexpr int kPfTiles = (kSmallMax + kTileKeys - 1) / kTileKeys;  // tile maxima of a row
-constexpr int kPfPer = (kPfTiles + kPfThreads - 1) / kPfThreads;   // tile maxima per thread
 static_assert(kPfTiles <= 65536, "tile ids are listed as 16-bit values");
 
-struct PfLds {
-  FinLds f;
+template <int NT>
+struct PfLdsT {
+  static constexpr int kPer = (kPfTiles + NT - 1) / NT;  // tile maxima per thread
+  FinLdsT<kPfBand> f;
   union {
     struct {
       float v[kPfMax];
       uint32_t i[kPfMax];
       uint16_t tiles[kPfTiles];  // the tiles that reach the floor
     } c;
-    FinTail tail;
+    FinTailT<kPfBand, 32> tail;
   } u;
-  float fr[4][kPfThreads / 64];
-  double dr[2][kPfThreads / 64];
-  uint32_t wsum[kPfThreads / 64];
+  float fr[4][NT / 64];
+  double dr[2][NT / 64];
+  uint32_t wsum[NT / 64];
   uint32_t res;
 };
 
-template <class Keys>
-__global__ __launch_bounds__(kPfThreads) void topk_rows_pf_kernel(
+// Steps 4-6 of the row selection over n listed values getv(i) (entry geti(i);
+// at least k of them finite): bracket the k-th, split sure entries from the
+// band, rescore the band (or stream the row when the band overflows) and
+// write the ordered result.
+template <int NT, class Lds, class Keys, class GetV, class GetI>
+__device__ __forceinline__ void pf_finish(Lds& L, int64_t n, GetV getv, GetI geti, uint32_t kk, int k, float eps,
+                          const float* row, int64_t nv, const uint16_t* qt, const float* wt, const Keys& kb,
+                          int bsel, int32_t* out) {
+  auto& sh = L.f;
+  auto& tl = L.u.tail;
+  float t_lo, t_hi;
+  bracket_kth(sh.sel, n, kk, getv, &t_lo, &t_hi);
+  double lo, hi;
+  band_bounds(t_lo, t_hi, eps, bsel, &lo, &hi);
+  for (int64_t i = threadIdx.x; i < n; i += NT) {
+    const double v = (double)getv(i);
+    if (v > hi) sh.out[atomicAdd(&sh.n_out, 1u)] = geti(i);
+    else if (v >= lo) {
+      const uint32_t p = atomicAdd(&sh.n_band, 1u);
+      if (p < (uint32_t)kPfBand) sh.band_idx[p] = geti(i);
+    }
+  }
+  __syncthreads();
+  const bool fast = sh.n_band <= (uint32_t)kPfBand;
+  __syncthreads();
+  if (fast) finish_band<NT>(sh, tl, kk, qt, wt, kb, bsel);
+  else finish_streaming(sh, kk, row, nv, lo, hi, qt, wt, kb, bsel);
+  write_sorted_bits(sh, tl, kk, k, nv, L.wsum, out);
+}
+
+template <int NT, class Keys>
+__global__ __launch_bounds__(NT) void topk_rows_pf_kernel(
     const float* __restrict__ scores, const float* __restrict__ tile_max, uint32_t* __restrict__ stats,
-    const float* __restrict__ parts, int64_t n_parts, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ parts, int64_t n_parts, int qg, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w_idx, Keys keys, const int32_t* __restrict__ q_pos, int ratio, int q_per_seq,
     int64_t N, int k, int32_t* __restrict__ indices, int bsel) {
-  __shared__ PfLds L;
-  FinLds& sh = L.f;
-  FinTail& tl = L.u.tail;
+  using Lds = PfLdsT<NT>;
+  constexpr int kPer = Lds::kPer;
+  __shared__ Lds L;
+  auto& sh = L.f;
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t nv = n_visible(q_pos, t, ratio, N);
@@ -768,23 +882,23 @@ __global__ __launch_bounds__(kPfThreads) void topk_rows_pf_kernel(
   const Keys kb = keys.seq(b, N);
   const float* row = scores + (size_t)t * N;
   const int64_t ntv = (nv + kTileKeys - 1) / kTileKeys;
-  // 1. this thread's tile maxima (tiles tid, tid + kPfThreads, ...) and the bound
+  // 1. this thread's tile maxima (tiles tid, tid + NT, ...) and the bound
   // terms, every load issued before any is used
-  float tv[kPfPer];
+  float tv[kPer];
   const float* tmr = tile_max + (size_t)t * tile_ld(N);
 #pragma unroll
-  for (int r = 0; r < kPfPer; ++r) {
-    const int64_t j = tid + (int64_t)r * kPfThreads;
+  for (int r = 0; r < kPer; ++r) {
+    const int64_t j = tid + (int64_t)r * NT;
     tv[r] = j < ntv ? tmr[j] : -INFINITY;
   }
   float m2;
   double qf, sw;
-  bound_terms(qt, wt, parts + (size_t)b * n_parts, n_parts, tid, kPfThreads, &m2, &qf, &sw);
-  for (int i = tid; i < 256; i += kPfThreads) { sh.sel.hist[i] = 0u; sh.sel.bmin[i] = 0xFFFFFFFFu; }
+  bound_terms(qt, wt, group_parts(parts, t, q_per_seq, qg, n_parts), n_parts, tid, NT, &m2, &qf, &sw);
+  for (int i = tid; i < 256; i += NT) { sh.sel.hist[i] = 0u; sh.sel.bmin[i] = 0xFFFFFFFFu; }
   if (tid == 0) { sh.n_out = 0; sh.n_band = 0; }
   float lmax = -INFINITY, lmin = INFINITY;
 #pragma unroll
-  for (int r = 0; r < kPfPer; ++r) {
+  for (int r = 0; r < kPer; ++r) {
     lmax = fmaxf(lmax, tv[r]);
     lmin = fminf(lmin, tv[r] > -INFINITY ? tv[r] : INFINITY);
   }
@@ -808,7 +922,7 @@ __global__ __launch_bounds__(kPfThreads) void topk_rows_pf_kernel(
   qf = L.dr[0][0];
   sw = L.dr[1][0];
   uint32_t tthr = L.wsum[0];
-  for (int i = 1; i < kPfThreads / 64; ++i) {
+  for (int i = 1; i < NT / 64; ++i) {
     m2 = fmaxf(m2, L.fr[0][i]); mx = fmaxf(mx, L.fr[1][i]); gmin = fminf(gmin, L.fr[2][i]);
     l0 = fminf(l0, L.fr[3][i]);
     qf += L.dr[0][i]; sw += L.dr[1][i]; tthr += L.wsum[i];
@@ -816,22 +930,23 @@ __global__ __launch_bounds__(kPfThreads) void topk_rows_pf_kernel(
   const float eps = bound_eps(m2, qf, sw);
   if (tid == 0) stats[(size_t)t * CSA2_STATS_WORDS] = __float_as_uint(eps);
   if (nv <= k) {
-    for (int i = tid; i < k; i += kPfThreads) out[i] = i < nv ? i : -1;
+    for (int i = tid; i < k; i += NT) out[i] = i < nv ? i : -1;
     return;
   }
   // 2. the floor tau from the tile maxima, which are distinct visible entries'
   // scores: at least k of them are >= tau.  When k threads hold a tile, their
   // k maxima reach the smallest per-thread maximum l0, so the k-th largest tile
-  // maximum is >= l0 and only values >= l0 enter a 256-bin histogram over
-  // [l0, max] that keeps each bin's minimum; the bins at and above the one
-  // holding the k-th largest hold at least k values, and tau is the smallest of
-  // them.  (All tiles are kept when there are at most k.)
+  // maximum is >= l0; otherwise it is >= the smallest maximum.  Only values >=
+  // that enter a 256-bin histogram over [it, max] that keeps each bin's
+  // minimum; the bins at and above the one holding the k-th largest hold at
+  // least k values, and tau is the smallest of them.  (All tiles are kept when
+  // there are at most k.)
   double thr = -INFINITY;
   if (ntv > k) {
     const float lo = tthr >= kk ? l0 : gmin;
     const float scale = mx > lo ? 255.99f / (mx - lo) : 0.f;
 #pragma unroll
-    for (int r = 0; r < kPfPer; ++r) {
+    for (int r = 0; r < kPer; ++r) {
       if (tv[r] >= lo) {
         const uint32_t bin = value_bin(tv[r], lo, scale);
         atomicAdd(&sh.sel.hist[bin], 1u);
@@ -867,29 +982,30 @@ __global__ __launch_bounds__(kPfThreads) void topk_rows_pf_kernel(
     if (!(thr <= (double)tau)) thr = -INFINITY;  // eps not finite: keep everything
   }
   // 3. the tiles that reach it, listed in tile order; then their entries that
-  // reach it, compacted (two tiles per thread and round, both loads issued
+  // reach it, compacted (512 tiles per round, a thread's loads issued
   // together; the list's order is immaterial: every later step ranks by value
   // and index)
   uint32_t n_t;
   {
     uint32_t ct = 0;
 #pragma unroll
-    for (int r = 0; r < kPfPer; ++r) ct += ((double)tv[r] >= thr && tid + (int64_t)r * kPfThreads < ntv) ? 1u : 0u;
+    for (int r = 0; r < kPer; ++r) ct += ((double)tv[r] >= thr && tid + (int64_t)r * NT < ntv) ? 1u : 0u;
     uint32_t off = block_excl_scan(ct, L.wsum, &n_t);
 #pragma unroll
-    for (int r = 0; r < kPfPer; ++r) {
-      const int64_t j = tid + (int64_t)r * kPfThreads;
+    for (int r = 0; r < kPer; ++r) {
+      const int64_t j = tid + (int64_t)r * NT;
       if ((double)tv[r] >= thr && j < ntv) L.u.c.tiles[off++] = (uint16_t)j;
     }
     __syncthreads();
   }
+  constexpr int TR = NT >= 512 ? 1 : 512 / NT;  // tiles per thread and round
   uint32_t n = 0;
-  for (uint32_t p0 = 0; p0 < n_t; p0 += 2 * kPfThreads) {
-    float vs[2][16];
-    int64_t s0[2];
+  for (uint32_t p0 = 0; p0 < n_t; p0 += TR * NT) {
+    float vs[TR][16];
+    int64_t s0[TR];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t p = p0 + h * kPfThreads + tid;
+    for (int h = 0; h < TR; ++h) {
+      const uint32_t p = p0 + h * NT + tid;
       s0[h] = p < n_t ? (int64_t)L.u.c.tiles[p] * kTileKeys : -1;
       if (s0[h] >= 0) {
         const float4* q4 = reinterpret_cast<const float4*>(row + s0[h]);
@@ -902,13 +1018,13 @@ __global__ __launch_bounds__(kPfThreads) void topk_rows_pf_kernel(
     }
     uint32_t c = 0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < TR; ++h)
 #pragma unroll
       for (int e = 0; e < 16; ++e) c += (s0[h] >= 0 && s0[h] + e < nv && (double)vs[h][e] >= thr) ? 1u : 0u;
     uint32_t tot;
     uint32_t pos = n + block_excl_scan(c, L.wsum, &tot);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < TR; ++h)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         if (s0[h] >= 0 && s0[h] + e < nv && (double)vs[h][e] >= thr) {
@@ -918,31 +1034,18 @@ __global__ __launch_bounds__(kPfThreads) void topk_rows_pf_kernel(
     n += tot;
   }
   __syncthreads();
-  if (n > (uint32_t)kPfMax) {  // too many to hold: exact streaming pass over the row
-    finish_streaming(sh, kk, row, nv, thr, INFINITY, qt, wt, kb, bsel);
-    write_sorted_bits(sh, tl, kk, k, nv, L.wsum, out);
-    return;
-  }
-  // 4. the full-row selection over the list
-  float t_lo, t_hi;
-  bracket_kth(sh.sel, n, kk, [&](int64_t i) { return L.u.c.v[i]; }, &t_lo, &t_hi);
-  double lo, hi;
-  band_bounds(t_lo, t_hi, eps, bsel, &lo, &hi);
-  for (uint32_t i = tid; i < n; i += kPfThreads) {
-    const double v = (double)L.u.c.v[i];
-    const uint32_t idx = L.u.c.i[i];
-    if (v > hi) sh.out[atomicAdd(&sh.n_out, 1u)] = idx;
-    else if (v >= lo) {
-      const uint32_t p = atomicAdd(&sh.n_band, 1u);
-      if (p < kBandLds) sh.band_idx[p] = idx;
-    }
-  }
-  __syncthreads();
-  const bool fast = sh.n_band <= kBandLds;
-  __syncthreads();
-  if (fast) finish_band(sh, tl, kk, qt, wt, kb, bsel);
-  else finish_streaming(sh, kk, row, nv, lo, hi, qt, wt, kb, bsel);
-  write_sorted_bits(sh, tl, kk, k, nv, L.wsum, out);
+  // 4-6. the full-row selection over the list, or, when it is too long to
+  // hold (short rows keep every entry), over the row itself with the entries
+  // below the floor counting as -inf
+  const bool listed = n <= (uint32_t)kPfMax;
+  pf_finish<NT>(
+      L, listed ? (int64_t)n : nv,
+      [&](int64_t i) {
+        if (listed) return L.u.c.v[i];
+        const float v = row[i];
+        return (double)v >= thr ? v : -INFINITY;
+      },
+      [&](int64_t i) { return listed ? L.u.c.i[i] : (uint32_t)i; }, kk, k, eps, row, nv, qt, wt, kb, bsel, out);
 }
 
 // ------------------------------------------------------------ tile regime
@@ -1007,7 +1110,7 @@ struct alignas(16) FloorLds {
 // `rank` values, and tau is the smallest of them.
 __global__ __launch_bounds__(kFloorThreads) void topk_floor_kernel(
     const float* __restrict__ tile_max, uint32_t* __restrict__ stats, const float* __restrict__ gmax,
-    int64_t n_groups, const float* __restrict__ parts, int64_t n_parts, const uint16_t* __restrict__ q_idx,
+    int64_t n_groups, const float* __restrict__ parts, int64_t n_parts, int qg, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w_idx, const int32_t* __restrict__ q_pos, int ratio, int q_per_seq, int64_t N,
     int rank, int64_t all_below) {
   __shared__ FloorLds F;
@@ -1034,7 +1137,7 @@ __global__ __launch_bounds__(kFloorThreads) void topk_floor_kernel(
   float m2;
   double qf, sw;
   bound_terms(q_idx + (size_t)t * kIdxHeads * kIdxDim, w_idx + (size_t)t * kIdxHeads,
-              parts + (size_t)(t / q_per_seq) * n_parts, n_parts, tid, kFloorThreads, &m2, &qf, &sw);
+              group_parts(parts, t, q_per_seq, qg, n_parts), n_parts, tid, kFloorThreads, &m2, &qf, &sw);
   // folding: one level of kFloorVals values at a time, each level's loads issued together
   for (int64_t lvl = kFloorVals; lvl < nsrc; lvl += kFloorVals) {
     float4 x[kFloorPer / 4];
@@ -2367,7 +2470,8 @@ struct Summary {
   const float* gmax;
   int64_t n_groups;
   const float* parts;
-  int64_t n_parts;
+  int64_t n_parts;  // norm partials per query group (the scan's blocks_x)
+  int qg;           // queries per group
   const uint16_t* q;
 };
 
@@ -2378,7 +2482,8 @@ static bool summary_bf16(const uint32_t* stats, size_t stats_bytes, const void* 
   sm->gmax = (const float*)(stats + stats_groups_off(T));
   sm->n_groups = p.n_groups;
   sm->parts = (const float*)(stats + stats_parts_off(T, p.n_groups));
-  sm->n_parts = p.parts();
+  sm->n_parts = p.blocks_x;
+  sm->qg = p.qg;
   sm->q = (const uint16_t*)q_idx;
   return true;
 }
@@ -2390,7 +2495,8 @@ static bool summary_mx(const uint32_t* stats, size_t stats_bytes, int32_t T, int
   sm->gmax = (const float*)(stats + (size_t)T * CSA2_STATS_WORDS);
   sm->n_groups = p.n_groups;
   sm->parts = sm->gmax + (size_t)T * p.n_groups;
-  sm->n_parts = p.parts();
+  sm->n_parts = p.blocks_x;
+  sm->qg = p.qg;
   sm->q = (const uint16_t*)(stats + mx_qdeq_off(T, p));
   return true;
 }
@@ -2403,11 +2509,11 @@ static csa2_status topk_launch(const float* scores, const float* tile_max, uint3
   (void)hipGetLastError();
   if (topk_row_regime(scores, N)) {
     if (tile_max)
-      hipLaunchKernelGGL(topk_rows_pf_kernel<Keys>, dim3(T), dim3(kPfThreads), 0, st, scores, tile_max, stats,
-                         sm.parts, sm.n_parts, sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, k, indices, bsel);
+      hipLaunchKernelGGL((topk_rows_pf_kernel<kPfThreads, Keys>), dim3(T), dim3(kPfThreads), 0, st, scores, tile_max, stats,
+                         sm.parts, sm.n_parts, sm.qg, sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, k, indices, bsel);
     else
       hipLaunchKernelGGL(topk_small_kernel<Keys>, dim3(T), dim3(kFinThreads), 0, st, scores, stats, sm.parts,
-                         sm.n_parts, sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, k, indices, bsel);
+                         sm.n_parts, sm.qg, sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, k, indices, bsel);
     if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
     return CSA2_OK;
   }
@@ -2419,7 +2525,7 @@ static csa2_status topk_launch(const float* scores, const float* tile_max, uint3
   if (!topk_layout(workspace_bytes, T, N, &slots, &cap)) return CSA2_ERR_WORKSPACE;
   const int64_t nblk = cand_blocks(N);
   hipLaunchKernelGGL(topk_floor_kernel, dim3(T), dim3(kFloorThreads), 0, st, tile_max, stats, sm.gmax, sm.n_groups,
-                     sm.parts, sm.n_parts, sm.q, w_idx, q_pos, ratio, q_per_seq, N, kTopK, (int64_t)kTopK);
+                     sm.parts, sm.n_parts, sm.qg, sm.q, w_idx, q_pos, ratio, q_per_seq, N, kTopK, (int64_t)kTopK);
   hipLaunchKernelGGL(topk_cand_kernel<Keys>, dim3((unsigned)nblk, T), dim3(kCandThreads), 0, st, scores, tile_max,
                      stats, sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, k, workspace, T, cap, slots, bsel);
   hipLaunchKernelGGL(topk_select_kernel<Keys>, dim3(T), dim3(kSelThreads), 0, st, tile_max, stats, sm.q, w_idx, keys,
@@ -2502,7 +2608,7 @@ static csa2_status hsi_launch(const float* tile_max, const Summary& sm, const fl
   (void)hipGetLastError();
   uint32_t* hdr = (uint32_t*)workspace;  // HsiWs::hdr is at the start of the workspace
   hipLaunchKernelGGL(topk_floor_kernel, dim3(T), dim3(kFloorThreads), 0, st, tile_max, hdr, sm.gmax, sm.n_groups,
-                     sm.parts, sm.n_parts, sm.q, w_idx, q_pos, ratio, q_per_seq, N, kHsiBlocks, (int64_t)kHsiPool);
+                     sm.parts, sm.n_parts, sm.qg, sm.q, w_idx, q_pos, ratio, q_per_seq, N, kHsiBlocks, (int64_t)kHsiPool);
   hipLaunchKernelGGL(hsi_cand_kernel<Keys>, dim3((unsigned)cand_blocks(N), T), dim3(kCandThreads), 0, st, tile_max,
                      sm.q, w_idx, keys, q_pos, ratio, q_per_seq, N, workspace, T);
   hipLaunchKernelGGL(hsi_select_kernel, dim3(T), dim3(kHsiSelThreads), 0, st, q_pos, ratio, N, workspace, T, pool);

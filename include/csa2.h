@@ -95,7 +95,7 @@ const char* csa2_version(void);
  *            words are a header per query that the scan sets to zero and
  *            csa2_topk fills (see there); the rest (maxima of disjoint groups
  *            of each query's entries, partial maxima of ||K_s||^2 per
- *            sequence) has no documented layout.
+ *            group of queries of a sequence) has no documented layout.
  *  stats_bytes  size of stats; smaller than csa2_index_stats_bytes -> INVALID_ARG
  * The call is one kernel and uses no workspace.
  * Requires T >= 1, q_per_seq >= 1, T % q_per_seq == 0, 1 <= N < 2^31

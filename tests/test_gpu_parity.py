@@ -25,6 +25,7 @@ SMALL = {
     "qps3": dict(B=2, N=777, q_per_seq=3),
     "qps5_ratio2": dict(B=1, N=2501, q_per_seq=5, ratio=2),
     "prefill_small": dict(B=1, N=998, q_per_seq=96, ratio=2, prefix=1900),
+    "mid_rows": dict(B=2, N=20000),        # row regime with a finite floor (more than 512 tiles)
     "large_rows": dict(B=2, N=40000),
     "large_rows_ragged": dict(B=2, N=40001),
     "large_qps3": dict(B=2, N=40003, q_per_seq=3),
@@ -143,12 +144,14 @@ def test_topk_streaming_fallback_matches():
 
 
 @pytest.mark.parametrize("path", ["rows", "tiles", "tiles_scores"])
-@pytest.mark.parametrize("mode", ["all_equal", "all_equal_overflow", "all_equal_large", "tie_block", "tie_block_large"])
+@pytest.mark.parametrize("mode", ["all_equal", "all_equal_overflow", "all_equal_mid", "all_equal_large", "tie_block",
+                                  "tie_block_mid", "tie_block_large"])
 def test_topk_planted_ties(mode, path):
     if path == "tiles_scores" and not mode.endswith("_large"):
         pytest.skip("rows within CSA2_TOPK_ROW_MAX: a score matrix selects in the row regime (path rows)")
     log(f"[topk] ties {mode} ({path})")
-    N = {"all_equal_overflow": 3000, "all_equal_large": 40000, "tie_block_large": 40000}.get(mode, 2048)
+    N = {"all_equal_overflow": 3000, "all_equal_mid": 20000, "all_equal_large": 40000, "tie_block_mid": 20000,
+         "tie_block_large": 40000}.get(mode, 2048)
     c = G.make_case("ties", B=1, N=N, seed=5, device=DEV, with_kv=False)
     if mode.startswith("all_equal"):
         c.k_idx[:] = c.k_idx[0, 7]                       # every key identical: lowest 512 indices win
