@@ -15,6 +15,12 @@
 
 namespace csa2 {
 
+// The selection over the scanned pools (topk.hip).
+csa2_status reindex_select_launch(const float* scores, const uint32_t* stats, size_t stats_bytes,
+                                  const void* q_bf16, const float* w_idx, const uint16_t* keys,
+                                  const int32_t* last_pos, const int32_t* pool, int32_t T, int32_t k,
+                                  int32_t* indices, hipStream_t st);
+
 constexpr int kPool = CSA2_HSI_POOL;
 constexpr int kGatherThreads = 256;
 constexpr int kGatherRows = 64;                          // pool rows per block
@@ -27,7 +33,6 @@ struct ReindexWs {
   float* scores;     // [T][kPool]
   float* tile_max;   // [T][tile_ld]
   uint32_t* stats;   // csa2_index summary for (T, 1, kPool)
-  int32_t* pos;      // [T][k] selected pool positions
   size_t stats_bytes;
 };
 
@@ -46,7 +51,6 @@ static ReindexWs reindex_ws(void* base, int T, int k, size_t* total) {
   w.tile_max = (float*)take((size_t)T * (size_t)csa2_tile_max_ld(kPool) * 4);
   w.stats_bytes = csa2_index_stats_bytes(T, 1, kPool);
   w.stats = (uint32_t*)take(w.stats_bytes);
-  w.pos = (int32_t*)take((size_t)T * k * 4);
   *total = off;
   return w;
 }
@@ -108,17 +112,6 @@ __global__ __launch_bounds__(kGatherThreads) void reindex_gather_kernel(const in
   }
 }
 
-// indices[t][j] = pool[t][pos[t][j]] (-1 stays -1).
-__global__ __launch_bounds__(256) void reindex_map_kernel(const int32_t* __restrict__ pool,
-                                                          const int32_t* __restrict__ pos, int k,
-                                                          int32_t* __restrict__ indices) {
-  const int t = blockIdx.x;
-  for (int j = threadIdx.x; j < k; j += blockDim.x) {
-    const int32_t p = pos[(size_t)t * k + j];
-    indices[(size_t)t * k + j] = p >= 0 ? pool[(size_t)t * kPool + p] : -1;
-  }
-}
-
 }  // namespace csa2
 
 using namespace csa2;
@@ -131,18 +124,15 @@ extern "C" size_t csa2_reindex_workspace_bytes(int32_t T, int32_t k) {
 }
 
 // The gathered pool keys as a batch of T one-query "sequences" of kPool keys:
-// the regular scan and row-regime selection, then positions -> entry ids.
+// the regular scan, then the selection within each pool, which writes the
+// selected positions' entry ids.
 static csa2_status reindex_finish(const ReindexWs& w, const void* q_bf16, const float* w_idx, const int32_t* pool,
                                   int32_t T, int32_t k, int32_t* indices, void* hip_stream) {
   csa2_status s = csa2_index(q_bf16, w_idx, w.keys, w.qpos, 1, T, 1, kPool, w.scores, w.tile_max, w.stats,
                              w.stats_bytes, hip_stream);
   if (s != CSA2_OK) return s;
-  s = csa2_topk(w.scores, w.tile_max, w.stats, w.stats_bytes, q_bf16, w_idx, w.keys, w.qpos, 1, T, 1, kPool, k,
-                w.pos, nullptr, 0, hip_stream);
-  if (s != CSA2_OK) return s;
-  hipLaunchKernelGGL(reindex_map_kernel, dim3(T), dim3(256), 0, (hipStream_t)hip_stream, pool, w.pos, k, indices);
-  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
-  return CSA2_OK;
+  return reindex_select_launch(w.scores, w.stats, w.stats_bytes, q_bf16, w_idx, w.keys, w.qpos, pool, T, k, indices,
+                               (hipStream_t)hip_stream);
 }
 
 extern "C" csa2_status csa2_reindex(const int32_t* pool, const void* q_idx, const float* w_idx, const void* k_idx,

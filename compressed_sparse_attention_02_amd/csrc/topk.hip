@@ -309,11 +309,12 @@ __device__ __forceinline__ void for_each4(int64_t n, Get get, F f) {
 // over [L, max], counting only values >= L, narrow T to one bin; lo and hi are
 // the smallest and largest values in it.  The value histograms thus see a few
 // times rank values, not n.  All threads call this.
-template <typename Get>
-__device__ void bracket_kth(SelLds& s, int64_t n, uint32_t rank, Get get, float* lo, float* hi) {
+// visit(f) calls f(v) for each of the calling thread's values.
+template <typename Visit>
+__device__ void bracket_visit(SelLds& s, uint32_t rank, Visit visit, float* lo, float* hi) {
   const float inf = INFINITY;
   float tmax = -inf, tmin = inf, mx = -inf;
-  for_each4(n, get, [&](float v) { tmax = fmaxf(tmax, v); tmin = fminf(tmin, v > -inf ? v : inf); });
+  visit([&](float v) { tmax = fmaxf(tmax, v); tmin = fminf(tmin, v > -inf ? v : inf); });
   // one reduction: smallest finite per-thread maximum, maximum, smallest
   // finite value, threads holding a finite value
   float2 r;
@@ -364,13 +365,13 @@ __device__ void bracket_kth(SelLds& s, int64_t n, uint32_t rank, Get get, float*
   const float a1 = L, s1 = mx > L ? 255.99f / (mx - L) : 0.f;
   for (int i = threadIdx.x; i < 256; i += blockDim.x) s.hist[i] = 0;
   __syncthreads();
-  for_each4(n, get, [&](float v) { if (v >= L) atomicAdd(&s.hist[value_bin(v, a1, s1)], 1u); });
+  visit([&](float v) { if (v >= L) atomicAdd(&s.hist[value_bin(v, a1, s1)], 1u); });
   pick_digit(s.hist, rank, s.pick);
   const uint32_t b1 = s.pick[0];
   rank = s.pick[1];
   float mn = inf;
   mx = -inf;
-  for_each4(n, get, [&](float v) {
+  visit([&](float v) {
     if (v >= L && value_bin(v, a1, s1) == b1) { mn = fminf(mn, v); mx = fmaxf(mx, v); }
   });
   r = block_minmax(s, mn, mx);
@@ -378,19 +379,73 @@ __device__ void bracket_kth(SelLds& s, int64_t n, uint32_t rank, Get get, float*
   const float a2 = r.x, s2 = r.y > r.x ? 255.99f / (r.y - r.x) : 0.f;
   for (int i = threadIdx.x; i < 256; i += blockDim.x) s.hist[i] = 0;
   __syncthreads();
-  for_each4(n, get, [&](float v) {
+  visit([&](float v) {
     if (v >= L && value_bin(v, a1, s1) == b1) atomicAdd(&s.hist[value_bin(v, a2, s2)], 1u);
   });
   pick_digit(s.hist, rank, s.pick);
   const uint32_t b2 = s.pick[0];
   mn = inf;
   mx = -inf;
-  for_each4(n, get, [&](float v) {
+  visit([&](float v) {
     if (v >= L && value_bin(v, a1, s1) == b1 && value_bin(v, a2, s2) == b2) { mn = fminf(mn, v); mx = fmaxf(mx, v); }
   });
   r = block_minmax(s, mn, mx);
   *lo = r.x;
   *hi = r.y;
+}
+
+template <typename Get>
+__device__ void bracket_kth(SelLds& s, int64_t n, uint32_t rank, Get get, float* lo, float* hi) {
+  bracket_visit(s, rank, [&](auto f) { for_each4(n, get, f); }, lo, hi);
+}
+
+// Order-preserving key of the rank-th largest (1-based) of n values get(i)
+// (finite or -inf, at least rank finite), by one wave and no block barrier:
+// four passes over 8-bit digits of the keys, each counting the values that
+// match the digits found so far in a 256-bin LDS histogram (`hist`, which no
+// other wave touches meanwhile) and picking the digit that holds the rank-th.
+// All 64 lanes of the calling wave call this; every lane gets the key.
+template <typename Get>
+__device__ uint32_t wave_kth_key(int64_t n, uint32_t rank, Get get, uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0u, mask = 0u;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = lane; i < 256; i += 64) hist[i] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    for (int64_t i = lane; i < n; i += 64) {
+      const uint32_t key = f32_key(get(i));
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // lane owns digits 255-4*lane .. 252-4*lane (descending)
+    uint32_t c[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { c[i] = hist[255 - 4 * lane - i]; sum += c[i]; }
+    uint32_t incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t x = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += x;
+    }
+    uint32_t cum = incl - sum, digit = 0u, left = 0u;
+    bool mine = false;
+    if (cum < rank && rank <= incl) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!mine && cum + c[i] >= rank) { digit = 255u - 4u * lane - i; left = rank - cum; mine = true; }
+        cum += c[i];
+      }
+    }
+    const uint64_t who = __ballot(mine);
+    const int src = __ffsll((unsigned long long)who) - 1;
+    digit = __shfl(digit, src, 64);
+    rank = __shfl(left, src, 64);
+    prefix |= digit << shift;
+    mask |= 255u << shift;
+  }
+  return prefix;
 }
 
 // --------------------------------------------------------- finish (shared)
@@ -639,14 +694,29 @@ __device__ __forceinline__ uint32_t block_flag_scan(bool flag, uint32_t* wsum, u
   return off + below;
 }
 
+// Slot of this lane's item in an LDS array appended to through `counter`: one
+// atomic add per wave for the wave's set flags (ascending lane order within
+// the wave).  Every lane of the wave calls this; the result is meaningful
+// only where flag is set.
+__device__ __forceinline__ uint32_t wave_append(bool flag, uint32_t* counter) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t b = __ballot(flag);
+  if (b == 0ull) return 0u;
+  const int leader = __ffsll((unsigned long long)b) - 1;
+  uint32_t base = 0u;
+  if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(b));
+  base = __shfl(base, leader, 64);
+  return base + (uint32_t)__popcll(b & ((1ull << lane) - 1ull));
+}
+
 // Ascending output for rows of at most kSmallMax entries: a bitmap of the
-// selected indices in LDS (over the finishing tail's key-row staging, free by
-// then), word popcounts prefix-summed over the block, and each index stored
-// at its rank.  `wsum`: one word per wave for the block scan.
+// selected indices in LDS (over the finishing tail's key and query rows, free
+// by then), word popcounts prefix-summed over the block, and map(index)
+// stored at the index's rank.  `wsum`: one word per wave for the block scan.
 constexpr int kBitWords = (kSmallMax + 31) / 32;
-template <class FL, class FT>
+template <class FL, class FT, class Map>
 __device__ void write_sorted_bits(FL& sh, FT& tl, uint32_t kk, int k, int64_t nv, uint32_t* wsum,
-                                  int32_t* out) {
+                                  int32_t* out, Map map) {
   static_assert(offsetof(FT, qrows) == offsetof(FT, krows) + sizeof(tl.krows) &&
                     2 * kBitWords * sizeof(uint32_t) <= sizeof(tl.krows) + sizeof(tl.qrows),
                 "bitmap and prefix fit the key and query rows");
@@ -674,7 +744,7 @@ __device__ void write_sorted_bits(FL& sh, FT& tl, uint32_t kk, int k, int64_t nv
   __syncthreads();
   for (uint32_t i = tid; i < kk; i += bd) {
     const uint32_t v = sh.out[i];
-    out[pre[v >> 5] + (uint32_t)__popc(bits[v >> 5] & ((1u << (v & 31u)) - 1u))] = (int32_t)v;
+    out[pre[v >> 5] + (uint32_t)__popc(bits[v >> 5] & ((1u << (v & 31u)) - 1u))] = map(v);
   }
   for (int i = (int)kk + tid; i < k; i += bd) out[i] = -1;
 }
@@ -835,30 +905,90 @@ struct PfLdsT {
 // at least k of them finite): bracket the k-th, split sure entries from the
 // band, rescore the band (or stream the row when the band overflows) and
 // write the ordered result.
-template <int NT, class Lds, class Keys, class GetV, class GetI>
+template <int NT, class Lds, class Keys, class GetV, class GetI, class Map>
 __device__ __forceinline__ void pf_finish(Lds& L, int64_t n, GetV getv, GetI geti, uint32_t kk, int k, float eps,
-                          const float* row, int64_t nv, const uint16_t* qt, const float* wt, const Keys& kb,
-                          int bsel, int32_t* out) {
+                                          const float* row, int64_t nv, const uint16_t* qt, const float* wt,
+                                          const Keys& kb, int bsel, int32_t* out, Map map) {
   auto& sh = L.f;
   auto& tl = L.u.tail;
   float t_lo, t_hi;
-  bracket_kth(sh.sel, n, kk, getv, &t_lo, &t_hi);
+  if (n <= kPfMax) {  // a list in LDS: the exact k-th by one wave
+    if (threadIdx.x < 64) {
+      const uint32_t key = wave_kth_key(n, kk, getv, sh.sel.hist);
+      if (threadIdx.x == 0) sh.sel.pick[2] = key;
+    }
+    __syncthreads();
+    t_lo = t_hi = key_f32(sh.sel.pick[2]);
+  } else {
+    bracket_kth(sh.sel, n, kk, getv, &t_lo, &t_hi);
+  }
   double lo, hi;
   band_bounds(t_lo, t_hi, eps, bsel, &lo, &hi);
-  for (int64_t i = threadIdx.x; i < n; i += NT) {
-    const double v = (double)getv(i);
-    if (v > hi) sh.out[atomicAdd(&sh.n_out, 1u)] = geti(i);
-    else if (v >= lo) {
-      const uint32_t p = atomicAdd(&sh.n_band, 1u);
-      if (p < (uint32_t)kPfBand) sh.band_idx[p] = geti(i);
-    }
+  for (int64_t i0 = 0; i0 < n; i0 += NT) {  // every lane takes every round (wave appends)
+    const int64_t i = i0 + threadIdx.x;
+    const double v = i < n ? (double)getv(i) : -INFINITY;
+    const bool sure = v > hi, band = !sure && v >= lo;
+    const uint32_t ps = wave_append(sure, &sh.n_out);
+    const uint32_t pb = wave_append(band, &sh.n_band);
+    if (sure) sh.out[ps] = geti(i);
+    if (band && pb < (uint32_t)kPfBand) sh.band_idx[pb] = geti(i);
   }
   __syncthreads();
   const bool fast = sh.n_band <= (uint32_t)kPfBand;
   __syncthreads();
   if (fast) finish_band<NT>(sh, tl, kk, qt, wt, kb, bsel);
   else finish_streaming(sh, kk, row, nv, lo, hi, qt, wt, kb, bsel);
-  write_sorted_bits(sh, tl, kk, k, nv, L.wsum, out);
+  write_sorted_bits(sh, tl, kk, k, nv, L.wsum, out, map);
+}
+
+// The floor tau over PER values per thread (distinct entries' scores, -inf
+// where absent; the block's finite count is above k): at least k values are
+// >= tau.  When k threads hold a value their k maxima reach the smallest
+// per-thread maximum l0, so the k-th largest is >= l0; otherwise it is >= the
+// smallest value gmin.  Values at or above that bound enter a 256-bin
+// histogram over [bound, mx] that keeps each bin's minimum; the bins at and
+// above the one holding the k-th largest hold at least k values, and tau is
+// the smallest of them.  hist / bmin start zeroed / all ones; all threads call
+// this; `res` is one LDS word.
+template <int PER>
+__device__ float floor_of_values(SelLds& sel, const float (&tv)[PER], uint32_t kk, uint32_t tthr, float l0,
+                                 float gmin, float mx, uint32_t* res) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const float lo = tthr >= kk ? l0 : gmin;
+  const float scale = mx > lo ? 255.99f / (mx - lo) : 0.f;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    if (tv[r] >= lo) {
+      const uint32_t bin = value_bin(tv[r], lo, scale);
+      atomicAdd(&sel.hist[bin], 1u);
+      atomicMin(&sel.bmin[bin], f32_key(tv[r]));
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // lane owns bins 255-4*lane .. 252-4*lane (descending); the bins at or
+    // above the one holding the k-th largest are those whose exclusive
+    // count from the top is below k
+    uint32_t c[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { c[i] = sel.hist[255 - 4 * lane - i]; sum += c[i]; }
+    uint32_t incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t x = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += x;
+    }
+    uint32_t cum = incl - sum, kmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (cum < kk) kmin = min(kmin, sel.bmin[255 - 4 * lane - i]);
+      cum += c[i];
+    }
+    kmin = wave_min_u32_dpp(kmin);
+    if (lane == 0) *res = kmin;
+  }
+  __syncthreads();
+  return key_f32(*res);
 }
 
 template <int NT, class Keys>
@@ -934,50 +1064,10 @@ __global__ __launch_bounds__(NT) void topk_rows_pf_kernel(
     return;
   }
   // 2. the floor tau from the tile maxima, which are distinct visible entries'
-  // scores: at least k of them are >= tau.  When k threads hold a tile, their
-  // k maxima reach the smallest per-thread maximum l0, so the k-th largest tile
-  // maximum is >= l0; otherwise it is >= the smallest maximum.  Only values >=
-  // that enter a 256-bin histogram over [it, max] that keeps each bin's
-  // minimum; the bins at and above the one holding the k-th largest hold at
-  // least k values, and tau is the smallest of them.  (All tiles are kept when
-  // there are at most k.)
+  // scores (all tiles are kept when there are at most k)
   double thr = -INFINITY;
   if (ntv > k) {
-    const float lo = tthr >= kk ? l0 : gmin;
-    const float scale = mx > lo ? 255.99f / (mx - lo) : 0.f;
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-      if (tv[r] >= lo) {
-        const uint32_t bin = value_bin(tv[r], lo, scale);
-        atomicAdd(&sh.sel.hist[bin], 1u);
-        atomicMin(&sh.sel.bmin[bin], f32_key(tv[r]));
-      }
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // lane owns bins 255-4*lane .. 252-4*lane (descending); the bins at or
-      // above the one holding the k-th largest are those whose exclusive
-      // count from the top is below k
-      uint32_t c[4], sum = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { c[i] = sh.sel.hist[255 - 4 * lane - i]; sum += c[i]; }
-      uint32_t incl = sum;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t x = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += x;
-      }
-      uint32_t cum = incl - sum, kmin = 0xFFFFFFFFu;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (cum < kk) kmin = min(kmin, sh.sel.bmin[255 - 4 * lane - i]);
-        cum += c[i];
-      }
-      kmin = wave_min_u32_dpp(kmin);
-      if (lane == 0) L.res = kmin;
-    }
-    __syncthreads();
-    const float tau = key_f32(L.res);
+    const float tau = floor_of_values<kPer>(sh.sel, tv, kk, tthr, l0, gmin, mx, &L.res);
     thr = cand_threshold(tau, eps, bsel);
     if (!(thr <= (double)tau)) thr = -INFINITY;  // eps not finite: keep everything
   }
@@ -1045,7 +1135,118 @@ __global__ __launch_bounds__(NT) void topk_rows_pf_kernel(
         const float v = row[i];
         return (double)v >= thr ? v : -INFINITY;
       },
-      [&](int64_t i) { return listed ? L.u.c.i[i] : (uint32_t)i; }, kk, k, eps, row, nv, qt, wt, kb, bsel, out);
+      [&](int64_t i) { return listed ? L.u.c.i[i] : (uint32_t)i; }, kk, k, eps, row, nv, qt, wt, kb, bsel, out,
+      [](uint32_t i) { return (int32_t)i; });
+}
+
+// ------------------------------------------------------ Reindex selection
+
+// Top-k within one Reindex query's candidate pool (report sec. 2.3.2), one
+// block per query over the scan of its gathered pool keys: the pool's P fp32
+// scores sit in registers (P / kRxThreads per thread), the k-th is bracketed
+// from them directly, the band is rescored in fp64 from the gathered keys (the
+// pool rows' own bf16 values), and the selected pool positions are written as
+// the entry ids they hold, ascending (the pool is ascending, so position order
+// is entry order and the lower-index tie rule carries over).  Positions past
+// the pool's entry count are pad and never selected.
+constexpr int kRxThreads = 1024;
+constexpr int kRxPer = CSA2_HSI_POOL / kRxThreads;
+static_assert(CSA2_HSI_POOL % kRxThreads == 0 && CSA2_HSI_POOL <= kSmallMax, "pool positions fit the bitmap");
+
+__global__ __launch_bounds__(kRxThreads) void reindex_select_kernel(
+    const float* __restrict__ scores, const float* __restrict__ parts, int64_t n_parts,
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, const uint16_t* __restrict__ keys,
+    const int32_t* __restrict__ last_pos, const int32_t* __restrict__ pool, int k, int32_t* __restrict__ indices) {
+  using Lds = PfLdsT<kRxThreads>;
+  __shared__ Lds L;
+  auto& sh = L.f;
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nv = (int64_t)last_pos[t] + 1;  // pool entries; the rest is pad
+  const uint32_t kk = (uint32_t)k;
+  const uint16_t* qt = q_idx + (size_t)t * kIdxHeads * kIdxDim;
+  const float* wt = w_idx + (size_t)t * kIdxHeads;
+  const Bf16Keys kb = Bf16Keys{keys}.seq(t, CSA2_HSI_POOL);
+  const float* row = scores + (size_t)t * CSA2_HSI_POOL;
+  const int32_t* pl = pool + (size_t)t * CSA2_HSI_POOL;
+  int32_t* out = indices + (size_t)t * k;
+  // the pool's scores (positions tid, tid + kRxThreads, ...) and the bound
+  // terms, every load issued before any is used
+  float v[kRxPer];
+#pragma unroll
+  for (int r = 0; r < kRxPer; ++r) {
+    const int64_t i = tid + (int64_t)r * kRxThreads;
+    v[r] = i < nv ? row[i] : -INFINITY;
+  }
+  float m2;
+  double qf, sw;
+  bound_terms(qt, wt, parts + (size_t)t * n_parts, n_parts, tid, kRxThreads, &m2, &qf, &sw);
+  for (int i = tid; i < 256; i += kRxThreads) { sh.sel.hist[i] = 0u; sh.sel.bmin[i] = 0xFFFFFFFFu; }
+  if (tid == 0) { sh.n_out = 0; sh.n_band = 0; }
+  float lmax = -INFINITY, lmin = INFINITY;
+#pragma unroll
+  for (int r = 0; r < kRxPer; ++r) {
+    lmax = fmaxf(lmax, v[r]);
+    lmin = fminf(lmin, v[r] > -INFINITY ? v[r] : INFINITY);
+  }
+  m2 = wave_max_dpp(m2);
+  qf = wave_sum_groups8_f64(qf);
+  sw = wave_sum_groups8_f64(sw);
+  const float wmax = wave_max_dpp(lmax);
+  const float wmin = wave_min_dpp(lmin);
+  const float wl0 = wave_min_dpp(lmax > -INFINITY ? lmax : INFINITY);
+  const uint32_t wthr = (uint32_t)__popcll(__ballot(lmax > -INFINITY));
+  if (lane == 0) {
+    L.fr[0][wave] = m2; L.fr[1][wave] = wmax; L.fr[2][wave] = wmin; L.fr[3][wave] = wl0;
+    L.dr[0][wave] = qf; L.dr[1][wave] = sw;
+    L.wsum[wave] = wthr;
+  }
+  __syncthreads();
+  m2 = L.fr[0][0];
+  float mx = L.fr[1][0], gmin = L.fr[2][0], l0 = L.fr[3][0];
+  qf = L.dr[0][0];
+  sw = L.dr[1][0];
+  uint32_t tthr = L.wsum[0];
+  for (int i = 1; i < kRxThreads / 64; ++i) {
+    m2 = fmaxf(m2, L.fr[0][i]); mx = fmaxf(mx, L.fr[1][i]); gmin = fminf(gmin, L.fr[2][i]);
+    l0 = fminf(l0, L.fr[3][i]);
+    qf += L.dr[0][i]; sw += L.dr[1][i]; tthr += L.wsum[i];
+  }
+  const float eps = bound_eps(m2, qf, sw);
+  if (nv <= k) {
+    for (int i = tid; i < k; i += kRxThreads) out[i] = i < nv ? pl[i] : -1;
+    return;
+  }
+  // the floor from the per-thread maxima (distinct entries' scores), then the
+  // entries that reach it listed through one block scan
+  const float pm[1] = {lmax};
+  const float tau = floor_of_values<1>(sh.sel, pm, kk, tthr, l0, gmin, mx, &L.res);
+  double thr = cand_threshold(tau, eps, 0);
+  if (!(thr <= (double)tau)) thr = -INFINITY;  // eps not finite: keep everything
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int r = 0; r < kRxPer; ++r) cnt += (tid + (int64_t)r * kRxThreads < nv && (double)v[r] >= thr) ? 1u : 0u;
+  uint32_t n;
+  uint32_t pos = block_excl_scan(cnt, L.wsum, &n);
+#pragma unroll
+  for (int r = 0; r < kRxPer; ++r) {
+    const uint32_t i = tid + r * kRxThreads;
+    if ((int64_t)i < nv && (double)v[r] >= thr) {
+      if (pos < (uint32_t)kPfMax) { L.u.c.v[pos] = v[r]; L.u.c.i[pos] = i; }
+      ++pos;
+    }
+  }
+  __syncthreads();
+  const bool listed = n <= (uint32_t)kPfMax;
+  pf_finish<kRxThreads>(
+      L, listed ? (int64_t)n : nv,
+      [&](int64_t i) {
+        if (listed) return L.u.c.v[i];
+        const float x = row[i];
+        return (double)x >= thr ? x : -INFINITY;
+      },
+      [&](int64_t i) { return listed ? L.u.c.i[i] : (uint32_t)i; }, kk, k, eps, row, nv, qt, wt, kb, 0, out,
+      [&](uint32_t i) { return pl[i]; });
 }
 
 // ------------------------------------------------------------ tile regime
@@ -2500,6 +2701,25 @@ static bool summary_mx(const uint32_t* stats, size_t stats_bytes, int32_t T, int
   sm->q = (const uint16_t*)(stats + mx_qdeq_off(T, p));
   return true;
 }
+
+namespace csa2 {
+
+// The Reindex selection over the scan of a batch of gathered pools (one
+// one-query "sequence" of CSA2_HSI_POOL keys per query; stats is that scan's
+// summary).  Used by csa2_reindex.
+csa2_status reindex_select_launch(const float* scores, const uint32_t* stats, size_t stats_bytes,
+                                  const void* q_bf16, const float* w_idx, const uint16_t* keys,
+                                  const int32_t* last_pos, const int32_t* pool, int32_t T, int32_t k,
+                                  int32_t* indices, hipStream_t st) {
+  Summary sm;
+  if (!summary_bf16(stats, stats_bytes, q_bf16, T, 1, CSA2_HSI_POOL, &sm)) return CSA2_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(reindex_select_kernel, dim3(T), dim3(kRxThreads), 0, st, scores, sm.parts, sm.n_parts, sm.q,
+                     w_idx, keys, last_pos, pool, k, indices);
+  return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
+}
+
+}  // namespace csa2
 
 template <class Keys>
 static csa2_status topk_launch(const float* scores, const float* tile_max, uint32_t* stats, const Summary& sm,
