@@ -62,7 +62,8 @@ def parse():
 # public header, only its constants count: its documentation does not change the kernel).
 SCAN_SOURCES = ["compressed_sparse_attention_02_amd/csrc/index.hip", "compressed_sparse_attention_02_amd/csrc/idx_tile.h",
                 "compressed_sparse_attention_02_amd/csrc/idx_plan.h",
-                "compressed_sparse_attention_02_amd/csrc/csa2_common.h", "include/csa2.h"]
+                "compressed_sparse_attention_02_amd/csrc/csa2_common.h", "include/csa2.h",
+                "compressed_sparse_attention_02_amd/build.py"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "idx_scan_kernel_long_decode_hbm_traffic.md")
 CAL_BYTES = 1 << 30          # bytes the calibration dispatch reads, and writes
 

@@ -4,17 +4,23 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa2.so")
 SOURCES = ["abi.hip", "index.hip", "index_mx.hip", "topk.hip", "reindex.hip", "attend.hip", "kvwrite.hip"]
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Werror", "-Wno-unused-command-line-argument",
     # no packed fp32 (v_pk_*_f32) instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-source flags.  The grouped-query scan keeps its 32 x 32 MFMA accumulators in
+# VGPRs (by default the compiler puts them in AGPRs and copies each query's 16 values
+# out before the head fold; measured 4 % slower on the causal-prefill scan).
+FILE_FLAGS = {"index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 # Host-side AddressSanitizer + UndefinedBehaviorSanitizer (the argument checks and launch code of
@@ -25,17 +31,27 @@ HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize
                  "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g0"]
 
 
-def build(verbose: bool = False, extra=(), sanitize: bool = False) -> str:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    out = LIB_SAN if sanitize else LIB
-    san = HOST_SANITIZE if sanitize else []
-    cmd = [hipcc, *FLAGS, *san, *extra, *[os.path.join(CSRC, s) for s in SOURCES], "-o", out + ".tmp"]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{errs}")
+
+
+def build(verbose: bool = False, extra=(), sanitize: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the shared library."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    out = LIB_SAN if sanitize else LIB
+    san = HOST_SANITIZE if sanitize else []
+    with tempfile.TemporaryDirectory(prefix="csa2_build_") as tmp:
+        objs = [os.path.join(tmp, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[hipcc, *FLAGS, *san, *extra, *FILE_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
+        _run([hipcc, "--offload-arch=gfx950", "-shared", *san, *objs, "-o", out + ".tmp"], verbose)
     os.replace(out + ".tmp", out)
     return out
 
