@@ -4,13 +4,13 @@
 // preceding Full layer left for its query, with its own indexer query over the
 // shared indexer keys, and keeps its own top-k within the pool.  The pool rows
 // are gathered into a contiguous key block per query (zero rows past the pool's
-// end), which turns the call into the regular scan and the row-regime
-// selection over P = CSA2_HSI_POOL keys per "sequence" of one query, with the
-// pool size as the visible count; the selected pool positions are mapped back
-// to entry ids.  The pool is ascending, so position order is entry order: the
-// tie rule (lower index first) and the ascending output carry over unchanged,
-// and the fp64 scores are those of the original rows (same bf16 values, same
-// operation order).
+// end), which turns the scoring into the regular scan over P = CSA2_HSI_POOL
+// keys per "sequence" of one query, with the pool size as the visible count;
+// the selection within each pool (reindex_select_kernel, topk.hip) writes the
+// selected positions' entry ids.  The pool is ascending, so position order is
+// entry order: the tie rule (lower index first) and the ascending output carry
+// over unchanged, and the fp64 scores are those of the original rows (same
+// bf16 values, same operation order).
 #include "mxfp4.h"
 
 namespace csa2 {

@@ -224,8 +224,9 @@ csa2_status csa2_hsi_pool(const float* tile_max, const uint32_t* stats, size_t s
  *  k        must be CSA2_TOPK;  indices int32 [T][k] out
  *  workspace >= csa2_reindex_workspace_bytes(T, k) (about 4.2 MiB per query:
  *           the gathered pool keys, their scores and the selection's summary)
- *  Runs a gather kernel, csa2_index and csa2_topk (row regime) over the
- *  gathered keys, and a map kernel, all on hip_stream.
+ *  Runs a gather kernel, csa2_index over the gathered keys and a selection
+ *  kernel within each pool (one block per query, writing entry ids), all on
+ *  hip_stream.
  */
 size_t csa2_reindex_workspace_bytes(int32_t T, int32_t k);
 csa2_status csa2_reindex(const int32_t* pool, const void* q_idx, const float* w_idx, const void* k_idx,
