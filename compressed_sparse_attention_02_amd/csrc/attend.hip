@@ -805,45 +805,49 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
       __syncthreads();  // the window rows of every wave in sh.x
       cs_s_product<KVF, true>(sh, raw, qb, acc, sc0);
     }
-    sh.sx[w][0][lane] = acc[0];
-    sh.sx[w][1][lane] = acc[1];
+    if (h == 1) {  // the second half's partial S, for the first half's softmax
+      sh.sx[w][0][lane] = acc[0];
+      sh.sx[w][1][lane] = acc[1];
+    }
     if (c + 1 < c1) {
       cs_load_raw<KVF, SWF>(a, t, b, c + 1, layer, ix, raw);
       if (c + 2 < c1) cs_load_indices(a, t, c + 2, ix);
     }
     __syncthreads();
-    // full S^T of the group's 16 heads (own + partner half: the same sum in both waves)
-    acc[0] += sh.sx[w ^ 4][0][lane];
-    acc[1] += sh.sx[w ^ 4][1][lane];
-    // acc[m][i]: row 16 m + 4 g + i, head 16 hg + r16
-    float z[8];
-    const uint32_t okg = ok >> (4 * g);
+    // Softmax of head group hg by its first-half wave only (the second half's
+    // partial S is all it contributes; it takes P and the rescale state from LDS).
+    if (h == 0) {
+      // full S^T of the group's 16 heads (own + partner half)
+      acc[0] += sh.sx[w ^ 4][0][lane];
+      acc[1] += sh.sx[w ^ 4][1][lane];
+      // acc[m][i]: row 16 m + 4 g + i, head 16 hg + r16
+      float z[8];
+      const uint32_t okg = ok >> (4 * g);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = ((okg >> i) & 1u) ? acc[0][i] * a.scale_log2 : -INFINITY;
-      z[4 + i] = ((okg >> (16 + i)) & 1u) ? acc[1][i] * a.scale_log2 : -INFINITY;
-    }
-    float cm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-    cm = max_xor16(cm);
-    cm = max_xor32(cm);
-    // lazy rescaling: the reference maximum stays while the chunk's scores
-    // exceed it by at most kRescaleSlack (log2 units)
-    const float mtrue = fmaxf(st.m, cm);
-    const bool grow = mtrue > st.m + kRescaleSlack;
-    const float mn = grow ? mtrue : st.m;
-    const float alpha = grow ? exp2f(st.m - mn) : 1.f;
-    uint32_t pb[4];
-    float psum = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        z[i] = ((okg >> i) & 1u) ? acc[0][i] * a.scale_log2 : -INFINITY;
+        z[4 + i] = ((okg >> (16 + i)) & 1u) ? acc[1][i] * a.scale_log2 : -INFINITY;
+      }
+      float cm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+      cm = max_xor16(cm);
+      cm = max_xor32(cm);
+      // lazy rescaling: the reference maximum stays while the chunk's scores
+      // exceed it by at most kRescaleSlack (log2 units)
+      const float mtrue = fmaxf(st.m, cm);
+      const bool grow = mtrue > st.m + kRescaleSlack;
+      const float mn = grow ? mtrue : st.m;
+      const float alpha = grow ? exp2f(st.m - mn) : 1.f;
+      uint32_t pb[4];
+      float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p0 = z[2 * i] == -INFINITY ? 0.f : exp2f(z[2 * i] - mn);
-      const float p1 = z[2 * i + 1] == -INFINITY ? 0.f : exp2f(z[2 * i + 1] - mn);
-      psum += p0 + p1;
-      pb[i] = pack_bf16x2_rne(p0, p1);
-    }
-    st.l = st.l * alpha + psum;
-    st.m = mn;
-    if (h == 0) {  // wave hg publishes head group hg
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = z[2 * i] == -INFINITY ? 0.f : exp2f(z[2 * i] - mn);
+        const float p1 = z[2 * i + 1] == -INFINITY ? 0.f : exp2f(z[2 * i + 1] - mn);
+        psum += p0 + p1;
+        pb[i] = pack_bf16x2_rne(p0, p1);
+      }
+      st.l = st.l * alpha + psum;
+      st.m = mn;
       bf16x8 pv;
       __builtin_memcpy(&pv, pb, 16);
       sh.p[hg][lane] = pv;
