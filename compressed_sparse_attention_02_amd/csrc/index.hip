@@ -28,12 +28,24 @@ namespace csa2 {
 // Group maxima: group (x * kScanTiles + u) * S + (i % S) holds the maxima of
 // tile u of every wave in the block's iterations i, so a group samples the
 // whole row and neighbouring tiles never share a group.
-template <int QG, int S>
+//
+// With POOL (Reindex: csa2_reindex scores each query's candidate pool),
+// "sequence" b is query b's pool: position s holds entry pool.rows[b N + s] of
+// key sequence b / pool.qps of k_idx (pool.N_all rows each), or -1 (padding,
+// scored -inf), and every position is visible.
+struct PoolRows {
+  const int32_t* rows;
+  int64_t N_all;
+  int qps;
+};
+
+template <int QG, int S, bool POOL = false>
 __global__ __launch_bounds__(kScanThreads, QG == 1 ? 6 : QG == 2 ? 4 : 2) void idx_scan_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx,
     const uint16_t* __restrict__ k_idx, const int32_t* __restrict__ q_pos, int ratio,
     int q_per_seq, int64_t N, float* __restrict__ scores, float* __restrict__ tile_max,
-    uint32_t* __restrict__ header, float* __restrict__ group_max, float* __restrict__ norm_partial) {
+    uint32_t* __restrict__ header, float* __restrict__ group_max, float* __restrict__ norm_partial,
+    PoolRows pool = PoolRows{}) {
   __shared__ __attribute__((aligned(16))) uint16_t sq[QG * kIdxHeads * kQRowPad];
   __shared__ float red[kScanWaves];
   const int lane = threadIdx.x & 63;
@@ -67,7 +79,7 @@ __global__ __launch_bounds__(kScanThreads, QG == 1 ? 6 : QG == 2 ? 4 : 2) void i
   __syncthreads();
 
   const int64_t nchunks = (N + kChunkKeys - 1) / kChunkKeys;
-  const uint16_t* kseq = k_idx + (size_t)b * N * kIdxDim;
+  const uint16_t* kseq = POOL ? k_idx + (size_t)(b / pool.qps) * pool.N_all * kIdxDim : k_idx + (size_t)b * N * kIdxDim;
   const int64_t last = (nvis_max < N ? (nvis_max > 0 ? nvis_max : 1) : N) - 1;  // last row worth reading
   float maxn2 = 0.f;
   float gm[QG][S];
@@ -82,10 +94,18 @@ __global__ __launch_bounds__(kScanThreads, QG == 1 ? 6 : QG == 2 ? 4 : 2) void i
     // Unconditional loads keep the code branch-free: keys past the end or past
     // every query's visibility re-read row `last`, which is already cached.
     uint4 kv[kScanTiles][4];
+    bool live[kScanTiles];
 #pragma unroll
     for (int u = 0; u < kScanTiles; ++u) {
       const int64_t s = base + u * kTileKeys + col;
-      load_key_slices(kseq, s < last ? s : last, g, kv[u]);
+      int64_t row = s < last ? s : last;
+      live[u] = true;
+      if (POOL) {
+        const int32_t e = pool.rows[(size_t)b * N + row];
+        live[u] = e >= 0;
+        row = e >= 0 ? e : 0;
+      }
+      load_key_slices(kseq, row, g, kv[u]);
     }
     float sc[QG][kScanTiles];
 #pragma unroll
@@ -112,7 +132,7 @@ __global__ __launch_bounds__(kScanThreads, QG == 1 ? 6 : QG == 2 ? 4 : 2) void i
       for (int qq = 0; qq < QG; ++qq) {
         if (!valid[qq]) continue;
         const float part = tile_score(&sq[qq * kIdxHeads * kQRowPad], kv[u], wr[qq], col, g);
-        sc[qq][u] = (s < nvis[qq]) ? part : -INFINITY;
+        sc[qq][u] = (s < nvis[qq] && live[u]) ? part : -INFINITY;
       }
     }
     // Every lane holds the score of key `col` of each tile.  Lane l < 32 stores
@@ -386,6 +406,38 @@ static void launch_scan(const IndexPlan& p, hipStream_t st, const uint16_t* q, c
   else
     launch_scan_s<QG, 4>(grid, st, q, w, k, q_pos, ratio, q_per_seq, N, scores, tile_max, header, gmax, partial);
 }
+
+namespace csa2 {
+
+// The Reindex scan: query t's pool as its own one-query "sequence" of P
+// positions (key rows through the pool, padding scored -inf), with the outputs
+// and summary of csa2_index(T, 1, P).
+csa2_status index_pool_launch(const void* q_idx, const float* w_idx, const void* k_all, int64_t N_all, int qps,
+                              const int32_t* pool, int32_t T, int64_t P, float* scores, float* tile_max,
+                              uint32_t* stats, size_t stats_bytes, hipStream_t st) {
+  IndexPlan p;
+  if (!index_plan(T, 1, P, &p)) return CSA2_ERR_UNSUPPORTED;
+  if (stats_bytes < stats_words(T, p) * sizeof(uint32_t)) return CSA2_ERR_INVALID_ARG;
+  (void)hipGetLastError();
+  float* gmax = (float*)(stats + stats_groups_off(T));
+  float* partial = (float*)(stats + stats_parts_off(T, p.n_groups));
+  const dim3 grid(p.blocks_x, p.B, p.groups);
+  const PoolRows pr{pool, N_all, qps};
+  const uint16_t* q = (const uint16_t*)q_idx;
+  const uint16_t* k = (const uint16_t*)k_all;
+  if (p.slots == 1)
+    hipLaunchKernelGGL((idx_scan_kernel<1, 1, true>), grid, dim3(kScanThreads), 0, st, q, w_idx, k, nullptr, 1, 1, P,
+                       scores, tile_max, stats, gmax, partial, pr);
+  else if (p.slots == 2)
+    hipLaunchKernelGGL((idx_scan_kernel<1, 2, true>), grid, dim3(kScanThreads), 0, st, q, w_idx, k, nullptr, 1, 1, P,
+                       scores, tile_max, stats, gmax, partial, pr);
+  else
+    hipLaunchKernelGGL((idx_scan_kernel<1, 4, true>), grid, dim3(kScanThreads), 0, st, q, w_idx, k, nullptr, 1, 1, P,
+                       scores, tile_max, stats, gmax, partial, pr);
+  return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
+}
+
+}  // namespace csa2
 
 extern "C" csa2_status csa2_index(const void* q_idx, const float* w_idx, const void* k_idx,
                                   const int32_t* q_pos, int32_t ratio, int32_t T, int32_t q_per_seq,

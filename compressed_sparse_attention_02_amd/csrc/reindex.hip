@@ -2,24 +2,31 @@
 //
 // A Reindex layer (report sec. 2.3.2) scores only the candidate pool the
 // preceding Full layer left for its query, with its own indexer query over the
-// shared indexer keys, and keeps its own top-k within the pool.  The pool rows
-// are gathered into a contiguous key block per query (zero rows past the pool's
-// end), which turns the scoring into the regular scan over P = CSA2_HSI_POOL
-// keys per "sequence" of one query, with the pool size as the visible count;
-// the selection within each pool (reindex_select_kernel, topk.hip) writes the
-// selected positions' entry ids.  The pool is ascending, so position order is
-// entry order: the tie rule (lower index first) and the ascending output carry
-// over unchanged, and the fp64 scores are those of the original rows (same
-// bf16 values, same operation order).
+// shared indexer keys, and keeps its own top-k within the pool.  Each query's
+// pool is scanned as a "sequence" of its own of P = CSA2_HSI_POOL positions:
+// with bf16 keys the scan reads the key rows through the pool (index.hip,
+// index_pool_launch); with MXFP4 keys the pool rows are first dequantised
+// (exactly) into a contiguous bf16 block per query, which the regular scan then
+// reads with the pool size as the visible count.  Padding positions score
+// -inf either way.  The selection within each pool (reindex_select_kernel,
+// topk.hip) writes the selected positions' entry ids.  The pool is ascending,
+// so position order is entry order: the tie rule (lower index first) and the
+// ascending output carry over unchanged, and the fp64 scores are those of the
+// original rows (same bf16 values, same operation order).
 #include "mxfp4.h"
 
 namespace csa2 {
 
-// The selection over the scanned pools (topk.hip).
+// The selection over the scanned pools (topk.hip); keys are the gathered rows
+// (pool_qps == 0) or the shared keys read through the pool.
 csa2_status reindex_select_launch(const float* scores, const uint32_t* stats, size_t stats_bytes,
-                                  const void* q_bf16, const float* w_idx, const uint16_t* keys,
-                                  const int32_t* last_pos, const int32_t* pool, int32_t T, int32_t k,
-                                  int32_t* indices, hipStream_t st);
+                                  const void* q_bf16, const float* w_idx, const uint16_t* keys, int64_t N_all,
+                                  int pool_qps, const int32_t* pool, int32_t T, int32_t k, int32_t* indices,
+                                  hipStream_t st);
+// The scan of each query's pool through the pool (index.hip).
+csa2_status index_pool_launch(const void* q_idx, const float* w_idx, const void* k_all, int64_t N_all, int qps,
+                              const int32_t* pool, int32_t T, int64_t P, float* scores, float* tile_max,
+                              uint32_t* stats, size_t stats_bytes, hipStream_t st);
 
 constexpr int kPool = CSA2_HSI_POOL;
 constexpr int kGatherThreads = 256;
@@ -123,18 +130,6 @@ extern "C" size_t csa2_reindex_workspace_bytes(int32_t T, int32_t k) {
   return total;
 }
 
-// The gathered pool keys as a batch of T one-query "sequences" of kPool keys:
-// the regular scan, then the selection within each pool, which writes the
-// selected positions' entry ids.
-static csa2_status reindex_finish(const ReindexWs& w, const void* q_bf16, const float* w_idx, const int32_t* pool,
-                                  int32_t T, int32_t k, int32_t* indices, void* hip_stream) {
-  csa2_status s = csa2_index(q_bf16, w_idx, w.keys, w.qpos, 1, T, 1, kPool, w.scores, w.tile_max, w.stats,
-                             w.stats_bytes, hip_stream);
-  if (s != CSA2_OK) return s;
-  return reindex_select_launch(w.scores, w.stats, w.stats_bytes, q_bf16, w_idx, w.keys, w.qpos, pool, T, k, indices,
-                               (hipStream_t)hip_stream);
-}
-
 extern "C" csa2_status csa2_reindex(const int32_t* pool, const void* q_idx, const float* w_idx, const void* k_idx,
                                     int32_t T, int32_t q_per_seq, int64_t N, int32_t k, int32_t* indices,
                                     void* workspace, size_t workspace_bytes, void* hip_stream) {
@@ -146,12 +141,14 @@ extern "C" csa2_status csa2_reindex(const int32_t* pool, const void* q_idx, cons
   size_t need;
   ReindexWs w = reindex_ws(workspace, T, k, &need);
   if (!workspace || !aligned16(workspace) || workspace_bytes < need) return CSA2_ERR_WORKSPACE;
-  (void)hipGetLastError();
-  hipLaunchKernelGGL(reindex_gather_kernel<Bf16Keys>, dim3(kPool / kGatherRows, T), dim3(kGatherThreads), 0,
-                     (hipStream_t)hip_stream, pool, Bf16Keys{(const uint16_t*)k_idx}, q_per_seq, N, w.keys, w.qpos,
-                     nullptr, nullptr, nullptr);
-  if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
-  return reindex_finish(w, q_idx, w_idx, pool, T, k, indices, hip_stream);
+  // the scan reads the key rows through the pool; the selection rescores its
+  // band through the pool too
+  const hipStream_t st = (hipStream_t)hip_stream;
+  csa2_status s = index_pool_launch(q_idx, w_idx, k_idx, N, q_per_seq, pool, T, kPool, w.scores, w.tile_max, w.stats,
+                                    w.stats_bytes, st);
+  if (s != CSA2_OK) return s;
+  return reindex_select_launch(w.scores, w.stats, w.stats_bytes, q_idx, w_idx, (const uint16_t*)k_idx, N, q_per_seq,
+                               pool, T, k, indices, st);
 }
 
 extern "C" csa2_status csa2_reindex_mxfp4(const int32_t* pool, const uint8_t* q_codes, const uint8_t* q_scales,
@@ -172,5 +169,10 @@ extern "C" csa2_status csa2_reindex_mxfp4(const int32_t* pool, const uint8_t* q_
                      (hipStream_t)hip_stream, pool, Mx4Keys{k_codes, k_scales}, q_per_seq, N, w.keys, w.qpos, q_codes,
                      q_scales, w.q);
   if (hipGetLastError() != hipSuccess) return CSA2_ERR_LAUNCH;
-  return reindex_finish(w, w.q, w_idx, pool, T, k, indices, hip_stream);
+  // the gathered rows as a batch of T one-query "sequences" of kPool keys
+  csa2_status s = csa2_index(w.q, w_idx, w.keys, w.qpos, 1, T, 1, kPool, w.scores, w.tile_max, w.stats,
+                             w.stats_bytes, hip_stream);
+  if (s != CSA2_OK) return s;
+  return reindex_select_launch(w.scores, w.stats, w.stats_bytes, w.q, w_idx, w.keys, kPool, 0, pool, T, k, indices,
+                               (hipStream_t)hip_stream);
 }

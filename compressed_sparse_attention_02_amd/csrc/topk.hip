@@ -31,6 +31,8 @@
 //    largest fp32 value (lo <= T^ <= hi, two levels of 256 value bins), accepts
 //    entries above hi + 2 eps, rescores the band [lo - 2 eps, hi + 2 eps] in
 //    fp64 and takes the rest by (fp64 score desc, index asc).
+#include <type_traits>
+
 #include "idx_plan.h"
 #include "mxfp4.h"
 
@@ -1142,52 +1144,76 @@ __global__ __launch_bounds__(NT) void topk_rows_pf_kernel(
 // ------------------------------------------------------ Reindex selection
 
 // Top-k within one Reindex query's candidate pool (report sec. 2.3.2), one
-// block per query over the scan of its gathered pool keys: the pool's P fp32
-// scores sit in registers (P / kRxThreads per thread), the k-th is bracketed
-// from them directly, the band is rescored in fp64 from the gathered keys (the
-// pool rows' own bf16 values), and the selected pool positions are written as
-// the entry ids they hold, ascending (the pool is ascending, so position order
-// is entry order and the lower-index tie rule carries over).  Positions past
-// the pool's entry count are pad and never selected.
-constexpr int kRxThreads = 1024;
+// block per query over the scan of its pool: the pool's P fp32 scores sit in
+// registers (P / kRxThreads per thread; 512 threads leave every wave 256
+// VGPRs, so nothing spills), the floor comes from each thread's two largest,
+// the entries that reach it are listed and the k-th among them found by one
+// wave, the band is rescored in fp64 from the pool rows' own bf16 values, and
+// the selected pool positions are written as the entry ids they hold,
+// ascending (the pool is ascending, so position order is entry order and the
+// lower-index tie rule carries over).  Positions past the pool's entry count
+// are pad and never selected.
+constexpr int kRxThreads = 512;
 constexpr int kRxPer = CSA2_HSI_POOL / kRxThreads;
 static_assert(CSA2_HSI_POOL % kRxThreads == 0 && CSA2_HSI_POOL <= kSmallMax, "pool positions fit the bitmap");
 
+// Band key rows read through the pool: position p is entry pool[p] of the
+// query's key sequence (the positions rescored are never padding).
+struct PoolKeys {
+  const uint16_t* k;    // the query's key sequence
+  const int32_t* pool;  // the query's pool
+  __device__ __forceinline__ uint4 piece(int64_t row, int i) const {
+    return *reinterpret_cast<const uint4*>(k + (size_t)pool[row] * kIdxDim + 8 * i);
+  }
+};
+
+// keys: the gathered pool keys ([T][P][128] bf16, row = position) or, with
+// pool_qps > 0, the shared keys [B][N_all][128] read through the pool.
+template <bool GATHERED>
 __global__ __launch_bounds__(kRxThreads) void reindex_select_kernel(
     const float* __restrict__ scores, const float* __restrict__ parts, int64_t n_parts,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, const uint16_t* __restrict__ keys,
-    const int32_t* __restrict__ last_pos, const int32_t* __restrict__ pool, int k, int32_t* __restrict__ indices) {
+    int64_t N_all, int pool_qps, const int32_t* __restrict__ pool, int k, int32_t* __restrict__ indices) {
   using Lds = PfLdsT<kRxThreads>;
   __shared__ Lds L;
   auto& sh = L.f;
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t nv = (int64_t)last_pos[t] + 1;  // pool entries; the rest is pad
   const uint32_t kk = (uint32_t)k;
   const uint16_t* qt = q_idx + (size_t)t * kIdxHeads * kIdxDim;
   const float* wt = w_idx + (size_t)t * kIdxHeads;
-  const Bf16Keys kb = Bf16Keys{keys}.seq(t, CSA2_HSI_POOL);
   const float* row = scores + (size_t)t * CSA2_HSI_POOL;
   const int32_t* pl = pool + (size_t)t * CSA2_HSI_POOL;
+  using Keys = std::conditional_t<GATHERED, Bf16Keys, PoolKeys>;
+  Keys kb;
+  if constexpr (GATHERED) kb = Bf16Keys{keys}.seq(t, CSA2_HSI_POOL);
+  else kb = PoolKeys{keys + (size_t)(t / pool_qps) * N_all * kIdxDim, pl};
   int32_t* out = indices + (size_t)t * k;
-  // the pool's scores (positions tid, tid + kRxThreads, ...) and the bound
-  // terms, every load issued before any is used
+  // the pool's scores (positions tid, tid + kRxThreads, ...; the scan scored
+  // the positions past the pool -inf), its entries (the count of them is the
+  // visible count: the pool is a prefix) and the bound terms, every load
+  // issued before any is used
   float v[kRxPer];
+  uint32_t nin = 0;
 #pragma unroll
   for (int r = 0; r < kRxPer; ++r) {
     const int64_t i = tid + (int64_t)r * kRxThreads;
-    v[r] = i < nv ? row[i] : -INFINITY;
+    v[r] = row[i];
+    nin += pl[i] >= 0 ? 1u : 0u;
   }
   float m2;
   double qf, sw;
   bound_terms(qt, wt, parts + (size_t)t * n_parts, n_parts, tid, kRxThreads, &m2, &qf, &sw);
   for (int i = tid; i < 256; i += kRxThreads) { sh.sel.hist[i] = 0u; sh.sel.bmin[i] = 0xFFFFFFFFu; }
   if (tid == 0) { sh.n_out = 0; sh.n_band = 0; }
-  float lmax = -INFINITY, lmin = INFINITY;
+  // the thread's two largest values (distinct entries) and smallest value
+  float lmax = -INFINITY, lmax2 = -INFINITY, lmin = INFINITY;
 #pragma unroll
   for (int r = 0; r < kRxPer; ++r) {
-    lmax = fmaxf(lmax, v[r]);
-    lmin = fminf(lmin, v[r] > -INFINITY ? v[r] : INFINITY);
+    const float x = v[r];
+    lmax2 = fmaxf(lmax2, fminf(lmax, x));
+    lmax = fmaxf(lmax, x);
+    lmin = fminf(lmin, x > -INFINITY ? x : INFINITY);
   }
   m2 = wave_max_dpp(m2);
   qf = wave_sum_groups8_f64(qf);
@@ -1196,31 +1222,33 @@ __global__ __launch_bounds__(kRxThreads) void reindex_select_kernel(
   const float wmin = wave_min_dpp(lmin);
   const float wl0 = wave_min_dpp(lmax > -INFINITY ? lmax : INFINITY);
   const uint32_t wthr = (uint32_t)__popcll(__ballot(lmax > -INFINITY));
+  const uint32_t win = wave_sum_u32_dpp(nin);
   if (lane == 0) {
     L.fr[0][wave] = m2; L.fr[1][wave] = wmax; L.fr[2][wave] = wmin; L.fr[3][wave] = wl0;
     L.dr[0][wave] = qf; L.dr[1][wave] = sw;
-    L.wsum[wave] = wthr;
+    L.wsum[wave] = wthr | (win << 16);
   }
   __syncthreads();
   m2 = L.fr[0][0];
   float mx = L.fr[1][0], gmin = L.fr[2][0], l0 = L.fr[3][0];
   qf = L.dr[0][0];
   sw = L.dr[1][0];
-  uint32_t tthr = L.wsum[0];
+  uint32_t tthr = L.wsum[0] & 0xFFFFu, cnt_in = L.wsum[0] >> 16;
   for (int i = 1; i < kRxThreads / 64; ++i) {
     m2 = fmaxf(m2, L.fr[0][i]); mx = fmaxf(mx, L.fr[1][i]); gmin = fminf(gmin, L.fr[2][i]);
     l0 = fminf(l0, L.fr[3][i]);
-    qf += L.dr[0][i]; sw += L.dr[1][i]; tthr += L.wsum[i];
+    qf += L.dr[0][i]; sw += L.dr[1][i]; tthr += L.wsum[i] & 0xFFFFu; cnt_in += L.wsum[i] >> 16;
   }
+  const int64_t nv = cnt_in;  // pool entries (a prefix of the positions)
   const float eps = bound_eps(m2, qf, sw);
   if (nv <= k) {
     for (int i = tid; i < k; i += kRxThreads) out[i] = i < nv ? pl[i] : -1;
     return;
   }
-  // the floor from the per-thread maxima (distinct entries' scores), then the
-  // entries that reach it listed through one block scan
-  const float pm[1] = {lmax};
-  const float tau = floor_of_values<1>(sh.sel, pm, kk, tthr, l0, gmin, mx, &L.res);
+  // the floor from the per-thread two largest (distinct entries' scores), then
+  // the entries that reach it listed through one block scan
+  const float pm[2] = {lmax, lmax2};
+  const float tau = floor_of_values<2>(sh.sel, pm, kk, tthr, l0, gmin, mx, &L.res);
   double thr = cand_threshold(tau, eps, 0);
   if (!(thr <= (double)tau)) thr = -INFINITY;  // eps not finite: keep everything
   uint32_t cnt = 0;
@@ -2707,15 +2735,21 @@ namespace csa2 {
 // The Reindex selection over the scan of a batch of gathered pools (one
 // one-query "sequence" of CSA2_HSI_POOL keys per query; stats is that scan's
 // summary).  Used by csa2_reindex.
+// keys: the gathered pool keys (pool_qps == 0) or the shared keys [B][N_all][128]
+// read through the pool (pool_qps queries per key sequence).
 csa2_status reindex_select_launch(const float* scores, const uint32_t* stats, size_t stats_bytes,
-                                  const void* q_bf16, const float* w_idx, const uint16_t* keys,
-                                  const int32_t* last_pos, const int32_t* pool, int32_t T, int32_t k,
-                                  int32_t* indices, hipStream_t st) {
+                                  const void* q_bf16, const float* w_idx, const uint16_t* keys, int64_t N_all,
+                                  int pool_qps, const int32_t* pool, int32_t T, int32_t k, int32_t* indices,
+                                  hipStream_t st) {
   Summary sm;
   if (!summary_bf16(stats, stats_bytes, q_bf16, T, 1, CSA2_HSI_POOL, &sm)) return CSA2_ERR_INVALID_ARG;
   (void)hipGetLastError();
-  hipLaunchKernelGGL(reindex_select_kernel, dim3(T), dim3(kRxThreads), 0, st, scores, sm.parts, sm.n_parts, sm.q,
-                     w_idx, keys, last_pos, pool, k, indices);
+  if (pool_qps == 0)
+    hipLaunchKernelGGL(reindex_select_kernel<true>, dim3(T), dim3(kRxThreads), 0, st, scores, sm.parts, sm.n_parts,
+                       sm.q, w_idx, keys, N_all, 1, pool, k, indices);
+  else
+    hipLaunchKernelGGL(reindex_select_kernel<false>, dim3(T), dim3(kRxThreads), 0, st, scores, sm.parts, sm.n_parts,
+                       sm.q, w_idx, keys, N_all, pool_qps, pool, k, indices);
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH;
 }
 
