@@ -401,36 +401,66 @@ __device__ void bracket_kth(SelLds& s, int64_t n, uint32_t rank, Get get, float*
   bracket_visit(s, rank, [&](auto f) { for_each4(n, get, f); }, lo, hi);
 }
 
-// Order-preserving key of the rank-th largest (1-based) of n values get(i)
-// (finite or -inf, at least rank finite), by one wave and no block barrier:
-// four passes over 8-bit digits of the keys, each counting the values that
-// match the digits found so far in a 256-bin LDS histogram (`hist`, which no
-// other wave touches meanwhile) and picking the digit that holds the rank-th.
-// All 64 lanes of the calling wave call this; every lane gets the key.
-template <typename Get>
+// Inclusive prefix sum over the 64 lanes of a wave, in lane order (DPP: shifts
+// by 1, 2, 4 and 8 within each row of 16 lanes, then each row's total carried
+// into the rows above by the row broadcasts of lanes 15 and 31).
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+// Order-preserving key of the rank-th largest (1-based) of n <= MAXN values
+// get(i) (finite or -inf, at least rank finite), by one wave and no block
+// barrier.  Lane l holds the keys of values l, l + 64, ... in registers.  Every
+// key lies between the smallest and the largest, so the high bits those two
+// share are the answer's; the bits below are taken 8 at a time from the top,
+// each digit by counting the keys that match the answer's bits so far in a
+// 256-bin LDS histogram (`hist`, which no other wave touches meanwhile) and
+// picking the digit that holds the rank-th.  All 64 lanes of the calling wave
+// call this; every lane gets the key.
+template <int MAXN, typename Get>
 __device__ uint32_t wave_kth_key(int64_t n, uint32_t rank, Get get, uint32_t* hist) {
+  static_assert(MAXN % 64 == 0, "whole registers");
+  constexpr int J = MAXN / 64;
   const int lane = threadIdx.x & 63;
-  uint32_t prefix = 0u, mask = 0u;
-#pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = lane; i < 256; i += 64) hist[i] = 0u;
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    for (int64_t i = lane; i < n; i += 64) {
-      const uint32_t key = f32_key(get(i));
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+  const int jn = (int)((n + 63) >> 6);
+  uint32_t key[J];
+  uint32_t kmin = 0xFFFFFFFFu, nkmax = 0xFFFFFFFFu;  // smallest key, complement of the largest
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    key[j] = 0u;  // below every value's key: a slot past n never reaches the rank-th
+    if (j < jn && lane + 64 * j < n) {
+      key[j] = f32_key(get(lane + 64 * j));
+      kmin = min(kmin, key[j]);
+      nkmax = min(nkmax, ~key[j]);
     }
+  }
+  kmin = wave_min_u32_dpp(kmin);
+  const uint32_t kmax = ~wave_min_u32_dpp(nkmax);
+  if (kmin == kmax) return kmax;  // all keys equal
+  int top = 31 - __clz(kmin ^ kmax);                    // highest bit that differs
+  uint32_t mask = ~(uint32_t)((2ull << top) - 1ull);  // the bits above it
+  uint32_t prefix = kmax & mask;
+#pragma unroll 1
+  while (top >= 0) {
+    const int shift = top >= 7 ? top - 7 : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hist[lane + 64 * i] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (j < jn && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 255u], 1u);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     // lane owns digits 255-4*lane .. 252-4*lane (descending)
     uint32_t c[4], sum = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) { c[i] = hist[255 - 4 * lane - i]; sum += c[i]; }
-    uint32_t incl = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t x = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += x;
-    }
+    const uint32_t incl = wave_incl_scan_u32(sum);
     uint32_t cum = incl - sum, digit = 0u, left = 0u;
     bool mine = false;
     if (cum < rank && rank <= incl) {
@@ -440,12 +470,12 @@ __device__ uint32_t wave_kth_key(int64_t n, uint32_t rank, Get get, uint32_t* hi
         cum += c[i];
       }
     }
-    const uint64_t who = __ballot(mine);
-    const int src = __ffsll((unsigned long long)who) - 1;
-    digit = __shfl(digit, src, 64);
-    rank = __shfl(left, src, 64);
-    prefix |= digit << shift;
+    const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+    digit = (uint32_t)__builtin_amdgcn_readlane((int)digit, src);
+    rank = (uint32_t)__builtin_amdgcn_readlane((int)left, src);
+    prefix |= (digit & 255u) << shift;
     mask |= 255u << shift;
+    top = shift - 1;
   }
   return prefix;
 }
@@ -916,7 +946,7 @@ __device__ __forceinline__ void pf_finish(Lds& L, int64_t n, GetV getv, GetI get
   float t_lo, t_hi;
   if (n <= kPfMax) {  // a list in LDS: the exact k-th by one wave
     if (threadIdx.x < 64) {
-      const uint32_t key = wave_kth_key(n, kk, getv, sh.sel.hist);
+      const uint32_t key = wave_kth_key<kPfMax>(n, kk, getv, sh.sel.hist);
       if (threadIdx.x == 0) sh.sel.pick[2] = key;
     }
     __syncthreads();
@@ -1144,28 +1174,53 @@ __global__ __launch_bounds__(NT) void topk_rows_pf_kernel(
 // ------------------------------------------------------ Reindex selection
 
 // Top-k within one Reindex query's candidate pool (report sec. 2.3.2), one
-// block per query over the scan of its pool: the pool's P fp32 scores sit in
+// block per query over the scan of its pool.  The pool's P fp32 scores sit in
 // registers (P / kRxThreads per thread; 512 threads leave every wave 256
-// VGPRs, so nothing spills), the floor comes from each thread's two largest,
-// the entries that reach it are listed and the k-th among them found by one
-// wave, the band is rescored in fp64 from the pool rows' own bf16 values, and
-// the selected pool positions are written as the entry ids they hold,
-// ascending (the pool is ascending, so position order is entry order and the
-// lower-index tie rule carries over).  Positions past the pool's entry count
-// are pad and never selected.
+// VGPRs, so nothing spills) and its entry ids in LDS.  One histogram of the
+// scores at or above the smallest per-thread maximum (kRxBins value bins, each
+// keeping its count and its smallest and largest score) brackets the k-th
+// largest fp32 score by the scores of its bin; the scores above the bracket's
+// band are in, those in it form the band, rescored in fp64 from the pool rows'
+// own bf16 values, and the selected pool positions are written as the entry
+// ids they hold, ascending (the pool is ascending, so position order is entry
+// order and the lower-index tie rule carries over).  Positions past the pool's
+// entry count are pad and never selected.
 constexpr int kRxThreads = 512;
 constexpr int kRxPer = CSA2_HSI_POOL / kRxThreads;
+constexpr int kRxBins = 2048;  // four per thread
 static_assert(CSA2_HSI_POOL % kRxThreads == 0 && CSA2_HSI_POOL <= kSmallMax, "pool positions fit the bitmap");
+static_assert(kRxBins == 4 * kRxThreads, "four bins per thread");
 
 // Band key rows read through the pool: position p is entry pool[p] of the
 // query's key sequence (the positions rescored are never padding).
 struct PoolKeys {
   const uint16_t* k;    // the query's key sequence
-  const int32_t* pool;  // the query's pool
+  const int32_t* pool;  // the query's pool (entry ids by position)
   __device__ __forceinline__ uint4 piece(int64_t row, int i) const {
     return *reinterpret_cast<const uint4*>(k + (size_t)pool[row] * kIdxDim + 8 * i);
   }
 };
+
+struct RxLds {
+  FinLdsT<kPfBand> f;
+  union {
+    struct {
+      uint32_t cnt[kRxBins];
+      uint32_t kmin[kRxBins], kmax[kRxBins];  // smallest / largest score key of each bin
+    } h;
+    FinTailT<kPfBand, 32> tail;  // after the band is known
+  } u;
+  int32_t ent[CSA2_HSI_POOL];  // the pool's entry ids
+  float fr[4][kRxThreads / 64];
+  double dr[2][kRxThreads / 64];
+  uint32_t wsum[kRxThreads / 64], wsum2[kRxThreads / 64];
+  uint32_t pick[2];
+};
+
+__device__ __forceinline__ uint32_t rx_bin(float x, float a, float scale) {
+  const float f = (x - a) * scale;
+  return f >= (float)(kRxBins - 1) ? (uint32_t)(kRxBins - 1) : (f > 0.f ? (uint32_t)f : 0u);
+}
 
 // keys: the gathered pool keys ([T][P][128] bf16, row = position) or, with
 // pool_qps > 0, the shared keys [B][N_all][128] read through the pool.
@@ -1174,8 +1229,7 @@ __global__ __launch_bounds__(kRxThreads) void reindex_select_kernel(
     const float* __restrict__ scores, const float* __restrict__ parts, int64_t n_parts,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w_idx, const uint16_t* __restrict__ keys,
     int64_t N_all, int pool_qps, const int32_t* __restrict__ pool, int k, int32_t* __restrict__ indices) {
-  using Lds = PfLdsT<kRxThreads>;
-  __shared__ Lds L;
+  __shared__ RxLds L;
   auto& sh = L.f;
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1187,33 +1241,38 @@ __global__ __launch_bounds__(kRxThreads) void reindex_select_kernel(
   using Keys = std::conditional_t<GATHERED, Bf16Keys, PoolKeys>;
   Keys kb;
   if constexpr (GATHERED) kb = Bf16Keys{keys}.seq(t, CSA2_HSI_POOL);
-  else kb = PoolKeys{keys + (size_t)(t / pool_qps) * N_all * kIdxDim, pl};
+  else kb = PoolKeys{keys + (size_t)(t / pool_qps) * N_all * kIdxDim, L.ent};
   int32_t* out = indices + (size_t)t * k;
-  // the pool's scores (positions tid, tid + kRxThreads, ...; the scan scored
-  // the positions past the pool -inf), its entries (the count of them is the
-  // visible count: the pool is a prefix) and the bound terms, every load
-  // issued before any is used
+  // the pool's scores and entries (positions tid, tid + kRxThreads, ...; the
+  // scan scored the positions past the pool -inf) and the bound terms, every
+  // load issued before any is used
   float v[kRxPer];
-  uint32_t nin = 0;
+  int32_t pe[kRxPer];
 #pragma unroll
   for (int r = 0; r < kRxPer; ++r) {
-    const int64_t i = tid + (int64_t)r * kRxThreads;
-    v[r] = row[i];
-    nin += pl[i] >= 0 ? 1u : 0u;
+    v[r] = row[tid + r * kRxThreads];
+    pe[r] = pl[tid + r * kRxThreads];
   }
   float m2;
   double qf, sw;
   bound_terms(qt, wt, parts + (size_t)t * n_parts, n_parts, tid, kRxThreads, &m2, &qf, &sw);
-  for (int i = tid; i < 256; i += kRxThreads) { sh.sel.hist[i] = 0u; sh.sel.bmin[i] = 0xFFFFFFFFu; }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    L.u.h.cnt[tid + i * kRxThreads] = 0u;
+    L.u.h.kmin[tid + i * kRxThreads] = 0xFFFFFFFFu;
+    L.u.h.kmax[tid + i * kRxThreads] = 0u;
+  }
   if (tid == 0) { sh.n_out = 0; sh.n_band = 0; }
-  // the thread's two largest values (distinct entries) and smallest value
-  float lmax = -INFINITY, lmax2 = -INFINITY, lmin = INFINITY;
+  // entry ids to LDS (the count of entries is the visible count: the pool is a
+  // prefix); the thread's largest and smallest score
+  uint32_t nin = 0;
+  float lmax = -INFINITY, lmin = INFINITY;
 #pragma unroll
   for (int r = 0; r < kRxPer; ++r) {
-    const float x = v[r];
-    lmax2 = fmaxf(lmax2, fminf(lmax, x));
-    lmax = fmaxf(lmax, x);
-    lmin = fminf(lmin, x > -INFINITY ? x : INFINITY);
+    L.ent[tid + r * kRxThreads] = pe[r];
+    nin += pe[r] >= 0 ? 1u : 0u;
+    lmax = fmaxf(lmax, v[r]);
+    lmin = fminf(lmin, v[r] > -INFINITY ? v[r] : INFINITY);
   }
   m2 = wave_max_dpp(m2);
   qf = wave_sum_groups8_f64(qf);
@@ -1242,39 +1301,81 @@ __global__ __launch_bounds__(kRxThreads) void reindex_select_kernel(
   const int64_t nv = cnt_in;  // pool entries (a prefix of the positions)
   const float eps = bound_eps(m2, qf, sw);
   if (nv <= k) {
-    for (int i = tid; i < k; i += kRxThreads) out[i] = i < nv ? pl[i] : -1;
+    for (int i = tid; i < k; i += kRxThreads) out[i] = i < nv ? L.ent[i] : -1;
     return;
   }
-  // the floor from the per-thread two largest (distinct entries' scores), then
-  // the entries that reach it listed through one block scan
-  const float pm[2] = {lmax, lmax2};
-  const float tau = floor_of_values<2>(sh.sel, pm, kk, tthr, l0, gmin, mx, &L.res);
-  double thr = cand_threshold(tau, eps, 0);
-  if (!(thr <= (double)tau)) thr = -INFINITY;  // eps not finite: keep everything
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int r = 0; r < kRxPer; ++r) cnt += (tid + (int64_t)r * kRxThreads < nv && (double)v[r] >= thr) ? 1u : 0u;
-  uint32_t n;
-  uint32_t pos = block_excl_scan(cnt, L.wsum, &n);
+  // The histogram over [lo_h, mx]: when k threads hold a score, their maxima
+  // put at least k scores at or above the smallest of them, l0; else every
+  // finite score counts.  Bins are monotone in the score, so the k-th largest
+  // lies in the bin where the count from the top first reaches k.
+  const float lo_h = tthr >= kk ? l0 : gmin;
+  const float scale = mx > lo_h ? ((float)kRxBins - 0.01f) / (mx - lo_h) : 0.f;
+  if (tid == 0) { L.pick[0] = f32_key(lo_h); L.pick[1] = f32_key(mx); }  // the whole range until a bin is picked
 #pragma unroll
   for (int r = 0; r < kRxPer; ++r) {
-    const uint32_t i = tid + r * kRxThreads;
-    if ((int64_t)i < nv && (double)v[r] >= thr) {
-      if (pos < (uint32_t)kPfMax) { L.u.c.v[pos] = v[r]; L.u.c.i[pos] = i; }
-      ++pos;
+    if (v[r] >= lo_h) {
+      const uint32_t bin = rx_bin(v[r], lo_h, scale), key = f32_key(v[r]);
+      atomicAdd(&L.u.h.cnt[bin], 1u);
+      atomicMin(&L.u.h.kmin[bin], key);
+      atomicMax(&L.u.h.kmax[bin], key);
     }
   }
   __syncthreads();
-  const bool listed = n <= (uint32_t)kPfMax;
-  pf_finish<kRxThreads>(
-      L, listed ? (int64_t)n : nv,
-      [&](int64_t i) {
-        if (listed) return L.u.c.v[i];
-        const float x = row[i];
-        return (double)x >= thr ? x : -INFINITY;
-      },
-      [&](int64_t i) { return listed ? L.u.c.i[i] : (uint32_t)i; }, kk, k, eps, row, nv, qt, wt, kb, 0, out,
-      [&](uint32_t i) { return pl[i]; });
+  {
+    // thread j owns bins kRxBins-1-4j .. kRxBins-4-4j (descending)
+    uint32_t c[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { c[i] = L.u.h.cnt[kRxBins - 1 - 4 * tid - i]; sum += c[i]; }
+    uint32_t tot;
+    uint32_t cum = block_excl_scan(sum, L.wsum, &tot);
+    if (cum < kk && kk <= cum + sum) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (cum < kk && kk <= cum + c[i]) {
+          const int bin = kRxBins - 1 - 4 * tid - i;
+          L.pick[0] = L.u.h.kmin[bin];
+          L.pick[1] = L.u.h.kmax[bin];
+        }
+        cum += c[i];
+      }
+    }
+  }
+  __syncthreads();
+  double lo, hi;
+  band_bounds(key_f32(L.pick[0]), key_f32(L.pick[1]), eps, 0, &lo, &hi);
+  // sure entries (above the band) and the band, placed by one block scan of
+  // the packed counts (each total is at most P < 2^16)
+  {
+    uint32_t ns = 0, nb = 0;
+#pragma unroll
+    for (int r = 0; r < kRxPer; ++r) {
+      const bool in = tid + r * kRxThreads < nv;
+      const double x = (double)v[r];
+      ns += (in && x > hi) ? 1u : 0u;
+      nb += (in && !(x > hi) && x >= lo) ? 1u : 0u;
+    }
+    uint32_t tot;
+    const uint32_t pos = block_excl_scan(ns | (nb << 16), L.wsum2, &tot);
+    uint32_t ps = pos & 0xFFFFu, pb = pos >> 16;
+#pragma unroll
+    for (int r = 0; r < kRxPer; ++r) {
+      const uint32_t i = tid + r * kRxThreads;
+      const double x = (double)v[r];
+      if ((int64_t)i < nv && x > hi) {
+        if (ps < kk) sh.out[ps] = i;  // fewer than k lie above the k-th's bin
+        ++ps;
+      } else if ((int64_t)i < nv && x >= lo) {
+        if (pb < (uint32_t)kPfBand) sh.band_idx[pb] = i;
+        ++pb;
+      }
+    }
+    if (tid == 0) { sh.n_out = tot & 0xFFFFu; sh.n_band = tot >> 16; }
+  }
+  __syncthreads();
+  auto& tl = L.u.tail;
+  if (sh.n_band <= (uint32_t)kPfBand) finish_band<kRxThreads>(sh, tl, kk, qt, wt, kb, 0);
+  else finish_streaming(sh, kk, row, nv, lo, hi, qt, wt, kb, 0);
+  write_sorted_bits(sh, tl, kk, k, nv, L.wsum, out, [&](uint32_t i) { return L.ent[i]; });
 }
 
 // ------------------------------------------------------------ tile regime
