@@ -594,6 +594,15 @@ __device__ void rescore_band(FL& sh, FT& tl, uint32_t nb, const uint16_t* __rest
   }
 }
 
+// Sum over each row of 16 lanes, in every lane of the row (DPP).
+__device__ __forceinline__ uint32_t row_sum16_u32(uint32_t v) {
+  v += dpp_u32<kDppXor1>(v);
+  v += dpp_u32<kDppXor2>(v);
+  v += dpp_u32<kDppHalfMirror>(v);
+  v += dpp_u32<kDppMirror>(v);
+  return v;
+}
+
 // Complete the selection once T^ is known and the sure entries and band are
 // in sh.out / sh.band_idx (n_band <= FL::kBand): rescore and pick the band's share.
 template <int NT, class FL, class FT, class Keys>
@@ -603,16 +612,23 @@ __device__ void finish_band(FL& sh, FT& tl, uint32_t kk, const uint16_t* qt, con
   rescore_band<NT>(sh, tl, nb, qt, wt, kb, bsel);
   const uint32_t r = kk - sh.n_out;
   const uint32_t base_out = sh.n_out;
-  for (uint32_t i = threadIdx.x; i < nb; i += blockDim.x) {
-    const uint64_t ki = tl.band_key[i];
-    const uint32_t ii = sh.band_idx[i];
-    uint32_t rank = 0;
-#pragma unroll 4
-    for (uint32_t j = 0; j < nb; ++j) {
-      const uint64_t kj = tl.band_key[j];
-      rank += (kj > ki) | ((kj == ki) & (sh.band_idx[j] < ii));
+  // entry i's rank in the band (key descending, then index ascending) by a
+  // row of 16 lanes: lane g compares entries g, g + 16, ..., the row sums
+  const int g = threadIdx.x & 15;
+  for (uint32_t i0 = 0; i0 < nb; i0 += NT / 16) {
+    const uint32_t i = i0 + (threadIdx.x >> 4);
+    uint64_t ki = 0;
+    uint32_t ii = 0, rank = 0;
+    if (i < nb) {
+      ki = tl.band_key[i];
+      ii = sh.band_idx[i];
+      for (uint32_t j = g; j < nb; j += 16) {
+        const uint64_t kj = tl.band_key[j];
+        rank += (kj > ki) | ((kj == ki) & (sh.band_idx[j] < ii));
+      }
     }
-    if (rank < r) sh.out[base_out + rank] = ii;
+    rank = row_sum16_u32(rank);
+    if (i < nb && g == 0 && rank < r) sh.out[base_out + rank] = ii;
   }
   __syncthreads();
 }
@@ -1177,14 +1193,13 @@ __global__ __launch_bounds__(NT) void topk_rows_pf_kernel(
 // block per query over the scan of its pool.  The pool's P fp32 scores sit in
 // registers (P / kRxThreads per thread; 512 threads leave every wave 256
 // VGPRs, so nothing spills) and its entry ids in LDS.  One histogram of the
-// scores at or above the smallest per-thread maximum (kRxBins value bins, each
-// keeping its count and its smallest and largest score) brackets the k-th
-// largest fp32 score by the scores of its bin; the scores above the bracket's
-// band are in, those in it form the band, rescored in fp64 from the pool rows'
-// own bf16 values, and the selected pool positions are written as the entry
-// ids they hold, ascending (the pool is ascending, so position order is entry
-// order and the lower-index tie rule carries over).  Positions past the pool's
-// entry count are pad and never selected.
+// scores at or above the smallest per-thread maximum (kRxBins value bins)
+// brackets the k-th largest fp32 score by the float range of its bin; the
+// scores above the bracket's band are in, those in it form the band, rescored
+// in fp64 from the pool rows' own bf16 values, and the selected pool positions
+// are written as the entry ids they hold, ascending (the pool is ascending, so
+// position order is entry order and the lower-index tie rule carries over).
+// Positions past the pool's entry count are pad and never selected.
 constexpr int kRxThreads = 512;
 constexpr int kRxPer = CSA2_HSI_POOL / kRxThreads;
 constexpr int kRxBins = 2048;  // four per thread
@@ -1204,10 +1219,7 @@ struct PoolKeys {
 struct RxLds {
   FinLdsT<kPfBand> f;
   union {
-    struct {
-      uint32_t cnt[kRxBins];
-      uint32_t kmin[kRxBins], kmax[kRxBins];  // smallest / largest score key of each bin
-    } h;
+    uint32_t cnt[kRxBins];       // the histogram
     FinTailT<kPfBand, 32> tail;  // after the band is known
   } u;
   int32_t ent[CSA2_HSI_POOL];  // the pool's entry ids
@@ -1220,6 +1232,32 @@ struct RxLds {
 __device__ __forceinline__ uint32_t rx_bin(float x, float a, float scale) {
   const float f = (x - a) * scale;
   return f >= (float)(kRxBins - 1) ? (uint32_t)(kRxBins - 1) : (f > 0.f ? (uint32_t)f : 0u);
+}
+
+// The smallest float x in [a, mx] with rx_bin(x) >= b (0 < b < kRxBins), by
+// all 64 lanes of a wave: rx_bin is monotone in x, 0 at a and kRxBins - 1 at
+// mx, so a search over the float keys that keeps bin(lo) < b <= bin(hi) and
+// tries 64 evenly spaced keys per round ends at it.  The first interval is the
+// 64 floats around a + b / scale (a few floats from the answer when a >= 0),
+// else the whole range.
+__device__ float rx_edge(uint32_t b, float a, float scale, float mx) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t ka = f32_key(a), km = f32_key(mx);
+  const uint32_t ke = f32_key(fminf(fmaxf(a + (float)b / scale, a), mx));
+  uint32_t lo = ke - ka > 32u ? ke - 32u : ka;
+  uint32_t hi = km - ke > 32u ? ke + 32u : km;
+  if (!(rx_bin(key_f32(lo), a, scale) < b && rx_bin(key_f32(hi), a, scale) >= b)) { lo = ka; hi = km; }
+  while (hi - lo > 1u) {
+    const uint32_t step = (hi - lo) / 64u + 1u;
+    const uint32_t off = (uint32_t)(lane + 1) * step;
+    const uint32_t c = off < hi - lo ? lo + off : hi;
+    const uint64_t ge = __ballot(rx_bin(key_f32(c), a, scale) >= b);  // lane 63 (c = hi) always
+    const int f = __ffsll((unsigned long long)ge) - 1;
+    const uint32_t cf = (uint32_t)__builtin_amdgcn_readlane((int)c, f);
+    lo = f > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)c, f - 1) : lo;
+    hi = cf;
+  }
+  return key_f32(hi);
 }
 
 // keys: the gathered pool keys ([T][P][128] bf16, row = position) or, with
@@ -1257,11 +1295,7 @@ __global__ __launch_bounds__(kRxThreads) void reindex_select_kernel(
   double qf, sw;
   bound_terms(qt, wt, parts + (size_t)t * n_parts, n_parts, tid, kRxThreads, &m2, &qf, &sw);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    L.u.h.cnt[tid + i * kRxThreads] = 0u;
-    L.u.h.kmin[tid + i * kRxThreads] = 0xFFFFFFFFu;
-    L.u.h.kmax[tid + i * kRxThreads] = 0u;
-  }
+  for (int i = 0; i < 4; ++i) L.u.cnt[tid + i * kRxThreads] = 0u;
   if (tid == 0) { sh.n_out = 0; sh.n_band = 0; }
   // entry ids to LDS (the count of entries is the visible count: the pool is a
   // prefix); the thread's largest and smallest score
@@ -1307,67 +1341,70 @@ __global__ __launch_bounds__(kRxThreads) void reindex_select_kernel(
   // The histogram over [lo_h, mx]: when k threads hold a score, their maxima
   // put at least k scores at or above the smallest of them, l0; else every
   // finite score counts.  Bins are monotone in the score, so the k-th largest
-  // lies in the bin where the count from the top first reaches k.
+  // lies in the bin where the count from the top first reaches k, between the
+  // smallest float of that bin and the float below the next bin's smallest.
   const float lo_h = tthr >= kk ? l0 : gmin;
   const float scale = mx > lo_h ? ((float)kRxBins - 0.01f) / (mx - lo_h) : 0.f;
   if (tid == 0) { L.pick[0] = f32_key(lo_h); L.pick[1] = f32_key(mx); }  // the whole range until a bin is picked
 #pragma unroll
   for (int r = 0; r < kRxPer; ++r) {
-    if (v[r] >= lo_h) {
-      const uint32_t bin = rx_bin(v[r], lo_h, scale), key = f32_key(v[r]);
-      atomicAdd(&L.u.h.cnt[bin], 1u);
-      atomicMin(&L.u.h.kmin[bin], key);
-      atomicMax(&L.u.h.kmax[bin], key);
-    }
+    if (v[r] >= lo_h) atomicAdd(&L.u.cnt[rx_bin(v[r], lo_h, scale)], 1u);
   }
   __syncthreads();
   {
     // thread j owns bins kRxBins-1-4j .. kRxBins-4-4j (descending)
     uint32_t c[4], sum = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { c[i] = L.u.h.cnt[kRxBins - 1 - 4 * tid - i]; sum += c[i]; }
+    for (int i = 0; i < 4; ++i) { c[i] = L.u.cnt[kRxBins - 1 - 4 * tid - i]; sum += c[i]; }
     uint32_t tot;
     uint32_t cum = block_excl_scan(sum, L.wsum, &tot);
-    if (cum < kk && kk <= cum + sum) {
+    const bool mine = cum < kk && kk <= cum + sum;
+    uint32_t bin = 0u;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (cum < kk && kk <= cum + c[i]) {
-          const int bin = kRxBins - 1 - 4 * tid - i;
-          L.pick[0] = L.u.h.kmin[bin];
-          L.pick[1] = L.u.h.kmax[bin];
-        }
-        cum += c[i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      if (mine && cum < kk && kk <= cum + c[i]) bin = kRxBins - 1 - 4 * tid - i;
+      cum += c[i];
+    }
+    // the wave holding that bin finds its float range: [start(bin), start(bin + 1))
+    const uint64_t who = __ballot(mine);
+    if (who != 0ull && scale > 0.f) {
+      const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)bin, __ffsll((unsigned long long)who) - 1);
+      const float t_lo = b > 0u ? rx_edge(b, lo_h, scale, mx) : lo_h;
+      const float t_hi = b + 1u < (uint32_t)kRxBins ? key_f32(f32_key(rx_edge(b + 1u, lo_h, scale, mx)) - 1u) : mx;
+      if (lane == 0) { L.pick[0] = f32_key(t_lo); L.pick[1] = f32_key(t_hi); }
     }
   }
   __syncthreads();
   double lo, hi;
   band_bounds(key_f32(L.pick[0]), key_f32(L.pick[1]), eps, 0, &lo, &hi);
   // sure entries (above the band) and the band, placed by one block scan of
-  // the packed counts (each total is at most P < 2^16)
+  // the packed counts (each total is at most P < 2^16).  For a float x,
+  // x > hi exactly when x > hi rounded down to float, and x >= lo exactly when
+  // x >= lo rounded up.
   {
-    uint32_t ns = 0, nb = 0;
+    const float fhi = __double2float_rd(hi), flo = __double2float_ru(lo);
+    const uint32_t nvu = (uint32_t)nv;
+    uint32_t sb = 0u, bb = 0u;  // one bit per register: sure, band
 #pragma unroll
     for (int r = 0; r < kRxPer; ++r) {
-      const bool in = tid + r * kRxThreads < nv;
-      const double x = (double)v[r];
-      ns += (in && x > hi) ? 1u : 0u;
-      nb += (in && !(x > hi) && x >= lo) ? 1u : 0u;
+      const bool in = (uint32_t)(tid + r * kRxThreads) < nvu;
+      sb |= (in && v[r] > fhi ? 1u : 0u) << r;
+      bb |= (in && !(v[r] > fhi) && v[r] >= flo ? 1u : 0u) << r;
     }
     uint32_t tot;
-    const uint32_t pos = block_excl_scan(ns | (nb << 16), L.wsum2, &tot);
+    const uint32_t pos = block_excl_scan((uint32_t)__popc(sb) | ((uint32_t)__popc(bb) << 16), L.wsum2, &tot);
     uint32_t ps = pos & 0xFFFFu, pb = pos >> 16;
-#pragma unroll
-    for (int r = 0; r < kRxPer; ++r) {
-      const uint32_t i = tid + r * kRxThreads;
-      const double x = (double)v[r];
-      if ((int64_t)i < nv && x > hi) {
-        if (ps < kk) sh.out[ps] = i;  // fewer than k lie above the k-th's bin
-        ++ps;
-      } else if ((int64_t)i < nv && x >= lo) {
-        if (pb < (uint32_t)kPfBand) sh.band_idx[pb] = i;
-        ++pb;
-      }
+    while (sb != 0u) {
+      const int r = __builtin_ctz(sb);
+      sb &= sb - 1u;
+      if (ps < kk) sh.out[ps] = tid + r * kRxThreads;  // fewer than k lie above the k-th's bin
+      ++ps;
+    }
+    while (bb != 0u) {
+      const int r = __builtin_ctz(bb);
+      bb &= bb - 1u;
+      if (pb < (uint32_t)kPfBand) sh.band_idx[pb] = tid + r * kRxThreads;
+      ++pb;
     }
     if (tid == 0) { sh.n_out = tot & 0xFFFFu; sh.n_band = tot >> 16; }
   }
