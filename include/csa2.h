@@ -222,11 +222,12 @@ csa2_status csa2_hsi_pool(const float* tile_max, const uint32_t* stats, size_t s
  *  q_idx    bf16 [T][32][128], w_idx fp32 [T][32]: the Reindex layer's query
  *  k_idx    bf16 [B][N][128]: the shared indexer keys
  *  k        must be CSA2_TOPK;  indices int32 [T][k] out
- *  workspace >= csa2_reindex_workspace_bytes(T, k) (about 4.2 MiB per query:
- *           the gathered pool keys, their scores and the selection's summary)
- *  Runs a gather kernel, csa2_index over the gathered keys and a selection
- *  kernel within each pool (one block per query, writing entry ids), all on
- *  hip_stream.
+ *  workspace >= csa2_reindex_workspace_bytes(T, k) (about 4.2 MiB per query,
+ *           sized for csa2_reindex_mxfp4's dequantised copy of the pool keys;
+ *           this call uses only the pool's scores and their summary)
+ *  Runs the scan over each query's pool (key rows read through the pool; no
+ *  copy) and a selection kernel within each pool (one block per query,
+ *  writing entry ids), both on hip_stream.
  */
 size_t csa2_reindex_workspace_bytes(int32_t T, int32_t k);
 csa2_status csa2_reindex(const int32_t* pool, const void* q_idx, const float* w_idx, const void* k_idx,

@@ -57,7 +57,7 @@ def test_workspace_queries(L):
     # pool: per candidate block of 4096 entries one count and 512 (block, fp64 max) records
     assert csa.hsi_pool_workspace_bytes(4, 1 << 20) >= 4 * 256 * 512 * 12
     assert csa.hsi_pool_workspace_bytes(0, 1 << 20) == 0
-    # reindex: the gathered pool keys (16384 x 256 B per query) dominate
+    # reindex: the MXFP4 variant's dequantised pool keys (16384 x 256 B per query) dominate
     assert csa.reindex_workspace_bytes(4) >= 4 * csa.HSI_POOL * 256
     assert csa.reindex_workspace_bytes(4, 256) == 0
 
