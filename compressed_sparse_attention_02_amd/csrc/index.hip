@@ -252,6 +252,11 @@ __global__ __launch_bounds__(kScanThreads) void idx_scan32_kernel(
   const int64_t nchunks = (N + kChunkKeys - 1) / kChunkKeys;
   const uint16_t* kseq = k_idx + (size_t)b * N * kIdxDim;
   const int64_t last = (nvis_max < N ? (nvis_max > 0 ? nvis_max : 1) : N) - 1;  // last row worth reading
+  // Query group 0 bounds ||K_s||^2 over every key of its chunks, visible or
+  // not, and that bound stands for every group of the sequence (the others
+  // skip the norms): a bound over all keys bounds each query's visible ones.
+  const bool norms = blockIdx.z == 0;
+  const int64_t lastk = norms ? N - 1 : last;
   float maxn2 = 0.f;
   float gm[QG][S];
 #pragma unroll
@@ -266,13 +271,13 @@ __global__ __launch_bounds__(kScanThreads) void idx_scan32_kernel(
     // key s, channels 16j + 8(l/32) .. +7 of k-step j (keys past the end or
     // past every query's visibility re-read row `last`, already cached)
     uint4 kv[8];
-    const uint16_t* kp = kseq + (size_t)(s < last ? s : last) * kIdxDim + 8 * hf;
+    const uint16_t* kp = kseq + (size_t)(s < lastk ? s : lastk) * kIdxDim + 8 * hf;
 #pragma unroll
     for (int j = 0; j < 8; ++j) kv[j] = *reinterpret_cast<const uint4*>(kp + 16 * j);
     float sc[QG];
 #pragma unroll
     for (int qq = 0; qq < QG; ++qq) sc[qq] = -INFINITY;
-    if (base < nvis_max) {
+    if (norms) {
       // this lane's 64 channels of ||K_s||^2 (bf16 dot2); the block sums the two
       // channel halves' maxima over its keys, an upper bound of max_s ||K_s||^2
       float n2 = 0.f;
@@ -287,6 +292,8 @@ __global__ __launch_bounds__(kScanThreads) void idx_scan32_kernel(
         }
       }
       if (s < N) maxn2 = fmaxf(maxn2, n2);
+    }
+    if (base < nvis_max) {
 #pragma unroll
       for (int qq = 0; qq < QG; ++qq) {
         if (!valid[qq]) continue;
@@ -361,11 +368,12 @@ __global__ __launch_bounds__(kScanThreads) void idx_scan32_kernel(
       if (blockIdx.x == 0 && valid[qq] && lane < n_groups - used) group_max[trow[qq] * n_groups + used + lane] = -INFINITY;
     }
   }
-  if (threadIdx.x == 0) {
+  if (norms && wave == 0) {  // the same bound into every group's slot of this key range
     float m = red[0];
 #pragma unroll
     for (int i = 1; i < kScanWaves; ++i) m = fmaxf(m, red[i]);
-    norm_partial[((size_t)b * gridDim.z + blockIdx.z) * gridDim.x + blockIdx.x] = m;
+    for (int z = lane; z < (int)gridDim.z; z += 64)
+      norm_partial[((size_t)b * gridDim.z + z) * gridDim.x + blockIdx.x] = m;
   }
 }
 
