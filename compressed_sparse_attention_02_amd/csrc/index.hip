@@ -294,32 +294,41 @@ __global__ __launch_bounds__(kScanThreads) void idx_scan32_kernel(
       if (s < N) maxn2 = fmaxf(maxn2, n2);
     }
     if (base < nvis_max) {
-#pragma unroll
-      for (int qq = 0; qq < QG; ++qq) {
-        if (!valid[qq]) continue;
+      // The queries' products in two accumulators, one query ahead of its
+      // fold, so that query qq's fold (VALU) overlaps query qq + 1's MFMA
+      // chain.  A padding query (past q_per_seq) repeats the last query's
+      // row and is computed and discarded.
+      floatx16 acc[2];
+      const auto chain = [&](int qq, floatx16& a) {
         const uint16_t* qa = &sq[qq * kIdxHeads * kQRowPad] + col * kQRowPad + 8 * hf;
-        floatx16 acc = {};
+        a = floatx16{};
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qa + 16 * j),
-                                                        as_bf16x8(kv[j]), acc, 0, 0, 0);
+          a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qa + 16 * j),
+                                                      as_bf16x8(kv[j]), a, 0, 0, 0);
+      };
+      chain(0, acc[0]);
+#pragma unroll
+      for (int qq = 0; qq < QG; ++qq) {
+        if (qq + 1 < QG) chain(qq + 1, acc[(qq + 1) & 1]);
+        const floatx16& a = acc[qq & 1];
         // heads 8i + 4(l/32) + 0..3 sit in registers 4i .. 4i+3
         float p0 = 0.f, p1 = 0.f;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const float4 w0 = *reinterpret_cast<const float4*>(&sw[qq][8 * i + 4 * hf]);
           const float4 w1 = *reinterpret_cast<const float4*>(&sw[qq][8 * (i + 2) + 4 * hf]);
-          p0 = fmaf(w0.x, relu_bits(acc[4 * i]), p0);
-          p0 = fmaf(w0.y, relu_bits(acc[4 * i + 1]), p0);
-          p0 = fmaf(w0.z, relu_bits(acc[4 * i + 2]), p0);
-          p0 = fmaf(w0.w, relu_bits(acc[4 * i + 3]), p0);
-          p1 = fmaf(w1.x, relu_bits(acc[4 * i + 8]), p1);
-          p1 = fmaf(w1.y, relu_bits(acc[4 * i + 9]), p1);
-          p1 = fmaf(w1.z, relu_bits(acc[4 * i + 10]), p1);
-          p1 = fmaf(w1.w, relu_bits(acc[4 * i + 11]), p1);
+          p0 = fmaf(w0.x, relu_bits(a[4 * i]), p0);
+          p0 = fmaf(w0.y, relu_bits(a[4 * i + 1]), p0);
+          p0 = fmaf(w0.z, relu_bits(a[4 * i + 2]), p0);
+          p0 = fmaf(w0.w, relu_bits(a[4 * i + 3]), p0);
+          p1 = fmaf(w1.x, relu_bits(a[4 * i + 8]), p1);
+          p1 = fmaf(w1.y, relu_bits(a[4 * i + 9]), p1);
+          p1 = fmaf(w1.z, relu_bits(a[4 * i + 10]), p1);
+          p1 = fmaf(w1.w, relu_bits(a[4 * i + 11]), p1);
         }
         const float tot = sum_xor32(p0 + p1);
-        sc[qq] = (s < nvis[qq]) ? tot : -INFINITY;
+        sc[qq] = (valid[qq] && s < nvis[qq]) ? tot : -INFINITY;
       }
     }
     // Lanes 0..31 store keys base .. base + 31 (one 128-byte store); the tile
