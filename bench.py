@@ -58,24 +58,26 @@ def parse():
     return ap.parse_args()
 
 
-# Sources of the scan kernel: the recorded traffic holds only while they are unchanged (of the
-# public header, only its constants count: its documentation does not change the kernel).
+# Sources of the one-query scan kernel: the recorded traffic holds only while they and its compile
+# flags are unchanged (of the public header, only its constants count: its documentation does not
+# change the kernel).
 SCAN_SOURCES = ["compressed_sparse_attention_02_amd/csrc/index.hip", "compressed_sparse_attention_02_amd/csrc/idx_tile.h",
                 "compressed_sparse_attention_02_amd/csrc/idx_plan.h",
-                "compressed_sparse_attention_02_amd/csrc/csa2_common.h", "include/csa2.h",
-                "compressed_sparse_attention_02_amd/build.py"]
+                "compressed_sparse_attention_02_amd/csrc/csa2_common.h", "include/csa2.h"]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "idx_scan_kernel_long_decode_hbm_traffic.md")
 CAL_BYTES = 1 << 30          # bytes the calibration dispatch reads, and writes
 
 
 def scan_sources_sha256():
     import hashlib
+    from compressed_sparse_attention_02_amd import build as hip_build
     h = hashlib.sha256()
     for f in SCAN_SOURCES:
         data = open(os.path.join(ROOT, f), "rb").read()
         if f.endswith("csa2.h"):
             data = b"".join(l for l in data.splitlines(keepends=True) if l.lstrip().startswith(b"#define"))
         h.update(data)
+    h.update(repr((hip_build.FLAGS, hip_build.FILE_FLAGS.get("index.hip", []))).encode())
     return h.hexdigest()
 
 

@@ -10,7 +10,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa2.so")
-SOURCES = ["abi.hip", "index.hip", "index_mx.hip", "topk.hip", "reindex.hip", "attend.hip", "kvwrite.hip"]
+SOURCES = ["abi.hip", "index.hip", "index_group.hip", "index_mx.hip", "topk.hip", "reindex.hip", "attend.hip", "kvwrite.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Werror", "-Wno-unused-command-line-argument",
@@ -20,7 +20,7 @@ FLAGS = [
 # Per-source flags.  The grouped-query scan keeps its 32 x 32 MFMA accumulators in
 # VGPRs (by default the compiler puts them in AGPRs and copies each query's 16 values
 # out before the head fold; measured 4 % slower on the causal-prefill scan).
-FILE_FLAGS = {"index.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+FILE_FLAGS = {"index_group.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 # Host-side AddressSanitizer + UndefinedBehaviorSanitizer (the argument checks and launch code of

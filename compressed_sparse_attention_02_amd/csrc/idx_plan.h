@@ -59,6 +59,11 @@ inline bool index_plan(int32_t T, int32_t q_per_seq, int64_t N, IndexPlan* p) {
   return p->B <= 65535 && p->groups <= 65535;
 }
 
+// The grouped-query scan (index_group.hip): plans with p.qg >= 2.
+void launch_scan_grouped(const IndexPlan& p, hipStream_t st, const uint16_t* q, const float* w, const uint16_t* k,
+                         const int32_t* q_pos, int ratio, int q_per_seq, int64_t N, float* scores, float* tile_max,
+                         uint32_t* header, float* gmax, float* partial);
+
 // Word offsets of the summary's parts (all multiples of 4: 16-byte aligned).
 __host__ __device__ inline size_t stats_groups_off(int T) { return (size_t)T * CSA2_STATS_WORDS; }
 __host__ __device__ inline size_t stats_parts_off(int T, int64_t n_groups) {
