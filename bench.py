@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run torch.neg over 1 GiB of fp32 (reads and writes 1 GiB: the reference dispatch "
                          "that scales rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE to bytes)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
+                    help="KERNEL DIR...: per-dispatch means of every counter that rocprofv3 --pmc runs "
+                         "wrote under the DIRs, for the kernels whose name contains KERNEL")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
                     help="print the profile summary of rocprofv3 CSV output (kernel stats, the FETCH_SIZE run, the "
                          "WRITE_SIZE run and optionally the MFMA-counter run) instead of benchmarking")
@@ -96,6 +99,26 @@ def recorded_traffic():
         return float(fields["HBM bytes per launch"])
     except (KeyError, ValueError):
         return None
+
+
+def summarize_counters(kernel, dirs):
+    """Markdown table of the per-dispatch mean of each counter in rocprofv3 --pmc CSV output,
+    over the dispatches of the kernels whose name contains `kernel`."""
+    import csv
+    import glob
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(list))
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if kernel in r["Kernel_Name"]:
+                    vals[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    for name, cs in sorted(vals.items()):
+        print(f"### {name}\n\n| counter | per dispatch | dispatches |\n|---|---|---|")
+        for c, v in sorted(cs.items()):
+            print(f"| {c} | {sum(v) / len(v):.4g} | {len(v)} |")
+        print()
+    return 0
 
 
 def summarize(stats_dir, fetch_dir=None, write_dir=None, mfma_dir=None):
@@ -194,6 +217,8 @@ def main():
     args = parse()
     if args.summarize:
         return summarize(*args.summarize)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters[0], args.summarize_counters[1:])
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the data-parallel path would shard sequences across GPUs with no exchange", file=sys.stderr)
