@@ -570,6 +570,14 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 1 : CSA2_ATTN_WAVES_PER_SIMD) void
 constexpr int kCsThreads = 512;
 constexpr int kCsSlice = kDim / 8;  // output channels per wave
 
+// The bytes of one selected-row chunk (the kernel keeps two, each an LDS
+// object of its own, so that the compiler can tell the direct-to-LDS requests
+// into one from every other LDS access).
+struct CsRows {
+  alignas(16) uint8_t rawc[kChunk * 256];  // E2M1 codes, 16-byte pieces swizzled (cs_piece)
+  alignas(16) uint8_t raws[kChunk * 32];   // scales: 16 (MXFP4) or 32 (E4M3) bytes per row
+};
+
 struct CsShared {
   alignas(16) uint16_t xt[8][kCsSlice * kXTStride];  // per wave: channel c of its slice, 32 rows (k order)
   alignas(16) uint16_t x[kChunk * kXStride];          // window chunks: row-major rows (S operand)
@@ -579,6 +587,7 @@ struct CsShared {
   alignas(16) int grow[4];                            // head group G rescales this chunk
   float fin_m[kHeads], fin_l[kHeads];                 // final (max, sum) per head
   float rope[32][2];
+  int32_t idx[CSA2_TOPK];                             // the query's selected rows
 };
 
 // XT slice layout: row c (channel), four 16-byte blocks of 8 rows (k order),
@@ -601,77 +610,70 @@ __device__ __forceinline__ float max_xor32(float x) {
 // 4 ((l >> 3) & 1) + i), channels 64 w + 8 (l & 7) .. +7.
 __device__ __forceinline__ int cs_slice_row(int lane, int i) { return group_row(lane >> 4, 4 * ((lane >> 3) & 1) + i); }
 
-// Raw bytes of a chunk for one wave.  S layout, selected rows only (lane
-// (r, g), rows r and 16 + r, channels 256 (w >> 2) + 64 g .. +63): s[m][0..1]
-// the 32 code bytes, s[m][2].x the scale bytes (two E8M0 or four E4M3).
-// Slice layout: x[i] for row cs_slice_row(lane, i) (selected rows: code word,
-// scale byte; window rows: the 16-byte piece, or FP8 code bytes and scale).
+// Raw bytes of a window chunk for one wave, slice layout: x[i] for row
+// cs_slice_row(lane, i) (the 16-byte piece, or FP8 code bytes and scale).
 struct CsRaw {
-  uint4 s[2][3];
   uint4 x[4];
   uint32_t ok;  // bit r: row r of the chunk valid (the same in every lane)
 };
 
-struct CsIdx {
-  int32_t s[2], x[4];
-};
+// Selected-row chunks go through LDS: a chunk's 32 rows are requested with
+// one 16-byte piece per lane, each wave four whole rows of codes (whole cache
+// lines per request, every byte requested once), wave 0 also the rows'
+// scales, straight into LDS (global_load_lds_dwordx4: lane l's piece lands at
+// the wave's base + 16 l); every wave then reads its operands from there.
+// Piece p of row r sits in slot p ^ (r % 16), so that the sixteen rows an
+// operand read spans fall in distinct bank groups.
+__device__ __forceinline__ int cs_piece(int r, int p) { return r * 256 + 16 * (p ^ (r & 15)); }
 
-__device__ __forceinline__ void cs_load_indices(const AttnArgs& a, int t, int c, CsIdx& ix) {
-  if (c >= a.n_main) return;
-  const int lane = threadIdx.x & 63, r16 = lane & 15;
-  const int32_t* ip = a.indices + (size_t)t * a.k + c * kChunk;
-  ix.s[0] = ip[r16];
-  ix.s[1] = ip[16 + r16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) ix.x[i] = ip[cs_slice_row(lane, i)];
+template <int KVF>
+__device__ __forceinline__ void cs_issue_rows(const AttnArgs& a, const CsShared& sh, CsRows& rw, int b, int c) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = 4 * w + (lane >> 4);
+  const int32_t e = sh.idx[c * kChunk + r];
+  const size_t rowid = (size_t)b * a.N + (e >= 0 ? e : 0);  // invalid rows read row 0, masked later
+  __builtin_amdgcn_global_load_lds(a.kv_fp4 + rowid * 256 + 16 * ((lane & 15) ^ (r & 15)), &rw.rawc[w * 1024],
+                                   16, 0, 0);
+  if (w == 0) {
+    if (KVF == CSA2_KV_MXFP4) {
+      if (lane < kChunk) {
+        const int32_t es = sh.idx[c * kChunk + lane];
+        __builtin_amdgcn_global_load_lds(a.kv_scale + ((size_t)b * a.N + (es >= 0 ? es : 0)) * 16, &rw.raws[0],
+                                         16, 0, 0);
+      }
+    } else {
+      const int32_t es = sh.idx[c * kChunk + (lane >> 1)];
+      __builtin_amdgcn_global_load_lds(a.kv_scale + ((size_t)b * a.N + (es >= 0 ? es : 0)) * 32 + 16 * (lane & 1),
+                                       &rw.raws[0], 16, 0, 0);
+    }
+  }
 }
 
+// Every vector-memory request of this wave done (the row staging included).
+__device__ __forceinline__ void cs_wait_rows() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int KVF, int SWF>
-__device__ __forceinline__ void cs_load_raw(const AttnArgs& a, int t, int b, int c, int layer, const CsIdx& ix,
-                                            CsRaw& raw) {
+__device__ __forceinline__ void cs_load_raw(const AttnArgs& a, int t, int b, int c, int layer, CsRaw& raw) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int g = lane >> 4;
-  const int sc0 = 256 * (w >> 2) + 64 * g;       // S-layout channels sc0 .. sc0 + 63
   const int xc0 = kCsSlice * w + 8 * (lane & 7);  // slice-layout channels xc0 .. xc0 + 7
-  if (c < a.n_main) {
-    // row validity of the chunk from the S-layout indices (rows lane % 16 and 16 + lane % 16)
-    raw.ok = (uint32_t)(__ballot(ix.s[0] >= 0) & 0xFFFFull) | ((uint32_t)(__ballot(ix.s[1] >= 0) & 0xFFFFull) << 16);
+  const int we = a.swa_end[t];
+  const int ws = we - a.window > 0 ? we - a.window : 0;
+  const int row0 = ws + (c - a.n_main) * kChunk;
+  const size_t base = ((size_t)layer * a.B + b) * a.S;
+  const int last = we > 0 ? we - 1 : 0;
+  const int nvalid = we - row0 < 0 ? 0 : (we - row0 > kChunk ? kChunk : we - row0);  // rows row0 .. we-1
+  raw.ok = nvalid >= kChunk ? 0xFFFFFFFFu : (1u << nvalid) - 1u;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const size_t rowid = (size_t)b * a.N + (ix.s[m] >= 0 ? ix.s[m] : 0);
-      const uint4* cp = reinterpret_cast<const uint4*>(a.kv_fp4 + rowid * 256 + sc0 / 2);
-      raw.s[m][0] = cp[0];
-      raw.s[m][1] = cp[1];
-      raw.s[m][2].x = KVF == CSA2_KV_MXFP4
-                          ? (uint32_t)*reinterpret_cast<const uint16_t*>(a.kv_scale + rowid * 16 + sc0 / 32)
-                          : *reinterpret_cast<const uint32_t*>(a.kv_scale + rowid * 32 + sc0 / 16);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t rowid = (size_t)b * a.N + (ix.x[i] >= 0 ? ix.x[i] : 0);
-      raw.x[i].x = *reinterpret_cast<const uint32_t*>(a.kv_fp4 + rowid * 256 + xc0 / 2);
-      raw.x[i].y = KVF == CSA2_KV_MXFP4 ? a.kv_scale[rowid * 16 + xc0 / 32] : a.kv_scale[rowid * 32 + xc0 / 16];
-    }
-  } else {
-    const int we = a.swa_end[t];
-    const int ws = we - a.window > 0 ? we - a.window : 0;
-    const int row0 = ws + (c - a.n_main) * kChunk;
-    const size_t base = ((size_t)layer * a.B + b) * a.S;
-    const int last = we > 0 ? we - 1 : 0;
-    const int nvalid = we - row0 < 0 ? 0 : (we - row0 > kChunk ? kChunk : we - row0);  // rows row0 .. we-1
-    raw.ok = nvalid >= kChunk ? 0xFFFFFFFFu : (1u << nvalid) - 1u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = row0 + cs_slice_row(lane, i);
-      const size_t rr = base + (row < we ? row : last);
-      if (SWF == CSA2_SWA_BF16) {
-        raw.x[i] = *reinterpret_cast<const uint4*>(a.swa + rr * kDim + xc0);
-      } else if (xc0 >= 448) {
-        raw.x[i] = *reinterpret_cast<const uint4*>(a.swa_rope + rr * 64 + (xc0 - 448));
-      } else {
-        const uint2 cw = *reinterpret_cast<const uint2*>(a.swa_fp8 + rr * 448 + xc0);
-        raw.x[i] = make_uint4(cw.x, cw.y, a.swa_sc[rr * 8 + xc0 / 64], 0u);
-      }
+  for (int i = 0; i < 4; ++i) {
+    const int row = row0 + cs_slice_row(lane, i);
+    const size_t rr = base + (row < we ? row : last);
+    if (SWF == CSA2_SWA_BF16) {
+      raw.x[i] = *reinterpret_cast<const uint4*>(a.swa + rr * kDim + xc0);
+    } else if (xc0 >= 448) {
+      raw.x[i] = *reinterpret_cast<const uint4*>(a.swa_rope + rr * 64 + (xc0 - 448));
+    } else {
+      const uint2 cw = *reinterpret_cast<const uint2*>(a.swa_fp8 + rr * 448 + xc0);
+      raw.x[i] = make_uint4(cw.x, cw.y, a.swa_sc[rr * 8 + xc0 / 64], 0u);
     }
   }
 }
@@ -679,16 +681,20 @@ __device__ __forceinline__ void cs_load_raw(const AttnArgs& a, int t, int b, int
 // The wave's transposed slice of chunk c into LDS; for window chunks also its
 // part of the row-major copy.
 template <int KVF, int SWF>
-__device__ __forceinline__ void cs_store_slice(const AttnArgs& a, CsShared& sh, int c, const CsRaw& raw) {
+__device__ __forceinline__ void cs_store_slice(const AttnArgs& a, CsShared& sh, const CsRows& rw, int c,
+                                               const CsRaw& raw) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int cg = lane & 7, kb = lane >> 3;
   const int xc0 = kCsSlice * w + 8 * cg;
+  const int q = 2 * w + (cg >> 2);  // code piece of channels xc0 .. xc0 + 7 (and their MXFP4 scale block)
   uint32_t v[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     uint4 o;
     if (c < a.n_main) {
-      o = KVF == CSA2_KV_MXFP4 ? dequant8(raw.x[i].x, raw.x[i].y) : dequant8_e4m3(raw.x[i].x, raw.x[i].y);
+      const int r = cs_slice_row(lane, i);
+      const uint32_t cw = *reinterpret_cast<const uint32_t*>(&rw.rawc[cs_piece(r, q) + 4 * (cg & 3)]);
+      o = KVF == CSA2_KV_MXFP4 ? dequant8(cw, rw.raws[r * 16 + q]) : dequant8_e4m3(cw, rw.raws[r * 32 + 4 * w + (cg >> 1)]);
     } else if (SWF == CSA2_SWA_BF16 || xc0 >= 448) {
       o = raw.x[i];
     } else {
@@ -725,11 +731,26 @@ __device__ __forceinline__ void cs_store_slice(const AttnArgs& a, CsShared& sh, 
 // operands of selected-row chunks from the raw S-layout bytes, of window
 // chunks from the row-major LDS copy (rows r and 16 + r, channels sc0 + 8 j).
 template <int KVF, bool WIN>
-__device__ __forceinline__ void cs_s_product(const CsShared& sh, const CsRaw& raw, const bf16x8 (&qb)[8],
+__device__ __forceinline__ void cs_s_product(const CsShared& sh, const CsRows& rw, const bf16x8 (&qb)[8],
                                              floatx4 (&acc)[2], int sc0) {
   const int r16 = threadIdx.x & 15;
   acc[0] = floatx4{0.f, 0.f, 0.f, 0.f};
   acc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // selected rows: lane (r, g) reads rows r and 16 + r, code pieces sc0 / 32 and + 1 (channels sc0 .. + 63)
+  // and their scale bytes (two E8M0 or four E4M3)
+  uint32_t cw[2][8], ss[2];
+  if (!WIN) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int r = 16 * m + r16;
+      const uint4 c0 = *reinterpret_cast<const uint4*>(&rw.rawc[cs_piece(r, sc0 / 32)]);
+      const uint4 c1 = *reinterpret_cast<const uint4*>(&rw.rawc[cs_piece(r, sc0 / 32 + 1)]);
+      cw[m][0] = c0.x; cw[m][1] = c0.y; cw[m][2] = c0.z; cw[m][3] = c0.w;
+      cw[m][4] = c1.x; cw[m][5] = c1.y; cw[m][6] = c1.z; cw[m][7] = c1.w;
+      ss[m] = KVF == CSA2_KV_MXFP4 ? (uint32_t)*reinterpret_cast<const uint16_t*>(&rw.raws[r * 16 + sc0 / 32])
+                                   : *reinterpret_cast<const uint32_t*>(&rw.raws[r * 32 + sc0 / 16]);
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
 #pragma unroll
@@ -738,10 +759,8 @@ __device__ __forceinline__ void cs_s_product(const CsShared& sh, const CsRaw& ra
       if (WIN) {
         av = lds_read16(&sh.x[(16 * m + r16) * kXStride + sc0 + 8 * j]);
       } else {
-        const uint32_t* cw = reinterpret_cast<const uint32_t*>(&raw.s[m][0]);
-        const uint32_t sb = KVF == CSA2_KV_MXFP4 ? (raw.s[m][2].x >> (8 * (j >> 2))) & 255u
-                                                 : (raw.s[m][2].x >> (8 * (j >> 1))) & 255u;
-        av = as_bf16x8(KVF == CSA2_KV_MXFP4 ? dequant8(cw[j], sb) : dequant8_e4m3(cw[j], sb));
+        const uint32_t sb = KVF == CSA2_KV_MXFP4 ? (ss[m] >> (8 * (j >> 2))) & 255u : (ss[m] >> (8 * (j >> 1))) & 255u;
+        av = as_bf16x8(KVF == CSA2_KV_MXFP4 ? dequant8(cw[m][j], sb) : dequant8_e4m3(cw[m][j], sb));
       }
       acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[j], acc[m], 0, 0, 0);
     }
@@ -759,6 +778,7 @@ struct CsState {
 template <int KVF, int SWF, bool FINAL>
 __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
   __shared__ CsShared sh;
+  __shared__ CsRows rows0, rows1;
   const int item = blockIdx.x, t = blockIdx.y, layer = blockIdx.z;
   const int b = t / a.q_per_seq;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -773,11 +793,12 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
     sh.rope[threadIdx.x][0] = cv;
     sh.rope[threadIdx.x][1] = sv;
   }
-  CsIdx ix;
+  // the query's selected rows (one coalesced load), then the first chunk's bytes
+  for (int i = threadIdx.x; i < a.n_main * kChunk; i += kCsThreads) sh.idx[i] = a.indices[(size_t)t * a.k + i];
+  __syncthreads();
   CsRaw raw;
-  cs_load_indices(a, t, c0, ix);
-  cs_load_raw<KVF, SWF>(a, t, b, c0, layer, ix, raw);
-  if (c0 + 1 < c1) cs_load_indices(a, t, c0 + 1, ix);
+  if (c0 < a.n_main) cs_issue_rows<KVF>(a, sh, rows0, b, c0);
+  else cs_load_raw<KVF, SWF>(a, t, b, c0, layer, raw);
   // the query operand: head 16 hg + r16, channels sc0 + 8 j .. + 8
   bf16x8 qb[8];
   {
@@ -794,86 +815,101 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
   st.m = -INFINITY;
   st.l = 0.f;
   st.started = false;
+  // The rows of selected-row chunk c are requested two chunks ahead, into the
+  // buffer chunk c - 2 used (consumed before the barrier that precedes the
+  // request), and every wave waits for its own requests before the barrier
+  // ahead of the chunk; window chunks are loaded into registers one chunk ahead.
+  cs_wait_rows();
+  __syncthreads();
+  if (c0 + 1 < c1 && c0 + 1 < a.n_main) cs_issue_rows<KVF>(a, sh, rows1, b, c0 + 1);
 
-  for (int c = c0; c < c1; ++c) {
-    cs_store_slice<KVF, SWF>(a, sh, c, raw);
-    const uint32_t ok = __builtin_amdgcn_readfirstlane(raw.ok);  // this chunk's valid rows
-    floatx4 acc[2];
-    if (c < a.n_main) {
-      cs_s_product<KVF, false>(sh, raw, qb, acc, sc0);
-    } else {
-      __syncthreads();  // the window rows of every wave in sh.x
-      cs_s_product<KVF, true>(sh, raw, qb, acc, sc0);
-    }
-    if (h == 1) {  // the second half's partial S, for the first half's softmax
-      sh.sx[w][0][lane] = acc[0];
-      sh.sx[w][1][lane] = acc[1];
-    }
-    if (c + 1 < c1) {
-      cs_load_raw<KVF, SWF>(a, t, b, c + 1, layer, ix, raw);
-      if (c + 2 < c1) cs_load_indices(a, t, c + 2, ix);
-    }
-    __syncthreads();
-    // Softmax of head group hg by its first-half wave only (the second half's
-    // partial S is all it contributes; it takes P and the rescale state from LDS).
-    if (h == 0) {
-      // full S^T of the group's 16 heads (own + partner half)
-      acc[0] += sh.sx[w ^ 4][0][lane];
-      acc[1] += sh.sx[w ^ 4][1][lane];
-      // acc[m][i]: row 16 m + 4 g + i, head 16 hg + r16
-      float z[8];
-      const uint32_t okg = ok >> (4 * g);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        z[i] = ((okg >> i) & 1u) ? acc[0][i] * a.scale_log2 : -INFINITY;
-        z[4 + i] = ((okg >> (16 + i)) & 1u) ? acc[1][i] * a.scale_log2 : -INFINITY;
+  // One chunk: its rows in `cur` (selected rows), which then receives chunk c + 2.
+  const auto chunk = [&](int c, CsRows& cur) {
+      cs_store_slice<KVF, SWF>(a, sh, cur, c, raw);
+      uint32_t ok;  // this chunk's valid rows
+      floatx4 acc[2];
+      if (c < a.n_main) {
+        ok = (uint32_t)__ballot(lane < kChunk && sh.idx[c * kChunk + (lane & (kChunk - 1))] >= 0);
+        cs_s_product<KVF, false>(sh, cur, qb, acc, sc0);
+      } else {
+        ok = __builtin_amdgcn_readfirstlane(raw.ok);
+        __syncthreads();  // the window rows of every wave in sh.x
+        cs_s_product<KVF, true>(sh, cur, qb, acc, sc0);
       }
-      float cm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-      cm = max_xor16(cm);
-      cm = max_xor32(cm);
-      // lazy rescaling: the reference maximum stays while the chunk's scores
-      // exceed it by at most kRescaleSlack (log2 units)
-      const float mtrue = fmaxf(st.m, cm);
-      const bool grow = mtrue > st.m + kRescaleSlack;
-      const float mn = grow ? mtrue : st.m;
-      const float alpha = grow ? exp2f(st.m - mn) : 1.f;
-      uint32_t pb[4];
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = z[2 * i] == -INFINITY ? 0.f : exp2f(z[2 * i] - mn);
-        const float p1 = z[2 * i + 1] == -INFINITY ? 0.f : exp2f(z[2 * i + 1] - mn);
-        psum += p0 + p1;
-        pb[i] = pack_bf16x2_rne(p0, p1);
+      if (h == 1) {  // the second half's partial S, for the first half's softmax
+        sh.sx[w][0][lane] = acc[0];
+        sh.sx[w][1][lane] = acc[1];
       }
-      st.l = st.l * alpha + psum;
-      st.m = mn;
-      bf16x8 pv;
-      __builtin_memcpy(&pv, pb, 16);
-      sh.p[hg][lane] = pv;
-      if (g == 0) sh.alpha[16 * hg + r16] = alpha;
-      const bool any = __ballot(grow) != 0ull;
-      if (lane == 0) sh.grow[hg] = any ? 1 : 0;
-    }
-    __syncthreads();
-    // O^T of this wave's channels, all four head groups
-    const int4 grows = *reinterpret_cast<const int4*>(sh.grow);
-    const int grw[4] = {grows.x, grows.y, grows.z, grows.w};
-#pragma unroll
-    for (int G = 0; G < 4; ++G) {
-      if (st.started && grw[G]) {
-        const float al = sh.alpha[16 * G + r16];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) st.o[mb][G] *= al;
+      if (c + 1 < c1 && c + 1 >= a.n_main) cs_load_raw<KVF, SWF>(a, t, b, c + 1, layer, raw);
+      __syncthreads();
+      // Softmax of head group hg by its first-half wave only (the second half's
+      // partial S is all it contributes; it takes P and the rescale state from LDS).
+      if (h == 0) {
+        // full S^T of the group's 16 heads (own + partner half)
+        acc[0] += sh.sx[w ^ 4][0][lane];
+        acc[1] += sh.sx[w ^ 4][1][lane];
+        // acc[m][i]: row 16 m + 4 g + i, head 16 hg + r16
+        float z[8];
+        const uint32_t okg = ok >> (4 * g);
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          z[i] = ((okg >> i) & 1u) ? acc[0][i] * a.scale_log2 : -INFINITY;
+          z[4 + i] = ((okg >> (16 + i)) & 1u) ? acc[1][i] * a.scale_log2 : -INFINITY;
+        }
+        float cm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+        cm = max_xor16(cm);
+        cm = max_xor32(cm);
+        // lazy rescaling: the reference maximum stays while the chunk's scores
+        // exceed it by at most kRescaleSlack (log2 units)
+        const float mtrue = fmaxf(st.m, cm);
+        const bool grow = mtrue > st.m + kRescaleSlack;
+        const float mn = grow ? mtrue : st.m;
+        const float alpha = grow ? exp2f(st.m - mn) : 1.f;
+        uint32_t pb[4];
+        float psum = 0.f;
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p0 = z[2 * i] == -INFINITY ? 0.f : exp2f(z[2 * i] - mn);
+          const float p1 = z[2 * i + 1] == -INFINITY ? 0.f : exp2f(z[2 * i + 1] - mn);
+          psum += p0 + p1;
+          pb[i] = pack_bf16x2_rne(p0, p1);
+        }
+        st.l = st.l * alpha + psum;
+        st.m = mn;
+        bf16x8 pv;
+        __builtin_memcpy(&pv, pb, 16);
+        sh.p[hg][lane] = pv;
+        if (g == 0) sh.alpha[16 * hg + r16] = alpha;
+        const bool any = __ballot(grow) != 0ull;
+        if (lane == 0) sh.grow[hg] = any ? 1 : 0;
       }
-      const bf16x8 pv = sh.p[G][lane];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const bf16x8 xa = lds_read16(&sh.xt[w][cs_xt_off(16 * mb + r16, g)]);
-        st.o[mb][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, pv, st.o[mb][G], 0, 0, 0);
+      cs_wait_rows();  // the next chunk's rows (requested a chunk ago) are in LDS
+      __syncthreads();
+      if (c + 2 < c1 && c + 2 < a.n_main) cs_issue_rows<KVF>(a, sh, cur, b, c + 2);
+      // O^T of this wave's channels, all four head groups
+      const int4 grows = *reinterpret_cast<const int4*>(sh.grow);
+      const int grw[4] = {grows.x, grows.y, grows.z, grows.w};
+  #pragma unroll
+      for (int G = 0; G < 4; ++G) {
+        if (st.started && grw[G]) {
+          const float al = sh.alpha[16 * G + r16];
+  #pragma unroll
+          for (int mb = 0; mb < 4; ++mb) st.o[mb][G] *= al;
+        }
+        const bf16x8 pv = sh.p[G][lane];
+  #pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const bf16x8 xa = lds_read16(&sh.xt[w][cs_xt_off(16 * mb + r16, g)]);
+          st.o[mb][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, pv, st.o[mb][G], 0, 0, 0);
+        }
       }
-    }
-    st.started = true;
+      st.started = true;
+  };
+  // chunks c0, c0 + 2, ... use rows0, the others rows1 (two LDS objects: the requests into one
+  // never make the compiler wait before reads of the other)
+  for (int c = c0; c < c1; c += 2) {
+    chunk(c, rows0);
+    if (c + 1 < c1) chunk(c + 1, rows1);
   }
   // (max, sum) of each head from its publishing wave
   {
