@@ -84,8 +84,8 @@ __device__ __forceinline__ int block_layer() { return W == 1 ? (int)(blockIdx.z 
 // Two fp32 values rounded to nearest-even bf16 and packed, lo in the low half
 // (one v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // Split-K partial slot layout: 64 heads x 512 channels as 16 x 16 tiles,
@@ -585,7 +585,7 @@ struct CsShared {
   alignas(16) bf16x8 p[4][64];                        // P^T of head group G, B-operand layout
   float alpha[kHeads];                                // this chunk's rescale factor per head
   alignas(16) int grow[4];                            // head group G rescales this chunk
-  float fin_m[kHeads], fin_l[kHeads];                 // final (max, sum) per head
+  float fin_m[kHeads], fin_l[kHeads][2];              // final max, and sum of each half's rows, per head
   float rope[32][2];
   int32_t idx[CSA2_TOPK];                             // the query's selected rows
 };
@@ -678,11 +678,11 @@ __device__ __forceinline__ void cs_load_raw(const AttnArgs& a, int t, int b, int
   }
 }
 
-// The wave's transposed slice of chunk c into LDS; for window chunks also its
-// part of the row-major copy.
-template <int KVF, int SWF>
-__device__ __forceinline__ void cs_store_slice(const AttnArgs& a, CsShared& sh, const CsRows& rw, int c,
-                                               const CsRaw& raw) {
+// The wave's transposed slice of a chunk into LDS (selected rows from `rw`,
+// window rows from `raw`); for window chunks (WIN) also its part of the
+// row-major copy.
+template <int KVF, int SWF, bool WIN>
+__device__ __forceinline__ void cs_store_slice(const AttnArgs& a, CsShared& sh, const CsRows& rw, const CsRaw& raw) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int cg = lane & 7, kb = lane >> 3;
   const int xc0 = kCsSlice * w + 8 * cg;
@@ -691,7 +691,7 @@ __device__ __forceinline__ void cs_store_slice(const AttnArgs& a, CsShared& sh, 
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     uint4 o;
-    if (c < a.n_main) {
+    if (!WIN) {
       const int r = cs_slice_row(lane, i);
       const uint32_t cw = *reinterpret_cast<const uint32_t*>(&rw.rawc[cs_piece(r, q) + 4 * (cg & 3)]);
       o = KVF == CSA2_KV_MXFP4 ? dequant8(cw, rw.raws[r * 16 + q]) : dequant8_e4m3(cw, rw.raws[r * 32 + 4 * w + (cg >> 1)]);
@@ -706,7 +706,7 @@ __device__ __forceinline__ void cs_store_slice(const AttnArgs& a, CsShared& sh, 
     }
     v[i][0] = o.x; v[i][1] = o.y; v[i][2] = o.z; v[i][3] = o.w;
   }
-  if (c >= a.n_main) {
+  if (WIN) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<uint4*>(&sh.x[cs_slice_row(lane, i) * kXStride + xc0]) =
@@ -771,7 +771,11 @@ struct CsState {
   floatx4 o[4][4];  // O^T: o[mb][G][i] = O[16 G + lane % 16][64 w + 16 mb + 4 (lane / 16) + i]
   float m;          // running max (log2 units) of head 16 (w & 3) + lane % 16
   float l;          // running sum over this lane's rows
-  bool started;     // o holds something
+};
+
+template <bool B>
+struct CsWin {
+  static constexpr bool value = B;
 };
 
 // grid (n_items, T, L), 512 threads; chunks and outputs as attend_kernel.
@@ -793,8 +797,12 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
     sh.rope[threadIdx.x][0] = cv;
     sh.rope[threadIdx.x][1] = sv;
   }
-  // the query's selected rows (one coalesced load), then the first chunk's bytes
+  // the query's selected rows (one coalesced load), then the first chunk's
+  // bytes; the O^T operands of the (empty) chunk before the first are zeros
   for (int i = threadIdx.x; i < a.n_main * kChunk; i += kCsThreads) sh.idx[i] = a.indices[(size_t)t * a.k + i];
+  for (int i = lane; i < kCsSlice * kXTStride / 8; i += 64) reinterpret_cast<uint4*>(sh.xt[w])[i] = uint4{0u, 0u, 0u, 0u};
+  if (threadIdx.x < 4 * 64) reinterpret_cast<uint4*>(&sh.p[0][0])[threadIdx.x] = uint4{0u, 0u, 0u, 0u};
+  if (threadIdx.x < 4) sh.grow[threadIdx.x] = 0;
   __syncthreads();
   CsRaw raw;
   if (c0 < a.n_main) cs_issue_rows<KVF>(a, sh, rows0, b, c0);
@@ -814,7 +822,6 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
     for (int G = 0; G < 4; ++G) st.o[mb][G] = floatx4{0.f, 0.f, 0.f, 0.f};
   st.m = -INFINITY;
   st.l = 0.f;
-  st.started = false;
   // The rows of selected-row chunk c are requested two chunks ahead, into the
   // buffer chunk c - 2 used (consumed before the barrier that precedes the
   // request), and every wave waits for its own requests before the barrier
@@ -823,12 +830,43 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
   __syncthreads();
   if (c0 + 1 < c1 && c0 + 1 < a.n_main) cs_issue_rows<KVF>(a, sh, rows1, b, c0 + 1);
 
-  // One chunk: its rows in `cur` (selected rows), which then receives chunk c + 2.
-  const auto chunk = [&](int c, CsRows& cur) {
-      cs_store_slice<KVF, SWF>(a, sh, cur, c, raw);
+  // O^T of the previous chunk, all four head groups of this wave's channels:
+  // its slice in sh.xt (this wave's own), its P^T, rescale factors and flags
+  // from that chunk's softmax.  Before the first chunk the slice and P^T are
+  // zeros and no group rescales.
+  const auto o_phase = [&]() {
+    const int4 grows = *reinterpret_cast<const int4*>(sh.grow);
+    const int grw[4] = {grows.x, grows.y, grows.z, grows.w};
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      if (grw[G]) {
+        const float al = sh.alpha[16 * G + r16];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) st.o[mb][G] *= al;
+      }
+    }
+    bf16x8 xa[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) xa[mb] = lds_read16(&sh.xt[w][cs_xt_off(16 * mb + r16, g)]);
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      const bf16x8 pv = sh.p[G][lane];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) st.o[mb][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mb], pv, st.o[mb][G], 0, 0, 0);
+    }
+  };
+
+  // One chunk c: the previous chunk's O^T, this chunk's slice and S^T, its
+  // softmax.  Selected rows (WIN false) come from `cur`, which then receives
+  // chunk c + 2; window rows from `raw`, loaded one chunk ahead.  The O^T
+  // products overlap this chunk's staging: the two need different units.
+  const auto chunk = [&](auto win, int c, CsRows& cur) {
+      constexpr bool WIN = decltype(win)::value;
+      o_phase();
+      cs_store_slice<KVF, SWF, WIN>(a, sh, cur, raw);
       uint32_t ok;  // this chunk's valid rows
       floatx4 acc[2];
-      if (c < a.n_main) {
+      if (!WIN) {
         ok = (uint32_t)__ballot(lane < kChunk && sh.idx[c * kChunk + (lane & (kChunk - 1))] >= 0);
         cs_s_product<KVF, false>(sh, cur, qb, acc, sc0);
       } else {
@@ -836,25 +874,33 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
         __syncthreads();  // the window rows of every wave in sh.x
         cs_s_product<KVF, true>(sh, cur, qb, acc, sc0);
       }
-      if (h == 1) {  // the second half's partial S, for the first half's softmax
-        sh.sx[w][0][lane] = acc[0];
-        sh.sx[w][1][lane] = acc[1];
-      }
+      // each half's partial S, for both halves' softmax
+      sh.sx[w][0][lane] = acc[0];
+      sh.sx[w][1][lane] = acc[1];
       if (c + 1 < c1 && c + 1 >= a.n_main) cs_load_raw<KVF, SWF>(a, t, b, c + 1, layer, raw);
       __syncthreads();
-      // Softmax of head group hg by its first-half wave only (the second half's
-      // partial S is all it contributes; it takes P and the rescale state from LDS).
-      if (h == 0) {
-        // full S^T of the group's 16 heads (own + partner half)
+      // Softmax of head group hg: both halves form the full S^T (own + partner
+      // partial, the same sums in either order) and the same maximum and
+      // rescale state; half h forms the probabilities of rows 16 h + 4 g + i
+      // and keeps the sum of its own rows.
+      {
         acc[0] += sh.sx[w ^ 4][0][lane];
         acc[1] += sh.sx[w ^ 4][1][lane];
         // acc[m][i]: row 16 m + 4 g + i, head 16 hg + r16
         float z[8];
-        const uint32_t okg = ok >> (4 * g);
+        if (ok == 0xFFFFFFFFu) {
   #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          z[i] = ((okg >> i) & 1u) ? acc[0][i] * a.scale_log2 : -INFINITY;
-          z[4 + i] = ((okg >> (16 + i)) & 1u) ? acc[1][i] * a.scale_log2 : -INFINITY;
+          for (int i = 0; i < 4; ++i) {
+            z[i] = acc[0][i] * a.scale_log2;
+            z[4 + i] = acc[1][i] * a.scale_log2;
+          }
+        } else {
+          const uint32_t okg = ok >> (4 * g);
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            z[i] = ((okg >> i) & 1u) ? acc[0][i] * a.scale_log2 : -INFINITY;
+            z[4 + i] = ((okg >> (16 + i)) & 1u) ? acc[1][i] * a.scale_log2 : -INFINITY;
+          }
         }
         float cm = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
         cm = max_xor16(cm);
@@ -865,60 +911,45 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
         const bool grow = mtrue > st.m + kRescaleSlack;
         const float mn = grow ? mtrue : st.m;
         const float alpha = grow ? exp2f(st.m - mn) : 1.f;
-        uint32_t pb[4];
-        float psum = 0.f;
+        // 2^(z - mn) by v_exp_f32 (masked scores -inf give 0; mn is -inf only
+        // while every score so far is masked)
+        const float mref = mn == -INFINITY ? 0.f : mn;
+        float p[4];
   #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p0 = z[2 * i] == -INFINITY ? 0.f : exp2f(z[2 * i] - mn);
-          const float p1 = z[2 * i + 1] == -INFINITY ? 0.f : exp2f(z[2 * i + 1] - mn);
-          psum += p0 + p1;
-          pb[i] = pack_bf16x2_rne(p0, p1);
-        }
-        st.l = st.l * alpha + psum;
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f((h == 0 ? z[i] : z[4 + i]) - mref);
+        st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
         st.m = mn;
-        bf16x8 pv;
-        __builtin_memcpy(&pv, pb, 16);
-        sh.p[hg][lane] = pv;
-        if (g == 0) sh.alpha[16 * hg + r16] = alpha;
+        reinterpret_cast<u32x2*>(&sh.p[hg][lane])[h] = u32x2{pack_bf16x2_rne(p[0], p[1]), pack_bf16x2_rne(p[2], p[3])};
         const bool any = __ballot(grow) != 0ull;
-        if (lane == 0) sh.grow[hg] = any ? 1 : 0;
+        if (h == 0) {
+          if (g == 0) sh.alpha[16 * hg + r16] = alpha;
+          if (lane == 0) sh.grow[hg] = any ? 1 : 0;
+        }
       }
-      cs_wait_rows();  // the next chunk's rows (requested a chunk ago) are in LDS
+      if (!WIN) cs_wait_rows();  // the next chunk's rows (requested a chunk ago) are in LDS
       __syncthreads();
-      if (c + 2 < c1 && c + 2 < a.n_main) cs_issue_rows<KVF>(a, sh, cur, b, c + 2);
-      // O^T of this wave's channels, all four head groups
-      const int4 grows = *reinterpret_cast<const int4*>(sh.grow);
-      const int grw[4] = {grows.x, grows.y, grows.z, grows.w};
-  #pragma unroll
-      for (int G = 0; G < 4; ++G) {
-        if (st.started && grw[G]) {
-          const float al = sh.alpha[16 * G + r16];
-  #pragma unroll
-          for (int mb = 0; mb < 4; ++mb) st.o[mb][G] *= al;
-        }
-        const bf16x8 pv = sh.p[G][lane];
-  #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          const bf16x8 xa = lds_read16(&sh.xt[w][cs_xt_off(16 * mb + r16, g)]);
-          st.o[mb][G] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, pv, st.o[mb][G], 0, 0, 0);
-        }
-      }
-      st.started = true;
+      if (!WIN && c + 2 < c1 && c + 2 < a.n_main) cs_issue_rows<KVF>(a, sh, cur, b, c + 2);
   };
-  // chunks c0, c0 + 2, ... use rows0, the others rows1 (two LDS objects: the requests into one
-  // never make the compiler wait before reads of the other)
-  for (int c = c0; c < c1; c += 2) {
-    chunk(c, rows0);
-    if (c + 1 < c1) chunk(c + 1, rows1);
+  // selected-row chunks alternate between rows0 and rows1 (two LDS objects:
+  // the requests into one never make the compiler wait before reads of the
+  // other), then the window chunks
+  const int cs_end = c1 < a.n_main ? c1 : a.n_main;
+  int c = c0;
+  for (; c + 1 < cs_end; c += 2) {
+    chunk(CsWin<false>(), c, rows0);
+    chunk(CsWin<false>(), c + 1, rows1);
   }
-  // (max, sum) of each head from its publishing wave
+  if (c < cs_end) chunk(CsWin<false>(), c++, rows0);
+  for (; c < c1; ++c) chunk(CsWin<true>(), c, rows0);
+  o_phase();
+  // max of each head (the same in both halves), sum of each half's rows
   {
     float l = st.l;
     l = sum_xor16(l);
     l = sum_xor32(l);
-    if (h == 0 && g == 0) {
-      sh.fin_m[16 * hg + r16] = st.m;
-      sh.fin_l[16 * hg + r16] = l;
+    if (g == 0) {
+      if (h == 0) sh.fin_m[16 * hg + r16] = st.m;
+      sh.fin_l[16 * hg + r16][h] = l;
     }
   }
   __syncthreads();
@@ -927,7 +958,7 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
   for (int G = 0; G < 4; ++G) {
     const int head = 16 * G + r16;
     float m = sh.fin_m[head];
-    const float l = sh.fin_l[head];
+    const float l = sh.fin_l[head][0] + sh.fin_l[head][1];
     if (FINAL) {
       float den = l, f = 1.f;
       if (a.sink) {
