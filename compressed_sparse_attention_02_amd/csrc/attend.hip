@@ -774,7 +774,7 @@ struct CsState {
 };
 
 template <bool B>
-struct CsWin {
+struct CsFlag {
   static constexpr bool value = B;
 };
 
@@ -797,12 +797,8 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
     sh.rope[threadIdx.x][0] = cv;
     sh.rope[threadIdx.x][1] = sv;
   }
-  // the query's selected rows (one coalesced load), then the first chunk's
-  // bytes; the O^T operands of the (empty) chunk before the first are zeros
+  // the query's selected rows (one coalesced load), then the first chunk's bytes
   for (int i = threadIdx.x; i < a.n_main * kChunk; i += kCsThreads) sh.idx[i] = a.indices[(size_t)t * a.k + i];
-  for (int i = lane; i < kCsSlice * kXTStride / 8; i += 64) reinterpret_cast<uint4*>(sh.xt[w])[i] = uint4{0u, 0u, 0u, 0u};
-  if (threadIdx.x < 4 * 64) reinterpret_cast<uint4*>(&sh.p[0][0])[threadIdx.x] = uint4{0u, 0u, 0u, 0u};
-  if (threadIdx.x < 4) sh.grow[threadIdx.x] = 0;
   __syncthreads();
   CsRaw raw;
   if (c0 < a.n_main) cs_issue_rows<KVF>(a, sh, rows0, b, c0);
@@ -832,8 +828,7 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
 
   // O^T of the previous chunk, all four head groups of this wave's channels:
   // its slice in sh.xt (this wave's own), its P^T, rescale factors and flags
-  // from that chunk's softmax.  Before the first chunk the slice and P^T are
-  // zeros and no group rescales.
+  // from that chunk's softmax (the first chunk's rescale multiplies zeros).
   const auto o_phase = [&]() {
     const int4 grows = *reinterpret_cast<const int4*>(sh.grow);
     const int grw[4] = {grows.x, grows.y, grows.z, grows.w};
@@ -856,13 +851,14 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
     }
   };
 
-  // One chunk c: the previous chunk's O^T, this chunk's slice and S^T, its
-  // softmax.  Selected rows (WIN false) come from `cur`, which then receives
-  // chunk c + 2; window rows from `raw`, loaded one chunk ahead.  The O^T
-  // products overlap this chunk's staging: the two need different units.
-  const auto chunk = [&](auto win, int c, CsRows& cur) {
+  // One chunk c: the previous chunk's O^T (none before the item's first
+  // chunk), this chunk's slice and S^T, its softmax.  Selected rows (WIN
+  // false) come from `cur`, which then receives chunk c + 2; window rows from
+  // `raw`, loaded one chunk ahead.  The O^T products overlap this chunk's
+  // staging: the two need different units.
+  const auto chunk = [&](auto win, auto first, int c, CsRows& cur) {
       constexpr bool WIN = decltype(win)::value;
-      o_phase();
+      if (!decltype(first)::value) o_phase();
       cs_store_slice<KVF, SWF, WIN>(a, sh, cur, raw);
       uint32_t ok;  // this chunk's valid rows
       floatx4 acc[2];
@@ -930,17 +926,19 @@ __global__ __launch_bounds__(kCsThreads) void attend_cs_kernel(AttnArgs a) {
       __syncthreads();
       if (!WIN && c + 2 < c1 && c + 2 < a.n_main) cs_issue_rows<KVF>(a, sh, cur, b, c + 2);
   };
-  // selected-row chunks alternate between rows0 and rows1 (two LDS objects:
-  // the requests into one never make the compiler wait before reads of the
-  // other), then the window chunks
+  // selected-row chunks alternate between rows0 and rows1 (chunk c0 + i in
+  // rows0 for even i; two LDS objects: the requests into one never make the
+  // compiler wait before reads of the other), then the window chunks
   const int cs_end = c1 < a.n_main ? c1 : a.n_main;
   int c = c0;
+  if (c < cs_end) chunk(CsFlag<false>(), CsFlag<true>(), c++, rows0);
+  else chunk(CsFlag<true>(), CsFlag<true>(), c++, rows0);
   for (; c + 1 < cs_end; c += 2) {
-    chunk(CsWin<false>(), c, rows0);
-    chunk(CsWin<false>(), c + 1, rows1);
+    chunk(CsFlag<false>(), CsFlag<false>(), c, rows1);
+    chunk(CsFlag<false>(), CsFlag<false>(), c + 1, rows0);
   }
-  if (c < cs_end) chunk(CsWin<false>(), c++, rows0);
-  for (; c < c1; ++c) chunk(CsWin<true>(), c, rows0);
+  if (c < cs_end) chunk(CsFlag<false>(), CsFlag<false>(), c++, rows1);
+  for (; c < c1; ++c) chunk(CsFlag<true>(), CsFlag<false>(), c, rows0);
   o_phase();
   // max of each head (the same in both halves), sum of each half's rows
   {
