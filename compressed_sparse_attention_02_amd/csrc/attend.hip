@@ -552,20 +552,21 @@ __global__ __launch_bounds__(64 * W, W == 1 ? 1 : CSA2_ATTN_WAVES_PER_SIMD) void
 // that every wave touches only a slice of it and holds half a wave's worth of
 // state (two waves per SIMD):
 //   S^T = X Q^T: wave w takes heads 16 (w & 3) .. +15 over channels
-//     256 (w >> 2) .. +255.  For selected rows the A operands come straight
-//     from memory into registers: lane (r, g) holds rows r and 16 + r,
-//     channels 256 (w >> 2) + 64 g .. +63, k-step j taking channels + 8 j ..
-//     + 8 (the order of the channels along k does not change the products;
-//     the query operand uses the same order).  Window chunks (bf16 or FP8
-//     rows, four times the bytes of FP4 ones) take them from a row-major copy
-//     in LDS.  The two channel halves of a head group add their partial S^T
-//     through LDS (2 KB per wave).
+//     256 (w >> 2) .. +255.  For selected rows the A operands are dequantised
+//     from the chunk's raw bytes, which arrive in LDS by direct-to-LDS
+//     requests (cs_issue_rows): lane (r, g) holds rows r and 16 + r, channels
+//     256 (w >> 2) + 64 g .. +63, k-step j taking channels + 8 j .. + 8 (the
+//     order of the channels along k does not change the products; the query
+//     operand uses the same order).  Window chunks (bf16 or FP8 rows, four
+//     times the bytes of FP4 ones) take them from a row-major copy in LDS.
+//     The two channel halves of a head group exchange their partial S^T
+//     through LDS (2 KB per wave); both form the head group's maximum and
+//     rescale state, each the probabilities of its own 16 rows.
 //   O^T += X^T P^T: wave w takes channels 64 w .. +63 of all 64 heads; its A
 //     operand is its own transposed slice of the chunk in LDS (staged by the
-//     wave itself), the B operand P^T of head group G is published in LDS by
-//     wave G.
-// Every element of a selected-row chunk is written to LDS once and read
-// back once.
+//     wave itself), the B operand P^T of head group G comes from LDS, written
+//     by the two waves of group G.  These products of a chunk run at the start
+//     of the next chunk, ahead of its staging.
 
 constexpr int kCsThreads = 512;
 constexpr int kCsSlice = kDim / 8;  // output channels per wave
