@@ -123,3 +123,42 @@ def test_attend_ex_reuse_layers_with_sink_and_rope():
         for t, (o, lr) in ref.items():
             assert_close_bf16(out[l, t], o, what=f"layer {l} t={t}")
             assert np.allclose(npy(lse[l, t]), lr, atol=1e-4, rtol=1e-5)
+
+
+# Windows that end before the window length (the first tokens of a sequence: rows
+# [max(0, e - 128), e), e = 0 an empty window) and fewer than k visible entries (-1
+# slots in every chunk past the last entry), in every format: "short_split" runs the
+# eight-wave kernel with split work items (three layers of four queries, some items
+# starting in the window chunks), "short_wide" the one-item-per-query launch.
+SHORT = {
+    "short_split": dict(B=4, N=300, n_layers=3),
+    "short_wide": dict(B=1, N=300, q_per_seq=256),
+}
+SHORT_ENDS = [0, 1, 31, 32, 33, 64, 100, 127, 128]
+
+
+@pytest.mark.parametrize("swf", [0, 1])
+@pytest.mark.parametrize("kvf", [0, 1])
+@pytest.mark.parametrize("name", list(SHORT))
+def test_attend_ex_short_windows_and_masked_rows(name, kvf, swf):
+    log(f"[attend_ex] {name} kv={kvf} swa={swf}")
+    c = G.make_case(name, **SHORT[name], seed=43, device=DEV)
+    c.extra["nv"] = G.kv_e4m3_16(c)
+    c.extra["fp8"] = G.window_fp8(c)
+    ends = torch.tensor(SHORT_ENDS, dtype=torch.int32)
+    c.swa_end = ends[torch.arange(c.T) % len(SHORT_ENDS)].to(DEV).contiguous()
+    # N < k: every query selects all N entries (ascending), the rest of its slots -1
+    idx = torch.full((c.T, c.k), -1, dtype=torch.int32)
+    idx[:, :c.N] = torch.arange(c.N, dtype=torch.int32)
+    c.extra["idx"] = idx.to(DEV).contiguous()
+    L = c.n_layers
+    out, lse = run_gpu(c, kvf, swf, False, layer0=0, n_layers=L)
+    torch.cuda.synchronize()
+    if L == 1:
+        out, lse = out[None], lse[None]
+    ts = list(range(c.T)) if c.T <= 16 else list(range(12)) + [100, 200, 255]
+    for l in range(L):
+        ref = run_oracle(c, kvf, swf, False, l, ts)
+        for t, (o, lr) in ref.items():
+            assert_close_bf16(out[l, t], o, what=f"{name} layer {l} t={t} end={int(c.swa_end[t])}")
+            assert np.allclose(npy(lse[l, t]), lr, atol=1e-4, rtol=1e-5)
